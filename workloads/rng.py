@@ -1,0 +1,179 @@
+"""Seeded, counter-based synthetic inputs shared by the tests, the smoke check and the benchmark.
+
+This module draws random numbers and stores them in the storage dtypes the kernels read
+(fp32, bf16, OCP fp8 e4m3fn).  It holds none of the attention method's arithmetic: no
+softmax, no pooling, no scoring.  Both the HIP path and the CPU oracle receive the very
+bytes produced here.
+
+Generator: SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
+generators", OOPSLA 2014; finaliser constants as published by Vigna for splitmix64.c)
+used in counter mode.  Element i of tensor `tid` under `seed` is
+
+    key   = mix64(mix64(seed) ^ tid)
+    u64_i = mix64(key + (i + 1) * 0x9E3779B97F4A7C15)          (mod 2**64)
+
+so any element can be produced independently of the others (chunked, multi-threaded,
+bit-reproducible).  Uniforms take the top 53 bits: u = (u64 >> 11) * 2**-53 in [0, 1).
+Normals use the Box-Muller transform on the pair of uniforms drawn at counters 2i and
+2i + 1:  z_i = sqrt(-2 ln(1 - u_2i)) * cos(2 pi u_{2i+1}), evaluated in float64.
+
+Rounding to storage: float64 -> float32 (IEEE round-to-nearest-even), then
+float32 -> bf16 round-to-nearest-even on the bit pattern, or float32 -> e4m3fn
+round-to-nearest-even with saturation to +-448.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+GOLDEN = np.uint64(0x9E3779B97F4A7C15)
+_M1 = np.uint64(0xBF58476D1CE4E5B9)
+_M2 = np.uint64(0x94D049BB133111EB)
+
+# Storage dtype codes; the values match the C-ABI enum csa_dtype.
+F32, BF16, FP8 = 0, 1, 2
+DTYPE_NAMES = {F32: "f32", BF16: "bf16", FP8: "fp8_e4m3"}
+NP_STORAGE = {F32: np.float32, BF16: np.uint16, FP8: np.uint8}
+
+_CHUNK = 1 << 20
+
+
+def mix64(x: np.ndarray) -> np.ndarray:
+    """SplitMix64 finaliser on a uint64 array (wrapping arithmetic)."""
+    x = np.asarray(x, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        x = (x ^ (x >> np.uint64(30))) * _M1
+        x = (x ^ (x >> np.uint64(27))) * _M2
+    return x ^ (x >> np.uint64(31))
+
+
+def stream_key(seed: int, tid: int) -> np.uint64:
+    k = mix64(np.array([seed], dtype=np.uint64))[0]
+    return mix64(np.array([k ^ np.uint64(tid)], dtype=np.uint64))[0]
+
+
+def raw_u64(seed: int, tid: int, start: int, count: int) -> np.ndarray:
+    key = stream_key(seed, tid)
+    ctr = np.arange(start + 1, start + count + 1, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        return mix64(key + ctr * GOLDEN)
+
+
+def _uniform_chunk(seed, tid, start, count):
+    return (raw_u64(seed, tid, start, count) >> np.uint64(11)).astype(np.float64) * (2.0 ** -53)
+
+
+def _normal_chunk(seed, tid, start, count):
+    u = _uniform_chunk(seed, tid, 2 * start, 2 * count)
+    u1 = 1.0 - u[0::2]
+    u2 = u[1::2]
+    return np.sqrt(-2.0 * np.log(u1)) * np.cos(2.0 * np.pi * u2)
+
+
+# ---------------------------------------------------------------- storage rounding
+def f32_to_bf16_bits(x32: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit pattern, round to nearest even (NaN kept quiet)."""
+    b = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32)
+    rounding = np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))
+    with np.errstate(over="ignore"):
+        out = ((b + rounding) >> np.uint32(16)).astype(np.uint16)
+    nan = np.isnan(x32)
+    if nan.any():
+        out[nan] = 0x7FC0
+    return out
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _e4m3_grid():
+    # all finite non-negative e4m3fn values, ascending, with their codes
+    vals, codes = [], []
+    for code in range(0x7F):  # 0x7F is NaN
+        e, mant = code >> 3, code & 7
+        v = mant * 2.0 ** -9 if e == 0 else (1 + mant / 8) * 2.0 ** (e - 7)
+        vals.append(v)
+        codes.append(code)
+    return np.array(vals), np.array(codes, dtype=np.uint8)
+
+
+_E4M3_VALS, _E4M3_CODES = _e4m3_grid()
+
+
+def f32_to_e4m3_bits(x32: np.ndarray) -> np.ndarray:
+    """float32 -> OCP e4m3fn code, round to nearest even, saturating at +-448."""
+    x = np.asarray(x32, dtype=np.float64)
+    a = np.minimum(np.abs(x), 448.0)
+    hi = np.searchsorted(_E4M3_VALS, a, side="left")  # first grid value >= a
+    hi = np.minimum(hi, len(_E4M3_VALS) - 1)
+    lo = np.maximum(hi - 1, 0)
+    vhi, vlo = _E4M3_VALS[hi], _E4M3_VALS[lo]
+    exact = vhi == a
+    dlo, dhi = a - vlo, vhi - a
+    pick_hi = exact | (dhi < dlo) | ((dhi == dlo) & ((_E4M3_CODES[hi] & 1) == 0))
+    code = np.where(pick_hi, _E4M3_CODES[hi], _E4M3_CODES[lo]).astype(np.uint8)
+    sign = np.signbit(x).astype(np.uint8) << np.uint8(7)
+    return code | sign
+
+
+def e4m3_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    b = np.asarray(b, dtype=np.uint8)
+    mag = _E4M3_VALS[np.minimum(b & 0x7F, 0x7E)].astype(np.float32)
+    mag = np.where((b & 0x7F) == 0x7F, np.float32(np.nan), mag)
+    return np.where(b & 0x80, -mag, mag).astype(np.float32)
+
+
+def to_storage(x64: np.ndarray, dtype: int) -> np.ndarray:
+    x32 = np.asarray(x64, dtype=np.float64).astype(np.float32)
+    if dtype == F32:
+        return x32
+    if dtype == BF16:
+        return f32_to_bf16_bits(x32)
+    if dtype == FP8:
+        return f32_to_e4m3_bits(x32)
+    raise ValueError(dtype)
+
+
+def storage_to_f32(a: np.ndarray, dtype: int) -> np.ndarray:
+    if dtype == F32:
+        return np.asarray(a, dtype=np.float32)
+    if dtype == BF16:
+        return bf16_bits_to_f32(a)
+    if dtype == FP8:
+        return e4m3_bits_to_f32(a)
+    raise ValueError(dtype)
+
+
+# ---------------------------------------------------------------- tensor draws
+def _threads():
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _fill(shape, dtype, fn):
+    count = int(np.prod(shape))
+    out = np.empty(count, dtype=NP_STORAGE[dtype])
+    starts = list(range(0, count, _CHUNK))
+
+    def work(s):
+        e = min(count, s + _CHUNK)
+        out[s:e] = to_storage(fn(s, e - s), dtype)
+
+    if len(starts) <= 1:
+        for s in starts:
+            work(s)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(work, starts))
+    return out.reshape(shape)
+
+
+def normal(seed: int, tid: int, shape, dtype: int = F32, std: float = 1.0) -> np.ndarray:
+    """N(0, std^2) samples in storage dtype `dtype`, as a numpy array of the storage type."""
+    return _fill(shape, dtype, lambda s, c: std * _normal_chunk(seed, tid, s, c))
+
+
+def uniform(seed: int, tid: int, shape, dtype: int = F32, lo: float = 0.0, hi: float = 1.0) -> np.ndarray:
+    return _fill(shape, dtype, lambda s, c: lo + (hi - lo) * _uniform_chunk(seed, tid, s, c))
