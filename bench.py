@@ -1,0 +1,283 @@
+"""Benchmark of the CSA / HCA hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--no-graph] [--no-cpu-baseline]
+
+Default workload: CSA decode at a 131,072-token context (batch 32, 32,768 compressed entries
+per sequence, c = 512, 128 query heads, fp8 e4m3 indexer 64 x 128, top-k 1024).  One step =
+index + top-k + sparse MQA for one new token per sequence (that token opens an incomplete
+block, so no entry is compressed in the step).  The step is captured once in a HIP graph and
+replayed K times between two synchronisations; inputs are resident in HBM before timing.
+
+Prints one JSON line: whole-step throughput (query tokens/s), the roofline of the dominant
+kernel (timed with HIP events on the stream it runs on), and the CPU oracle's throughput on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "CSA query tokens/s (compress+index+top-k+MQA) at 128K ctx; % of roofline"
+HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
+MFMA_PEAK = {"bf16": 2.5e15, "fp8": 5.0e15}
+DT_BYTES = {0: 4, 1: 2, 2: 1}
+DT_NAME = {0: "f32", 1: "bf16", 2: "fp8_e4m3"}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------- algorithmic work
+def stage_work(cfg):
+    """Per-stage algorithmic bytes / flops of one step (each input byte read once, each output
+    written once; flops over visible or selected pairs only)."""
+    B, c, H = cfg.batch, cfg.c, cfg.H
+    e = DT_BYTES[cfg.dt]
+    st = {}
+    if cfg.kind in ("csa_decode", "csa_prefill"):
+        T, N, HI, cI, k = cfg.T, cfg.N, cfg.H_I, cfg.c_I, cfg.k
+        eq = DT_BYTES[cfg.qk_dt]
+        pos = cfg.q_pos0 + np.arange(T)
+        vis = np.minimum(N, (pos + 1) // cfg.m)          # visible entries per query
+        pairs = int(vis.sum()) * B
+        sel = int(np.minimum(vis, k).sum()) * B
+        if cfg.kind == "csa_prefill":
+            n = cfg.n
+            st["compress_kv"] = dict(bytes=4 * B * n * c * e + B * (n // cfg.m) * c * e + 2 * cfg.m * c * 4, flops=0,
+                                     bound="hbm")
+            st["compress_kI"] = dict(bytes=4 * B * n * cI * e + B * (n // cfg.m) * cI * e + 2 * cfg.m * cI * 4,
+                                     flops=0, bound="hbm")
+        idx_bytes = B * N * cI * eq + B * T * HI * (cI * eq + 4) + pairs * 4
+        st["index"] = dict(bytes=idx_bytes, flops=2 * pairs * HI * cI,
+                           bound="hbm" if cfg.kind == "csa_decode" else "mfma")
+        st["topk"] = dict(bytes=pairs * 4 + B * T * k * 8, flops=0, bound="hbm")
+        # decode gathers distinct rows per sequence from HBM; prefill re-gathers from a cache
+        # that stays in L2/MALL, so its HBM bytes are the cache read once
+        kv_bytes = sel * c * e if cfg.kind == "csa_decode" else B * N * c * e
+        st["mqa"] = dict(bytes=kv_bytes + 2 * B * T * H * c * e + B * T * k * 4, flops=4 * sel * H * c,
+                         bound="hbm" if cfg.kind == "csa_decode" else "mfma")
+    else:
+        n, mp, T, N = cfg.n, cfg.m_prime, cfg.T, cfg.N
+        pos = cfg.q_pos0 + np.arange(T)
+        vis = np.minimum(N, (pos + 1) // mp)
+        pairs = int(vis.sum()) * B
+        st["compress"] = dict(bytes=2 * B * n * c * e + B * N * c * e + mp * c * 4, flops=0, bound="hbm")
+        st["mqa"] = dict(bytes=B * N * c * e + 2 * B * T * H * c * e, flops=4 * pairs * H * c, bound="mfma")
+    return st
+
+
+def peak_for(cfg, stage, bound):
+    if bound == "hbm":
+        return HBM_PEAK, "GB/s"
+    if stage == "index" and cfg.qk_dt == 2:
+        return MFMA_PEAK["fp8"], "TFLOP/s"
+    return MFMA_PEAK["bf16"], "TFLOP/s"
+
+
+# ---------------------------------------------------------------------------- CPU baseline
+def cpu_baseline(cfg, host, budget_s=20.0):
+    import oracle
+
+    t0 = time.perf_counter()
+    if cfg.kind == "csa_decode":
+        nseq = cfg.batch
+        sub = {k: host[k][:nseq] for k in ("kv", "kI", "q", "qI", "w")}
+        sc = oracle.index_scores(sub["qI"], sub["w"], sub["kI"], cfg.m, q_pos0=cfg.q_pos0, qk_dtype=cfg.qk_dt)
+        idx, _ = oracle.topk(sc, cfg.m, cfg.k, q_pos0=cfg.q_pos0)
+        oracle.sparse_mqa(sub["q"], sub["kv"], idx, cfg.scale, dtype=cfg.dt)
+        tokens = nseq * cfg.T
+        sample = f"all {nseq} sequences x {cfg.T} token (index + top-k + MQA, float64)"
+    elif cfg.kind == "csa_prefill":
+        rows = np.arange(cfg.T - 64, cfg.T)
+        dt = cfg.dt
+        kv = oracle.csa_compress(host["Ca"], host["Cb"], host["Za"], host["Zb"], host["Ba"], host["Bb"], cfg.m,
+                                 in_dtype=dt, out_dtype=dt)
+        kI = oracle.csa_compress(host["ICa"], host["ICb"], host["IZa"], host["IZb"], host["IBa"], host["IBb"], cfg.m,
+                                 in_dtype=dt, out_dtype=dt)
+        qpos = cfg.q_pos0 + rows
+        sc = oracle.index_scores(host["qI"][:, rows], host["w"][:, rows], kI, cfg.m, qk_dtype=cfg.qk_dt, qpos=qpos)
+        idx, _ = oracle.topk(sc, cfg.m, cfg.k, qpos=qpos)
+        oracle.sparse_mqa(host["q"][:, rows], kv, idx, cfg.scale, dtype=dt)
+        tokens = len(rows)
+        sample = f"full compression + the last {len(rows)} query rows (index + top-k + MQA), float64"
+    else:
+        rows = np.arange(cfg.T - 8, cfg.T)
+        kv = oracle.hca_compress(host["C"], host["Z"], host["B"], cfg.m_prime, in_dtype=cfg.dt, out_dtype=cfg.dt)
+        oracle.hca_dense_mqa(host["q"][:, rows], kv, cfg.m_prime, cfg.scale, dtype=cfg.dt, qpos=cfg.q_pos0 + rows)
+        tokens = len(rows)
+        sample = f"full HCA compression + {len(rows)} query rows of dense MQA, float64"
+    dt = time.perf_counter() - t0
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 3)}
+
+
+# ---------------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="cfg2_csa_decode_128k")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stage-reps", type=int, default=0, help="launches per stage for kernel timing (0: = steps)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import long_context_sparse_08_amd as csa
+    from long_context_sparse_08_amd.pipeline import CsaDecode, CsaPrefill, HcaChunk
+    from workloads import CONFIGS, make_inputs, shapes
+
+    cfg = CONFIGS[args.config]
+    torch.cuda.set_device(0)
+    log(f"[bench] generating inputs for {cfg.name}")
+    host = make_inputs(cfg)
+    sh = shapes(cfg)
+    dev = {}
+    for k, v in host.items():
+        t = torch.from_numpy(v)
+        if sh[k][1] == 1:
+            t = t.view(torch.bfloat16)
+        dev[k] = t.cuda()
+    torch.cuda.synchronize()
+    log("[bench] inputs resident on the GPU")
+
+    if cfg.kind == "csa_decode":
+        pipe = CsaDecode(dev, cfg.m, cfg.k, cfg.q_pos0)
+    elif cfg.kind == "csa_prefill":
+        pipe = CsaPrefill(dev, cfg.m, cfg.k, cfg.q_pos0)
+    else:
+        pipe = HcaChunk(dev, cfg.m_prime, cfg.q_pos0)
+
+    for _ in range(args.warmup):
+        pipe.run()
+    torch.cuda.synchronize()
+
+    graph = None
+    if not args.no_graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            pipe.run()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            pipe.run()
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+
+    # ---- timed region: K whole steps
+    log(f"[bench] timing {args.steps} steps ({'graph' if graph else 'eager'})")
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        if graph is not None:
+            graph.replay()
+        else:
+            pipe.run()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    tokens = cfg.batch * cfg.T
+    value = tokens / (ms * 1e-3)
+
+    # ---- per-stage kernel time: back-to-back launches of each stage, HIP events on the
+    # stream the launches go to (torch's current stream)
+    reps = args.stage_reps or args.steps
+    stages = {}
+    if cfg.kind == "csa_decode":
+        i = dev
+        scores = torch.empty((cfg.batch, cfg.T, cfg.N), dtype=torch.float32, device="cuda")
+        stages["index"] = lambda: csa.csa_index_scores(i["qI"], i["w"], i["kI"], cfg.q_pos0, cfg.m, scores=scores)
+        stages["topk"] = lambda: csa.csa_topk(scores, cfg.q_pos0, cfg.m, cfg.k, idx=pipe.idx, sel_scores=pipe.sel)
+        stages["mqa"] = pipe.attend
+    elif cfg.kind == "csa_prefill":
+        i = dev
+        stages["compress_kv"] = lambda: csa.csa_compress(i["Ca"], i["Cb"], i["Za"], i["Zb"], i["Ba"], i["Bb"], cfg.m,
+                                                         out=pipe.kv)
+        stages["compress_kI"] = lambda: csa.csa_compress(i["ICa"], i["ICb"], i["IZa"], i["IZb"], i["IBa"], i["IBb"],
+                                                         cfg.m, out=pipe.kI)
+        scores = torch.empty((cfg.batch, cfg.T, cfg.N), dtype=torch.float32, device="cuda")
+        stages["index"] = lambda: csa.csa_index_scores(i["qI"], i["w"], pipe.kI, cfg.q_pos0, cfg.m, scores=scores)
+        stages["topk"] = lambda: csa.csa_topk(scores, cfg.q_pos0, cfg.m, cfg.k, idx=pipe.idx, sel_scores=pipe.sel)
+        stages["mqa"] = pipe.attend
+    else:
+        stages["compress"] = pipe.compress
+        stages["mqa"] = pipe.attend
+    work = stage_work(cfg)
+    stage_ms = {}
+    for name, fn in stages.items():
+        fn()
+        torch.cuda.synchronize()
+        n_rep = max(3, reps if cfg.kind != "hca_chunk" else min(reps, 20))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n_rep):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        stage_ms[name] = a.elapsed_time(b) / n_rep
+    dom = max(stage_ms, key=stage_ms.get)
+    w = work[dom]
+    peak, unit = peak_for(cfg, dom, w["bound"])
+    t_s = stage_ms[dom] * 1e-3
+    if w["bound"] == "hbm":
+        achieved = w["bytes"] / t_s
+        roof = {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": peak / 1e9, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": None}
+    else:
+        achieved = w["flops"] / t_s
+        roof = {"bound": "mfma", "achieved": round(achieved / 1e12, 1), "peak": peak / 1e12, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": None}
+    roof["kernel"] = dom
+    roof["ms_per_launch"] = round(stage_ms[dom], 5)
+    ideal = sum(max(v["bytes"] / HBM_PEAK, v["flops"] / peak_for(cfg, k, "mfma")[0]) for k, v in work.items())
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.qk_dt != 2 else "bf16+fp8",
+        "data": "synthetic (seeded SplitMix64 normals/uniforms; no dataset)",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "query_tokens_per_seq": cfg.T, "q_pos0": cfg.q_pos0,
+                   "entries": cfg.N, "c": cfg.c, "heads": cfg.H, "H_I": cfg.H_I, "c_I": cfg.c_I, "k": cfg.k,
+                   "m": cfg.m if cfg.kind != "hca_chunk" else cfg.m_prime, "kv_dtype": DT_NAME[cfg.dt],
+                   "qk_dtype": DT_NAME[cfg.qk_dt] if cfg.kind != "hca_chunk" else None,
+                   "graph": graph is not None},
+        "roofline": roof,
+        "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        "step_roofline_frac": round(ideal / (ms * 1e-3), 4),
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline")
+        result["cpu_baseline"] = cpu_baseline(cfg, host)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

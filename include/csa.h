@@ -1,0 +1,176 @@
+/*
+ * csa.h — C ABI of libcsa: the CSA / HCA attention hot path on AMD Instinct MI355X (gfx950).
+ *
+ * Method sources (web pages on the DeepSeek-V4 report):
+ *   [N] "DeepSeek-V4: 迈向高效百万级上下文智能" (notes.kuangjux.top): §1.1 step 1 (token-level
+ *       compression, eq. C_i^Comp), §1.1 step 2 (lightning indexer eq. I_{t,s}, top-k,
+ *       shared-KV MQA), §1.2 (HCA: ratio m' = 128, no overlap, dense attention).
+ *   [M] mlpod.com summary of "DeepSeek-V4: Towards Highly Efficient Million-Token Context
+ *       Intelligence": §2.3.1 (CSA), §2.3.2 (HCA, shared-KV MQA).
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA memory), owned by the
+ *     caller, dense row-major with the shapes given, 16-byte aligned.  The library keeps no
+ *     reference to them after the call returns.
+ *   - `batch` independent sequences of equal length.  Query i of every sequence sits at the
+ *     absolute position q_pos0 + i.
+ *   - Causal visibility: compressed entry s (ratio r) may be used by a query at absolute
+ *     position p iff r*(s+1)-1 <= p, i.e. once every raw token of the entry is at or before
+ *     the query.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null stream).  The
+ *     library never allocates device memory, never synchronises, and holds no mutable global
+ *     state, so calls on different streams may overlap freely.
+ *   - Return value: CSA_OK or a negative csa_status.  All argument checks run on the host
+ *     before anything is launched; an invalid call launches nothing and writes nothing.
+ *     CSA_ERR_HIP reports a launch failure (hipGetLastError); faults inside a kernel surface
+ *     at the caller's next synchronisation.
+ *   - Raw tokens past the last full window (n mod ratio) are not compressed: they belong to
+ *     the caller's state cache.
+ *   - fp8 means OCP FP8 e4m3fn (max 448, no infinities), one byte per value, scale 1.
+ */
+#ifndef LIBCSA_CSA_H
+#define LIBCSA_CSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3 = 2 } csa_dtype;
+
+typedef enum {
+    CSA_OK = 0,
+    CSA_ERR_INVALID_ARG = -1,  /* null pointer, negative or inconsistent size */
+    CSA_ERR_UNSUPPORTED = -2,  /* valid but not implemented: dtype combination or shape limit */
+    CSA_ERR_WORKSPACE = -3,    /* workspace pointer null or smaller than the required size */
+    CSA_ERR_HIP = -4           /* the HIP runtime reported an error at launch */
+} csa_status;
+
+/* A hipStream_t passed through the C ABI. */
+typedef void* csa_stream_t;
+
+/* Shape limits (CSA_ERR_UNSUPPORTED beyond them). */
+#define CSA_MAX_RATIO 1024      /* m, m' */
+#define CSA_MAX_WIDTH 1024      /* c, c_I: must be a multiple of 8 */
+#define CSA_MAX_TOPK 2048       /* k */
+#define CSA_MAX_HEADS 256       /* H, H_I */
+
+/*
+ * csa_compress — overlapped softmax-weighted compression ([N] §1.1 step 1, eq. C_i^Comp;
+ * [M] §2.3.1).  For entry i < N = floor(n/m) and channel d, one softmax per channel taken
+ * jointly over the 2m scores
+ *     Za[j,d] + Ba[j-mi, d]      for j in [mi, m(i+1))        (window i of stream a)
+ *     Zb[j,d] + Bb[j-m(i-1), d]  for j in [m(i-1), mi)        (window i-1 of stream b)
+ * weights the matching Ca / Cb values:  out[i,d] = sum_j S_j * C_j.  Entry 0 has no previous
+ * window; its weights come from window 0 of stream a alone.
+ *   Ca, Cb, Za, Zb : [batch, n, c], dtype in_t (CSA_F32 or CSA_BF16)
+ *   Ba, Bb         : [m, c] float32 learned position biases
+ *   out            : [batch, floor(n/m), c], dtype out_t (CSA_F32 or CSA_BF16; bf16 is
+ *                    rounded to nearest even from the fp32 result)
+ * Used for both the KV entries (width c) and the indexer keys (width c_I).
+ * Limits: 1 <= m <= CSA_MAX_RATIO, c % 8 == 0, c <= CSA_MAX_WIDTH.  n < m is valid and
+ * writes nothing.
+ */
+int csa_compress(const void* Ca, const void* Cb, const void* Za, const void* Zb, const float* Ba,
+                 const float* Bb, int64_t batch, int64_t n, int m, int c, csa_dtype in_t, void* out,
+                 csa_dtype out_t, csa_stream_t stream);
+
+/*
+ * hca_compress — non-overlapping compression for HCA ([N] §1.2 table: m' = 128, no
+ * overlap; [M] §2.3.2).  out[i,d] = sum over j in [m'i, m'(i+1)) of softmax_j(Z[j,d] +
+ * B[j-m'i, d]) * C[j,d].
+ *   C, Z : [batch, n, c], dtype in_t;  B : [m', c] float32;  out : [batch, floor(n/m'), c].
+ * Limits as csa_compress.
+ */
+int hca_compress(const void* C, const void* Z, const float* B, int64_t batch, int64_t n, int m_prime,
+                 int c, csa_dtype in_t, void* out, csa_dtype out_t, csa_stream_t stream);
+
+/*
+ * csa_index_topk_workspace_size — bytes of device workspace csa_index_topk needs for these
+ * sizes (the fp32 score rows plus selection state).  Returns 0 for invalid sizes.
+ */
+size_t csa_index_topk_workspace_size(int64_t batch, int64_t T, int64_t N, int H_I, int k);
+
+/*
+ * csa_index_topk — lightning indexer + per-query top-k ([N] §1.1 step 2, eq. I_{t,s};
+ * [M] §2.3.1).  For every query t and visible entry s:
+ *     I[t,s] = sum_{h < H_I} w[t,h] * ReLU(qI[t,h,:] . kI[s,:])      (fp32 accumulation,
+ *     ReLU(x) = x > 0 ? x : +0), no scale factor.
+ * Then keeps the min(k, |visible|) entries with the highest score, ties broken toward the
+ * LOWER entry index, and writes them in ASCENDING entry order, padded with -1.
+ *   qI : [batch, T, H_I, c_I], kI : [batch, N, c_I], both dtype qk_t (F32, BF16 or FP8_E4M3)
+ *   w  : [batch, T, H_I] float32
+ *   idx        : [batch, T, k] int32 out
+ *   sel_scores : [batch, T, k] float32 out, or NULL: the score of each selected entry
+ *                (-inf at pads)
+ *   workspace  : device scratch of at least csa_index_topk_workspace_size(...) bytes,
+ *                16-byte aligned; contents on entry are ignored.
+ *   m          : CSA compression ratio (for the visibility rule).
+ * Limits: c_I % 8 == 0, c_I <= CSA_MAX_WIDTH, 1 <= H_I <= CSA_MAX_HEADS, 1 <= k <=
+ * CSA_MAX_TOPK, N < 2^31.
+ */
+int csa_index_topk(const void* qI, const float* w, const void* kI, int64_t batch, int64_t T, int64_t q_pos0,
+                   int64_t N, int H_I, int c_I, int m, int k, csa_dtype qk_t, int32_t* idx, float* sel_scores,
+                   void* workspace, size_t ws_bytes, csa_stream_t stream);
+
+/*
+ * csa_index_scores — the indexer scores alone, as a dense [batch, T, N] float32 matrix
+ * (invisible pairs = -inf).  Same arguments and formula as csa_index_topk; meant for
+ * parity checks and for callers with their own selection.
+ */
+int csa_index_scores(const void* qI, const float* w, const void* kI, int64_t batch, int64_t T, int64_t q_pos0,
+                     int64_t N, int H_I, int c_I, int m, csa_dtype qk_t, float* scores, csa_stream_t stream);
+
+/*
+ * csa_topk_workspace_size / csa_topk — the selection step of csa_index_topk alone, over
+ * caller-provided fp32 score rows (for callers that produce scores with csa_index_scores
+ * or their own kernel).  Same rule as csa_index_topk: per row, among the entries s < nv
+ * visible to the query (m(s+1)-1 <= q_pos0 + t), keep the min(k, nv) highest scores, ties
+ * toward the lower index, written in ascending index order and padded with -1.
+ *   scores : [batch*T rows] fp32, row r starting at scores + r*ld (ld >= N, ld % 4 == 0);
+ *            only the first nv entries of each row are read
+ *   idx, sel_scores, workspace : as csa_index_topk (sel_scores may be NULL)
+ * Limits: 1 <= k <= CSA_MAX_TOPK, N < 2^31.
+ */
+size_t csa_topk_workspace_size(int64_t batch, int64_t T, int64_t N, int k);
+int csa_topk(const float* scores, int64_t ld, int64_t batch, int64_t T, int64_t q_pos0, int64_t N, int m, int k,
+             int32_t* idx, float* sel_scores, void* workspace, size_t ws_bytes, csa_stream_t stream);
+
+/*
+ * csa_sparse_mqa — shared-KV multi-query attention over the selected entries ([N] §1.1
+ * step 2, last paragraph; [M] §2.3.2): all H heads of query t attend to the same entries
+ * idx[t,:], each entry serving as both key and value:
+ *     out[t,h,:] = sum_{s in idx[t]} softmax_s(scale * q[t,h,:] . kv[s,:]) * kv[s,:]
+ * (fp32 logits, softmax and accumulation).  Ids outside [0, N) — the -1 pads — are
+ * skipped; a query with no valid id gets a zero output.  Ids must be distinct.
+ *   q   : [batch, T, H, c]  dtype t (CSA_F32 or CSA_BF16)
+ *   kv  : [batch, N, c]     dtype t
+ *   idx : [batch, T, k]     int32
+ *   out : [batch, T, H, c]  dtype t
+ * Limits: c % 8 == 0, c <= CSA_MAX_WIDTH, 1 <= H <= CSA_MAX_HEADS, 1 <= k <= CSA_MAX_TOPK.
+ */
+int csa_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t batch, int64_t T, int64_t N, int H,
+                   int c, int k, float scale, csa_dtype t, void* out, csa_stream_t stream);
+
+/*
+ * hca_dense_mqa — dense causal shared-KV MQA over every visible HCA entry ([M] §2.3.2; [N]
+ * §1.2: no selection): for the query at position p, the entries s with m'(s+1)-1 <= p.
+ *   q : [batch, T, H, c], kv : [batch, N, c], out : [batch, T, H, c], all dtype t.
+ * A query that sees no entry gets a zero output.  Limits as csa_sparse_mqa.
+ */
+int hca_dense_mqa(const void* q, const void* kv, int64_t batch, int64_t T, int64_t q_pos0, int64_t N, int H,
+                  int c, int m_prime, float scale, csa_dtype t, void* out, csa_stream_t stream);
+
+/* Human-readable name of a csa_status value (static storage). */
+const char* csa_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int csa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBCSA_CSA_H */

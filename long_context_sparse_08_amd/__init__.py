@@ -1,0 +1,216 @@
+"""libcsa — CSA / HCA attention hot path (DeepSeek-V4 style) on AMD MI355X (gfx950).
+
+A thin ctypes binding over `_build/libcsa.so`: each function checks the tensors it is
+given, allocates outputs with torch when the caller passes none, and calls the C entry
+point of the same name on torch's current HIP stream.  All computation happens in the HIP
+kernels of the library; there is no CPU fallback.  Importing this module fails loudly if
+the library has not been built (`python long_context_sparse_08_amd/build.py`).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "_build", "libcsa.so")
+
+CSA_F32, CSA_BF16, CSA_FP8_E4M3 = 0, 1, 2
+STATUS = {0: "CSA_OK", -1: "CSA_ERR_INVALID_ARG", -2: "CSA_ERR_UNSUPPORTED", -3: "CSA_ERR_WORKSPACE",
+          -4: "CSA_ERR_HIP"}
+
+ENTRY_POINTS = ("csa_compress", "hca_compress", "csa_index_topk_workspace_size", "csa_index_topk",
+                "csa_index_scores", "csa_topk_workspace_size", "csa_topk", "csa_sparse_mqa", "hca_dense_mqa",
+                "csa_status_string", "csa_version")
+
+
+class CsaError(RuntimeError):
+    def __init__(self, name: str, status: int, msg: str):
+        super().__init__(f"{name} failed with {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libcsa is not built ({LIB_PATH} missing); run `python long_context_sparse_08_amd/build.py`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I64, I, F, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    sig = {
+        "csa_compress": ([P, P, P, P, P, P, I64, I64, I, I, I, P, I, P], I),
+        "hca_compress": ([P, P, P, I64, I64, I, I, I, P, I, P], I),
+        "csa_index_topk_workspace_size": ([I64, I64, I64, I, I], SZ),
+        "csa_index_topk": ([P, P, P, I64, I64, I64, I64, I, I, I, I, I, P, P, P, SZ, P], I),
+        "csa_index_scores": ([P, P, P, I64, I64, I64, I64, I, I, I, I, P, P], I),
+        "csa_topk_workspace_size": ([I64, I64, I64, I], SZ),
+        "csa_topk": ([P, I64, I64, I64, I64, I64, I, I, P, P, P, SZ, P], I),
+        "csa_sparse_mqa": ([P, P, P, I64, I64, I64, I, I, I, F, I, P, P], I),
+        "hca_dense_mqa": ([P, P, I64, I64, I64, I64, I, I, I, F, I, P, P], I),
+        "csa_status_string": ([I], ctypes.c_char_p),
+        "csa_version": ([], I),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = res
+    return L
+
+
+lib = _load()
+
+
+def _check(name: str, rc: int):
+    if rc != 0:
+        raise CsaError(name, rc, lib.csa_status_string(rc).decode())
+
+
+def _dt(x: torch.Tensor) -> int:
+    if x.dtype == torch.float32:
+        return CSA_F32
+    if x.dtype == torch.bfloat16:
+        return CSA_BF16
+    if x.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return CSA_FP8_E4M3
+    raise TypeError(f"unsupported dtype {x.dtype}")
+
+
+_TORCH_DT = {CSA_F32: torch.float32, CSA_BF16: torch.bfloat16}
+
+
+def _dev(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("libcsa takes device tensors only")
+        if not t.is_contiguous():
+            raise ValueError("libcsa takes contiguous tensors only")
+        dev = t.device if dev is None else dev
+        if t.device != dev:
+            raise ValueError("all tensors must be on one device")
+    return dev
+
+
+def _stream(dev) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _p(t):
+    return None if t is None else t.data_ptr()
+
+
+def version() -> int:
+    return lib.csa_version()
+
+
+def csa_compress(Ca, Cb, Za, Zb, Ba, Bb, m: int, out=None, out_dtype=None):
+    """[batch, n, c] streams (f32/bf16), [m, c] fp32 biases -> [batch, n // m, c]."""
+    dev = _dev(Ca, Cb, Za, Zb, Ba, Bb, out)
+    batch, n, c = Ca.shape
+    for t in (Cb, Za, Zb):
+        assert t.shape == Ca.shape and t.dtype == Ca.dtype
+    assert Ba.dtype == torch.float32 and Bb.dtype == torch.float32
+    if out is None:
+        out = torch.empty((batch, n // m, c), dtype=out_dtype or Ca.dtype, device=dev)
+    assert out.shape == (batch, n // m, c)
+    _check("csa_compress", lib.csa_compress(_p(Ca), _p(Cb), _p(Za), _p(Zb), _p(Ba), _p(Bb), batch, n, m, c, _dt(Ca),
+                                            _p(out), _dt(out), _stream(dev)))
+    return out
+
+
+def hca_compress(C, Z, B, m_prime: int, out=None, out_dtype=None):
+    dev = _dev(C, Z, B, out)
+    batch, n, c = C.shape
+    assert Z.shape == C.shape and Z.dtype == C.dtype and B.dtype == torch.float32
+    if out is None:
+        out = torch.empty((batch, n // m_prime, c), dtype=out_dtype or C.dtype, device=dev)
+    assert out.shape == (batch, n // m_prime, c)
+    _check("hca_compress", lib.hca_compress(_p(C), _p(Z), _p(B), batch, n, m_prime, c, _dt(C), _p(out), _dt(out),
+                                            _stream(dev)))
+    return out
+
+
+def csa_index_topk_workspace_size(batch: int, T: int, N: int, H_I: int, k: int) -> int:
+    return int(lib.csa_index_topk_workspace_size(batch, T, N, H_I, k))
+
+
+def workspace_for(batch, T, N, H_I, k, device) -> torch.Tensor:
+    nbytes = csa_index_topk_workspace_size(batch, T, N, H_I, k)
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
+def csa_index_topk(qI, w, kI, q_pos0: int, m: int, k: int, idx=None, sel_scores=None, workspace=None,
+                   want_scores: bool = True):
+    """qI [batch, T, H_I, c_I], w [batch, T, H_I] fp32, kI [batch, N, c_I] -> (idx, sel_scores)."""
+    dev = _dev(qI, w, kI, idx, sel_scores, workspace)
+    batch, T, H_I, c_I = qI.shape
+    N = kI.shape[1]
+    assert kI.shape == (batch, N, c_I) and w.shape == (batch, T, H_I) and w.dtype == torch.float32
+    assert _dt(qI) == _dt(kI)
+    if idx is None:
+        idx = torch.empty((batch, T, k), dtype=torch.int32, device=dev)
+    if sel_scores is None and want_scores:
+        sel_scores = torch.empty((batch, T, k), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = workspace_for(batch, T, N, H_I, k, dev)
+    _check("csa_index_topk", lib.csa_index_topk(_p(qI), _p(w), _p(kI), batch, T, q_pos0, N, H_I, c_I, m, k, _dt(qI),
+                                                _p(idx), _p(sel_scores), _p(workspace), workspace.numel(),
+                                                _stream(dev)))
+    return idx, sel_scores
+
+
+def csa_index_scores(qI, w, kI, q_pos0: int, m: int, scores=None):
+    dev = _dev(qI, w, kI, scores)
+    batch, T, H_I, c_I = qI.shape
+    N = kI.shape[1]
+    if scores is None:
+        scores = torch.empty((batch, T, N), dtype=torch.float32, device=dev)
+    _check("csa_index_scores", lib.csa_index_scores(_p(qI), _p(w), _p(kI), batch, T, q_pos0, N, H_I, c_I, m, _dt(qI),
+                                                    _p(scores), _stream(dev)))
+    return scores
+
+
+def csa_topk(scores, q_pos0: int, m: int, k: int, idx=None, sel_scores=None, workspace=None,
+             want_scores: bool = True):
+    """scores [batch, T, N] fp32 (N % 4 == 0 for 16-byte rows) -> (idx, sel_scores)."""
+    dev = _dev(scores, idx, sel_scores, workspace)
+    batch, T, N = scores.shape
+    assert scores.dtype == torch.float32
+    if idx is None:
+        idx = torch.empty((batch, T, k), dtype=torch.int32, device=dev)
+    if sel_scores is None and want_scores:
+        sel_scores = torch.empty((batch, T, k), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(int(lib.csa_topk_workspace_size(batch, T, N, k)), 16), dtype=torch.uint8,
+                                device=dev)
+    _check("csa_topk", lib.csa_topk(_p(scores), N, batch, T, q_pos0, N, m, k, _p(idx), _p(sel_scores),
+                                    _p(workspace), workspace.numel(), _stream(dev)))
+    return idx, sel_scores
+
+
+def csa_sparse_mqa(q, kv, idx, scale: float, out=None):
+    """q [batch, T, H, c], kv [batch, N, c], idx [batch, T, k] int32 -> out [batch, T, H, c]."""
+    dev = _dev(q, kv, idx, out)
+    batch, T, H, c = q.shape
+    N = kv.shape[1]
+    k = idx.shape[2]
+    assert kv.shape == (batch, N, c) and kv.dtype == q.dtype and idx.dtype == torch.int32
+    assert idx.shape == (batch, T, k)
+    if out is None:
+        out = torch.empty_like(q)
+    _check("csa_sparse_mqa", lib.csa_sparse_mqa(_p(q), _p(kv), _p(idx), batch, T, N, H, c, k, float(scale), _dt(q),
+                                                _p(out), _stream(dev)))
+    return out
+
+
+def hca_dense_mqa(q, kv, q_pos0: int, m_prime: int, scale: float, out=None):
+    dev = _dev(q, kv, out)
+    batch, T, H, c = q.shape
+    N = kv.shape[1]
+    assert kv.shape == (batch, N, c) and kv.dtype == q.dtype
+    if out is None:
+        out = torch.empty_like(q)
+    _check("hca_dense_mqa", lib.hca_dense_mqa(_p(q), _p(kv), batch, T, q_pos0, N, H, c, m_prime, float(scale), _dt(q),
+                                              _p(out), _stream(dev)))
+    return out

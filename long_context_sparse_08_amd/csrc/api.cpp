@@ -1,0 +1,176 @@
+// api.cpp — the C ABI of libcsa (declared in include/csa.h): host-side argument checks, then
+// dispatch to the kernel launchers.  Nothing here allocates, synchronises or keeps state.
+// Every check runs before the first HIP call, so an invalid call never touches the device.
+#include <math.h>
+
+#include "../../include/csa.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int kVersion = 100;   // 0.1.0
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool width_ok(int c) { return c > 0 && c % 8 == 0 && c <= CSA_MAX_WIDTH; }
+
+bool io_dtype(csa_dtype t) { return t == CSA_F32 || t == CSA_BF16; }
+
+int finish(int rc) {
+    if (rc == -2) return CSA_ERR_UNSUPPORTED;
+    if (rc != 0) return CSA_ERR_INVALID_ARG;
+    return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_HIP;
+}
+
+// Row stride (floats) of the score workspace: N rounded up to 4 so rows stay 16-byte aligned.
+int64_t score_ld(int64_t N) { return (N + 3) & ~int64_t(3); }
+
+constexpr size_t kWsAlign = 256;
+size_t round_up(size_t x) { return (x + kWsAlign - 1) & ~(kWsAlign - 1); }
+
+int check_indexer(const void* qI, const float* w, const void* kI, int64_t batch, int64_t T, int64_t q_pos0, int64_t N,
+                  int H_I, int c_I, int m, csa_dtype qk_t) {
+    if (batch < 0 || T < 0 || N < 0 || q_pos0 < 0) return CSA_ERR_INVALID_ARG;
+    if (m < 1 || H_I < 1 || c_I < 1) return CSA_ERR_INVALID_ARG;
+    if (!qI || !w || !kI) return CSA_ERR_INVALID_ARG;
+    if (!aligned16(qI) || !aligned16(kI) || !aligned16(w)) return CSA_ERR_INVALID_ARG;
+    if (qk_t != CSA_F32 && qk_t != CSA_BF16 && qk_t != CSA_FP8_E4M3) return CSA_ERR_UNSUPPORTED;
+    if (!width_ok(c_I) || H_I > CSA_MAX_HEADS || m > CSA_MAX_RATIO) return CSA_ERR_UNSUPPORTED;
+    if (N >= (int64_t(1) << 31)) return CSA_ERR_UNSUPPORTED;
+    return CSA_OK;
+}
+
+int check_mqa(const void* q, const void* kv, void* out, int64_t batch, int64_t T, int64_t N, int H, int c, float scale,
+              csa_dtype t) {
+    if (batch < 0 || T < 0 || N < 0 || H < 1 || c < 1) return CSA_ERR_INVALID_ARG;
+    if (!q || !kv || !out) return CSA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(kv) || !aligned16(out)) return CSA_ERR_INVALID_ARG;
+    if (!isfinite(scale)) return CSA_ERR_INVALID_ARG;
+    if (!io_dtype(t)) return CSA_ERR_UNSUPPORTED;
+    if (!width_ok(c) || H > CSA_MAX_HEADS) return CSA_ERR_UNSUPPORTED;
+    return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* csa_status_string(int status) {
+    switch (status) {
+        case CSA_OK: return "CSA_OK";
+        case CSA_ERR_INVALID_ARG: return "CSA_ERR_INVALID_ARG: null pointer, misalignment or inconsistent size";
+        case CSA_ERR_UNSUPPORTED: return "CSA_ERR_UNSUPPORTED: dtype or shape outside the implemented limits";
+        case CSA_ERR_WORKSPACE: return "CSA_ERR_WORKSPACE: workspace missing or too small";
+        case CSA_ERR_HIP: return "CSA_ERR_HIP: the HIP runtime reported a launch error";
+        default: return "unknown csa_status";
+    }
+}
+
+int csa_version(void) { return kVersion; }
+
+int csa_compress(const void* Ca, const void* Cb, const void* Za, const void* Zb, const float* Ba, const float* Bb,
+                 int64_t batch, int64_t n, int m, int c, csa_dtype in_t, void* out, csa_dtype out_t,
+                 csa_stream_t stream) {
+    if (batch < 0 || n < 0 || m < 1 || c < 1) return CSA_ERR_INVALID_ARG;
+    if (!Ca || !Cb || !Za || !Zb || !Ba || !Bb || !out) return CSA_ERR_INVALID_ARG;
+    if (!aligned16(Ca) || !aligned16(Cb) || !aligned16(Za) || !aligned16(Zb) || !aligned16(Ba) || !aligned16(Bb) ||
+        !aligned16(out))
+        return CSA_ERR_INVALID_ARG;
+    if (!io_dtype(in_t) || !io_dtype(out_t)) return CSA_ERR_UNSUPPORTED;
+    if (!width_ok(c) || m > CSA_MAX_RATIO) return CSA_ERR_UNSUPPORTED;
+    if (batch == 0 || n / m == 0) return CSA_OK;
+    return finish(csa::launch_compress(Ca, Za, Ba, Cb, Zb, Bb, batch, n, m, c, in_t, out, out_t,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int hca_compress(const void* C, const void* Z, const float* B, int64_t batch, int64_t n, int m_prime, int c,
+                 csa_dtype in_t, void* out, csa_dtype out_t, csa_stream_t stream) {
+    if (batch < 0 || n < 0 || m_prime < 1 || c < 1) return CSA_ERR_INVALID_ARG;
+    if (!C || !Z || !B || !out) return CSA_ERR_INVALID_ARG;
+    if (!aligned16(C) || !aligned16(Z) || !aligned16(B) || !aligned16(out)) return CSA_ERR_INVALID_ARG;
+    if (!io_dtype(in_t) || !io_dtype(out_t)) return CSA_ERR_UNSUPPORTED;
+    if (!width_ok(c) || m_prime > CSA_MAX_RATIO) return CSA_ERR_UNSUPPORTED;
+    if (batch == 0 || n / m_prime == 0) return CSA_OK;
+    return finish(csa::launch_compress(C, Z, B, nullptr, nullptr, nullptr, batch, n, m_prime, c, in_t, out, out_t,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+size_t csa_index_topk_workspace_size(int64_t batch, int64_t T, int64_t N, int H_I, int k) {
+    if (batch < 0 || T < 0 || N < 0 || H_I < 1 || k < 1) return 0;
+    const int64_t rows = batch * T;
+    const size_t scores = round_up((size_t)rows * (size_t)score_ld(N) * sizeof(float));
+    return scores + round_up(csa::topk_extra_workspace(rows, N, k)) + kWsAlign;
+}
+
+int csa_index_topk(const void* qI, const float* w, const void* kI, int64_t batch, int64_t T, int64_t q_pos0, int64_t N,
+                   int H_I, int c_I, int m, int k, csa_dtype qk_t, int32_t* idx, float* sel_scores, void* workspace,
+                   size_t ws_bytes, csa_stream_t stream) {
+    int rc = check_indexer(qI, w, kI, batch, T, q_pos0, N, H_I, c_I, m, qk_t);
+    if (rc != CSA_OK) return rc;
+    if (k < 1 || !idx) return CSA_ERR_INVALID_ARG;
+    if (k > CSA_MAX_TOPK) return CSA_ERR_UNSUPPORTED;
+    if (sel_scores && !aligned16(sel_scores)) return CSA_ERR_INVALID_ARG;
+    const size_t need = csa_index_topk_workspace_size(batch, T, N, H_I, k);
+    if (!workspace || ws_bytes < need || !aligned16(workspace)) return CSA_ERR_WORKSPACE;
+    if (batch == 0 || T == 0) return CSA_OK;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t ld = score_ld(N);
+    float* scores = static_cast<float*>(workspace);
+    const int64_t rows = batch * T;
+    void* extra = static_cast<char*>(workspace) + round_up((size_t)rows * (size_t)ld * sizeof(float));
+    rc = csa::launch_index_scores(qI, w, kI, batch, T, q_pos0, N, H_I, c_I, m, qk_t, scores, ld, false, st);
+    if (rc != 0) return finish(rc);
+    return finish(csa::launch_topk(scores, ld, batch, T, q_pos0, N, m, k, idx, sel_scores, extra, st));
+}
+
+int csa_index_scores(const void* qI, const float* w, const void* kI, int64_t batch, int64_t T, int64_t q_pos0, int64_t N,
+                     int H_I, int c_I, int m, csa_dtype qk_t, float* scores, csa_stream_t stream) {
+    int rc = check_indexer(qI, w, kI, batch, T, q_pos0, N, H_I, c_I, m, qk_t);
+    if (rc != CSA_OK) return rc;
+    if (!scores) return CSA_ERR_INVALID_ARG;
+    if (batch == 0 || T == 0 || N == 0) return CSA_OK;
+    return finish(csa::launch_index_scores(qI, w, kI, batch, T, q_pos0, N, H_I, c_I, m, qk_t, scores, N, true,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+size_t csa_topk_workspace_size(int64_t batch, int64_t T, int64_t N, int k) {
+    if (batch < 0 || T < 0 || N < 0 || k < 1) return 0;
+    return round_up(csa::topk_extra_workspace(batch * T, N, k)) + kWsAlign;
+}
+
+int csa_topk(const float* scores, int64_t ld, int64_t batch, int64_t T, int64_t q_pos0, int64_t N, int m, int k,
+             int32_t* idx, float* sel_scores, void* workspace, size_t ws_bytes, csa_stream_t stream) {
+    if (batch < 0 || T < 0 || N < 0 || q_pos0 < 0 || m < 1 || k < 1) return CSA_ERR_INVALID_ARG;
+    if (!scores || !idx || ld < N || ld % 4 != 0 || !aligned16(scores)) return CSA_ERR_INVALID_ARG;
+    if (sel_scores && !aligned16(sel_scores)) return CSA_ERR_INVALID_ARG;
+    if (k > CSA_MAX_TOPK || m > CSA_MAX_RATIO || N >= (int64_t(1) << 31)) return CSA_ERR_UNSUPPORTED;
+    if (!workspace || ws_bytes < csa_topk_workspace_size(batch, T, N, k) || !aligned16(workspace))
+        return CSA_ERR_WORKSPACE;
+    if (batch == 0 || T == 0) return CSA_OK;
+    return finish(csa::launch_topk(scores, ld, batch, T, q_pos0, N, m, k, idx, sel_scores, workspace,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+int csa_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t batch, int64_t T, int64_t N, int H, int c,
+                   int k, float scale, csa_dtype t, void* out, csa_stream_t stream) {
+    int rc = check_mqa(q, kv, out, batch, T, N, H, c, scale, t);
+    if (rc != CSA_OK) return rc;
+    if (k < 1 || !idx) return CSA_ERR_INVALID_ARG;
+    if (k > CSA_MAX_TOPK) return CSA_ERR_UNSUPPORTED;
+    if (batch == 0 || T == 0) return CSA_OK;
+    return finish(csa::launch_sparse_mqa(q, kv, idx, batch, T, N, H, c, k, scale, t, out,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int hca_dense_mqa(const void* q, const void* kv, int64_t batch, int64_t T, int64_t q_pos0, int64_t N, int H, int c,
+                  int m_prime, float scale, csa_dtype t, void* out, csa_stream_t stream) {
+    int rc = check_mqa(q, kv, out, batch, T, N, H, c, scale, t);
+    if (rc != CSA_OK) return rc;
+    if (m_prime < 1 || q_pos0 < 0) return CSA_ERR_INVALID_ARG;
+    if (m_prime > CSA_MAX_RATIO) return CSA_ERR_UNSUPPORTED;
+    if (batch == 0 || T == 0) return CSA_OK;
+    return finish(csa::launch_dense_mqa(q, kv, batch, T, q_pos0, N, H, c, m_prime, scale, t, out,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

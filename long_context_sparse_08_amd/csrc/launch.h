@@ -1,0 +1,34 @@
+// launch.h — host-side launchers implemented next to their kernels (internal to libcsa).
+// Each returns 0 on success, -2 when the shape/dtype has no kernel.  Arguments were
+// validated by the C-ABI layer (api.cpp) before any of these runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa {
+
+int launch_compress(const void* Ca, const void* Za, const float* Ba, const void* Cb, const void* Zb, const float* Bb,
+                    int64_t batch, int64_t n, int m, int c, int in_t, void* out, int out_t, hipStream_t stream);
+
+// Indexer scores for every (query, entry) pair into `scores` ([batch*T, ld] fp32, ld >= N).
+// write_invisible: also write -inf for entries the query may not see (else they are skipped).
+int launch_index_scores(const void* qI, const float* w, const void* kI, int64_t batch, int64_t T, int64_t q_pos0,
+                        int64_t N, int H_I, int c_I, int m, int qk_t, float* scores, int64_t ld, bool write_invisible,
+                        hipStream_t stream);
+
+// Workspace bytes needed by launch_topk beyond the score rows.
+size_t topk_extra_workspace(int64_t rows, int64_t N, int k);
+
+// Per-row top-k over visible prefix of each score row.
+int launch_topk(const float* scores, int64_t ld, int64_t batch, int64_t T, int64_t q_pos0, int64_t N, int m, int k,
+                int32_t* idx, float* sel, void* extra_ws, hipStream_t stream);
+
+int launch_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t batch, int64_t T, int64_t N, int H,
+                      int c, int k, float scale, int t, void* out, hipStream_t stream);
+
+int launch_dense_mqa(const void* q, const void* kv, int64_t batch, int64_t T, int64_t q_pos0, int64_t N, int H, int c,
+                     int ratio, float scale, int t, void* out, hipStream_t stream);
+
+}  // namespace csa

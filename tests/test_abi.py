@@ -1,0 +1,131 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function include/csa.h
+declares, and rejects invalid calls with the documented status before launching anything
+(pointers used here are never dereferenced: each call fails its host-side checks first)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+A = 0x10000      # a 16-byte aligned fake address, never dereferenced
+MIS = 0x10004    # misaligned fake address
+
+
+@pytest.fixture(scope="module")
+def L():
+    import long_context_sparse_08_amd as pkg
+    return pkg.lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_five_entry_points():
+    names = declared_functions()
+    for n in ("csa_compress", "hca_compress", "csa_index_topk", "csa_sparse_mqa", "hca_dense_mqa",
+              "csa_index_topk_workspace_size", "csa_index_scores", "csa_status_string", "csa_version"):
+        assert n in names, n
+
+
+def test_library_exports_every_declared_symbol(L):
+    lib = ctypes.CDLL(L._name)
+    for n in declared_functions():
+        assert hasattr(lib, n), f"libcsa does not export {n}"
+
+
+def test_version_and_status_strings(L):
+    assert L.csa_version() == 100
+    for s, tag in ((0, "CSA_OK"), (-1, "INVALID"), (-2, "UNSUPPORTED"), (-3, "WORKSPACE"), (-4, "HIP")):
+        assert tag in L.csa_status_string(s).decode()
+    assert "unknown" in L.csa_status_string(7).decode()
+
+
+def test_compress_rejects_bad_arguments(L):
+    f = L.csa_compress
+    good = dict(Ca=A, Cb=A, Za=A, Zb=A, Ba=A, Bb=A, batch=1, n=64, m=4, c=64, in_t=0, out=A, out_t=0)
+
+    def call(**over):
+        a = dict(good, **over)
+        return f(a["Ca"], a["Cb"], a["Za"], a["Zb"], a["Ba"], a["Bb"], a["batch"], a["n"], a["m"], a["c"],
+                 a["in_t"], a["out"], a["out_t"], None)
+
+    assert call(Ca=None) == INVALID
+    assert call(Bb=None) == INVALID
+    assert call(out=None) == INVALID
+    assert call(Za=MIS) == INVALID
+    assert call(batch=-1) == INVALID
+    assert call(m=0) == INVALID
+    assert call(c=60) == UNSUPPORTED           # not a multiple of 8
+    assert call(c=2048) == UNSUPPORTED
+    assert call(m=4096) == UNSUPPORTED
+    assert call(in_t=2) == UNSUPPORTED         # fp8 streams are not a compress input
+    assert call(out_t=5) == UNSUPPORTED
+    assert call(n=3) == OK                     # fewer tokens than one window: nothing to do
+    assert call(batch=0) == OK
+
+
+def test_hca_compress_rejects_bad_arguments(L):
+    f = L.hca_compress
+    assert f(None, A, A, 1, 256, 128, 64, 0, A, 0, None) == INVALID
+    assert f(A, A, A, 1, 256, 0, 64, 0, A, 0, None) == INVALID
+    assert f(A, A, A, 1, 256, 128, 12, 0, A, 0, None) == UNSUPPORTED
+    assert f(A, A, A, 1, 100, 128, 64, 0, A, 0, None) == OK
+
+
+def test_workspace_size(L):
+    ws = L.csa_index_topk_workspace_size
+    assert ws(1, 4, 10, 2, 8) >= 4 * 12 * 4          # rows padded to 4 floats
+    assert ws(32, 1, 32768, 64, 1024) >= 32 * 32768 * 4
+    assert ws(-1, 1, 10, 1, 1) == 0 and ws(1, 1, 10, 1, 0) == 0
+
+
+def test_index_topk_rejects_bad_arguments(L):
+    f = L.csa_index_topk
+    need = L.csa_index_topk_workspace_size(1, 8, 64, 2, 8)
+    good = dict(qI=A, w=A, kI=A, batch=1, T=8, q_pos0=0, N=64, H_I=2, c_I=32, m=4, k=8, t=0, idx=A, sel=A, ws=A,
+                wsb=need)
+
+    def call(**over):
+        a = dict(good, **over)
+        return f(a["qI"], a["w"], a["kI"], a["batch"], a["T"], a["q_pos0"], a["N"], a["H_I"], a["c_I"], a["m"],
+                 a["k"], a["t"], a["idx"], a["sel"], a["ws"], a["wsb"], None)
+
+    assert call(qI=None) == INVALID
+    assert call(idx=None) == INVALID
+    assert call(k=0) == INVALID
+    assert call(q_pos0=-1) == INVALID
+    assert call(sel=MIS) == INVALID
+    assert call(k=4096) == UNSUPPORTED
+    assert call(c_I=20) == UNSUPPORTED
+    assert call(H_I=1000) == UNSUPPORTED
+    assert call(t=3) == UNSUPPORTED
+    assert call(N=1 << 31) == UNSUPPORTED
+    assert call(ws=None) == WORKSPACE
+    assert call(wsb=need - 1) == WORKSPACE
+    assert call(batch=0, wsb=L.csa_index_topk_workspace_size(0, 8, 64, 2, 8)) == OK
+
+
+def test_mqa_rejects_bad_arguments(L):
+    f = L.csa_sparse_mqa
+    assert f(None, A, A, 1, 4, 64, 4, 64, 8, 0.125, 0, A, None) == INVALID
+    assert f(A, A, None, 1, 4, 64, 4, 64, 8, 0.125, 0, A, None) == INVALID
+    assert f(A, A, A, 1, 4, 64, 4, 64, 0, 0.125, 0, A, None) == INVALID
+    assert f(A, A, A, 1, 4, 64, 4, 64, 8, float("nan"), 0, A, None) == INVALID
+    assert f(A, A, A, 1, 4, 64, 4, 64, 8, 0.125, 2, A, None) == UNSUPPORTED
+    assert f(A, A, A, 1, 4, 64, 4, 64, 4096, 0.125, 0, A, None) == UNSUPPORTED
+    assert f(A, A, A, 1, 4, 64, 0, 64, 8, 0.125, 0, A, None) == INVALID
+    assert f(A, A, A, 0, 4, 64, 4, 64, 8, 0.125, 0, A, None) == OK
+    g = L.hca_dense_mqa
+    assert g(A, A, 1, 4, 0, 8, 4, 64, 0, 0.125, 0, A, None) == INVALID
+    assert g(A, A, 1, 4, -5, 8, 4, 64, 128, 0.125, 0, A, None) == INVALID
+    assert g(A, MIS, 1, 4, 0, 8, 4, 64, 128, 0.125, 0, A, None) == INVALID
+    assert g(A, A, 1, 4, 0, 8, 4, 60, 128, 0.125, 0, A, None) == UNSUPPORTED
+    assert g(A, A, 1, 0, 0, 8, 4, 64, 128, 0.125, 0, A, None) == OK

@@ -1,0 +1,132 @@
+"""End-to-end GPU parity on the five workload configurations, through the same pipeline
+objects (and therefore the same kernel launches) the benchmark times.
+
+cfg0 runs the oracle on everything.  The large configs run the GPU at full size and the
+oracle on sampled query rows / sequences (every stage of the oracle chain starts from the
+generator's bytes: the oracle compresses, scores, selects and attends on its own)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from long_context_sparse_08_amd.pipeline import CsaDecode, CsaPrefill, HcaChunk
+from tests._util import (BF16, F32, FP8, assert_abs_close, assert_fp32_close, check_topk_recall, from_dev, say,
+                         to_dev)
+from workloads import CONFIGS, make_inputs, shapes
+
+pytestmark = pytest.mark.gpu
+
+
+def upload(cfg, host):
+    sh = shapes(cfg)
+    return {k: to_dev(v, sh[k][1]) for k, v in host.items()}
+
+
+def oracle_csa_front(cfg, h, rows):
+    """Oracle compress of KV and index keys, then scores / top-k / MQA for query rows `rows`."""
+    dt = cfg.dt
+    kv = oracle.csa_compress(h["Ca"], h["Cb"], h["Za"], h["Zb"], h["Ba"], h["Bb"], cfg.m, in_dtype=dt, out_dtype=dt)
+    kI = oracle.csa_compress(h["ICa"], h["ICb"], h["IZa"], h["IZb"], h["IBa"], h["IBb"], cfg.m, in_dtype=dt,
+                             out_dtype=dt)
+    qpos = cfg.q_pos0 + np.asarray(rows, dtype=np.int64)
+    sc = oracle.index_scores(h["qI"][:, rows], h["w"][:, rows], kI, cfg.m, qk_dtype=cfg.qk_dt, qpos=qpos)
+    idx, sel = oracle.topk(sc, cfg.m, cfg.k, qpos=qpos)
+    out = oracle.sparse_mqa(h["q"][:, rows], kv, idx, cfg.scale, dtype=dt)
+    return kv, kI, sc, idx, sel, out
+
+
+def test_cfg0_tiny_full_forward():
+    cfg = CONFIGS["cfg0_tiny"]
+    say(f"config {cfg.name}: full forward, oracle on every row")
+    h = make_inputs(cfg)
+    pipe = CsaPrefill(upload(cfg, h), cfg.m, cfg.k, cfg.q_pos0)
+    pipe.run()
+    torch.cuda.synchronize()
+    rows = np.arange(cfg.T)
+    kv, kI, sc, idx, sel, out = oracle_csa_front(cfg, h, rows)
+    assert_fp32_close(from_dev(pipe.kv), kv, "KV")
+    assert_fp32_close(from_dev(pipe.kI), kI, "K^I")
+    gidx = from_dev(pipe.idx)
+    # report the smallest k-th / (k+1)-th oracle score gap, so a mismatch can be told from a tie
+    gaps = []
+    for t in range(cfg.T):
+        v = np.sort(sc[0, t][np.isfinite(sc[0, t])])[::-1]
+        if len(v) > cfg.k:
+            gaps.append(v[cfg.k - 1] - v[cfg.k])
+    say(f"  min k-th/(k+1)-th score gap: {min(g for g in gaps if g > 0):.3e}")
+    assert np.array_equal(gidx, idx), np.argwhere(gidx != idx)[:5]
+    gsel = from_dev(pipe.sel)
+    fin = np.isfinite(sel)
+    assert np.array_equal(np.isfinite(gsel), fin)
+    assert_fp32_close(gsel[fin], sel[fin], "sel_scores")
+    assert_fp32_close(from_dev(pipe.out), out, "O")
+
+
+@pytest.mark.timeout(900)
+def test_cfg1_csa_prefill_sampled():
+    cfg = CONFIGS["cfg1_csa_prefill"]
+    say(f"config {cfg.name}: GPU full size, oracle on sampled rows")
+    h = make_inputs(cfg)
+    pipe = CsaPrefill(upload(cfg, h), cfg.m, cfg.k, cfg.q_pos0)
+    pipe.run()
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, 8), [2047, 2048, 2051, 4095], np.arange(8192 - 6, 8192),
+                                     np.random.RandomState(1).choice(8192, 24, replace=False)]))
+    kv, kI, sc, idx, sel, out = oracle_csa_front(cfg, h, rows)
+    gkv, gkI = from_dev(pipe.kv), from_dev(pipe.kI)
+    assert_abs_close(gkv, kv, 2e-2, "KV (bf16)")
+    assert_abs_close(gkI, kI, 2e-2, "K^I (bf16)")
+    say(f"  KV equal to oracle rounding: {np.mean(gkv == kv):.5f}")
+    assert np.mean(gkv == kv) >= 0.999
+    gidx = from_dev(pipe.idx)[0, rows]
+    check_topk_recall(gidx, idx[0], sc[0], cfg.k, what="top-k")
+    assert_abs_close(from_dev(pipe.out)[0, rows], out[0], 2e-2, "O")
+
+
+def _decode_case(name, seqs):
+    cfg = CONFIGS[name]
+    say(f"config {cfg.name}: GPU full size, oracle on sequences {list(seqs)}")
+    h = make_inputs(cfg)
+    pipe = CsaDecode(upload(cfg, h), cfg.m, cfg.k, cfg.q_pos0)
+    pipe.run()
+    torch.cuda.synchronize()
+    sub = {k: h[k][seqs] for k in ("kv", "kI", "q", "qI", "w")}
+    sc = oracle.index_scores(sub["qI"], sub["w"], sub["kI"], cfg.m, q_pos0=cfg.q_pos0, qk_dtype=cfg.qk_dt)
+    idx, sel = oracle.topk(sc, cfg.m, cfg.k, q_pos0=cfg.q_pos0)
+    out = oracle.sparse_mqa(sub["q"], sub["kv"], idx, cfg.scale, dtype=cfg.dt)
+    gidx = from_dev(pipe.idx)[seqs]
+    check_topk_recall(gidx.reshape(-1, cfg.k), idx.reshape(-1, cfg.k), sc.reshape(-1, sc.shape[-1]), cfg.k,
+                      what="top-k")
+    gsel = from_dev(pipe.sel)[seqs]
+    same = gidx == idx
+    assert_abs_close(gsel[same], sel[same], 2e-2, "sel_scores where ids agree")
+    assert_abs_close(from_dev(pipe.out)[seqs], out, 2e-2, "O")
+
+
+@pytest.mark.timeout(900)
+def test_cfg2_csa_decode_128k_sampled():
+    _decode_case("cfg2_csa_decode_128k", np.array([0, 7, 19, 31]))
+
+
+@pytest.mark.timeout(900)
+def test_cfg4_csa_decode_1m_sampled():
+    _decode_case("cfg4_csa_decode_1m", np.array([0, 5]))
+
+
+@pytest.mark.timeout(900)
+def test_cfg3_hca_chunk_sampled():
+    cfg = CONFIGS["cfg3_hca_chunk_1m"]
+    say(f"config {cfg.name}: GPU full size, oracle compress in full and MQA on sampled rows")
+    h = make_inputs(cfg)
+    pipe = HcaChunk(upload(cfg, h), cfg.m_prime, cfg.q_pos0)
+    pipe.run()
+    torch.cuda.synchronize()
+    kv = oracle.hca_compress(h["C"], h["Z"], h["B"], cfg.m_prime, in_dtype=cfg.dt, out_dtype=cfg.dt)
+    gkv = from_dev(pipe.kv)
+    assert_abs_close(gkv, kv, 2e-2, "HCA KV (bf16)")
+    say(f"  KV equal to oracle rounding: {np.mean(gkv == kv):.5f}")
+    assert np.mean(gkv == kv) >= 0.999
+    rows = np.array([0, 1, 126, 127, 128, 2047, 2048, 4094, 4095])
+    qpos = cfg.q_pos0 + rows
+    out = oracle.hca_dense_mqa(h["q"][:, rows], kv, cfg.m_prime, cfg.scale, dtype=cfg.dt, qpos=qpos)
+    assert_abs_close(from_dev(pipe.out)[:, rows], out, 2e-2, "O")
