@@ -20,6 +20,8 @@
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null stream).  The
  *     library never allocates device memory, never synchronises, and holds no mutable global
  *     state, so calls on different streams may overlap freely.
+ *   - A tensor with zero elements may be passed as NULL (calls with an empty output return
+ *     CSA_OK after the size and dtype checks and launch nothing).
  *   - Return value: CSA_OK or a negative csa_status.  All argument checks run on the host
  *     before anything is launched; an invalid call launches nothing and writes nothing.
  *     CSA_ERR_HIP reports a launch failure (hipGetLastError); faults inside a kernel surface
@@ -149,10 +151,15 @@ int csa_topk(const float* scores, int64_t ld, int64_t batch, int64_t T, int64_t 
  *   kv  : [batch, N, c]     dtype t
  *   idx : [batch, T, k]     int32
  *   out : [batch, T, H, c]  dtype t
+ *   workspace : device scratch of at least csa_sparse_mqa_workspace_size(...) bytes (may be
+ *               NULL when that size is 0), 16-byte aligned; holds per-key-range partial
+ *               results when a query's keys are split over several workgroups.
  * Limits: c % 8 == 0, c <= CSA_MAX_WIDTH, 1 <= H <= CSA_MAX_HEADS, 1 <= k <= CSA_MAX_TOPK.
  */
+size_t csa_sparse_mqa_workspace_size(int64_t batch, int64_t T, int H, int c, int k, csa_dtype t);
 int csa_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t batch, int64_t T, int64_t N, int H,
-                   int c, int k, float scale, csa_dtype t, void* out, csa_stream_t stream);
+                   int c, int k, float scale, csa_dtype t, void* out, void* workspace, size_t ws_bytes,
+                   csa_stream_t stream);
 
 /*
  * hca_dense_mqa — dense causal shared-KV MQA over every visible HCA entry ([M] §2.3.2; [N]

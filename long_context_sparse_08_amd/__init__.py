@@ -21,7 +21,7 @@ STATUS = {0: "CSA_OK", -1: "CSA_ERR_INVALID_ARG", -2: "CSA_ERR_UNSUPPORTED", -3:
           -4: "CSA_ERR_HIP"}
 
 ENTRY_POINTS = ("csa_compress", "hca_compress", "csa_index_topk_workspace_size", "csa_index_topk",
-                "csa_index_scores", "csa_topk_workspace_size", "csa_topk", "csa_sparse_mqa", "hca_dense_mqa",
+                "csa_index_scores", "csa_topk_workspace_size", "csa_topk", "csa_sparse_mqa_workspace_size", "csa_sparse_mqa", "hca_dense_mqa",
                 "csa_status_string", "csa_version")
 
 
@@ -44,7 +44,8 @@ def _load():
         "csa_index_scores": ([P, P, P, I64, I64, I64, I64, I, I, I, I, P, P], I),
         "csa_topk_workspace_size": ([I64, I64, I64, I], SZ),
         "csa_topk": ([P, I64, I64, I64, I64, I64, I, I, P, P, P, SZ, P], I),
-        "csa_sparse_mqa": ([P, P, P, I64, I64, I64, I, I, I, F, I, P, P], I),
+        "csa_sparse_mqa_workspace_size": ([I64, I64, I, I, I, I], SZ),
+        "csa_sparse_mqa": ([P, P, P, I64, I64, I64, I, I, I, F, I, P, P, SZ, P], I),
         "hca_dense_mqa": ([P, P, I64, I64, I64, I64, I, I, I, F, I, P, P], I),
         "csa_status_string": ([I], ctypes.c_char_p),
         "csa_version": ([], I),
@@ -189,9 +190,19 @@ def csa_topk(scores, q_pos0: int, m: int, k: int, idx=None, sel_scores=None, wor
     return idx, sel_scores
 
 
-def csa_sparse_mqa(q, kv, idx, scale: float, out=None):
+def csa_sparse_mqa_workspace_size(batch: int, T: int, H: int, c: int, k: int, dtype: int) -> int:
+    return int(lib.csa_sparse_mqa_workspace_size(batch, T, H, c, k, dtype))
+
+
+def mqa_workspace_for(q: torch.Tensor, k: int):
+    batch, T, H, c = q.shape
+    nbytes = csa_sparse_mqa_workspace_size(batch, T, H, c, k, _dt(q))
+    return None if nbytes == 0 else torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+
+
+def csa_sparse_mqa(q, kv, idx, scale: float, out=None, workspace=None):
     """q [batch, T, H, c], kv [batch, N, c], idx [batch, T, k] int32 -> out [batch, T, H, c]."""
-    dev = _dev(q, kv, idx, out)
+    dev = _dev(q, kv, idx, out, workspace)
     batch, T, H, c = q.shape
     N = kv.shape[1]
     k = idx.shape[2]
@@ -199,8 +210,11 @@ def csa_sparse_mqa(q, kv, idx, scale: float, out=None):
     assert idx.shape == (batch, T, k)
     if out is None:
         out = torch.empty_like(q)
+    if workspace is None:
+        workspace = mqa_workspace_for(q, k)
+    ws_bytes = 0 if workspace is None else workspace.numel()
     _check("csa_sparse_mqa", lib.csa_sparse_mqa(_p(q), _p(kv), _p(idx), batch, T, N, H, c, k, float(scale), _dt(q),
-                                                _p(out), _stream(dev)))
+                                                _p(out), _p(workspace), ws_bytes, _stream(dev)))
     return out
 
 

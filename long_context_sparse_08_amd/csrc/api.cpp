@@ -32,22 +32,24 @@ int check_indexer(const void* qI, const float* w, const void* kI, int64_t batch,
                   int H_I, int c_I, int m, csa_dtype qk_t) {
     if (batch < 0 || T < 0 || N < 0 || q_pos0 < 0) return CSA_ERR_INVALID_ARG;
     if (m < 1 || H_I < 1 || c_I < 1) return CSA_ERR_INVALID_ARG;
-    if (!qI || !w || !kI) return CSA_ERR_INVALID_ARG;
-    if (!aligned16(qI) || !aligned16(kI) || !aligned16(w)) return CSA_ERR_INVALID_ARG;
     if (qk_t != CSA_F32 && qk_t != CSA_BF16 && qk_t != CSA_FP8_E4M3) return CSA_ERR_UNSUPPORTED;
     if (!width_ok(c_I) || H_I > CSA_MAX_HEADS || m > CSA_MAX_RATIO) return CSA_ERR_UNSUPPORTED;
     if (N >= (int64_t(1) << 31)) return CSA_ERR_UNSUPPORTED;
+    if (batch * T == 0) return CSA_OK;   // nothing to compute: pointers may be NULL
+    if (!qI || !w || (N > 0 && !kI)) return CSA_ERR_INVALID_ARG;
+    if (!aligned16(qI) || !aligned16(kI) || !aligned16(w)) return CSA_ERR_INVALID_ARG;
     return CSA_OK;
 }
 
 int check_mqa(const void* q, const void* kv, void* out, int64_t batch, int64_t T, int64_t N, int H, int c, float scale,
               csa_dtype t) {
     if (batch < 0 || T < 0 || N < 0 || H < 1 || c < 1) return CSA_ERR_INVALID_ARG;
-    if (!q || !kv || !out) return CSA_ERR_INVALID_ARG;
-    if (!aligned16(q) || !aligned16(kv) || !aligned16(out)) return CSA_ERR_INVALID_ARG;
     if (!isfinite(scale)) return CSA_ERR_INVALID_ARG;
     if (!io_dtype(t)) return CSA_ERR_UNSUPPORTED;
     if (!width_ok(c) || H > CSA_MAX_HEADS) return CSA_ERR_UNSUPPORTED;
+    if (batch * T == 0) return CSA_OK;   // nothing to compute: pointers may be NULL
+    if (!q || (N > 0 && !kv) || !out) return CSA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(kv) || !aligned16(out)) return CSA_ERR_INVALID_ARG;
     return CSA_OK;
 }
 
@@ -72,13 +74,13 @@ int csa_compress(const void* Ca, const void* Cb, const void* Za, const void* Zb,
                  int64_t batch, int64_t n, int m, int c, csa_dtype in_t, void* out, csa_dtype out_t,
                  csa_stream_t stream) {
     if (batch < 0 || n < 0 || m < 1 || c < 1) return CSA_ERR_INVALID_ARG;
+    if (!io_dtype(in_t) || !io_dtype(out_t)) return CSA_ERR_UNSUPPORTED;
+    if (!width_ok(c) || m > CSA_MAX_RATIO) return CSA_ERR_UNSUPPORTED;
+    if (batch == 0 || n / m == 0) return CSA_OK;   // empty output: pointers may be NULL
     if (!Ca || !Cb || !Za || !Zb || !Ba || !Bb || !out) return CSA_ERR_INVALID_ARG;
     if (!aligned16(Ca) || !aligned16(Cb) || !aligned16(Za) || !aligned16(Zb) || !aligned16(Ba) || !aligned16(Bb) ||
         !aligned16(out))
         return CSA_ERR_INVALID_ARG;
-    if (!io_dtype(in_t) || !io_dtype(out_t)) return CSA_ERR_UNSUPPORTED;
-    if (!width_ok(c) || m > CSA_MAX_RATIO) return CSA_ERR_UNSUPPORTED;
-    if (batch == 0 || n / m == 0) return CSA_OK;
     return finish(csa::launch_compress(Ca, Za, Ba, Cb, Zb, Bb, batch, n, m, c, in_t, out, out_t,
                                        static_cast<hipStream_t>(stream)));
 }
@@ -86,11 +88,11 @@ int csa_compress(const void* Ca, const void* Cb, const void* Za, const void* Zb,
 int hca_compress(const void* C, const void* Z, const float* B, int64_t batch, int64_t n, int m_prime, int c,
                  csa_dtype in_t, void* out, csa_dtype out_t, csa_stream_t stream) {
     if (batch < 0 || n < 0 || m_prime < 1 || c < 1) return CSA_ERR_INVALID_ARG;
-    if (!C || !Z || !B || !out) return CSA_ERR_INVALID_ARG;
-    if (!aligned16(C) || !aligned16(Z) || !aligned16(B) || !aligned16(out)) return CSA_ERR_INVALID_ARG;
     if (!io_dtype(in_t) || !io_dtype(out_t)) return CSA_ERR_UNSUPPORTED;
     if (!width_ok(c) || m_prime > CSA_MAX_RATIO) return CSA_ERR_UNSUPPORTED;
-    if (batch == 0 || n / m_prime == 0) return CSA_OK;
+    if (batch == 0 || n / m_prime == 0) return CSA_OK;   // empty output: pointers may be NULL
+    if (!C || !Z || !B || !out) return CSA_ERR_INVALID_ARG;
+    if (!aligned16(C) || !aligned16(Z) || !aligned16(B) || !aligned16(out)) return CSA_ERR_INVALID_ARG;
     return finish(csa::launch_compress(C, Z, B, nullptr, nullptr, nullptr, batch, n, m_prime, c, in_t, out, out_t,
                                        static_cast<hipStream_t>(stream)));
 }
@@ -107,12 +109,13 @@ int csa_index_topk(const void* qI, const float* w, const void* kI, int64_t batch
                    size_t ws_bytes, csa_stream_t stream) {
     int rc = check_indexer(qI, w, kI, batch, T, q_pos0, N, H_I, c_I, m, qk_t);
     if (rc != CSA_OK) return rc;
-    if (k < 1 || !idx) return CSA_ERR_INVALID_ARG;
+    if (k < 1) return CSA_ERR_INVALID_ARG;
     if (k > CSA_MAX_TOPK) return CSA_ERR_UNSUPPORTED;
+    if (batch == 0 || T == 0) return CSA_OK;
+    if (!idx) return CSA_ERR_INVALID_ARG;
     if (sel_scores && !aligned16(sel_scores)) return CSA_ERR_INVALID_ARG;
     const size_t need = csa_index_topk_workspace_size(batch, T, N, H_I, k);
     if (!workspace || ws_bytes < need || !aligned16(workspace)) return CSA_ERR_WORKSPACE;
-    if (batch == 0 || T == 0) return CSA_OK;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int64_t ld = score_ld(N);
     float* scores = static_cast<float*>(workspace);
@@ -127,8 +130,8 @@ int csa_index_scores(const void* qI, const float* w, const void* kI, int64_t bat
                      int H_I, int c_I, int m, csa_dtype qk_t, float* scores, csa_stream_t stream) {
     int rc = check_indexer(qI, w, kI, batch, T, q_pos0, N, H_I, c_I, m, qk_t);
     if (rc != CSA_OK) return rc;
-    if (!scores) return CSA_ERR_INVALID_ARG;
     if (batch == 0 || T == 0 || N == 0) return CSA_OK;
+    if (!scores) return CSA_ERR_INVALID_ARG;
     return finish(csa::launch_index_scores(qI, w, kI, batch, T, q_pos0, N, H_I, c_I, m, qk_t, scores, N, true,
                                            static_cast<hipStream_t>(stream)));
 }
@@ -140,25 +143,34 @@ size_t csa_topk_workspace_size(int64_t batch, int64_t T, int64_t N, int k) {
 
 int csa_topk(const float* scores, int64_t ld, int64_t batch, int64_t T, int64_t q_pos0, int64_t N, int m, int k,
              int32_t* idx, float* sel_scores, void* workspace, size_t ws_bytes, csa_stream_t stream) {
-    if (batch < 0 || T < 0 || N < 0 || q_pos0 < 0 || m < 1 || k < 1) return CSA_ERR_INVALID_ARG;
-    if (!scores || !idx || ld < N || ld % 4 != 0 || !aligned16(scores)) return CSA_ERR_INVALID_ARG;
-    if (sel_scores && !aligned16(sel_scores)) return CSA_ERR_INVALID_ARG;
+    if (batch < 0 || T < 0 || N < 0 || q_pos0 < 0 || m < 1 || k < 1 || ld < N || ld % 4 != 0)
+        return CSA_ERR_INVALID_ARG;
     if (k > CSA_MAX_TOPK || m > CSA_MAX_RATIO || N >= (int64_t(1) << 31)) return CSA_ERR_UNSUPPORTED;
+    if (batch == 0 || T == 0) return CSA_OK;
+    if (!idx || (N > 0 && !scores) || !aligned16(scores)) return CSA_ERR_INVALID_ARG;
+    if (sel_scores && !aligned16(sel_scores)) return CSA_ERR_INVALID_ARG;
     if (!workspace || ws_bytes < csa_topk_workspace_size(batch, T, N, k) || !aligned16(workspace))
         return CSA_ERR_WORKSPACE;
-    if (batch == 0 || T == 0) return CSA_OK;
     return finish(csa::launch_topk(scores, ld, batch, T, q_pos0, N, m, k, idx, sel_scores, workspace,
                                    static_cast<hipStream_t>(stream)));
 }
 
+size_t csa_sparse_mqa_workspace_size(int64_t batch, int64_t T, int H, int c, int k, csa_dtype t) {
+    if (batch < 0 || T < 0 || H < 1 || c < 1 || k < 1) return 0;
+    return csa::sparse_mqa_workspace(batch, T, H, c, k, t);
+}
+
 int csa_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t batch, int64_t T, int64_t N, int H, int c,
-                   int k, float scale, csa_dtype t, void* out, csa_stream_t stream) {
+                   int k, float scale, csa_dtype t, void* out, void* workspace, size_t ws_bytes, csa_stream_t stream) {
     int rc = check_mqa(q, kv, out, batch, T, N, H, c, scale, t);
     if (rc != CSA_OK) return rc;
-    if (k < 1 || !idx) return CSA_ERR_INVALID_ARG;
+    if (k < 1) return CSA_ERR_INVALID_ARG;
     if (k > CSA_MAX_TOPK) return CSA_ERR_UNSUPPORTED;
     if (batch == 0 || T == 0) return CSA_OK;
-    return finish(csa::launch_sparse_mqa(q, kv, idx, batch, T, N, H, c, k, scale, t, out,
+    if (!idx) return CSA_ERR_INVALID_ARG;
+    const size_t need = csa_sparse_mqa_workspace_size(batch, T, H, c, k, t);
+    if (need > 0 && (!workspace || ws_bytes < need || !aligned16(workspace))) return CSA_ERR_WORKSPACE;
+    return finish(csa::launch_sparse_mqa(q, kv, idx, batch, T, N, H, c, k, scale, t, out, workspace,
                                          static_cast<hipStream_t>(stream)));
 }
 

@@ -4,8 +4,8 @@
 // before the query).  fp32 accumulation, ReLU(x) = max(x, +0), no scale factor.
 //
 // Kernels:
-//   index_scores_generic  any dtype / head count: VALU dot products, q of one query in LDS.
-//   (the MFMA kernels for the large prefill and decode shapes live further down)
+//   index_scores_mfma     c_I = 128, H_I in {32, 64}, bf16 or fp8: matrix cores (below).
+//   index_scores_generic  any other dtype / shape: VALU dot products, q of one query in LDS.
 #include "device_common.h"
 #include "launch.h"
 
@@ -82,12 +82,184 @@ int launch_generic(const void* qI, const float* w, const void* kI, int64_t batch
     return 0;
 }
 
+
+// ============================================================================ MFMA kernel
+// Scores for c_I = 128 and H_I = 32 * MB heads with v_mfma_f32_32x32x16 (bf16 or fp8 e4m3).
+// Heads sit on the MFMA M dimension and 32 entries on N, so one 32x32 accumulator holds 32
+// heads x 32 entries and the ReLU * w head-sum runs in-lane over a lane's 16 heads plus one
+// cross-lane add (lane l and l^32 hold the two halves of an entry's heads).
+//
+// Operand layout: lane l takes entry (or head) l%32 and the contiguous half g = l/32 of the
+// 128-wide key (64 bytes fp8, 128 bytes bf16), read as 16-byte loads.  MFMA step j (K = 16)
+// feeds elements [8j, 8j+8) of that half.  q and k use the same (g, j) -> channel map, so the
+// dot product is over the right pairs whatever order the unit sums its K slots in.
+//
+// Accumulator layout (32x32, f32): lane l holds column n = l%32 and rows
+// m = 8*(r/4) + 4*(l/32) + r%4 for r = 0..15.
+//
+// TOK = 1 (decode): the 4 waves of a workgroup take interleaved 32-entry blocks of one query.
+// TOK = 4 (prefill): wave w takes query t0 + w; all four read the same key blocks (L1 hits).
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kMfmaCI = 128;
+
+template <int DT>
+struct IdxOps;
+
+template <>
+struct IdxOps<DT_FP8> {
+    static constexpr int kLoads = 4;      // 16-byte loads per half row (64 fp8)
+    static constexpr int kEsz = 1;
+    struct Frag { uint4 v[kLoads]; };
+    static __device__ __forceinline__ f32x16 mma(const Frag& a, const Frag& b, f32x16 acc) {
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) {
+            const long a0 = (long)(((unsigned long)a.v[i].y << 32) | a.v[i].x);
+            const long a1 = (long)(((unsigned long)a.v[i].w << 32) | a.v[i].z);
+            const long b0 = (long)(((unsigned long)b.v[i].y << 32) | b.v[i].x);
+            const long b1 = (long)(((unsigned long)b.v[i].w << 32) | b.v[i].z);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a0, b0, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a1, b1, acc, 0, 0, 0);
+        }
+        return acc;
+    }
+};
+
+template <>
+struct IdxOps<DT_BF16> {
+    static constexpr int kLoads = 8;      // 16-byte loads per half row (64 bf16)
+    static constexpr int kEsz = 2;
+    struct Frag { uint4 v[kLoads]; };
+    static __device__ __forceinline__ f32x16 mma(const Frag& a, const Frag& b, f32x16 acc) {
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) {
+            const bf16x8 av = __builtin_bit_cast(bf16x8, a.v[i]);
+            const bf16x8 bv = __builtin_bit_cast(bf16x8, b.v[i]);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+        }
+        return acc;
+    }
+};
+
+template <int DT>
+__device__ __forceinline__ void load_half_row(const void* __restrict__ base, int64_t row, int g,
+                                              typename IdxOps<DT>::Frag& f) {
+    using O = IdxOps<DT>;
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(base) +
+                                                    (row * kMfmaCI + g * (kMfmaCI / 2)) * O::kEsz);
+#pragma unroll
+    for (int i = 0; i < O::kLoads; ++i) f.v[i] = p[i];
+}
+
+template <int DT, int MB, int TOK>
+__global__ void __launch_bounds__(256)
+index_scores_mfma(const void* __restrict__ qI, const float* __restrict__ w, const void* __restrict__ kI, int64_t batch,
+                  int64_t T, int64_t q_pos0, int64_t N, int m, float* __restrict__ scores, int64_t ld,
+                  int write_invisible, int chunks, int cb) {
+    using O = IdxOps<DT>;
+    constexpr int H = 32 * MB;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int g = lane >> 5, n = lane & 31;
+    const int64_t groups = (T + TOK - 1) / TOK;
+    const int64_t unit = blockIdx.x;
+    const int chunk = (int)(unit % chunks);
+    const int64_t bg = unit / chunks;
+    const int64_t b = bg / groups, tg = bg - b * groups;
+    const int64_t t = TOK == 1 ? tg : tg * TOK + wid;
+    if (b >= batch || t >= T) return;
+    const int64_t row = b * T + t;
+    const int64_t nv = visible_entries(q_pos0 + t, m, N);
+    const int64_t nblk_all = (N + 31) / 32;
+
+    // per-wave block list
+    const int64_t blk0 = (int64_t)chunk * cb;
+    const int64_t blk1 = min(blk0 + cb, nblk_all);
+    const int first = TOK == 1 ? wid : 0;
+    const int step = TOK == 1 ? 4 : 1;
+    float* out = scores + row * ld;
+
+    // q of this token (A operands) and the w of the heads this lane's accumulator rows hold
+    typename O::Frag qa[MB];
+    float wv[MB][16];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        load_half_row<DT>(qI, row * H + 32 * mb + n, g, qa[mb]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) wv[mb][r] = w[row * H + 32 * mb + 8 * (r >> 2) + 4 * g + (r & 3)];
+    }
+
+    const int64_t kbase = b * N;
+    int64_t blk = blk0 + first;
+    typename O::Frag kb;
+    if (blk < blk1 && blk * 32 < nv) load_half_row<DT>(kI, kbase + min(blk * 32 + n, N - 1), g, kb);
+    for (; blk < blk1; blk += step) {
+        const int64_t s = blk * 32 + n;
+        if (blk * 32 >= nv) {   // block wholly invisible (uniform over the wave)
+            if (write_invisible && g == 0 && s < N) out[s] = -INFINITY;
+            continue;
+        }
+        typename O::Frag cur = kb;
+        const int64_t nxt = blk + step;
+        if (nxt < blk1 && nxt * 32 < nv) load_half_row<DT>(kI, kbase + min(nxt * 32 + n, N - 1), g, kb);
+        float contrib = 0.f;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            f32x16 acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            acc = O::mma(qa[mb], cur, acc);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) contrib = fmaf(wv[mb][r], fmaxf(acc[r], 0.f), contrib);
+        }
+        contrib += __shfl_xor(contrib, 32, kWave);
+        if (g == 0 && s < N) {
+            if (s < nv) out[s] = contrib;
+            else if (write_invisible) out[s] = -INFINITY;
+        }
+    }
+}
+
+template <int DT, int MB>
+int launch_mfma(const void* qI, const float* w, const void* kI, int64_t batch, int64_t T, int64_t q_pos0, int64_t N,
+                int m, float* scores, int64_t ld, bool write_invisible, hipStream_t stream) {
+    const int64_t nblk = (N + 31) / 32;
+    if (T >= 4) {
+        // prefill: 4 queries per workgroup share the key blocks
+        const int64_t groups = batch * ((T + 3) / 4);
+        const int cb = 16;
+        const int chunks = (int)((nblk + cb - 1) / cb);
+        const int64_t grid = groups * chunks;
+        if (grid > 0x7fffffffLL) return -2;
+        hipLaunchKernelGGL((index_scores_mfma<DT, MB, 4>), dim3((unsigned)grid), dim3(256), 0, stream, qI, w, kI, batch,
+                           T, q_pos0, N, m, scores, ld, write_invisible ? 1 : 0, chunks, cb);
+    } else {
+        // decode: split each query's entries across many workgroups (16 blocks = 512 entries each)
+        const int cb = 16;
+        const int chunks = (int)((nblk + cb - 1) / cb);
+        const int64_t grid = batch * T * chunks;
+        if (grid > 0x7fffffffLL) return -2;
+        hipLaunchKernelGGL((index_scores_mfma<DT, MB, 1>), dim3((unsigned)grid), dim3(256), 0, stream, qI, w, kI, batch,
+                           T, q_pos0, N, m, scores, ld, write_invisible ? 1 : 0, chunks, cb);
+    }
+    return 0;
+}
+
 }  // namespace
 
 int launch_index_scores(const void* qI, const float* w, const void* kI, int64_t batch, int64_t T, int64_t q_pos0,
                         int64_t N, int H_I, int c_I, int m, int qk_t, float* scores, int64_t ld, bool write_invisible,
                         hipStream_t stream) {
     if (batch == 0 || T == 0 || N == 0) return 0;
+    if (c_I == kMfmaCI && (H_I == 32 || H_I == 64) && (qk_t == DT_FP8 || qk_t == DT_BF16)) {
+        if (qk_t == DT_FP8)
+            return H_I == 64 ? launch_mfma<DT_FP8, 2>(qI, w, kI, batch, T, q_pos0, N, m, scores, ld, write_invisible,
+                                                      stream)
+                             : launch_mfma<DT_FP8, 1>(qI, w, kI, batch, T, q_pos0, N, m, scores, ld, write_invisible,
+                                                      stream);
+        return H_I == 64 ? launch_mfma<DT_BF16, 2>(qI, w, kI, batch, T, q_pos0, N, m, scores, ld, write_invisible,
+                                                   stream)
+                         : launch_mfma<DT_BF16, 1>(qI, w, kI, batch, T, q_pos0, N, m, scores, ld, write_invisible,
+                                                   stream);
+    }
     switch (qk_t) {
         case DT_F32:
             return launch_generic<DT_F32>(qI, w, kI, batch, T, q_pos0, N, H_I, c_I, m, scores, ld, write_invisible,

@@ -25,8 +25,11 @@ size_t topk_extra_workspace(int64_t rows, int64_t N, int k);
 int launch_topk(const float* scores, int64_t ld, int64_t batch, int64_t T, int64_t q_pos0, int64_t N, int m, int k,
                 int32_t* idx, float* sel, void* extra_ws, hipStream_t stream);
 
+// Device workspace bytes launch_sparse_mqa needs (0: none) for the key-range partials.
+size_t sparse_mqa_workspace(int64_t batch, int64_t T, int H, int c, int k, int t);
+
 int launch_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t batch, int64_t T, int64_t N, int H,
-                      int c, int k, float scale, int t, void* out, hipStream_t stream);
+                      int c, int k, float scale, int t, void* out, void* ws, hipStream_t stream);
 
 int launch_dense_mqa(const void* q, const void* kv, int64_t batch, int64_t T, int64_t q_pos0, int64_t N, int H, int c,
                      int ratio, float scale, int t, void* out, hipStream_t stream);

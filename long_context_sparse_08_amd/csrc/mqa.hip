@@ -7,10 +7,12 @@
 // over s in idx[t] (CSA, sparse) or over every visible HCA entry (dense, causal).
 //
 // mqa_generic: one wave per (query, head), lanes across channels, online softmax over the
-// entries four at a time, fp32 throughout.  Works for any c % 8 == 0 up to 1024.  The MFMA
-// kernels for the large shapes are further down.
+// entries four at a time, fp32 throughout.  Works for any c % 8 == 0 up to 1024.
+// mqa_sparse_mfma: bf16, c = 512, H % 64 == 0 on matrix cores (further down).
 #include "device_common.h"
 #include "launch.h"
+
+#define CSA_MAX_TOPK_DEV 2048
 
 namespace csa {
 
@@ -111,11 +113,287 @@ int launch_generic(const void* q, const void* kv, const int32_t* idx, int64_t ba
     return -2;
 }
 
+
+// ============================================================================ MFMA kernel
+// Sparse MQA for bf16, c = 512, H % 64 == 0 (the workload shapes), on v_mfma_f32_16x16x32_bf16.
+//
+// Workgroup = (query row, 64 heads, one contiguous range of key slots).  Its 4 waves own 16
+// heads each and walk the same 32-key blocks: the selected KV rows of a block are gathered
+// straight from global memory into LDS (global_load_lds_dwordx4: one 1 KB row per
+// instruction, no registers), double-buffered, so block j+1 loads while block j computes.
+//
+//   S^T = KV_blk . Q^T   M = 16 keys, N = 16 heads, K = c.  A = KV rows from LDS (16-byte
+//                        reads), B = this wave's q, held in registers for the whole kernel.
+//   online softmax       per head (accumulator column), exp2 domain, fp32.
+//   O^T += V^T . P^T     M = 16 columns of c, N = 16 heads, K = 32 keys.  B = P straight from
+//                        the S^T accumulators (bf16), A = V^T read with the gfx950 transpose
+//                        LDS read (ds_read_b64_tr_b16: 4 consecutive keys of one column).
+//
+// K and V are the same rows (shared-KV MQA), so one staged block serves both products.  Key
+// slot <-> MFMA K index: the S^T accumulator gives lane group g the keys {4g..4g+3} of each
+// 16-key half; P^T uses them as K slots (g, e) = key 4g+e (e < 4) or 16+4g+(e-4), and the
+// V^T operand is read with exactly that map.
+//
+// Accumulator layout (16x16 f32): lane l holds column n = l%16, rows 4*(l/16) + i, i = 0..3.
+// With several key ranges per row (few rows, e.g. decode), each workgroup writes its
+// unnormalised partial (acc, running max, running sum) and mqa_combine merges them.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(1))) void* glb_void_ptr;
+
+constexpr int kMC = 512;                       // head dim handled by the MFMA kernel
+constexpr int kMHeadsWG = 64;                  // heads per workgroup (16 per wave)
+constexpr int kMBlk = 32;                      // keys per staged block
+constexpr int kMPitch = kMC * 2 + 32;          // LDS bytes per staged row (bank spread)
+constexpr int kMBuf = kMBlk * kMPitch;         // bytes per staged block
+constexpr int kMColBlk = kMC / 16;             // 16-column blocks of the output
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return f32_to_bf16_rne(a) | (f32_to_bf16_rne(b) << 16);
+}
+
+// DENSE: the key list of the query at position p is 0 .. nv-1 with nv the number of HCA
+// entries it may see (ratio*(s+1)-1 <= p); `k` is then unused.
+template <bool DENSE>
+__global__ void __launch_bounds__(256)
+mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
+                int64_t rows, int64_t T, int64_t N, int H, int k, int ks_count, int keys_per_split, float sl2,
+                int64_t q_pos0, int ratio, uint16_t* __restrict__ out, float* __restrict__ part,
+                float* __restrict__ part_ml) {
+    __shared__ __attribute__((aligned(16))) uint8_t stage[2 * kMBuf];
+    __shared__ int32_t ids[DENSE ? 1 : CSA_MAX_TOPK_DEV];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int g = lane >> 4, n16 = lane & 15;
+    const int HG = H / kMHeadsWG;
+    // XCD-aware order: consecutive units of a row go to one XCD (workgroups are dealt
+    // round-robin over the 8 XCDs), so they share that XCD's L2 for the row's KV.
+    const int64_t x = blockIdx.x;
+    const int64_t per_row = (int64_t)HG * ks_count;
+    const int64_t slot = x / 8, xcd = x % 8;
+    const int64_t row = (slot / per_row) * 8 + xcd;
+    const int64_t rem = slot % per_row;
+    const int hg = (int)(rem / ks_count), ks = (int)(rem % ks_count);
+    if (row >= rows) return;
+    const int64_t b = row / T;
+    const int64_t klen = DENSE ? visible_entries(q_pos0 + row % T, ratio, N) : (int64_t)k;
+    const int key0 = ks * keys_per_split;
+    const int nkeys = (int)max((int64_t)0, min(klen, (int64_t)key0 + keys_per_split) - key0);
+    const int h0 = hg * kMHeadsWG + 16 * wid;
+    // key id of slot i of this range (-1: none)
+    auto key_id = [&](int i) -> int {
+        if (i >= nkeys) return -1;
+        if constexpr (DENSE) return key0 + i;
+        else return ids[i];
+    };
+
+    if constexpr (!DENSE) {
+        for (int i = tid; i < nkeys; i += 256) ids[i] = idx[row * k + key0 + i];
+        __syncthreads();
+    }
+
+    // this wave's q as the B operand of S^T: head n16, channels 32*s + 8*g .. +8
+    bf16x8_t qb[kMC / 32];
+    const uint16_t* qrow = q + ((row * H) + h0 + n16) * (int64_t)kMC + 8 * g;
+#pragma unroll
+    for (int s = 0; s < kMC / 32; ++s) qb[s] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * s);
+
+    f32x4 acc[kMColBlk];
+#pragma unroll
+    for (int cb = 0; cb < kMColBlk; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    const int nblk = (nkeys + kMBlk - 1) / kMBlk;
+    const uint16_t* kvseq = kv + b * N * (int64_t)kMC;
+    auto gather = [&](int blk, int buf) {
+        // wave w stages rows 8w .. 8w+7 of the block; invalid slots load row 0 (masked later)
+#pragma unroll
+        for (int r8 = 0; r8 < 8; ++r8) {
+            const int r = 8 * wid + r8;
+            int sidx = key_id(blk * kMBlk + r);
+            if (sidx < 0 || sidx >= N) sidx = 0;
+            const uint16_t* src = kvseq + (int64_t)sidx * kMC + 8 * lane;
+            __builtin_amdgcn_global_load_lds((glb_void_ptr)src, (lds_void_ptr)(stage + buf * kMBuf + r * kMPitch), 16,
+                                             0, 0);
+        }
+    };
+    if (nblk > 0) gather(0, 0);
+
+    for (int blk = 0; blk < nblk; ++blk) {
+        const int buf = blk & 1;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();   // block blk is staged; every wave is done with block blk-1
+        if (blk + 1 < nblk) gather(blk + 1, buf ^ 1);
+        const uint8_t* st = stage + buf * kMBuf;
+
+        // validity of the 32 keys of this block (bit r)
+        uint32_t valid = 0;
+        {
+            const int sidx = key_id(blk * kMBlk + (lane & 31));
+            const unsigned long long bal = __ballot(lane < 32 && sidx >= 0 && sidx < N);
+            valid = (uint32_t)bal;
+        }
+
+        // S^T for the two 16-key halves
+        f32x4 sacc[2];
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+            sacc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const uint8_t* arow = st + (hb * 16 + n16) * kMPitch + 16 * g;
+#pragma unroll
+            for (int s = 0; s < kMC / 32; ++s) {
+                const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(arow + 64 * s);
+                sacc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[s], sacc[hb], 0, 0, 0);
+            }
+        }
+        // online softmax for head n16 (values of lane: keys 16*hb + 4g + i)
+        float p[8];
+        float bmax = -INFINITY;
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = 16 * hb + 4 * g + i;
+                const float v = ((valid >> key) & 1u) ? sacc[hb][i] * sl2 : -INFINITY;
+                p[4 * hb + i] = v;
+                bmax = fmaxf(bmax, v);
+            }
+        bmax = fmaxf(bmax, __shfl_xor(bmax, 16, kWave));
+        bmax = fmaxf(bmax, __shfl_xor(bmax, 32, kWave));
+        const float m_new = fmaxf(m_run, bmax);
+        if (m_new == -INFINITY) continue;   // nothing valid yet (uniform per head column)
+        const float alpha = exp2f(m_run - m_new);
+        float psum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            p[e] = exp2f(p[e] - m_new);
+            psum += p[e];
+        }
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+        uint4 pw;
+        pw.x = pack_bf16x2(p[0], p[1]);
+        pw.y = pack_bf16x2(p[2], p[3]);
+        pw.z = pack_bf16x2(p[4], p[5]);
+        pw.w = pack_bf16x2(p[6], p[7]);
+        const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
+
+        // O^T += V^T P^T: V^T operand via transpose reads of keys {4g..4g+3} and {16+4g..}
+        const uint8_t* vbase0 = st + (4 * g + (n16 >> 2)) * kMPitch + 8 * (n16 & 3);
+        const uint8_t* vbase1 = vbase0 + 16 * kMPitch;
+#pragma unroll
+        for (int cb = 0; cb < kMColBlk; ++cb) {
+            const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(
+                vbase0 + 32 * cb));
+            const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(
+                vbase1 + 32 * cb));
+            typedef short i16x8 __attribute__((ext_vector_type(8)));
+            const i16x8 va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+            acc[cb] = acc[cb] * alpha;
+            acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, va), pb, acc[cb], 0, 0, 0);
+        }
+    }
+
+    // sum of the softmax denominators over the four lane groups that share a head
+    l_run += __shfl_xor(l_run, 16, kWave);
+    l_run += __shfl_xor(l_run, 32, kWave);
+    const int64_t head_row = row * H + h0 + n16;
+    if (part == nullptr) {
+        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+        uint16_t* orow = out + head_row * kMC;
+#pragma unroll
+        for (int cb = 0; cb < kMColBlk; ++cb) {
+            uint2 w2;
+            w2.x = pack_bf16x2(acc[cb][0] * inv, acc[cb][1] * inv);
+            w2.y = pack_bf16x2(acc[cb][2] * inv, acc[cb][3] * inv);
+            *reinterpret_cast<uint2*>(orow + 16 * cb + 4 * g) = w2;
+        }
+    } else {
+        const int64_t prow = (row * ks_count + ks) * H + h0 + n16;
+        float* pr = part + prow * kMC;
+#pragma unroll
+        for (int cb = 0; cb < kMColBlk; ++cb) *reinterpret_cast<f32x4*>(pr + 16 * cb + 4 * g) = acc[cb];
+        if (g == 0) {
+            part_ml[2 * prow] = m_run;
+            part_ml[2 * prow + 1] = l_run;
+        }
+    }
+}
+
+// Merge the key-range partials of one (row, head): out = sum_j e^(m_j - M) acc_j / sum_j e^(m_j - M) l_j.
+__global__ void __launch_bounds__(64)
+mqa_combine(const float* __restrict__ part, const float* __restrict__ part_ml, int64_t rows, int H, int ks_count,
+            uint16_t* __restrict__ out) {
+    const int64_t rh = blockIdx.x;   // row * H + head
+    const int64_t row = rh / H, head = rh % H;
+    const int lane = threadIdx.x;
+    float M = -INFINITY;
+    for (int j = 0; j < ks_count; ++j) M = fmaxf(M, part_ml[2 * ((row * ks_count + j) * H + head)]);
+    float L = 0.f;
+    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (M != -INFINITY) {
+        for (int j = 0; j < ks_count; ++j) {
+            const int64_t prow = (row * ks_count + j) * H + head;
+            const float sc = exp2f(part_ml[2 * prow] - M);
+            L = fmaf(part_ml[2 * prow + 1], sc, L);
+            const f32x4* p4 = reinterpret_cast<const f32x4*>(part + prow * kMC + 8 * lane);
+            const f32x4 a = p4[0], c = p4[1];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                o[e] = fmaf(a[e], sc, o[e]);
+                o[4 + e] = fmaf(c[e], sc, o[4 + e]);
+            }
+        }
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] *= inv;
+    store8<DT_BF16>(out, rh * kMC + 8 * lane, o);
+}
+
+// Key ranges per row: enough workgroups to fill the chip, at least 4 blocks per range.
+int mqa_splits(int64_t rows, int H, int k) {
+    const int64_t wgs = rows * (H / kMHeadsWG);
+    int ks = 1;
+    while (wgs * ks < 256 && (k + ks * 2 - 1) / (ks * 2) >= 4 * kMBlk) ks *= 2;
+    return ks;
+}
+
 }  // namespace
 
+size_t sparse_mqa_workspace(int64_t batch, int64_t T, int H, int c, int k, int t) {
+    if (t != DT_BF16 || c != kMC || H % kMHeadsWG != 0) return 0;
+    const int64_t rows = batch * T;
+    const int ks = mqa_splits(rows, H, k);
+    if (ks == 1) return 0;
+    return (size_t)rows * ks * H * (kMC + 2) * sizeof(float) + 256;
+}
+
 int launch_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t batch, int64_t T, int64_t N, int H,
-                      int c, int k, float scale, int t, void* out, hipStream_t stream) {
+                      int c, int k, float scale, int t, void* out, void* ws, hipStream_t stream) {
     if (batch == 0 || T == 0) return 0;
+    if (t == DT_BF16 && c == kMC && H % kMHeadsWG == 0) {
+        const int64_t rows = batch * T;
+        const int ks = mqa_splits(rows, H, k);
+        const int kps = ((k + ks - 1) / ks + kMBlk - 1) / kMBlk * kMBlk;
+        const int64_t units = ((rows + 7) / 8) * 8 * (H / kMHeadsWG) * ks;
+        if (units > 0x7fffffffLL) return -2;
+        float* part = nullptr;
+        float* part_ml = nullptr;
+        if (ks > 1) {
+            part = static_cast<float*>(ws);
+            part_ml = part + rows * ks * H * (int64_t)kMC;
+        }
+        const float sl2 = scale * kLog2e;
+        hipLaunchKernelGGL(mqa_sparse_mfma<false>, dim3((unsigned)units), dim3(256), 0, stream,
+                           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx, rows, T, N, H, k, ks,
+                           kps, sl2, (int64_t)0, 1, static_cast<uint16_t*>(out), part, part_ml);
+        if (ks > 1)
+            hipLaunchKernelGGL(mqa_combine, dim3((unsigned)(rows * H)), dim3(64), 0, stream, part, part_ml, rows, H, ks,
+                               static_cast<uint16_t*>(out));
+        return 0;
+    }
     if (t == DT_F32) return launch_generic<DT_F32, false>(q, kv, idx, batch, T, N, H, c, k, scale, 0, 1, out, stream);
     if (t == DT_BF16) return launch_generic<DT_BF16, false>(q, kv, idx, batch, T, N, H, c, k, scale, 0, 1, out, stream);
     return -2;
@@ -124,6 +402,17 @@ int launch_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t
 int launch_dense_mqa(const void* q, const void* kv, int64_t batch, int64_t T, int64_t q_pos0, int64_t N, int H, int c,
                      int ratio, float scale, int t, void* out, hipStream_t stream) {
     if (batch == 0 || T == 0) return 0;
+    if (t == DT_BF16 && c == kMC && H % kMHeadsWG == 0 && N <= 0x7fffffffLL) {
+        // one workgroup per (query, 64 heads) walks every visible entry: no key split, no
+        // partials (used for query chunks, which supply rows * H / 64 >= 256 workgroups)
+        const int64_t rows = batch * T;
+        const int64_t units = ((rows + 7) / 8) * 8 * (H / kMHeadsWG);
+        if (units > 0x7fffffffLL) return -2;
+        hipLaunchKernelGGL(mqa_sparse_mfma<true>, dim3((unsigned)units), dim3(256), 0, stream,
+                           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), nullptr, rows, T, N, H, 0,
+                           1, 0x7fffffff, scale * kLog2e, q_pos0, ratio, static_cast<uint16_t*>(out), nullptr, nullptr);
+        return 0;
+    }
     if (t == DT_F32)
         return launch_generic<DT_F32, true>(q, kv, nullptr, batch, T, N, H, c, 0, scale, q_pos0, ratio, out, stream);
     if (t == DT_BF16)

@@ -7,17 +7,19 @@
 // ascending order and padded with -1 (pad scores -inf).  Scores compare as fp32 values
 // (+0 == -0) through an order-preserving uint32 key.
 //
-// One workgroup of 1024 threads per row:
-//   A  min / max of the row                          (one read of the row)
-//   B  2048-bin histogram, bins LINEAR in value       (one read; spreads the atomics,
-//      unlike a radix digit of the float bit pattern, where almost all scores share the
-//      top byte and every atomic hits one bin)
-//   C  the bin b* holding the k-th largest value; its members are gathered to LDS and the
-//      exact k-th (value desc, index asc) is found by ranking (one read)
-//      — if b* holds more than kCap members (heavy ties), an exact 8-bit radix select on
-//      the order keys restricted to b* runs instead (four reads).
-//   D  ordered compaction: keep s iff key > K* or (key == K* and it is among the first
-//      `need_eq` such s), written at its prefix-sum position (one read).
+// One workgroup of 1024 threads per row.  Rows of up to 32768 visible entries are staged
+// in LDS once (128 KB of the 160 KB a gfx950 CU has); longer rows are read from global
+// memory in every pass.
+//   A  min / max of the row (fused into the LDS staging pass)
+//   B  2048-bin histogram with bins LINEAR in value: spreads the LDS atomics (a radix digit
+//      of the float bit pattern would put nearly every score of a row in one bin)
+//   C  the bin b* that holds the k-th largest value; its members are gathered and the exact
+//      k-th element in (value desc, index asc) order is found by ranking them.  If b*
+//      holds more than kCap members (heavy ties), an exact 8-bit radix select on the order
+//      keys restricted to b* runs instead.
+//   D  ordered compaction: keep s iff key > K*, or key == K* and s is among the first
+//      need_eq such indices.  Each wave compacts a contiguous segment with ballots; a
+//      16-entry scan of the per-wave counts gives each segment its output offset.
 #include "device_common.h"
 #include "launch.h"
 
@@ -28,15 +30,15 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kBins = 2048;
-constexpr int kCap = 4096;
+constexpr int kCap = 1024;
+constexpr int kRowLds = 32768;   // floats of a row staged in LDS
 
 struct TopkShared {
     uint32_t hist[kBins];
     float cval[kCap];
     int32_t cidx[kCap];
     float red_lo[kWaves], red_hi[kWaves];
-    uint32_t wsum[kWaves];
-    uint32_t wsum2[kWaves];
+    uint32_t wgt[kWaves], weq[kWaves];
     float lo, inv;
     int bstar;
     uint32_t need;        // how many of bin b* to take
@@ -52,33 +54,12 @@ __device__ __forceinline__ int bin_of(float v, float lo, float inv) {
     return (int)x;
 }
 
-// Inclusive prefix within the block of a per-thread count; returns exclusive prefix and
-// writes the block total to *total.  Uses `buf` (kWaves entries).
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* buf, uint32_t* total) {
-    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-    uint32_t inc = x;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        uint32_t y = __shfl_up(inc, off, kWave);
-        if (lane >= off) inc += y;
-    }
-    if (lane == kWave - 1) buf[wid] = inc;
-    __syncthreads();
-    uint32_t before = 0, all = 0;
-    for (int i = 0; i < kWaves; ++i) {
-        const uint32_t v = buf[i];
-        before += (i < wid) ? v : 0u;
-        all += v;
-    }
-    __syncthreads();
-    *total = all;
-    return before + inc - x;
-}
-
+template <bool IN_LDS>
 __global__ void __launch_bounds__(kThreads)
 topk_row_kernel(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_pos0, int64_t N, int m, int k,
                 int32_t* __restrict__ idx, float* __restrict__ sel) {
     __shared__ TopkShared sh;
+    __shared__ float rowbuf[IN_LDS ? kRowLds : 1];
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1), wid = tid / kWave;
     const int64_t row = blockIdx.x;
@@ -95,13 +76,35 @@ topk_row_kernel(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t
         }
         return;
     }
+    auto val = [&](int64_t s) -> float {
+        if constexpr (IN_LDS) return rowbuf[s];
+        else return sc[s];
+    };
 
-    // ---- A: min / max
+    // ---- A: min / max (and LDS staging)
     float lo = INFINITY, hi = -INFINITY;
-    for (int64_t s = tid; s < nv; s += kThreads) {
-        const float v = sc[s];
-        lo = fminf(lo, v);
-        hi = fmaxf(hi, v);
+    if constexpr (IN_LDS) {
+        const int64_t n4 = nv >> 2;
+        const float4* s4 = reinterpret_cast<const float4*>(sc);
+        float4* d4 = reinterpret_cast<float4*>(rowbuf);
+        for (int64_t i = tid; i < n4; i += kThreads) {
+            const float4 v = s4[i];
+            d4[i] = v;
+            lo = fminf(lo, fminf(fminf(v.x, v.y), fminf(v.z, v.w)));
+            hi = fmaxf(hi, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+        }
+        for (int64_t s = 4 * n4 + tid; s < nv; s += kThreads) {
+            const float v = sc[s];
+            rowbuf[s] = v;
+            lo = fminf(lo, v);
+            hi = fmaxf(hi, v);
+        }
+    } else {
+        for (int64_t s = tid; s < nv; s += kThreads) {
+            const float v = sc[s];
+            lo = fminf(lo, v);
+            hi = fmaxf(hi, v);
+        }
     }
     lo = -wave_max(-lo);
     hi = wave_max(hi);
@@ -124,7 +127,7 @@ topk_row_kernel(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t
     const float inv = sh.inv;
 
     // ---- B: histogram
-    for (int64_t s = tid; s < nv; s += kThreads) atomicAdd(&sh.hist[bin_of(sc[s], lo, inv)], 1u);
+    for (int64_t s = tid; s < nv; s += kThreads) atomicAdd(&sh.hist[bin_of(val(s), lo, inv)], 1u);
     __syncthreads();
 
     // find b*: bins scanned from the top; wave 0 does it, 32 bins per lane
@@ -161,7 +164,7 @@ topk_row_kernel(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t
     if (cnt_star <= (uint32_t)kCap) {
         // ---- C: gather bin b* and rank its members
         for (int64_t s = tid; s < nv; s += kThreads) {
-            const float v = sc[s];
+            const float v = val(s);
             if (bin_of(v, lo, inv) == bstar) {
                 const uint32_t p = atomicAdd(&sh.ncand, 1u);
                 if (p < (uint32_t)kCap) {   // always true: b* holds cnt_star <= kCap members
@@ -183,10 +186,12 @@ topk_row_kernel(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t
             if (rank == need - 1) sh.kstar = ki;
         }
         __syncthreads();
-        if (tid == 0) {
+        if (wid == 0) {
             uint32_t gt = 0;
-            for (uint32_t j = 0; j < nc; ++j) gt += order_key(sh.cval[j]) > sh.kstar ? 1u : 0u;
-            sh.need_eq = need - gt;
+            for (uint32_t j = lane; j < nc; j += kWave) gt += order_key(sh.cval[j]) > sh.kstar ? 1u : 0u;
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) gt += __shfl_xor(gt, off, kWave);
+            if (lane == 0) sh.need_eq = need - gt;
         }
         __syncthreads();
     } else {
@@ -198,7 +203,7 @@ topk_row_kernel(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t
             __syncthreads();
             const uint32_t prefix = sh.prefix, pmask = sh.pmask;
             for (int64_t s = tid; s < nv; s += kThreads) {
-                const float v = sc[s];
+                const float v = val(s);
                 if (bin_of(v, lo, inv) != bstar) continue;
                 const uint32_t key = order_key(v);
                 if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
@@ -223,31 +228,44 @@ topk_row_kernel(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t
         __syncthreads();
     }
 
-    // ---- D: ordered compaction
+    // ---- D: ordered compaction, one contiguous segment per wave
     const uint32_t kstar = sh.kstar, need_eq = sh.need_eq;
-    uint32_t taken = 0, eq_seen = 0;
-    for (int64_t base = 0; base < nv; base += kThreads) {
-        const int64_t s = base + tid;
-        float v = 0.f;
-        uint32_t key = 0u;
-        if (s < nv) { v = sc[s]; key = order_key(v); }
-        const uint32_t is_eq = (s < nv && key == kstar) ? 1u : 0u;
-        uint32_t eq_total;
-        const uint32_t eq_rank = eq_seen + block_exclusive_scan(is_eq, sh.wsum, &eq_total);
-        const uint32_t take = (s < nv && (key > kstar || (is_eq && eq_rank < need_eq))) ? 1u : 0u;
-        uint32_t take_total;
-        const uint32_t pos = taken + block_exclusive_scan(take, sh.wsum2, &take_total);
+    const int64_t seg = ((nv + (int64_t)kWaves * kWave - 1) / ((int64_t)kWaves * kWave)) * kWave;
+    const int64_t s_begin = (int64_t)wid * seg;
+    const int64_t s_end = min(nv, s_begin + seg);
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    uint32_t c_gt = 0, c_eq = 0;
+    for (int64_t s0 = s_begin; s0 < s_end; s0 += kWave) {
+        const int64_t s = s0 + lane;
+        const bool ok = s < s_end;
+        const uint32_t key = ok ? order_key(val(s)) : 0u;
+        c_gt += __popcll(__ballot(ok && key > kstar));
+        c_eq += __popcll(__ballot(ok && key == kstar));
+    }
+    if (lane == 0) { sh.wgt[wid] = c_gt; sh.weq[wid] = c_eq; }
+    __syncthreads();
+    uint32_t gt_before = 0, eq_before = 0;
+    for (int v = 0; v < wid; ++v) { gt_before += sh.wgt[v]; eq_before += sh.weq[v]; }
+    uint32_t run_eq = eq_before;
+    uint32_t run_take = gt_before + min(eq_before, need_eq);
+    for (int64_t s0 = s_begin; s0 < s_end; s0 += kWave) {
+        const int64_t s = s0 + lane;
+        const bool ok = s < s_end;
+        const float v = ok ? val(s) : 0.f;
+        const uint32_t key = ok ? order_key(v) : 0u;
+        const bool is_gt = ok && key > kstar;
+        const bool is_eq = ok && key == kstar;
+        const unsigned long long meq = __ballot(is_eq);
+        const uint32_t eq_rank = run_eq + __popcll(meq & lt);
+        const bool take = is_gt || (is_eq && eq_rank < need_eq);
+        const unsigned long long mt = __ballot(take);
+        const uint32_t pos = run_take + __popcll(mt & lt);
         if (take && pos < (uint32_t)k) {
             oi[pos] = (int32_t)s;
             if (os) os[pos] = v;
         }
-        taken += take_total;
-        eq_seen += eq_total;
-        if (taken >= (uint32_t)k) break;   // uniform across the block
-    }
-    for (int64_t r = (int64_t)taken + tid; r < k; r += kThreads) {   // defensive: unreachable when nv > k
-        oi[r] = -1;
-        if (os) os[r] = -INFINITY;
+        run_eq += __popcll(meq);
+        run_take += __popcll(mt);
     }
 }
 
@@ -266,8 +284,15 @@ int launch_topk(const float* scores, int64_t ld, int64_t batch, int64_t T, int64
     const int64_t rows = batch * T;
     if (rows == 0) return 0;
     if (rows > 0x7fffffffLL) return -2;
-    hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, scores, ld, T, q_pos0, N, m, k,
-                       idx, sel);
+    // the longest visible row is that of the last query
+    int64_t nv_max = (q_pos0 + T) / m;
+    if (nv_max > N) nv_max = N;
+    if (nv_max <= kRowLds)
+        hipLaunchKernelGGL((topk_row_kernel<true>), dim3((unsigned)rows), dim3(kThreads), 0, stream, scores, ld, T,
+                           q_pos0, N, m, k, idx, sel);
+    else
+        hipLaunchKernelGGL((topk_row_kernel<false>), dim3((unsigned)rows), dim3(kThreads), 0, stream, scores, ld, T,
+                           q_pos0, N, m, k, idx, sel);
     return 0;
 }
 

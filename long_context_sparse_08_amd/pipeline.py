@@ -16,7 +16,8 @@ import math
 
 import torch
 
-from . import (csa_compress, csa_index_topk, csa_sparse_mqa, hca_compress, hca_dense_mqa, workspace_for)
+from . import (csa_compress, csa_index_topk, csa_sparse_mqa, hca_compress, hca_dense_mqa, mqa_workspace_for,
+               workspace_for)
 
 
 class CsaPrefill:
@@ -34,6 +35,7 @@ class CsaPrefill:
         self.idx = torch.empty((batch, T, k), dtype=torch.int32, device=dev)
         self.sel = torch.empty((batch, T, k), dtype=torch.float32, device=dev)
         self.ws = workspace_for(batch, T, N, H_I, k, dev)
+        self.mqa_ws = mqa_workspace_for(q, k)
         self.out = torch.empty_like(q)
 
     def compress(self):
@@ -47,7 +49,7 @@ class CsaPrefill:
                        workspace=self.ws)
 
     def attend(self):
-        csa_sparse_mqa(self.inp["q"], self.kv, self.idx, self.scale, out=self.out)
+        csa_sparse_mqa(self.inp["q"], self.kv, self.idx, self.scale, out=self.out, workspace=self.mqa_ws)
 
     def run(self):
         self.compress()
@@ -68,6 +70,7 @@ class CsaDecode:
         self.idx = torch.empty((batch, T, k), dtype=torch.int32, device=dev)
         self.sel = torch.empty((batch, T, k), dtype=torch.float32, device=dev)
         self.ws = workspace_for(batch, T, N, H_I, k, dev)
+        self.mqa_ws = mqa_workspace_for(q, k)
         self.out = torch.empty_like(q)
 
     def select(self):
@@ -76,7 +79,7 @@ class CsaDecode:
                        workspace=self.ws)
 
     def attend(self):
-        csa_sparse_mqa(self.inp["q"], self.inp["kv"], self.idx, self.scale, out=self.out)
+        csa_sparse_mqa(self.inp["q"], self.inp["kv"], self.idx, self.scale, out=self.out, workspace=self.mqa_ws)
 
     def run(self):
         self.select()

@@ -70,6 +70,8 @@ def test_compress_rejects_bad_arguments(L):
     assert call(out_t=5) == UNSUPPORTED
     assert call(n=3) == OK                     # fewer tokens than one window: nothing to do
     assert call(batch=0) == OK
+    assert call(n=3, Ca=None, out=None) == OK  # empty output: pointers may be NULL
+    assert call(n=3, c=60) == UNSUPPORTED      # ...but sizes and dtypes are still checked
 
 
 def test_hca_compress_rejects_bad_arguments(L):
@@ -114,7 +116,9 @@ def test_index_topk_rejects_bad_arguments(L):
 
 
 def test_mqa_rejects_bad_arguments(L):
-    f = L.csa_sparse_mqa
+    def f(*a):
+        return L.csa_sparse_mqa(*a[:-1], None, 0, a[-1])
+
     assert f(None, A, A, 1, 4, 64, 4, 64, 8, 0.125, 0, A, None) == INVALID
     assert f(A, A, None, 1, 4, 64, 4, 64, 8, 0.125, 0, A, None) == INVALID
     assert f(A, A, A, 1, 4, 64, 4, 64, 0, 0.125, 0, A, None) == INVALID
@@ -123,6 +127,12 @@ def test_mqa_rejects_bad_arguments(L):
     assert f(A, A, A, 1, 4, 64, 4, 64, 4096, 0.125, 0, A, None) == UNSUPPORTED
     assert f(A, A, A, 1, 4, 64, 0, 64, 8, 0.125, 0, A, None) == INVALID
     assert f(A, A, A, 0, 4, 64, 4, 64, 8, 0.125, 0, A, None) == OK
+    # decode shape with few rows: keys split over workgroups -> a workspace is required
+    need = L.csa_sparse_mqa_workspace_size(32, 1, 128, 512, 1024, 1)
+    assert need > 0
+    assert L.csa_sparse_mqa(A, A, A, 32, 1, 32768, 128, 512, 1024, 0.05, 1, A, None, 0, None) == WORKSPACE
+    assert L.csa_sparse_mqa(A, A, A, 32, 1, 32768, 128, 512, 1024, 0.05, 1, A, A, need - 1, None) == WORKSPACE
+    assert L.csa_sparse_mqa_workspace_size(1, 8192, 64, 512, 512, 1) == 0   # prefill: no split
     g = L.hca_dense_mqa
     assert g(A, A, 1, 4, 0, 8, 4, 64, 0, 0.125, 0, A, None) == INVALID
     assert g(A, A, 1, 4, -5, 8, 4, 64, 128, 0.125, 0, A, None) == INVALID

@@ -85,6 +85,8 @@ IDX_CASES = [  # batch, T, q_pos0, N, H_I, c_I, m, dtype
     (3, 2, 4000, 1000, 64, 128, 4, FP8),
     (2, 1, 131072, 4099, 64, 128, 4, FP8),
     (1, 9, 5, 40, 1, 8, 4, F32),
+    (1, 6, 50, 300, 32, 128, 4, BF16),       # 32 indexer heads, prefill mapping with a ragged group
+    (2, 3, 1000, 333, 32, 128, 4, FP8),      # 32 indexer heads, decode mapping
 ]
 
 
@@ -103,7 +105,7 @@ def test_index_scores_parity(case):
     qd = oracle.decode(qI, dt)
     kd = oracle.decode(kI, dt)
     mag = np.einsum("bth,bthc,bsc->bts", w.astype(np.float64), np.abs(qd), np.abs(kd))
-    err = np.abs(got - ref)[vis] / np.maximum(mag[vis], 1.0)
+    err = np.abs(got[vis] - ref[vis]) / np.maximum(mag[vis], 1.0)
     say(f"  scores: max err / magnitude {err.max() if err.size else 0:.3e}")
     assert err.size == 0 or err.max() <= 1e-5
 
@@ -170,6 +172,9 @@ MQA_CASES = [  # batch, T, N, H, c, k, dtype
     (3, 1, 3000, 128, 512, 1024, BF16),
     (1, 4, 20, 3, 8, 7, F32),
     (1, 2, 50, 2, 1024, 16, F32),
+    (2, 5, 700, 64, 512, 100, BF16),       # k not a multiple of the 32-key block
+    (1, 2, 5000, 64, 512, 2048, BF16),     # maximum k, keys split over workgroups
+    (1, 3, 40, 48, 512, 16, BF16),         # head count off the 64-head tiling (generic kernel)
 ]
 
 
