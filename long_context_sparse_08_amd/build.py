@@ -27,13 +27,19 @@ SOURCES = ["api.cpp", "compress.hip", "indexer.hip", "topk.hip", "mqa.hip"]
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in ordinary VGPRs: the softmax rescale and the indexer epilogue
+    # read them with VALU ops, which would otherwise copy every accumulator out of AGPRs
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
+# per-file extras: the indexer's ReLU (max with 0) needs no NaN canonicalisation of MFMA
+# results; its scores are finite for finite inputs
+FILE_FLAGS = {"indexer.hip": ["-fno-honor-nans", "-Wno-nan-infinity-disabled"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

@@ -97,11 +97,19 @@ int hca_compress(const void* C, const void* Z, const float* B, int64_t batch, in
                                        static_cast<hipStream_t>(stream)));
 }
 
+// Workspace of csa_index_topk: the fp32 score rows, then room for the indexer's per-chunk
+// (min, max) pairs, then whatever the selection needs.  The chunk region is sized for the
+// largest chunk count any shape/dtype could use (one pair per 512 entries).
+size_t chunk_region(int64_t rows, int64_t N) {
+    const int64_t chunks = (N + 511) / 512;
+    return round_up((size_t)rows * (size_t)chunks * 2 * sizeof(float));
+}
+
 size_t csa_index_topk_workspace_size(int64_t batch, int64_t T, int64_t N, int H_I, int k) {
     if (batch < 0 || T < 0 || N < 0 || H_I < 1 || k < 1) return 0;
     const int64_t rows = batch * T;
     const size_t scores = round_up((size_t)rows * (size_t)score_ld(N) * sizeof(float));
-    return scores + round_up(csa::topk_extra_workspace(rows, N, k)) + kWsAlign;
+    return scores + chunk_region(rows, N) + round_up(csa::topk_extra_workspace(rows, N, k)) + kWsAlign;
 }
 
 int csa_index_topk(const void* qI, const float* w, const void* kI, int64_t batch, int64_t T, int64_t q_pos0, int64_t N,
@@ -120,10 +128,14 @@ int csa_index_topk(const void* qI, const float* w, const void* kI, int64_t batch
     const int64_t ld = score_ld(N);
     float* scores = static_cast<float*>(workspace);
     const int64_t rows = batch * T;
-    void* extra = static_cast<char*>(workspace) + round_up((size_t)rows * (size_t)ld * sizeof(float));
-    rc = csa::launch_index_scores(qI, w, kI, batch, T, q_pos0, N, H_I, c_I, m, qk_t, scores, ld, false, st);
+    float* chunk_mm = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                               round_up((size_t)rows * (size_t)ld * sizeof(float)));
+    int n_chunk_mm = 0;
+    rc = csa::launch_index_scores(qI, w, kI, batch, T, q_pos0, N, H_I, c_I, m, qk_t, scores, ld, false, chunk_mm,
+                                  &n_chunk_mm, st);
     if (rc != 0) return finish(rc);
-    return finish(csa::launch_topk(scores, ld, batch, T, q_pos0, N, m, k, idx, sel_scores, extra, st));
+    return finish(csa::launch_topk(scores, ld, batch, T, q_pos0, N, m, k, idx, sel_scores,
+                                   n_chunk_mm > 0 ? chunk_mm : nullptr, n_chunk_mm, st));
 }
 
 int csa_index_scores(const void* qI, const float* w, const void* kI, int64_t batch, int64_t T, int64_t q_pos0, int64_t N,
@@ -132,8 +144,8 @@ int csa_index_scores(const void* qI, const float* w, const void* kI, int64_t bat
     if (rc != CSA_OK) return rc;
     if (batch == 0 || T == 0 || N == 0) return CSA_OK;
     if (!scores) return CSA_ERR_INVALID_ARG;
-    return finish(csa::launch_index_scores(qI, w, kI, batch, T, q_pos0, N, H_I, c_I, m, qk_t, scores, N, true,
-                                           static_cast<hipStream_t>(stream)));
+    return finish(csa::launch_index_scores(qI, w, kI, batch, T, q_pos0, N, H_I, c_I, m, qk_t, scores, N, true, nullptr,
+                                           nullptr, static_cast<hipStream_t>(stream)));
 }
 
 size_t csa_topk_workspace_size(int64_t batch, int64_t T, int64_t N, int k) {
@@ -151,7 +163,7 @@ int csa_topk(const float* scores, int64_t ld, int64_t batch, int64_t T, int64_t 
     if (sel_scores && !aligned16(sel_scores)) return CSA_ERR_INVALID_ARG;
     if (!workspace || ws_bytes < csa_topk_workspace_size(batch, T, N, k) || !aligned16(workspace))
         return CSA_ERR_WORKSPACE;
-    return finish(csa::launch_topk(scores, ld, batch, T, q_pos0, N, m, k, idx, sel_scores, workspace,
+    return finish(csa::launch_topk(scores, ld, batch, T, q_pos0, N, m, k, idx, sel_scores, nullptr, 0,
                                    static_cast<hipStream_t>(stream)));
 }
 

@@ -107,20 +107,25 @@ constexpr int kMfmaCI = 128;
 template <int DT>
 struct IdxOps;
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
 template <>
 struct IdxOps<DT_FP8> {
     static constexpr int kLoads = 4;      // 16-byte loads per half row (64 fp8)
     static constexpr int kEsz = 1;
     struct Frag { uint4 v[kLoads]; };
+    // gfx950 v_mfma_scale_f32_32x32x64_f8f6f4 with both operands e4m3 (format 0) and unit
+    // block scales (E8M0 exponent 127 = 2^0): each lane feeds 32 of its 64 bytes per step.
     static __device__ __forceinline__ f32x16 mma(const Frag& a, const Frag& b, f32x16 acc) {
 #pragma unroll
-        for (int i = 0; i < kLoads; ++i) {
-            const long a0 = (long)(((unsigned long)a.v[i].y << 32) | a.v[i].x);
-            const long a1 = (long)(((unsigned long)a.v[i].w << 32) | a.v[i].z);
-            const long b0 = (long)(((unsigned long)b.v[i].y << 32) | b.v[i].x);
-            const long b1 = (long)(((unsigned long)b.v[i].w << 32) | b.v[i].z);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a0, b0, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a1, b1, acc, 0, 0, 0);
+        for (int j = 0; j < 2; ++j) {
+            const i32x8 av = {(int)a.v[2 * j].x, (int)a.v[2 * j].y, (int)a.v[2 * j].z, (int)a.v[2 * j].w,
+                              (int)a.v[2 * j + 1].x, (int)a.v[2 * j + 1].y, (int)a.v[2 * j + 1].z,
+                              (int)a.v[2 * j + 1].w};
+            const i32x8 bv = {(int)b.v[2 * j].x, (int)b.v[2 * j].y, (int)b.v[2 * j].z, (int)b.v[2 * j].w,
+                              (int)b.v[2 * j + 1].x, (int)b.v[2 * j + 1].y, (int)b.v[2 * j + 1].z,
+                              (int)b.v[2 * j + 1].w};
+            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 0, 0, 0, 127, 0, 127);
         }
         return acc;
     }
@@ -156,7 +161,7 @@ template <int DT, int MB, int TOK>
 __global__ void __launch_bounds__(256)
 index_scores_mfma(const void* __restrict__ qI, const float* __restrict__ w, const void* __restrict__ kI, int64_t batch,
                   int64_t T, int64_t q_pos0, int64_t N, int m, float* __restrict__ scores, int64_t ld,
-                  int write_invisible, int chunks, int cb) {
+                  int write_invisible, int chunks, int cb, float* __restrict__ chunk_mm) {
     using O = IdxOps<DT>;
     constexpr int H = 32 * MB;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -185,23 +190,35 @@ index_scores_mfma(const void* __restrict__ qI, const float* __restrict__ w, cons
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
         load_half_row<DT>(qI, row * H + 32 * mb + n, g, qa[mb]);
+        // accumulator row r of this lane is head 8*(r/4) + 4*g + r%4: four runs of 4 heads
 #pragma unroll
-        for (int r = 0; r < 16; ++r) wv[mb][r] = w[row * H + 32 * mb + 8 * (r >> 2) + 4 * g + (r & 3)];
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 w4 = *reinterpret_cast<const float4*>(w + row * H + 32 * mb + 8 * q4 + 4 * g);
+            wv[mb][4 * q4 + 0] = w4.x;
+            wv[mb][4 * q4 + 1] = w4.y;
+            wv[mb][4 * q4 + 2] = w4.z;
+            wv[mb][4 * q4 + 3] = w4.w;
+        }
     }
 
     const int64_t kbase = b * N;
+    float smin = INFINITY, smax = -INFINITY;   // over this wave's visible scores (TOK == 1)
     int64_t blk = blk0 + first;
-    typename O::Frag kb;
-    if (blk < blk1 && blk * 32 < nv) load_half_row<DT>(kI, kbase + min(blk * 32 + n, N - 1), g, kb);
+    // two blocks in flight ahead of the one being computed
+    typename O::Frag kb0, kb1;
+    if (blk < blk1 && blk * 32 < nv) load_half_row<DT>(kI, kbase + min(blk * 32 + n, N - 1), g, kb0);
+    if (blk + step < blk1 && (blk + step) * 32 < nv)
+        load_half_row<DT>(kI, kbase + min((blk + step) * 32 + n, N - 1), g, kb1);
     for (; blk < blk1; blk += step) {
         const int64_t s = blk * 32 + n;
         if (blk * 32 >= nv) {   // block wholly invisible (uniform over the wave)
             if (write_invisible && g == 0 && s < N) out[s] = -INFINITY;
             continue;
         }
-        typename O::Frag cur = kb;
-        const int64_t nxt = blk + step;
-        if (nxt < blk1 && nxt * 32 < nv) load_half_row<DT>(kI, kbase + min(nxt * 32 + n, N - 1), g, kb);
+        typename O::Frag cur = kb0;
+        kb0 = kb1;
+        const int64_t nxt = blk + 2 * step;
+        if (nxt < blk1 && nxt * 32 < nv) load_half_row<DT>(kI, kbase + min(nxt * 32 + n, N - 1), g, kb1);
         float contrib = 0.f;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
@@ -215,12 +232,35 @@ index_scores_mfma(const void* __restrict__ qI, const float* __restrict__ w, cons
             if (s < nv) out[s] = contrib;
             else if (write_invisible) out[s] = -INFINITY;
         }
+        if (s < nv) {
+            smin = fminf(smin, contrib);
+            smax = fmaxf(smax, contrib);
+        }
     }
+    if constexpr (TOK == 1) {
+        if (chunk_mm != nullptr) {   // (min, max) of the chunk's visible scores for the selection
+            __shared__ float red[2][4];
+            smin = -wave_max(-smin);
+            smax = wave_max(smax);
+            if (lane == 0) { red[0][wid] = smin; red[1][wid] = smax; }
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                float* o = chunk_mm + (row * chunks + chunk) * 2;
+                o[0] = fminf(fminf(red[0][0], red[0][1]), fminf(red[0][2], red[0][3]));
+                o[1] = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+            }
+        }
+    }
+}
+
+bool mfma_shape(int H_I, int c_I, int qk_t) {
+    return c_I == kMfmaCI && (H_I == 32 || H_I == 64) && (qk_t == DT_FP8 || qk_t == DT_BF16);
 }
 
 template <int DT, int MB>
 int launch_mfma(const void* qI, const float* w, const void* kI, int64_t batch, int64_t T, int64_t q_pos0, int64_t N,
-                int m, float* scores, int64_t ld, bool write_invisible, hipStream_t stream) {
+                int m, float* scores, int64_t ld, bool write_invisible, float* chunk_mm, int* n_chunk_mm,
+                hipStream_t stream) {
     const int64_t nblk = (N + 31) / 32;
     if (T >= 4) {
         // prefill: 4 queries per workgroup share the key blocks
@@ -230,35 +270,53 @@ int launch_mfma(const void* qI, const float* w, const void* kI, int64_t batch, i
         const int64_t grid = groups * chunks;
         if (grid > 0x7fffffffLL) return -2;
         hipLaunchKernelGGL((index_scores_mfma<DT, MB, 4>), dim3((unsigned)grid), dim3(256), 0, stream, qI, w, kI, batch,
-                           T, q_pos0, N, m, scores, ld, write_invisible ? 1 : 0, chunks, cb);
+                           T, q_pos0, N, m, scores, ld, write_invisible ? 1 : 0, chunks, cb, (float*)nullptr);
+        if (n_chunk_mm) *n_chunk_mm = 0;
     } else {
-        // decode: split each query's entries across many workgroups (16 blocks = 512 entries each)
-        const int cb = 16;
+        // decode: split each query's entries over workgroups sized so that the whole grid is
+        // resident at once (3 workgroups of 4 waves per CU at this kernel's register use):
+        // no partially filled second round
+        const int64_t total_blk = batch * T * nblk;
+        const int64_t target = 3 * 256;
+        int cb = (int)(((total_blk + target - 1) / target + 3) / 4 * 4);
+        if (cb < 4) cb = 4;
         const int chunks = (int)((nblk + cb - 1) / cb);
         const int64_t grid = batch * T * chunks;
         if (grid > 0x7fffffffLL) return -2;
         hipLaunchKernelGGL((index_scores_mfma<DT, MB, 1>), dim3((unsigned)grid), dim3(256), 0, stream, qI, w, kI, batch,
-                           T, q_pos0, N, m, scores, ld, write_invisible ? 1 : 0, chunks, cb);
+                           T, q_pos0, N, m, scores, ld, write_invisible ? 1 : 0, chunks, cb, chunk_mm);
+        if (n_chunk_mm) *n_chunk_mm = chunk_mm ? chunks : 0;
     }
     return 0;
 }
 
 }  // namespace
 
+int index_chunks(int64_t batch, int64_t T, int64_t N, int H_I, int c_I, int qk_t) {
+    if (!mfma_shape(H_I, c_I, qk_t) || T >= 4 || N == 0) return 0;
+    const int64_t nblk = (N + 31) / 32;
+    const int64_t total_blk = batch * T * nblk;
+    const int64_t target = 3 * 256;
+    int cb = (int)(((total_blk + target - 1) / target + 3) / 4 * 4);
+    if (cb < 4) cb = 4;
+    return (int)((nblk + cb - 1) / cb);
+}
+
 int launch_index_scores(const void* qI, const float* w, const void* kI, int64_t batch, int64_t T, int64_t q_pos0,
                         int64_t N, int H_I, int c_I, int m, int qk_t, float* scores, int64_t ld, bool write_invisible,
-                        hipStream_t stream) {
+                        float* chunk_mm, int* n_chunk_mm, hipStream_t stream) {
+    if (n_chunk_mm) *n_chunk_mm = 0;
     if (batch == 0 || T == 0 || N == 0) return 0;
-    if (c_I == kMfmaCI && (H_I == 32 || H_I == 64) && (qk_t == DT_FP8 || qk_t == DT_BF16)) {
+    if (mfma_shape(H_I, c_I, qk_t)) {
         if (qk_t == DT_FP8)
             return H_I == 64 ? launch_mfma<DT_FP8, 2>(qI, w, kI, batch, T, q_pos0, N, m, scores, ld, write_invisible,
-                                                      stream)
+                                                      chunk_mm, n_chunk_mm, stream)
                              : launch_mfma<DT_FP8, 1>(qI, w, kI, batch, T, q_pos0, N, m, scores, ld, write_invisible,
-                                                      stream);
+                                                      chunk_mm, n_chunk_mm, stream);
         return H_I == 64 ? launch_mfma<DT_BF16, 2>(qI, w, kI, batch, T, q_pos0, N, m, scores, ld, write_invisible,
-                                                   stream)
+                                                   chunk_mm, n_chunk_mm, stream)
                          : launch_mfma<DT_BF16, 1>(qI, w, kI, batch, T, q_pos0, N, m, scores, ld, write_invisible,
-                                                   stream);
+                                                   chunk_mm, n_chunk_mm, stream);
     }
     switch (qk_t) {
         case DT_F32:

@@ -14,16 +14,23 @@ int launch_compress(const void* Ca, const void* Za, const float* Ba, const void*
 
 // Indexer scores for every (query, entry) pair into `scores` ([batch*T, ld] fp32, ld >= N).
 // write_invisible: also write -inf for entries the query may not see (else they are skipped).
+// chunk_mm (optional, [batch*T, index_chunks(...)] pairs): min / max of each chunk of visible
+// scores, written by the decode-shaped MFMA kernel (chunks without visible entries hold
+// +inf / -inf); *n_chunk_mm receives the chunk count, 0 when the kernel used writes none.
 int launch_index_scores(const void* qI, const float* w, const void* kI, int64_t batch, int64_t T, int64_t q_pos0,
                         int64_t N, int H_I, int c_I, int m, int qk_t, float* scores, int64_t ld, bool write_invisible,
-                        hipStream_t stream);
+                        float* chunk_mm, int* n_chunk_mm, hipStream_t stream);
+
+// Number of (min, max) pairs per row the indexer writes into chunk_mm for these sizes (0: none).
+int index_chunks(int64_t batch, int64_t T, int64_t N, int H_I, int c_I, int qk_t);
 
 // Workspace bytes needed by launch_topk beyond the score rows.
 size_t topk_extra_workspace(int64_t rows, int64_t N, int k);
 
-// Per-row top-k over visible prefix of each score row.
+// Per-row top-k over the visible prefix of each score row.  chunk_mm / n_chunk_mm: optional
+// per-chunk (min, max) of the row's visible scores from the indexer (NULL / 0: not available).
 int launch_topk(const float* scores, int64_t ld, int64_t batch, int64_t T, int64_t q_pos0, int64_t N, int m, int k,
-                int32_t* idx, float* sel, void* extra_ws, hipStream_t stream);
+                int32_t* idx, float* sel, const float* chunk_mm, int n_chunk_mm, hipStream_t stream);
 
 // Device workspace bytes launch_sparse_mqa needs (0: none) for the key-range partials.
 size_t sparse_mqa_workspace(int64_t batch, int64_t T, int H, int c, int k, int t);

@@ -149,6 +149,14 @@ constexpr int kMBlk = 32;                      // keys per staged block
 constexpr int kMPitch = kMC * 2 + 32;          // LDS bytes per staged row (bank spread)
 constexpr int kMBuf = kMBlk * kMPitch;         // bytes per staged block
 constexpr int kMColBlk = kMC / 16;             // 16-column blocks of the output
+constexpr int kMLoadsPerBlk = kMBlk / 4;       // rows each wave of a team stages per block (8)
+
+// s_waitcnt with vmcnt = n (0..63), expcnt and lgkmcnt left at their maximum (no wait)
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(n >= 0 && n < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return f32_to_bf16_rne(a) | (f32_to_bf16_rne(b) << 16);
@@ -156,15 +164,26 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 
 // DENSE: the key list of the query at position p is 0 .. nv-1 with nv the number of HCA
 // entries it may see (ratio*(s+1)-1 <= p); `k` is then unused.
+//
+// Workgroup = 8 waves = two key teams of 4 waves (2 waves per SIMD, so one wave's LDS and
+// matrix-core latencies hide behind the other's work).  Team t computes the blocks
+// t, t+2, t+4, ... of the workgroup's key range; inside a team wave w owns heads 16w..16w+15.
+// Each team has two staging buffers, so while a block pair is computed the next pair loads.
+// At the end team 1 hands its (running max, running sum, acc) to team 0 through LDS.
+constexpr int kMTeams = 2;
+constexpr int kMTeamStages = 2;
+
 template <bool DENSE>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(512)
 mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
                 int64_t rows, int64_t T, int64_t N, int H, int k, int ks_count, int keys_per_split, float sl2,
                 int64_t q_pos0, int ratio, uint16_t* __restrict__ out, float* __restrict__ part,
                 float* __restrict__ part_ml) {
-    __shared__ __attribute__((aligned(16))) uint8_t stage[2 * kMBuf];
+    __shared__ __attribute__((aligned(16))) uint8_t stage[kMTeams * kMTeamStages * kMBuf];
     __shared__ int32_t ids[DENSE ? 1 : CSA_MAX_TOPK_DEV];
+    __shared__ float xm[4][16], xl[4][16];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int team = wid >> 2, tw = wid & 3;
     const int g = lane >> 4, n16 = lane & 15;
     const int HG = H / kMHeadsWG;
     // XCD-aware order: consecutive units of a row go to one XCD (workgroups are dealt
@@ -180,16 +199,14 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int64_t klen = DENSE ? visible_entries(q_pos0 + row % T, ratio, N) : (int64_t)k;
     const int key0 = ks * keys_per_split;
     const int nkeys = (int)max((int64_t)0, min(klen, (int64_t)key0 + keys_per_split) - key0);
-    const int h0 = hg * kMHeadsWG + 16 * wid;
-    // key id of slot i of this range (-1: none)
-    auto key_id = [&](int i) -> int {
+    const int h0 = hg * kMHeadsWG + 16 * tw;
+    auto key_id = [&](int i) -> int {   // key id of slot i of this range (-1: none)
         if (i >= nkeys) return -1;
         if constexpr (DENSE) return key0 + i;
         else return ids[i];
     };
-
     if constexpr (!DENSE) {
-        for (int i = tid; i < nkeys; i += 256) ids[i] = idx[row * k + key0 + i];
+        for (int i = tid; i < nkeys; i += 512) ids[i] = idx[row * k + key0 + i];
         __syncthreads();
     }
 
@@ -205,47 +222,49 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     float m_run = -INFINITY, l_run = 0.f;
 
     const int nblk = (nkeys + kMBlk - 1) / kMBlk;
+    const int npair = (nblk + kMTeams - 1) / kMTeams;   // iterations: one block per team each
     const uint16_t* kvseq = kv + b * N * (int64_t)kMC;
-    auto gather = [&](int blk, int buf) {
-        // wave w stages rows 8w .. 8w+7 of the block; invalid slots load row 0 (masked later)
+    uint8_t* team_stage = stage + team * kMTeamStages * kMBuf;
+    auto gather = [&](int it, int buf) {   // this team's block of iteration `it`
+        const int blk = kMTeams * it + team;
 #pragma unroll
-        for (int r8 = 0; r8 < 8; ++r8) {
-            const int r = 8 * wid + r8;
+        for (int r8 = 0; r8 < kMLoadsPerBlk; ++r8) {
+            const int r = kMLoadsPerBlk * tw + r8;
             int sidx = key_id(blk * kMBlk + r);
-            if (sidx < 0 || sidx >= N) sidx = 0;
+            if (sidx < 0 || sidx >= N) sidx = 0;   // invalid slots load row 0, masked below
             const uint16_t* src = kvseq + (int64_t)sidx * kMC + 8 * lane;
-            __builtin_amdgcn_global_load_lds((glb_void_ptr)src, (lds_void_ptr)(stage + buf * kMBuf + r * kMPitch), 16,
-                                             0, 0);
+            __builtin_amdgcn_global_load_lds((glb_void_ptr)src, (lds_void_ptr)(team_stage + buf * kMBuf + r * kMPitch),
+                                             16, 0, 0);
         }
     };
-    if (nblk > 0) gather(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);   // q is in registers
+    if (npair > 0) gather(0, 0);
 
-    for (int blk = 0; blk < nblk; ++blk) {
-        const int buf = blk & 1;
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();   // block blk is staged; every wave is done with block blk-1
-        if (blk + 1 < nblk) gather(blk + 1, buf ^ 1);
-        const uint8_t* st = stage + buf * kMBuf;
+    for (int it = 0; it < npair; ++it) {
+        const int buf = it & 1;
+        wait_vmcnt<0>();
+        __syncthreads();   // iteration it is staged; every wave is done with iteration it-1
+        if (it + 1 < npair) gather(it + 1, buf ^ 1);
+        const uint8_t* st = team_stage + buf * kMBuf;
+        const int blk = kMTeams * it + team;
 
-        // validity of the 32 keys of this block (bit r)
+        // validity of the 32 keys of this block (bit r); all-zero for a block past the range
         uint32_t valid = 0;
         {
             const int sidx = key_id(blk * kMBlk + (lane & 31));
-            const unsigned long long bal = __ballot(lane < 32 && sidx >= 0 && sidx < N);
-            valid = (uint32_t)bal;
+            valid = (uint32_t)__ballot(lane < 32 && sidx >= 0 && sidx < N);
         }
 
-        // S^T for the two 16-key halves
-        f32x4 sacc[2];
+        // S^T for the two 16-key halves (two independent accumulation chains, interleaved)
+        f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        const uint8_t* arow0 = st + n16 * kMPitch + 16 * g;
+        const uint8_t* arow1 = arow0 + 16 * kMPitch;
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-            sacc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const uint8_t* arow = st + (hb * 16 + n16) * kMPitch + 16 * g;
-#pragma unroll
-            for (int s = 0; s < kMC / 32; ++s) {
-                const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(arow + 64 * s);
-                sacc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[s], sacc[hb], 0, 0, 0);
-            }
+        for (int s = 0; s < kMC / 32; ++s) {
+            const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(arow0 + 64 * s);
+            const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(arow1 + 64 * s);
+            sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qb[s], sacc[0], 0, 0, 0);
+            sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qb[s], sacc[1], 0, 0, 0);
         }
         // online softmax for head n16 (values of lane: keys 16*hb + 4g + i)
         float p[8];
@@ -261,17 +280,26 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
             }
         bmax = fmaxf(bmax, __shfl_xor(bmax, 16, kWave));
         bmax = fmaxf(bmax, __shfl_xor(bmax, 32, kWave));
-        const float m_new = fmaxf(m_run, bmax);
-        if (m_new == -INFINITY) continue;   // nothing valid yet (uniform per head column)
-        const float alpha = exp2f(m_run - m_new);
+        // Lazy rescale: the reference max moves (and acc / l are rescaled) only when a logit
+        // exceeds it by more than 2^8 in the exp2 domain; otherwise p <= 256, exact enough in
+        // bf16 / fp32.  Decided for the whole wave (a lane whose max did not grow gets 1).
+        if (__any(bmax > m_run + 8.f)) {
+            const float m_new = fmaxf(m_run, bmax);
+            const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);   // 0 at the first valid block
+            l_run *= alpha;
+#pragma unroll
+            for (int cb = 0; cb < kMColBlk; ++cb) acc[cb] = acc[cb] * alpha;
+            m_run = m_new;
+        }
+        // while nothing valid has been seen m_run is -inf and every p is exp2(-inf) = 0
+        const float m_ref = m_run == -INFINITY ? 0.f : m_run;
         float psum = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            p[e] = exp2f(p[e] - m_new);
+            p[e] = exp2f(p[e] - m_ref);
             psum += p[e];
         }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
+        l_run += psum;
         uint4 pw;
         pw.x = pack_bf16x2(p[0], p[1]);
         pw.y = pack_bf16x2(p[2], p[3]);
@@ -290,7 +318,6 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                 vbase1 + 32 * cb));
             typedef short i16x8 __attribute__((ext_vector_type(8)));
             const i16x8 va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-            acc[cb] = acc[cb] * alpha;
             acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, va), pb, acc[cb], 0, 0, 0);
         }
     }
@@ -298,6 +325,33 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     // sum of the softmax denominators over the four lane groups that share a head
     l_run += __shfl_xor(l_run, 16, kWave);
     l_run += __shfl_xor(l_run, 32, kWave);
+
+    // team 1 hands its state to team 0 (the stage buffers are free after this barrier)
+    __syncthreads();
+    constexpr int kXPitch = kMC + 4;   // padded head stride: the 16 heads of a write hit distinct banks
+    static_assert(4 * 16 * kXPitch * sizeof(float) <= sizeof(stage), "team handoff fits the stage buffers");
+    float* xacc = reinterpret_cast<float*>(stage) + tw * (16 * kXPitch);   // [head 16][col] per wave
+    if (team == 1) {
+        if (g == 0) { xm[tw][n16] = m_run; xl[tw][n16] = l_run; }
+#pragma unroll
+        for (int cb = 0; cb < kMColBlk; ++cb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xacc[n16 * kXPitch + 16 * cb + 4 * g + i] = acc[cb][i];
+    }
+    __syncthreads();
+    if (team == 1) return;
+    {
+        const float m1 = xm[tw][n16], l1 = xl[tw][n16];
+        const float M = fmaxf(m_run, m1);
+        const float a0 = M == -INFINITY ? 0.f : exp2f(m_run - M);
+        const float a1 = M == -INFINITY ? 0.f : exp2f(m1 - M);
+        l_run = l_run * a0 + l1 * a1;
+        m_run = M;
+#pragma unroll
+        for (int cb = 0; cb < kMColBlk; ++cb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[cb][i] = acc[cb][i] * a0 + xacc[n16 * kXPitch + 16 * cb + 4 * g + i] * a1;
+    }
     const int64_t head_row = row * H + h0 + n16;
     if (part == nullptr) {
         const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
@@ -386,7 +440,7 @@ int launch_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t
             part_ml = part + rows * ks * H * (int64_t)kMC;
         }
         const float sl2 = scale * kLog2e;
-        hipLaunchKernelGGL(mqa_sparse_mfma<false>, dim3((unsigned)units), dim3(256), 0, stream,
+        hipLaunchKernelGGL(mqa_sparse_mfma<false>, dim3((unsigned)units), dim3(512), 0, stream,
                            static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx, rows, T, N, H, k, ks,
                            kps, sl2, (int64_t)0, 1, static_cast<uint16_t*>(out), part, part_ml);
         if (ks > 1)
@@ -408,7 +462,7 @@ int launch_dense_mqa(const void* q, const void* kv, int64_t batch, int64_t T, in
         const int64_t rows = batch * T;
         const int64_t units = ((rows + 7) / 8) * 8 * (H / kMHeadsWG);
         if (units > 0x7fffffffLL) return -2;
-        hipLaunchKernelGGL(mqa_sparse_mfma<true>, dim3((unsigned)units), dim3(256), 0, stream,
+        hipLaunchKernelGGL(mqa_sparse_mfma<true>, dim3((unsigned)units), dim3(512), 0, stream,
                            static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), nullptr, rows, T, N, H, 0,
                            1, 0x7fffffff, scale * kLog2e, q_pos0, ratio, static_cast<uint16_t*>(out), nullptr, nullptr);
         return 0;

@@ -7,7 +7,8 @@
 // ascending order and padded with -1 (pad scores -inf).  Scores compare as fp32 values
 // (+0 == -0) through an order-preserving uint32 key.
 //
-// One workgroup of 1024 threads per row.  Rows of up to 32768 visible entries are staged
+// topk_row_kernel (rows longer than 262144 visible entries), one workgroup of 1024 threads
+// per row.  Rows of up to 32768 visible entries are staged
 // in LDS once (128 KB of the 160 KB a gfx950 CU has); longer rows are read from global
 // memory in every pass.
 //   A  min / max of the row (fused into the LDS staging pass)
@@ -269,6 +270,328 @@ topk_row_kernel(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t
     }
 }
 
+
+// ============================================================================ bitmap kernel
+// topk_bitmap: the same selection with two changes that cut the per-element work.
+//  * The row range (min / max) can come from per-chunk min / max the decode indexer writes
+//    next to the scores, so no pass is spent on it.
+//  * After b* is known, one pass marks every entry of a bin above b* in an LDS bitmap (all of
+//    them are kept) and gathers b*'s members; the members that are kept are marked after
+//    ranking.  The ordered output is then read off the bitmap: each thread owns a run of
+//    32-bit words, one block scan of their popcounts gives its output offset.
+// Rows up to kBmMaxRow = 262144 visible entries (a 32 KB bitmap); rows up to kRowLds are
+// staged in LDS first.
+constexpr int kBmMaxRow = 262144;
+constexpr int kBmWordsLds = kRowLds / 32;
+constexpr int kBmWordsGlb = kBmMaxRow / 32;
+
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* buf, uint32_t* total) {
+    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+    uint32_t inc = x;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const uint32_t y = __shfl_up(inc, off, kWave);
+        if (lane >= off) inc += y;
+    }
+    if (lane == kWave - 1) buf[wid] = inc;
+    __syncthreads();
+    uint32_t before = 0, all = 0;
+    for (int i = 0; i < kWaves; ++i) {
+        const uint32_t v = buf[i];
+        before += (i < wid) ? v : 0u;
+        all += v;
+    }
+    __syncthreads();
+    *total = all;
+    return before + inc - x;
+}
+
+template <bool IN_LDS>
+__global__ void __launch_bounds__(kThreads)
+topk_bitmap(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_pos0, int64_t N, int m, int k,
+            const float* __restrict__ mm, int nmm, int32_t* __restrict__ idx, float* __restrict__ sel) {
+    constexpr int kWords = IN_LDS ? kBmWordsLds : kBmWordsGlb;
+    __shared__ float rowbuf[IN_LDS ? kRowLds : 1];
+    __shared__ uint32_t bits[kWords];
+    __shared__ uint32_t hist[kBins];
+    __shared__ float cval[kCap];
+    __shared__ int32_t cidx[kCap];
+    __shared__ float red_lo[kWaves], red_hi[kWaves];
+    __shared__ uint32_t scan_buf[kWaves];
+    __shared__ float s_lo, s_inv;
+    __shared__ int s_bstar;
+    __shared__ uint32_t s_need, s_ncand, s_need_eq, s_prefix, s_pmask;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+    const int64_t row = blockIdx.x;
+    const int64_t nv = visible_entries(q_pos0 + row % T, m, N);
+    const float* sc = scores + row * ld;
+    int32_t* oi = idx + row * k;
+    float* os = sel ? sel + row * k : nullptr;
+    if (nv <= k) {
+        for (int r = tid; r < k; r += kThreads) {
+            oi[r] = r < nv ? r : -1;
+            if (os) os[r] = r < nv ? sc[r] : -INFINITY;
+        }
+        return;
+    }
+    auto val = [&](int64_t s) -> float {
+        if constexpr (IN_LDS) return rowbuf[s];
+        else return sc[s];
+    };
+    const int64_t nwords = (nv + 31) >> 5;
+
+    // ---- row range, LDS staging, histogram.  With the indexer's per-chunk (min, max) the
+    // range is known first and the histogram is built from the staging registers (one pass).
+    float lo = INFINITY, hi = -INFINITY;
+    const bool have_mm = mm != nullptr;
+    auto publish_range = [&]() {
+        lo = -wave_max(-lo);
+        hi = wave_max(hi);
+        if (lane == 0) { red_lo[wid] = lo; red_hi[wid] = hi; }
+        for (int i = tid; i < kBins; i += kThreads) hist[i] = 0u;
+        for (int64_t i = tid; i < nwords; i += kThreads) bits[i] = 0u;
+        __syncthreads();
+        if (tid == 0) {
+            float l = red_lo[0], h = red_hi[0];
+            for (int i = 1; i < kWaves; ++i) { l = fminf(l, red_lo[i]); h = fmaxf(h, red_hi[i]); }
+            float inv = (float)kBins / (h - l);
+            if (!(h > l) || !isfinite(inv)) inv = 0.f;
+            s_lo = l;
+            s_inv = inv;
+            s_ncand = 0u;
+            s_bstar = 0;   // always overwritten: the bin counts sum to nv > k
+            s_need = (uint32_t)k;
+        }
+        __syncthreads();
+        lo = s_lo;
+    };
+    if (have_mm) {
+        const float* r = mm + row * (int64_t)nmm * 2;
+        for (int i = tid; i < nmm; i += kThreads) {
+            lo = fminf(lo, r[2 * i]);
+            hi = fmaxf(hi, r[2 * i + 1]);
+        }
+        publish_range();
+    }
+    if constexpr (IN_LDS) {
+        const float hlo = have_mm ? s_lo : 0.f, hinv = have_mm ? s_inv : 0.f;
+        const int64_t n4 = nv >> 2;
+        const float4* s4 = reinterpret_cast<const float4*>(sc);
+        float4* d4 = reinterpret_cast<float4*>(rowbuf);
+        for (int64_t i0 = tid; i0 < n4; i0 += 8 * kThreads) {
+            float4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int64_t i = i0 + (int64_t)u * kThreads;
+                v[u] = i < n4 ? s4[i] : make_float4(INFINITY, INFINITY, -INFINITY, -INFINITY);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int64_t i = i0 + (int64_t)u * kThreads;
+                if (i >= n4) continue;
+                d4[i] = v[u];
+                if (have_mm) {
+                    atomicAdd(&hist[bin_of(v[u].x, hlo, hinv)], 1u);
+                    atomicAdd(&hist[bin_of(v[u].y, hlo, hinv)], 1u);
+                    atomicAdd(&hist[bin_of(v[u].z, hlo, hinv)], 1u);
+                    atomicAdd(&hist[bin_of(v[u].w, hlo, hinv)], 1u);
+                } else {
+                    lo = fminf(lo, fminf(fminf(v[u].x, v[u].y), fminf(v[u].z, v[u].w)));
+                    hi = fmaxf(hi, fmaxf(fmaxf(v[u].x, v[u].y), fmaxf(v[u].z, v[u].w)));
+                }
+            }
+        }
+        for (int64_t s = 4 * n4 + tid; s < nv; s += kThreads) {
+            const float v = sc[s];
+            rowbuf[s] = v;
+            if (have_mm) atomicAdd(&hist[bin_of(v, hlo, hinv)], 1u);
+            else { lo = fminf(lo, v); hi = fmaxf(hi, v); }
+        }
+    } else if (!have_mm) {
+        for (int64_t s = tid; s < nv; s += kThreads) {
+            const float v = sc[s];
+            lo = fminf(lo, v);
+            hi = fmaxf(hi, v);
+        }
+    }
+    if (!have_mm) {
+        __syncthreads();   // staging done before the range is published (hist is reset there)
+        publish_range();
+    }
+    const float inv = s_inv;
+
+    // ---- histogram (unless built while staging)
+    if (!(IN_LDS && have_mm)) {
+        if constexpr (IN_LDS) {
+            for (int64_t s = tid; s < nv; s += kThreads) atomicAdd(&hist[bin_of(rowbuf[s], lo, inv)], 1u);
+        } else {
+            for (int64_t s0 = tid; s0 < nv; s0 += 8 * kThreads) {
+                float v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int64_t s = s0 + (int64_t)u * kThreads;
+                    v[u] = s < nv ? sc[s] : 0.f;
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (s0 + (int64_t)u * kThreads < nv) atomicAdd(&hist[bin_of(v[u], lo, inv)], 1u);
+            }
+        }
+    }
+    __syncthreads();
+    if (wid == 0) {   // b*: bins scanned from the top, 32 per lane
+        const int per = kBins / kWave;
+        const int top = kBins - 1 - lane * per;
+        uint32_t mine = 0;
+        for (int j = 0; j < per; ++j) mine += hist[top - j];
+        uint32_t inc = mine;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const uint32_t y = __shfl_up(inc, off, kWave);
+            if (lane >= off) inc += y;
+        }
+        const uint32_t before = inc - mine;
+        if (before < (uint32_t)k && inc >= (uint32_t)k) {
+            uint32_t acc = before;
+            for (int j = 0; j < per; ++j) {
+                const uint32_t hh = hist[top - j];
+                if (acc + hh >= (uint32_t)k) {
+                    s_bstar = top - j;
+                    s_need = (uint32_t)k - acc;
+                    break;
+                }
+                acc += hh;
+            }
+        }
+    }
+    __syncthreads();
+    const int bstar = s_bstar;
+    const uint32_t need = s_need;
+    const bool fits = hist[bstar] <= (uint32_t)kCap;
+
+    // ---- mark bins above b*, gather b*'s members
+    auto mark = [&](int64_t s, float v) {
+        const int bn = bin_of(v, lo, inv);
+        if (bn > bstar) {
+            atomicOr(&bits[s >> 5], 1u << (s & 31));
+        } else if (bn == bstar && fits) {
+            const uint32_t p = atomicAdd(&s_ncand, 1u);
+            if (p < (uint32_t)kCap) { cval[p] = v; cidx[p] = (int32_t)s; }
+        }
+    };
+    if constexpr (IN_LDS) {
+        for (int64_t s = tid; s < nv; s += kThreads) mark(s, rowbuf[s]);
+    } else {
+        for (int64_t s0 = tid; s0 < nv; s0 += 8 * kThreads) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int64_t s = s0 + (int64_t)u * kThreads;
+                v[u] = s < nv ? sc[s] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (s0 + (int64_t)u * kThreads < nv) mark(s0 + (int64_t)u * kThreads, v[u]);
+        }
+    }
+    __syncthreads();
+
+    if (fits) {
+        // rank b*'s members by (value desc, index asc); keep ranks < need
+        const uint32_t nc = min(s_ncand, (uint32_t)kCap);
+        for (uint32_t i = tid; i < nc; i += kThreads) {
+            const uint32_t ki = order_key(cval[i]);
+            const int32_t si = cidx[i];
+            uint32_t rank = 0;
+            for (uint32_t j = 0; j < nc; ++j) {
+                const uint32_t kj = order_key(cval[j]);
+                rank += (kj > ki || (kj == ki && cidx[j] < si)) ? 1u : 0u;
+            }
+            if (rank < need) atomicOr(&bits[si >> 5], 1u << (si & 31));
+        }
+    } else {
+        // heavy ties in b*: exact 8-bit radix select of the need-th largest order key in b*
+        if (tid == 0) { s_prefix = 0u; s_pmask = 0u; s_need_eq = need; }
+        __syncthreads();
+        for (int shift = 24; shift >= 0; shift -= 8) {
+            for (int i = tid; i < 256; i += kThreads) hist[i] = 0u;
+            __syncthreads();
+            const uint32_t prefix = s_prefix, pmask = s_pmask;
+            for (int64_t s = tid; s < nv; s += kThreads) {
+                const float v = val(s);
+                if (bin_of(v, lo, inv) != bstar) continue;
+                const uint32_t key = order_key(v);
+                if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+            }
+            __syncthreads();
+            if (tid == 0) {
+                uint32_t remaining = s_need_eq, acc = 0;
+                for (int d = 255; d >= 0; --d) {
+                    const uint32_t hh = hist[d];
+                    if (acc + hh >= remaining) {
+                        s_prefix = prefix | ((uint32_t)d << shift);
+                        s_pmask = pmask | (255u << shift);
+                        s_need_eq = remaining - acc;
+                        break;
+                    }
+                    acc += hh;
+                }
+            }
+            __syncthreads();
+        }
+        const uint32_t kstar = s_prefix, need_eq = s_need_eq;
+        // keys above K* in b* are kept; of the keys equal to K*, the need_eq lowest indices
+        const int64_t seg = ((nv + (int64_t)kWaves * kWave - 1) / ((int64_t)kWaves * kWave)) * kWave;
+        const int64_t a = (int64_t)wid * seg, e = min(nv, a + seg);
+        const unsigned long long lt = (1ull << lane) - 1ull;
+        uint32_t c_eq = 0;
+        for (int64_t b0 = a; b0 < e; b0 += kWave) {
+            const int64_t s = b0 + lane;
+            const bool ok = s < e;
+            const float v = ok ? val(s) : 0.f;
+            const bool inb = ok && bin_of(v, lo, inv) == bstar;
+            const uint32_t key = order_key(v);
+            if (inb && key > kstar) atomicOr(&bits[s >> 5], 1u << (s & 31));
+            c_eq += __popcll(__ballot(inb && key == kstar));
+        }
+        if (lane == 0) scan_buf[wid] = c_eq;
+        __syncthreads();
+        uint32_t run = 0;
+        for (int v = 0; v < wid; ++v) run += scan_buf[v];
+        for (int64_t b0 = a; b0 < e; b0 += kWave) {
+            const int64_t s = b0 + lane;
+            const bool ok = s < e;
+            const float v = ok ? val(s) : 0.f;
+            const bool is_eq = ok && bin_of(v, lo, inv) == bstar && order_key(v) == kstar;
+            const unsigned long long meq = __ballot(is_eq);
+            if (is_eq && run + __popcll(meq & lt) < need_eq) atomicOr(&bits[s >> 5], 1u << (s & 31));
+            run += __popcll(meq);
+        }
+    }
+    __syncthreads();
+
+    // ---- ordered extraction: each thread owns a run of bitmap words
+    const int64_t per = (nwords + kThreads - 1) / kThreads;
+    const int64_t w0 = (int64_t)tid * per, w1 = min(nwords, w0 + per);
+    uint32_t cnt = 0;
+    for (int64_t w = w0; w < w1; ++w) cnt += __popc(bits[w]);
+    uint32_t total;
+    uint32_t pos = block_excl_scan(cnt, scan_buf, &total);
+    for (int64_t w = w0; w < w1; ++w) {
+        uint32_t word = bits[w];
+        while (word) {
+            const int b = __ffs(word) - 1;
+            word &= word - 1;
+            const int64_t s = (w << 5) + b;
+            if (pos < (uint32_t)k) {
+                oi[pos] = (int32_t)s;
+                if (os) os[pos] = val(s);
+            }
+            ++pos;
+        }
+    }
+}
+
 }  // namespace
 
 size_t topk_extra_workspace(int64_t rows, int64_t N, int k) {
@@ -279,20 +602,22 @@ size_t topk_extra_workspace(int64_t rows, int64_t N, int k) {
 }
 
 int launch_topk(const float* scores, int64_t ld, int64_t batch, int64_t T, int64_t q_pos0, int64_t N, int m, int k,
-                int32_t* idx, float* sel, void* extra_ws, hipStream_t stream) {
-    (void)extra_ws;
+                int32_t* idx, float* sel, const float* chunk_mm, int n_chunk_mm, hipStream_t stream) {
     const int64_t rows = batch * T;
     if (rows == 0) return 0;
     if (rows > 0x7fffffffLL) return -2;
     // the longest visible row is that of the last query
     int64_t nv_max = (q_pos0 + T) / m;
     if (nv_max > N) nv_max = N;
+    const dim3 grid((unsigned)rows), block(kThreads);
     if (nv_max <= kRowLds)
-        hipLaunchKernelGGL((topk_row_kernel<true>), dim3((unsigned)rows), dim3(kThreads), 0, stream, scores, ld, T,
-                           q_pos0, N, m, k, idx, sel);
+        hipLaunchKernelGGL((topk_bitmap<true>), grid, block, 0, stream, scores, ld, T, q_pos0, N, m, k, chunk_mm,
+                           n_chunk_mm, idx, sel);
+    else if (nv_max <= kBmMaxRow)
+        hipLaunchKernelGGL((topk_bitmap<false>), grid, block, 0, stream, scores, ld, T, q_pos0, N, m, k, chunk_mm,
+                           n_chunk_mm, idx, sel);
     else
-        hipLaunchKernelGGL((topk_row_kernel<false>), dim3((unsigned)rows), dim3(kThreads), 0, stream, scores, ld, T,
-                           q_pos0, N, m, k, idx, sel);
+        hipLaunchKernelGGL((topk_row_kernel<false>), grid, block, 0, stream, scores, ld, T, q_pos0, N, m, k, idx, sel);
     return 0;
 }
 
