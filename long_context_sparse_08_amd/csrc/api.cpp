@@ -130,12 +130,18 @@ int csa_index_topk(const void* qI, const float* w, const void* kI, int64_t batch
     const int64_t rows = batch * T;
     float* chunk_mm = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                                round_up((size_t)rows * (size_t)ld * sizeof(float)));
+    void* extra = reinterpret_cast<char*>(chunk_mm) + chunk_region(rows, N);
+    int64_t nv_max = (q_pos0 + T) / m;
+    if (nv_max > N) nv_max = N;
+    // the decode-shaped indexer clears the selection's per-row counters when it will use them
+    const int zero_words = csa::index_chunks(batch, T, N, H_I, c_I, qk_t) > 0 ? csa::topk_zero_words(rows, nv_max) : 0;
+    uint32_t* zero = zero_words > 0 ? csa::topk_zero_region(extra, rows, N) : nullptr;
     int n_chunk_mm = 0;
     rc = csa::launch_index_scores(qI, w, kI, batch, T, q_pos0, N, H_I, c_I, m, qk_t, scores, ld, false, chunk_mm,
-                                  &n_chunk_mm, st);
+                                  &n_chunk_mm, zero, zero_words, st);
     if (rc != 0) return finish(rc);
     return finish(csa::launch_topk(scores, ld, batch, T, q_pos0, N, m, k, idx, sel_scores,
-                                   n_chunk_mm > 0 ? chunk_mm : nullptr, n_chunk_mm, st));
+                                   n_chunk_mm > 0 ? chunk_mm : nullptr, n_chunk_mm, zero_words > 0 ? extra : nullptr, st));
 }
 
 int csa_index_scores(const void* qI, const float* w, const void* kI, int64_t batch, int64_t T, int64_t q_pos0, int64_t N,
@@ -145,7 +151,7 @@ int csa_index_scores(const void* qI, const float* w, const void* kI, int64_t bat
     if (batch == 0 || T == 0 || N == 0) return CSA_OK;
     if (!scores) return CSA_ERR_INVALID_ARG;
     return finish(csa::launch_index_scores(qI, w, kI, batch, T, q_pos0, N, H_I, c_I, m, qk_t, scores, N, true, nullptr,
-                                           nullptr, static_cast<hipStream_t>(stream)));
+                                           nullptr, nullptr, 0, static_cast<hipStream_t>(stream)));
 }
 
 size_t csa_topk_workspace_size(int64_t batch, int64_t T, int64_t N, int k) {
@@ -163,7 +169,7 @@ int csa_topk(const float* scores, int64_t ld, int64_t batch, int64_t T, int64_t 
     if (sel_scores && !aligned16(sel_scores)) return CSA_ERR_INVALID_ARG;
     if (!workspace || ws_bytes < csa_topk_workspace_size(batch, T, N, k) || !aligned16(workspace))
         return CSA_ERR_WORKSPACE;
-    return finish(csa::launch_topk(scores, ld, batch, T, q_pos0, N, m, k, idx, sel_scores, nullptr, 0,
+    return finish(csa::launch_topk(scores, ld, batch, T, q_pos0, N, m, k, idx, sel_scores, nullptr, 0, nullptr,
                                    static_cast<hipStream_t>(stream)));
 }
 

@@ -161,7 +161,8 @@ template <int DT, int MB, int TOK>
 __global__ void __launch_bounds__(256)
 index_scores_mfma(const void* __restrict__ qI, const float* __restrict__ w, const void* __restrict__ kI, int64_t batch,
                   int64_t T, int64_t q_pos0, int64_t N, int m, float* __restrict__ scores, int64_t ld,
-                  int write_invisible, int chunks, int cb, float* __restrict__ chunk_mm) {
+                  int write_invisible, int chunks, int cb, float* __restrict__ chunk_mm, uint32_t* __restrict__ zero,
+                  int zero_words) {
     using O = IdxOps<DT>;
     constexpr int H = 32 * MB;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -176,6 +177,8 @@ index_scores_mfma(const void* __restrict__ qI, const float* __restrict__ w, cons
     const int64_t row = b * T + t;
     const int64_t nv = visible_entries(q_pos0 + t, m, N);
     const int64_t nblk_all = (N + 31) / 32;
+    if (TOK == 1 && zero != nullptr && chunk == 0)   // clear the selection's per-row counters
+        for (int i = threadIdx.x; i < zero_words; i += 256) zero[row * zero_words + i] = 0u;
 
     // per-wave block list
     const int64_t blk0 = (int64_t)chunk * cb;
@@ -203,22 +206,28 @@ index_scores_mfma(const void* __restrict__ qI, const float* __restrict__ w, cons
 
     const int64_t kbase = b * N;
     float smin = INFINITY, smax = -INFINITY;   // over this wave's visible scores (TOK == 1)
-    int64_t blk = blk0 + first;
-    // two blocks in flight ahead of the one being computed
-    typename O::Frag kb0, kb1;
-    if (blk < blk1 && blk * 32 < nv) load_half_row<DT>(kI, kbase + min(blk * 32 + n, N - 1), g, kb0);
-    if (blk + step < blk1 && (blk + step) * 32 < nv)
-        load_half_row<DT>(kI, kbase + min((blk + step) * 32 + n, N - 1), g, kb1);
-    for (; blk < blk1; blk += step) {
-        const int64_t s = blk * 32 + n;
-        if (blk * 32 >= nv) {   // block wholly invisible (uniform over the wave)
-            if (write_invisible && g == 0 && s < N) out[s] = -INFINITY;
-            continue;
+
+    // this wave's blocks: blk0 + first + i*step for i < nb_all (those inside the chunk); the
+    // first nb of them hold visible entries (visibility is a prefix of the row)
+    const int64_t span = blk1 - (blk0 + first);
+    const int nb_all = span > 0 ? (int)((span + step - 1) / step) : 0;
+    const int64_t nvis_blk = (nv + 31) / 32;   // blocks with at least one visible entry
+    int nb = 0;
+    if (blk0 + first < nvis_blk) nb = (int)min((int64_t)nb_all, (nvis_blk - (blk0 + first) + step - 1) / step);
+    if (write_invisible && g == 0) {
+        for (int i = nb; i < nb_all; ++i) {
+            const int64_t s = (blk0 + first + (int64_t)i * step) * 32 + n;
+            if (s < N) out[s] = -INFINITY;
         }
-        typename O::Frag cur = kb0;
-        kb0 = kb1;
-        const int64_t nxt = blk + 2 * step;
-        if (nxt < blk1 && nxt * 32 < nv) load_half_row<DT>(kI, kbase + min(nxt * 32 + n, N - 1), g, kb1);
+    }
+    // three fragment buffers in a ring (the block computed + two in flight); loads are issued
+    // unconditionally, clamped to this wave's last visible block, so the waits stay static
+    auto load_blk = [&](typename O::Frag& f, int i) {
+        const int64_t bb = blk0 + first + (int64_t)min(i, nb - 1) * step;
+        load_half_row<DT>(kI, kbase + min(bb * 32 + n, N - 1), g, f);
+    };
+    auto compute_blk = [&](const typename O::Frag& cur, int i) {
+        const int64_t s = (blk0 + first + (int64_t)i * step) * 32 + n;
         float contrib = 0.f;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
@@ -235,6 +244,21 @@ index_scores_mfma(const void* __restrict__ qI, const float* __restrict__ w, cons
         if (s < nv) {
             smin = fminf(smin, contrib);
             smax = fmaxf(smax, contrib);
+        }
+    };
+    if (nb > 0) {
+        typename O::Frag f0, f1, f2;
+        load_blk(f0, 0);
+        load_blk(f1, 1);
+        for (int i = 0; i < nb; i += 3) {
+            load_blk(f2, i + 2);
+            compute_blk(f0, i);
+            if (i + 1 >= nb) break;
+            load_blk(f0, i + 3);
+            compute_blk(f1, i + 1);
+            if (i + 2 >= nb) break;
+            load_blk(f1, i + 4);
+            compute_blk(f2, i + 2);
         }
     }
     if constexpr (TOK == 1) {
@@ -260,7 +284,7 @@ bool mfma_shape(int H_I, int c_I, int qk_t) {
 template <int DT, int MB>
 int launch_mfma(const void* qI, const float* w, const void* kI, int64_t batch, int64_t T, int64_t q_pos0, int64_t N,
                 int m, float* scores, int64_t ld, bool write_invisible, float* chunk_mm, int* n_chunk_mm,
-                hipStream_t stream) {
+                uint32_t* zero, int zero_words, hipStream_t stream) {
     const int64_t nblk = (N + 31) / 32;
     if (T >= 4) {
         // prefill: 4 queries per workgroup share the key blocks
@@ -270,7 +294,8 @@ int launch_mfma(const void* qI, const float* w, const void* kI, int64_t batch, i
         const int64_t grid = groups * chunks;
         if (grid > 0x7fffffffLL) return -2;
         hipLaunchKernelGGL((index_scores_mfma<DT, MB, 4>), dim3((unsigned)grid), dim3(256), 0, stream, qI, w, kI, batch,
-                           T, q_pos0, N, m, scores, ld, write_invisible ? 1 : 0, chunks, cb, (float*)nullptr);
+                           T, q_pos0, N, m, scores, ld, write_invisible ? 1 : 0, chunks, cb, (float*)nullptr,
+                           (uint32_t*)nullptr, 0);
         if (n_chunk_mm) *n_chunk_mm = 0;
     } else {
         // decode: split each query's entries over workgroups sized so that the whole grid is
@@ -284,7 +309,8 @@ int launch_mfma(const void* qI, const float* w, const void* kI, int64_t batch, i
         const int64_t grid = batch * T * chunks;
         if (grid > 0x7fffffffLL) return -2;
         hipLaunchKernelGGL((index_scores_mfma<DT, MB, 1>), dim3((unsigned)grid), dim3(256), 0, stream, qI, w, kI, batch,
-                           T, q_pos0, N, m, scores, ld, write_invisible ? 1 : 0, chunks, cb, chunk_mm);
+                           T, q_pos0, N, m, scores, ld, write_invisible ? 1 : 0, chunks, cb, chunk_mm, zero,
+                           zero_words);
         if (n_chunk_mm) *n_chunk_mm = chunk_mm ? chunks : 0;
     }
     return 0;
@@ -304,19 +330,19 @@ int index_chunks(int64_t batch, int64_t T, int64_t N, int H_I, int c_I, int qk_t
 
 int launch_index_scores(const void* qI, const float* w, const void* kI, int64_t batch, int64_t T, int64_t q_pos0,
                         int64_t N, int H_I, int c_I, int m, int qk_t, float* scores, int64_t ld, bool write_invisible,
-                        float* chunk_mm, int* n_chunk_mm, hipStream_t stream) {
+                        float* chunk_mm, int* n_chunk_mm, uint32_t* zero, int zero_words, hipStream_t stream) {
     if (n_chunk_mm) *n_chunk_mm = 0;
     if (batch == 0 || T == 0 || N == 0) return 0;
     if (mfma_shape(H_I, c_I, qk_t)) {
         if (qk_t == DT_FP8)
             return H_I == 64 ? launch_mfma<DT_FP8, 2>(qI, w, kI, batch, T, q_pos0, N, m, scores, ld, write_invisible,
-                                                      chunk_mm, n_chunk_mm, stream)
+                                                      chunk_mm, n_chunk_mm, zero, zero_words, stream)
                              : launch_mfma<DT_FP8, 1>(qI, w, kI, batch, T, q_pos0, N, m, scores, ld, write_invisible,
-                                                      chunk_mm, n_chunk_mm, stream);
+                                                      chunk_mm, n_chunk_mm, zero, zero_words, stream);
         return H_I == 64 ? launch_mfma<DT_BF16, 2>(qI, w, kI, batch, T, q_pos0, N, m, scores, ld, write_invisible,
-                                                   chunk_mm, n_chunk_mm, stream)
+                                                   chunk_mm, n_chunk_mm, zero, zero_words, stream)
                          : launch_mfma<DT_BF16, 1>(qI, w, kI, batch, T, q_pos0, N, m, scores, ld, write_invisible,
-                                                   chunk_mm, n_chunk_mm, stream);
+                                                   chunk_mm, n_chunk_mm, zero, zero_words, stream);
     }
     switch (qk_t) {
         case DT_F32:

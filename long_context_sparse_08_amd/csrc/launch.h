@@ -17,9 +17,11 @@ int launch_compress(const void* Ca, const void* Za, const float* Ba, const void*
 // chunk_mm (optional, [batch*T, index_chunks(...)] pairs): min / max of each chunk of visible
 // scores, written by the decode-shaped MFMA kernel (chunks without visible entries hold
 // +inf / -inf); *n_chunk_mm receives the chunk count, 0 when the kernel used writes none.
+// zero / zero_words (optional): the decode-shaped kernel also zeroes zero_words uint32 per row
+// at zero + row * zero_words (the selection's per-row histogram and counters).
 int launch_index_scores(const void* qI, const float* w, const void* kI, int64_t batch, int64_t T, int64_t q_pos0,
                         int64_t N, int H_I, int c_I, int m, int qk_t, float* scores, int64_t ld, bool write_invisible,
-                        float* chunk_mm, int* n_chunk_mm, hipStream_t stream);
+                        float* chunk_mm, int* n_chunk_mm, uint32_t* zero, int zero_words, hipStream_t stream);
 
 // Number of (min, max) pairs per row the indexer writes into chunk_mm for these sizes (0: none).
 int index_chunks(int64_t batch, int64_t T, int64_t N, int H_I, int c_I, int qk_t);
@@ -29,8 +31,13 @@ size_t topk_extra_workspace(int64_t rows, int64_t N, int k);
 
 // Per-row top-k over the visible prefix of each score row.  chunk_mm / n_chunk_mm: optional
 // per-chunk (min, max) of the row's visible scores from the indexer (NULL / 0: not available).
+// extra_ws: topk_extra_workspace(...) bytes.  With chunk_mm, few rows and long rows, the
+// multi-workgroup path runs; it expects the region topk_zero_region(...) to hold zeros for the
+// topk_zero_words(...) words of each row (the decode indexer clears it).
 int launch_topk(const float* scores, int64_t ld, int64_t batch, int64_t T, int64_t q_pos0, int64_t N, int m, int k,
-                int32_t* idx, float* sel, const float* chunk_mm, int n_chunk_mm, hipStream_t stream);
+                int32_t* idx, float* sel, const float* chunk_mm, int n_chunk_mm, void* extra_ws, hipStream_t stream);
+int topk_zero_words(int64_t rows, int64_t nv_max);
+uint32_t* topk_zero_region(void* extra_ws, int64_t rows, int64_t N);
 
 // Device workspace bytes launch_sparse_mqa needs (0: none) for the key-range partials.
 size_t sparse_mqa_workspace(int64_t batch, int64_t T, int H, int c, int k, int t);

@@ -179,7 +179,11 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                 int64_t rows, int64_t T, int64_t N, int H, int k, int ks_count, int keys_per_split, float sl2,
                 int64_t q_pos0, int ratio, uint16_t* __restrict__ out, float* __restrict__ part,
                 float* __restrict__ part_ml) {
-    __shared__ __attribute__((aligned(16))) uint8_t stage[kMTeams * kMTeamStages * kMBuf];
+    // one array per pipeline parity (both teams' blocks): the DMA into one and the reads of
+    // the other are then provably disjoint, so no wait for the in-flight gather is forced
+    // before the current block's LDS reads
+    __shared__ __attribute__((aligned(16))) uint8_t stage_a[kMTeams * kMBuf];
+    __shared__ __attribute__((aligned(16))) uint8_t stage_b[kMTeams * kMBuf];
     __shared__ int32_t ids[DENSE ? 1 : CSA_MAX_TOPK_DEV];
     __shared__ float xm[4][16], xl[4][16];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -224,30 +228,21 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int nblk = (nkeys + kMBlk - 1) / kMBlk;
     const int npair = (nblk + kMTeams - 1) / kMTeams;   // iterations: one block per team each
     const uint16_t* kvseq = kv + b * N * (int64_t)kMC;
-    uint8_t* team_stage = stage + team * kMTeamStages * kMBuf;
-    auto gather = [&](int it, int buf) {   // this team's block of iteration `it`
+    auto gather = [&](int it, uint8_t* arr) {   // this team's block of iteration `it` into `arr`
         const int blk = kMTeams * it + team;
+        uint8_t* dst = arr + team * kMBuf;
 #pragma unroll
         for (int r8 = 0; r8 < kMLoadsPerBlk; ++r8) {
             const int r = kMLoadsPerBlk * tw + r8;
             int sidx = key_id(blk * kMBlk + r);
             if (sidx < 0 || sidx >= N) sidx = 0;   // invalid slots load row 0, masked below
             const uint16_t* src = kvseq + (int64_t)sidx * kMC + 8 * lane;
-            __builtin_amdgcn_global_load_lds((glb_void_ptr)src, (lds_void_ptr)(team_stage + buf * kMBuf + r * kMPitch),
-                                             16, 0, 0);
+            __builtin_amdgcn_global_load_lds((glb_void_ptr)src, (lds_void_ptr)(dst + r * kMPitch), 16, 0, 0);
         }
     };
-    __builtin_amdgcn_s_waitcnt(0);   // q is in registers
-    if (npair > 0) gather(0, 0);
-
-    for (int it = 0; it < npair; ++it) {
-        const int buf = it & 1;
-        wait_vmcnt<0>();
-        __syncthreads();   // iteration it is staged; every wave is done with iteration it-1
-        if (it + 1 < npair) gather(it + 1, buf ^ 1);
-        const uint8_t* st = team_stage + buf * kMBuf;
+    auto compute = [&](int it, const uint8_t* arr) {
+        const uint8_t* st = arr + team * kMBuf;
         const int blk = kMTeams * it + team;
-
         // validity of the 32 keys of this block (bit r); all-zero for a block past the range
         uint32_t valid = 0;
         {
@@ -320,6 +315,19 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
             const i16x8 va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
             acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, va), pb, acc[cb], 0, 0, 0);
         }
+    };
+    __builtin_amdgcn_s_waitcnt(0);   // q is in registers
+    if (npair > 0) gather(0, stage_a);
+    for (int it = 0; it < npair; it += 2) {
+        wait_vmcnt<0>();
+        __syncthreads();   // iteration it is staged in A; every wave is done with B
+        if (it + 1 < npair) gather(it + 1, stage_b);
+        compute(it, stage_a);
+        if (it + 1 >= npair) break;
+        wait_vmcnt<0>();
+        __syncthreads();   // iteration it+1 is staged in B; every wave is done with A
+        if (it + 2 < npair) gather(it + 2, stage_a);
+        compute(it + 1, stage_b);
     }
 
     // sum of the softmax denominators over the four lane groups that share a head
@@ -329,8 +337,8 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     // team 1 hands its state to team 0 (the stage buffers are free after this barrier)
     __syncthreads();
     constexpr int kXPitch = kMC + 4;   // padded head stride: the 16 heads of a write hit distinct banks
-    static_assert(4 * 16 * kXPitch * sizeof(float) <= sizeof(stage), "team handoff fits the stage buffers");
-    float* xacc = reinterpret_cast<float*>(stage) + tw * (16 * kXPitch);   // [head 16][col] per wave
+    static_assert(2 * 16 * kXPitch * sizeof(float) <= sizeof(stage_a), "team handoff fits the stage buffers");
+    float* xacc = reinterpret_cast<float*>(tw < 2 ? stage_a : stage_b) + (tw & 1) * (16 * kXPitch);
     if (team == 1) {
         if (g == 0) { xm[tw][n16] = m_run; xl[tw][n16] = l_run; }
 #pragma unroll

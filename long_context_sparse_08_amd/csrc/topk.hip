@@ -592,23 +592,363 @@ topk_bitmap(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
     }
 }
 
+
+// ============================================================================ multi-workgroup
+// Few long rows (decode: 8-32 rows of 32K-262K scores): the row is cut into slices of
+// kSlice entries and three kernels share the work.  Needs the indexer's per-chunk (min, max)
+// (the row range) and a per-row region the indexer zeroes (histogram + counters).
+//   tkm_hist   (row x slice)  slice histogram in LDS, added into the row histogram
+//   tkm_mark   (row x slice)  every slice finds b* from the row histogram; writes its words of
+//                             the row keep-bitmap (bins above b*) and appends b*'s members
+//   tkm_select (row)          ranks b*'s members, sets the bits of the kept ones, reads the
+//                             ordered output off the bitmap
+// If b* has more members than kMCap (heavy ties), tkm_select finds the cut with an exact
+// radix select over the row instead.
+constexpr int kSlice = 4096;
+constexpr int kMCap = 8192;
+constexpr int kZeroWords = kBins + 8;   // per row: histogram + counters, zeroed by the indexer
+constexpr int kSliceThreads = 256;
+
+struct MultiWs {
+    uint32_t* zero;    // [rows][kZeroWords]: hist[kBins], then counter[0] = b* member count
+    float* cval;       // [rows][kMCap]
+    int32_t* cidx;     // [rows][kMCap]
+    uint32_t* bits;    // [rows][words]
+    int64_t words;     // bitmap words per row
+};
+
+__host__ inline size_t multi_bytes(int64_t rows, int64_t N, MultiWs* L, void* base) {
+    const int64_t words = (N + 63) / 64 * 2;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off += (bytes + 255) & ~size_t(255); return o; };
+    const size_t o_zero = take((size_t)rows * kZeroWords * 4);
+    const size_t o_cval = take((size_t)rows * kMCap * 4);
+    const size_t o_cidx = take((size_t)rows * kMCap * 4);
+    const size_t o_bits = take((size_t)rows * words * 4);
+    if (L && base) {
+        uint8_t* b = static_cast<uint8_t*>(base);
+        L->zero = reinterpret_cast<uint32_t*>(b + o_zero);
+        L->cval = reinterpret_cast<float*>(b + o_cval);
+        L->cidx = reinterpret_cast<int32_t*>(b + o_cidx);
+        L->bits = reinterpret_cast<uint32_t*>(b + o_bits);
+        L->words = words;
+    }
+    return off;
+}
+
+__device__ __forceinline__ void row_range_mm(const float* mm, int nmm, float& lo, float& inv) {
+    float l = INFINITY, h = -INFINITY;
+    for (int i = 0; i < nmm; ++i) {
+        l = fminf(l, mm[2 * i]);
+        h = fmaxf(h, mm[2 * i + 1]);
+    }
+    float iv = (float)kBins / (h - l);
+    if (!(h > l) || !isfinite(iv)) iv = 0.f;
+    lo = l;
+    inv = iv;
+}
+
+__global__ void __launch_bounds__(kSliceThreads)
+tkm_hist(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_pos0, int64_t N, int m, int k,
+         const float* __restrict__ mm, int nmm, int P, MultiWs L) {
+    __shared__ uint32_t h[kBins];
+    __shared__ float s_lo, s_inv;
+    const int64_t row = blockIdx.x / P;
+    const int p = (int)(blockIdx.x % P);
+    const int64_t nv = visible_entries(q_pos0 + row % T, m, N);
+    if (nv <= k) return;
+    const int64_t s0 = (int64_t)p * kSlice, s1 = min(nv, s0 + kSlice);
+    if (s0 >= s1) return;
+    for (int i = threadIdx.x; i < kBins; i += kSliceThreads) h[i] = 0u;
+    if (threadIdx.x == 0) {
+        float lo, inv;
+        row_range_mm(mm + row * (int64_t)nmm * 2, nmm, lo, inv);
+        s_lo = lo;
+        s_inv = inv;
+    }
+    __syncthreads();
+    const float lo = s_lo, inv = s_inv;
+    const float* sc = scores + row * ld;
+    // 16 entries per thread, loads issued before use
+    float v[kSlice / kSliceThreads];
+#pragma unroll
+    for (int u = 0; u < kSlice / kSliceThreads; ++u) {
+        const int64_t s = s0 + threadIdx.x + (int64_t)u * kSliceThreads;
+        v[u] = s < s1 ? sc[s] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kSlice / kSliceThreads; ++u)
+        if (s0 + threadIdx.x + (int64_t)u * kSliceThreads < s1) atomicAdd(&h[bin_of(v[u], lo, inv)], 1u);
+    __syncthreads();
+    uint32_t* hg = L.zero + row * kZeroWords;
+    for (int i = threadIdx.x; i < kBins; i += kSliceThreads)
+        if (h[i]) atomicAdd(&hg[i], h[i]);
+}
+
+// b* and need from the row histogram (all threads of the block get them)
+__device__ __forceinline__ void find_bstar(const uint32_t* hg, int k, uint32_t* sh_hist, uint32_t* scan, int& bstar,
+                                           uint32_t& need, int nthreads) {
+    // suffix sums over bins from the top: thread t owns kBins/nthreads consecutive bins
+    const int per = kBins / nthreads;
+    const int tid = threadIdx.x;
+    const int top = kBins - 1 - tid * per;
+    uint32_t mine = 0;
+    for (int j = 0; j < per; ++j) {
+        const uint32_t c = hg[top - j];
+        sh_hist[top - j] = c;
+        mine += c;
+    }
+    // inclusive scan of `mine` over threads (thread 0 = highest bins)
+    const int lane = tid & 63, wid = tid >> 6;
+    uint32_t inc = mine;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const uint32_t y = __shfl_up(inc, off, kWave);
+        if (lane >= off) inc += y;
+    }
+    if (lane == kWave - 1) scan[wid] = inc;
+    __syncthreads();
+    uint32_t before_w = 0;
+    for (int w = 0; w < wid; ++w) before_w += scan[w];
+    const uint32_t before = before_w + inc - mine;
+    if (before < (uint32_t)k && before + mine >= (uint32_t)k) {
+        uint32_t acc = before;
+        for (int j = 0; j < per; ++j) {
+            const uint32_t c = sh_hist[top - j];
+            if (acc + c >= (uint32_t)k) {
+                scan[nthreads / kWave] = (uint32_t)(top - j);
+                scan[nthreads / kWave + 1] = (uint32_t)k - acc;
+                break;
+            }
+            acc += c;
+        }
+    }
+    __syncthreads();
+    bstar = (int)scan[nthreads / kWave];
+    need = scan[nthreads / kWave + 1];
+}
+
+__global__ void __launch_bounds__(kSliceThreads)
+tkm_mark(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_pos0, int64_t N, int m, int k,
+         const float* __restrict__ mm, int nmm, int P, MultiWs L) {
+    __shared__ uint32_t sh_hist[kBins];
+    __shared__ uint32_t scan[kSliceThreads / kWave + 2];
+    __shared__ float s_lo, s_inv;
+    const int64_t row = blockIdx.x / P;
+    const int p = (int)(blockIdx.x % P);
+    const int64_t nv = visible_entries(q_pos0 + row % T, m, N);
+    if (nv <= k) return;
+    const int64_t s0 = (int64_t)p * kSlice, s1 = min(nv, s0 + kSlice);
+    if (s0 >= s1) return;
+    if (threadIdx.x == 0) {
+        float lo, inv;
+        row_range_mm(mm + row * (int64_t)nmm * 2, nmm, lo, inv);
+        s_lo = lo;
+        s_inv = inv;
+        scan[kSliceThreads / kWave] = 0;
+        scan[kSliceThreads / kWave + 1] = (uint32_t)k;
+    }
+    int bstar;
+    uint32_t need;
+    uint32_t* hg = L.zero + row * kZeroWords;
+    __syncthreads();
+    find_bstar(hg, k, sh_hist, scan, bstar, need, kSliceThreads);
+    const float lo = s_lo, inv = s_inv;
+    const float* sc = scores + row * ld;
+    uint32_t* bits = L.bits + row * L.words;
+    uint32_t* ccount = hg + kBins;
+    float* cval = L.cval + row * kMCap;
+    int32_t* cidx = L.cidx + row * kMCap;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    // each wave takes 64-entry runs: one ballot gives two bitmap words
+    for (int64_t b0 = s0 + (int64_t)wid * kWave; b0 < s1; b0 += kSliceThreads) {
+        const int64_t s = b0 + lane;
+        const bool ok = s < s1;
+        const float v = ok ? sc[s] : 0.f;
+        const int bn = ok ? bin_of(v, lo, inv) : -1;
+        const unsigned long long above = __ballot(bn > bstar);
+        if (bn == bstar) {
+            const uint32_t pos = atomicAdd(ccount, 1u);
+            if (pos < (uint32_t)kMCap) { cval[pos] = v; cidx[pos] = (int32_t)s; }
+        }
+        if (lane == 0) {
+            bits[b0 >> 5] = (uint32_t)above;
+            bits[(b0 >> 5) + 1] = (uint32_t)(above >> 32);
+        }
+    }
+}
+
+__global__ void __launch_bounds__(kThreads)
+tkm_select(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_pos0, int64_t N, int m, int k,
+           const float* __restrict__ mm, int nmm, MultiWs L, int32_t* __restrict__ idx, float* __restrict__ sel) {
+    __shared__ uint32_t sh_hist[kBins];
+    __shared__ uint32_t scan[kThreads / kWave + 2];
+    __shared__ float cv[kCap];
+    __shared__ int32_t ci[kCap];
+    __shared__ uint32_t s_prefix, s_pmask, s_rem;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int64_t row = blockIdx.x;
+    const int64_t nv = visible_entries(q_pos0 + row % T, m, N);
+    const float* sc = scores + row * ld;
+    int32_t* oi = idx + row * k;
+    float* os = sel ? sel + row * k : nullptr;
+    if (nv <= k) {
+        for (int r = tid; r < k; r += kThreads) {
+            oi[r] = r < nv ? r : -1;
+            if (os) os[r] = r < nv ? sc[r] : -INFINITY;
+        }
+        return;
+    }
+    uint32_t* hg = L.zero + row * kZeroWords;
+    uint32_t* bits = L.bits + row * L.words;
+    if (tid == 0) { scan[kThreads / kWave] = 0; scan[kThreads / kWave + 1] = (uint32_t)k; }
+    __syncthreads();
+    int bstar;
+    uint32_t need;
+    find_bstar(hg, k, sh_hist, scan, bstar, need, kThreads);
+    const uint32_t ncand = hg[kBins];
+    if (ncand <= (uint32_t)kCap) {
+        const float* cval = L.cval + row * kMCap;
+        const int32_t* cidx = L.cidx + row * kMCap;
+        for (uint32_t i = tid; i < ncand; i += kThreads) { cv[i] = cval[i]; ci[i] = cidx[i]; }
+        __syncthreads();
+        for (uint32_t i = tid; i < ncand; i += kThreads) {
+            const uint32_t ki = order_key(cv[i]);
+            const int32_t si = ci[i];
+            uint32_t rank = 0;
+            for (uint32_t j = 0; j < ncand; ++j) {
+                const uint32_t kj = order_key(cv[j]);
+                rank += (kj > ki || (kj == ki && ci[j] < si)) ? 1u : 0u;
+            }
+            if (rank < need) atomicOr(&bits[si >> 5], 1u << (si & 31));
+        }
+    } else {
+        // heavy ties in b*: exact radix select of the need-th largest order key among b*'s
+        // members, over the row in global memory
+        float lo, inv;
+        row_range_mm(mm + row * (int64_t)nmm * 2, nmm, lo, inv);
+        if (tid == 0) { s_prefix = 0u; s_pmask = 0u; s_rem = need; }
+        __syncthreads();
+        for (int shift = 24; shift >= 0; shift -= 8) {
+            for (int i = tid; i < 256; i += kThreads) sh_hist[i] = 0u;
+            __syncthreads();
+            const uint32_t prefix = s_prefix, pmask = s_pmask;
+            for (int64_t s = tid; s < nv; s += kThreads) {
+                const float v = sc[s];
+                if (bin_of(v, lo, inv) != bstar) continue;
+                const uint32_t key = order_key(v);
+                if ((key & pmask) == prefix) atomicAdd(&sh_hist[(key >> shift) & 255u], 1u);
+            }
+            __syncthreads();
+            if (tid == 0) {
+                uint32_t remaining = s_rem, acc = 0;
+                for (int d = 255; d >= 0; --d) {
+                    const uint32_t hh = sh_hist[d];
+                    if (acc + hh >= remaining) {
+                        s_prefix = prefix | ((uint32_t)d << shift);
+                        s_pmask = pmask | (255u << shift);
+                        s_rem = remaining - acc;
+                        break;
+                    }
+                    acc += hh;
+                }
+            }
+            __syncthreads();
+        }
+        const uint32_t kstar = s_prefix, need_eq = s_rem;
+        // members above K* are kept; of those equal to K*, the need_eq lowest indices
+        const int64_t seg = ((nv + (int64_t)kWaves * kWave - 1) / ((int64_t)kWaves * kWave)) * kWave;
+        const int64_t a = (int64_t)wid * seg, e = min(nv, a + seg);
+        const unsigned long long lt = (1ull << lane) - 1ull;
+        uint32_t c_eq = 0;
+        for (int64_t b0 = a; b0 < e; b0 += kWave) {
+            const int64_t s = b0 + lane;
+            const bool ok = s < e;
+            const float v = ok ? sc[s] : 0.f;
+            const bool inb = ok && bin_of(v, lo, inv) == bstar;
+            const uint32_t key = order_key(v);
+            if (inb && key > kstar) atomicOr(&bits[s >> 5], 1u << (s & 31));
+            c_eq += __popcll(__ballot(inb && key == kstar));
+        }
+        if (lane == 0) scan[wid] = c_eq;
+        __syncthreads();
+        uint32_t run = 0;
+        for (int v = 0; v < wid; ++v) run += scan[v];
+        for (int64_t b0 = a; b0 < e; b0 += kWave) {
+            const int64_t s = b0 + lane;
+            const bool ok = s < e;
+            const float v = ok ? sc[s] : 0.f;
+            const bool is_eq = ok && bin_of(v, lo, inv) == bstar && order_key(v) == kstar;
+            const unsigned long long meq = __ballot(is_eq);
+            if (is_eq && run + __popcll(meq & lt) < need_eq) atomicOr(&bits[s >> 5], 1u << (s & 31));
+            run += __popcll(meq);
+        }
+    }
+    __threadfence();   // the bit updates above are device-memory atomics: make them visible
+    __syncthreads();
+    // ordered extraction: each thread owns a run of bitmap words
+    const int64_t nwords = (nv + 31) >> 5;
+    const int64_t per = (nwords + kThreads - 1) / kThreads;
+    const int64_t w0 = (int64_t)tid * per, w1 = min(nwords, w0 + per);
+    uint32_t cnt = 0;
+    for (int64_t w = w0; w < w1; ++w) {
+        uint32_t word = bits[w];
+        if (w == nwords - 1 && (nv & 31)) word &= (1u << (nv & 31)) - 1u;
+        cnt += __popc(word);
+    }
+    uint32_t total;
+    uint32_t pos = block_excl_scan(cnt, scan, &total);
+    for (int64_t w = w0; w < w1; ++w) {
+        uint32_t word = bits[w];
+        if (w == nwords - 1 && (nv & 31)) word &= (1u << (nv & 31)) - 1u;
+        while (word) {
+            const int b = __ffs(word) - 1;
+            word &= word - 1;
+            const int64_t s = (w << 5) + b;
+            if (pos < (uint32_t)k) {
+                oi[pos] = (int32_t)s;
+                if (os) os[pos] = sc[s];
+            }
+            ++pos;
+        }
+    }
+}
+
+// rows that fit the LDS staging are faster in one workgroup (no inter-kernel round trips)
+bool multi_rows(int64_t rows, int64_t nv_max) { return rows < 256 && nv_max > kRowLds; }
+
 }  // namespace
 
 size_t topk_extra_workspace(int64_t rows, int64_t N, int k) {
-    (void)rows;
-    (void)N;
     (void)k;
-    return 0;
+    if (!multi_rows(rows, N)) return 0;
+    return multi_bytes(rows, N, nullptr, nullptr);
 }
 
+int topk_zero_words(int64_t rows, int64_t nv_max) { return multi_rows(rows, nv_max) ? kZeroWords : 0; }
+
 int launch_topk(const float* scores, int64_t ld, int64_t batch, int64_t T, int64_t q_pos0, int64_t N, int m, int k,
-                int32_t* idx, float* sel, const float* chunk_mm, int n_chunk_mm, hipStream_t stream) {
+                int32_t* idx, float* sel, const float* chunk_mm, int n_chunk_mm, void* extra_ws, hipStream_t stream) {
     const int64_t rows = batch * T;
     if (rows == 0) return 0;
     if (rows > 0x7fffffffLL) return -2;
     // the longest visible row is that of the last query
     int64_t nv_max = (q_pos0 + T) / m;
     if (nv_max > N) nv_max = N;
+    if (chunk_mm != nullptr && extra_ws != nullptr && multi_rows(rows, nv_max)) {
+        // the indexer zeroed the per-row histogram / counter region (topk_zero_words)
+        MultiWs L;
+        multi_bytes(rows, N, &L, extra_ws);
+        const int P = (int)((nv_max + kSlice - 1) / kSlice);
+        const dim3 grid((unsigned)(rows * P));
+        hipLaunchKernelGGL(tkm_hist, grid, dim3(kSliceThreads), 0, stream, scores, ld, T, q_pos0, N, m, k, chunk_mm,
+                           n_chunk_mm, P, L);
+        hipLaunchKernelGGL(tkm_mark, grid, dim3(kSliceThreads), 0, stream, scores, ld, T, q_pos0, N, m, k, chunk_mm,
+                           n_chunk_mm, P, L);
+        hipLaunchKernelGGL(tkm_select, dim3((unsigned)rows), dim3(kThreads), 0, stream, scores, ld, T, q_pos0, N, m, k,
+                           chunk_mm, n_chunk_mm, L, idx, sel);
+        return 0;
+    }
     const dim3 grid((unsigned)rows), block(kThreads);
     if (nv_max <= kRowLds)
         hipLaunchKernelGGL((topk_bitmap<true>), grid, block, 0, stream, scores, ld, T, q_pos0, N, m, k, chunk_mm,
@@ -619,6 +959,12 @@ int launch_topk(const float* scores, int64_t ld, int64_t batch, int64_t T, int64
     else
         hipLaunchKernelGGL((topk_row_kernel<false>), grid, block, 0, stream, scores, ld, T, q_pos0, N, m, k, idx, sel);
     return 0;
+}
+
+uint32_t* topk_zero_region(void* extra_ws, int64_t rows, int64_t N) {
+    MultiWs L;
+    multi_bytes(rows, N, &L, extra_ws);
+    return L.zero;
 }
 
 }  // namespace csa
