@@ -144,12 +144,11 @@ typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef __attribute__((address_space(1))) void* glb_void_ptr;
 
 constexpr int kMC = 512;                       // head dim handled by the MFMA kernel
-constexpr int kMHeadsWG = 64;                  // heads per workgroup (16 per wave)
+constexpr int kMHeadsWG = 64;                  // heads per workgroup
 constexpr int kMBlk = 32;                      // keys per staged block
 constexpr int kMPitch = kMC * 2 + 32;          // LDS bytes per staged row (bank spread)
 constexpr int kMBuf = kMBlk * kMPitch;         // bytes per staged block
-constexpr int kMColBlk = kMC / 16;             // 16-column blocks of the output
-constexpr int kMLoadsPerBlk = kMBlk / 4;       // rows each wave of a team stages per block (8)
+constexpr int kMLoadsPerBlk = kMBlk / 4;       // rows each of the 4 waves stages per block (8)
 
 // s_waitcnt with vmcnt = n (0..63), expcnt and lgkmcnt left at their maximum (no wait)
 template <int n>
@@ -158,36 +157,70 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
 }
 
+// two floats to bf16 (round to nearest even, v_cvt_pk_bf16_f32), a in the low half
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    return f32_to_bf16_rne(a) | (f32_to_bf16_rne(b) << 16);
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// max / sum of x over lanes l and l^32 (l^16): gfx950's lane swaps return the pair
+// {x[l], x[l^32]} ({x[l], x[l^16]}) in the two results, on the VALU instead of through LDS
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // DENSE: the key list of the query at position p is 0 .. nv-1 with nv the number of HCA
 // entries it may see (ratio*(s+1)-1 <= p); `k` is then unused.
 //
-// Workgroup = 8 waves = two key teams of 4 waves (2 waves per SIMD, so one wave's LDS and
-// matrix-core latencies hide behind the other's work).  Team t computes the blocks
-// t, t+2, t+4, ... of the workgroup's key range; inside a team wave w owns heads 16w..16w+15.
-// Each team has two staging buffers, so while a block pair is computed the next pair loads.
-// At the end team 1 hands its (running max, running sum, acc) to team 0 through LDS.
-constexpr int kMTeams = 2;
-constexpr int kMTeamStages = 2;
+// Workgroup = 4 waves over the workgroup's 64 heads and key range, ~80 KB of LDS, so two
+// workgroups share a CU (one wave of each per SIMD).  Their barriers are independent, so the
+// phases of the two drift apart and one workgroup's softmax and barrier waits overlap the
+// other's matrix-core work.  The scores and their softmax are split by heads (wave w: heads
+// 16w..16w+15) and the P.KV product by output columns (wave w: columns 128w..128w+127 for all
+// 64 heads).  The P.KV operand is the transposed KV block, read from LDS with transposing
+// reads that run at about half the rate of plain ones; split by columns, each transposed
+// fragment feeds four head tiles instead of one.  The waves swap their bf16 probability
+// tiles (1 KB each) and rescale factors through LDS once per block.  Two staging buffers:
+// while one 32-key block is computed the next one loads.
+constexpr int kMWaves = 4;
+constexpr int kMHT = kMHeadsWG / 16;      // 16-head tiles per workgroup (4)
+constexpr int kMColW = kMC / kMHT;        // output columns per wave (128)
+constexpr int kMColBlkW = kMColW / 16;    // 16-column blocks per wave (8)
+constexpr int kMIdsLds = 1024;            // key ids staged per workgroup (longer ranges are split)
+constexpr int kMFillWGs = 256;            // workgroups a key split aims for
 
 template <bool DENSE>
-__global__ void __launch_bounds__(512)
+__global__ void __launch_bounds__(kMWaves * kWave, 2)   // two waves per SIMD: two workgroups per CU
 mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
                 int64_t rows, int64_t T, int64_t N, int H, int k, int ks_count, int keys_per_split, float sl2,
                 int64_t q_pos0, int ratio, uint16_t* __restrict__ out, float* __restrict__ part,
                 float* __restrict__ part_ml) {
-    // one array per pipeline parity (both teams' blocks): the DMA into one and the reads of
-    // the other are then provably disjoint, so no wait for the in-flight gather is forced
-    // before the current block's LDS reads
-    __shared__ __attribute__((aligned(16))) uint8_t stage_a[kMTeams * kMBuf];
-    __shared__ __attribute__((aligned(16))) uint8_t stage_b[kMTeams * kMBuf];
-    __shared__ int32_t ids[DENSE ? 1 : CSA_MAX_TOPK_DEV];
-    __shared__ float xm[4][16], xl[4][16];
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int team = wid >> 2, tw = wid & 3;
+    // one array per pipeline parity: the DMA into one and the reads of the other are then
+    // provably disjoint, so no wait for the in-flight gather is forced before the current
+    // block's LDS reads
+    __shared__ __attribute__((aligned(16))) uint8_t stage_a[kMBuf];
+    __shared__ __attribute__((aligned(16))) uint8_t stage_b[kMBuf];
+    __shared__ int32_t ids[DENSE ? 1 : kMIdsLds];
+    __shared__ uint4 xp[kMHT][kWave];     // probability tiles, B-operand lane layout
+    __shared__ float xalpha[kMHT][16];    // rescale factor per head of a tile
+    __shared__ int xflag[kMHT];           // tile rescaled in the current block
+    __shared__ float xm[kMHT][16], xl[kMHT][16];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int tw = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: kept in scalar registers
     const int g = lane >> 4, n16 = lane & 15;
     const int HG = H / kMHeadsWG;
     // XCD-aware order: consecutive units of a row go to one XCD (workgroups are dealt
@@ -203,34 +236,34 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int64_t klen = DENSE ? visible_entries(q_pos0 + row % T, ratio, N) : (int64_t)k;
     const int key0 = ks * keys_per_split;
     const int nkeys = (int)max((int64_t)0, min(klen, (int64_t)key0 + keys_per_split) - key0);
-    const int h0 = hg * kMHeadsWG + 16 * tw;
+    const int h0 = hg * kMHeadsWG;
     auto key_id = [&](int i) -> int {   // key id of slot i of this range (-1: none)
         if (i >= nkeys) return -1;
         if constexpr (DENSE) return key0 + i;
         else return ids[i];
     };
+
+    // this wave's q (head tile tw) as the B operand of S^T: head n16, channels 32*s + 8*g .. +8
+    bf16x8_t qb[kMC / 32];
+    const uint16_t* qrow = q + ((row * H) + h0 + 16 * tw + n16) * (int64_t)kMC + 8 * g;
+#pragma unroll
+    for (int s = 0; s < kMC / 32; ++s) qb[s] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * s);
     if constexpr (!DENSE) {
-        for (int i = tid; i < nkeys; i += 512) ids[i] = idx[row * k + key0 + i];
+        for (int i = tid; i < nkeys; i += kMWaves * kWave) ids[i] = idx[row * k + key0 + i];
         __syncthreads();
     }
 
-    // this wave's q as the B operand of S^T: head n16, channels 32*s + 8*g .. +8
-    bf16x8_t qb[kMC / 32];
-    const uint16_t* qrow = q + ((row * H) + h0 + n16) * (int64_t)kMC + 8 * g;
+    // O^T of this wave: columns 128*tw + 16*cb + 4*g + i, head 16*ht + n16
+    f32x4 acc[kMHT][kMColBlkW];
 #pragma unroll
-    for (int s = 0; s < kMC / 32; ++s) qb[s] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * s);
-
-    f32x4 acc[kMColBlk];
+    for (int ht = 0; ht < kMHT; ++ht)
 #pragma unroll
-    for (int cb = 0; cb < kMColBlk; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;
+        for (int cb = 0; cb < kMColBlkW; ++cb) acc[ht][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;   // head 16*tw + n16
 
     const int nblk = (nkeys + kMBlk - 1) / kMBlk;
-    const int npair = (nblk + kMTeams - 1) / kMTeams;   // iterations: one block per team each
     const uint16_t* kvseq = kv + b * N * (int64_t)kMC;
-    auto gather = [&](int it, uint8_t* arr) {   // this team's block of iteration `it` into `arr`
-        const int blk = kMTeams * it + team;
-        uint8_t* dst = arr + team * kMBuf;
+    auto gather = [&](int blk, uint8_t* dst) {   // block `blk` of the range into `dst`
 #pragma unroll
         for (int r8 = 0; r8 < kMLoadsPerBlk; ++r8) {
             const int r = kMLoadsPerBlk * tw + r8;
@@ -240,10 +273,8 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
             __builtin_amdgcn_global_load_lds((glb_void_ptr)src, (lds_void_ptr)(dst + r * kMPitch), 16, 0, 0);
         }
     };
-    auto compute = [&](int it, const uint8_t* arr) {
-        const uint8_t* st = arr + team * kMBuf;
-        const int blk = kMTeams * it + team;
-        // validity of the 32 keys of this block (bit r); all-zero for a block past the range
+    auto compute = [&](int blk, const uint8_t* st) {
+        // validity of the 32 keys of this block (bit r)
         uint32_t valid = 0;
         {
             const int sidx = key_id(blk * kMBlk + (lane & 31));
@@ -261,7 +292,7 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
             sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qb[s], sacc[0], 0, 0, 0);
             sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qb[s], sacc[1], 0, 0, 0);
         }
-        // online softmax for head n16 (values of lane: keys 16*hb + 4g + i)
+        // online softmax for head 16*tw + n16 (values of lane: keys 16*hb + 4g + i)
         float p[8];
         float bmax = -INFINITY;
 #pragma unroll
@@ -273,25 +304,24 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                 p[4 * hb + i] = v;
                 bmax = fmaxf(bmax, v);
             }
-        bmax = fmaxf(bmax, __shfl_xor(bmax, 16, kWave));
-        bmax = fmaxf(bmax, __shfl_xor(bmax, 32, kWave));
+        bmax = max_xor32(max_xor16(bmax));
         // Lazy rescale: the reference max moves (and acc / l are rescaled) only when a logit
         // exceeds it by more than 2^8 in the exp2 domain; otherwise p <= 256, exact enough in
         // bf16 / fp32.  Decided for the whole wave (a lane whose max did not grow gets 1).
-        if (__any(bmax > m_run + 8.f)) {
+        const bool resc = __any(bmax > m_run + 8.f);
+        if (resc) {
             const float m_new = fmaxf(m_run, bmax);
-            const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);   // 0 at the first valid block
+            const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);   // 0 at the first valid block
             l_run *= alpha;
-#pragma unroll
-            for (int cb = 0; cb < kMColBlk; ++cb) acc[cb] = acc[cb] * alpha;
             m_run = m_new;
+            if (g == 0) xalpha[tw][n16] = alpha;
         }
         // while nothing valid has been seen m_run is -inf and every p is exp2(-inf) = 0
         const float m_ref = m_run == -INFINITY ? 0.f : m_run;
         float psum = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            p[e] = exp2f(p[e] - m_ref);
+            p[e] = __builtin_amdgcn_exp2f(p[e] - m_ref);   // argument <= 8: no range reduction needed
             psum += p[e];
         }
         l_run += psum;
@@ -300,85 +330,86 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
         pw.y = pack_bf16x2(p[2], p[3]);
         pw.z = pack_bf16x2(p[4], p[5]);
         pw.w = pack_bf16x2(p[6], p[7]);
-        const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
+        xp[tw][lane] = pw;
+        if (lane == 0) xflag[tw] = resc ? 1 : 0;
+        __syncthreads();   // the four probability tiles and rescale factors are published
 
-        // O^T += V^T P^T: V^T operand via transpose reads of keys {4g..4g+3} and {16+4g..}
-        const uint8_t* vbase0 = st + (4 * g + (n16 >> 2)) * kMPitch + 8 * (n16 & 3);
+        bf16x8_t pb[kMHT];
+#pragma unroll
+        for (int ht = 0; ht < kMHT; ++ht) {
+            pb[ht] = __builtin_bit_cast(bf16x8_t, xp[ht][lane]);
+            if (__builtin_amdgcn_readfirstlane(xflag[ht])) {
+                const float a = xalpha[ht][n16];
+#pragma unroll
+                for (int cb = 0; cb < kMColBlkW; ++cb) acc[ht][cb] = acc[ht][cb] * a;
+            }
+        }
+
+        // O^T += V^T P^T over this wave's columns: V^T operand via transpose reads of keys
+        // {4g..4g+3} and {16+4g..}, shared by the four head tiles
+        const uint8_t* vbase0 = st + (4 * g + (n16 >> 2)) * kMPitch + 8 * (n16 & 3) + 2 * kMColW * tw;
         const uint8_t* vbase1 = vbase0 + 16 * kMPitch;
 #pragma unroll
-        for (int cb = 0; cb < kMColBlk; ++cb) {
+        for (int cb = 0; cb < kMColBlkW; ++cb) {
             const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(
                 vbase0 + 32 * cb));
             const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(
                 vbase1 + 32 * cb));
             typedef short i16x8 __attribute__((ext_vector_type(8)));
             const i16x8 va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-            acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, va), pb, acc[cb], 0, 0, 0);
+            const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, va);
+#pragma unroll
+            for (int ht = 0; ht < kMHT; ++ht)
+                acc[ht][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pb[ht], acc[ht][cb], 0, 0, 0);
         }
     };
     __builtin_amdgcn_s_waitcnt(0);   // q is in registers
-    if (npair > 0) gather(0, stage_a);
-    for (int it = 0; it < npair; it += 2) {
+    if (nblk > 0) gather(0, stage_a);
+    for (int blk = 0; blk < nblk; blk += 2) {
         wait_vmcnt<0>();
-        __syncthreads();   // iteration it is staged in A; every wave is done with B
-        if (it + 1 < npair) gather(it + 1, stage_b);
-        compute(it, stage_a);
-        if (it + 1 >= npair) break;
+        __syncthreads();   // block blk is staged in A; every wave is done with B
+        if (blk + 1 < nblk) gather(blk + 1, stage_b);
+        compute(blk, stage_a);
+        if (blk + 1 >= nblk) break;
         wait_vmcnt<0>();
-        __syncthreads();   // iteration it+1 is staged in B; every wave is done with A
-        if (it + 2 < npair) gather(it + 2, stage_a);
-        compute(it + 1, stage_b);
+        __syncthreads();   // block blk+1 is staged in B; every wave is done with A
+        if (blk + 2 < nblk) gather(blk + 2, stage_a);
+        compute(blk + 1, stage_b);
     }
 
     // sum of the softmax denominators over the four lane groups that share a head
-    l_run += __shfl_xor(l_run, 16, kWave);
-    l_run += __shfl_xor(l_run, 32, kWave);
-
-    // team 1 hands its state to team 0 (the stage buffers are free after this barrier)
-    __syncthreads();
-    constexpr int kXPitch = kMC + 4;   // padded head stride: the 16 heads of a write hit distinct banks
-    static_assert(2 * 16 * kXPitch * sizeof(float) <= sizeof(stage_a), "team handoff fits the stage buffers");
-    float* xacc = reinterpret_cast<float*>(tw < 2 ? stage_a : stage_b) + (tw & 1) * (16 * kXPitch);
-    if (team == 1) {
-        if (g == 0) { xm[tw][n16] = m_run; xl[tw][n16] = l_run; }
-#pragma unroll
-        for (int cb = 0; cb < kMColBlk; ++cb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) xacc[n16 * kXPitch + 16 * cb + 4 * g + i] = acc[cb][i];
+    l_run = sum_xor32(sum_xor16(l_run));
+    if (g == 0) {
+        xm[tw][n16] = m_run;
+        xl[tw][n16] = l_run;
     }
     __syncthreads();
-    if (team == 1) return;
-    {
-        const float m1 = xm[tw][n16], l1 = xl[tw][n16];
-        const float M = fmaxf(m_run, m1);
-        const float a0 = M == -INFINITY ? 0.f : exp2f(m_run - M);
-        const float a1 = M == -INFINITY ? 0.f : exp2f(m1 - M);
-        l_run = l_run * a0 + l1 * a1;
-        m_run = M;
-#pragma unroll
-        for (int cb = 0; cb < kMColBlk; ++cb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[cb][i] = acc[cb][i] * a0 + xacc[n16 * kXPitch + 16 * cb + 4 * g + i] * a1;
-    }
-    const int64_t head_row = row * H + h0 + n16;
+    const int c0 = kMColW * tw;
     if (part == nullptr) {
-        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-        uint16_t* orow = out + head_row * kMC;
 #pragma unroll
-        for (int cb = 0; cb < kMColBlk; ++cb) {
-            uint2 w2;
-            w2.x = pack_bf16x2(acc[cb][0] * inv, acc[cb][1] * inv);
-            w2.y = pack_bf16x2(acc[cb][2] * inv, acc[cb][3] * inv);
-            *reinterpret_cast<uint2*>(orow + 16 * cb + 4 * g) = w2;
+        for (int ht = 0; ht < kMHT; ++ht) {
+            const float l = xl[ht][n16];
+            const float inv = l > 0.f ? 1.f / l : 0.f;
+            uint16_t* orow = out + (row * H + h0 + 16 * ht + n16) * kMC + c0;
+#pragma unroll
+            for (int cb = 0; cb < kMColBlkW; ++cb) {
+                uint2 w2;
+                w2.x = pack_bf16x2(acc[ht][cb][0] * inv, acc[ht][cb][1] * inv);
+                w2.y = pack_bf16x2(acc[ht][cb][2] * inv, acc[ht][cb][3] * inv);
+                *reinterpret_cast<uint2*>(orow + 16 * cb + 4 * g) = w2;
+            }
         }
     } else {
-        const int64_t prow = (row * ks_count + ks) * H + h0 + n16;
-        float* pr = part + prow * kMC;
 #pragma unroll
-        for (int cb = 0; cb < kMColBlk; ++cb) *reinterpret_cast<f32x4*>(pr + 16 * cb + 4 * g) = acc[cb];
-        if (g == 0) {
-            part_ml[2 * prow] = m_run;
-            part_ml[2 * prow + 1] = l_run;
+        for (int ht = 0; ht < kMHT; ++ht) {
+            const int64_t prow = (row * ks_count + ks) * H + h0 + 16 * ht + n16;
+            float* pr = part + prow * kMC + c0;
+#pragma unroll
+            for (int cb = 0; cb < kMColBlkW; ++cb) *reinterpret_cast<f32x4*>(pr + 16 * cb + 4 * g) = acc[ht][cb];
+            if (ht == tw && g == 0) {
+                part_ml[2 * prow] = m_run;
+                part_ml[2 * prow + 1] = l_run;
+            }
         }
     }
 }
@@ -414,11 +445,13 @@ mqa_combine(const float* __restrict__ part, const float* __restrict__ part_ml, i
     store8<DT_BF16>(out, rh * kMC + 8 * lane, o);
 }
 
-// Key ranges per row: enough workgroups to fill the chip, at least 4 blocks per range.
+// Key ranges per row: each range's key ids fit the LDS list; then, while the chip (two
+// workgroups per CU) is not filled, halve the ranges down to 4 blocks each.
 int mqa_splits(int64_t rows, int H, int k) {
     const int64_t wgs = rows * (H / kMHeadsWG);
     int ks = 1;
-    while (wgs * ks < 256 && (k + ks * 2 - 1) / (ks * 2) >= 4 * kMBlk) ks *= 2;
+    while ((k + ks - 1) / ks > kMIdsLds) ks *= 2;
+    while (wgs * ks < kMFillWGs && (k + ks * 2 - 1) / (ks * 2) >= 4 * kMBlk) ks *= 2;
     return ks;
 }
 
@@ -448,7 +481,7 @@ int launch_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t
             part_ml = part + rows * ks * H * (int64_t)kMC;
         }
         const float sl2 = scale * kLog2e;
-        hipLaunchKernelGGL(mqa_sparse_mfma<false>, dim3((unsigned)units), dim3(512), 0, stream,
+        hipLaunchKernelGGL(mqa_sparse_mfma<false>, dim3((unsigned)units), dim3(kMWaves * kWave), 0, stream,
                            static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx, rows, T, N, H, k, ks,
                            kps, sl2, (int64_t)0, 1, static_cast<uint16_t*>(out), part, part_ml);
         if (ks > 1)
@@ -470,7 +503,7 @@ int launch_dense_mqa(const void* q, const void* kv, int64_t batch, int64_t T, in
         const int64_t rows = batch * T;
         const int64_t units = ((rows + 7) / 8) * 8 * (H / kMHeadsWG);
         if (units > 0x7fffffffLL) return -2;
-        hipLaunchKernelGGL(mqa_sparse_mfma<true>, dim3((unsigned)units), dim3(512), 0, stream,
+        hipLaunchKernelGGL(mqa_sparse_mfma<true>, dim3((unsigned)units), dim3(kMWaves * kWave), 0, stream,
                            static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), nullptr, rows, T, N, H, 0,
                            1, 0x7fffffff, scale * kLog2e, q_pos0, ratio, static_cast<uint16_t*>(out), nullptr, nullptr);
         return 0;
