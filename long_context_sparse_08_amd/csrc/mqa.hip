@@ -158,6 +158,16 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // two floats to bf16 (round to nearest even, v_cvt_pk_bf16_f32), a in the low half
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations, not for its
+// global loads (the next block's gather stays in flight).  The empty asm statements keep the
+// compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0); vmcnt and expcnt at their maximum
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     const bf16x2_t v = {(__bf16)a, (__bf16)b};
@@ -215,9 +225,10 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     __shared__ __attribute__((aligned(16))) uint8_t stage_a[kMBuf];
     __shared__ __attribute__((aligned(16))) uint8_t stage_b[kMBuf];
     __shared__ int32_t ids[DENSE ? 1 : kMIdsLds];
-    __shared__ uint4 xp[kMHT][kWave];     // probability tiles, B-operand lane layout
-    __shared__ float xalpha[kMHT][16];    // rescale factor per head of a tile
-    __shared__ int xflag[kMHT];           // tile rescaled in the current block
+    // [0]: probability tiles in the B-operand lane layout; [1][tile][head].x: rescale factor.
+    // One array, so both are stored through the same lane address (no extra register).
+    __shared__ uint4 xp[2][kMHT][kWave];
+    __shared__ __attribute__((aligned(16))) int xflag[kMHT];   // tile rescaled in the current block
     __shared__ float xm[kMHT][16], xl[kMHT][16];
     const int tid = threadIdx.x, lane = tid & 63;
     const int tw = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: kept in scalar registers
@@ -262,36 +273,66 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     float m_run = -INFINITY, l_run = 0.f;   // head 16*tw + n16
 
     const int nblk = (nkeys + kMBlk - 1) / kMBlk;
-    const uint16_t* kvseq = kv + b * N * (int64_t)kMC;
+    const uint8_t* kvbytes = reinterpret_cast<const uint8_t*>(kv + b * N * (int64_t)kMC);
+    const uint32_t lane_off = 16u * lane;
     auto gather = [&](int blk, uint8_t* dst) {   // block `blk` of the range into `dst`
 #pragma unroll
         for (int r8 = 0; r8 < kMLoadsPerBlk; ++r8) {
             const int r = kMLoadsPerBlk * tw + r8;
-            int sidx = key_id(blk * kMBlk + r);
+            // one 1 KB row per instruction: the row is wave-uniform (scalar base, lane offset)
+            int sidx = __builtin_amdgcn_readfirstlane(key_id(blk * kMBlk + r));
             if (sidx < 0 || sidx >= N) sidx = 0;   // invalid slots load row 0, masked below
-            const uint16_t* src = kvseq + (int64_t)sidx * kMC + 8 * lane;
+            const uint8_t* src = kvbytes + (int64_t)sidx * (2 * kMC) + lane_off;
             __builtin_amdgcn_global_load_lds((glb_void_ptr)src, (lds_void_ptr)(dst + r * kMPitch), 16, 0, 0);
         }
     };
     auto compute = [&](int blk, const uint8_t* st) {
-        // validity of the 32 keys of this block (bit r)
-        uint32_t valid = 0;
+        // validity of the 32 keys of this block (bit r), shifted to this lane's key group
+        uint32_t vg;
         {
             const int sidx = key_id(blk * kMBlk + (lane & 31));
-            valid = (uint32_t)__ballot(lane < 32 && sidx >= 0 && sidx < N);
+            const uint32_t valid = (uint32_t)__ballot(lane < 32 && sidx >= 0 && sidx < N);
+            vg = valid >> (4 * g);
         }
 
-        // S^T for the two 16-key halves (two independent accumulation chains, interleaved)
+        // S^T for the two 16-key halves (two independent accumulation chains); the A operands
+        // are read kSD steps ahead of their use so LDS latency overlaps the matrix work
+        constexpr int kSD = 4;
         f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-        const uint8_t* arow0 = st + n16 * kMPitch + 16 * g;
-        const uint8_t* arow1 = arow0 + 16 * kMPitch;
+        const uint8_t* arow = st + n16 * kMPitch + 16 * g;
+        auto lda = [&](int s, int h) { return *reinterpret_cast<const bf16x8_t*>(arow + 16 * kMPitch * h + 64 * s); };
+        bf16x8_t ra[kSD][2];
+#pragma unroll
+        for (int j = 0; j < kSD; ++j) {
+            ra[j][0] = lda(j, 0);
+            ra[j][1] = lda(j, 1);
+        }
 #pragma unroll
         for (int s = 0; s < kMC / 32; ++s) {
-            const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(arow0 + 64 * s);
-            const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(arow1 + 64 * s);
-            sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qb[s], sacc[0], 0, 0, 0);
-            sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qb[s], sacc[1], 0, 0, 0);
+            sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[s % kSD][0], qb[s], sacc[0], 0, 0, 0);
+            sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[s % kSD][1], qb[s], sacc[1], 0, 0, 0);
+            if (s + kSD < kMC / 32) {
+                ra[s % kSD][0] = lda(s + kSD, 0);
+                ra[s % kSD][1] = lda(s + kSD, 1);
+            }
         }
+
+        // V^T operands of this wave's columns: transpose reads of keys {4g..4g+3} and
+        // {16+4g..}; the first kVD column blocks are requested before the softmax
+        constexpr int kVD = 3;
+        const uint8_t* vbase = st + (4 * g + (n16 >> 2)) * kMPitch + 8 * (n16 & 3) + 2 * kMColW * tw;
+        auto ldv = [&](int cb) {
+            typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+            const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 32 * cb));
+            const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 16 * kMPitch + 32 * cb));
+            typedef short i16x8 __attribute__((ext_vector_type(8)));
+            const i16x8 va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+            return __builtin_bit_cast(bf16x8_t, va);
+        };
+        bf16x8_t rv[kVD];
+#pragma unroll
+        for (int j = 0; j < kVD; ++j) rv[j] = ldv(j);
+
         // online softmax for head 16*tw + n16 (values of lane: keys 16*hb + 4g + i)
         float p[8];
         float bmax = -INFINITY;
@@ -299,8 +340,7 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
         for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int key = 16 * hb + 4 * g + i;
-                const float v = ((valid >> key) & 1u) ? sacc[hb][i] * sl2 : -INFINITY;
+                const float v = ((vg >> (16 * hb + i)) & 1u) ? sacc[hb][i] * sl2 : -INFINITY;
                 p[4 * hb + i] = v;
                 bmax = fmaxf(bmax, v);
             }
@@ -314,7 +354,7 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
             const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);   // 0 at the first valid block
             l_run *= alpha;
             m_run = m_new;
-            if (g == 0) xalpha[tw][n16] = alpha;
+            if (g == 0) xp[1][tw][lane].x = __float_as_uint(alpha);   // lane == n16 here
         }
         // while nothing valid has been seen m_run is -inf and every p is exp2(-inf) = 0
         const float m_ref = m_run == -INFINITY ? 0.f : m_run;
@@ -330,34 +370,29 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
         pw.y = pack_bf16x2(p[2], p[3]);
         pw.z = pack_bf16x2(p[4], p[5]);
         pw.w = pack_bf16x2(p[6], p[7]);
-        xp[tw][lane] = pw;
+        xp[0][tw][lane] = pw;
         if (lane == 0) xflag[tw] = resc ? 1 : 0;
-        __syncthreads();   // the four probability tiles and rescale factors are published
+        lds_barrier();   // the four probability tiles and rescale factors are published
 
         bf16x8_t pb[kMHT];
 #pragma unroll
+        for (int ht = 0; ht < kMHT; ++ht) pb[ht] = __builtin_bit_cast(bf16x8_t, xp[0][ht][lane]);
+        const int4 fl = *reinterpret_cast<const int4*>(xflag);
+        const int flags[kMHT] = {fl.x, fl.y, fl.z, fl.w};
+#pragma unroll
         for (int ht = 0; ht < kMHT; ++ht) {
-            pb[ht] = __builtin_bit_cast(bf16x8_t, xp[ht][lane]);
-            if (__builtin_amdgcn_readfirstlane(xflag[ht])) {
-                const float a = xalpha[ht][n16];
+            if (__builtin_amdgcn_readfirstlane(flags[ht])) {
+                const float a = __uint_as_float(xp[1][ht][n16].x);
 #pragma unroll
                 for (int cb = 0; cb < kMColBlkW; ++cb) acc[ht][cb] = acc[ht][cb] * a;
             }
         }
 
-        // O^T += V^T P^T over this wave's columns: V^T operand via transpose reads of keys
-        // {4g..4g+3} and {16+4g..}, shared by the four head tiles
-        const uint8_t* vbase0 = st + (4 * g + (n16 >> 2)) * kMPitch + 8 * (n16 & 3) + 2 * kMColW * tw;
-        const uint8_t* vbase1 = vbase0 + 16 * kMPitch;
+        // O^T += V^T P^T over this wave's columns, each V^T operand shared by the four head tiles
 #pragma unroll
         for (int cb = 0; cb < kMColBlkW; ++cb) {
-            const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(
-                vbase0 + 32 * cb));
-            const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(
-                vbase1 + 32 * cb));
-            typedef short i16x8 __attribute__((ext_vector_type(8)));
-            const i16x8 va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-            const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, va);
+            const bf16x8_t vb = rv[cb % kVD];
+            if (cb + kVD < kMColBlkW) rv[cb % kVD] = ldv(cb + kVD);
 #pragma unroll
             for (int ht = 0; ht < kMHT; ++ht)
                 acc[ht][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pb[ht], acc[ht][cb], 0, 0, 0);
