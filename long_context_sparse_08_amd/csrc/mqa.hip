@@ -135,8 +135,9 @@ int launch_generic(const void* q, const void* kv, const int32_t* idx, int64_t ba
 // V^T operand is read with exactly that map.
 //
 // Accumulator layout (16x16 f32): lane l holds column n = l%16, rows 4*(l/16) + i, i = 0..3.
-// With several key ranges per row (few rows, e.g. decode), each workgroup writes its
-// unnormalised partial (acc, running max, running sum) and mqa_combine merges them.
+// With several key ranges per row (few rows, e.g. decode), each workgroup writes its partial
+// normalised by its own softmax sum (bf16) with its (running max, running sum) in fp32, and
+// mqa_combine merges them.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -217,7 +218,7 @@ template <bool DENSE>
 __global__ void __launch_bounds__(kMWaves * kWave, 2)   // two waves per SIMD: two workgroups per CU
 mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
                 int64_t rows, int64_t T, int64_t N, int H, int k, int ks_count, int keys_per_split, float sl2,
-                int64_t q_pos0, int ratio, uint16_t* __restrict__ out, float* __restrict__ part,
+                int64_t q_pos0, int ratio, uint16_t* __restrict__ out, uint16_t* __restrict__ part,
                 float* __restrict__ part_ml) {
     // one array per pipeline parity: the DMA into one and the reads of the other are then
     // provably disjoint, so no wait for the in-flight gather is forced before the current
@@ -248,19 +249,34 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int key0 = ks * keys_per_split;
     const int nkeys = (int)max((int64_t)0, min(klen, (int64_t)key0 + keys_per_split) - key0);
     const int h0 = hg * kMHeadsWG;
+    const int n_ent = (int)N;   // entry ids are 32-bit (the C ABI rejects N >= 2^31)
     auto key_id = [&](int i) -> int {   // key id of slot i of this range (-1: none)
         if (i >= nkeys) return -1;
         if constexpr (DENSE) return key0 + i;
         else return ids[i];
     };
 
+    // key ids first, then q: q's loads overlap the id round trip and the first gather
+    constexpr int kIdsPerThread = DENSE ? 1 : kMIdsLds / (kMWaves * kWave);
+    int idv[kIdsPerThread];
+    if constexpr (!DENSE) {
+#pragma unroll
+        for (int u = 0; u < kIdsPerThread; ++u) {
+            const int i = tid + u * kMWaves * kWave;
+            idv[u] = i < nkeys ? idx[row * k + key0 + i] : -1;
+        }
+    }
     // this wave's q (head tile tw) as the B operand of S^T: head n16, channels 32*s + 8*g .. +8
     bf16x8_t qb[kMC / 32];
     const uint16_t* qrow = q + ((row * H) + h0 + 16 * tw + n16) * (int64_t)kMC + 8 * g;
 #pragma unroll
     for (int s = 0; s < kMC / 32; ++s) qb[s] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * s);
     if constexpr (!DENSE) {
-        for (int i = tid; i < nkeys; i += kMWaves * kWave) ids[i] = idx[row * k + key0 + i];
+#pragma unroll
+        for (int u = 0; u < kIdsPerThread; ++u) {
+            const int i = tid + u * kMWaves * kWave;
+            if (i < nkeys) ids[i] = idv[u];
+        }
         __syncthreads();
     }
 
@@ -281,7 +297,7 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
             const int r = kMLoadsPerBlk * tw + r8;
             // one 1 KB row per instruction: the row is wave-uniform (scalar base, lane offset)
             int sidx = __builtin_amdgcn_readfirstlane(key_id(blk * kMBlk + r));
-            if (sidx < 0 || sidx >= N) sidx = 0;   // invalid slots load row 0, masked below
+            if (sidx < 0 || sidx >= n_ent) sidx = 0;   // invalid slots load row 0, masked below
             const uint8_t* src = kvbytes + (int64_t)sidx * (2 * kMC) + lane_off;
             __builtin_amdgcn_global_load_lds((glb_void_ptr)src, (lds_void_ptr)(dst + r * kMPitch), 16, 0, 0);
         }
@@ -291,7 +307,7 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
         uint32_t vg;
         {
             const int sidx = key_id(blk * kMBlk + (lane & 31));
-            const uint32_t valid = (uint32_t)__ballot(lane < 32 && sidx >= 0 && sidx < N);
+            const uint32_t valid = (uint32_t)__ballot(lane < 32 && (uint32_t)sidx < (uint32_t)n_ent);
             vg = valid >> (4 * g);
         }
 
@@ -398,8 +414,7 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                 acc[ht][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pb[ht], acc[ht][cb], 0, 0, 0);
         }
     };
-    __builtin_amdgcn_s_waitcnt(0);   // q is in registers
-    if (nblk > 0) gather(0, stage_a);
+    if (nblk > 0) gather(0, stage_a);   // the loop's first wait also covers q
     for (int blk = 0; blk < nblk; blk += 2) {
         wait_vmcnt<0>();
         __syncthreads();   // block blk is staged in A; every wave is done with B
@@ -438,9 +453,16 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
 #pragma unroll
         for (int ht = 0; ht < kMHT; ++ht) {
             const int64_t prow = (row * ks_count + ks) * H + h0 + 16 * ht + n16;
-            float* pr = part + prow * kMC + c0;
+            const float l = xl[ht][n16];
+            const float inv = l > 0.f ? 1.f / l : 0.f;
+            uint16_t* pr = part + prow * kMC + c0;
 #pragma unroll
-            for (int cb = 0; cb < kMColBlkW; ++cb) *reinterpret_cast<f32x4*>(pr + 16 * cb + 4 * g) = acc[ht][cb];
+            for (int cb = 0; cb < kMColBlkW; ++cb) {
+                uint2 w2;
+                w2.x = pack_bf16x2(acc[ht][cb][0] * inv, acc[ht][cb][1] * inv);
+                w2.y = pack_bf16x2(acc[ht][cb][2] * inv, acc[ht][cb][3] * inv);
+                *reinterpret_cast<uint2*>(pr + 16 * cb + 4 * g) = w2;
+            }
             if (ht == tw && g == 0) {
                 part_ml[2 * prow] = m_run;
                 part_ml[2 * prow + 1] = l_run;
@@ -449,9 +471,10 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     }
 }
 
-// Merge the key-range partials of one (row, head): out = sum_j e^(m_j - M) acc_j / sum_j e^(m_j - M) l_j.
+// Merge the key-range partials of one (row, head).  Partial j holds o_j = acc_j / l_j:
+// out = sum_j w_j o_j / sum_j w_j with w_j = l_j 2^(m_j - M), M = max_j m_j (log2 domain).
 __global__ void __launch_bounds__(64)
-mqa_combine(const float* __restrict__ part, const float* __restrict__ part_ml, int64_t rows, int H, int ks_count,
+mqa_combine(const uint16_t* __restrict__ part, const float* __restrict__ part_ml, int64_t rows, int H, int ks_count,
             uint16_t* __restrict__ out) {
     const int64_t rh = blockIdx.x;   // row * H + head
     const int64_t row = rh / H, head = rh % H;
@@ -463,15 +486,12 @@ mqa_combine(const float* __restrict__ part, const float* __restrict__ part_ml, i
     if (M != -INFINITY) {
         for (int j = 0; j < ks_count; ++j) {
             const int64_t prow = (row * ks_count + j) * H + head;
-            const float sc = exp2f(part_ml[2 * prow] - M);
-            L = fmaf(part_ml[2 * prow + 1], sc, L);
-            const f32x4* p4 = reinterpret_cast<const f32x4*>(part + prow * kMC + 8 * lane);
-            const f32x4 a = p4[0], c = p4[1];
+            const float w = part_ml[2 * prow + 1] * exp2f(part_ml[2 * prow] - M);
+            L += w;
+            float pv[8];
+            load8<DT_BF16>(part, prow * kMC + 8 * lane, pv);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                o[e] = fmaf(a[e], sc, o[e]);
-                o[4 + e] = fmaf(c[e], sc, o[4 + e]);
-            }
+            for (int e = 0; e < 8; ++e) o[e] = fmaf(pv[e], w, o[e]);
         }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -497,7 +517,7 @@ size_t sparse_mqa_workspace(int64_t batch, int64_t T, int H, int c, int k, int t
     const int64_t rows = batch * T;
     const int ks = mqa_splits(rows, H, k);
     if (ks == 1) return 0;
-    return (size_t)rows * ks * H * (kMC + 2) * sizeof(float) + 256;
+    return (size_t)rows * ks * H * (kMC * sizeof(uint16_t) + 2 * sizeof(float)) + 256;
 }
 
 int launch_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t batch, int64_t T, int64_t N, int H,
@@ -509,11 +529,11 @@ int launch_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t
         const int kps = ((k + ks - 1) / ks + kMBlk - 1) / kMBlk * kMBlk;
         const int64_t units = ((rows + 7) / 8) * 8 * (H / kMHeadsWG) * ks;
         if (units > 0x7fffffffLL) return -2;
-        float* part = nullptr;
+        uint16_t* part = nullptr;
         float* part_ml = nullptr;
         if (ks > 1) {
-            part = static_cast<float*>(ws);
-            part_ml = part + rows * ks * H * (int64_t)kMC;
+            part = static_cast<uint16_t*>(ws);
+            part_ml = reinterpret_cast<float*>(part + rows * ks * H * (int64_t)kMC);
         }
         const float sl2 = scale * kLog2e;
         hipLaunchKernelGGL(mqa_sparse_mfma<false>, dim3((unsigned)units), dim3(kMWaves * kWave), 0, stream,
