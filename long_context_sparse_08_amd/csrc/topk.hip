@@ -365,53 +365,59 @@ topk_bitmap(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
         __syncthreads();
         lo = s_lo;
     };
-    if (have_mm) {
+    auto range_from_mm = [&]() {
         const float* r = mm + row * (int64_t)nmm * 2;
         for (int i = tid; i < nmm; i += kThreads) {
             lo = fminf(lo, r[2 * i]);
             hi = fmaxf(hi, r[2 * i + 1]);
         }
         publish_range();
-    }
+    };
     if constexpr (IN_LDS) {
-        const float hlo = have_mm ? s_lo : 0.f, hinv = have_mm ? s_inv : 0.f;
+        // one pass: the row's loads are issued first (their latency overlaps the range
+        // reduction), then the values go to LDS and into the histogram (or the min / max)
+        static_assert(kRowLds == 32 * kThreads, "a staged row is 8 float4 per thread");
         const int64_t n4 = nv >> 2;
         const float4* s4 = reinterpret_cast<const float4*>(sc);
         float4* d4 = reinterpret_cast<float4*>(rowbuf);
-        for (int64_t i0 = tid; i0 < n4; i0 += 8 * kThreads) {
-            float4 v[8];
+        float4 v[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int64_t i = i0 + (int64_t)u * kThreads;
-                v[u] = i < n4 ? s4[i] : make_float4(INFINITY, INFINITY, -INFINITY, -INFINITY);
-            }
+        for (int u = 0; u < 8; ++u) {
+            const int64_t i = tid + (int64_t)u * kThreads;
+            v[u] = i < n4 ? s4[i] : make_float4(INFINITY, INFINITY, -INFINITY, -INFINITY);
+        }
+        const int64_t st = 4 * n4 + tid;   // the last nv % 4 entries, one per thread
+        const float vt = st < nv ? sc[st] : 0.f;
+        if (have_mm) range_from_mm();
+        const float hlo = have_mm ? s_lo : 0.f, hinv = have_mm ? s_inv : 0.f;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int64_t i = i0 + (int64_t)u * kThreads;
-                if (i >= n4) continue;
-                d4[i] = v[u];
-                if (have_mm) {
-                    atomicAdd(&hist[bin_of(v[u].x, hlo, hinv)], 1u);
-                    atomicAdd(&hist[bin_of(v[u].y, hlo, hinv)], 1u);
-                    atomicAdd(&hist[bin_of(v[u].z, hlo, hinv)], 1u);
-                    atomicAdd(&hist[bin_of(v[u].w, hlo, hinv)], 1u);
-                } else {
-                    lo = fminf(lo, fminf(fminf(v[u].x, v[u].y), fminf(v[u].z, v[u].w)));
-                    hi = fmaxf(hi, fmaxf(fmaxf(v[u].x, v[u].y), fmaxf(v[u].z, v[u].w)));
-                }
+        for (int u = 0; u < 8; ++u) {
+            const int64_t i = tid + (int64_t)u * kThreads;
+            if (i >= n4) continue;
+            d4[i] = v[u];
+            if (have_mm) {
+                atomicAdd(&hist[bin_of(v[u].x, hlo, hinv)], 1u);
+                atomicAdd(&hist[bin_of(v[u].y, hlo, hinv)], 1u);
+                atomicAdd(&hist[bin_of(v[u].z, hlo, hinv)], 1u);
+                atomicAdd(&hist[bin_of(v[u].w, hlo, hinv)], 1u);
+            } else {
+                lo = fminf(lo, fminf(fminf(v[u].x, v[u].y), fminf(v[u].z, v[u].w)));
+                hi = fmaxf(hi, fmaxf(fmaxf(v[u].x, v[u].y), fmaxf(v[u].z, v[u].w)));
             }
         }
-        for (int64_t s = 4 * n4 + tid; s < nv; s += kThreads) {
-            const float v = sc[s];
-            rowbuf[s] = v;
-            if (have_mm) atomicAdd(&hist[bin_of(v, hlo, hinv)], 1u);
-            else { lo = fminf(lo, v); hi = fmaxf(hi, v); }
+        if (st < nv) {
+            rowbuf[st] = vt;
+            if (have_mm) atomicAdd(&hist[bin_of(vt, hlo, hinv)], 1u);
+            else { lo = fminf(lo, vt); hi = fmaxf(hi, vt); }
         }
-    } else if (!have_mm) {
-        for (int64_t s = tid; s < nv; s += kThreads) {
-            const float v = sc[s];
-            lo = fminf(lo, v);
-            hi = fmaxf(hi, v);
+    } else {
+        if (have_mm) range_from_mm();
+        else {
+            for (int64_t s = tid; s < nv; s += kThreads) {
+                const float v = sc[s];
+                lo = fminf(lo, v);
+                hi = fmaxf(hi, v);
+            }
         }
     }
     if (!have_mm) {
@@ -439,28 +445,19 @@ topk_bitmap(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
         }
     }
     __syncthreads();
-    if (wid == 0) {   // b*: bins scanned from the top, 32 per lane
-        const int per = kBins / kWave;
-        const int top = kBins - 1 - lane * per;
-        uint32_t mine = 0;
-        for (int j = 0; j < per; ++j) mine += hist[top - j];
-        uint32_t inc = mine;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const uint32_t y = __shfl_up(inc, off, kWave);
-            if (lane >= off) inc += y;
-        }
-        const uint32_t before = inc - mine;
-        if (before < (uint32_t)k && inc >= (uint32_t)k) {
-            uint32_t acc = before;
-            for (int j = 0; j < per; ++j) {
-                const uint32_t hh = hist[top - j];
-                if (acc + hh >= (uint32_t)k) {
-                    s_bstar = top - j;
-                    s_need = (uint32_t)k - acc;
-                    break;
-                }
-                acc += hh;
+    {   // b*: a block scan over the bins from the top, two per thread
+        static_assert(kBins == 2 * kThreads, "two bins per thread");
+        const int top = kBins - 1 - 2 * tid;
+        const uint32_t h0 = hist[top], h1 = hist[top - 1];
+        uint32_t total;
+        const uint32_t before = block_excl_scan(h0 + h1, scan_buf, &total);
+        if (before < (uint32_t)k && before + h0 + h1 >= (uint32_t)k) {   // exactly one thread
+            if (before + h0 >= (uint32_t)k) {
+                s_bstar = top;
+                s_need = (uint32_t)k - before;
+            } else {
+                s_bstar = top - 1;
+                s_need = (uint32_t)k - before - h0;
             }
         }
     }
@@ -480,7 +477,39 @@ topk_bitmap(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
         }
     };
     if constexpr (IN_LDS) {
-        for (int64_t s = tid; s < nv; s += kThreads) mark(s, rowbuf[s]);
+        // chunks of 64 entries, one per wave step: a ballot gives the chunk's two bitmap words
+        // (every word is written, no atomics); b*'s members are appended one wave at a time
+        const int nvi = (int)nv;   // <= kRowLds
+        const int nchunk = (nvi + kWave - 1) / kWave;
+        const unsigned long long below = (1ull << lane) - 1ull;
+        for (int c0 = wid; c0 < nchunk; c0 += 8 * kWaves) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)   // clamped reads: always in the row; masked below
+                v[u] = rowbuf[min((c0 + u * kWaves) * kWave + lane, nvi - 1)];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int c = c0 + u * kWaves;
+                if (c >= nchunk) break;
+                const int s = c * kWave + lane;
+                const bool ok = s < nvi;
+                const int bn = bin_of(v[u], lo, inv);
+                const unsigned long long mk = __ballot(ok && bn > bstar);
+                if (lane == 0) reinterpret_cast<uint2*>(bits)[c] = make_uint2((uint32_t)mk, (uint32_t)(mk >> 32));
+                const bool eq = ok && bn == bstar && fits;
+                const unsigned long long me = __ballot(eq);
+                if (me) {
+                    uint32_t base = 0;
+                    if (lane == 0) base = atomicAdd(&s_ncand, (uint32_t)__popcll(me));
+                    base = __shfl(base, 0, kWave);
+                    const uint32_t p = base + (uint32_t)__popcll(me & below);
+                    if (eq && p < (uint32_t)kCap) {
+                        cval[p] = v[u];
+                        cidx[p] = s;
+                    }
+                }
+            }
+        }
     } else {
         for (int64_t s0 = tid; s0 < nv; s0 += 8 * kThreads) {
             float v[8];
@@ -496,7 +525,23 @@ topk_bitmap(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
     }
     __syncthreads();
 
-    if (fits) {
+    if (fits && s_ncand <= (uint32_t)kWave) {
+        // rank b*'s members by (value desc, index asc) within one wave: lane i holds member i,
+        // the others' keys are read with readlane (no LDS round trips); keep ranks < need
+        const uint32_t nc = s_ncand;
+        if (wid == 0) {
+            const bool have = (uint32_t)lane < nc;
+            const uint32_t ki = have ? order_key(cval[lane]) : 0u;
+            const int32_t si = have ? cidx[lane] : 0;
+            uint32_t rank = 0;
+            for (uint32_t j = 0; j < nc; ++j) {
+                const uint32_t kj = __builtin_amdgcn_readlane(ki, j);
+                const int32_t sj = __builtin_amdgcn_readlane(si, j);
+                rank += (kj > ki || (kj == ki && sj < si)) ? 1u : 0u;
+            }
+            if (have && rank < need) atomicOr(&bits[si >> 5], 1u << (si & 31));
+        }
+    } else if (fits) {
         // rank b*'s members by (value desc, index asc); keep ranks < need
         const uint32_t nc = min(s_ncand, (uint32_t)kCap);
         for (uint32_t i = tid; i < nc; i += kThreads) {
