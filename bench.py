@@ -85,7 +85,23 @@ def peak_for(cfg, stage, bound):
 
 
 # ---------------------------------------------------------------------------- CPU baseline
-def cpu_baseline(cfg, host, budget_s=20.0):
+def cpu_baseline(cfg, host, budget_s=10.0):
+    """The oracle on a bounded sample of the workload, repeated until about budget_s seconds of
+    CPU work have been timed."""
+    reps, tokens, elapsed = 0, 0, 0.0
+    while elapsed < budget_s:
+        r = _cpu_sample(cfg, host)
+        reps += 1
+        tokens += r["tokens"]
+        elapsed += r["seconds"]
+        sample = r["sample"]
+    import oracle
+
+    return {"value": tokens / elapsed, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{sample}; {reps} repetitions", "seconds": round(elapsed, 3)}
+
+
+def _cpu_sample(cfg, host):
     import oracle
 
     t0 = time.perf_counter()
@@ -116,9 +132,7 @@ def cpu_baseline(cfg, host, budget_s=20.0):
         oracle.hca_dense_mqa(host["q"][:, rows], kv, cfg.m_prime, cfg.scale, dtype=cfg.dt, qpos=cfg.q_pos0 + rows)
         tokens = len(rows)
         sample = f"full HCA compression + {len(rows)} query rows of dense MQA, float64"
-    dt = time.perf_counter() - t0
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": sample, "seconds": round(dt, 3)}
+    return {"tokens": tokens, "sample": sample, "seconds": time.perf_counter() - t0}
 
 
 # ---------------------------------------------------------------------------- main
@@ -131,7 +145,18 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stage-reps", type=int, default=0, help="launches per stage for kernel timing (0: = steps)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run device-to-device copies of BYTES (HBM counter calibration) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        src = torch.ones(args.copy_calibration, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_calibration, "copies": 5}), flush=True)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
@@ -199,32 +224,37 @@ def main():
     tokens = cfg.batch * cfg.T
     value = tokens / (ms * 1e-3)
 
-    # ---- per-stage kernel time: back-to-back launches of each stage, HIP events on the
-    # stream the launches go to (torch's current stream)
+    # ---- per-stage time: back-to-back launches of each stage's library call, HIP events on the
+    # stream the launches go to (torch's current stream).  Each stage is one of the step's own
+    # calls, plus the indexer alone (csa_index_scores launches exactly the indexer kernel the
+    # step runs), so every single-kernel figure below is that kernel's launch duration.
     reps = args.stage_reps or args.steps
-    stages = {}
+    i = dev
+    stages = {}   # name -> (callable, kernels it launches, work key or None)
     if cfg.kind == "csa_decode":
-        i = dev
         scores = torch.empty((cfg.batch, cfg.T, cfg.N), dtype=torch.float32, device="cuda")
-        stages["index"] = lambda: csa.csa_index_scores(i["qI"], i["w"], i["kI"], cfg.q_pos0, cfg.m, scores=scores)
-        stages["topk"] = lambda: csa.csa_topk(scores, cfg.q_pos0, cfg.m, cfg.k, idx=pipe.idx, sel_scores=pipe.sel)
-        stages["mqa"] = pipe.attend
+        split = csa.csa_sparse_mqa_workspace_size(cfg.batch, cfg.T, cfg.H, cfg.c, cfg.k, cfg.dt) > 0
+        stages["index"] = (lambda: csa.csa_index_scores(i["qI"], i["w"], i["kI"], cfg.q_pos0, cfg.m, scores=scores),
+                           ["index_scores_mfma"], "index")
+        stages["select"] = (pipe.select, ["index_scores_mfma", "topk"], None)
+        stages["attend"] = (pipe.attend, ["mqa_sparse_mfma"] + (["mqa_combine"] if split else []),
+                            None if split else "mqa")
     elif cfg.kind == "csa_prefill":
-        i = dev
-        stages["compress_kv"] = lambda: csa.csa_compress(i["Ca"], i["Cb"], i["Za"], i["Zb"], i["Ba"], i["Bb"], cfg.m,
-                                                         out=pipe.kv)
-        stages["compress_kI"] = lambda: csa.csa_compress(i["ICa"], i["ICb"], i["IZa"], i["IZb"], i["IBa"], i["IBb"],
-                                                         cfg.m, out=pipe.kI)
         scores = torch.empty((cfg.batch, cfg.T, cfg.N), dtype=torch.float32, device="cuda")
-        stages["index"] = lambda: csa.csa_index_scores(i["qI"], i["w"], pipe.kI, cfg.q_pos0, cfg.m, scores=scores)
-        stages["topk"] = lambda: csa.csa_topk(scores, cfg.q_pos0, cfg.m, cfg.k, idx=pipe.idx, sel_scores=pipe.sel)
-        stages["mqa"] = pipe.attend
+        stages["compress_kv"] = (lambda: csa.csa_compress(i["Ca"], i["Cb"], i["Za"], i["Zb"], i["Ba"], i["Bb"], cfg.m,
+                                                          out=pipe.kv), ["compress_kernel"], "compress_kv")
+        stages["compress_kI"] = (lambda: csa.csa_compress(i["ICa"], i["ICb"], i["IZa"], i["IZb"], i["IBa"], i["IBb"],
+                                                          cfg.m, out=pipe.kI), ["compress_kernel"], "compress_kI")
+        stages["index"] = (lambda: csa.csa_index_scores(i["qI"], i["w"], pipe.kI, cfg.q_pos0, cfg.m, scores=scores),
+                           ["index_scores_mfma"], "index")
+        stages["select"] = (pipe.select, ["index_scores_mfma", "topk"], None)
+        stages["attend"] = (pipe.attend, ["mqa_sparse_mfma"], "mqa")
     else:
-        stages["compress"] = pipe.compress
-        stages["mqa"] = pipe.attend
+        stages["compress"] = (pipe.compress, ["compress_kernel"], "compress")
+        stages["attend"] = (pipe.attend, ["mqa_sparse_mfma"], "mqa")
     work = stage_work(cfg)
     stage_ms = {}
-    for name, fn in stages.items():
+    for name, (fn, _, _) in stages.items():
         fn()
         torch.cuda.synchronize()
         n_rep = max(3, reps if cfg.kind != "hca_chunk" else min(reps, 20))
@@ -235,20 +265,28 @@ def main():
         b.record()
         torch.cuda.synchronize()
         stage_ms[name] = a.elapsed_time(b) / n_rep
-    dom = max(stage_ms, key=stage_ms.get)
-    w = work[dom]
-    peak, unit = peak_for(cfg, dom, w["bound"])
+    # roofline of the dominant kernel: the longest stage that is a single kernel
+    single = [n for n, (_, ks, wk) in stages.items() if len(ks) == 1 and wk is not None]
+    dom = max(single, key=stage_ms.get)
+    kernel, wkey = stages[dom][1][0], stages[dom][2]
+    w = work[wkey]
+    peak, unit = peak_for(cfg, wkey, w["bound"])
     t_s = stage_ms[dom] * 1e-3
+    from long_context_sparse_08_amd.profiling import traffic_for
+    tr = traffic_for(kernel, cfg.name)
     if w["bound"] == "hbm":
         achieved = w["bytes"] / t_s
         roof = {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": peak / 1e9, "unit": unit,
-                "frac": round(achieved / peak, 4), "traffic": None}
+                "frac": round(achieved / peak, 4)}
     else:
         achieved = w["flops"] / t_s
         roof = {"bound": "mfma", "achieved": round(achieved / 1e12, 1), "peak": peak / 1e12, "unit": unit,
-                "frac": round(achieved / peak, 4), "traffic": None}
-    roof["kernel"] = dom
+                "frac": round(achieved / peak, 4)}
+    roof["traffic"] = None if tr is None else tr["traffic_bytes"]
+    roof["kernel"] = kernel
     roof["ms_per_launch"] = round(stage_ms[dom], 5)
+    roof["algorithmic_bytes"] = int(w["bytes"])
+    roof["algorithmic_flops"] = int(w["flops"])
     ideal = sum(max(v["bytes"] / HBM_PEAK, v["flops"] / peak_for(cfg, k, "mfma")[0]) for k, v in work.items())
 
     result = {
@@ -271,6 +309,7 @@ def main():
                    "graph": graph is not None},
         "roofline": roof,
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        "stage_kernels": {k: v[1] for k, v in stages.items()},
         "step_roofline_frac": round(ideal / (ms * 1e-3), 4),
     }
     if not args.no_cpu_baseline:

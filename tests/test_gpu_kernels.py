@@ -221,3 +221,27 @@ def test_repeat_runs_are_bitwise_identical():
     a = csa.csa_sparse_mqa(qd, kvd, idx, 0.05)
     b = csa.csa_sparse_mqa(qd, kvd, idx, 0.05)
     assert torch.equal(a, b)
+
+
+def test_sparse_mqa_workspace_reuse_split_keys():
+    """Decode shapes split each query's keys over workgroups and merge the ranges' partials in
+    a second kernel.  One workspace serves several calls in a row (two shapes), each checked
+    against the oracle; a repeated call is bitwise identical."""
+    shapes = [(4, 1, 3000, 128, 512, 1024), (2, 1, 1500, 64, 512, 512)]
+    need = max(csa.csa_sparse_mqa_workspace_size(b, T, H, c, k, BF16) for b, T, N, H, c, k in shapes)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    first = None
+    for rep, (batch, T, N, H, c, k) in enumerate([shapes[0], shapes[0], shapes[1]]):
+        say(f"csa_sparse_mqa reuse {rep} {(batch, T, N, H, c, k)}")
+        sd = 1300 + N
+        q, kv = draw(sd, 1, (batch, T, H, c), BF16), draw(sd, 2, (batch, N, c), BF16)
+        idx = _distinct_ids(np.random.RandomState(sd), batch, T, N, k)
+        scale = 1.0 / np.sqrt(c)
+        got = csa.csa_sparse_mqa(to_dev(q, BF16), to_dev(kv, BF16), torch.from_numpy(idx).cuda(), scale,
+                                 workspace=ws)
+        if rep == 0:
+            first = got.clone()
+        elif rep == 1:
+            assert torch.equal(got, first)
+        out_tol(BF16)(from_dev(got), oracle.sparse_mqa(q, kv, idx, scale, dtype=BF16), "sparse_mqa reuse")
