@@ -473,25 +473,49 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
 
 // Merge the key-range partials of one (row, head).  Partial j holds o_j = acc_j / l_j:
 // out = sum_j w_j o_j / sum_j w_j with w_j = l_j 2^(m_j - M), M = max_j m_j (log2 domain).
+// Ranges are taken 8 at a time with every load of a group in flight together (decode has 4:
+// one round trip); a later group with a larger max rescales what is already summed.
+constexpr int kCombGroup = 8;
+
 __global__ void __launch_bounds__(64)
 mqa_combine(const uint16_t* __restrict__ part, const float* __restrict__ part_ml, int64_t rows, int H, int ks_count,
             uint16_t* __restrict__ out) {
     const int64_t rh = blockIdx.x;   // row * H + head
     const int64_t row = rh / H, head = rh % H;
     const int lane = threadIdx.x;
-    float M = -INFINITY;
-    for (int j = 0; j < ks_count; ++j) M = fmaxf(M, part_ml[2 * ((row * ks_count + j) * H + head)]);
-    float L = 0.f;
+    const int64_t prow0 = row * ks_count * H + head;   // partial row of range j: prow0 + j * H
+    float M = -INFINITY, L = 0.f;
     float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (M != -INFINITY) {
-        for (int j = 0; j < ks_count; ++j) {
-            const int64_t prow = (row * ks_count + j) * H + head;
-            const float w = part_ml[2 * prow + 1] * exp2f(part_ml[2 * prow] - M);
-            L += w;
-            float pv[8];
-            load8<DT_BF16>(part, prow * kMC + 8 * lane, pv);
+    for (int j0 = 0; j0 < ks_count; j0 += kCombGroup) {
+        uint4 pv[kCombGroup];
+        float mj[kCombGroup], lj[kCombGroup];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = fmaf(pv[e], w, o[e]);
+        for (int u = 0; u < kCombGroup; ++u) {
+            const bool have = j0 + u < ks_count;
+            const int64_t prow = prow0 + (int64_t)min(j0 + u, ks_count - 1) * H;
+            pv[u] = *reinterpret_cast<const uint4*>(part + prow * kMC + 8 * lane);
+            mj[u] = have ? part_ml[2 * prow] : -INFINITY;
+            lj[u] = part_ml[2 * prow + 1];
+        }
+        float Mg = M;
+#pragma unroll
+        for (int u = 0; u < kCombGroup; ++u) Mg = fmaxf(Mg, mj[u]);
+        if (Mg == -INFINITY) continue;   // nothing visible so far
+        const float a = M == -INFINITY ? 0.f : exp2f(M - Mg);   // rescale of the sum so far
+        L *= a;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] *= a;
+        M = Mg;
+#pragma unroll
+        for (int u = 0; u < kCombGroup; ++u) {
+            const float w = mj[u] == -INFINITY ? 0.f : lj[u] * exp2f(mj[u] - M);
+            L += w;
+            const uint32_t pw[4] = {pv[u].x, pv[u].y, pv[u].z, pv[u].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                o[2 * e] = fmaf(bf16_to_f32(pw[e] & 0xffffu), w, o[2 * e]);
+                o[2 * e + 1] = fmaf(bf16_to_f32(pw[e] >> 16), w, o[2 * e + 1]);
+            }
         }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
