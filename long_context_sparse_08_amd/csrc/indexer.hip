@@ -277,6 +277,130 @@ index_scores_mfma(const void* __restrict__ qI, const float* __restrict__ w, cons
     }
 }
 
+// Prefill shape (many queries): a workgroup of 8 waves takes 8 consecutive queries (wave w:
+// query t0 + w) and a chunk of 32-entry key blocks.  Each key block is read from global memory
+// once per workgroup, coalesced (one 16-byte load per lane covers 1 KB of consecutive rows),
+// three blocks ahead into registers, and written to LDS rows padded by 16 bytes, from where
+// every wave reads its MFMA operand without bank conflicts (each 16-lane phase of a read then
+// touches 16 distinct 4-bank groups).  Visibility grows with the query, so the group walks the
+// blocks its last query sees and each wave masks its own tail.
+constexpr int kPfWaves = 8;
+constexpr int kPfPad = 16;
+
+template <int DT, int MB>
+__global__ void __launch_bounds__(kPfWaves * kWave, 1)
+index_scores_prefill(const void* __restrict__ qI, const float* __restrict__ w, const void* __restrict__ kI,
+                     int64_t batch, int64_t T, int64_t q_pos0, int64_t N, int m, float* __restrict__ scores, int64_t ld,
+                     int write_invisible, int chunks, int cb) {
+    using O = IdxOps<DT>;
+    constexpr int H = 32 * MB;
+    constexpr int kRowB = kMfmaCI * O::kEsz;          // bytes per key row: 256 (bf16) / 128 (fp8)
+    constexpr int kPitch = kRowB + kPfPad;
+    constexpr int kLanesPerRow = kRowB / 16;
+    constexpr int kRowsPerLoad = kWave / kLanesPerRow;  // rows one wave-wide 16-byte load covers
+    constexpr int kLoadWaves = 32 / kRowsPerLoad;       // waves that stage a block (8 / 4)
+    static_assert(kLoadWaves <= kPfWaves, "staging waves");
+    __shared__ __attribute__((aligned(16))) uint8_t stg[2][32 * kPitch];
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 5, n = lane & 31;
+    const int64_t groups = (T + kPfWaves - 1) / kPfWaves;
+    const int64_t unit = blockIdx.x;
+    const int chunk = (int)(unit % chunks);
+    const int64_t bg = unit / chunks;
+    const int64_t b = bg / groups, tg = bg - b * groups;
+    if (b >= batch) return;
+    const int64_t t0 = tg * kPfWaves;
+    const int64_t t = t0 + wid;
+    const bool tok = t < T;
+    const int64_t tq = tok ? t : T - 1;   // waves past T run on the last query and store nothing
+    const int64_t row = b * T + tq;
+    const int64_t nv = tok ? visible_entries(q_pos0 + t, m, N) : 0;
+    const int64_t nv_last = visible_entries(q_pos0 + min(t0 + kPfWaves - 1, T - 1), m, N);
+    const int64_t nblk_all = (N + 31) / 32;
+    const int64_t blk0 = (int64_t)chunk * cb;
+    const int64_t blk1 = min(blk0 + cb, nblk_all);
+    float* out = scores + row * ld;
+    if (write_invisible && tok)
+        for (int64_t s = max(nv, blk0 * 32) + lane; s < min(blk1 * 32, N); s += kWave) out[s] = -INFINITY;
+    const int64_t bend = min(blk1, (nv_last + 31) / 32);
+    const int nb = bend > blk0 ? (int)(bend - blk0) : 0;   // the same for the whole workgroup
+    if (nb == 0) return;
+
+    // this wave's q (A operands) and the w of the heads its accumulator rows hold
+    typename O::Frag qa[MB];
+    float wv[MB][16];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        load_half_row<DT>(qI, row * H + 32 * mb + n, g, qa[mb]);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 w4 = *reinterpret_cast<const float4*>(w + row * H + 32 * mb + 8 * q4 + 4 * g);
+            wv[mb][4 * q4 + 0] = w4.x;
+            wv[mb][4 * q4 + 1] = w4.y;
+            wv[mb][4 * q4 + 2] = w4.z;
+            wv[mb][4 * q4 + 3] = w4.w;
+        }
+    }
+
+    const bool loader = wid < kLoadWaves;
+    const int srow = kRowsPerLoad * wid + lane / kLanesPerRow;   // row of the block this lane stages
+    const int scol = 16 * (lane % kLanesPerRow);
+    const uint8_t* kb = static_cast<const uint8_t*>(kI) + b * N * (int64_t)kRowB;
+    auto gload = [&](int i) {   // block blk0 + min(i, nb-1); rows past N repeat the last row (never scored)
+        const int64_t e = min((blk0 + min(i, nb - 1)) * 32 + srow, N - 1);
+        return *reinterpret_cast<const uint4*>(kb + e * kRowB + scol);
+    };
+    auto compute = [&](int i) {
+        const uint8_t* st = &stg[i & 1][0] + n * kPitch + g * (kRowB / 2);
+        typename O::Frag kf;
+#pragma unroll
+        for (int j = 0; j < O::kLoads; ++j) kf.v[j] = *reinterpret_cast<const uint4*>(st + 16 * j);
+        float contrib = 0.f;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            f32x16 acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            acc = O::mma(qa[mb], kf, acc);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) contrib = fmaf(wv[mb][r], fmaxf(acc[r], 0.f), contrib);
+        }
+        // lanes l and l^32 hold the two halves of entry n's heads
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(contrib), __float_as_uint(contrib), false,
+                                                         false);
+        contrib = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        const int64_t s = (blk0 + i) * 32 + n;
+        if (g == 0 && tok && s < nv) out[s] = contrib;
+    };
+    // block i is computed from buffer i & 1; during step i the block i+1 goes from registers
+    // to the other buffer (read by everyone in step i-1, closed by its barrier) and block i+3
+    // is requested into the registers block i-1 used
+    uint4 ra = {}, rb = {}, rc = {}, rd = {};
+    if (loader) {
+        ra = gload(0);
+        rb = gload(1);
+        rc = gload(2);
+        *reinterpret_cast<uint4*>(&stg[0][srow * kPitch + scol]) = ra;
+    }
+    __syncthreads();
+    auto step = [&](int i, const uint4& next, uint4& fetch) {
+        if (loader) {
+            fetch = gload(i + 3);
+            if (i + 1 < nb) *reinterpret_cast<uint4*>(&stg[(i + 1) & 1][srow * kPitch + scol]) = next;
+        }
+        compute(i);
+        __syncthreads();
+    };
+    for (int i = 0; i < nb; i += 4) {
+        step(i, rb, rd);
+        if (i + 1 >= nb) break;
+        step(i + 1, rc, ra);
+        if (i + 2 >= nb) break;
+        step(i + 2, rd, rb);
+        if (i + 3 >= nb) break;
+        step(i + 3, ra, rc);
+    }
+}
+
 bool mfma_shape(int H_I, int c_I, int qk_t) {
     return c_I == kMfmaCI && (H_I == 32 || H_I == 64) && (qk_t == DT_FP8 || qk_t == DT_BF16);
 }
@@ -287,15 +411,14 @@ int launch_mfma(const void* qI, const float* w, const void* kI, int64_t batch, i
                 uint32_t* zero, int zero_words, hipStream_t stream) {
     const int64_t nblk = (N + 31) / 32;
     if (T >= 4) {
-        // prefill: 4 queries per workgroup share the key blocks
-        const int64_t groups = batch * ((T + 3) / 4);
+        // prefill: 8 queries per workgroup share each staged key block
+        const int64_t groups = batch * ((T + kPfWaves - 1) / kPfWaves);
         const int cb = 16;
         const int chunks = (int)((nblk + cb - 1) / cb);
         const int64_t grid = groups * chunks;
         if (grid > 0x7fffffffLL) return -2;
-        hipLaunchKernelGGL((index_scores_mfma<DT, MB, 4>), dim3((unsigned)grid), dim3(256), 0, stream, qI, w, kI, batch,
-                           T, q_pos0, N, m, scores, ld, write_invisible ? 1 : 0, chunks, cb, (float*)nullptr,
-                           (uint32_t*)nullptr, 0);
+        hipLaunchKernelGGL((index_scores_prefill<DT, MB>), dim3((unsigned)grid), dim3(kPfWaves * kWave), 0, stream, qI,
+                           w, kI, batch, T, q_pos0, N, m, scores, ld, write_invisible ? 1 : 0, chunks, cb);
         if (n_chunk_mm) *n_chunk_mm = 0;
     } else {
         // decode: split each query's entries over workgroups sized so that the whole grid is
