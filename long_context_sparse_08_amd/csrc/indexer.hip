@@ -411,9 +411,13 @@ int launch_mfma(const void* qI, const float* w, const void* kI, int64_t batch, i
                 uint32_t* zero, int zero_words, hipStream_t stream) {
     const int64_t nblk = (N + 31) / 32;
     if (T >= 4) {
-        // prefill: 8 queries per workgroup share each staged key block
+        // prefill: 8 queries per workgroup share each staged key block.  Long chunks amortise
+        // the workgroup's q loads (128 KB); rows are cut into chunks only as far as needed to
+        // keep ~1024 workgroups (four rounds of one per CU)
         const int64_t groups = batch * ((T + kPfWaves - 1) / kPfWaves);
-        const int cb = 16;
+        const int64_t want = (1024 + groups - 1) / groups;
+        int cb = (int)(((nblk + want - 1) / want + 3) / 4 * 4);
+        if (cb < 4) cb = 4;
         const int chunks = (int)((nblk + cb - 1) / cb);
         const int64_t grid = groups * chunks;
         if (grid > 0x7fffffffLL) return -2;
