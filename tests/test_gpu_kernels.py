@@ -87,6 +87,8 @@ IDX_CASES = [  # batch, T, q_pos0, N, H_I, c_I, m, dtype
     (1, 9, 5, 40, 1, 8, 4, F32),
     (1, 6, 50, 300, 32, 128, 4, BF16),       # 32 indexer heads, prefill mapping with a ragged group
     (2, 3, 1000, 333, 32, 128, 4, FP8),      # 32 indexer heads, decode mapping
+    (2, 20, 100, 700, 64, 128, 4, FP8),      # fp8 prefill mapping: many chunks, most past the visible prefix
+    (1, 64, 4000, 1200, 64, 128, 4, BF16),   # prefill mapping over several chunks, ragged last block
 ]
 
 
