@@ -282,9 +282,11 @@ topk_row_kernel(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t
 // Rows up to kBmMaxRow = 262144 visible entries (a 32 KB bitmap); rows up to kRowLds are
 // staged in LDS first.
 constexpr int kBmMaxRow = 262144;
-constexpr int kBmWordsLds = kRowLds / 32;
+constexpr int kShortRow = 4096;      // rows up to this use 256-thread workgroups
+constexpr int kShortThreads = 256;
 constexpr int kBmWordsGlb = kBmMaxRow / 32;
 
+template <int NW>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* buf, uint32_t* total) {
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
     uint32_t inc = x;
@@ -296,7 +298,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* buf, u
     if (lane == kWave - 1) buf[wid] = inc;
     __syncthreads();
     uint32_t before = 0, all = 0;
-    for (int i = 0; i < kWaves; ++i) {
+    for (int i = 0; i < NW; ++i) {
         const uint32_t v = buf[i];
         before += (i < wid) ? v : 0u;
         all += v;
@@ -306,18 +308,27 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* buf, u
     return before + inc - x;
 }
 
-template <bool IN_LDS>
-__global__ void __launch_bounds__(kThreads)
+template <int NB>
+__device__ __forceinline__ int bin_of_n(float v, float lo, float inv) {
+    float x = (v - lo) * inv;
+    x = fminf(fmaxf(x, 0.f), (float)(NB - 1));
+    return (int)x;
+}
+
+// NT threads per row, rows up to ROWL entries staged in LDS (IN_LDS), NB linear bins.
+template <bool IN_LDS, int NT, int ROWL, int NB>
+__global__ void __launch_bounds__(NT)
 topk_bitmap(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_pos0, int64_t N, int m, int k,
             const float* __restrict__ mm, int nmm, int32_t* __restrict__ idx, float* __restrict__ sel) {
-    constexpr int kWords = IN_LDS ? kBmWordsLds : kBmWordsGlb;
-    __shared__ float rowbuf[IN_LDS ? kRowLds : 1];
+    constexpr int NW = NT / kWave;
+    constexpr int kWords = IN_LDS ? ROWL / 32 : kBmWordsGlb;
+    __shared__ float rowbuf[IN_LDS ? ROWL : 1];
     __shared__ uint32_t bits[kWords];
-    __shared__ uint32_t hist[kBins];
+    __shared__ uint32_t hist[NB];
     __shared__ float cval[kCap];
     __shared__ int32_t cidx[kCap];
-    __shared__ float red_lo[kWaves], red_hi[kWaves];
-    __shared__ uint32_t scan_buf[kWaves];
+    __shared__ float red_lo[NW], red_hi[NW];
+    __shared__ uint32_t scan_buf[NW];
     __shared__ float s_lo, s_inv;
     __shared__ int s_bstar;
     __shared__ uint32_t s_need, s_ncand, s_need_eq, s_prefix, s_pmask;
@@ -328,7 +339,7 @@ topk_bitmap(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
     int32_t* oi = idx + row * k;
     float* os = sel ? sel + row * k : nullptr;
     if (nv <= k) {
-        for (int r = tid; r < k; r += kThreads) {
+        for (int r = tid; r < k; r += NT) {
             oi[r] = r < nv ? r : -1;
             if (os) os[r] = r < nv ? sc[r] : -INFINITY;
         }
@@ -348,13 +359,13 @@ topk_bitmap(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
         lo = -wave_max(-lo);
         hi = wave_max(hi);
         if (lane == 0) { red_lo[wid] = lo; red_hi[wid] = hi; }
-        for (int i = tid; i < kBins; i += kThreads) hist[i] = 0u;
-        for (int64_t i = tid; i < nwords; i += kThreads) bits[i] = 0u;
+        for (int i = tid; i < NB; i += NT) hist[i] = 0u;
+        for (int64_t i = tid; i < nwords; i += NT) bits[i] = 0u;
         __syncthreads();
         if (tid == 0) {
             float l = red_lo[0], h = red_hi[0];
-            for (int i = 1; i < kWaves; ++i) { l = fminf(l, red_lo[i]); h = fmaxf(h, red_hi[i]); }
-            float inv = (float)kBins / (h - l);
+            for (int i = 1; i < NW; ++i) { l = fminf(l, red_lo[i]); h = fmaxf(h, red_hi[i]); }
+            float inv = (float)NB / (h - l);
             if (!(h > l) || !isfinite(inv)) inv = 0.f;
             s_lo = l;
             s_inv = inv;
@@ -367,7 +378,7 @@ topk_bitmap(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
     };
     auto range_from_mm = [&]() {
         const float* r = mm + row * (int64_t)nmm * 2;
-        for (int i = tid; i < nmm; i += kThreads) {
+        for (int i = tid; i < nmm; i += NT) {
             lo = fminf(lo, r[2 * i]);
             hi = fmaxf(hi, r[2 * i + 1]);
         }
@@ -376,14 +387,15 @@ topk_bitmap(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
     if constexpr (IN_LDS) {
         // one pass: the row's loads are issued first (their latency overlaps the range
         // reduction), then the values go to LDS and into the histogram (or the min / max)
-        static_assert(kRowLds == 32 * kThreads, "a staged row is 8 float4 per thread");
+        constexpr int kF4 = ROWL / (4 * NT);   // float4 per thread
+        static_assert(ROWL == 4 * kF4 * NT, "a staged row is kF4 float4 per thread");
         const int64_t n4 = nv >> 2;
         const float4* s4 = reinterpret_cast<const float4*>(sc);
         float4* d4 = reinterpret_cast<float4*>(rowbuf);
-        float4 v[8];
+        float4 v[kF4];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int64_t i = tid + (int64_t)u * kThreads;
+        for (int u = 0; u < kF4; ++u) {
+            const int64_t i = tid + (int64_t)u * NT;
             v[u] = i < n4 ? s4[i] : make_float4(INFINITY, INFINITY, -INFINITY, -INFINITY);
         }
         const int64_t st = 4 * n4 + tid;   // the last nv % 4 entries, one per thread
@@ -391,15 +403,15 @@ topk_bitmap(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
         if (have_mm) range_from_mm();
         const float hlo = have_mm ? s_lo : 0.f, hinv = have_mm ? s_inv : 0.f;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int64_t i = tid + (int64_t)u * kThreads;
+        for (int u = 0; u < kF4; ++u) {
+            const int64_t i = tid + (int64_t)u * NT;
             if (i >= n4) continue;
             d4[i] = v[u];
             if (have_mm) {
-                atomicAdd(&hist[bin_of(v[u].x, hlo, hinv)], 1u);
-                atomicAdd(&hist[bin_of(v[u].y, hlo, hinv)], 1u);
-                atomicAdd(&hist[bin_of(v[u].z, hlo, hinv)], 1u);
-                atomicAdd(&hist[bin_of(v[u].w, hlo, hinv)], 1u);
+                atomicAdd(&hist[bin_of_n<NB>(v[u].x, hlo, hinv)], 1u);
+                atomicAdd(&hist[bin_of_n<NB>(v[u].y, hlo, hinv)], 1u);
+                atomicAdd(&hist[bin_of_n<NB>(v[u].z, hlo, hinv)], 1u);
+                atomicAdd(&hist[bin_of_n<NB>(v[u].w, hlo, hinv)], 1u);
             } else {
                 lo = fminf(lo, fminf(fminf(v[u].x, v[u].y), fminf(v[u].z, v[u].w)));
                 hi = fmaxf(hi, fmaxf(fmaxf(v[u].x, v[u].y), fmaxf(v[u].z, v[u].w)));
@@ -407,13 +419,13 @@ topk_bitmap(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
         }
         if (st < nv) {
             rowbuf[st] = vt;
-            if (have_mm) atomicAdd(&hist[bin_of(vt, hlo, hinv)], 1u);
+            if (have_mm) atomicAdd(&hist[bin_of_n<NB>(vt, hlo, hinv)], 1u);
             else { lo = fminf(lo, vt); hi = fmaxf(hi, vt); }
         }
     } else {
         if (have_mm) range_from_mm();
         else {
-            for (int64_t s = tid; s < nv; s += kThreads) {
+            for (int64_t s = tid; s < nv; s += NT) {
                 const float v = sc[s];
                 lo = fminf(lo, v);
                 hi = fmaxf(hi, v);
@@ -429,28 +441,28 @@ topk_bitmap(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
     // ---- histogram (unless built while staging)
     if (!(IN_LDS && have_mm)) {
         if constexpr (IN_LDS) {
-            for (int64_t s = tid; s < nv; s += kThreads) atomicAdd(&hist[bin_of(rowbuf[s], lo, inv)], 1u);
+            for (int64_t s = tid; s < nv; s += NT) atomicAdd(&hist[bin_of_n<NB>(rowbuf[s], lo, inv)], 1u);
         } else {
-            for (int64_t s0 = tid; s0 < nv; s0 += 8 * kThreads) {
+            for (int64_t s0 = tid; s0 < nv; s0 += 8 * NT) {
                 float v[8];
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
-                    const int64_t s = s0 + (int64_t)u * kThreads;
+                    const int64_t s = s0 + (int64_t)u * NT;
                     v[u] = s < nv ? sc[s] : 0.f;
                 }
 #pragma unroll
                 for (int u = 0; u < 8; ++u)
-                    if (s0 + (int64_t)u * kThreads < nv) atomicAdd(&hist[bin_of(v[u], lo, inv)], 1u);
+                    if (s0 + (int64_t)u * NT < nv) atomicAdd(&hist[bin_of_n<NB>(v[u], lo, inv)], 1u);
             }
         }
     }
     __syncthreads();
     {   // b*: a block scan over the bins from the top, two per thread
-        static_assert(kBins == 2 * kThreads, "two bins per thread");
-        const int top = kBins - 1 - 2 * tid;
+        static_assert(NB == 2 * NT, "two bins per thread");
+        const int top = NB - 1 - 2 * tid;
         const uint32_t h0 = hist[top], h1 = hist[top - 1];
         uint32_t total;
-        const uint32_t before = block_excl_scan(h0 + h1, scan_buf, &total);
+        const uint32_t before = block_excl_scan<NW>(h0 + h1, scan_buf, &total);
         if (before < (uint32_t)k && before + h0 + h1 >= (uint32_t)k) {   // exactly one thread
             if (before + h0 >= (uint32_t)k) {
                 s_bstar = top;
@@ -468,7 +480,7 @@ topk_bitmap(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
 
     // ---- mark bins above b*, gather b*'s members
     auto mark = [&](int64_t s, float v) {
-        const int bn = bin_of(v, lo, inv);
+        const int bn = bin_of_n<NB>(v, lo, inv);
         if (bn > bstar) {
             atomicOr(&bits[s >> 5], 1u << (s & 31));
         } else if (bn == bstar && fits) {
@@ -479,21 +491,21 @@ topk_bitmap(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
     if constexpr (IN_LDS) {
         // chunks of 64 entries, one per wave step: a ballot gives the chunk's two bitmap words
         // (every word is written, no atomics); b*'s members are appended one wave at a time
-        const int nvi = (int)nv;   // <= kRowLds
+        const int nvi = (int)nv;   // <= ROWL
         const int nchunk = (nvi + kWave - 1) / kWave;
         const unsigned long long below = (1ull << lane) - 1ull;
-        for (int c0 = wid; c0 < nchunk; c0 += 8 * kWaves) {
+        for (int c0 = wid; c0 < nchunk; c0 += 8 * NW) {
             float v[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u)   // clamped reads: always in the row; masked below
-                v[u] = rowbuf[min((c0 + u * kWaves) * kWave + lane, nvi - 1)];
+                v[u] = rowbuf[min((c0 + u * NW) * kWave + lane, nvi - 1)];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                const int c = c0 + u * kWaves;
+                const int c = c0 + u * NW;
                 if (c >= nchunk) break;
                 const int s = c * kWave + lane;
                 const bool ok = s < nvi;
-                const int bn = bin_of(v[u], lo, inv);
+                const int bn = bin_of_n<NB>(v[u], lo, inv);
                 const unsigned long long mk = __ballot(ok && bn > bstar);
                 if (lane == 0) reinterpret_cast<uint2*>(bits)[c] = make_uint2((uint32_t)mk, (uint32_t)(mk >> 32));
                 const bool eq = ok && bn == bstar && fits;
@@ -511,16 +523,16 @@ topk_bitmap(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
             }
         }
     } else {
-        for (int64_t s0 = tid; s0 < nv; s0 += 8 * kThreads) {
+        for (int64_t s0 = tid; s0 < nv; s0 += 8 * NT) {
             float v[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                const int64_t s = s0 + (int64_t)u * kThreads;
+                const int64_t s = s0 + (int64_t)u * NT;
                 v[u] = s < nv ? sc[s] : 0.f;
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u)
-                if (s0 + (int64_t)u * kThreads < nv) mark(s0 + (int64_t)u * kThreads, v[u]);
+                if (s0 + (int64_t)u * NT < nv) mark(s0 + (int64_t)u * NT, v[u]);
         }
     }
     __syncthreads();
@@ -544,7 +556,7 @@ topk_bitmap(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
     } else if (fits) {
         // rank b*'s members by (value desc, index asc); keep ranks < need
         const uint32_t nc = min(s_ncand, (uint32_t)kCap);
-        for (uint32_t i = tid; i < nc; i += kThreads) {
+        for (uint32_t i = tid; i < nc; i += NT) {
             const uint32_t ki = order_key(cval[i]);
             const int32_t si = cidx[i];
             uint32_t rank = 0;
@@ -559,12 +571,12 @@ topk_bitmap(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
         if (tid == 0) { s_prefix = 0u; s_pmask = 0u; s_need_eq = need; }
         __syncthreads();
         for (int shift = 24; shift >= 0; shift -= 8) {
-            for (int i = tid; i < 256; i += kThreads) hist[i] = 0u;
+            for (int i = tid; i < 256; i += NT) hist[i] = 0u;
             __syncthreads();
             const uint32_t prefix = s_prefix, pmask = s_pmask;
-            for (int64_t s = tid; s < nv; s += kThreads) {
+            for (int64_t s = tid; s < nv; s += NT) {
                 const float v = val(s);
-                if (bin_of(v, lo, inv) != bstar) continue;
+                if (bin_of_n<NB>(v, lo, inv) != bstar) continue;
                 const uint32_t key = order_key(v);
                 if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
             }
@@ -586,7 +598,7 @@ topk_bitmap(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
         }
         const uint32_t kstar = s_prefix, need_eq = s_need_eq;
         // keys above K* in b* are kept; of the keys equal to K*, the need_eq lowest indices
-        const int64_t seg = ((nv + (int64_t)kWaves * kWave - 1) / ((int64_t)kWaves * kWave)) * kWave;
+        const int64_t seg = ((nv + (int64_t)NW * kWave - 1) / ((int64_t)NW * kWave)) * kWave;
         const int64_t a = (int64_t)wid * seg, e = min(nv, a + seg);
         const unsigned long long lt = (1ull << lane) - 1ull;
         uint32_t c_eq = 0;
@@ -594,7 +606,7 @@ topk_bitmap(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
             const int64_t s = b0 + lane;
             const bool ok = s < e;
             const float v = ok ? val(s) : 0.f;
-            const bool inb = ok && bin_of(v, lo, inv) == bstar;
+            const bool inb = ok && bin_of_n<NB>(v, lo, inv) == bstar;
             const uint32_t key = order_key(v);
             if (inb && key > kstar) atomicOr(&bits[s >> 5], 1u << (s & 31));
             c_eq += __popcll(__ballot(inb && key == kstar));
@@ -607,7 +619,7 @@ topk_bitmap(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
             const int64_t s = b0 + lane;
             const bool ok = s < e;
             const float v = ok ? val(s) : 0.f;
-            const bool is_eq = ok && bin_of(v, lo, inv) == bstar && order_key(v) == kstar;
+            const bool is_eq = ok && bin_of_n<NB>(v, lo, inv) == bstar && order_key(v) == kstar;
             const unsigned long long meq = __ballot(is_eq);
             if (is_eq && run + __popcll(meq & lt) < need_eq) atomicOr(&bits[s >> 5], 1u << (s & 31));
             run += __popcll(meq);
@@ -616,12 +628,12 @@ topk_bitmap(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
     __syncthreads();
 
     // ---- ordered extraction: each thread owns a run of bitmap words
-    const int64_t per = (nwords + kThreads - 1) / kThreads;
+    const int64_t per = (nwords + NT - 1) / NT;
     const int64_t w0 = (int64_t)tid * per, w1 = min(nwords, w0 + per);
     uint32_t cnt = 0;
     for (int64_t w = w0; w < w1; ++w) cnt += __popc(bits[w]);
     uint32_t total;
-    uint32_t pos = block_excl_scan(cnt, scan_buf, &total);
+    uint32_t pos = block_excl_scan<NW>(cnt, scan_buf, &total);
     for (int64_t w = w0; w < w1; ++w) {
         uint32_t word = bits[w];
         while (word) {
@@ -942,7 +954,7 @@ tkm_select(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_po
         cnt += __popc(word);
     }
     uint32_t total;
-    uint32_t pos = block_excl_scan(cnt, scan, &total);
+    uint32_t pos = block_excl_scan<kWaves>(cnt, scan, &total);
     for (int64_t w = w0; w < w1; ++w) {
         uint32_t word = bits[w];
         if (w == nwords - 1 && (nv & 31)) word &= (1u << (nv & 31)) - 1u;
@@ -995,12 +1007,15 @@ int launch_topk(const float* scores, int64_t ld, int64_t batch, int64_t T, int64
         return 0;
     }
     const dim3 grid((unsigned)rows), block(kThreads);
-    if (nv_max <= kRowLds)
-        hipLaunchKernelGGL((topk_bitmap<true>), grid, block, 0, stream, scores, ld, T, q_pos0, N, m, k, chunk_mm,
-                           n_chunk_mm, idx, sel);
+    if (nv_max <= kShortRow)   // short rows (prefill): small workgroups, several rows per CU
+        hipLaunchKernelGGL((topk_bitmap<true, kShortThreads, kShortRow, 2 * kShortThreads>), grid, dim3(kShortThreads),
+                           0, stream, scores, ld, T, q_pos0, N, m, k, chunk_mm, n_chunk_mm, idx, sel);
+    else if (nv_max <= kRowLds)
+        hipLaunchKernelGGL((topk_bitmap<true, kThreads, kRowLds, kBins>), grid, block, 0, stream, scores, ld, T, q_pos0,
+                           N, m, k, chunk_mm, n_chunk_mm, idx, sel);
     else if (nv_max <= kBmMaxRow)
-        hipLaunchKernelGGL((topk_bitmap<false>), grid, block, 0, stream, scores, ld, T, q_pos0, N, m, k, chunk_mm,
-                           n_chunk_mm, idx, sel);
+        hipLaunchKernelGGL((topk_bitmap<false, kThreads, kRowLds, kBins>), grid, block, 0, stream, scores, ld, T,
+                           q_pos0, N, m, k, chunk_mm, n_chunk_mm, idx, sel);
     else
         hipLaunchKernelGGL((topk_row_kernel<false>), grid, block, 0, stream, scores, ld, T, q_pos0, N, m, k, idx, sel);
     return 0;
