@@ -32,6 +32,7 @@ CSA_CASES = [  # batch, n, m, c, in_t, out_t
     (1, 2 * 20 + 1, 2, 1024, F32, BF16),
     (3, 7 * 6 + 5, 7, 24, F32, F32),     # odd ratio, width not dividing a wave
     (1, 3, 4, 64, F32, F32),             # fewer tokens than one window: empty output
+    (1, 1024 * 3 + 5, 1024, 16, F32, F32),   # maximum ratio: 2048-token joint window
 ]
 
 
@@ -89,6 +90,8 @@ IDX_CASES = [  # batch, T, q_pos0, N, H_I, c_I, m, dtype
     (2, 3, 1000, 333, 32, 128, 4, FP8),      # 32 indexer heads, decode mapping
     (2, 20, 100, 700, 64, 128, 4, FP8),      # fp8 prefill mapping: many chunks, most past the visible prefix
     (1, 64, 4000, 1200, 64, 128, 4, BF16),   # prefill mapping over several chunks, ragged last block
+    (1, 3, 100, 50, 256, 16, 4, F32),        # maximum indexer heads (generic kernel)
+    (1, 2, 40, 30, 8, 1024, 4, F32),         # maximum indexer width (generic kernel)
 ]
 
 
@@ -177,6 +180,8 @@ MQA_CASES = [  # batch, T, N, H, c, k, dtype
     (2, 5, 700, 64, 512, 100, BF16),       # k not a multiple of the 32-key block
     (1, 2, 5000, 64, 512, 2048, BF16),     # maximum k, keys split over workgroups
     (1, 3, 40, 48, 512, 16, BF16),         # head count off the 64-head tiling (generic kernel)
+    (1, 2, 300, 256, 512, 64, BF16),       # maximum heads: four 64-head groups on matrix cores
+    (1, 1, 50, 256, 1024, 8, F32),         # maximum heads and width (generic kernel)
 ]
 
 
@@ -200,6 +205,7 @@ DENSE_CASES = [  # batch, T, q_pos0, N, H, c, m', dtype
     (1, 64, 128 * 300 - 40, 300, 64, 512, 128, BF16),
     (2, 3, 5000, 100, 2, 8, 128, F32),
     (1, 5, 0, 4, 2, 16, 128, F32),         # nothing visible at all
+    (1, 8, 128 * 200, 200, 128, 512, 128, BF16),   # two 64-head groups, every entry visible
 ]
 
 
