@@ -99,10 +99,9 @@ int hca_compress(const void* C, const void* Z, const float* B, int64_t batch, in
 
 // Workspace of csa_index_topk: the fp32 score rows, then room for the indexer's per-chunk
 // (min, max) pairs, then whatever the selection needs.  The chunk region is sized for the
-// largest chunk count any shape/dtype could use (one pair per 512 entries).
+// largest chunk count any shape/dtype could use (csa::max_index_chunks).
 size_t chunk_region(int64_t rows, int64_t N) {
-    const int64_t chunks = (N + 511) / 512;
-    return round_up((size_t)rows * (size_t)chunks * 2 * sizeof(float));
+    return round_up((size_t)rows * (size_t)csa::max_index_chunks(N) * 2 * sizeof(float));
 }
 
 size_t csa_index_topk_workspace_size(int64_t batch, int64_t T, int64_t N, int H_I, int k) {
@@ -134,7 +133,9 @@ int csa_index_topk(const void* qI, const float* w, const void* kI, int64_t batch
     int64_t nv_max = (q_pos0 + T) / m;
     if (nv_max > N) nv_max = N;
     // the decode-shaped indexer clears the selection's per-row counters when it will use them
-    const int zero_words = csa::index_chunks(batch, T, N, H_I, c_I, qk_t) > 0 ? csa::topk_zero_words(rows, nv_max) : 0;
+    const int n_chunks = csa::index_chunks(batch, T, N, H_I, c_I, qk_t);
+    if (n_chunks > csa::max_index_chunks(N)) return CSA_ERR_UNSUPPORTED;   // would overrun the chunk region
+    const int zero_words = n_chunks > 0 ? csa::topk_zero_words(rows, nv_max) : 0;
     uint32_t* zero = zero_words > 0 ? csa::topk_zero_region(extra, rows, N) : nullptr;
     int n_chunk_mm = 0;
     rc = csa::launch_index_scores(qI, w, kI, batch, T, q_pos0, N, H_I, c_I, m, qk_t, scores, ld, false, chunk_mm,

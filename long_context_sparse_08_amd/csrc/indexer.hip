@@ -445,6 +445,9 @@ int launch_mfma(const void* qI, const float* w, const void* kI, int64_t batch, i
 
 }  // namespace
 
+// a decode chunk holds at least 4 key blocks of 32 entries
+int64_t max_index_chunks(int64_t N) { return (N + 127) / 128; }
+
 int index_chunks(int64_t batch, int64_t T, int64_t N, int H_I, int c_I, int qk_t) {
     if (!mfma_shape(H_I, c_I, qk_t) || T >= 4 || N == 0) return 0;
     const int64_t nblk = (N + 31) / 32;

@@ -25,6 +25,8 @@ int launch_index_scores(const void* qI, const float* w, const void* kI, int64_t 
 
 // Number of (min, max) pairs per row the indexer writes into chunk_mm for these sizes (0: none).
 int index_chunks(int64_t batch, int64_t T, int64_t N, int H_I, int c_I, int qk_t);
+// Upper bound of index_chunks(...) over every batch, T, shape and dtype for N entries.
+int64_t max_index_chunks(int64_t N);
 
 // Workspace bytes needed by launch_topk beyond the score rows.
 size_t topk_extra_workspace(int64_t rows, int64_t N, int k);

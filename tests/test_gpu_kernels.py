@@ -147,6 +147,33 @@ def test_topk_bit_exact_with_exact_scores(case):
     assert np.array_equal(sel, ref_sel.astype(np.float32).astype(np.float64))
 
 
+MULTI_TOPK_CASES = [  # batch, T, q_pos0, N, k, levels, zero-key fraction: rows over 32K entries
+    (2, 1, 4 * 40000, 40000, 1024, 4, 0.0),
+    (1, 3, 4 * 70000 - 6, 70000, 2048, 2, 0.0),   # rows of different lengths; ~150-way tie at the cut
+    (1, 2, 4 * 50000, 50000, 1024, 3, 0.99),      # the cut falls in a tie of ~49K zero scores
+    (1, 1, 4 * 36000, 36000, 512, 1, 0.0),        # every score equal
+]
+
+
+@pytest.mark.parametrize("case", MULTI_TOPK_CASES, ids=lambda c: "b%d_T%d_p%d_N%d_k%d_l%d_z%g" % c)
+def test_topk_multi_workgroup_bit_exact(case):
+    # few long rows with the decode indexer's per-chunk ranges take the selection that splits
+    # each row over several workgroups; integer-valued fp8 inputs keep every score exact
+    batch, T, p0, N, k, levels, zfrac = case
+    H, cI, m = 64, 128, 4
+    say(f"csa_index_topk multi-workgroup case {case}")
+    qI, w, kI = _integer_inputs(batch, T, N, H, cI, 950 + N, levels)
+    kI[np.random.RandomState(N).random_sample((batch, N)) < zfrac] = 0.0
+    q8, k8 = rng.f32_to_e4m3_bits(qI), rng.f32_to_e4m3_bits(kI)
+    assert np.array_equal(rng.e4m3_bits_to_f32(q8), qI) and np.array_equal(rng.e4m3_bits_to_f32(k8), kI)
+    sc = oracle.index_scores(q8, w, k8, m, q_pos0=p0, qk_dtype=FP8)
+    ref_idx, ref_sel = oracle.topk(sc, m, k, q_pos0=p0)
+    idx, sel = csa.csa_index_topk(to_dev(q8, FP8), to_dev(w, F32), to_dev(k8, FP8), p0, m, k)
+    idx, sel = from_dev(idx), from_dev(sel)
+    assert np.array_equal(idx, ref_idx)
+    assert np.array_equal(sel, ref_sel.astype(np.float32).astype(np.float64))
+
+
 def test_topk_bit_exact_random_fp32():
     batch, T, N, H, cI, m, k = 2, 200, 50, 2, 32, 4, 8
     sd = 900
