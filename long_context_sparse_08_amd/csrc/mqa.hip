@@ -119,8 +119,11 @@ int launch_generic(const void* q, const void* kv, const int32_t* idx, int64_t ba
 //
 // Workgroup = (query row, 64 heads, one contiguous range of key slots).  Its 4 waves own 16
 // heads each and walk the same 32-key blocks: the selected KV rows of a block are gathered
-// straight from global memory into LDS (global_load_lds_dwordx4: one 1 KB row per
-// instruction, no registers), double-buffered, so block j+1 loads while block j computes.
+// straight from global memory into LDS (buffer_load_dwordx4 ... lds: one 1 KB row per
+// instruction, no registers), so later blocks load while block j computes.  The buffer form,
+// not global_load_lds: the compiler counts a global (flat-encoded) load to LDS as pending on
+// both memory counters, and would then wait for every LDS read in flight (lgkmcnt(0)) before
+// using any one of them, which defeats the operand prefetch below.
 //
 //   S^T = KV_blk . Q^T   M = 16 keys, N = 16 heads, K = c.  A = KV rows from LDS (16-byte
 //                        reads), B = this wave's q, held in registers for the whole kernel.
@@ -142,14 +145,29 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
-typedef __attribute__((address_space(1))) void* glb_void_ptr;
 
 constexpr int kMC = 512;                       // head dim handled by the MFMA kernel
+// entries of one sequence's KV one buffer resource can address (32-bit byte offsets)
+constexpr int64_t kMMaxEntries = ((int64_t(1) << 32) - 1) / (2 * kMC);
 constexpr int kMHeadsWG = 64;                  // heads per workgroup
 constexpr int kMBlk = 32;                      // keys per staged block
-constexpr int kMPitch = kMC * 2 + 32;          // LDS bytes per staged row (bank spread)
-constexpr int kMBuf = kMBlk * kMPitch;         // bytes per staged block
+// LDS bytes per staged row: swizzled 1 KB rows (see swz) or, where the registers for the
+// swizzled addresses are not available, plain rows padded by 32 bytes (a bank spread that
+// leaves the plain reads of the scores with two-way conflicts)
+template <bool SWZ> constexpr int kMPitch = SWZ ? kMC * 2 : kMC * 2 + 32;
+template <bool SWZ> constexpr int kMBuf = kMBlk * kMPitch<SWZ>;   // bytes per staged block
 constexpr int kMLoadsPerBlk = kMBlk / 4;       // rows each of the 4 waves stages per block (8)
+
+// A staged row keeps its 16-byte chunk c (8 channels) at chunk position c ^ swz(r), r the
+// row's index in its block.  The 64 banks of 4 bytes see the 16 rows a 16-lane group of
+// plain reads touches (same chunk, rows 0-15) in 16 different 4-bank groups, and the 8 rows
+// of a half-wave of transposing reads (two chunks each, rows 0-7 or 8-15) in 16 groups too:
+// neither access pattern has a bank conflict, where an unswizzled layout (or a padded row
+// pitch) gives at least one of them a two-way conflict.
+__device__ __forceinline__ int swz(int r) {   // chunk swizzle of row r (0..15 per half block)
+    r &= 15;
+    return ((2 * r) & 15) | (r >> 3);
+}
 
 // s_waitcnt with vmcnt = n (0..63), expcnt and lgkmcnt left at their maximum (no wait)
 template <int n>
@@ -205,8 +223,13 @@ __device__ __forceinline__ float sum_xor16(float x) {
 // 64 heads).  The P.KV operand is the transposed KV block, read from LDS with transposing
 // reads that run at about half the rate of plain ones; split by columns, each transposed
 // fragment feeds four head tiles instead of one.  The waves swap their bf16 probability
-// tiles (1 KB each) and rescale factors through LDS once per block.  Two staging buffers:
-// while one 32-key block is computed the next one loads.
+// tiles (1 KB each) and rescale factors through LDS once per block.
+//
+// NS staging buffers of one 32-key block each.  NS = 2: while one block is computed the next
+// one loads; the co-resident workgroup covers the rest of the gather latency.  NS = 4 (~148 KB
+// of LDS, one workgroup per CU, for launches of at most one workgroup per CU such as decode):
+// three blocks are in flight while one is computed, which covers the latency of a gather of
+// scattered 1 KB rows within the workgroup itself.
 constexpr int kMWaves = 4;
 constexpr int kMHT = kMHeadsWG / 16;      // 16-head tiles per workgroup (4)
 constexpr int kMColW = kMC / kMHT;        // output columns per wave (128)
@@ -214,8 +237,8 @@ constexpr int kMColBlkW = kMColW / 16;    // 16-column blocks per wave (8)
 constexpr int kMIdsLds = 1024;            // key ids staged per workgroup (longer ranges are split)
 constexpr int kMFillWGs = 256;            // workgroups a key split aims for
 
-template <bool DENSE>
-__global__ void __launch_bounds__(kMWaves * kWave, 2)   // two waves per SIMD: two workgroups per CU
+template <bool DENSE, int NS>
+__global__ void __launch_bounds__(kMWaves * kWave, NS == 2 ? 2 : 1)   // NS = 2: two workgroups per CU
 mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
                 int64_t rows, int64_t T, int64_t N, int H, int k, int ks_count, int keys_per_split, float sl2,
                 int64_t q_pos0, int ratio, uint16_t* __restrict__ out, uint16_t* __restrict__ part,
@@ -223,9 +246,16 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     // one array per pipeline parity: the DMA into one and the reads of the other are then
     // provably disjoint, so no wait for the in-flight gather is forced before the current
     // block's LDS reads
-    __shared__ __attribute__((aligned(16))) uint8_t stage_a[kMBuf];
-    __shared__ __attribute__((aligned(16))) uint8_t stage_b[kMBuf];
+    static_assert(NS == 2 || NS == 4, "stages");
+    // the four-stage kernel (one workgroup per CU) has the registers for swizzled addresses
+    constexpr bool SWZ = NS == 4;
+    constexpr int kPitch = kMPitch<SWZ>, kBuf = kMBuf<SWZ>;
+    __shared__ __attribute__((aligned(16))) uint8_t stage_a[kBuf];
+    __shared__ __attribute__((aligned(16))) uint8_t stage_b[kBuf];
+    __shared__ __attribute__((aligned(16))) uint8_t stage_c[NS == 4 ? kBuf : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t stage_d[NS == 4 ? kBuf : 16];
     __shared__ int32_t ids[DENSE ? 1 : kMIdsLds];
+    __shared__ uint32_t vmask[DENSE ? 1 : kMIdsLds / 32];
     // [0]: probability tiles in the B-operand lane layout; [1][tile][head].x: rescale factor.
     // One array, so both are stored through the same lane address (no extra register).
     __shared__ uint4 xp[2][kMHT][kWave];
@@ -250,8 +280,10 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int nkeys = (int)max((int64_t)0, min(klen, (int64_t)key0 + keys_per_split) - key0);
     const int h0 = hg * kMHeadsWG;
     const int n_ent = (int)N;   // entry ids are 32-bit (the C ABI rejects N >= 2^31)
-    auto key_id = [&](int i) -> int {   // key id of slot i of this range (-1: none)
-        if (i >= nkeys) return -1;
+    // entry gathered for slot i of this range: slots past the range and invalid ids load
+    // entry 0, which the validity mask of the block keeps out of the softmax
+    auto key_id = [&](int i) -> int {
+        if (i >= nkeys) return 0;
         if constexpr (DENSE) return key0 + i;
         else return ids[i];
     };
@@ -272,10 +304,19 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
 #pragma unroll
     for (int s = 0; s < kMC / 32; ++s) qb[s] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * s);
     if constexpr (!DENSE) {
+        // ids in LDS with invalid ones (negative padding, or >= N) replaced by 0, and a bit
+        // per slot (word j: the 32 slots of block j) that tells the valid ones
 #pragma unroll
         for (int u = 0; u < kIdsPerThread; ++u) {
             const int i = tid + u * kMWaves * kWave;
-            if (i < nkeys) ids[i] = idv[u];
+            const bool ok = i < nkeys && (uint32_t)idv[u] < (uint32_t)n_ent;
+            if (i < nkeys) ids[i] = ok ? idv[u] : 0;
+            const unsigned long long bits = __ballot(ok);
+            if (lane == 0) {
+                const int w = (u * kMWaves * kWave + kWave * tw) / 32;
+                vmask[w] = (uint32_t)bits;
+                vmask[w + 1] = (uint32_t)(bits >> 32);
+            }
         }
         __syncthreads();
     }
@@ -290,33 +331,51 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
 
     const int nblk = (nkeys + kMBlk - 1) / kMBlk;
     const uint8_t* kvbytes = reinterpret_cast<const uint8_t*>(kv + b * N * (int64_t)kMC);
+    // this sequence's KV rows (N <= kMMaxEntries, checked at launch); loads past them read 0
+    const __amdgpu_buffer_rsrc_t kvres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(kvbytes), (short)0, (int)(uint32_t)(N * 2 * kMC), 0x00020000);
     const uint32_t lane_off = 16u * lane;
     auto gather = [&](int blk, uint8_t* dst) {   // block `blk` of the range into `dst`
+        // NS = 4: the wave's 8 key ids in one LDS round trip (lane j holds row j's id).  The
+        // two-stage kernels, at the register limit of two workgroups per CU, read them one by one.
+        const int myid = NS == 4 && lane < kMLoadsPerBlk ? key_id(blk * kMBlk + kMLoadsPerBlk * tw + lane) : 0;
 #pragma unroll
         for (int r8 = 0; r8 < kMLoadsPerBlk; ++r8) {
             const int r = kMLoadsPerBlk * tw + r8;
             // one 1 KB row per instruction: the row is wave-uniform (scalar base, lane offset)
-            int sidx = __builtin_amdgcn_readfirstlane(key_id(blk * kMBlk + r));
-            if (sidx < 0 || sidx >= n_ent) sidx = 0;   // invalid slots load row 0, masked below
-            const uint8_t* src = kvbytes + (int64_t)sidx * (2 * kMC) + lane_off;
-            __builtin_amdgcn_global_load_lds((glb_void_ptr)src, (lds_void_ptr)(dst + r * kMPitch), 16, 0, 0);
+            const int sidx = NS == 4 ? __builtin_amdgcn_readlane(myid, r8)
+                                     : __builtin_amdgcn_readfirstlane(key_id(blk * kMBlk + r));
+            // lane j fetches the chunk that belongs at position j of the (swizzled) row
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kvres, (lds_void_ptr)(dst + r * kPitch), 16,
+                                                     SWZ ? 16u * (lane ^ swz(r)) : lane_off,
+                                                     (uint32_t)sidx * (2 * kMC), 0, 0);
         }
     };
+    // per-lane parts of the LDS addresses of the operands (swizzled: see swz)
+    int aoff[4];
+#pragma unroll
+    for (int b4 = 0; b4 < 4; ++b4) aoff[b4] = SWZ ? 16 * ((4 * b4 + g) ^ swz(n16)) : 0;
     auto compute = [&](int blk, const uint8_t* st) {
         // validity of the 32 keys of this block (bit r), shifted to this lane's key group
         uint32_t vg;
-        {
-            const int sidx = key_id(blk * kMBlk + (lane & 31));
-            const uint32_t valid = (uint32_t)__ballot(lane < 32 && (uint32_t)sidx < (uint32_t)n_ent);
-            vg = valid >> (4 * g);
+        if constexpr (DENSE) {
+            const int nv = nkeys - blk * kMBlk;   // >= 1
+            vg = (nv >= 32 ? ~0u : (1u << nv) - 1u) >> (4 * g);
+        } else {
+            vg = vmask[blk] >> (4 * g);
         }
 
         // S^T for the two 16-key halves (two independent accumulation chains); the A operands
         // are read kSD steps ahead of their use so LDS latency overlaps the matrix work
-        constexpr int kSD = 4;
+        constexpr int kSD = NS == 2 && !DENSE ? 3 : 4;   // the two-stage sparse kernel is at its register limit
         f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-        const uint8_t* arow = st + n16 * kMPitch + 16 * g;
-        auto lda = [&](int s, int h) { return *reinterpret_cast<const bf16x8_t*>(arow + 16 * kMPitch * h + 64 * s); };
+        // chunk 4s + g of rows n16 and 16 + n16 (swizzled, s = 4a + b: at position
+        // 16a + ((4b + g) ^ swz(n16)))
+        const uint8_t* arow = st + n16 * kPitch + (SWZ ? 0 : 16 * g);
+        auto lda = [&](int s, int h) {
+            const int o = SWZ ? 256 * (s >> 2) + aoff[s & 3] : 64 * s;
+            return *reinterpret_cast<const bf16x8_t*>(arow + 16 * kPitch * h + o);
+        };
         bf16x8_t ra[kSD][2];
 #pragma unroll
         for (int j = 0; j < kSD; ++j) {
@@ -336,11 +395,17 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
         // V^T operands of this wave's columns: transpose reads of keys {4g..4g+3} and
         // {16+4g..}; the first kVD column blocks are requested before the softmax
         constexpr int kVD = 3;
-        const uint8_t* vbase = st + (4 * g + (n16 >> 2)) * kMPitch + 8 * (n16 & 3) + 2 * kMColW * tw;
+        // columns 128 tw + 16 cb + 4 (n16 & 3) .. +4 of rows 4g + (n16 >> 2) and 16 + that:
+        // chunk 16 tw + 2 cb + ((n16 & 3) >> 1), at position 16 tw + ((2 cb + ..) ^ swz(row))
+        const int vr = 4 * g + (n16 >> 2), vs = swz(vr);
+        // swizzled: bits 5-7 of vofs hold (swz >> 1); column block cb is then at vofs ^ (32 cb)
+        const int vofs = vr * kPitch + 256 * tw + 32 * (vs >> 1) + 16 * (((n16 & 3) >> 1) ^ (vs & 1)) + 8 * (n16 & 1);
+        const uint8_t* vbase = st + vr * kPitch + 8 * (n16 & 3) + 2 * kMColW * tw;   // unswizzled
         auto ldv = [&](int cb) {
             typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-            const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 32 * cb));
-            const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 16 * kMPitch + 32 * cb));
+            const uint8_t* va_ = SWZ ? st + (vofs ^ (32 * cb)) : vbase + 32 * cb;
+            const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)va_);
+            const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(va_ + 16 * kPitch));
             typedef short i16x8 __attribute__((ext_vector_type(8)));
             const i16x8 va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
             return __builtin_bit_cast(bf16x8_t, va);
@@ -414,17 +479,54 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                 acc[ht][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pb[ht], acc[ht][cb], 0, 0, 0);
         }
     };
-    if (nblk > 0) gather(0, stage_a);   // the loop's first wait also covers q
-    for (int blk = 0; blk < nblk; blk += 2) {
-        wait_vmcnt<0>();
-        __syncthreads();   // block blk is staged in A; every wave is done with B
-        if (blk + 1 < nblk) gather(blk + 1, stage_b);
-        compute(blk, stage_a);
-        if (blk + 1 >= nblk) break;
-        wait_vmcnt<0>();
-        __syncthreads();   // block blk+1 is staged in B; every wave is done with A
-        if (blk + 2 < nblk) gather(blk + 2, stage_a);
-        compute(blk + 1, stage_b);
+    if constexpr (NS == 2) {
+        if (nblk > 0) gather(0, stage_a);   // the loop's first wait also covers q
+        for (int blk = 0; blk < nblk; blk += 2) {
+            wait_vmcnt<0>();
+            __syncthreads();   // block blk is staged in A; every wave is done with B
+            if (blk + 1 < nblk) gather(blk + 1, stage_b);
+            compute(blk, stage_a);
+            if (blk + 1 >= nblk) break;
+            wait_vmcnt<0>();
+            __syncthreads();   // block blk+1 is staged in B; every wave is done with A
+            if (blk + 2 < nblk) gather(blk + 2, stage_a);
+            compute(blk + 1, stage_b);
+        }
+    } else if (nblk > 0) {
+        // Every step issues its gather, also past the last block (all of whose slots load
+        // row 0 of the sequence, from L2, into a buffer no later step reads), so that every
+        // step has the same count of outstanding loads and one wait count fits all steps.
+        // (With counts that depend on the step, the compiler cannot tell which buffer a
+        // pending load writes and waits for all of them before reading any buffer.)
+        // Blocks 0..2 are in flight before the first wait (which also covers q).
+        gather(0, stage_a);
+        gather(1, stage_b);
+        gather(2, stage_c);
+        // block b is staged once only the two later steps' loads are outstanding (a wave's
+        // loads complete in issue order); the barrier then also tells that every wave is done
+        // with the buffer of block b-1, which the load of block b+3 reuses
+        auto staged = [&]() {
+            wait_vmcnt<2 * kMLoadsPerBlk>();
+            lds_barrier();
+        };
+        for (int blk = 0; blk < nblk; blk += 4) {
+            staged();
+            gather(blk + 3, stage_d);
+            compute(blk, stage_a);
+            if (blk + 1 >= nblk) break;
+            staged();
+            gather(blk + 4, stage_a);
+            compute(blk + 1, stage_b);
+            if (blk + 2 >= nblk) break;
+            staged();
+            gather(blk + 5, stage_b);
+            compute(blk + 2, stage_c);
+            if (blk + 3 >= nblk) break;
+            staged();
+            gather(blk + 6, stage_c);
+            compute(blk + 3, stage_d);
+        }
+        wait_vmcnt<0>();   // the loads past the last block, before the buffers are reused
     }
 
     // sum of the softmax denominators over the four lane groups that share a head
@@ -433,40 +535,47 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
         xm[tw][n16] = m_run;
         xl[tw][n16] = l_run;
     }
-    __syncthreads();
-    const int c0 = kMColW * tw;
-    if (part == nullptr) {
+    __syncthreads();   // every wave is past its last block: the staging buffers are free
+    // Normalised bf16 rows go through LDS (heads 0-31 in A, 32-63 in B, one row per head) so
+    // that each store below writes one head's whole 1 KB row instead of 32-byte pieces of 16.
 #pragma unroll
-        for (int ht = 0; ht < kMHT; ++ht) {
-            const float l = xl[ht][n16];
-            const float inv = l > 0.f ? 1.f / l : 0.f;
-            uint16_t* orow = out + (row * H + h0 + 16 * ht + n16) * kMC + c0;
+    for (int ht = 0; ht < kMHT; ++ht) {
+        const float l = xl[ht][n16];
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        // columns 128 tw + 16 cb + 4g .. +4 of head row 16 (ht & 1) + n16, swizzled as the
+        // staged keys are: chunk 16 tw + 2 cb + (g >> 1) at position 16 tw + ((2 cb + ..) ^ swz)
+        const int sw = swz(n16);
+        const int erow = (16 * (ht & 1) + n16) * kPitch + 256 * tw;
+        const int eofs = SWZ ? erow + 32 * (sw >> 1) + 16 * ((g >> 1) ^ (sw & 1)) + 8 * (g & 1) : erow + 8 * g;
+        uint8_t* sbuf = ht < 2 ? stage_a : stage_b;
 #pragma unroll
-            for (int cb = 0; cb < kMColBlkW; ++cb) {
-                uint2 w2;
-                w2.x = pack_bf16x2(acc[ht][cb][0] * inv, acc[ht][cb][1] * inv);
-                w2.y = pack_bf16x2(acc[ht][cb][2] * inv, acc[ht][cb][3] * inv);
-                *reinterpret_cast<uint2*>(orow + 16 * cb + 4 * g) = w2;
-            }
+        for (int cb = 0; cb < kMColBlkW; ++cb) {
+            uint2 w2;
+            w2.x = pack_bf16x2(acc[ht][cb][0] * inv, acc[ht][cb][1] * inv);
+            w2.y = pack_bf16x2(acc[ht][cb][2] * inv, acc[ht][cb][3] * inv);
+            *reinterpret_cast<uint2*>(sbuf + (SWZ ? eofs ^ (32 * cb) : eofs + 32 * cb)) = w2;
         }
-    } else {
+    }
+    __syncthreads();
+    // the (row, 64 heads) slab of the output, or of this key range's partials
+    uint16_t* dst = out + (row * H + h0) * (int64_t)kMC;
+    if constexpr (!DENSE)
+        if (part != nullptr) dst = part + ((row * ks_count + ks) * H + h0) * (int64_t)kMC;
 #pragma unroll
-        for (int ht = 0; ht < kMHT; ++ht) {
-            const int64_t prow = (row * ks_count + ks) * H + h0 + 16 * ht + n16;
-            const float l = xl[ht][n16];
-            const float inv = l > 0.f ? 1.f / l : 0.f;
-            uint16_t* pr = part + prow * kMC + c0;
-#pragma unroll
-            for (int cb = 0; cb < kMColBlkW; ++cb) {
-                uint2 w2;
-                w2.x = pack_bf16x2(acc[ht][cb][0] * inv, acc[ht][cb][1] * inv);
-                w2.y = pack_bf16x2(acc[ht][cb][2] * inv, acc[ht][cb][3] * inv);
-                *reinterpret_cast<uint2*>(pr + 16 * cb + 4 * g) = w2;
-            }
-            if (ht == tw && g == 0) {
-                part_ml[2 * prow] = m_run;
-                part_ml[2 * prow + 1] = l_run;
-            }
+    for (int j = 0; j < 8; ++j) {
+        const int r = 8 * tw + j;
+        // position `lane` of row r holds chunk lane ^ swz(r) (rows r and 32 + r swizzle alike)
+        const int c = SWZ ? lane ^ swz(r) : lane;
+        const uint4 va = *reinterpret_cast<const uint4*>(stage_a + r * kPitch + 16 * lane);
+        const uint4 vb = *reinterpret_cast<const uint4*>(stage_b + r * kPitch + 16 * lane);
+        *reinterpret_cast<uint4*>(dst + (int64_t)r * kMC + 8 * c) = va;
+        *reinterpret_cast<uint4*>(dst + (int64_t)(32 + r) * kMC + 8 * c) = vb;
+    }
+    if constexpr (!DENSE) {
+        if (part != nullptr && g == 0) {
+            const int64_t prow = (row * ks_count + ks) * H + h0 + 16 * tw + n16;
+            part_ml[2 * prow] = m_run;
+            part_ml[2 * prow + 1] = l_run;
         }
     }
 }
@@ -547,7 +656,7 @@ size_t sparse_mqa_workspace(int64_t batch, int64_t T, int H, int c, int k, int t
 int launch_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t batch, int64_t T, int64_t N, int H,
                       int c, int k, float scale, int t, void* out, void* ws, hipStream_t stream) {
     if (batch == 0 || T == 0) return 0;
-    if (t == DT_BF16 && c == kMC && H % kMHeadsWG == 0) {
+    if (t == DT_BF16 && c == kMC && H % kMHeadsWG == 0 && N > 0 && N <= kMMaxEntries) {
         const int64_t rows = batch * T;
         const int ks = mqa_splits(rows, H, k);
         const int kps = ((k + ks - 1) / ks + kMBlk - 1) / kMBlk * kMBlk;
@@ -560,7 +669,9 @@ int launch_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t
             part_ml = reinterpret_cast<float*>(part + rows * ks * H * (int64_t)kMC);
         }
         const float sl2 = scale * kLog2e;
-        hipLaunchKernelGGL(mqa_sparse_mfma<false>, dim3((unsigned)units), dim3(kMWaves * kWave), 0, stream,
+        // at most one workgroup per CU: the deep pipeline (its LDS allows only one)
+        auto kern = units <= kMFillWGs ? mqa_sparse_mfma<false, 4> : mqa_sparse_mfma<false, 2>;
+        hipLaunchKernelGGL(kern, dim3((unsigned)units), dim3(kMWaves * kWave), 0, stream,
                            static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx, rows, T, N, H, k, ks,
                            kps, sl2, (int64_t)0, 1, static_cast<uint16_t*>(out), part, part_ml);
         if (ks > 1)
@@ -576,13 +687,13 @@ int launch_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t
 int launch_dense_mqa(const void* q, const void* kv, int64_t batch, int64_t T, int64_t q_pos0, int64_t N, int H, int c,
                      int ratio, float scale, int t, void* out, hipStream_t stream) {
     if (batch == 0 || T == 0) return 0;
-    if (t == DT_BF16 && c == kMC && H % kMHeadsWG == 0 && N <= 0x7fffffffLL) {
+    if (t == DT_BF16 && c == kMC && H % kMHeadsWG == 0 && N <= kMMaxEntries) {
         // one workgroup per (query, 64 heads) walks every visible entry: no key split, no
         // partials (used for query chunks, which supply rows * H / 64 >= 256 workgroups)
         const int64_t rows = batch * T;
         const int64_t units = ((rows + 7) / 8) * 8 * (H / kMHeadsWG);
         if (units > 0x7fffffffLL) return -2;
-        hipLaunchKernelGGL(mqa_sparse_mfma<true>, dim3((unsigned)units), dim3(kMWaves * kWave), 0, stream,
+        hipLaunchKernelGGL((mqa_sparse_mfma<true, 2>), dim3((unsigned)units), dim3(kMWaves * kWave), 0, stream,
                            static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), nullptr, rows, T, N, H, 0,
                            1, 0x7fffffff, scale * kLog2e, q_pos0, ratio, static_cast<uint16_t*>(out), nullptr, nullptr);
         return 0;
