@@ -104,11 +104,19 @@ size_t chunk_region(int64_t rows, int64_t N) {
     return round_up((size_t)rows * (size_t)csa::max_index_chunks(N) * 2 * sizeof(float));
 }
 
+// Group maxima for the group-bounded selection (decode-shaped calls, T < 4): at most
+// csa::kTopkMaxGroups per row.
+size_t group_region(int64_t rows, int64_t T, int64_t N, int k) {
+    if (T >= 4 || N <= k) return 0;
+    return round_up((size_t)rows * (size_t)csa::kTopkMaxGroups * sizeof(float));
+}
+
 size_t csa_index_topk_workspace_size(int64_t batch, int64_t T, int64_t N, int H_I, int k) {
     if (batch < 0 || T < 0 || N < 0 || H_I < 1 || k < 1) return 0;
     const int64_t rows = batch * T;
     const size_t scores = round_up((size_t)rows * (size_t)score_ld(N) * sizeof(float));
-    return scores + chunk_region(rows, N) + round_up(csa::topk_extra_workspace(rows, N, k)) + kWsAlign;
+    return scores + chunk_region(rows, N) + round_up(csa::topk_extra_workspace(rows, N, k)) +
+           group_region(rows, T, N, k) + kWsAlign;
 }
 
 int csa_index_topk(const void* qI, const float* w, const void* kI, int64_t batch, int64_t T, int64_t q_pos0, int64_t N,
@@ -135,14 +143,22 @@ int csa_index_topk(const void* qI, const float* w, const void* kI, int64_t batch
     // the decode-shaped indexer clears the selection's per-row counters when it will use them
     const int n_chunks = csa::index_chunks(batch, T, N, H_I, c_I, qk_t);
     if (n_chunks > csa::max_index_chunks(N)) return CSA_ERR_UNSUPPORTED;   // would overrun the chunk region
-    const int zero_words = n_chunks > 0 ? csa::topk_zero_words(rows, nv_max) : 0;
+    // the decode-shaped indexer (n_chunks > 0) also writes group maxima when the selection can
+    // use them; otherwise it clears the multi-workgroup selection's per-row counters if needed
+    const int G = n_chunks > 0 && group_region(rows, T, N, k) > 0 ? csa::topk_group(nv_max, k) : 0;
+    const int64_t gld = G > 0 ? (nv_max + G - 1) / G : 0;   // <= kTopkMaxGroups
+    float* gmax = G > 0 ? reinterpret_cast<float*>(static_cast<char*>(extra) +
+                                                   round_up(csa::topk_extra_workspace(rows, N, k)))
+                        : nullptr;
+    const int zero_words = n_chunks > 0 && G == 0 ? csa::topk_zero_words(rows, nv_max) : 0;
     uint32_t* zero = zero_words > 0 ? csa::topk_zero_region(extra, rows, N) : nullptr;
     int n_chunk_mm = 0;
     rc = csa::launch_index_scores(qI, w, kI, batch, T, q_pos0, N, H_I, c_I, m, qk_t, scores, ld, false, chunk_mm,
-                                  &n_chunk_mm, zero, zero_words, st);
+                                  &n_chunk_mm, zero, zero_words, gmax, G, gld, st);
     if (rc != 0) return finish(rc);
     return finish(csa::launch_topk(scores, ld, batch, T, q_pos0, N, m, k, idx, sel_scores,
-                                   n_chunk_mm > 0 ? chunk_mm : nullptr, n_chunk_mm, zero_words > 0 ? extra : nullptr, st));
+                                   n_chunk_mm > 0 ? chunk_mm : nullptr, n_chunk_mm, gmax, G, gld,
+                                   zero_words > 0 ? extra : nullptr, st));
 }
 
 int csa_index_scores(const void* qI, const float* w, const void* kI, int64_t batch, int64_t T, int64_t q_pos0, int64_t N,
@@ -152,7 +168,7 @@ int csa_index_scores(const void* qI, const float* w, const void* kI, int64_t bat
     if (batch == 0 || T == 0 || N == 0) return CSA_OK;
     if (!scores) return CSA_ERR_INVALID_ARG;
     return finish(csa::launch_index_scores(qI, w, kI, batch, T, q_pos0, N, H_I, c_I, m, qk_t, scores, N, true, nullptr,
-                                           nullptr, nullptr, 0, static_cast<hipStream_t>(stream)));
+                                           nullptr, nullptr, 0, nullptr, 0, 0, static_cast<hipStream_t>(stream)));
 }
 
 size_t csa_topk_workspace_size(int64_t batch, int64_t T, int64_t N, int k) {
@@ -170,8 +186,8 @@ int csa_topk(const float* scores, int64_t ld, int64_t batch, int64_t T, int64_t 
     if (sel_scores && !aligned16(sel_scores)) return CSA_ERR_INVALID_ARG;
     if (!workspace || ws_bytes < csa_topk_workspace_size(batch, T, N, k) || !aligned16(workspace))
         return CSA_ERR_WORKSPACE;
-    return finish(csa::launch_topk(scores, ld, batch, T, q_pos0, N, m, k, idx, sel_scores, nullptr, 0, nullptr,
-                                   static_cast<hipStream_t>(stream)));
+    return finish(csa::launch_topk(scores, ld, batch, T, q_pos0, N, m, k, idx, sel_scores, nullptr, 0, nullptr, 0, 0,
+                                   nullptr, static_cast<hipStream_t>(stream)));
 }
 
 size_t csa_sparse_mqa_workspace_size(int64_t batch, int64_t T, int H, int c, int k, csa_dtype t) {

@@ -157,12 +157,29 @@ __device__ __forceinline__ void load_half_row(const void* __restrict__ base, int
     for (int i = 0; i < O::kLoads; ++i) f.v[i] = p[i];
 }
 
+// Outputs of the decode-shaped kernel for the selection (each optional): per-chunk (min, max)
+// of the visible scores, a per-row region to clear, and the maximum of every group of
+// `group` consecutive visible scores at gmax + row * gld + s / group.
+struct DecodeOut {
+    float* chunk_mm;
+    uint32_t* zero;
+    int zero_words;
+    float* gmax;
+    int group;
+    int64_t gld;
+};
+
+// x of the lane that the DPP control CTRL names (all rows and banks enabled)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
 template <int DT, int MB, int TOK>
 __global__ void __launch_bounds__(256)
 index_scores_mfma(const void* __restrict__ qI, const float* __restrict__ w, const void* __restrict__ kI, int64_t batch,
                   int64_t T, int64_t q_pos0, int64_t N, int m, float* __restrict__ scores, int64_t ld,
-                  int write_invisible, int chunks, int cb, float* __restrict__ chunk_mm, uint32_t* __restrict__ zero,
-                  int zero_words) {
+                  int write_invisible, int chunks, int cb, DecodeOut dec) {
     using O = IdxOps<DT>;
     constexpr int H = 32 * MB;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -177,8 +194,8 @@ index_scores_mfma(const void* __restrict__ qI, const float* __restrict__ w, cons
     const int64_t row = b * T + t;
     const int64_t nv = visible_entries(q_pos0 + t, m, N);
     const int64_t nblk_all = (N + 31) / 32;
-    if (TOK == 1 && zero != nullptr && chunk == 0)   // clear the selection's per-row counters
-        for (int i = threadIdx.x; i < zero_words; i += 256) zero[row * zero_words + i] = 0u;
+    if (TOK == 1 && dec.zero != nullptr && chunk == 0)   // clear the selection's per-row counters
+        for (int i = threadIdx.x; i < dec.zero_words; i += 256) dec.zero[row * dec.zero_words + i] = 0u;
 
     // per-wave block list
     const int64_t blk0 = (int64_t)chunk * cb;
@@ -245,6 +262,20 @@ index_scores_mfma(const void* __restrict__ qI, const float* __restrict__ w, cons
             smin = fminf(smin, contrib);
             smax = fmaxf(smax, contrib);
         }
+        if (TOK == 1 && dec.gmax != nullptr) {
+            // maximum of each group of G consecutive visible scores (lanes n of one group)
+            float v = s < nv ? contrib : -INFINITY;
+            const int G = dec.group;
+            if (G >= 2) v = fmaxf(v, dpp_f<0xB1>(v));    // quad_perm [1,0,3,2]: lane ^ 1
+            if (G >= 4) v = fmaxf(v, dpp_f<0x4E>(v));    // quad_perm [2,3,0,1]: lane ^ 2
+            if (G >= 8) v = fmaxf(v, dpp_f<0x141>(v));   // row_half_mirror: the other quad of 8
+            if (G >= 16) v = fmaxf(v, dpp_f<0x140>(v));  // row_mirror: the other half of 16
+            if (G >= 32) {                               // lanes l and l ^ 16
+                const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+                v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+            }
+            if (g == 0 && (n & (G - 1)) == 0 && s < nv) dec.gmax[row * dec.gld + s / G] = v;
+        }
     };
     if (nb > 0) {
         typename O::Frag f0, f1, f2;
@@ -262,14 +293,14 @@ index_scores_mfma(const void* __restrict__ qI, const float* __restrict__ w, cons
         }
     }
     if constexpr (TOK == 1) {
-        if (chunk_mm != nullptr) {   // (min, max) of the chunk's visible scores for the selection
+        if (dec.chunk_mm != nullptr) {   // (min, max) of the chunk's visible scores for the selection
             __shared__ float red[2][4];
             smin = -wave_max(-smin);
             smax = wave_max(smax);
             if (lane == 0) { red[0][wid] = smin; red[1][wid] = smax; }
             __syncthreads();
             if (threadIdx.x == 0) {
-                float* o = chunk_mm + (row * chunks + chunk) * 2;
+                float* o = dec.chunk_mm + (row * chunks + chunk) * 2;
                 o[0] = fminf(fminf(red[0][0], red[0][1]), fminf(red[0][2], red[0][3]));
                 o[1] = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
             }
@@ -407,8 +438,8 @@ bool mfma_shape(int H_I, int c_I, int qk_t) {
 
 template <int DT, int MB>
 int launch_mfma(const void* qI, const float* w, const void* kI, int64_t batch, int64_t T, int64_t q_pos0, int64_t N,
-                int m, float* scores, int64_t ld, bool write_invisible, float* chunk_mm, int* n_chunk_mm,
-                uint32_t* zero, int zero_words, hipStream_t stream) {
+                int m, float* scores, int64_t ld, bool write_invisible, DecodeOut dec, int* n_chunk_mm,
+                hipStream_t stream) {
     const int64_t nblk = (N + 31) / 32;
     if (T >= 4) {
         // prefill: 8 queries per workgroup share each staged key block.  Long chunks amortise
@@ -436,9 +467,8 @@ int launch_mfma(const void* qI, const float* w, const void* kI, int64_t batch, i
         const int64_t grid = batch * T * chunks;
         if (grid > 0x7fffffffLL) return -2;
         hipLaunchKernelGGL((index_scores_mfma<DT, MB, 1>), dim3((unsigned)grid), dim3(256), 0, stream, qI, w, kI, batch,
-                           T, q_pos0, N, m, scores, ld, write_invisible ? 1 : 0, chunks, cb, chunk_mm, zero,
-                           zero_words);
-        if (n_chunk_mm) *n_chunk_mm = chunk_mm ? chunks : 0;
+                           T, q_pos0, N, m, scores, ld, write_invisible ? 1 : 0, chunks, cb, dec);
+        if (n_chunk_mm) *n_chunk_mm = dec.chunk_mm ? chunks : 0;
     }
     return 0;
 }
@@ -460,19 +490,22 @@ int index_chunks(int64_t batch, int64_t T, int64_t N, int H_I, int c_I, int qk_t
 
 int launch_index_scores(const void* qI, const float* w, const void* kI, int64_t batch, int64_t T, int64_t q_pos0,
                         int64_t N, int H_I, int c_I, int m, int qk_t, float* scores, int64_t ld, bool write_invisible,
-                        float* chunk_mm, int* n_chunk_mm, uint32_t* zero, int zero_words, hipStream_t stream) {
+                        float* chunk_mm, int* n_chunk_mm, uint32_t* zero, int zero_words, float* gmax, int G,
+                        int64_t gld, hipStream_t stream) {
     if (n_chunk_mm) *n_chunk_mm = 0;
     if (batch == 0 || T == 0 || N == 0) return 0;
+    if (gmax != nullptr && (G < 1 || G > 32 || (G & (G - 1)) != 0)) return -2;
+    const DecodeOut dec{chunk_mm, zero, zero_words, gmax, gmax ? G : 0, gld};
     if (mfma_shape(H_I, c_I, qk_t)) {
         if (qk_t == DT_FP8)
             return H_I == 64 ? launch_mfma<DT_FP8, 2>(qI, w, kI, batch, T, q_pos0, N, m, scores, ld, write_invisible,
-                                                      chunk_mm, n_chunk_mm, zero, zero_words, stream)
+                                                      dec, n_chunk_mm, stream)
                              : launch_mfma<DT_FP8, 1>(qI, w, kI, batch, T, q_pos0, N, m, scores, ld, write_invisible,
-                                                      chunk_mm, n_chunk_mm, zero, zero_words, stream);
+                                                      dec, n_chunk_mm, stream);
         return H_I == 64 ? launch_mfma<DT_BF16, 2>(qI, w, kI, batch, T, q_pos0, N, m, scores, ld, write_invisible,
-                                                   chunk_mm, n_chunk_mm, zero, zero_words, stream)
+                                                   dec, n_chunk_mm, stream)
                          : launch_mfma<DT_BF16, 1>(qI, w, kI, batch, T, q_pos0, N, m, scores, ld, write_invisible,
-                                                   chunk_mm, n_chunk_mm, zero, zero_words, stream);
+                                                   dec, n_chunk_mm, stream);
     }
     switch (qk_t) {
         case DT_F32:

@@ -19,9 +19,12 @@ int launch_compress(const void* Ca, const void* Za, const float* Ba, const void*
 // +inf / -inf); *n_chunk_mm receives the chunk count, 0 when the kernel used writes none.
 // zero / zero_words (optional): the decode-shaped kernel also zeroes zero_words uint32 per row
 // at zero + row * zero_words (the selection's per-row histogram and counters).
+// gmax / G / gld (optional, decode-shaped kernel only): the maximum of every group of G
+// consecutive visible scores of a row at gmax + row * gld + s / G (G from topk_group).
 int launch_index_scores(const void* qI, const float* w, const void* kI, int64_t batch, int64_t T, int64_t q_pos0,
                         int64_t N, int H_I, int c_I, int m, int qk_t, float* scores, int64_t ld, bool write_invisible,
-                        float* chunk_mm, int* n_chunk_mm, uint32_t* zero, int zero_words, hipStream_t stream);
+                        float* chunk_mm, int* n_chunk_mm, uint32_t* zero, int zero_words, float* gmax, int G,
+                        int64_t gld, hipStream_t stream);
 
 // Number of (min, max) pairs per row the indexer writes into chunk_mm for these sizes (0: none).
 int index_chunks(int64_t batch, int64_t T, int64_t N, int H_I, int c_I, int qk_t);
@@ -36,8 +39,15 @@ size_t topk_extra_workspace(int64_t rows, int64_t N, int k);
 // extra_ws: topk_extra_workspace(...) bytes.  With chunk_mm, few rows and long rows, the
 // multi-workgroup path runs; it expects the region topk_zero_region(...) to hold zeros for the
 // topk_zero_words(...) words of each row (the decode indexer clears it).
+// gmax / G / gld: group maxima from the indexer (NULL / 0: not available); with them the
+// group-bounded selection runs.
 int launch_topk(const float* scores, int64_t ld, int64_t batch, int64_t T, int64_t q_pos0, int64_t N, int m, int k,
-                int32_t* idx, float* sel, const float* chunk_mm, int n_chunk_mm, void* extra_ws, hipStream_t stream);
+                int32_t* idx, float* sel, const float* chunk_mm, int n_chunk_mm, const float* gmax, int G,
+                int64_t gld, void* extra_ws, hipStream_t stream);
+// Group size of the group-bounded selection for rows of up to nv_max visible entries (0: the
+// selection cannot use group maxima for these sizes).  At most 8192 groups per row.
+int topk_group(int64_t nv_max, int k);
+constexpr int64_t kTopkMaxGroups = 8192;
 int topk_zero_words(int64_t rows, int64_t nv_max);
 uint32_t* topk_zero_region(void* extra_ws, int64_t rows, int64_t N);
 

@@ -21,6 +21,8 @@
 //   D  ordered compaction: keep s iff key > K*, or key == K* and s is among the first
 //      need_eq such indices.  Each wave compacts a contiguous segment with ballots; a
 //      16-entry scan of the per-wave counts gives each segment its output offset.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -971,6 +973,443 @@ tkm_select(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_po
     }
 }
 
+// ============================================================================ group-bounded
+// Decode rows too long for LDS staging (32769 to 262144 visible entries, few queries).  The
+// indexer also writes the maximum of every group of G consecutive scores of a row (G a power
+// of two up to 32, chosen so that a row has several times k groups).  With the group maxima
+// put into 2048 bins linear in value, let b* be the highest bin that has at least k group
+// maxima in it and above.  Those k groups hold k distinct entries in bins >= b*, so the k-th
+// largest score is in a bin >= b* (binning is monotonic), and so is every entry of the row's
+// top k, whose group's maximum is then in a bin >= b* as well.  One workgroup per row:
+//   1  the group maxima into LDS, their range, the bin histogram and b*
+//   2  candidates: the entries in bins >= b* of the groups whose maximum is in a bin >= b*
+//      (about k of them for scores without heavy ties), loaded with 16-byte reads
+//   3  K* = the exact k-th largest candidate key (radix select from the highest bit where the
+//      candidates differ), and how many candidates equal to K* belong to the top k (need_eq);
+//      every entry equal to K* is a candidate
+//   4  bitmaps over the row: kept (key > K*) and ties (key == K*); the first need_eq ties in
+//      index order join the kept ones, and each kept candidate goes to its rank in index order
+// More than kGCap candidates (heavy ties) or too few groups: steps 3-4 run over the whole row,
+// read from global memory.
+constexpr int kGThreads = 1024;
+constexpr int kGWaves = kGThreads / kWave;
+constexpr int kGMaxGroups = 8192;    // group maxima per row, staged in LDS
+static_assert(kGMaxGroups == kTopkMaxGroups, "group region size");
+constexpr int kGMaxRow = 262144;     // visible entries per row: bitmaps of 32 KB
+constexpr int kGCap = 4096;          // candidates per row
+constexpr int kGMaxG = 32;           // groups never cross the indexer's 32-entry blocks
+
+constexpr int kGBins = 2048;         // linear bins over the group maxima
+
+struct GroupShared {
+    uint32_t a[kGMaxRow / 32];   // group maxima (fp32 bits), then the tie bitmap, then word offsets
+    uint32_t b[kGMaxRow / 32];   // indices of the selected groups, then the kept bitmap
+    uint32_t ckey[kGCap];
+    int32_t cidx[kGCap];
+    uint32_t hist[256];
+    uint32_t ghist[kGBins];
+    float flo, fhi;
+    int bstar;
+    uint32_t scan[kGWaves + 2];
+    uint32_t red_lo[kGWaves], red_hi[kGWaves];
+    uint32_t prefix, pmask, rem;
+    uint32_t ngroups, ncand;
+};
+static_assert(kGMaxRow / 32 >= kGMaxGroups, "group keys share the tie bitmap");
+
+// Block-wide min and max of the per-thread values lo / hi (every thread gets both).
+__device__ __forceinline__ void block_minmax(uint32_t& lo, uint32_t& hi, GroupShared& sh) {
+    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+        lo = min(lo, (uint32_t)__shfl_xor((int)lo, off, kWave));
+        hi = max(hi, (uint32_t)__shfl_xor((int)hi, off, kWave));
+    }
+    if (lane == 0) {
+        sh.red_lo[wid] = lo;
+        sh.red_hi[wid] = hi;
+    }
+    __syncthreads();
+    lo = sh.red_lo[0];
+    hi = sh.red_hi[0];
+#pragma unroll
+    for (int w = 1; w < kGWaves; ++w) {
+        lo = min(lo, sh.red_lo[w]);
+        hi = max(hi, sh.red_hi[w]);
+    }
+    __syncthreads();   // read by all before the next use
+}
+
+// Exact k-th largest (k >= 1) of the keys key_at(i), i < n (n >= k), all within [kmin, kmax]:
+// the bits above the highest bit where kmin and kmax differ are common to every key; the
+// rest is resolved in passes over 8-bit digits from the top, each narrowing to the keys that
+// share the digits found so far.  (Starting at the first varying bit spreads the histogram:
+// scores of similar size share their sign and exponent bits.)
+// Returns K*; *need_eq receives how many keys equal to K* belong to the k largest.
+template <class F>
+__device__ uint32_t radix_kth(F key_at, int64_t n, uint32_t k, uint32_t kmin, uint32_t kmax, GroupShared& sh,
+                              uint32_t* need_eq) {
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const uint32_t diff = kmin ^ kmax;
+    int hb = diff == 0u ? 0 : 32 - __clz(diff);   // bits [0, hb) vary
+    const uint32_t low = hb == 32 ? ~0u : (1u << hb) - 1u;
+    if (tid == 0) {
+        sh.prefix = kmin & ~low;
+        sh.pmask = ~low;
+        sh.rem = k;
+    }
+    while (hb > 0) {
+        const int wd = hb < 8 ? hb : 8, shift = hb - wd;
+        const uint32_t dmask = (1u << wd) - 1u;
+        for (int i = tid; i < 256; i += kGThreads) sh.hist[i] = 0u;
+        __syncthreads();   // also publishes the previous pass's prefix
+        const uint32_t prefix = sh.prefix, pmask = sh.pmask;
+        for (int64_t i = tid; i < n; i += kGThreads) {
+            const uint32_t key = key_at(i);
+            if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
+        }
+        __syncthreads();
+        if (tid < kWave) {
+            // lane l holds digits 255-4l .. 252-4l (descending); inclusive scan from the top
+            uint32_t c[4], mine = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                c[j] = sh.hist[255 - 4 * lane - j];
+                mine += c[j];
+            }
+            uint32_t inc = mine;
+#pragma unroll
+            for (int off = 1; off < kWave; off <<= 1) {
+                const uint32_t y = __shfl_up(inc, off, kWave);
+                if (lane >= off) inc += y;
+            }
+            const uint32_t rem = sh.rem, before = inc - mine;
+            if (before < rem && inc >= rem) {   // exactly one lane
+                uint32_t acc = before;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (acc + c[j] >= rem) {
+                        sh.prefix = prefix | ((uint32_t)(255 - 4 * lane - j) << shift);
+                        sh.pmask = pmask | (dmask << shift);
+                        sh.rem = rem - acc;
+                        break;
+                    }
+                    acc += c[j];
+                }
+            }
+        }
+        __syncthreads();   // the search is done before the histogram is cleared again
+        hb = shift;
+    }
+    __syncthreads();
+    const uint32_t kth = sh.prefix, rem = sh.rem;
+    __syncthreads();   // every thread has read them before a later call rewrites them
+    *need_eq = rem;
+    return kth;
+}
+
+// inverse of order_key (-0 comes back as +0)
+__device__ __forceinline__ float key_value(uint32_t key) {
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+// Appends the lanes with `take` to a list: one LDS atomic per wave; returns this lane's slot.
+__device__ __forceinline__ uint32_t wave_append(bool take, uint32_t* counter) {
+    const unsigned long long m = __ballot(take);
+    const int lane = threadIdx.x & (kWave - 1);
+    uint32_t base = 0;
+    if (lane == 0 && m != 0ull) base = atomicAdd(counter, (uint32_t)__popcll(m));
+    base = __shfl(base, 0, kWave);
+    return base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
+}
+
+// the first n set bits of w (n < popcount(w))
+__device__ __forceinline__ uint32_t first_bits(uint32_t w, uint32_t n) {
+    uint32_t r = 0u;
+    for (; n > 0; --n) {
+        r |= w & (0u - w);
+        w &= w - 1u;
+    }
+    return r;
+}
+
+__global__ void __launch_bounds__(kGThreads)
+topk_groups(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_pos0, int64_t N, int m, int k,
+            const float* __restrict__ gmax, int64_t gld, int G, int32_t* __restrict__ idx, float* __restrict__ sel) {
+    __shared__ GroupShared sh;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+    const int64_t row = blockIdx.x;
+    const int64_t nv = visible_entries(q_pos0 + row % T, m, N);
+    const float* sc = scores + row * ld;
+    int32_t* oi = idx + row * k;
+    float* os = sel ? sel + row * k : nullptr;
+    if (nv <= k) {
+        for (int r = tid; r < k; r += kGThreads) {
+            oi[r] = r < nv ? r : -1;
+            if (os) os[r] = r < nv ? sc[r] : -INFINITY;
+        }
+        return;
+    }
+    // (the launcher sends rows of at most kGMaxRow entries and at most kGMaxGroups groups)
+    const int64_t ng = (nv + G - 1) / G;
+    bool full = ng <= k;
+    uint32_t kstar = 0u, need_eq = 0u;
+    int64_t ncand = 0;
+    if (!full) {
+        // group maxima into LDS (all loads in flight together) and their range
+        const float* gm = gmax + row * gld;
+        float* gv = reinterpret_cast<float*>(sh.a);
+        constexpr int kPer = kGMaxGroups / kGThreads;
+        float v[kPer];
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int64_t j = tid + (int64_t)u * kGThreads;
+            v[u] = j < ng ? gm[j] : -INFINITY;
+        }
+        float flo = INFINITY, fhi = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int64_t j = tid + (int64_t)u * kGThreads;
+            if (j < ng) {
+                gv[j] = v[u];
+                flo = fminf(flo, v[u]);
+                fhi = fmaxf(fhi, v[u]);
+            }
+        }
+        for (int i2 = tid; i2 < kGBins; i2 += kGThreads) sh.ghist[i2] = 0u;
+        if (tid == 0) {
+            sh.ngroups = 0u;
+            sh.ncand = 0u;
+        }
+        uint32_t klo = order_key(flo), khi = order_key(fhi);
+        block_minmax(klo, khi, sh);   // its barriers also publish the maxima and the cleared bins
+        flo = key_value(klo);
+        fhi = key_value(khi);
+        float inv = (float)kGBins / (fhi - flo);
+        if (!(fhi > flo) || !isfinite(inv)) inv = 0.f;
+        // b*: the highest linear bin with at least k group maxima in it and above.  Every
+        // group in a bin >= b* has an entry in a bin >= b*, so the row's top k are among the
+        // entries in bins >= b* of those groups.
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int64_t j = tid + (int64_t)u * kGThreads;
+            if (j < ng) atomicAdd(&sh.ghist[bin_of_n<kGBins>(v[u], flo, inv)], 1u);
+        }
+        __syncthreads();
+        {
+            static_assert(kGBins == 2 * kGThreads, "two bins per thread");
+            const int top = kGBins - 1 - 2 * tid;
+            const uint32_t h0 = sh.ghist[top], h1 = sh.ghist[top - 1];
+            uint32_t total;
+            const uint32_t before = block_excl_scan<kGWaves>(h0 + h1, sh.scan, &total);
+            if (before < (uint32_t)k && before + h0 + h1 >= (uint32_t)k) sh.bstar = before + h0 >= (uint32_t)k ? top : top - 1;
+        }
+        __syncthreads();
+        const int bstar = sh.bstar;
+        // the selected groups (every lane of a wave runs the same trip count)
+        for (int64_t j0 = 0; j0 < ng; j0 += kGThreads) {
+            const int64_t j = j0 + tid;
+            const bool take = j < ng && bin_of_n<kGBins>(gv[j], flo, inv) >= bstar;
+            const uint32_t p = wave_append(take, &sh.ngroups);
+            if (take) sh.b[p] = (uint32_t)j;
+        }
+        __syncthreads();
+        const int64_t nsel = sh.ngroups;
+        // candidates: their entries in bins >= b*, loaded 8 at a time per thread (16-byte loads
+        // for groups of 4 or more); a thread's takes form a bit mask, and one wave-wide scan of
+        // the per-lane counts places them
+        uint32_t lo = ~0u, hi = 0u;
+        // (NX values per thread, PER consecutive entries from each ebase; static indexing keeps
+        // the arrays in registers)
+        auto append = [&](uint32_t mask, const int64_t* ebase, const float* xs, auto nx_tag, auto per_tag) {
+            constexpr int NX = decltype(nx_tag)::value, PER = decltype(per_tag)::value;
+            const uint32_t c = __popc(mask);
+            uint32_t inc = c;
+#pragma unroll
+            for (int off = 1; off < kWave; off <<= 1) {
+                const uint32_t y = __shfl_up(inc, off, kWave);
+                if (lane >= off) inc += y;
+            }
+            const uint32_t wtot = __shfl(inc, kWave - 1, kWave);
+            uint32_t base = 0;
+            if (lane == kWave - 1 && wtot) base = atomicAdd(&sh.ncand, wtot);
+            base = __shfl(base, kWave - 1, kWave) + inc - c;
+#pragma unroll
+            for (int bit = 0; bit < NX; ++bit) {
+                if ((mask >> bit) & 1u) {
+                    const int64_t e = ebase[bit / PER] + bit % PER;
+                    const uint32_t key = order_key(xs[bit]);
+                    lo = min(lo, key);
+                    hi = max(hi, key);
+                    if (base < (uint32_t)kGCap) {
+                        sh.ckey[base] = key;
+                        sh.cidx[base] = (int32_t)e;
+                    }
+                    ++base;
+                }
+            }
+        };
+        auto in_b = [&](int64_t e, float x) { return e < nv && bin_of_n<kGBins>(x, flo, inv) >= bstar; };
+        if (G >= 4) {
+            const int lq = __builtin_ctz((unsigned)G) - 2;   // 16-byte pieces per group: 1 << lq
+            const int64_t nq = nsel << lq;
+            for (int64_t q0 = 0; q0 < nq; q0 += 8 * kGThreads) {
+                float xs[32];
+                int64_t e0[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int64_t q = q0 + tid + (int64_t)u * kGThreads;
+                    e0[u] = q < nq ? ((int64_t)sh.b[q >> lq] << (lq + 2)) + ((q & ((1 << lq) - 1)) << 2) : -1;
+                    if (e0[u] >= nv) e0[u] = -1;   // wholly past the row (a piece that starts below
+                                                   // nv <= N ends inside the row's ld >= N, ld % 4 == 0)
+                    const float4 x4 = e0[u] >= 0 ? *reinterpret_cast<const float4*>(sc + e0[u]) : make_float4(0.f, 0.f, 0.f, 0.f);
+                    xs[4 * u] = x4.x;
+                    xs[4 * u + 1] = x4.y;
+                    xs[4 * u + 2] = x4.z;
+                    xs[4 * u + 3] = x4.w;
+                }
+                uint32_t mask = 0u;
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        if (e0[u] >= 0 && in_b(e0[u] + c, xs[4 * u + c])) mask |= 1u << (4 * u + c);
+                append(mask, e0, xs, std::integral_constant<int, 32>{}, std::integral_constant<int, 4>{});
+            }
+        } else {
+            const int lg = __builtin_ctz((unsigned)G);
+            const int64_t ne = nsel << lg;
+            for (int64_t i0 = 0; i0 < ne; i0 += 8 * kGThreads) {
+                float xs[8];
+                int64_t e[8];
+                uint32_t mask = 0u;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int64_t i2 = i0 + tid + (int64_t)u * kGThreads;
+                    e[u] = i2 < ne ? ((int64_t)sh.b[i2 >> lg] << lg) + (i2 & (G - 1)) : -1;
+                    xs[u] = e[u] >= 0 && e[u] < nv ? sc[e[u]] : 0.f;
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (e[u] >= 0 && in_b(e[u], xs[u])) mask |= 1u << u;
+                append(mask, e, xs, std::integral_constant<int, 8>{}, std::integral_constant<int, 1>{});
+            }
+        }
+        block_minmax(lo, hi, sh);   // (its barrier also publishes the candidates)
+        ncand = sh.ncand;
+        if (ncand > kGCap || ncand < k) full = true;   // heavy ties at b* (the second cannot happen)
+        else kstar = radix_kth([&](int64_t i2) { return sh.ckey[i2]; }, ncand, (uint32_t)k, lo, hi, sh, &need_eq);
+    }
+    if (full) {
+        uint32_t lo = ~0u, hi = 0u;
+        for (int64_t e = tid; e < nv; e += kGThreads) {
+            const uint32_t key = order_key(sc[e]);
+            lo = min(lo, key);
+            hi = max(hi, key);
+        }
+        block_minmax(lo, hi, sh);
+        kstar = radix_kth([&](int64_t e) { return order_key(sc[e]); }, nv, (uint32_t)k, lo, hi, sh, &need_eq);
+    }
+
+    // bitmaps: kept (key > K*) in b, ties (key == K*) in a
+    const int64_t nwords = (nv + 31) >> 5;
+    for (int64_t w = tid; w < nwords; w += kGThreads) {
+        sh.a[w] = 0u;
+        sh.b[w] = 0u;
+    }
+    __syncthreads();
+    if (!full) {
+        for (int64_t i = tid; i < ncand; i += kGThreads) {
+            const uint32_t key = sh.ckey[i];
+            const int32_t e = sh.cidx[i];
+            if (key > kstar) atomicOr(&sh.b[e >> 5], 1u << (e & 31));
+            else if (key == kstar) atomicOr(&sh.a[e >> 5], 1u << (e & 31));
+        }
+    } else {
+        // one ballot per 64 entries gives two words of each bitmap
+        for (int64_t b0 = (int64_t)wid * kWave; b0 < nv; b0 += kGThreads) {
+            const int64_t e = b0 + lane;
+            const bool ok = e < nv;
+            const uint32_t key = ok ? order_key(sc[e]) : 0u;
+            const unsigned long long gt = __ballot(ok && key > kstar);
+            const unsigned long long eq = __ballot(ok && key == kstar);
+            if (lane == 0) {
+                sh.b[b0 >> 5] = (uint32_t)gt;
+                sh.a[b0 >> 5] = (uint32_t)eq;
+                if ((b0 >> 5) + 1 < nwords) {
+                    sh.b[(b0 >> 5) + 1] = (uint32_t)(gt >> 32);
+                    sh.a[(b0 >> 5) + 1] = (uint32_t)(eq >> 32);
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ordered extraction: each thread owns a run of words; the ties ahead of its run decide
+    // how many of its own ties it keeps
+    const int64_t per = (nwords + kGThreads - 1) / kGThreads;
+    const int64_t w0 = (int64_t)tid * per, w1 = min(nwords, w0 + per);
+    uint32_t ceq = 0;
+    for (int64_t w = w0; w < w1; ++w) ceq += __popc(sh.a[w]);
+    uint32_t total;
+    uint32_t taken = block_excl_scan<kGWaves>(ceq, sh.scan, &total);
+    uint32_t cnt = 0;
+    for (int64_t w = w0; w < w1; ++w) {
+        uint32_t eqw = sh.a[w];
+        if (taken >= need_eq) eqw = 0u;
+        else if (taken + __popc(eqw) > need_eq) eqw = first_bits(eqw, need_eq - taken);
+        taken += __popc(sh.a[w]);
+        const uint32_t kw = sh.b[w] | eqw;
+        sh.b[w] = kw;   // this thread's words only
+        cnt += __popc(kw);
+    }
+    uint32_t pos = block_excl_scan<kGWaves>(cnt, sh.scan, &total);
+    if (!full) {
+        // every kept entry is a candidate: its slot is the kept count before its word plus
+        // the kept bits below it in the word; its score comes back from its key
+        for (int64_t w = w0; w < w1; ++w) {
+            sh.a[w] = pos;
+            pos += __popc(sh.b[w]);
+        }
+        __syncthreads();
+        for (int64_t i2 = tid; i2 < ncand; i2 += kGThreads) {
+            const int32_t e = sh.cidx[i2];
+            const uint32_t word = sh.b[e >> 5], bit = 1u << (e & 31);
+            if (word & bit) {
+                const uint32_t slot = sh.a[e >> 5] + __popc(word & (bit - 1u));
+                oi[slot] = e;
+                if (os) os[slot] = key_value(sh.ckey[i2]);
+            }
+        }
+        return;
+    }
+    for (int64_t w = w0; w < w1; ++w) {
+        uint32_t word = sh.b[w];
+        while (word) {
+            const int bit = __ffs(word) - 1;
+            word &= word - 1;
+            const int64_t e = (w << 5) + bit;
+            if (pos < (uint32_t)k) {
+                oi[pos] = (int32_t)e;
+                if (os) os[pos] = sc[e];
+            }
+            ++pos;
+        }
+    }
+}
+
+// Group size for the group-bounded selection (0: not used): a power of two up to kGMaxG with
+// at most kGMaxGroups groups in the longest row, and preferably at least 4k of them.
+// Rows that fit the LDS staging of the one-workgroup bitmap selection are faster there.
+int group_size(int64_t nv_max, int k) {
+    if (nv_max > kGMaxRow || nv_max <= k || nv_max <= kRowLds) return 0;
+    int g = 1;
+    while ((nv_max + g - 1) / g > kGMaxGroups) g *= 2;
+    while (g < kGMaxG && nv_max / (2 * g) >= 4 * (int64_t)k) g *= 2;
+    if (g > kGMaxG || (nv_max + g - 1) / g <= k) return 0;
+    return g;
+}
+
 // rows that fit the LDS staging are faster in one workgroup (no inter-kernel round trips)
 bool multi_rows(int64_t rows, int64_t nv_max) { return rows < 256 && nv_max > kRowLds; }
 
@@ -984,14 +1423,22 @@ size_t topk_extra_workspace(int64_t rows, int64_t N, int k) {
 
 int topk_zero_words(int64_t rows, int64_t nv_max) { return multi_rows(rows, nv_max) ? kZeroWords : 0; }
 
+int topk_group(int64_t nv_max, int k) { return group_size(nv_max, k); }
+
 int launch_topk(const float* scores, int64_t ld, int64_t batch, int64_t T, int64_t q_pos0, int64_t N, int m, int k,
-                int32_t* idx, float* sel, const float* chunk_mm, int n_chunk_mm, void* extra_ws, hipStream_t stream) {
+                int32_t* idx, float* sel, const float* chunk_mm, int n_chunk_mm, const float* gmax, int G,
+                int64_t gld, void* extra_ws, hipStream_t stream) {
     const int64_t rows = batch * T;
     if (rows == 0) return 0;
     if (rows > 0x7fffffffLL) return -2;
     // the longest visible row is that of the last query
     int64_t nv_max = (q_pos0 + T) / m;
     if (nv_max > N) nv_max = N;
+    if (gmax != nullptr && G > 0) {   // the indexer wrote the group maxima (G = topk_group)
+        hipLaunchKernelGGL(topk_groups, dim3((unsigned)rows), dim3(kGThreads), 0, stream, scores, ld, T, q_pos0, N, m,
+                           k, gmax, gld, G, idx, sel);
+        return 0;
+    }
     if (chunk_mm != nullptr && extra_ws != nullptr && multi_rows(rows, nv_max)) {
         // the indexer zeroed the per-row histogram / counter region (topk_zero_words)
         MultiWs L;

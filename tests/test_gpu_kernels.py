@@ -147,18 +147,25 @@ def test_topk_bit_exact_with_exact_scores(case):
     assert np.array_equal(sel, ref_sel.astype(np.float32).astype(np.float64))
 
 
-MULTI_TOPK_CASES = [  # batch, T, q_pos0, N, k, levels, zero-key fraction: rows over 32K entries
+DECODE_TOPK_CASES = [  # batch, T, q_pos0, N, k, levels, zero-key fraction
     (2, 1, 4 * 40000, 40000, 1024, 4, 0.0),
     (1, 3, 4 * 70000 - 6, 70000, 2048, 2, 0.0),   # rows of different lengths; ~150-way tie at the cut
     (1, 2, 4 * 50000, 50000, 1024, 3, 0.99),      # the cut falls in a tie of ~49K zero scores
     (1, 1, 4 * 36000, 36000, 512, 1, 0.0),        # every score equal
+    (3, 1, 4 * 5000, 5000, 1024, 4, 0.0),         # groups of one score
+    (2, 2, 4 * 20000 - 5, 20000, 1024, 3, 0.0),   # groups of four
+    (1, 3, 4 * 100000 - 3, 100000, 2048, 6, 0.0),
+    (1, 1, 4 * 262144, 262144, 1024, 8, 0.0),     # the longest row the group maxima serve
+    (1, 1, 4 * 300000, 300000, 1024, 8, 0.0),     # longer: the multi-workgroup selection
 ]
 
 
-@pytest.mark.parametrize("case", MULTI_TOPK_CASES, ids=lambda c: "b%d_T%d_p%d_N%d_k%d_l%d_z%g" % c)
-def test_topk_multi_workgroup_bit_exact(case):
-    # few long rows with the decode indexer's per-chunk ranges take the selection that splits
-    # each row over several workgroups; integer-valued fp8 inputs keep every score exact
+@pytest.mark.parametrize("case", DECODE_TOPK_CASES, ids=lambda c: "b%d_T%d_p%d_N%d_k%d_l%d_z%g" % c)
+def test_topk_decode_shapes_bit_exact(case):
+    # decode-shaped calls (fp8 indexer, T < 4): rows that fit LDS take the one-workgroup
+    # bitmap selection, longer ones up to 262144 entries the indexer's group maxima, longer
+    # still per-chunk ranges and several workgroups per row; integer-valued fp8 inputs keep
+    # every score exact
     batch, T, p0, N, k, levels, zfrac = case
     H, cI, m = 64, 128, 4
     say(f"csa_index_topk multi-workgroup case {case}")
