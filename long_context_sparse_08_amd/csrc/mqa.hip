@@ -580,6 +580,304 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     }
 }
 
+// Warp-specialised sparse MQA for launches of at most one workgroup per CU (decode).  With one
+// 4-wave workgroup per CU each SIMD runs a single wave, which idles the matrix core through
+// every LDS wait, softmax and barrier (a phase trace gave ~3600 cycles per 32-key block for
+// ~1100 cycles of MFMA issue).  Here a workgroup has 8 waves, two per SIMD, in two roles:
+//   waves 0-3 (score waves, 16 heads each): gather the key blocks, S^T = KV.Q^T, the online
+//     softmax, and publish block j's bf16 P tiles and rescale factors (parity j % 2)
+//   waves 4-7 (value waves, 128 output columns each over the 64 heads): rescale and add
+//     V^T.P^T of block j-1 while the score waves work on block j
+// One workgroup barrier per block; four staging buffers hold blocks j-1 (value waves), j
+// (score waves), and j+1, j+2 (loading).  The same swizzled LDS rows as the four-stage kernel.
+constexpr int kWsWaves = 8;
+
+__global__ void __launch_bounds__(kWsWaves * kWave, 1)
+mqa_sparse_ws(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
+              int64_t rows, int64_t T, int64_t N, int H, int k, int ks_count, int keys_per_split, float sl2,
+              uint16_t* __restrict__ out, uint16_t* __restrict__ part, float* __restrict__ part_ml) {
+    constexpr int kPitch = kMPitch<true>, kBuf = kMBuf<true>;
+    __shared__ __attribute__((aligned(16))) uint8_t stage_a[kBuf];
+    __shared__ __attribute__((aligned(16))) uint8_t stage_b[kBuf];
+    __shared__ __attribute__((aligned(16))) uint8_t stage_c[kBuf];
+    __shared__ __attribute__((aligned(16))) uint8_t stage_d[kBuf];
+    __shared__ int32_t ids[kMIdsLds];
+    __shared__ uint32_t vmask[kMIdsLds / 32];
+    __shared__ uint4 xpp[2][kMHT][kWave];     // P tiles of block j (B-operand lane layout), parity j % 2
+    __shared__ float xalpha[2][kMHT][16];     // rescale factor of each head at block j
+    __shared__ __attribute__((aligned(16))) int xflag[2][kMHT];   // head tile rescaled at block j
+    __shared__ float xm[kMHT][16], xl[kMHT][16];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool score = wid < kMHT;             // the role is wave-uniform
+    const int tw = wid & (kMHT - 1);           // head tile (score) / column group (value)
+    const int g = lane >> 4, n16 = lane & 15;
+    const int HG = H / kMHeadsWG;
+    // XCD-aware order: consecutive units of a row go to one XCD (workgroups are dealt
+    // round-robin over the 8 XCDs), so they share that XCD's L2 for the row's KV.
+    const int64_t x = blockIdx.x;
+    const int64_t per_row = (int64_t)HG * ks_count;
+    const int64_t slot = x / 8, xcd = x % 8;
+    const int64_t row = (slot / per_row) * 8 + xcd;
+    const int64_t rem = slot % per_row;
+    const int hg = (int)(rem / ks_count), ks = (int)(rem % ks_count);
+    if (row >= rows) return;
+    const int64_t b = row / T;
+    const int key0 = ks * keys_per_split;
+    const int nkeys = (int)max((int64_t)0, min((int64_t)k, (int64_t)key0 + keys_per_split) - key0);
+    const int h0 = hg * kMHeadsWG;
+    const int n_ent = (int)N;
+    auto key_id = [&](int i) -> int { return i < nkeys ? ids[i] : 0; };
+
+    // key ids (sanitised, with a validity bit per slot)
+    constexpr int kIdsPerThread = kMIdsLds / (kWsWaves * kWave);
+    int idv[kIdsPerThread];
+#pragma unroll
+    for (int u = 0; u < kIdsPerThread; ++u) {
+        const int i = tid + u * kWsWaves * kWave;
+        idv[u] = i < nkeys ? idx[row * k + key0 + i] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kIdsPerThread; ++u) {
+        const int i = tid + u * kWsWaves * kWave;
+        const bool ok = i < nkeys && (uint32_t)idv[u] < (uint32_t)n_ent;
+        if (i < nkeys) ids[i] = ok ? idv[u] : 0;
+        const unsigned long long bits = __ballot(ok);
+        if (lane == 0) {
+            const int w = (u * kWsWaves * kWave + kWave * wid) / 32;
+            vmask[w] = (uint32_t)bits;
+            vmask[w + 1] = (uint32_t)(bits >> 32);
+        }
+    }
+    __syncthreads();
+
+    const int nblk = (nkeys + kMBlk - 1) / kMBlk;
+    const uint8_t* kvbytes = reinterpret_cast<const uint8_t*>(kv + b * N * (int64_t)kMC);
+    // this sequence's KV rows (N <= kMMaxEntries, checked at launch); loads past them read 0
+    const __amdgpu_buffer_rsrc_t kvres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(kvbytes), (short)0, (int)(uint32_t)(N * 2 * kMC), 0x00020000);
+
+    // Each role keeps its state inside its own branch (the barriers of the two branches pair
+    // up one to one), so the score waves' q and the value waves' accumulators never share
+    // registers' live ranges.
+    if (score) {
+        float m_run = -INFINITY, l_run = 0.f;   // head 16*tw + n16
+        // this wave's q (head tile tw) as the B operand of S^T: head n16, channels 32*s + 8*g .. +8
+        bf16x8_t qb[kMC / 32];
+        const uint16_t* qrow = q + ((row * H) + h0 + 16 * tw + n16) * (int64_t)kMC + 8 * g;
+#pragma unroll
+        for (int s = 0; s < kMC / 32; ++s) qb[s] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * s);
+        // block `blk` into `dst`: this wave's 8 rows, ids in one LDS round trip; blocks past the
+        // range load entry 0 (a gather is issued every step: one wait count fits every step)
+        auto gather = [&](int blk, uint8_t* dst) {
+            const int myid = lane < kMLoadsPerBlk ? key_id(blk * kMBlk + kMLoadsPerBlk * tw + lane) : 0;
+#pragma unroll
+            for (int r8 = 0; r8 < kMLoadsPerBlk; ++r8) {
+                const int r = kMLoadsPerBlk * tw + r8;
+                const int sidx = __builtin_amdgcn_readlane(myid, r8);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(kvres, (lds_void_ptr)(dst + r * kPitch), 16,
+                                                         16u * (lane ^ swz(r)), (uint32_t)sidx * (2 * kMC), 0, 0);
+            }
+        };
+        int aoff[4];
+#pragma unroll
+        for (int b4 = 0; b4 < 4; ++b4) aoff[b4] = 16 * ((4 * b4 + g) ^ swz(n16));
+        // scores, softmax and P of block blk (parity par) from `st`
+        auto s_phase = [&](int blk, const uint8_t* st, int par) {
+            const uint32_t vg = vmask[blk] >> (4 * g);
+            constexpr int kSD = 8;
+            f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+            const uint8_t* arow = st + n16 * kPitch;
+            auto lda = [&](int s, int h) {
+                return *reinterpret_cast<const bf16x8_t*>(arow + 16 * kPitch * h + 256 * (s >> 2) + aoff[s & 3]);
+            };
+            bf16x8_t ra[kSD][2];
+#pragma unroll
+            for (int j = 0; j < kSD; ++j) {
+                ra[j][0] = lda(j, 0);
+                ra[j][1] = lda(j, 1);
+            }
+#pragma unroll
+            for (int s = 0; s < kMC / 32; ++s) {
+                sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[s % kSD][0], qb[s], sacc[0], 0, 0, 0);
+                sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[s % kSD][1], qb[s], sacc[1], 0, 0, 0);
+                if (s + kSD < kMC / 32) {
+                    ra[s % kSD][0] = lda(s + kSD, 0);
+                    ra[s % kSD][1] = lda(s + kSD, 1);
+                }
+            }
+            // online softmax for head 16*tw + n16 (values of lane: keys 16*hb + 4g + i)
+            float p[8];
+            float bmax = -INFINITY;
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float v = ((vg >> (16 * hb + i)) & 1u) ? sacc[hb][i] * sl2 : -INFINITY;
+                    p[4 * hb + i] = v;
+                    bmax = fmaxf(bmax, v);
+                }
+            bmax = max_xor32(max_xor16(bmax));
+            // lazy rescale (see mqa_sparse_mfma): the reference max moves only when a logit
+            // exceeds it by more than 2^8, decided for the whole wave
+            const bool resc = __any(bmax > m_run + 8.f);
+            if (resc) {
+                const float m_new = fmaxf(m_run, bmax);
+                const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+                l_run *= alpha;
+                m_run = m_new;
+                if (g == 0) xalpha[par][tw][n16] = alpha;
+            }
+            const float m_ref = m_run == -INFINITY ? 0.f : m_run;
+            float psum = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                p[e] = __builtin_amdgcn_exp2f(p[e] - m_ref);
+                psum += p[e];
+            }
+            l_run += psum;
+            uint4 pw;
+            pw.x = pack_bf16x2(p[0], p[1]);
+            pw.y = pack_bf16x2(p[2], p[3]);
+            pw.z = pack_bf16x2(p[4], p[5]);
+            pw.w = pack_bf16x2(p[6], p[7]);
+            xpp[par][tw][lane] = pw;
+            if (lane == 0) xflag[par][tw] = resc ? 1 : 0;
+        };
+        // blocks 0 and 1 in flight; block 0 staged before the first barrier
+        gather(0, stage_a);
+        gather(1, stage_b);
+        wait_vmcnt<kMLoadsPerBlk>();
+        // step j < nblk: barrier j, gather block j+2 into the buffer block j-2 used (its
+        // scores, then its values, are done by now), scores of block j, then wait until block
+        // j+1 is staged; every step issues the same loads (no data-dependent branch inside)
+        auto step = [&](int j, const uint8_t* cur, uint8_t* nxt) {
+            lds_barrier();
+            gather(j + 2, nxt);
+            asm volatile("" ::: "memory");   // the gather is issued before the block's reads
+            s_phase(j, cur, j & 1);
+            wait_vmcnt<kMLoadsPerBlk>();
+        };
+        for (int j = 0; j < nblk; j += 4) {
+            step(j, stage_a, stage_c);
+            if (j + 1 >= nblk) break;
+            step(j + 1, stage_b, stage_d);
+            if (j + 2 >= nblk) break;
+            step(j + 2, stage_c, stage_a);
+            if (j + 3 >= nblk) break;
+            step(j + 3, stage_d, stage_b);
+        }
+        lds_barrier();     // barrier nblk: the value waves take the last block
+        wait_vmcnt<0>();   // the loads past the last block, before the buffers are reused
+        l_run = sum_xor32(sum_xor16(l_run));
+        if (g == 0) {
+            xm[tw][n16] = m_run;
+            xl[tw][n16] = l_run;
+            if (part != nullptr) {
+                const int64_t prow = (row * ks_count + ks) * H + h0 + 16 * tw + n16;
+                part_ml[2 * prow] = m_run;
+                part_ml[2 * prow + 1] = l_run;
+            }
+        }
+        __syncthreads();   // pairs with the value waves' barrier after their last block
+        __syncthreads();   // pairs with the value waves' barrier after the staging
+    } else {
+        f32x4 acc[kMHT][kMColBlkW];   // columns 128*tw + 16*cb + 4*g + i, head 16*ht + n16
+#pragma unroll
+        for (int ht = 0; ht < kMHT; ++ht)
+#pragma unroll
+            for (int cb = 0; cb < kMColBlkW; ++cb) acc[ht][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // P.V of block blk (parity par) from `st`
+        auto pv_phase = [&](const uint8_t* st, int par) {
+            bf16x8_t pb[kMHT];
+#pragma unroll
+            for (int ht = 0; ht < kMHT; ++ht) pb[ht] = __builtin_bit_cast(bf16x8_t, xpp[par][ht][lane]);
+            const int4 fl = *reinterpret_cast<const int4*>(xflag[par]);
+            const int flags[kMHT] = {fl.x, fl.y, fl.z, fl.w};
+#pragma unroll
+            for (int ht = 0; ht < kMHT; ++ht) {
+                if (__builtin_amdgcn_readfirstlane(flags[ht])) {
+                    const float a = xalpha[par][ht][n16];
+#pragma unroll
+                    for (int cb = 0; cb < kMColBlkW; ++cb) acc[ht][cb] = acc[ht][cb] * a;
+                }
+            }
+            constexpr int kVD = 4;
+            const int vr = 4 * g + (n16 >> 2), vs = swz(vr);
+            const int vofs = vr * kPitch + 256 * tw + 32 * (vs >> 1) + 16 * (((n16 & 3) >> 1) ^ (vs & 1)) + 8 * (n16 & 1);
+            // the buffer's LDS address as a wave-uniform value the compiler does not fold into
+            // per-buffer address registers (the value waves issue no loads into LDS, so nothing
+            // needs to tell the buffers apart here)
+            typedef __attribute__((address_space(3))) uint8_t lds_u8;
+            uint32_t sbase = (uint32_t)(uintptr_t)(const lds_u8*)st;
+            asm("" : "+s"(sbase));   // opaque: kept in a scalar register, not folded per buffer
+            auto ldv = [&](int cb) {
+                typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+                const uint32_t va_ = sbase + (uint32_t)(vofs ^ (32 * cb));
+                const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)va_);
+                const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(va_ + 16 * kPitch));
+                typedef short i16x8 __attribute__((ext_vector_type(8)));
+                const i16x8 va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+                return __builtin_bit_cast(bf16x8_t, va);
+            };
+            bf16x8_t rv[kVD];
+#pragma unroll
+            for (int j = 0; j < kVD; ++j) rv[j] = ldv(j);
+#pragma unroll
+            for (int cb = 0; cb < kMColBlkW; ++cb) {
+                const bf16x8_t vb = rv[cb % kVD];
+                if (cb + kVD < kMColBlkW) rv[cb % kVD] = ldv(cb + kVD);
+#pragma unroll
+                for (int ht = 0; ht < kMHT; ++ht)
+                    acc[ht][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pb[ht], acc[ht][cb], 0, 0, 0);
+            }
+        };
+        // barrier 0, then step j = 1..nblk: barrier j, P.V of block j-1 (buffer (j-1) % 4,
+        // parity (j-1) % 2)
+        lds_barrier();
+        auto step = [&](int j, const uint8_t* prev) {
+            lds_barrier();
+            pv_phase(prev, (j - 1) & 1);
+        };
+        // (not unrolled: with four copies of the step and their early exits the compiler
+        // copies the accumulators between steps and runs out of registers)
+        for (int j = 1; j <= nblk; ++j) {
+            const int sl = (j - 1) & 3;
+            step(j, sl == 0 ? stage_a : sl == 1 ? stage_b : sl == 2 ? stage_c : stage_d);
+        }
+        __syncthreads();   // every block done, the (m, l) pairs published, no load in flight
+        // normalised bf16 rows through LDS (heads 0-31 in A, 32-63 in B, swizzled as the
+        // staged keys are); then every wave writes whole 1 KB head rows
+#pragma unroll
+        for (int ht = 0; ht < kMHT; ++ht) {
+            const float l = xl[ht][n16];
+            const float inv = l > 0.f ? 1.f / l : 0.f;
+            const int sw = swz(n16);
+            const int eofs = (16 * (ht & 1) + n16) * kPitch + 256 * tw + 32 * (sw >> 1) + 16 * ((g >> 1) ^ (sw & 1)) + 8 * (g & 1);
+            uint8_t* sbuf = ht < 2 ? stage_a : stage_b;
+#pragma unroll
+            for (int cb = 0; cb < kMColBlkW; ++cb) {
+                uint2 w2;
+                w2.x = pack_bf16x2(acc[ht][cb][0] * inv, acc[ht][cb][1] * inv);
+                w2.y = pack_bf16x2(acc[ht][cb][2] * inv, acc[ht][cb][3] * inv);
+                *reinterpret_cast<uint2*>(sbuf + (eofs ^ (32 * cb))) = w2;
+            }
+        }
+        __syncthreads();
+    }
+    uint16_t* dst = part != nullptr ? part + ((row * ks_count + ks) * H + h0) * (int64_t)kMC
+                                    : out + (row * H + h0) * (int64_t)kMC;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int hr = 8 * wid + j;   // head row 0..63: rows 0-31 of A, then of B
+        const int r = hr & 31;
+        const uint8_t* sb = hr < 32 ? stage_a : stage_b;
+        const int c = lane ^ swz(r);
+        const uint4 v = *reinterpret_cast<const uint4*>(sb + r * kPitch + 16 * lane);
+        *reinterpret_cast<uint4*>(dst + (int64_t)hr * kMC + 8 * c) = v;
+    }
+}
+
 // Merge the key-range partials of one (row, head).  Partial j holds o_j = acc_j / l_j:
 // out = sum_j w_j o_j / sum_j w_j with w_j = l_j 2^(m_j - M), M = max_j m_j (log2 domain).
 // Ranges are taken 8 at a time with every load of a group in flight together (decode has 4:
@@ -669,11 +967,14 @@ int launch_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t
             part_ml = reinterpret_cast<float*>(part + rows * ks * H * (int64_t)kMC);
         }
         const float sl2 = scale * kLog2e;
-        // at most one workgroup per CU: the deep pipeline (its LDS allows only one)
-        auto kern = units <= kMFillWGs ? mqa_sparse_mfma<false, 4> : mqa_sparse_mfma<false, 2>;
-        hipLaunchKernelGGL(kern, dim3((unsigned)units), dim3(kMWaves * kWave), 0, stream,
-                           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx, rows, T, N, H, k, ks,
-                           kps, sl2, (int64_t)0, 1, static_cast<uint16_t*>(out), part, part_ml);
+        if (units <= kMFillWGs)   // at most one workgroup per CU: two waves per SIMD in two roles
+            hipLaunchKernelGGL(mqa_sparse_ws, dim3((unsigned)units), dim3(kWsWaves * kWave), 0, stream,
+                               static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx, rows, T, N, H,
+                               k, ks, kps, sl2, static_cast<uint16_t*>(out), part, part_ml);
+        else
+            hipLaunchKernelGGL((mqa_sparse_mfma<false, 2>), dim3((unsigned)units), dim3(kMWaves * kWave), 0, stream,
+                               static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx, rows, T, N, H,
+                               k, ks, kps, sl2, (int64_t)0, 1, static_cast<uint16_t*>(out), part, part_ml);
         if (ks > 1)
             hipLaunchKernelGGL(mqa_combine, dim3((unsigned)(rows * H)), dim3(64), 0, stream, part, part_ml, rows, H, ks,
                                static_cast<uint16_t*>(out));
