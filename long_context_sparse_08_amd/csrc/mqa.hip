@@ -669,21 +669,29 @@ mqa_sparse_ws(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
         for (int s = 0; s < kMC / 32; ++s) qb[s] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * s);
         // block `blk` into `dst`: this wave's 8 rows, ids in one LDS round trip; blocks past the
         // range load entry 0 (a gather is issued every step: one wait count fits every step)
+        auto gather_ids = [&](int blk) {   // lane j: the id of this wave's row j of block blk
+            return lane < kMLoadsPerBlk ? key_id(blk * kMBlk + kMLoadsPerBlk * tw + lane) : 0;
+        };
+        auto gather_row = [&](int myid, int r8, uint8_t* dst) {
+            const int r = kMLoadsPerBlk * tw + r8;
+            const int sidx = __builtin_amdgcn_readlane(myid, r8);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kvres, (lds_void_ptr)(dst + r * kPitch), 16,
+                                                     16u * (lane ^ swz(r)), (uint32_t)sidx * (2 * kMC), 0, 0);
+        };
         auto gather = [&](int blk, uint8_t* dst) {
-            const int myid = lane < kMLoadsPerBlk ? key_id(blk * kMBlk + kMLoadsPerBlk * tw + lane) : 0;
+            const int myid = gather_ids(blk);
 #pragma unroll
-            for (int r8 = 0; r8 < kMLoadsPerBlk; ++r8) {
-                const int r = kMLoadsPerBlk * tw + r8;
-                const int sidx = __builtin_amdgcn_readlane(myid, r8);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(kvres, (lds_void_ptr)(dst + r * kPitch), 16,
-                                                         16u * (lane ^ swz(r)), (uint32_t)sidx * (2 * kMC), 0, 0);
-            }
+            for (int r8 = 0; r8 < kMLoadsPerBlk; ++r8) gather_row(myid, r8, dst);
         };
         int aoff[4];
 #pragma unroll
         for (int b4 = 0; b4 < 4; ++b4) aoff[b4] = 16 * ((4 * b4 + g) ^ swz(n16));
         // scores, softmax and P of block blk (parity par) from `st`
-        auto s_phase = [&](int blk, const uint8_t* st, int par) {
+        // (the gather of a later block into `nxt` is issued row by row between the matrix
+        // instructions: its address work and the memory pipeline's intake then overlap them)
+        static_assert(kMC / 32 == 2 * kMLoadsPerBlk, "one gathered row every second step of the scores");
+        auto s_phase = [&](int blk, const uint8_t* st, int par, int gblk, uint8_t* nxt) {
+            const int gid = gather_ids(gblk);
             const uint32_t vg = vmask[blk] >> (4 * g);
             constexpr int kSD = 8;
             f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
@@ -705,6 +713,7 @@ mqa_sparse_ws(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
                     ra[s % kSD][0] = lda(s + kSD, 0);
                     ra[s % kSD][1] = lda(s + kSD, 1);
                 }
+                if ((s & 1) == 0) gather_row(gid, s >> 1, nxt);
             }
             // online softmax for head 16*tw + n16 (values of lane: keys 16*hb + 4g + i)
             float p[8];
@@ -753,9 +762,7 @@ mqa_sparse_ws(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
         // j+1 is staged; every step issues the same loads (no data-dependent branch inside)
         auto step = [&](int j, const uint8_t* cur, uint8_t* nxt) {
             lds_barrier();
-            gather(j + 2, nxt);
-            asm volatile("" ::: "memory");   // the gather is issued before the block's reads
-            s_phase(j, cur, j & 1);
+            s_phase(j, cur, j & 1, j + 2, nxt);
             wait_vmcnt<kMLoadsPerBlk>();
         };
         for (int j = 0; j < nblk; j += 4) {
