@@ -334,7 +334,8 @@ topk_bitmap(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
     __shared__ float s_lo, s_inv;
     __shared__ int s_bstar;
     __shared__ uint32_t s_need, s_ncand, s_need_eq, s_prefix, s_pmask;
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform: scalar registers
     const int64_t row = blockIdx.x;
     const int64_t nv = visible_entries(q_pos0 + row % T, m, N);
     const float* sc = scores + row * ld;
@@ -496,34 +497,53 @@ topk_bitmap(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
         const int nvi = (int)nv;   // <= ROWL
         const int nchunk = (nvi + kWave - 1) / kWave;
         const unsigned long long below = (1ull << lane) - 1ull;
-        for (int c0 = wid; c0 < nchunk; c0 += 8 * NW) {
+        // bin(v) > b* and bin(v) == b* straight from x = (v - lo) * inv, the expression the
+        // histogram's bins come from: bin(v) = trunc(clamp(x, 0, NB-1)), so bin(v) > b* iff
+        // x >= b*+1 (none when b* is the top bin), and bin(v) >= b* iff x >= b* (all when
+        // b* = 0: values below lo, -inf and NaN land in bin 0)
+        const float thr_gt = bstar < NB - 1 ? (float)(bstar + 1) : INFINITY;
+        const float thr_ge = bstar > 0 ? (float)bstar : -INFINITY;
+        // A wave takes 8 chunks per round (chunk c0 + u*NW).  Lane 2u / 2u+1 collects the two
+        // bitmap words of chunk u, so the words are stored once per round (no per-chunk
+        // exec-mask changes: the scalar unit, shared by the CU's 16 waves, bounds this loop).
+        const bool ge_all = bstar == 0;
+        // Lane masks come straight from compares (one VALU op each into a scalar register
+        // pair); the chunk's tail and the b* test combine on the scalar unit.
+        auto round = [&](int c0) {
             float v[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u)   // clamped reads: always in the row; masked below
                 v[u] = rowbuf[min((c0 + u * NW) * kWave + lane, nvi - 1)];
+            uint32_t wv = 0u;
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int c = c0 + u * NW;
-                if (c >= nchunk) break;
-                const int s = c * kWave + lane;
-                const bool ok = s < nvi;
-                const int bn = bin_of_n<NB>(v[u], lo, inv);
-                const unsigned long long mk = __ballot(ok && bn > bstar);
-                if (lane == 0) reinterpret_cast<uint2*>(bits)[c] = make_uint2((uint32_t)mk, (uint32_t)(mk >> 32));
-                const bool eq = ok && bn == bstar && fits;
-                const unsigned long long me = __ballot(eq);
-                if (me) {
-                    uint32_t base = 0;
-                    if (lane == 0) base = atomicAdd(&s_ncand, (uint32_t)__popcll(me));
-                    base = __shfl(base, 0, kWave);
-                    const uint32_t p = base + (uint32_t)__popcll(me & below);
-                    if (eq && p < (uint32_t)kCap) {
-                        cval[p] = v[u];
-                        cidx[p] = s;
+                const int nin = nvi - c * kWave;   // entries of this chunk in the row (uniform)
+                const unsigned long long okm = nin >= kWave ? ~0ull : nin > 0 ? (1ull << nin) - 1ull : 0ull;
+                const float x = (v[u] - lo) * inv;
+                const unsigned long long gtm = __ballot(x >= thr_gt);
+                const unsigned long long mk = gtm & okm;
+                wv = lane == 2 * u ? (uint32_t)mk : lane == 2 * u + 1 ? (uint32_t)(mk >> 32) : wv;
+                if (fits) {
+                    const unsigned long long gem = ge_all ? ~0ull : __ballot(x >= thr_ge);
+                    const unsigned long long me = gem & ~gtm & okm;
+                    if (me) {
+                        const bool eq = (me >> lane) & 1ull;
+                        uint32_t base = 0;
+                        if (lane == 0) base = atomicAdd(&s_ncand, (uint32_t)__popcll(me));
+                        base = __shfl(base, 0, kWave);
+                        const uint32_t p = base + (uint32_t)__popcll(me & below);
+                        if (eq && p < (uint32_t)kCap) {
+                            cval[p] = v[u];
+                            cidx[p] = c * kWave + lane;
+                        }
                     }
                 }
             }
-        }
+            const int cw = c0 + (lane >> 1) * NW;
+            if (lane < 16 && cw < nchunk) bits[2 * cw + (lane & 1)] = wv;
+        };
+        for (int c0 = wid; c0 < nchunk; c0 += 8 * NW) round(c0);
     } else {
         for (int64_t s0 = tid; s0 < nv; s0 += 8 * NT) {
             float v[8];
@@ -1137,7 +1157,8 @@ __global__ void __launch_bounds__(kGThreads)
 topk_groups(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_pos0, int64_t N, int m, int k,
             const float* __restrict__ gmax, int64_t gld, int G, int32_t* __restrict__ idx, float* __restrict__ sel) {
     __shared__ GroupShared sh;
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform: scalar registers
     const int64_t row = blockIdx.x;
     const int64_t nv = visible_entries(q_pos0 + row % T, m, N);
     const float* sc = scores + row * ld;
