@@ -237,7 +237,8 @@ def main():
         stages["index"] = (lambda: csa.csa_index_scores(i["qI"], i["w"], i["kI"], cfg.q_pos0, cfg.m, scores=scores),
                            ["index_scores_mfma"], "index")
         stages["select"] = (pipe.select, ["index_scores_mfma", "topk"], None)
-        stages["attend"] = (pipe.attend, ["mqa_sparse_mfma"] + (["mqa_combine"] if split else []),
+        # (decode launches have at most one workgroup per CU: the warp-specialised kernel)
+        stages["attend"] = (pipe.attend, ["mqa_sparse_ws"] + (["mqa_combine"] if split else []),
                             None if split else "mqa")
     elif cfg.kind == "csa_prefill":
         scores = torch.empty((cfg.batch, cfg.T, cfg.N), dtype=torch.float32, device="cuda")
@@ -246,8 +247,8 @@ def main():
         stages["compress_kI"] = (lambda: csa.csa_compress(i["ICa"], i["ICb"], i["IZa"], i["IZb"], i["IBa"], i["IBb"],
                                                           cfg.m, out=pipe.kI), ["compress_kernel"], "compress_kI")
         stages["index"] = (lambda: csa.csa_index_scores(i["qI"], i["w"], pipe.kI, cfg.q_pos0, cfg.m, scores=scores),
-                           ["index_scores_mfma"], "index")
-        stages["select"] = (pipe.select, ["index_scores_mfma", "topk"], None)
+                           ["index_scores_prefill"], "index")
+        stages["select"] = (pipe.select, ["index_scores_prefill", "topk"], None)
         stages["attend"] = (pipe.attend, ["mqa_sparse_mfma"], "mqa")
     else:
         stages["compress"] = (pipe.compress, ["compress_kernel"], "compress")

@@ -887,16 +887,21 @@ mqa_sparse_ws(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
 
 // Merge the key-range partials of one (row, head).  Partial j holds o_j = acc_j / l_j:
 // out = sum_j w_j o_j / sum_j w_j with w_j = l_j 2^(m_j - M), M = max_j m_j (log2 domain).
-// Ranges are taken 8 at a time with every load of a group in flight together (decode has 4:
-// one round trip); a later group with a larger max rescales what is already summed.
-constexpr int kCombGroup = 8;
+// Ranges are taken CG at a time with every load of a group in flight together (CG = 4 for
+// up to four ranges, as in decode: one round trip, no duplicate loads; else 8); a later group
+// with a larger max rescales what is already summed.  One wave per (row, head), four per
+// workgroup.
+constexpr int kCombWaves = 4;
 
-__global__ void __launch_bounds__(64)
+template <int CG>
+__global__ void __launch_bounds__(kCombWaves * kWave)
 mqa_combine(const uint16_t* __restrict__ part, const float* __restrict__ part_ml, int64_t rows, int H, int ks_count,
             uint16_t* __restrict__ out) {
-    const int64_t rh = blockIdx.x;   // row * H + head
+    constexpr int kCombGroup = CG;
+    const int64_t rh = (int64_t)blockIdx.x * kCombWaves + (threadIdx.x >> 6);   // row * H + head
+    if (rh >= rows * H) return;
     const int64_t row = rh / H, head = rh % H;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
     const int64_t prow0 = row * ks_count * H + head;   // partial row of range j: prow0 + j * H
     float M = -INFINITY, L = 0.f;
     float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -982,9 +987,15 @@ int launch_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t
             hipLaunchKernelGGL((mqa_sparse_mfma<false, 2>), dim3((unsigned)units), dim3(kMWaves * kWave), 0, stream,
                                static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx, rows, T, N, H,
                                k, ks, kps, sl2, (int64_t)0, 1, static_cast<uint16_t*>(out), part, part_ml);
-        if (ks > 1)
-            hipLaunchKernelGGL(mqa_combine, dim3((unsigned)(rows * H)), dim3(64), 0, stream, part, part_ml, rows, H, ks,
-                               static_cast<uint16_t*>(out));
+        if (ks > 1) {
+            const dim3 cgrid((unsigned)((rows * H + kCombWaves - 1) / kCombWaves)), cblock(kCombWaves * kWave);
+            if (ks <= 4)
+                hipLaunchKernelGGL(mqa_combine<4>, cgrid, cblock, 0, stream, part, part_ml, rows, H, ks,
+                                   static_cast<uint16_t*>(out));
+            else
+                hipLaunchKernelGGL(mqa_combine<8>, cgrid, cblock, 0, stream, part, part_ml, rows, H, ks,
+                                   static_cast<uint16_t*>(out));
+        }
         return 0;
     }
     if (t == DT_F32) return launch_generic<DT_F32, false>(q, kv, idx, batch, T, N, H, c, k, scale, 0, 1, out, stream);
