@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace csa {
 
 enum Dt : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
@@ -108,6 +110,49 @@ __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
     return v;
+}
+
+// ------------------------------------------------------------------ VALU-only wave scans
+// Cross-lane steps through DPP and the gfx950 lane swaps: no LDS round trip (a __shfl is a
+// ds_bpermute), so a chain of them costs a few cycles per step instead of an LDS latency.
+
+// x of the lane the DPP control CTRL names, in the rows of ROW_MASK; 0 elsewhere and where
+// the named lane is outside the row
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xF, true);
+}
+
+// Inclusive prefix sum over the 64 lanes: row_shr 1, 2, 4, 8 scan each row of 16 lanes,
+// row_bcast:15 adds row 0's total to row 1 (and row 2's to row 3), row_bcast:31 adds the
+// total of rows 0-1 to rows 2-3.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+    x += dpp_u32<0x111, 0xF>(x);
+    x += dpp_u32<0x112, 0xF>(x);
+    x += dpp_u32<0x114, 0xF>(x);
+    x += dpp_u32<0x118, 0xF>(x);
+    x += dpp_u32<0x142, 0xA>(x);
+    x += dpp_u32<0x143, 0xC>(x);
+    return x;
+}
+
+// max / min over the wave, every lane gets it: lane ^ 1, lane ^ 2 (quad_perm), the other quad
+// of 8 (row_half_mirror), the other half of 16 (row_mirror), then lanes l ^ 16 and l ^ 32
+// (permlane16 / permlane32 swaps return the pair {x[l], x[l ^ 16 or 32]})
+template <bool MAX>
+__device__ __forceinline__ float wave_ext(float x) {
+    auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : fminf(a, b); };
+    auto dp = [](float v, auto ctrl) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value, 0xF, 0xF, false));
+    };
+    x = op(x, dp(x, std::integral_constant<int, 0xB1>{}));
+    x = op(x, dp(x, std::integral_constant<int, 0x4E>{}));
+    x = op(x, dp(x, std::integral_constant<int, 0x141>{}));
+    x = op(x, dp(x, std::integral_constant<int, 0x140>{}));
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = op(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return op(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
 }
 
 // Number of compressed entries (ratio r) visible to the query at absolute position p:

@@ -288,15 +288,13 @@ constexpr int kShortRow = 4096;      // rows up to this use 256-thread workgroup
 constexpr int kShortThreads = 256;
 constexpr int kBmWordsGlb = kBmMaxRow / 32;
 
+// Exclusive prefix sum of x over the workgroup's NW waves (every thread active) and the
+// total; two barriers, buf holds NW words.
 template <int NW>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* buf, uint32_t* total) {
-    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-    uint32_t inc = x;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const uint32_t y = __shfl_up(inc, off, kWave);
-        if (lane >= off) inc += y;
-    }
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t inc = wave_incl_scan(x);
     if (lane == kWave - 1) buf[wid] = inc;
     __syncthreads();
     uint32_t before = 0, all = 0;
@@ -1032,7 +1030,7 @@ struct GroupShared {
     int bstar;
     uint32_t scan[kGWaves + 2];
     uint32_t red_lo[kGWaves], red_hi[kGWaves];
-    uint32_t prefix, pmask, rem;
+    uint32_t ctl[3];   // radix select state
     uint32_t ngroups, ncand;
 };
 static_assert(kGMaxRow / 32 >= kGMaxGroups, "group keys share the tie bitmap");
@@ -1060,58 +1058,54 @@ __device__ __forceinline__ void block_minmax(uint32_t& lo, uint32_t& hi, GroupSh
     __syncthreads();   // read by all before the next use
 }
 
-// Exact k-th largest (k >= 1) of the keys key_at(i), i < n (n >= k), all within [kmin, kmax]:
-// the bits above the highest bit where kmin and kmax differ are common to every key; the
-// rest is resolved in passes over 8-bit digits from the top, each narrowing to the keys that
-// share the digits found so far.  (Starting at the first varying bit spreads the histogram:
-// scores of similar size share their sign and exponent bits.)
-// Returns K*; *need_eq receives how many keys equal to K* belong to the k largest.
-template <class F>
-__device__ uint32_t radix_kth(F key_at, int64_t n, uint32_t k, uint32_t kmin, uint32_t kmax, GroupShared& sh,
+// Exact k-th largest (k >= 1) of the keys the workgroup's NT threads visit (visit(f) calls
+// f(key) for every key the calling thread holds; at least k keys in all, all within [kmin,
+// kmax]): the bits above the highest bit where kmin and kmax differ are common to every key;
+// the rest is resolved in passes over 8-bit digits from the top, each narrowing to the keys
+// that share the digits found so far.  (Starting at the first varying bit spreads the
+// histogram: scores of similar size share their sign and exponent bits.)
+// hist: 256 words of LDS, ctl: 3 (prefix, mask, remaining).  Returns K*; *need_eq receives
+// how many keys equal to K* belong to the k largest.
+template <int NT, class V>
+__device__ __forceinline__ uint32_t radix_kth(V visit, uint32_t k, uint32_t kmin, uint32_t kmax, uint32_t* hist, uint32_t* ctl,
                               uint32_t* need_eq) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const uint32_t diff = kmin ^ kmax;
     int hb = diff == 0u ? 0 : 32 - __clz(diff);   // bits [0, hb) vary
     const uint32_t low = hb == 32 ? ~0u : (1u << hb) - 1u;
     if (tid == 0) {
-        sh.prefix = kmin & ~low;
-        sh.pmask = ~low;
-        sh.rem = k;
+        ctl[0] = kmin & ~low;
+        ctl[1] = ~low;
+        ctl[2] = k;
     }
     while (hb > 0) {
         const int wd = hb < 8 ? hb : 8, shift = hb - wd;
         const uint32_t dmask = (1u << wd) - 1u;
-        for (int i = tid; i < 256; i += kGThreads) sh.hist[i] = 0u;
+        for (int i = tid; i < 256; i += NT) hist[i] = 0u;
         __syncthreads();   // also publishes the previous pass's prefix
-        const uint32_t prefix = sh.prefix, pmask = sh.pmask;
-        for (int64_t i = tid; i < n; i += kGThreads) {
-            const uint32_t key = key_at(i);
-            if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
-        }
+        const uint32_t prefix = ctl[0], pmask = ctl[1];
+        visit([&](uint32_t key) {
+            if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
+        });
         __syncthreads();
         if (tid < kWave) {
             // lane l holds digits 255-4l .. 252-4l (descending); inclusive scan from the top
             uint32_t c[4], mine = 0;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                c[j] = sh.hist[255 - 4 * lane - j];
+                c[j] = hist[255 - 4 * lane - j];
                 mine += c[j];
             }
-            uint32_t inc = mine;
-#pragma unroll
-            for (int off = 1; off < kWave; off <<= 1) {
-                const uint32_t y = __shfl_up(inc, off, kWave);
-                if (lane >= off) inc += y;
-            }
-            const uint32_t rem = sh.rem, before = inc - mine;
+            const uint32_t inc = wave_incl_scan(mine);
+            const uint32_t rem = ctl[2], before = inc - mine;
             if (before < rem && inc >= rem) {   // exactly one lane
                 uint32_t acc = before;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     if (acc + c[j] >= rem) {
-                        sh.prefix = prefix | ((uint32_t)(255 - 4 * lane - j) << shift);
-                        sh.pmask = pmask | (dmask << shift);
-                        sh.rem = rem - acc;
+                        ctl[0] = prefix | ((uint32_t)(255 - 4 * lane - j) << shift);
+                        ctl[1] = pmask | (dmask << shift);
+                        ctl[2] = rem - acc;
                         break;
                     }
                     acc += c[j];
@@ -1122,7 +1116,7 @@ __device__ uint32_t radix_kth(F key_at, int64_t n, uint32_t k, uint32_t kmin, ui
         hb = shift;
     }
     __syncthreads();
-    const uint32_t kth = sh.prefix, rem = sh.rem;
+    const uint32_t kth = ctl[0], rem = ctl[2];
     __syncthreads();   // every thread has read them before a later call rewrites them
     *need_eq = rem;
     return kth;
@@ -1139,7 +1133,7 @@ __device__ __forceinline__ uint32_t wave_append(bool take, uint32_t* counter) {
     const int lane = threadIdx.x & (kWave - 1);
     uint32_t base = 0;
     if (lane == 0 && m != 0ull) base = atomicAdd(counter, (uint32_t)__popcll(m));
-    base = __shfl(base, 0, kWave);
+    base = __builtin_amdgcn_readlane(base, 0);
     return base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
 }
 
@@ -1245,16 +1239,10 @@ topk_groups(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
         auto append = [&](uint32_t mask, const int64_t* ebase, const float* xs, auto nx_tag, auto per_tag) {
             constexpr int NX = decltype(nx_tag)::value, PER = decltype(per_tag)::value;
             const uint32_t c = __popc(mask);
-            uint32_t inc = c;
-#pragma unroll
-            for (int off = 1; off < kWave; off <<= 1) {
-                const uint32_t y = __shfl_up(inc, off, kWave);
-                if (lane >= off) inc += y;
-            }
-            const uint32_t wtot = __shfl(inc, kWave - 1, kWave);
+            const uint32_t inc = wave_incl_scan(c);
             uint32_t base = 0;
-            if (lane == kWave - 1 && wtot) base = atomicAdd(&sh.ncand, wtot);
-            base = __shfl(base, kWave - 1, kWave) + inc - c;
+            if (lane == kWave - 1 && inc) base = atomicAdd(&sh.ncand, inc);
+            base = __builtin_amdgcn_readlane(base, kWave - 1) + inc - c;
 #pragma unroll
             for (int bit = 0; bit < NX; ++bit) {
                 if ((mask >> bit) & 1u) {
@@ -1319,7 +1307,12 @@ topk_groups(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
         block_minmax(lo, hi, sh);   // (its barrier also publishes the candidates)
         ncand = sh.ncand;
         if (ncand > kGCap || ncand < k) full = true;   // heavy ties at b* (the second cannot happen)
-        else kstar = radix_kth([&](int64_t i2) { return sh.ckey[i2]; }, ncand, (uint32_t)k, lo, hi, sh, &need_eq);
+        else
+            kstar = radix_kth<kGThreads>(
+                [&](auto f) {
+                    for (int64_t i2 = tid; i2 < ncand; i2 += kGThreads) f(sh.ckey[i2]);
+                },
+                (uint32_t)k, lo, hi, sh.hist, sh.ctl, &need_eq);
     }
     if (full) {
         uint32_t lo = ~0u, hi = 0u;
@@ -1329,7 +1322,11 @@ topk_groups(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
             hi = max(hi, key);
         }
         block_minmax(lo, hi, sh);
-        kstar = radix_kth([&](int64_t e) { return order_key(sc[e]); }, nv, (uint32_t)k, lo, hi, sh, &need_eq);
+        kstar = radix_kth<kGThreads>(
+            [&](auto f) {
+                for (int64_t e = tid; e < nv; e += kGThreads) f(order_key(sc[e]));
+            },
+            (uint32_t)k, lo, hi, sh.hist, sh.ctl, &need_eq);
     }
 
     // bitmaps: kept (key > K*) in b, ties (key == K*) in a
@@ -1419,6 +1416,423 @@ topk_groups(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
     }
 }
 
+// ============================================================================ register-staged
+// Decode rows of up to 32768 visible entries with at least 8k of them (few queries, long
+// rows): one 1024-thread workgroup per row keeps the row in registers (float4 j of the row in
+// thread j % 1024, eight per thread, loaded coalesced; the nv % 4 last entries one per
+// thread).  Each float4 is a group of 4 entries.
+//   1  the group maxima, their range, a 2048-bin histogram linear in value of them (8 LDS
+//      atomics per thread instead of 32) and b1: the highest bin with at least k group maxima
+//      in it and above.  Those k groups hold k distinct entries in bins >= b1 and binning is
+//      monotonic, so the k-th largest entry and every entry of the top k (ties included) lie
+//      in bins >= b1: these are the candidates, about k of them.
+//   2  the groups whose maximum is in a bin >= b1 (about k) are copied to an LDS list, one
+//      wave ballot per float4; their entries in bins >= b1 become the candidates (value,
+//      index), counted at once into a second linear histogram over the candidates' range
+//   3  candidates above the bin b2 that holds the k-th largest are kept; b2's few members
+//      are ranked inside one wave (value desc, index asc) and the first need2 kept
+//   4  kept entries set their bit in a row bitmap; a block scan of the word popcounts gives
+//      each kept candidate its output slot (ids ascending)
+// The bin that holds the k-th largest count is found by one wave (32 bins per lane, one wave
+// scan) while the others wait at the next barrier.  More than kRGCap selected groups or kRCap
+// candidates (heavy ties) take an exact radix select over the row's keys, more than 64
+// members of b2 one over those members; ties at the cut are then resolved in index order
+// through a tie bitmap.
+constexpr int kRThreads = 1024;
+constexpr int kRWaves = kRThreads / kWave;
+constexpr int kRRow = 32768;                     // visible entries per row, at most
+constexpr int kRF4 = kRRow / (4 * kRThreads);    // float4 per thread
+constexpr int kRBins = 2048;
+constexpr int kRGCap = 4096;                     // selected groups
+constexpr int kRCap = 4096;                      // candidates
+constexpr int kRWords = kRRow / 32;
+static_assert(kRWords == kRThreads, "one bitmap word per thread");
+static_assert(kRBins == 32 * kWave, "32 bins per lane of the searching wave");
+static_assert(kRGCap % kRThreads == 0, "whole rounds over the group list");
+
+struct RegShared {
+    float4 gval[kRGCap];         // selected groups: values and float4 index
+    uint16_t gidx[kRGCap];
+    uint2 cand[kRCap];           // candidates: (value bits, index)
+    uint32_t kept[kRWords];
+    uint32_t ties[kRWords];
+    uint32_t wpos[kRWords];      // kept entries before each word
+    uint32_t hist[kRBins];       // group maxima; later the radix select's digits
+    uint32_t hist2[kRBins];      // candidates
+    uint2 mem[kWave];            // members of b2
+    float red_lo[kRWaves], red_hi[kRWaves];
+    uint32_t ured_lo[kRWaves], ured_hi[kRWaves];
+    uint32_t scan[kRWaves];
+    uint32_t ctl[3];
+    int b1, b2;
+    uint32_t need2, ngsel, ncand, nmem;
+};
+
+// block-wide min / max of order keys (every thread gets both)
+__device__ __forceinline__ void block_minmax_keys(uint32_t& lo, uint32_t& hi, RegShared& sh) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+        lo = min(lo, (uint32_t)__shfl_xor((int)lo, off, kWave));
+        hi = max(hi, (uint32_t)__shfl_xor((int)hi, off, kWave));
+    }
+    if (lane == 0) {
+        sh.ured_lo[wid] = lo;
+        sh.ured_hi[wid] = hi;
+    }
+    __syncthreads();
+    lo = sh.ured_lo[0];
+    hi = sh.ured_hi[0];
+#pragma unroll
+    for (int w = 1; w < kRWaves; ++w) {
+        lo = min(lo, sh.ured_lo[w]);
+        hi = max(hi, sh.ured_hi[w]);
+    }
+    __syncthreads();
+}
+
+// One wave: the bin of kRBins that holds the k-th largest of the counted values, searched from
+// the top; *b receives it and *need how many of its members belong to the k largest (nothing
+// is written when the counts sum to less than k).  Lane l sums the l-th chunk of 32 bins from
+// the top (16-byte reads rotated by l / 2 so that 16 lanes hit 16 different bank groups), a
+// wave scan finds the chunk, then the chunk's bins one per lane and a second scan the bin.
+__device__ __forceinline__ void wave_kth_bin(const uint32_t* hist, uint32_t k, int* b, uint32_t* need) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint4* h4 = reinterpret_cast<const uint4*>(hist + kRBins - 32 * (lane + 1));
+    uint32_t sum = 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const uint4 x = h4[(q + (lane >> 1)) & 7];
+        sum += x.x + x.y + x.z + x.w;
+    }
+    const uint32_t inc = wave_incl_scan(sum);
+    const unsigned long long hit = __ballot(inc - sum < k && inc >= k);   // at most one lane
+    if (hit == 0ull) return;
+    const int L = __builtin_ctzll(hit);
+    const uint32_t before = __builtin_amdgcn_readlane(inc - sum, L);
+    const int bin = kRBins - 32 * L - 1 - lane;   // lanes 0-31: the chunk's bins, top down
+    const uint32_t h = lane < 32 ? hist[bin] : 0u;
+    const uint32_t inc2 = before + wave_incl_scan(h);
+    if (lane < 32 && inc2 - h < k && inc2 >= k) {   // exactly one lane
+        *b = bin;
+        if (need) *need = k - (inc2 - h);
+    }
+}
+
+__global__ void __launch_bounds__(kRThreads)
+topk_regs(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_pos0, int64_t N, int m, int k,
+          int32_t* __restrict__ idx, float* __restrict__ sel) {
+    __shared__ RegShared sh;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform: scalar registers
+    const int64_t row = blockIdx.x;
+    const int64_t nv = visible_entries(q_pos0 + row % T, m, N);
+    const float* sc = scores + row * ld;
+    int32_t* oi = idx + row * k;
+    float* os = sel ? sel + row * k : nullptr;
+    if (nv <= k) {
+        for (int r = tid; r < k; r += kRThreads) {
+            oi[r] = r < nv ? r : -1;
+            if (os) os[r] = r < nv ? sc[r] : -INFINITY;
+        }
+        return;
+    }
+    // (the launcher sends rows of at most kRRow visible entries)
+    const int nvi = (int)nv, n4 = nvi >> 2;
+    const float4* s4 = reinterpret_cast<const float4*>(sc);
+    float4 v[kRF4];
+#pragma unroll
+    for (int u = 0; u < kRF4; ++u) {
+        const int j = tid + u * kRThreads;
+        v[u] = j < n4 ? s4[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    const int et = 4 * n4 + tid;   // the last nv % 4 entries, one per thread
+    const bool has_t = et < nvi;
+    const float vt = has_t ? sc[et] : 0.f;
+    auto valid = [&](int u) { return tid + u * kRThreads < n4; };
+
+    // LDS state cleared while the loads are in flight
+    sh.kept[tid] = 0u;
+    sh.ties[tid] = 0u;
+    sh.hist[tid] = 0u;
+    sh.hist[tid + kRThreads] = 0u;
+    sh.hist2[tid] = 0u;
+    sh.hist2[tid + kRThreads] = 0u;
+    if (tid == 0) {
+        sh.ngsel = 0u;
+        sh.ncand = 0u;
+        sh.nmem = 0u;
+        sh.b1 = 0;   // stays 0 when the groups number fewer than k: every entry is a candidate
+        sh.b2 = 0;
+        sh.need2 = 0u;
+    }
+
+    // ---- 1: group maxima, their range, histogram, b1
+    float gm[kRF4];
+    float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kRF4; ++u) {
+        gm[u] = fmaxf(fmaxf(v[u].x, v[u].y), fmaxf(v[u].z, v[u].w));
+        if (valid(u)) {
+            lo = fminf(lo, gm[u]);
+            hi = fmaxf(hi, gm[u]);
+        }
+    }
+    if (has_t) {
+        lo = fminf(lo, vt);
+        hi = fmaxf(hi, vt);
+    }
+    lo = wave_ext<false>(lo);
+    hi = wave_ext<true>(hi);
+    if (lane == 0) {
+        sh.red_lo[wid] = lo;
+        sh.red_hi[wid] = hi;
+    }
+    __syncthreads();
+    lo = sh.red_lo[0];
+    hi = sh.red_hi[0];
+#pragma unroll
+    for (int w = 1; w < kRWaves; ++w) {
+        lo = fminf(lo, sh.red_lo[w]);
+        hi = fmaxf(hi, sh.red_hi[w]);
+    }
+    float inv = (float)kRBins / (hi - lo);
+    if (!(hi > lo) || !isfinite(inv)) inv = 0.f;
+    int gb[kRF4];   // the groups' bins (-1: no group)
+#pragma unroll
+    for (int u = 0; u < kRF4; ++u) {
+        gb[u] = valid(u) ? bin_of_n<kRBins>(gm[u], lo, inv) : -1;
+        if (gb[u] >= 0) atomicAdd(&sh.hist[gb[u]], 1u);
+    }
+    if (has_t) atomicAdd(&sh.hist[bin_of_n<kRBins>(vt, lo, inv)], 1u);
+    __syncthreads();
+    if (wid == 0) wave_kth_bin(sh.hist, (uint32_t)k, &sh.b1, nullptr);
+    __syncthreads();
+    const int b1 = sh.b1;
+
+    // ---- 2: an entry is in a bin >= b1 iff (v - lo) * inv >= b1 (the expression the bins come
+    // from, before clamping; every entry when b1 = 0).  First the groups whose maximum is:
+    const float thr = (float)b1;
+    auto is_cand = [&](float x) { return b1 == 0 || (x - lo) * inv >= thr; };
+    {
+        // (a group is selected iff its bin is >= b1: the same test on its maximum)
+        unsigned long long sm[kRF4];
+        uint32_t wtot = 0u;
+#pragma unroll
+        for (int u = 0; u < kRF4; ++u) {
+            sm[u] = __ballot(gb[u] >= b1);
+            wtot += (uint32_t)__popcll(sm[u]);
+        }
+        uint32_t gbase = 0u;
+        if (lane == 0 && wtot != 0u) gbase = atomicAdd(&sh.ngsel, wtot);
+        gbase = __builtin_amdgcn_readlane(gbase, 0);
+        if (gbase + wtot <= (uint32_t)kRGCap) {   // (else the row takes the radix select)
+#pragma unroll
+            for (int u = 0; u < kRF4; ++u) {
+                if (gb[u] >= b1) {
+                    const uint32_t slot = gbase + __builtin_amdgcn_mbcnt_hi((uint32_t)(sm[u] >> 32),
+                                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)sm[u], 0u));
+                    sh.gval[slot] = v[u];
+                    sh.gidx[slot] = (uint16_t)(tid + u * kRThreads);
+                }
+                gbase += (uint32_t)__popcll(sm[u]);
+            }
+        }
+    }
+    __syncthreads();
+    const uint32_t ngsel = sh.ngsel;
+    // the candidates' histogram: over [about the lower edge of b1, hi] (b1 > 0: inv > 0)
+    const float lo2 = b1 > 0 ? lo + thr / inv : lo;
+    float inv2 = (float)kRBins / (hi - lo2);
+    if (!(hi > lo2) || !isfinite(inv2)) inv2 = 0.f;
+    bool row_select = ngsel > (uint32_t)kRGCap;   // heavy ties (block-uniform)
+    if (!row_select) {
+        // the selected groups' entries in bins >= b1 (and the tail's), appended with one
+        // atomic per wave and counted into the second histogram
+        for (uint32_t i0 = 0; i0 == 0 || i0 < ngsel; i0 += kRThreads) {   // (the tail: round 0)
+            const uint32_t i = i0 + tid;
+            const bool ok = i < ngsel;
+            const float4 x = ok ? sh.gval[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+            const int e0 = ok ? 4 * (int)sh.gidx[i] : 0;
+            const bool tl = i0 == 0 && has_t && is_cand(vt);
+            const uint32_t cm = (ok && is_cand(x.x) ? 1u : 0u) | (ok && is_cand(x.y) ? 2u : 0u) |
+                                (ok && is_cand(x.z) ? 4u : 0u) | (ok && is_cand(x.w) ? 8u : 0u) | (tl ? 16u : 0u);
+            const uint32_t cnt = (uint32_t)__popc(cm);
+            const uint32_t inc = wave_incl_scan(cnt);
+            uint32_t base = 0u;
+            if (lane == kWave - 1 && inc != 0u) base = atomicAdd(&sh.ncand, inc);
+            base = __builtin_amdgcn_readlane(base, kWave - 1) + inc - cnt;
+            auto put = [&](float xv, int e) {
+                if (base < (uint32_t)kRCap) sh.cand[base] = make_uint2(__float_as_uint(xv), (uint32_t)e);
+                ++base;
+                atomicAdd(&sh.hist2[bin_of_n<kRBins>(xv, lo2, inv2)], 1u);
+            };
+            if (cm & 1u) put(x.x, e0);
+            if (cm & 2u) put(x.y, e0 + 1);
+            if (cm & 4u) put(x.z, e0 + 2);
+            if (cm & 8u) put(x.w, e0 + 3);
+            if (cm & 16u) put(vt, et);
+        }
+        __syncthreads();
+        row_select = sh.ncand > (uint32_t)kRCap;
+    }
+    const uint32_t ncand = sh.ncand;   // >= k: the candidates hold the top k
+
+    // ---- 3: the cut.  Entries set in `kept` are taken; of the entries set in `ties` (equal to
+    // the k-th key K*) the first need_eq in index order are taken too.
+    bool with_ties = false;
+    uint32_t need_eq = 0u;
+    if (!row_select) {
+        if (wid == 0) wave_kth_bin(sh.hist2, (uint32_t)k, &sh.b2, &sh.need2);
+        __syncthreads();
+        const int b2 = sh.b2;
+        const uint32_t need2 = sh.need2;
+        // candidates above b2 are kept; b2's members are listed (every lane of a wave runs the
+        // same trip count: the list append is wave-wide)
+        for (uint32_t i0 = 0; i0 < ncand; i0 += kRThreads) {
+            const uint32_t i = i0 + tid;
+            const bool ok = i < ncand;
+            const uint2 c = ok ? sh.cand[i] : make_uint2(0u, 0u);
+            const int bn = ok ? bin_of_n<kRBins>(__uint_as_float(c.x), lo2, inv2) : -1;
+            if (bn > b2) atomicOr(&sh.kept[c.y >> 5], 1u << (c.y & 31));
+            const bool mb = bn == b2;
+            const uint32_t p = wave_append(mb, &sh.nmem);
+            if (mb && p < (uint32_t)kWave) sh.mem[p] = c;
+        }
+        __syncthreads();
+        const uint32_t nmem = sh.nmem;
+        if (nmem <= (uint32_t)kWave) {
+            // lane i holds member i; the others' keys come by readlane (no LDS round trips)
+            if (wid == 0) {
+                const bool have = (uint32_t)lane < nmem;
+                const uint2 c = have ? sh.mem[lane] : make_uint2(0u, 0u);
+                const uint32_t ki = order_key(__uint_as_float(c.x));
+                uint32_t rank = 0u;
+                for (uint32_t j = 0; j < nmem; ++j) {
+                    const uint32_t kj = __builtin_amdgcn_readlane(ki, j);
+                    const uint32_t sj = __builtin_amdgcn_readlane(c.y, j);
+                    rank += (kj > ki || (kj == ki && sj < c.y)) ? 1u : 0u;
+                }
+                if (have && rank < need2) atomicOr(&sh.kept[c.y >> 5], 1u << (c.y & 31));
+            }
+        } else {
+            // many members (ties): K* among them by radix select
+            auto visit = [&](auto f) {
+                for (uint32_t i = tid; i < ncand; i += kRThreads) {
+                    const float x = __uint_as_float(sh.cand[i].x);
+                    if (bin_of_n<kRBins>(x, lo2, inv2) == b2) f(order_key(x));
+                }
+            };
+            uint32_t klo = ~0u, khi = 0u;
+            visit([&](uint32_t key) {
+                klo = min(klo, key);
+                khi = max(khi, key);
+            });
+            block_minmax_keys(klo, khi, sh);
+            const uint32_t kstar = radix_kth<kRThreads>(visit, need2, klo, khi, sh.hist, sh.ctl, &need_eq);
+            for (uint32_t i = tid; i < ncand; i += kRThreads) {
+                const uint2 c = sh.cand[i];
+                const float x = __uint_as_float(c.x);
+                if (bin_of_n<kRBins>(x, lo2, inv2) != b2) continue;
+                const uint32_t key = order_key(x);
+                if (key > kstar) atomicOr(&sh.kept[c.y >> 5], 1u << (c.y & 31));
+                else if (key == kstar) atomicOr(&sh.ties[c.y >> 5], 1u << (c.y & 31));
+            }
+            with_ties = true;
+        }
+    } else {
+        // heavy ties: K* over the whole row (keys from the registers)
+        auto visit = [&](auto f) {
+#pragma unroll
+            for (int u = 0; u < kRF4; ++u) {
+                if (!valid(u)) continue;
+                f(order_key(v[u].x));
+                f(order_key(v[u].y));
+                f(order_key(v[u].z));
+                f(order_key(v[u].w));
+            }
+            if (has_t) f(order_key(vt));
+        };
+        uint32_t klo = ~0u, khi = 0u;
+        visit([&](uint32_t key) {
+            klo = min(klo, key);
+            khi = max(khi, key);
+        });
+        block_minmax_keys(klo, khi, sh);
+        const uint32_t kstar = radix_kth<kRThreads>(visit, (uint32_t)k, klo, khi, sh.hist, sh.ctl, &need_eq);
+        // float4 j holds entries 4j .. 4j+3: bits 4 (j % 8) .. of word j / 8
+#pragma unroll
+        for (int u = 0; u < kRF4; ++u) {
+            if (!valid(u)) continue;
+            const int j = tid + u * kRThreads;
+            const float xs[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+            uint32_t kn = 0u, tn = 0u;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t key = order_key(xs[c]);
+                kn |= (key > kstar ? 1u : 0u) << c;
+                tn |= (key == kstar ? 1u : 0u) << c;
+            }
+            if (kn) atomicOr(&sh.kept[j >> 3], kn << (4 * (j & 7)));
+            if (tn) atomicOr(&sh.ties[j >> 3], tn << (4 * (j & 7)));
+        }
+        if (has_t) {
+            const uint32_t key = order_key(vt);
+            if (key > kstar) atomicOr(&sh.kept[et >> 5], 1u << (et & 31));
+            else if (key == kstar) atomicOr(&sh.ties[et >> 5], 1u << (et & 31));
+        }
+        with_ties = true;
+    }
+    __syncthreads();
+
+    // ---- 4: ordered output, thread w owns bitmap word w
+    const int nwords = (nvi + 31) >> 5;
+    uint32_t kw = tid < nwords ? sh.kept[tid] : 0u;
+    uint32_t total;
+    if (with_ties) {
+        const uint32_t tw = tid < nwords ? sh.ties[tid] : 0u;
+        const uint32_t taken = block_excl_scan<kRWaves>((uint32_t)__popc(tw), sh.scan, &total);
+        uint32_t eqw = tw;
+        if (taken >= need_eq) eqw = 0u;
+        else if (taken + (uint32_t)__popc(tw) > need_eq) eqw = first_bits(tw, need_eq - taken);
+        kw |= eqw;
+    }
+    const uint32_t pos = block_excl_scan<kRWaves>((uint32_t)__popc(kw), sh.scan, &total);
+    if (!row_select) {
+        // every kept entry is a candidate: its slot is the kept count before its word plus the
+        // kept bits below it in the word
+        if (tid < nwords) {
+            sh.kept[tid] = kw;
+            sh.wpos[tid] = pos;
+        }
+        __syncthreads();
+        for (uint32_t i = tid; i < ncand; i += kRThreads) {
+            const uint2 c = sh.cand[i];
+            const uint32_t word = sh.kept[c.y >> 5], bit = 1u << (c.y & 31);
+            if (word & bit) {
+                const uint32_t slot = sh.wpos[c.y >> 5] + (uint32_t)__popc(word & (bit - 1u));
+                if (slot < (uint32_t)k) {
+                    oi[slot] = (int32_t)c.y;
+                    if (os) os[slot] = __uint_as_float(c.x);
+                }
+            }
+        }
+    } else {
+        uint32_t p = pos, word = kw;
+        while (word) {
+            const int b = __ffs(word) - 1;
+            word &= word - 1u;
+            const int e = 32 * tid + b;
+            if (p < (uint32_t)k) {
+                oi[p] = e;
+                if (os) os[p] = sc[e];
+            }
+            ++p;
+        }
+    }
+}
+
 // Group size for the group-bounded selection (0: not used): a power of two up to kGMaxG with
 // at most kGMaxGroups groups in the longest row, and preferably at least 4k of them.
 // Rows that fit the LDS staging of the one-workgroup bitmap selection are faster there.
@@ -1475,6 +1889,13 @@ int launch_topk(const float* scores, int64_t ld, int64_t batch, int64_t T, int64
         return 0;
     }
     const dim3 grid((unsigned)rows), block(kThreads);
+    // the shortest visible row is that of each sequence's first query
+    int64_t nv_min = (q_pos0 + 1) / m;
+    if (nv_min > N) nv_min = N;
+    if (rows < 256 && nv_max > kShortRow && nv_max <= kRRow && nv_min >= 8 * (int64_t)k) {
+        hipLaunchKernelGGL(topk_regs, grid, dim3(kRThreads), 0, stream, scores, ld, T, q_pos0, N, m, k, idx, sel);
+        return 0;
+    }
     if (nv_max <= kShortRow)   // short rows (prefill): small workgroups, several rows per CU
         hipLaunchKernelGGL((topk_bitmap<true, kShortThreads, kShortRow, 2 * kShortThreads>), grid, dim3(kShortThreads),
                            0, stream, scores, ld, T, q_pos0, N, m, k, chunk_mm, n_chunk_mm, idx, sel);

@@ -153,7 +153,11 @@ DECODE_TOPK_CASES = [  # batch, T, q_pos0, N, k, levels, zero-key fraction
     (1, 2, 4 * 50000, 50000, 1024, 3, 0.99),      # the cut falls in a tie of ~49K zero scores
     (1, 1, 4 * 36000, 36000, 512, 1, 0.0),        # every score equal
     (3, 1, 4 * 5000, 5000, 1024, 4, 0.0),         # groups of one score
-    (2, 2, 4 * 20000 - 5, 20000, 1024, 3, 0.0),   # groups of four
+    (2, 2, 4 * 20000 - 5, 20000, 1024, 3, 0.0),   # register-staged rows, ragged tails
+    (2, 1, 4 * 32768, 32768, 1024, 6, 0.0),       # the 128K decode shape: b2 ranked in one wave
+    (1, 2, 4 * 30000, 30000, 1024, 3, 0.99),      # register-staged, heavy ties: select over the row
+    (1, 3, 4 * 30000 - 6, 30000, 2048, 2, 0.0),   # register-staged, 100-170 members of b2
+    (1, 1, 4 * 32768, 32768, 1024, 1, 0.0),       # register-staged, every score equal
     (1, 3, 4 * 100000 - 3, 100000, 2048, 6, 0.0),
     (1, 1, 4 * 262144, 262144, 1024, 8, 0.0),     # the longest row the group maxima serve
     (1, 1, 4 * 300000, 300000, 1024, 8, 0.0),     # longer: the multi-workgroup selection
@@ -162,10 +166,11 @@ DECODE_TOPK_CASES = [  # batch, T, q_pos0, N, k, levels, zero-key fraction
 
 @pytest.mark.parametrize("case", DECODE_TOPK_CASES, ids=lambda c: "b%d_T%d_p%d_N%d_k%d_l%d_z%g" % c)
 def test_topk_decode_shapes_bit_exact(case):
-    # decode-shaped calls (fp8 indexer, T < 4): rows that fit LDS take the one-workgroup
-    # bitmap selection, longer ones up to 262144 entries the indexer's group maxima, longer
-    # still per-chunk ranges and several workgroups per row; integer-valued fp8 inputs keep
-    # every score exact
+    # decode-shaped calls (fp8 indexer, T < 4): rows of up to 32768 entries (at least 8k) take
+    # the register-staged selection, other rows that fit LDS the one-workgroup bitmap
+    # selection, longer ones up to 262144 entries the indexer's group maxima, longer still
+    # per-chunk ranges and several workgroups per row; integer-valued fp8 inputs keep every
+    # score exact
     batch, T, p0, N, k, levels, zfrac = case
     H, cI, m = 64, 128, 4
     say(f"csa_index_topk multi-workgroup case {case}")
