@@ -185,9 +185,13 @@ index_scores_mfma(const void* __restrict__ qI, const float* __restrict__ w, cons
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int g = lane >> 5, n = lane & 31;
     const int64_t groups = (T + TOK - 1) / TOK;
+    // XCD-aware order: workgroups are dealt round-robin over the 8 XCDs, so unit u runs on XCD
+    // u % 8; every chunk of row group bg goes to XCD bg % 8, whose L2 then holds the whole
+    // score row for the selection that reads it next
     const int64_t unit = blockIdx.x;
-    const int chunk = (int)(unit % chunks);
-    const int64_t bg = unit / chunks;
+    const int64_t slot = unit / 8;
+    const int chunk = (int)(slot % chunks);
+    const int64_t bg = (slot / chunks) * 8 + unit % 8;
     const int64_t b = bg / groups, tg = bg - b * groups;
     const int64_t t = TOK == 1 ? tg : tg * TOK + wid;
     if (b >= batch || t >= T) return;
@@ -464,7 +468,7 @@ int launch_mfma(const void* qI, const float* w, const void* kI, int64_t batch, i
         int cb = (int)(((total_blk + target - 1) / target + 3) / 4 * 4);
         if (cb < 4) cb = 4;
         const int chunks = (int)((nblk + cb - 1) / cb);
-        const int64_t grid = batch * T * chunks;
+        const int64_t grid = (batch * T + 7) / 8 * 8 * chunks;   // row groups padded to whole XCD rounds
         if (grid > 0x7fffffffLL) return -2;
         hipLaunchKernelGGL((index_scores_mfma<DT, MB, 1>), dim3((unsigned)grid), dim3(256), 0, stream, qI, w, kI, batch,
                            T, q_pos0, N, m, scores, ld, write_invisible ? 1 : 0, chunks, cb, dec);

@@ -898,9 +898,12 @@ __global__ void __launch_bounds__(kCombWaves * kWave)
 mqa_combine(const uint16_t* __restrict__ part, const float* __restrict__ part_ml, int64_t rows, int H, int ks_count,
             uint16_t* __restrict__ out) {
     constexpr int kCombGroup = CG;
-    const int64_t rh = (int64_t)blockIdx.x * kCombWaves + (threadIdx.x >> 6);   // row * H + head
-    if (rh >= rows * H) return;
-    const int64_t row = rh / H, head = rh % H;
+    // XCD-aware order (as the attention kernel's): row r on XCD r % 8, whose L2 holds the
+    // row's partials; H / kCombWaves workgroups per row (H % 64 == 0 on this path)
+    const int64_t per_row = H / kCombWaves, x = blockIdx.x, slot = x / 8;
+    const int64_t row = (slot / per_row) * 8 + x % 8;
+    const int64_t head = (slot % per_row) * kCombWaves + (threadIdx.x >> 6);
+    if (row >= rows) return;
     const int lane = threadIdx.x & 63;
     const int64_t prow0 = row * ks_count * H + head;   // partial row of range j: prow0 + j * H
     float M = -INFINITY, L = 0.f;
@@ -940,7 +943,7 @@ mqa_combine(const uint16_t* __restrict__ part, const float* __restrict__ part_ml
     const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] *= inv;
-    store8<DT_BF16>(out, rh * kMC + 8 * lane, o);
+    store8<DT_BF16>(out, (row * H + head) * kMC + 8 * lane, o);
 }
 
 // Key ranges per row: each range's key ids fit the LDS list; then, while the chip (two
@@ -988,7 +991,7 @@ int launch_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t
                                static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx, rows, T, N, H,
                                k, ks, kps, sl2, (int64_t)0, 1, static_cast<uint16_t*>(out), part, part_ml);
         if (ks > 1) {
-            const dim3 cgrid((unsigned)((rows * H + kCombWaves - 1) / kCombWaves)), cblock(kCombWaves * kWave);
+            const dim3 cgrid((unsigned)((rows + 7) / 8 * 8 * (H / kCombWaves))), cblock(kCombWaves * kWave);
             if (ks <= 4)
                 hipLaunchKernelGGL(mqa_combine<4>, cgrid, cblock, 0, stream, part, part_ml, rows, H, ks,
                                    static_cast<uint16_t*>(out));
