@@ -690,7 +690,7 @@ mqa_sparse_ws(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
         // (the gather of a later block into `nxt` is issued row by row between the matrix
         // instructions: its address work and the memory pipeline's intake then overlap them)
         static_assert(kMC / 32 == 2 * kMLoadsPerBlk, "one gathered row every second step of the scores");
-        auto s_phase = [&](int blk, const uint8_t* st, int par, int gblk, uint8_t* nxt) {
+        auto s_phase = [&](int blk, const uint8_t* st, int par, int gblk, uint8_t* nxt) __attribute__((always_inline)) {
             const int gid = gather_ids(gblk);
             const uint32_t vg = vmask[blk] >> (4 * g);
             constexpr int kSD = 8;
@@ -760,19 +760,47 @@ mqa_sparse_ws(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
         // step j < nblk: barrier j, gather block j+2 into the buffer block j-2 used (its
         // scores, then its values, are done by now), scores of block j, then wait until block
         // j+1 is staged; every step issues the same loads (no data-dependent branch inside)
-        auto step = [&](int j, const uint8_t* cur, uint8_t* nxt) {
+        auto step = [&](int j, const uint8_t* cur, uint8_t* nxt) __attribute__((always_inline)) {
             lds_barrier();
             s_phase(j, cur, j & 1, j + 2, nxt);
             wait_vmcnt<kMLoadsPerBlk>();
         };
-        for (int j = 0; j < nblk; j += 4) {
-            step(j, stage_a, stage_c);
-            if (j + 1 >= nblk) break;
-            step(j + 1, stage_b, stage_d);
-            if (j + 2 >= nblk) break;
-            step(j + 2, stage_c, stage_a);
-            if (j + 3 >= nblk) break;
-            step(j + 3, stage_d, stage_b);
+        // The first 8 blocks (all of them in decode splits) run as nested straight-line steps:
+        // where control flow merges (a loop back-edge, the join after an early exit) the
+        // compiler no longer knows which buffer each in-flight gather writes, and would wait
+        // for every gather (the one of block j+2 too) before the next block's first read.
+        if (nblk > 0) {
+            step(0, stage_a, stage_c);
+            if (nblk > 1) {
+                step(1, stage_b, stage_d);
+                if (nblk > 2) {
+                    step(2, stage_c, stage_a);
+                    if (nblk > 3) {
+                        step(3, stage_d, stage_b);
+                        if (nblk > 4) {
+                            step(4, stage_a, stage_c);
+                            if (nblk > 5) {
+                                step(5, stage_b, stage_d);
+                                if (nblk > 6) {
+                                    step(6, stage_c, stage_a);
+                                    if (nblk > 7) {
+                                        step(7, stage_d, stage_b);
+                                        for (int j = 8; j < nblk; j += 4) {
+                                            step(j, stage_a, stage_c);
+                                            if (j + 1 >= nblk) break;
+                                            step(j + 1, stage_b, stage_d);
+                                            if (j + 2 >= nblk) break;
+                                            step(j + 2, stage_c, stage_a);
+                                            if (j + 3 >= nblk) break;
+                                            step(j + 3, stage_d, stage_b);
+                                        }
+                                    }
+                                }
+                            }
+                        }
+                    }
+                }
+            }
         }
         lds_barrier();     // barrier nblk: the value waves take the last block
         wait_vmcnt<0>();   // the loads past the last block, before the buffers are reused
