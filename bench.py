@@ -29,8 +29,8 @@ sys.path.insert(0, ROOT)
 METRIC = "CSA query tokens/s (compress+index+top-k+MQA) at 128K ctx; % of roofline"
 HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
 MFMA_PEAK = {"bf16": 2.5e15, "fp8": 5.0e15}
-DT_BYTES = {0: 4, 1: 2, 2: 1}
-DT_NAME = {0: "f32", 1: "bf16", 2: "fp8_e4m3"}
+DT_BYTES = {0: 4, 1: 2, 2: 1, 3: 17 / 32}   # MXFP4: a 4-bit value plus a 1-byte scale per 32
+DT_NAME = {0: "f32", 1: "bf16", 2: "fp8_e4m3", 3: "mxfp4"}
 
 
 def log(*a):
@@ -107,7 +107,12 @@ def _cpu_sample(cfg, host):
     t0 = time.perf_counter()
     if cfg.kind == "csa_decode":
         nseq = cfg.batch
-        sub = {k: host[k][:nseq] for k in ("kv", "kI", "q", "qI", "w")}
+        sub = {k: host[k][:nseq] for k in ("kv", "q", "w")}
+        if cfg.qk_dt == 3:   # MXFP4 storage: the oracle decodes it (shape from the config)
+            sub["qI"] = oracle.decode_mxfp4(host["qI"], (cfg.batch, cfg.T, cfg.H_I, cfg.c_I))
+            sub["kI"] = oracle.decode_mxfp4(host["kI"], (cfg.batch, cfg.N, cfg.c_I))
+        else:
+            sub["qI"], sub["kI"] = host["qI"][:nseq], host["kI"][:nseq]
         sc = oracle.index_scores(sub["qI"], sub["w"], sub["kI"], cfg.m, q_pos0=cfg.q_pos0, qk_dtype=cfg.qk_dt)
         idx, _ = oracle.topk(sc, cfg.m, cfg.k, q_pos0=cfg.q_pos0)
         oracle.sparse_mqa(sub["q"], sub["kv"], idx, cfg.scale, dtype=cfg.dt)
@@ -178,7 +183,7 @@ def main():
         t = torch.from_numpy(v)
         if sh[k][1] == 1:
             t = t.view(torch.bfloat16)
-        dev[k] = t.cuda()
+        dev[k] = csa.MXFP4(t.cuda(), sh[k][0]) if sh[k][1] == 3 else t.cuda()
     torch.cuda.synchronize()
     log("[bench] inputs resident on the GPU")
 
@@ -301,7 +306,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.qk_dt != 2 else "bf16+fp8",
+        "dtype": {2: "bf16+fp8", 3: "bf16+mxfp4"}.get(cfg.qk_dt, "bf16"),
         "data": "synthetic (seeded SplitMix64 normals/uniforms; no dataset)",
         "config": {"workload": cfg.name, "batch": cfg.batch, "query_tokens_per_seq": cfg.T, "q_pos0": cfg.q_pos0,
                    "entries": cfg.N, "c": cfg.c, "heads": cfg.H, "H_I": cfg.H_I, "c_I": cfg.c_I, "k": cfg.k,

@@ -40,7 +40,15 @@
 extern "C" {
 #endif
 
-typedef enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3 = 2 } csa_dtype;
+/*
+ * CSA_MXFP4 (indexer q / keys only; [N] §2.4: the indexer's QK activations are stored,
+ * loaded and multiplied in MXFP4): the OCP Microscaling Formats v1.0 MXFP4 — blocks of 32
+ * consecutive values of a row share one E8M0 scale (2^(s-127), s = 255 is NaN), each value
+ * is E2M1.  A tensor of R rows of c values (c % 32 == 0) is one buffer: all rows' element
+ * bytes first, c/2 per row with value 2i in the low nibble of byte i and 2i+1 in the high
+ * nibble, then all rows' scales, c/32 bytes per row (R * (c/2 + c/32) bytes in all).
+ */
+typedef enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3 = 2, CSA_MXFP4 = 3 } csa_dtype;
 
 typedef enum {
     CSA_OK = 0,
@@ -102,7 +110,9 @@ size_t csa_index_topk_workspace_size(int64_t batch, int64_t T, int64_t N, int H_
  *     ReLU(x) = x > 0 ? x : +0), no scale factor.
  * Then keeps the min(k, |visible|) entries with the highest score, ties broken toward the
  * LOWER entry index, and writes them in ASCENDING entry order, padded with -1.
- *   qI : [batch, T, H_I, c_I], kI : [batch, N, c_I], both dtype qk_t (F32, BF16 or FP8_E4M3)
+ *   qI : [batch, T, H_I, c_I], kI : [batch, N, c_I], both dtype qk_t (F32, BF16, FP8_E4M3,
+ *        or MXFP4 in the layout described at csa_dtype: rows of c_I values, batch*T*H_I
+ *        rows in qI and batch*N rows in kI)
  *   w  : [batch, T, H_I] float32
  *   idx        : [batch, T, k] int32 out
  *   sel_scores : [batch, T, k] float32 out, or NULL: the score of each selected entry
@@ -111,7 +121,8 @@ size_t csa_index_topk_workspace_size(int64_t batch, int64_t T, int64_t N, int H_
  *                16-byte aligned; contents on entry are ignored.
  *   m          : CSA compression ratio (for the visibility rule).
  * Limits: c_I % 8 == 0, c_I <= CSA_MAX_WIDTH, 1 <= H_I <= CSA_MAX_HEADS, 1 <= k <=
- * CSA_MAX_TOPK, N < 2^31.
+ * CSA_MAX_TOPK, N < 2^31.  MXFP4 runs on the matrix-core decode kernel only: T < 4,
+ * c_I = 128, H_I = 32 or 64 (else CSA_ERR_UNSUPPORTED); its scales must not be 255 (NaN).
  */
 int csa_index_topk(const void* qI, const float* w, const void* kI, int64_t batch, int64_t T, int64_t q_pos0,
                    int64_t N, int H_I, int c_I, int m, int k, csa_dtype qk_t, int32_t* idx, float* sel_scores,

@@ -16,7 +16,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "_build", "libcsa.so")
 
-CSA_F32, CSA_BF16, CSA_FP8_E4M3 = 0, 1, 2
+CSA_F32, CSA_BF16, CSA_FP8_E4M3, CSA_MXFP4 = 0, 1, 2, 3
 STATUS = {0: "CSA_OK", -1: "CSA_ERR_INVALID_ARG", -2: "CSA_ERR_UNSUPPORTED", -3: "CSA_ERR_WORKSPACE",
           -4: "CSA_ERR_HIP"}
 
@@ -76,6 +76,32 @@ def _dt(x: torch.Tensor) -> int:
 
 
 _TORCH_DT = {CSA_F32: torch.float32, CSA_BF16: torch.bfloat16}
+
+
+class MXFP4:
+    """An indexer operand in the library's MXFP4 storage (csa_dtype CSA_MXFP4): `data` is the
+    flat uint8 device buffer (the E2M1 element bytes of every row, then every row's E8M0
+    scales), `shape` the logical shape whose last dimension is the row length."""
+
+    def __init__(self, data: torch.Tensor, shape):
+        self.data = data
+        self.shape = tuple(int(d) for d in shape)
+        c = self.shape[-1]
+        rows = 1
+        for d in self.shape[:-1]:
+            rows *= d
+        if data.dtype != torch.uint8 or c % 32 != 0 or data.numel() != rows * (c // 2 + c // 32):
+            raise ValueError(f"an MXFP4 buffer of logical shape {self.shape} holds {rows * (c // 2 + c // 32)} bytes")
+
+
+def _qk(qI, kI):
+    """(q tensor, k tensor, q shape, k shape, csa dtype) of the indexer operands."""
+    if isinstance(qI, MXFP4) or isinstance(kI, MXFP4):
+        if not (isinstance(qI, MXFP4) and isinstance(kI, MXFP4)):
+            raise TypeError("qI and kI must both be MXFP4")
+        return qI.data, kI.data, qI.shape, kI.shape, CSA_MXFP4
+    assert _dt(qI) == _dt(kI)
+    return qI, kI, tuple(qI.shape), tuple(kI.shape), _dt(qI)
 
 
 def _dev(*ts):
@@ -143,31 +169,33 @@ def workspace_for(batch, T, N, H_I, k, device) -> torch.Tensor:
 
 def csa_index_topk(qI, w, kI, q_pos0: int, m: int, k: int, idx=None, sel_scores=None, workspace=None,
                    want_scores: bool = True):
-    """qI [batch, T, H_I, c_I], w [batch, T, H_I] fp32, kI [batch, N, c_I] -> (idx, sel_scores)."""
-    dev = _dev(qI, w, kI, idx, sel_scores, workspace)
-    batch, T, H_I, c_I = qI.shape
-    N = kI.shape[1]
-    assert kI.shape == (batch, N, c_I) and w.shape == (batch, T, H_I) and w.dtype == torch.float32
-    assert _dt(qI) == _dt(kI)
+    """qI [batch, T, H_I, c_I], w [batch, T, H_I] fp32, kI [batch, N, c_I] -> (idx, sel_scores).
+    qI and kI: tensors of one dtype (f32, bf16, e4m3 as uint8) or both MXFP4."""
+    qt, kt, qs, ks, qk_dt = _qk(qI, kI)
+    dev = _dev(qt, w, kt, idx, sel_scores, workspace)
+    batch, T, H_I, c_I = qs
+    N = ks[1]
+    assert ks == (batch, N, c_I) and w.shape == (batch, T, H_I) and w.dtype == torch.float32
     if idx is None:
         idx = torch.empty((batch, T, k), dtype=torch.int32, device=dev)
     if sel_scores is None and want_scores:
         sel_scores = torch.empty((batch, T, k), dtype=torch.float32, device=dev)
     if workspace is None:
         workspace = workspace_for(batch, T, N, H_I, k, dev)
-    _check("csa_index_topk", lib.csa_index_topk(_p(qI), _p(w), _p(kI), batch, T, q_pos0, N, H_I, c_I, m, k, _dt(qI),
+    _check("csa_index_topk", lib.csa_index_topk(_p(qt), _p(w), _p(kt), batch, T, q_pos0, N, H_I, c_I, m, k, qk_dt,
                                                 _p(idx), _p(sel_scores), _p(workspace), workspace.numel(),
                                                 _stream(dev)))
     return idx, sel_scores
 
 
 def csa_index_scores(qI, w, kI, q_pos0: int, m: int, scores=None):
-    dev = _dev(qI, w, kI, scores)
-    batch, T, H_I, c_I = qI.shape
-    N = kI.shape[1]
+    qt, kt, qs, ks, qk_dt = _qk(qI, kI)
+    dev = _dev(qt, w, kt, scores)
+    batch, T, H_I, c_I = qs
+    N = ks[1]
     if scores is None:
         scores = torch.empty((batch, T, N), dtype=torch.float32, device=dev)
-    _check("csa_index_scores", lib.csa_index_scores(_p(qI), _p(w), _p(kI), batch, T, q_pos0, N, H_I, c_I, m, _dt(qI),
+    _check("csa_index_scores", lib.csa_index_scores(_p(qt), _p(w), _p(kt), batch, T, q_pos0, N, H_I, c_I, m, qk_dt,
                                                     _p(scores), _stream(dev)))
     return scores
 

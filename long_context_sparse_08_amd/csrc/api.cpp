@@ -32,8 +32,10 @@ int check_indexer(const void* qI, const float* w, const void* kI, int64_t batch,
                   int H_I, int c_I, int m, csa_dtype qk_t) {
     if (batch < 0 || T < 0 || N < 0 || q_pos0 < 0) return CSA_ERR_INVALID_ARG;
     if (m < 1 || H_I < 1 || c_I < 1) return CSA_ERR_INVALID_ARG;
-    if (qk_t != CSA_F32 && qk_t != CSA_BF16 && qk_t != CSA_FP8_E4M3) return CSA_ERR_UNSUPPORTED;
+    if (qk_t != CSA_F32 && qk_t != CSA_BF16 && qk_t != CSA_FP8_E4M3 && qk_t != CSA_MXFP4) return CSA_ERR_UNSUPPORTED;
     if (!width_ok(c_I) || H_I > CSA_MAX_HEADS || m > CSA_MAX_RATIO) return CSA_ERR_UNSUPPORTED;
+    // MXFP4: the matrix-core decode kernel only (c_I = 128: four scale blocks per row)
+    if (qk_t == CSA_MXFP4 && (T >= 4 || c_I != 128 || (H_I != 32 && H_I != 64))) return CSA_ERR_UNSUPPORTED;
     if (N >= (int64_t(1) << 31)) return CSA_ERR_UNSUPPORTED;
     if (batch * T == 0) return CSA_OK;   // nothing to compute: pointers may be NULL
     if (!qI || !w || (N > 0 && !kI)) return CSA_ERR_INVALID_ARG;

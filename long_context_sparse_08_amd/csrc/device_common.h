@@ -9,7 +9,7 @@
 
 namespace csa {
 
-enum Dt : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
+enum Dt : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2, DT_MXFP4 = 3 };
 
 constexpr int kWave = 64;
 constexpr float kLog2e = 1.4426950408889634f;

@@ -131,6 +131,30 @@ struct IdxOps<DT_FP8> {
     }
 };
 
+// MXFP4 (OCP MX: E2M1 values, one E8M0 scale per 32 consecutive values of a row): the same
+// instruction with both operands in format 4 (E2M1, 16 bytes = 32 values per lane) and the
+// block scales as its per-lane scale operands.  A lane's half row g (values 64g .. 64g+63)
+// feeds 32 values to each of the two steps j, which are scale blocks 2g + j; the loader
+// shifts the row's 4 scale bytes so that byte j is block 2g + j (the step selects byte j).
+template <>
+struct IdxOps<DT_MXFP4> {
+    static constexpr int kLoads = 2;      // 16-byte loads per half row (64 E2M1 values)
+    struct Frag {
+        uint4 v[kLoads];
+        uint32_t s;                       // the two scale bytes of this half row, bytes 0 and 1
+    };
+    static __device__ __forceinline__ f32x16 mma(const Frag& a, const Frag& b, f32x16 acc) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const i32x8 av = {(int)a.v[j].x, (int)a.v[j].y, (int)a.v[j].z, (int)a.v[j].w, 0, 0, 0, 0};
+            const i32x8 bv = {(int)b.v[j].x, (int)b.v[j].y, (int)b.v[j].z, (int)b.v[j].w, 0, 0, 0, 0};
+            acc = j == 0 ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 4, 4, 0, (int)a.s, 0, (int)b.s)
+                         : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 4, 4, 1, (int)a.s, 1, (int)b.s);
+        }
+        return acc;
+    }
+};
+
 template <>
 struct IdxOps<DT_BF16> {
     static constexpr int kLoads = 8;      // 16-byte loads per half row (64 bf16)
@@ -147,14 +171,25 @@ struct IdxOps<DT_BF16> {
     }
 };
 
+// Half row g of `row` of a [rows_total, 128] operand (rows_total: MXFP4's scales follow the
+// element bytes of all rows)
 template <int DT>
 __device__ __forceinline__ void load_half_row(const void* __restrict__ base, int64_t row, int g,
-                                              typename IdxOps<DT>::Frag& f) {
+                                              typename IdxOps<DT>::Frag& f, int64_t rows_total) {
     using O = IdxOps<DT>;
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(base) +
-                                                    (row * kMfmaCI + g * (kMfmaCI / 2)) * O::kEsz);
+    const uint8_t* b = static_cast<const uint8_t*>(base);
+    if constexpr (DT == DT_MXFP4) {
+        const uint4* p = reinterpret_cast<const uint4*>(b + row * (kMfmaCI / 2) + g * (kMfmaCI / 4));
 #pragma unroll
-    for (int i = 0; i < O::kLoads; ++i) f.v[i] = p[i];
+        for (int i = 0; i < O::kLoads; ++i) f.v[i] = p[i];
+        const uint32_t sw = *reinterpret_cast<const uint32_t*>(b + rows_total * (kMfmaCI / 2) + row * (kMfmaCI / 32));
+        f.s = sw >> (16 * g);
+    } else {
+        (void)rows_total;
+        const uint4* p = reinterpret_cast<const uint4*>(b + (row * kMfmaCI + g * (kMfmaCI / 2)) * O::kEsz);
+#pragma unroll
+        for (int i = 0; i < O::kLoads; ++i) f.v[i] = p[i];
+    }
 }
 
 // Outputs of the decode-shaped kernel for the selection (each optional): per-chunk (min, max)
@@ -213,7 +248,7 @@ index_scores_mfma(const void* __restrict__ qI, const float* __restrict__ w, cons
     float wv[MB][16];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-        load_half_row<DT>(qI, row * H + 32 * mb + n, g, qa[mb]);
+        load_half_row<DT>(qI, row * H + 32 * mb + n, g, qa[mb], batch * T * H);
         // accumulator row r of this lane is head 8*(r/4) + 4*g + r%4: four runs of 4 heads
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
@@ -245,7 +280,7 @@ index_scores_mfma(const void* __restrict__ qI, const float* __restrict__ w, cons
     // unconditionally, clamped to this wave's last visible block, so the waits stay static
     auto load_blk = [&](typename O::Frag& f, int i) {
         const int64_t bb = blk0 + first + (int64_t)min(i, nb - 1) * step;
-        load_half_row<DT>(kI, kbase + min(bb * 32 + n, N - 1), g, f);
+        load_half_row<DT>(kI, kbase + min(bb * 32 + n, N - 1), g, f, batch * N);
     };
     auto compute_blk = [&](const typename O::Frag& cur, int i) {
         const int64_t s = (blk0 + first + (int64_t)i * step) * 32 + n;
@@ -367,7 +402,7 @@ index_scores_prefill(const void* __restrict__ qI, const float* __restrict__ w, c
     float wv[MB][16];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-        load_half_row<DT>(qI, row * H + 32 * mb + n, g, qa[mb]);
+        load_half_row<DT>(qI, row * H + 32 * mb + n, g, qa[mb], batch * T * H);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
             const float4 w4 = *reinterpret_cast<const float4*>(w + row * H + 32 * mb + 8 * q4 + 4 * g);
@@ -437,7 +472,7 @@ index_scores_prefill(const void* __restrict__ qI, const float* __restrict__ w, c
 }
 
 bool mfma_shape(int H_I, int c_I, int qk_t) {
-    return c_I == kMfmaCI && (H_I == 32 || H_I == 64) && (qk_t == DT_FP8 || qk_t == DT_BF16);
+    return c_I == kMfmaCI && (H_I == 32 || H_I == 64) && (qk_t == DT_FP8 || qk_t == DT_BF16 || qk_t == DT_MXFP4);
 }
 
 // Decode: 32-entry blocks per workgroup chunk (a multiple of 4, at least 4) for total_blk
@@ -458,6 +493,8 @@ int launch_mfma(const void* qI, const float* w, const void* kI, int64_t batch, i
                 hipStream_t stream) {
     const int64_t nblk = (N + 31) / 32;
     if (T >= 4) {
+        if constexpr (DT == DT_MXFP4) return -2;   // (decode shapes only)
+        else {
         // prefill: 8 queries per workgroup share each staged key block.  Long chunks amortise
         // the workgroup's q loads (128 KB); rows are cut into chunks only as far as needed to
         // keep ~1024 workgroups (four rounds of one per CU)
@@ -471,6 +508,7 @@ int launch_mfma(const void* qI, const float* w, const void* kI, int64_t batch, i
         hipLaunchKernelGGL((index_scores_prefill<DT, MB>), dim3((unsigned)grid), dim3(kPfWaves * kWave), 0, stream, qI,
                            w, kI, batch, T, q_pos0, N, m, scores, ld, write_invisible ? 1 : 0, chunks, cb);
         if (n_chunk_mm) *n_chunk_mm = 0;
+        }
     } else {
         const int cb = decode_chunk_blocks(batch * T * nblk);
         const int chunks = (int)((nblk + cb - 1) / cb);
@@ -504,6 +542,11 @@ int launch_index_scores(const void* qI, const float* w, const void* kI, int64_t 
     if (gmax != nullptr && (G < 1 || G > 32 || (G & (G - 1)) != 0)) return -2;
     const DecodeOut dec{chunk_mm, zero, zero_words, gmax, gmax ? G : 0, gld};
     if (mfma_shape(H_I, c_I, qk_t)) {
+        if (qk_t == DT_MXFP4)
+            return H_I == 64 ? launch_mfma<DT_MXFP4, 2>(qI, w, kI, batch, T, q_pos0, N, m, scores, ld, write_invisible,
+                                                        dec, n_chunk_mm, stream)
+                             : launch_mfma<DT_MXFP4, 1>(qI, w, kI, batch, T, q_pos0, N, m, scores, ld, write_invisible,
+                                                        dec, n_chunk_mm, stream);
         if (qk_t == DT_FP8)
             return H_I == 64 ? launch_mfma<DT_FP8, 2>(qI, w, kI, batch, T, q_pos0, N, m, scores, ld, write_invisible,
                                                       dec, n_chunk_mm, stream)

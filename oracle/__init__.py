@@ -21,7 +21,7 @@ SRC = os.path.join(HERE, "csa_oracle.c")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(BUILD_DIR, "libcsa_oracle.so")
 
-F32, BF16, FP8 = 0, 1, 2
+F32, BF16, FP8, MXFP4 = 0, 1, 2, 3
 KEEP_DOUBLE = -1
 
 _lib = None
@@ -52,6 +52,7 @@ def lib():
         sig = {
             "oracle_num_threads": ([], I),
             "oracle_decode": ([P, I, I64, P], I),
+            "oracle_decode_mxfp4": ([P, I64, I, P], I),
             "oracle_round": ([P, I, I64], I),
             "oracle_csa_compress": ([P, P, P, P, P, P, I64, I64, I, I, I, P], None),
             "oracle_hca_compress": ([P, P, P, I64, I64, I, I, I, P], None),
@@ -84,6 +85,21 @@ def decode(a: np.ndarray, dtype: int) -> np.ndarray:
     out = np.empty(a.shape, dtype=np.float64)
     if lib().oracle_decode(_p(a), dtype, a.size, _p(out)) != 0:
         raise ValueError(f"bad dtype {dtype}")
+    return out
+
+
+def decode_mxfp4(buf: np.ndarray, shape) -> np.ndarray:
+    """MXFP4 storage (flat uint8: element bytes of every row, then the scales) of a tensor of
+    logical shape `shape` (rows of shape[-1] values) -> exact float64 of that shape."""
+    shape = tuple(int(d) for d in shape)
+    c = shape[-1]
+    rows = int(np.prod(shape[:-1]))
+    buf = np.ascontiguousarray(buf, dtype=np.uint8).reshape(-1)
+    if c % 32 != 0 or buf.size != rows * (c // 2 + c // 32):
+        raise ValueError(f"MXFP4 buffer of {buf.size} bytes does not hold shape {shape}")
+    out = np.empty(shape, dtype=np.float64)
+    if lib().oracle_decode_mxfp4(_p(buf), rows, c, _p(out)) != 0:
+        raise ValueError("bad MXFP4 shape")
     return out
 
 

@@ -74,6 +74,35 @@ static double decode_e4m3(uint8_t b) {
     return sign ? -v : v;
 }
 
+/* MXFP4 ([N] §2.4: the indexer's QK path runs in MXFP4; format: OCP Microscaling Formats
+ * v1.0 — blocks of 32 elements, E2M1 elements, one E8M0 scale per block).
+ * E2M1: 1 sign, 2 exponent bits (bias 1), 1 mantissa bit; exponent 0 is subnormal
+ * (mant * 2^-1), otherwise (1 + mant/2) * 2^(e-1).  E8M0: 2^(s-127), s = 255 is NaN. */
+static double decode_e2m1(unsigned nib) {
+    unsigned e = (nib >> 1) & 3u, mant = nib & 1u;
+    double v = e == 0 ? 0.5 * mant : ldexp(1.0 + 0.5 * mant, (int)e - 1);
+    return (nib & 8u) ? -v : v;
+}
+
+/* Storage of `rows` rows of c values: rows * c/2 element bytes (value 2i in the low nibble
+ * of byte i of its row, 2i+1 in the high nibble), then rows * c/32 scale bytes. */
+int oracle_decode_mxfp4(const uint8_t* buf, int64_t rows, int c, double* dst) {
+    int64_t r;
+    int j;
+    if (c % 32 != 0) return -1;
+    for (r = 0; r < rows; ++r) {
+        const uint8_t* el = buf + r * (c / 2);
+        const uint8_t* sc = buf + rows * (c / 2) + r * (c / 32);
+        for (j = 0; j < c; ++j) {
+            unsigned byte = el[j / 2];
+            unsigned nib = (j % 2 == 0) ? (byte & 15u) : (byte >> 4);
+            unsigned s = sc[j / 32];
+            dst[r * c + j] = s == 255u ? NAN : decode_e2m1(nib) * ldexp(1.0, (int)s - 127);
+        }
+    }
+    return 0;
+}
+
 /* Decode `count` stored values of type `dtype` into doubles (exact). */
 int oracle_decode(const void* src, int dtype, int64_t count, double* dst) {
     int64_t i;

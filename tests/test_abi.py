@@ -108,8 +108,14 @@ def test_index_topk_rejects_bad_arguments(L):
     assert call(k=4096) == UNSUPPORTED
     assert call(c_I=20) == UNSUPPORTED
     assert call(H_I=1000) == UNSUPPORTED
-    assert call(t=3) == UNSUPPORTED
+    assert call(t=4) == UNSUPPORTED
     assert call(N=1 << 31) == UNSUPPORTED
+    # MXFP4 (t = 3) runs on the matrix-core decode kernel only: T < 4, c_I = 128, H_I 32 or 64
+    assert call(t=3) == UNSUPPORTED                         # T = 8, c_I = 32, H_I = 2
+    assert call(t=3, T=1, c_I=128, H_I=64, ws=None, wsb=0) == WORKSPACE   # accepted up to the workspace
+    assert call(t=3, T=4, c_I=128, H_I=64) == UNSUPPORTED
+    assert call(t=3, T=1, c_I=96, H_I=64) == UNSUPPORTED
+    assert call(t=3, T=1, c_I=128, H_I=16) == UNSUPPORTED
     assert call(ws=None) == WORKSPACE
     assert call(wsb=need - 1) == WORKSPACE
     assert call(batch=0, wsb=L.csa_index_topk_workspace_size(0, 8, 64, 2, 8)) == OK

@@ -8,18 +8,32 @@ import numpy as np
 import pytest
 import torch
 
+import long_context_sparse_08_amd as csa
 import oracle
 from long_context_sparse_08_amd.pipeline import CsaDecode, CsaPrefill, HcaChunk
 from tests._util import (BF16, F32, FP8, assert_abs_close, assert_fp32_close, check_topk_recall, from_dev, say,
                          to_dev)
-from workloads import CONFIGS, make_inputs, shapes
+from workloads import CONFIGS, make_inputs, rng, shapes
 
 pytestmark = pytest.mark.gpu
 
 
 def upload(cfg, host):
     sh = shapes(cfg)
-    return {k: to_dev(v, sh[k][1]) for k, v in host.items()}
+    return {k: csa.MXFP4(torch.from_numpy(v).cuda(), sh[k][0]) if sh[k][1] == rng.MXFP4 else to_dev(v, sh[k][1])
+            for k, v in host.items()}
+
+
+def indexer_operands(cfg, h, seqs):
+    """qI, kI of sequences `seqs` for the oracle (MXFP4: their rows, decoded by the oracle)."""
+    if cfg.qk_dt != rng.MXFP4:
+        return h["qI"][seqs], h["kI"][seqs]
+    qrows, krows = cfg.T * cfg.H_I, cfg.N
+    q = [oracle.decode_mxfp4(rng.mxfp4_rows(h["qI"], cfg.batch * qrows, cfg.c_I, b * qrows, (b + 1) * qrows),
+                             (cfg.T, cfg.H_I, cfg.c_I)) for b in seqs]
+    k = [oracle.decode_mxfp4(rng.mxfp4_rows(h["kI"], cfg.batch * krows, cfg.c_I, b * krows, (b + 1) * krows),
+                             (cfg.N, cfg.c_I)) for b in seqs]
+    return np.stack(q), np.stack(k)
 
 
 def oracle_csa_front(cfg, h, rows):
@@ -90,7 +104,8 @@ def _decode_case(name, seqs):
     pipe = CsaDecode(upload(cfg, h), cfg.m, cfg.k, cfg.q_pos0)
     pipe.run()
     torch.cuda.synchronize()
-    sub = {k: h[k][seqs] for k in ("kv", "kI", "q", "qI", "w")}
+    sub = {k: h[k][seqs] for k in ("kv", "q", "w")}
+    sub["qI"], sub["kI"] = indexer_operands(cfg, h, seqs)
     sc = oracle.index_scores(sub["qI"], sub["w"], sub["kI"], cfg.m, q_pos0=cfg.q_pos0, qk_dtype=cfg.qk_dt)
     idx, sel = oracle.topk(sc, cfg.m, cfg.k, q_pos0=cfg.q_pos0)
     out = oracle.sparse_mqa(sub["q"], sub["kv"], idx, cfg.scale, dtype=cfg.dt)
@@ -101,11 +116,30 @@ def _decode_case(name, seqs):
     same = gidx == idx
     assert_abs_close(gsel[same], sel[same], 2e-2, "sel_scores where ids agree")
     assert_abs_close(from_dev(pipe.out)[seqs], out, 2e-2, "O")
+    return cfg, h, gidx
 
 
 @pytest.mark.timeout(900)
 def test_cfg2_csa_decode_128k_sampled():
     _decode_case("cfg2_csa_decode_128k", np.array([0, 7, 19, 31]))
+
+
+@pytest.mark.timeout(900)
+def test_cfg2_csa_decode_128k_mxfp4_sampled():
+    """The 128K decode with the indexer's q and keys in MXFP4 (same draws as the fp8 config).
+    Besides parity with the oracle on the MXFP4 values, reports how many of the fp8 decode's
+    oracle selection the MXFP4 selection keeps (context: the notes page quotes 99.7% recall for
+    bf16 scores; FP4 keys are coarser)."""
+    seqs = np.array([0, 13, 31])
+    cfg, h, gidx = _decode_case("cfg2_csa_decode_128k_mxfp4", seqs)
+    f8 = CONFIGS["cfg2_csa_decode_128k"]
+    h8 = make_inputs(f8, names=["qI", "kI", "w"])
+    sc8 = oracle.index_scores(h8["qI"][seqs], h8["w"][seqs], h8["kI"][seqs], f8.m, q_pos0=f8.q_pos0, qk_dtype=FP8)
+    idx8, _ = oracle.topk(sc8, f8.m, f8.k, q_pos0=f8.q_pos0)
+    a, b = gidx.reshape(-1, cfg.k), idx8.reshape(-1, f8.k)
+    recall = np.mean([len(set(a[r]) & set(b[r])) / f8.k for r in range(a.shape[0])])
+    say(f"  MXFP4 selection keeps {recall:.4f} of the fp8 selection")
+    assert recall > 0.5
 
 
 @pytest.mark.timeout(900)

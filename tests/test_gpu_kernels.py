@@ -186,6 +186,49 @@ def test_topk_decode_shapes_bit_exact(case):
     assert np.array_equal(sel, ref_sel.astype(np.float32).astype(np.float64))
 
 
+# ------------------------------------------------------------------------------ MXFP4 indexer
+def _mxfp4_exact(r, rows, c):
+    """MXFP4 storage (element bytes of every row, then the scales) of random E2M1 codes with
+    block scales 2^-1 or 2^0: every value is a multiple of 1/4 of magnitude <= 6, so every
+    product, dot product and weighted head sum below is exact in fp32."""
+    codes = r.randint(0, 16, size=(rows, c)).astype(np.uint8)
+    scales = r.randint(126, 128, size=(rows, c // 32)).astype(np.uint8)
+    return np.concatenate([(codes[:, 0::2] | (codes[:, 1::2] << 4)).reshape(-1), scales.reshape(-1)]).astype(np.uint8)
+
+
+MXFP4_CASES = [  # batch, T, q_pos0, N, H_I, k
+    (2, 1, 4 * 3000, 3000, 64, 256),
+    (1, 3, 4 * 5000 - 2, 5000, 32, 512),      # rows of different lengths, 32 indexer heads
+    (3, 2, 4 * 1000 + 1, 1003, 64, 100),      # a ragged last key block
+    (1, 1, 4 * 20000, 20000, 64, 1024),       # register-staged selection
+    (1, 1, 4 * 40000, 40000, 64, 1024),       # group maxima from the MXFP4 indexer
+]
+
+
+@pytest.mark.parametrize("case", MXFP4_CASES, ids=lambda c: "b%d_T%d_p%d_N%d_H%d_k%d" % c)
+def test_index_mxfp4_scores_and_topk_bit_exact(case):
+    """MXFP4 q and keys on the matrix-core decode indexer: scores equal the oracle's on the
+    decoded values, and the selection is bit-exact."""
+    batch, T, p0, N, H_I, k = case
+    cI, m = 128, 4
+    say(f"MXFP4 indexer case {case}")
+    r = np.random.RandomState(2100 + N)
+    q = _mxfp4_exact(r, batch * T * H_I, cI)
+    kk = _mxfp4_exact(r, batch * N, cI)
+    w = r.randint(0, 2, (batch, T, H_I)).astype(np.float32)
+    sc = oracle.index_scores(oracle.decode_mxfp4(q, (batch, T, H_I, cI)), w, oracle.decode_mxfp4(kk, (batch, N, cI)),
+                             m, q_pos0=p0)
+    ref_idx, ref_sel = oracle.topk(sc, m, k, q_pos0=p0)
+    qt = csa.MXFP4(torch.from_numpy(q).cuda(), (batch, T, H_I, cI))
+    kt = csa.MXFP4(torch.from_numpy(kk).cuda(), (batch, N, cI))
+    wt = to_dev(w, F32)
+    got = from_dev(csa.csa_index_scores(qt, wt, kt, p0, m))
+    assert np.array_equal(got, sc)
+    idx, sel = csa.csa_index_topk(qt, wt, kt, p0, m, k)
+    assert np.array_equal(from_dev(idx), ref_idx)
+    assert np.array_equal(from_dev(sel), ref_sel.astype(np.float32).astype(np.float64))
+
+
 def test_topk_bit_exact_random_fp32():
     batch, T, N, H, cI, m, k = 2, 200, 50, 2, 32, 4, 8
     sd = 900

@@ -40,6 +40,64 @@ def test_decode_e4m3_matches_torch_all_codes(orc):
     assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9
 
 
+# MXFP4 (the notes page's §2.4: the indexer's QK path in MXFP4): OCP Microscaling Formats
+# v1.0 — E2M1 elements (its table of values), one E8M0 scale per 32 elements.
+E2M1_SPEC = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]   # codes 0..7, the spec's FP4 E2M1 values
+
+
+def test_decode_mxfp4_elements_match_the_spec_table(orc):
+    # one row of 32 values holding all 16 codes twice, scale 2^0: code 8 + j is -(code j)
+    codes = np.concatenate([np.arange(16), np.arange(16)[::-1]]).astype(np.uint8)
+    buf = np.concatenate([(codes[0::2] | (codes[1::2] << 4)).astype(np.uint8), np.array([127], np.uint8)])
+    got = orc.decode_mxfp4(buf, (1, 32))[0]
+    want = np.array([E2M1_SPEC[c & 7] * (-1.0 if c & 8 else 1.0) for c in codes])
+    assert np.array_equal(got, want) and np.signbit(got[8]) and not np.signbit(got[0])
+
+
+def test_decode_mxfp4_scales_match_torch_e8m0(orc):
+    # element code 2 (1.0) everywhere: the decoded value is the block scale; 255 is NaN
+    scales = np.arange(256, dtype=np.uint8)
+    buf = np.concatenate([np.full(256 * 16, 0x22, np.uint8), scales])
+    got = orc.decode_mxfp4(buf, (256, 32))
+    ref = torch.from_numpy(scales).view(torch.float8_e8m0fnu).double().numpy()
+    assert np.array_equal(np.isnan(got[:, 0]), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], np.repeat(ref[ok, None], 32, axis=1))
+
+
+def test_decode_mxfp4_layout_nibbles_blocks_and_rows(orc):
+    # 3 rows of 64 values: value 2i in the low nibble of byte i, block b of row r uses scale
+    # byte r * 2 + b of the scale region that follows all rows' element bytes
+    r = R(7)
+    codes = r.randint(0, 16, size=(3, 64)).astype(np.uint8)
+    sc = r.randint(120, 135, size=(3, 2)).astype(np.uint8)
+    buf = np.concatenate([(codes[:, 0::2] | (codes[:, 1::2] << 4)).reshape(-1), sc.reshape(-1)]).astype(np.uint8)
+    got = orc.decode_mxfp4(buf, (3, 64))
+    for row in range(3):
+        for j in range(64):
+            c = codes[row, j]
+            v = E2M1_SPEC[c & 7] * (-1.0 if c & 8 else 1.0) * 2.0 ** (int(sc[row, j // 32]) - 127)
+            assert got[row, j] == v, (row, j)
+
+
+def test_mxfp4_quantizer_follows_the_mx_conversion_rule():
+    # the input generator's rounding to MXFP4 (storage only): scale 2^(floor(log2 amax) - 2),
+    # elements rounded to the nearest E2M1 value, ties to the even code, saturating at 6
+    x = np.zeros((2, 32), np.float32)
+    x[0, :6] = [0.1, -0.25, 1.3, 6.0, -7.9, 0.75]        # amax 7.9: scale 2^0
+    x[1, :4] = [1000.0, 250.0, -96.0, 31.0]               # amax 1000: floor(log2) 9 -> 2^7
+    buf = rng.f32_to_mxfp4(x)
+    assert list(buf[-2:]) == [127, 134]
+    v = rng.mxfp4_to_f32(buf, 2, 32)
+    assert list(v[0, :6]) == [0.0, -0.0, 1.5, 6.0, -6.0, 1.0]   # 0.75: tie 0.5 / 1.0 -> even code 2
+    # 1000/128 = 7.8 -> 6 (saturates); 250/128 -> 2; -96/128 = -0.75: tie -> even code 2 (1.0);
+    # 31/128 = 0.24 -> 0
+    assert list(v[1, :4]) == [768.0, 256.0, -128.0, 0.0]
+    # values already on the grid come back exactly
+    on = (np.array(E2M1_SPEC * 4, np.float32) * np.float32(2.0 ** -3)).reshape(1, 32)
+    assert np.array_equal(rng.mxfp4_to_f32(rng.f32_to_mxfp4(on), 1, 32), on)
+
+
 def test_round_bf16_matches_torch_and_ties_to_even(orc):
     x = (R(1).randn(50000) * np.exp(R(2).uniform(-30, 30, 50000))).astype(np.float32)
     ref = torch.from_numpy(x).to(torch.bfloat16).double().numpy()

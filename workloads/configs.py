@@ -17,7 +17,7 @@ import numpy as np
 
 from . import rng
 
-F32, BF16, FP8 = rng.F32, rng.BF16, rng.FP8
+F32, BF16, FP8, MXFP4 = rng.F32, rng.BF16, rng.FP8, rng.MXFP4
 
 # tensor ids, fixed forever (changing one changes every input)
 TID = {
@@ -71,6 +71,12 @@ CONFIGS = {
     "cfg4_csa_decode_1m": Config("cfg4_csa_decode_1m", "csa_decode", batch=8, dt=BF16, c=512, H=128,
                                  k=1024, m=4, H_I=64, c_I=128, qk_dt=FP8, T=1, q_pos0=1 << 20,
                                  N=262144, seed=1004),
+    # the decode at a 128K context with the indexer's q and keys in MXFP4 (the notes page's
+    # §2.4: the indexer's QK path in FP4); the same seed and draws as the fp8 decode, so its
+    # selection can be compared with that one
+    "cfg2_csa_decode_128k_mxfp4": Config("cfg2_csa_decode_128k_mxfp4", "csa_decode", batch=32, dt=BF16, c=512,
+                                         H=128, k=1024, m=4, H_I=64, c_I=128, qk_dt=MXFP4, T=1,
+                                         q_pos0=131072, N=32768, seed=1002),
 }
 ORDER = list(CONFIGS)
 

@@ -1,7 +1,7 @@
 """Seeded, counter-based synthetic inputs shared by the tests, the smoke check and the benchmark.
 
 This module draws random numbers and stores them in the storage dtypes the kernels read
-(fp32, bf16, OCP fp8 e4m3fn).  It holds none of the attention method's arithmetic: no
+(fp32, bf16, OCP fp8 e4m3fn, OCP MXFP4).  It holds none of the attention method's arithmetic: no
 softmax, no pooling, no scoring.  Both the HIP path and the CPU oracle receive the very
 bytes produced here.
 
@@ -19,7 +19,14 @@ Normals use the Box-Muller transform on the pair of uniforms drawn at counters 2
 
 Rounding to storage: float64 -> float32 (IEEE round-to-nearest-even), then
 float32 -> bf16 round-to-nearest-even on the bit pattern, or float32 -> e4m3fn
-round-to-nearest-even with saturation to +-448.
+round-to-nearest-even with saturation to +-448, or float32 -> MXFP4 (OCP Microscaling
+Formats v1.0: blocks of 32 consecutive values of a row share one E8M0 scale 2^X with
+X = floor(log2(max |v|)) - 2, the largest E2M1 exponent; each v / 2^X is rounded to the
+nearest E2M1 value, ties to the even code, saturating at +-6).
+
+MXFP4 storage of a tensor whose rows hold c values (c % 32 == 0): all rows' element bytes
+first, c/2 bytes per row with value 2i in the low nibble of byte i and 2i+1 in the high
+nibble, then all rows' scales, c/32 E8M0 bytes per row; one flat uint8 array.
 """
 from __future__ import annotations
 
@@ -33,8 +40,9 @@ _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
 
 # Storage dtype codes; the values match the C-ABI enum csa_dtype.
-F32, BF16, FP8 = 0, 1, 2
-DTYPE_NAMES = {F32: "f32", BF16: "bf16", FP8: "fp8_e4m3"}
+F32, BF16, FP8, MXFP4 = 0, 1, 2, 3
+DTYPE_NAMES = {F32: "f32", BF16: "bf16", FP8: "fp8_e4m3", MXFP4: "mxfp4"}
+MX_BLOCK = 32
 NP_STORAGE = {F32: np.float32, BF16: np.uint16, FP8: np.uint8}
 
 _CHUNK = 1 << 20
@@ -126,6 +134,56 @@ def e4m3_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return np.where(b & 0x80, -mag, mag).astype(np.float32)
 
 
+# E2M1 magnitudes by code 0..7 (1 sign, 2 exponent bits with bias 1, 1 mantissa bit;
+# exponent 0 is subnormal: 0.5 * mantissa)
+_E2M1_VALS = np.array([(m * 0.5) if e == 0 else (1 + m / 2) * 2.0 ** (e - 1) for e in range(4) for m in range(2)])
+
+
+def f32_to_mxfp4(x32: np.ndarray) -> np.ndarray:
+    """float32 [..., c] -> MXFP4 storage (flat uint8: element bytes of every row, then scales)."""
+    x = np.asarray(x32, dtype=np.float32).astype(np.float64)
+    c = x.shape[-1]
+    assert c % MX_BLOCK == 0
+    blocks = x.reshape(-1, c // MX_BLOCK, MX_BLOCK)
+    amax = np.abs(blocks).max(axis=-1)
+    # floor(log2(amax)) exactly from the binary exponent (frexp: amax = f * 2^e, f in [0.5, 1))
+    _, e = np.frexp(np.where(amax > 0, amax, 1.0))
+    X = np.clip(np.where(amax > 0, e - 1 - 2, -127), -127, 127)
+    scaled = blocks / np.ldexp(1.0, X)[..., None]
+    a = np.minimum(np.abs(scaled), 6.0)
+    hi = np.minimum(np.searchsorted(_E2M1_VALS, a, side="left"), 7)
+    lo = np.maximum(hi - 1, 0)
+    vhi, vlo = _E2M1_VALS[hi], _E2M1_VALS[lo]
+    pick_hi = (vhi == a) | (vhi - a < a - vlo) | ((vhi - a == a - vlo) & ((hi & 1) == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8) | (np.signbit(scaled).astype(np.uint8) << np.uint8(3))
+    code = code.reshape(-1, c)
+    packed = (code[:, 0::2] | (code[:, 1::2] << np.uint8(4))).astype(np.uint8)
+    scales = (X + 127).astype(np.uint8).reshape(-1, c // MX_BLOCK)
+    return np.concatenate([packed.reshape(-1), scales.reshape(-1)])
+
+
+def mxfp4_to_f32(buf: np.ndarray, rows: int, c: int) -> np.ndarray:
+    """MXFP4 storage of `rows` rows of c values -> float32 [rows, c] (scale 255 is NaN)."""
+    buf = np.asarray(buf, dtype=np.uint8).reshape(-1)
+    assert buf.size == rows * (c // 2 + c // MX_BLOCK)
+    packed = buf[: rows * c // 2].reshape(rows, c // 2)
+    scales = buf[rows * c // 2:].reshape(rows, c // MX_BLOCK).astype(np.int64)
+    code = np.empty((rows, c), dtype=np.uint8)
+    code[:, 0::2] = packed & 0xF
+    code[:, 1::2] = packed >> 4
+    mag = _E2M1_VALS[code & 7]
+    v = np.where(code & 8, -mag, mag) * np.repeat(np.ldexp(1.0, scales - 127), MX_BLOCK, axis=1)
+    v = np.where(np.repeat(scales == 255, MX_BLOCK, axis=1), np.nan, v)
+    return v.astype(np.float32)
+
+
+def mxfp4_rows(buf: np.ndarray, rows: int, c: int, r0: int, r1: int) -> np.ndarray:
+    """Rows r0 .. r1-1 of an MXFP4 storage of `rows` rows of c values, as a storage of their own."""
+    buf = np.asarray(buf, dtype=np.uint8).reshape(-1)
+    eb, sb = c // 2, c // MX_BLOCK
+    return np.concatenate([buf[r0 * eb:r1 * eb], buf[rows * eb + r0 * sb:rows * eb + r1 * sb]])
+
+
 def to_storage(x64: np.ndarray, dtype: int) -> np.ndarray:
     x32 = np.asarray(x64, dtype=np.float64).astype(np.float32)
     if dtype == F32:
@@ -171,7 +229,10 @@ def _fill(shape, dtype, fn):
 
 
 def normal(seed: int, tid: int, shape, dtype: int = F32, std: float = 1.0) -> np.ndarray:
-    """N(0, std^2) samples in storage dtype `dtype`, as a numpy array of the storage type."""
+    """N(0, std^2) samples in storage dtype `dtype`, as a numpy array of the storage type
+    (MXFP4: the flat storage of rows of shape[-1] values; the same draws as the other dtypes)."""
+    if dtype == MXFP4:
+        return f32_to_mxfp4(_fill(shape, F32, lambda s, c: std * _normal_chunk(seed, tid, s, c)))
     return _fill(shape, dtype, lambda s, c: std * _normal_chunk(seed, tid, s, c))
 
 
