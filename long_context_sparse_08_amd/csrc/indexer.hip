@@ -479,10 +479,13 @@ bool mfma_shape(int H_I, int c_I, int qk_t) {
 // blocks over all rows.  The grid is sized to be resident at once (no partly filled second
 // round): up to 32768 blocks one workgroup of 4 waves per CU, each streaming a long chunk (its
 // start, the q / w loads and the first block loads, is paid once per CU); more, three per CU,
-// for more loads in flight.  (Measured: 22.7 vs 24.4 us for 32 rows of 32768 entries, 43.7 vs
-// 47.2 us the other way round for 8 rows of 262144.)
-int decode_chunk_blocks(int64_t total_blk) {
-    const int64_t target = total_blk <= 32768 ? 256 : 3 * 256;
+// for more loads in flight.  MXFP4 blocks are half the bytes: twice the workgroups keep as many
+// bytes in flight.  (Measured at 32 rows of 32768 entries: fp8 22.7 us at one workgroup per CU
+// vs 24.4 at three; MXFP4 13.7 at two vs 15.9 at one.  At 8 rows of 262144 fp8 entries: 43.7
+// us at three vs 47.2 at one.)
+int decode_chunk_blocks(int64_t total_blk, int qk_t) {
+    const int per_cu = min(3, (total_blk <= 32768 ? 1 : 3) * (qk_t == DT_MXFP4 ? 2 : 1));
+    const int64_t target = (int64_t)per_cu * 256;
     const int cb = (int)(((total_blk + target - 1) / target + 3) / 4 * 4);
     return cb < 4 ? 4 : cb;
 }
@@ -510,7 +513,7 @@ int launch_mfma(const void* qI, const float* w, const void* kI, int64_t batch, i
         if (n_chunk_mm) *n_chunk_mm = 0;
         }
     } else {
-        const int cb = decode_chunk_blocks(batch * T * nblk);
+        const int cb = decode_chunk_blocks(batch * T * nblk, DT);
         const int chunks = (int)((nblk + cb - 1) / cb);
         const int64_t grid = (batch * T + 7) / 8 * 8 * chunks;   // row groups padded to whole XCD rounds
         if (grid > 0x7fffffffLL) return -2;
@@ -529,7 +532,7 @@ int64_t max_index_chunks(int64_t N) { return (N + 127) / 128; }
 int index_chunks(int64_t batch, int64_t T, int64_t N, int H_I, int c_I, int qk_t) {
     if (!mfma_shape(H_I, c_I, qk_t) || T >= 4 || N == 0) return 0;
     const int64_t nblk = (N + 31) / 32;
-    const int cb = decode_chunk_blocks(batch * T * nblk);
+    const int cb = decode_chunk_blocks(batch * T * nblk, qk_t);
     return (int)((nblk + cb - 1) / cb);
 }
 
