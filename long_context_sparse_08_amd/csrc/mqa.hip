@@ -225,11 +225,9 @@ __device__ __forceinline__ float sum_xor16(float x) {
 // fragment feeds four head tiles instead of one.  The waves swap their bf16 probability
 // tiles (1 KB each) and rescale factors through LDS once per block.
 //
-// NS staging buffers of one 32-key block each.  NS = 2: while one block is computed the next
-// one loads; the co-resident workgroup covers the rest of the gather latency.  NS = 4 (~148 KB
-// of LDS, one workgroup per CU, for launches of at most one workgroup per CU such as decode):
-// three blocks are in flight while one is computed, which covers the latency of a gather of
-// scattered 1 KB rows within the workgroup itself.
+// Two staging buffers of one 32-key block each: while one block is computed the next one
+// loads; the co-resident workgroup covers the rest of the gather latency.  (Launches of at
+// most one workgroup per CU, such as decode, take mqa_sparse_ws below.)
 constexpr int kMWaves = 4;
 constexpr int kMHT = kMHeadsWG / 16;      // 16-head tiles per workgroup (4)
 constexpr int kMColW = kMC / kMHT;        // output columns per wave (128)
@@ -237,8 +235,8 @@ constexpr int kMColBlkW = kMColW / 16;    // 16-column blocks per wave (8)
 constexpr int kMIdsLds = 1024;            // key ids staged per workgroup (longer ranges are split)
 constexpr int kMFillWGs = 256;            // workgroups a key split aims for
 
-template <bool DENSE, int NS>
-__global__ void __launch_bounds__(kMWaves * kWave, NS == 2 ? 2 : 1)   // NS = 2: two workgroups per CU
+template <bool DENSE>
+__global__ void __launch_bounds__(kMWaves * kWave, 2)   // two workgroups per CU
 mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
                 int64_t rows, int64_t T, int64_t N, int H, int k, int ks_count, int keys_per_split, float sl2,
                 int64_t q_pos0, int ratio, uint16_t* __restrict__ out, uint16_t* __restrict__ part,
@@ -246,14 +244,11 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     // one array per pipeline parity: the DMA into one and the reads of the other are then
     // provably disjoint, so no wait for the in-flight gather is forced before the current
     // block's LDS reads
-    static_assert(NS == 2 || NS == 4, "stages");
-    // the four-stage kernel (one workgroup per CU) has the registers for swizzled addresses
-    constexpr bool SWZ = NS == 4;
-    constexpr int kPitch = kMPitch<SWZ>, kBuf = kMBuf<SWZ>;
+    // (plain padded rows: at two workgroups per CU the registers for swizzled addresses are
+    // not available)
+    constexpr int kPitch = kMPitch<false>, kBuf = kMBuf<false>;
     __shared__ __attribute__((aligned(16))) uint8_t stage_a[kBuf];
     __shared__ __attribute__((aligned(16))) uint8_t stage_b[kBuf];
-    __shared__ __attribute__((aligned(16))) uint8_t stage_c[NS == 4 ? kBuf : 16];
-    __shared__ __attribute__((aligned(16))) uint8_t stage_d[NS == 4 ? kBuf : 16];
     __shared__ int32_t ids[DENSE ? 1 : kMIdsLds];
     __shared__ uint32_t vmask[DENSE ? 1 : kMIdsLds / 32];
     // [0]: probability tiles in the B-operand lane layout; [1][tile][head].x: rescale factor.
@@ -336,25 +331,16 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
         const_cast<uint8_t*>(kvbytes), (short)0, (int)(uint32_t)(N * 2 * kMC), 0x00020000);
     const uint32_t lane_off = 16u * lane;
     auto gather = [&](int blk, uint8_t* dst) {   // block `blk` of the range into `dst`
-        // NS = 4: the wave's 8 key ids in one LDS round trip (lane j holds row j's id).  The
-        // two-stage kernels, at the register limit of two workgroups per CU, read them one by one.
-        const int myid = NS == 4 && lane < kMLoadsPerBlk ? key_id(blk * kMBlk + kMLoadsPerBlk * tw + lane) : 0;
+        // (the key ids one by one: at two workgroups per CU the kernel is at its register limit)
 #pragma unroll
         for (int r8 = 0; r8 < kMLoadsPerBlk; ++r8) {
             const int r = kMLoadsPerBlk * tw + r8;
             // one 1 KB row per instruction: the row is wave-uniform (scalar base, lane offset)
-            const int sidx = NS == 4 ? __builtin_amdgcn_readlane(myid, r8)
-                                     : __builtin_amdgcn_readfirstlane(key_id(blk * kMBlk + r));
-            // lane j fetches the chunk that belongs at position j of the (swizzled) row
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(kvres, (lds_void_ptr)(dst + r * kPitch), 16,
-                                                     SWZ ? 16u * (lane ^ swz(r)) : lane_off,
+            const int sidx = __builtin_amdgcn_readfirstlane(key_id(blk * kMBlk + r));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kvres, (lds_void_ptr)(dst + r * kPitch), 16, lane_off,
                                                      (uint32_t)sidx * (2 * kMC), 0, 0);
         }
     };
-    // per-lane parts of the LDS addresses of the operands (swizzled: see swz)
-    int aoff[4];
-#pragma unroll
-    for (int b4 = 0; b4 < 4; ++b4) aoff[b4] = SWZ ? 16 * ((4 * b4 + g) ^ swz(n16)) : 0;
     auto compute = [&](int blk, const uint8_t* st) {
         // validity of the 32 keys of this block (bit r), shifted to this lane's key group
         uint32_t vg;
@@ -367,14 +353,12 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
 
         // S^T for the two 16-key halves (two independent accumulation chains); the A operands
         // are read kSD steps ahead of their use so LDS latency overlaps the matrix work
-        constexpr int kSD = NS == 2 && !DENSE ? 3 : 4;   // the two-stage sparse kernel is at its register limit
+        constexpr int kSD = DENSE ? 4 : 3;   // the sparse kernel is at its register limit
         f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-        // chunk 4s + g of rows n16 and 16 + n16 (swizzled, s = 4a + b: at position
-        // 16a + ((4b + g) ^ swz(n16)))
-        const uint8_t* arow = st + n16 * kPitch + (SWZ ? 0 : 16 * g);
+        // chunk 4s + g of rows n16 and 16 + n16
+        const uint8_t* arow = st + n16 * kPitch + 16 * g;
         auto lda = [&](int s, int h) {
-            const int o = SWZ ? 256 * (s >> 2) + aoff[s & 3] : 64 * s;
-            return *reinterpret_cast<const bf16x8_t*>(arow + 16 * kPitch * h + o);
+            return *reinterpret_cast<const bf16x8_t*>(arow + 16 * kPitch * h + 64 * s);
         };
         bf16x8_t ra[kSD][2];
 #pragma unroll
@@ -395,15 +379,12 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
         // V^T operands of this wave's columns: transpose reads of keys {4g..4g+3} and
         // {16+4g..}; the first kVD column blocks are requested before the softmax
         constexpr int kVD = 3;
-        // columns 128 tw + 16 cb + 4 (n16 & 3) .. +4 of rows 4g + (n16 >> 2) and 16 + that:
-        // chunk 16 tw + 2 cb + ((n16 & 3) >> 1), at position 16 tw + ((2 cb + ..) ^ swz(row))
-        const int vr = 4 * g + (n16 >> 2), vs = swz(vr);
-        // swizzled: bits 5-7 of vofs hold (swz >> 1); column block cb is then at vofs ^ (32 cb)
-        const int vofs = vr * kPitch + 256 * tw + 32 * (vs >> 1) + 16 * (((n16 & 3) >> 1) ^ (vs & 1)) + 8 * (n16 & 1);
-        const uint8_t* vbase = st + vr * kPitch + 8 * (n16 & 3) + 2 * kMColW * tw;   // unswizzled
+        // columns 128 tw + 16 cb + 4 (n16 & 3) .. +4 of rows 4g + (n16 >> 2) and 16 + that
+        const int vr = 4 * g + (n16 >> 2);
+        const uint8_t* vbase = st + vr * kPitch + 8 * (n16 & 3) + 2 * kMColW * tw;
         auto ldv = [&](int cb) {
             typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-            const uint8_t* va_ = SWZ ? st + (vofs ^ (32 * cb)) : vbase + 32 * cb;
+            const uint8_t* va_ = vbase + 32 * cb;
             const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)va_);
             const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(va_ + 16 * kPitch));
             typedef short i16x8 __attribute__((ext_vector_type(8)));
@@ -479,7 +460,7 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                 acc[ht][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pb[ht], acc[ht][cb], 0, 0, 0);
         }
     };
-    if constexpr (NS == 2) {
+    {
         if (nblk > 0) gather(0, stage_a);   // the loop's first wait also covers q
         for (int blk = 0; blk < nblk; blk += 2) {
             wait_vmcnt<0>();
@@ -492,41 +473,6 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
             if (blk + 2 < nblk) gather(blk + 2, stage_a);
             compute(blk + 1, stage_b);
         }
-    } else if (nblk > 0) {
-        // Every step issues its gather, also past the last block (all of whose slots load
-        // row 0 of the sequence, from L2, into a buffer no later step reads), so that every
-        // step has the same count of outstanding loads and one wait count fits all steps.
-        // (With counts that depend on the step, the compiler cannot tell which buffer a
-        // pending load writes and waits for all of them before reading any buffer.)
-        // Blocks 0..2 are in flight before the first wait (which also covers q).
-        gather(0, stage_a);
-        gather(1, stage_b);
-        gather(2, stage_c);
-        // block b is staged once only the two later steps' loads are outstanding (a wave's
-        // loads complete in issue order); the barrier then also tells that every wave is done
-        // with the buffer of block b-1, which the load of block b+3 reuses
-        auto staged = [&]() {
-            wait_vmcnt<2 * kMLoadsPerBlk>();
-            lds_barrier();
-        };
-        for (int blk = 0; blk < nblk; blk += 4) {
-            staged();
-            gather(blk + 3, stage_d);
-            compute(blk, stage_a);
-            if (blk + 1 >= nblk) break;
-            staged();
-            gather(blk + 4, stage_a);
-            compute(blk + 1, stage_b);
-            if (blk + 2 >= nblk) break;
-            staged();
-            gather(blk + 5, stage_b);
-            compute(blk + 2, stage_c);
-            if (blk + 3 >= nblk) break;
-            staged();
-            gather(blk + 6, stage_c);
-            compute(blk + 3, stage_d);
-        }
-        wait_vmcnt<0>();   // the loads past the last block, before the buffers are reused
     }
 
     // sum of the softmax denominators over the four lane groups that share a head
@@ -542,18 +488,15 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     for (int ht = 0; ht < kMHT; ++ht) {
         const float l = xl[ht][n16];
         const float inv = l > 0.f ? 1.f / l : 0.f;
-        // columns 128 tw + 16 cb + 4g .. +4 of head row 16 (ht & 1) + n16, swizzled as the
-        // staged keys are: chunk 16 tw + 2 cb + (g >> 1) at position 16 tw + ((2 cb + ..) ^ swz)
-        const int sw = swz(n16);
-        const int erow = (16 * (ht & 1) + n16) * kPitch + 256 * tw;
-        const int eofs = SWZ ? erow + 32 * (sw >> 1) + 16 * ((g >> 1) ^ (sw & 1)) + 8 * (g & 1) : erow + 8 * g;
+        // columns 128 tw + 16 cb + 4g .. +4 of head row 16 (ht & 1) + n16
+        const int eofs = (16 * (ht & 1) + n16) * kPitch + 256 * tw + 8 * g;
         uint8_t* sbuf = ht < 2 ? stage_a : stage_b;
 #pragma unroll
         for (int cb = 0; cb < kMColBlkW; ++cb) {
             uint2 w2;
             w2.x = pack_bf16x2(acc[ht][cb][0] * inv, acc[ht][cb][1] * inv);
             w2.y = pack_bf16x2(acc[ht][cb][2] * inv, acc[ht][cb][3] * inv);
-            *reinterpret_cast<uint2*>(sbuf + (SWZ ? eofs ^ (32 * cb) : eofs + 32 * cb)) = w2;
+            *reinterpret_cast<uint2*>(sbuf + eofs + 32 * cb) = w2;
         }
     }
     __syncthreads();
@@ -564,12 +507,10 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const int r = 8 * tw + j;
-        // position `lane` of row r holds chunk lane ^ swz(r) (rows r and 32 + r swizzle alike)
-        const int c = SWZ ? lane ^ swz(r) : lane;
         const uint4 va = *reinterpret_cast<const uint4*>(stage_a + r * kPitch + 16 * lane);
         const uint4 vb = *reinterpret_cast<const uint4*>(stage_b + r * kPitch + 16 * lane);
-        *reinterpret_cast<uint4*>(dst + (int64_t)r * kMC + 8 * c) = va;
-        *reinterpret_cast<uint4*>(dst + (int64_t)(32 + r) * kMC + 8 * c) = vb;
+        *reinterpret_cast<uint4*>(dst + (int64_t)r * kMC + 8 * lane) = va;
+        *reinterpret_cast<uint4*>(dst + (int64_t)(32 + r) * kMC + 8 * lane) = vb;
     }
     if constexpr (!DENSE) {
         if (part != nullptr && g == 0) {
@@ -589,7 +530,7 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
 //   waves 4-7 (value waves, 128 output columns each over the 64 heads): rescale and add
 //     V^T.P^T of block j-1 while the score waves work on block j
 // One workgroup barrier per block; four staging buffers hold blocks j-1 (value waves), j
-// (score waves), and j+1, j+2 (loading).  The same swizzled LDS rows as the four-stage kernel.
+// (score waves), and j+1, j+2 (loading), in swizzled 1 KB rows (see swz).
 constexpr int kWsWaves = 8;
 
 __global__ void __launch_bounds__(kWsWaves * kWave, 1)
@@ -1015,7 +956,7 @@ int launch_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t
                                static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx, rows, T, N, H,
                                k, ks, kps, sl2, static_cast<uint16_t*>(out), part, part_ml);
         else
-            hipLaunchKernelGGL((mqa_sparse_mfma<false, 2>), dim3((unsigned)units), dim3(kMWaves * kWave), 0, stream,
+            hipLaunchKernelGGL((mqa_sparse_mfma<false>), dim3((unsigned)units), dim3(kMWaves * kWave), 0, stream,
                                static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx, rows, T, N, H,
                                k, ks, kps, sl2, (int64_t)0, 1, static_cast<uint16_t*>(out), part, part_ml);
         if (ks > 1) {
@@ -1043,7 +984,7 @@ int launch_dense_mqa(const void* q, const void* kv, int64_t batch, int64_t T, in
         const int64_t rows = batch * T;
         const int64_t units = ((rows + 7) / 8) * 8 * (H / kMHeadsWG);
         if (units > 0x7fffffffLL) return -2;
-        hipLaunchKernelGGL((mqa_sparse_mfma<true, 2>), dim3((unsigned)units), dim3(kMWaves * kWave), 0, stream,
+        hipLaunchKernelGGL((mqa_sparse_mfma<true>), dim3((unsigned)units), dim3(kMWaves * kWave), 0, stream,
                            static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), nullptr, rows, T, N, H, 0,
                            1, 0x7fffffff, scale * kLog2e, q_pos0, ratio, static_cast<uint16_t*>(out), nullptr, nullptr);
         return 0;
