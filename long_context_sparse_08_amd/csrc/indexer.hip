@@ -375,7 +375,9 @@ index_scores_prefill(const void* __restrict__ qI, const float* __restrict__ w, c
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 5, n = lane & 31;
     const int64_t groups = (T + kPfWaves - 1) / kPfWaves;
-    const int64_t unit = blockIdx.x;
+    // later query groups see more blocks: dealing the workgroups longest first (the hardware
+    // hands them out in blockIdx order) keeps the triangle's short ones for the end
+    const int64_t unit = (int64_t)gridDim.x - 1 - blockIdx.x;
     const int chunk = (int)(unit % chunks);
     const int64_t bg = unit / chunks;
     const int64_t b = bg / groups, tg = bg - b * groups;

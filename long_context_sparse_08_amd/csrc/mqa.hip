@@ -324,7 +324,13 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
         for (int cb = 0; cb < kMColBlkW; ++cb) acc[ht][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;   // head 16*tw + n16
 
-    const int nblk = (nkeys + kMBlk - 1) / kMBlk;
+    int nblk = (nkeys + kMBlk - 1) / kMBlk;
+    if constexpr (!DENSE) {
+        // a query that sees fewer than k entries has its tail padded with -1: blocks past the
+        // last valid key would leave the softmax state as it is, so the walk stops there
+        while (nblk > 0 && vmask[nblk - 1] == 0u) --nblk;
+        nblk = __builtin_amdgcn_readfirstlane(nblk);
+    }
     const uint8_t* kvbytes = reinterpret_cast<const uint8_t*>(kv + b * N * (int64_t)kMC);
     // this sequence's KV rows (N <= kMMaxEntries, checked at launch); loads past them read 0
     const __amdgpu_buffer_rsrc_t kvres = __builtin_amdgcn_make_buffer_rsrc(
