@@ -352,8 +352,9 @@ index_scores_mfma(const void* __restrict__ qI, const float* __restrict__ w, cons
 // once per workgroup, coalesced (one 16-byte load per lane covers 1 KB of consecutive rows),
 // three blocks ahead into registers, and written to LDS rows padded by 16 bytes, from where
 // every wave reads its MFMA operand without bank conflicts (each 16-lane phase of a read then
-// touches 16 distinct 4-bank groups).  Visibility grows with the query, so the group walks the
-// blocks its last query sees and each wave masks its own tail.
+// touches 16 distinct 4-bank groups).  The ReLU / w sum of a 32-head tile runs under the
+// matrix work of the next tile.  Visibility grows with the query, so the
+// group walks the blocks its last query sees and each wave masks its own tail.
 constexpr int kPfWaves = 8;
 constexpr int kPfPad = 16;
 
@@ -423,19 +424,25 @@ index_scores_prefill(const void* __restrict__ qI, const float* __restrict__ w, c
         const int64_t e = min((blk0 + min(i, nb - 1)) * 32 + srow, N - 1);
         return *reinterpret_cast<const uint4*>(kb + e * kRowB + scol);
     };
-    auto compute = [&](int i) {
+    // The ReLU / w head sum of each 32-head tile runs under the next tile's matrix work: with
+    // 64 heads, step i issues block i's tile 0, then the sum of block i-1's tile 1 (and block
+    // i-1's store), then block i's tile 1, then the sum of block i's tile 0; with 32 heads,
+    // block i's tile, then block i-1's sum.  Two accumulators alternate.
+    auto operand = [&](int i, typename O::Frag& kf) {   // entry n, channel half g, from buffer i & 1
         const uint8_t* st = &stg[i & 1][0] + n * kPitch + g * (kRowB / 2);
-        typename O::Frag kf;
 #pragma unroll
         for (int j = 0; j < O::kLoads; ++j) kf.v[j] = *reinterpret_cast<const uint4*>(st + 16 * j);
-        float contrib = 0.f;
+    };
+    auto tile = [&](const typename O::Frag& kf, int mb, f32x16& acc) {
+        acc = f32x16{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        acc = O::mma(qa[mb], kf, acc);
+    };
+    auto head_sum = [&](int mb, const f32x16& acc, float contrib) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            f32x16 acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            acc = O::mma(qa[mb], kf, acc);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) contrib = fmaf(wv[mb][r], fmaxf(acc[r], 0.f), contrib);
-        }
+        for (int r = 0; r < 16; ++r) contrib = fmaf(wv[mb][r], fmaxf(acc[r], 0.f), contrib);
+        return contrib;
+    };
+    auto finish = [&](int i, float contrib) {
         // lanes l and l^32 hold the two halves of entry n's heads
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(contrib), __float_as_uint(contrib), false,
                                                          false);
@@ -454,22 +461,42 @@ index_scores_prefill(const void* __restrict__ qI, const float* __restrict__ w, c
         *reinterpret_cast<uint4*>(&stg[0][srow * kPitch + scol]) = ra;
     }
     __syncthreads();
-    auto step = [&](int i, const uint4& next, uint4& fetch) {
+    f32x16 acc0, acc1;
+    float part = 0.f;   // 64 heads: block i's tile-0 sum, carried into step i+1
+    // x: the accumulator step i writes first; y: the one holding the previous tile
+    auto step = [&](int i, const uint4& next, uint4& fetch, f32x16& x, f32x16& y) {
         if (loader) {
             fetch = gload(i + 3);
             if (i + 1 < nb) *reinterpret_cast<uint4*>(&stg[(i + 1) & 1][srow * kPitch + scol]) = next;
         }
-        compute(i);
+        typename O::Frag kf;
+        operand(i, kf);
+        tile(kf, 0, x);
+        if constexpr (MB == 2) {
+            if (i > 0) finish(i - 1, head_sum(1, y, part));
+            tile(kf, 1, y);
+            part = head_sum(0, x, 0.f);
+        } else {
+            if (i > 0) finish(i - 1, head_sum(0, y, 0.f));
+        }
         __syncthreads();
     };
+    auto last = [&](int i, f32x16& x, f32x16& y) {   // the sums step i left
+        if constexpr (MB == 2) finish(i, head_sum(1, y, part));
+        else finish(i, head_sum(0, x, 0.f));
+    };
+    // with 64 heads tile 0 always goes to acc0; with 32, the blocks alternate
+    f32x16& x1 = MB == 2 ? acc0 : acc1;
+    f32x16& y1 = MB == 2 ? acc1 : acc0;
     for (int i = 0; i < nb; i += 4) {
-        step(i, rb, rd);
-        if (i + 1 >= nb) break;
-        step(i + 1, rc, ra);
-        if (i + 2 >= nb) break;
-        step(i + 2, rd, rb);
-        if (i + 3 >= nb) break;
-        step(i + 3, ra, rc);
+        step(i, rb, rd, acc0, acc1);
+        if (i + 1 >= nb) { last(i, acc0, acc1); break; }
+        step(i + 1, rc, ra, x1, y1);
+        if (i + 2 >= nb) { last(i + 1, x1, y1); break; }
+        step(i + 2, rd, rb, acc0, acc1);
+        if (i + 3 >= nb) { last(i + 2, acc0, acc1); break; }
+        step(i + 3, ra, rc, x1, y1);
+        if (i + 4 >= nb) { last(i + 3, x1, y1); break; }
     }
 }
 

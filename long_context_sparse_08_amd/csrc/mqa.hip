@@ -261,8 +261,11 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int g = lane >> 4, n16 = lane & 15;
     const int HG = H / kMHeadsWG;
     // XCD-aware order: consecutive units of a row go to one XCD (workgroups are dealt
-    // round-robin over the 8 XCDs), so they share that XCD's L2 for the row's KV.
-    const int64_t x = blockIdx.x;
+    // round-robin over the 8 XCDs), so they share that XCD's L2 for the row's KV.  Sparse rows
+    // are dealt last row first: early queries of a prefill see fewer than k entries (less
+    // work), which then fills the end (the grid is a multiple of 8, so x % 8 keeps a row on
+    // one XCD).
+    const int64_t x = DENSE ? (int64_t)blockIdx.x : (int64_t)gridDim.x - 1 - blockIdx.x;
     const int64_t per_row = (int64_t)HG * ks_count;
     const int64_t slot = x / 8, xcd = x % 8;
     const int64_t row = (slot / per_row) * 8 + xcd;
