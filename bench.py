@@ -29,8 +29,9 @@ sys.path.insert(0, ROOT)
 METRIC = "CSA query tokens/s (compress+index+top-k+MQA) at 128K ctx; % of roofline"
 HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
 MFMA_PEAK = {"bf16": 2.5e15, "fp8": 5.0e15}
-DT_BYTES = {0: 4, 1: 2, 2: 1, 3: 17 / 32}   # MXFP4: a 4-bit value plus a 1-byte scale per 32
-DT_NAME = {0: "f32", 1: "bf16", 2: "fp8_e4m3", 3: "mxfp4"}
+# MXFP4: a 4-bit value plus a 1-byte scale per 32; mixed KV rows: 448 fp8 + 64 bf16 per 512
+DT_BYTES = {0: 4, 1: 2, 2: 1, 3: 17 / 32, 4: 576 / 512}
+DT_NAME = {0: "f32", 1: "bf16", 2: "fp8_e4m3", 3: "mxfp4", 4: "kv_fp8_bf16"}
 
 
 def log(*a):
@@ -63,7 +64,8 @@ def stage_work(cfg):
         st["topk"] = dict(bytes=pairs * 4 + B * T * k * 8, flops=0, bound="hbm")
         # decode gathers distinct rows per sequence from HBM; prefill re-gathers from a cache
         # that stays in L2/MALL, so its HBM bytes are the cache read once
-        kv_bytes = sel * c * e if cfg.kind == "csa_decode" else B * N * c * e
+        ekv = DT_BYTES[cfg.dt if cfg.kv_dt < 0 else cfg.kv_dt]
+        kv_bytes = sel * c * ekv if cfg.kind == "csa_decode" else B * N * c * e
         st["mqa"] = dict(bytes=kv_bytes + 2 * B * T * H * c * e + B * T * k * 4, flops=4 * sel * H * c,
                          bound="hbm" if cfg.kind == "csa_decode" else "mfma")
     else:
@@ -108,6 +110,8 @@ def _cpu_sample(cfg, host):
     if cfg.kind == "csa_decode":
         nseq = cfg.batch
         sub = {k: host[k][:nseq] for k in ("kv", "q", "w")}
+        if cfg.kv_dt == 4:   # mixed fp8 / bf16 KV rows: the oracle decodes them
+            sub["kv"] = oracle.decode_kv_fp8_bf16(sub["kv"], cfg.c)
         if cfg.qk_dt == 3:   # MXFP4 storage: the oracle decodes it (shape from the config)
             sub["qI"] = oracle.decode_mxfp4(host["qI"], (cfg.batch, cfg.T, cfg.H_I, cfg.c_I))
             sub["kI"] = oracle.decode_mxfp4(host["kI"], (cfg.batch, cfg.N, cfg.c_I))
@@ -183,7 +187,12 @@ def main():
         t = torch.from_numpy(v)
         if sh[k][1] == 1:
             t = t.view(torch.bfloat16)
-        dev[k] = csa.MXFP4(t.cuda(), sh[k][0]) if sh[k][1] == 3 else t.cuda()
+        if sh[k][1] == 3:
+            dev[k] = csa.MXFP4(t.cuda(), sh[k][0])
+        elif sh[k][1] == 4:
+            dev[k] = csa.KVFp8Bf16(t.cuda(), sh[k][0][-1])
+        else:
+            dev[k] = t.cuda()
     torch.cuda.synchronize()
     log("[bench] inputs resident on the GPU")
 
@@ -310,7 +319,7 @@ def main():
         "data": "synthetic (seeded SplitMix64 normals/uniforms; no dataset)",
         "config": {"workload": cfg.name, "batch": cfg.batch, "query_tokens_per_seq": cfg.T, "q_pos0": cfg.q_pos0,
                    "entries": cfg.N, "c": cfg.c, "heads": cfg.H, "H_I": cfg.H_I, "c_I": cfg.c_I, "k": cfg.k,
-                   "m": cfg.m if cfg.kind != "hca_chunk" else cfg.m_prime, "kv_dtype": DT_NAME[cfg.dt],
+                   "m": cfg.m if cfg.kind != "hca_chunk" else cfg.m_prime, "kv_dtype": DT_NAME[cfg.dt if cfg.kv_dt < 0 else cfg.kv_dt],
                    "qk_dtype": DT_NAME[cfg.qk_dt] if cfg.kind != "hca_chunk" else None,
                    "graph": graph is not None},
         "roofline": roof,

@@ -48,7 +48,13 @@ extern "C" {
  * bytes first, c/2 per row with value 2i in the low nibble of byte i and 2i+1 in the high
  * nibble, then all rows' scales, c/32 bytes per row (R * (c/2 + c/32) bytes in all).
  */
-typedef enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3 = 2, CSA_MXFP4 = 3 } csa_dtype;
+/*
+ * CSA_KV_FP8_BF16 (KV entries of csa_sparse_mqa only; [N] §1.3 and [M] §2.3.4: the KV cache
+ * keeps its RoPE dimensions in bf16 and the others in fp8; [N] §1.3 and [M] §2.3.3 item 2:
+ * RoPE covers the last 64 dimensions): a row of c values is c - 64 fp8 bytes (dimensions
+ * 0 .. c-65), then 64 bf16 values (dimensions c-64 .. c-1): c + 64 bytes per row.
+ */
+typedef enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3 = 2, CSA_MXFP4 = 3, CSA_KV_FP8_BF16 = 4 } csa_dtype;
 
 typedef enum {
     CSA_OK = 0,
@@ -158,14 +164,18 @@ int csa_topk(const float* scores, int64_t ld, int64_t batch, int64_t T, int64_t 
  *     out[t,h,:] = sum_{s in idx[t]} softmax_s(scale * q[t,h,:] . kv[s,:]) * kv[s,:]
  * (fp32 logits, softmax and accumulation).  Ids outside [0, N) — the -1 pads — are
  * skipped; a query with no valid id gets a zero output.  Ids must be distinct.
- *   q   : [batch, T, H, c]  dtype t (CSA_F32 or CSA_BF16)
- *   kv  : [batch, N, c]     dtype t
+ *   q   : [batch, T, H, c]  dtype t (CSA_F32 or CSA_BF16; CSA_BF16 when t = CSA_KV_FP8_BF16)
+ *   kv  : [batch, N, c]     dtype t (CSA_KV_FP8_BF16: [batch, N, c + 64] bytes, the mixed rows)
  *   idx : [batch, T, k]     int32
- *   out : [batch, T, H, c]  dtype t
+ *   out : [batch, T, H, c]  dtype t (CSA_BF16 when t = CSA_KV_FP8_BF16)
  *   workspace : device scratch of at least csa_sparse_mqa_workspace_size(...) bytes (may be
  *               NULL when that size is 0), 16-byte aligned; holds per-key-range partial
  *               results when a query's keys are split over several workgroups.
  * Limits: c % 8 == 0, c <= CSA_MAX_WIDTH, 1 <= H <= CSA_MAX_HEADS, 1 <= k <= CSA_MAX_TOPK.
+ * CSA_KV_FP8_BF16 is built for decode shapes only: c == 512, H % 64 == 0,
+ * batch * T * H / 64 <= 256, k <= 1024; other shapes return CSA_ERR_UNSUPPORTED (as does
+ * hca_dense_mqa for it).  The fp8 values are used exactly (converted to bf16 for the
+ * products); logits, softmax and accumulation stay fp32.
  */
 size_t csa_sparse_mqa_workspace_size(int64_t batch, int64_t T, int H, int c, int k, csa_dtype t);
 int csa_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t batch, int64_t T, int64_t N, int H,

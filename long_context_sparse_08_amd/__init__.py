@@ -16,7 +16,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "_build", "libcsa.so")
 
-CSA_F32, CSA_BF16, CSA_FP8_E4M3, CSA_MXFP4 = 0, 1, 2, 3
+CSA_F32, CSA_BF16, CSA_FP8_E4M3, CSA_MXFP4, CSA_KV_FP8_BF16 = 0, 1, 2, 3, 4
 STATUS = {0: "CSA_OK", -1: "CSA_ERR_INVALID_ARG", -2: "CSA_ERR_UNSUPPORTED", -3: "CSA_ERR_WORKSPACE",
           -4: "CSA_ERR_HIP"}
 
@@ -92,6 +92,20 @@ class MXFP4:
             rows *= d
         if data.dtype != torch.uint8 or c % 32 != 0 or data.numel() != rows * (c // 2 + c // 32):
             raise ValueError(f"an MXFP4 buffer of logical shape {self.shape} holds {rows * (c // 2 + c // 32)} bytes")
+
+
+class KVFp8Bf16:
+    """KV entries in the library's mixed-precision storage (csa_dtype CSA_KV_FP8_BF16): `data`
+    is a uint8 device tensor [batch, N, c + 64] whose rows hold c - 64 e4m3 bytes, then the
+    last 64 values as bf16; `c` is the logical row length."""
+
+    def __init__(self, data: torch.Tensor, c: int):
+        self.data = data
+        self.c = int(c)
+        if data.dtype != torch.uint8 or data.dim() != 3 or data.shape[-1] != self.c + 64:
+            raise ValueError(f"mixed KV rows of {tuple(data.shape)} bytes do not hold {c} values")
+        self.shape = (data.shape[0], data.shape[1], self.c)
+        self.device = data.device
 
 
 def _qk(qI, kI):
@@ -222,26 +236,34 @@ def csa_sparse_mqa_workspace_size(batch: int, T: int, H: int, c: int, k: int, dt
     return int(lib.csa_sparse_mqa_workspace_size(batch, T, H, c, k, dtype))
 
 
-def mqa_workspace_for(q: torch.Tensor, k: int):
+def mqa_workspace_for(q: torch.Tensor, k: int, dtype: int | None = None):
     batch, T, H, c = q.shape
-    nbytes = csa_sparse_mqa_workspace_size(batch, T, H, c, k, _dt(q))
+    nbytes = csa_sparse_mqa_workspace_size(batch, T, H, c, k, _dt(q) if dtype is None else dtype)
     return None if nbytes == 0 else torch.empty(nbytes, dtype=torch.uint8, device=q.device)
 
 
 def csa_sparse_mqa(q, kv, idx, scale: float, out=None, workspace=None):
-    """q [batch, T, H, c], kv [batch, N, c], idx [batch, T, k] int32 -> out [batch, T, H, c]."""
-    dev = _dev(q, kv, idx, out, workspace)
+    """q [batch, T, H, c], kv [batch, N, c] (or KVFp8Bf16 with bf16 q), idx [batch, T, k] int32
+    -> out [batch, T, H, c]."""
+    mixed = isinstance(kv, KVFp8Bf16)
+    kvt = kv.data if mixed else kv
+    dev = _dev(q, kvt, idx, out, workspace)
     batch, T, H, c = q.shape
     N = kv.shape[1]
     k = idx.shape[2]
-    assert kv.shape == (batch, N, c) and kv.dtype == q.dtype and idx.dtype == torch.int32
-    assert idx.shape == (batch, T, k)
+    if mixed:
+        assert q.dtype == torch.bfloat16 and kv.c == c and kvt.shape[0] == batch
+        dt = CSA_KV_FP8_BF16
+    else:
+        assert kv.shape == (batch, N, c) and kv.dtype == q.dtype
+        dt = _dt(q)
+    assert idx.dtype == torch.int32 and idx.shape == (batch, T, k)
     if out is None:
         out = torch.empty_like(q)
     if workspace is None:
-        workspace = mqa_workspace_for(q, k)
+        workspace = mqa_workspace_for(q, k, dt)
     ws_bytes = 0 if workspace is None else workspace.numel()
-    _check("csa_sparse_mqa", lib.csa_sparse_mqa(_p(q), _p(kv), _p(idx), batch, T, N, H, c, k, float(scale), _dt(q),
+    _check("csa_sparse_mqa", lib.csa_sparse_mqa(_p(q), _p(kvt), _p(idx), batch, T, N, H, c, k, float(scale), dt,
                                                 _p(out), _p(workspace), ws_bytes, _stream(dev)))
     return out
 

@@ -199,10 +199,13 @@ size_t csa_sparse_mqa_workspace_size(int64_t batch, int64_t T, int H, int c, int
 
 int csa_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t batch, int64_t T, int64_t N, int H, int c,
                    int k, float scale, csa_dtype t, void* out, void* workspace, size_t ws_bytes, csa_stream_t stream) {
-    int rc = check_mqa(q, kv, out, batch, T, N, H, c, scale, t);
+    const bool mixed = t == CSA_KV_FP8_BF16;   // q and out are bf16 then
+    int rc = check_mqa(q, kv, out, batch, T, N, H, c, scale, mixed ? CSA_BF16 : t);
     if (rc != CSA_OK) return rc;
     if (k < 1) return CSA_ERR_INVALID_ARG;
     if (k > CSA_MAX_TOPK) return CSA_ERR_UNSUPPORTED;
+    if (mixed && (c != 512 || H % 64 != 0 || batch * T * (H / 64) > 256 || k > 1024 || N > 0xffffffffLL / (c + 64)))
+        return CSA_ERR_UNSUPPORTED;
     if (batch == 0 || T == 0) return CSA_OK;
     if (!idx) return CSA_ERR_INVALID_ARG;
     const size_t need = csa_sparse_mqa_workspace_size(batch, T, H, c, k, t);

@@ -9,7 +9,8 @@
 
 namespace csa {
 
-enum Dt : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2, DT_MXFP4 = 3 };
+// DT_KV_FP8_BF16: KV rows of c values stored as c - 64 e4m3 bytes, then 64 bf16 values
+enum Dt : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2, DT_MXFP4 = 3, DT_KV_FP8_BF16 = 4 };
 
 constexpr int kWave = 64;
 constexpr float kLog2e = 1.4426950408889634f;

@@ -540,17 +540,55 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
 //     V^T.P^T of block j-1 while the score waves work on block j
 // One workgroup barrier per block; four staging buffers hold blocks j-1 (value waves), j
 // (score waves), and j+1, j+2 (loading), in swizzled 1 KB rows (see swz).
+//
+// MIX: KV rows in the mixed format (448 fp8 channels, then the 64 RoPE channels in bf16; 576
+// bytes).  The gathers land unconverted in three raw buffers (blocks j, j+1, j+2).  A score
+// wave's 8 rows fill a 5 KB region of a raw buffer: 8 x 576 bytes back to back, then 512
+// bytes of padding, written by five 1 KB LDS-DMA loads in which lane i fetches the 16 bytes
+// that belong at region byte 1024 j + 16 i (the padding's lanes fetch entry 0); no lane is
+// masked off.  Row n keeps its 16-byte chunk c at chunk position (c + (n % 16) / 4) mod 36,
+// so the 16 rows a 16-lane group reads (same chunk) fall in 16 different 4-bank groups.  A
+// score wave reads 16 bytes per lane per two score steps (16 fp8 channels), converts them to
+// bf16 in registers, and writes the converted channels of its quarter (128 of them) of every
+// row into a swizzled 1 KB-row buffer (parity j % 2), from which the value waves take block
+// j in the next step, unchanged.  For the score products the 32 channels of step s < 14 are
+// 64 (s/2) + 16 g + 8 (s%2) + 0..7 for lane group g (q is loaded in the same order).
 constexpr int kWsWaves = 8;
+constexpr int kMixRowB = kMC + 64;       // bytes of a mixed row (36 chunks)
+constexpr int kMixRegion = 5 * 1024;     // one score wave's 8 rows in a raw buffer
+constexpr int kMixGathers = 5;           // LDS-DMA loads per score wave and block
 
+// byte offset of chunk c (0..35) of row n (0..31) in a raw buffer
+__device__ __forceinline__ int mix_pos(int n, int c) {
+    int pc = c + ((n & 15) >> 2);
+    if (pc >= 36) pc -= 36;
+    return (n >> 3) * kMixRegion + (n & 7) * kMixRowB + 16 * pc;
+}
+
+// 8 fp8 e4m3 values (bytes of w0, then of w1) -> 8 bf16 (exact)
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+    const auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, false);
+    const auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, true);
+    const auto c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, false);
+    const auto d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, true);
+    return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+template <bool MIX>
 __global__ void __launch_bounds__(kWsWaves * kWave, 1)
-mqa_sparse_ws(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
+mqa_sparse_ws(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kvb, const int32_t* __restrict__ idx,
               int64_t rows, int64_t T, int64_t N, int H, int k, int ks_count, int keys_per_split, float sl2,
               uint16_t* __restrict__ out, uint16_t* __restrict__ part, float* __restrict__ part_ml) {
     constexpr int kPitch = kMPitch<true>, kBuf = kMBuf<true>;
+    constexpr int kRawBuf = kMHT * kMixRegion;
+    constexpr int kRowB = MIX ? kMixRowB : 2 * kMC;   // bytes of one KV row in memory
+    // bf16: a-d are the four staging buffers; MIX: c-e hold raw gathered blocks, a-b the
+    // converted blocks the value waves read
     __shared__ __attribute__((aligned(16))) uint8_t stage_a[kBuf];
     __shared__ __attribute__((aligned(16))) uint8_t stage_b[kBuf];
-    __shared__ __attribute__((aligned(16))) uint8_t stage_c[kBuf];
-    __shared__ __attribute__((aligned(16))) uint8_t stage_d[kBuf];
+    __shared__ __attribute__((aligned(16))) uint8_t stage_c[MIX ? kRawBuf : kBuf];
+    __shared__ __attribute__((aligned(16))) uint8_t stage_d[MIX ? kRawBuf : kBuf];
+    __shared__ __attribute__((aligned(16))) uint8_t stage_e[MIX ? kRawBuf : 16];
     __shared__ int32_t ids[kMIdsLds];
     __shared__ uint32_t vmask[kMIdsLds / 32];
     __shared__ uint4 xpp[2][kMHT][kWave];     // P tiles of block j (B-operand lane layout), parity j % 2
@@ -602,10 +640,10 @@ mqa_sparse_ws(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
     __syncthreads();
 
     const int nblk = (nkeys + kMBlk - 1) / kMBlk;
-    const uint8_t* kvbytes = reinterpret_cast<const uint8_t*>(kv + b * N * (int64_t)kMC);
-    // this sequence's KV rows (N <= kMMaxEntries, checked at launch); loads past them read 0
+    const uint8_t* kvbytes = kvb + b * N * (int64_t)kRowB;
+    // this sequence's KV rows (N * kRowB < 2^32, checked at launch); loads past them read 0
     const __amdgpu_buffer_rsrc_t kvres = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(kvbytes), (short)0, (int)(uint32_t)(N * 2 * kMC), 0x00020000);
+        const_cast<uint8_t*>(kvbytes), (short)0, (int)(uint32_t)(N * kRowB), 0x00020000);
 
     // Each role keeps its state inside its own branch (the barriers of the two branches pair
     // up one to one), so the score waves' q and the value waves' accumulators never share
@@ -614,9 +652,12 @@ mqa_sparse_ws(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
         float m_run = -INFINITY, l_run = 0.f;   // head 16*tw + n16
         // this wave's q (head tile tw) as the B operand of S^T: head n16, channels 32*s + 8*g .. +8
         bf16x8_t qb[kMC / 32];
-        const uint16_t* qrow = q + ((row * H) + h0 + 16 * tw + n16) * (int64_t)kMC + 8 * g;
+        const uint16_t* qrow = q + ((row * H) + h0 + 16 * tw + n16) * (int64_t)kMC;
 #pragma unroll
-        for (int s = 0; s < kMC / 32; ++s) qb[s] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * s);
+        for (int s = 0; s < kMC / 32; ++s) {
+            const int ch = MIX && s < 14 ? 64 * (s >> 1) + 16 * g + 8 * (s & 1) : 32 * s + 8 * g;
+            qb[s] = *reinterpret_cast<const bf16x8_t*>(qrow + ch);
+        }
         // block `blk` into `dst`: this wave's 8 rows, ids in one LDS round trip; blocks past the
         // range load entry 0 (a gather is issued every step: one wait count fits every step)
         auto gather_ids = [&](int blk) {   // lane j: the id of this wave's row j of block blk
@@ -626,13 +667,32 @@ mqa_sparse_ws(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
             const int r = kMLoadsPerBlk * tw + r8;
             const int sidx = __builtin_amdgcn_readlane(myid, r8);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(kvres, (lds_void_ptr)(dst + r * kPitch), 16,
-                                                     16u * (lane ^ swz(r)), (uint32_t)sidx * (2 * kMC), 0, 0);
+                                                     16u * (lane ^ swz(r)), (uint32_t)sidx * kRowB, 0, 0);
+        };
+        // MIX: load j (0..4) of this wave's region of block blk; `myid` as from gather_ids
+        auto gather_mix = [&](int myid, int j, uint8_t* dst) {
+            const int pbyte = 1024 * j + 16 * lane;   // byte of this wave's region
+            const int r8 = pbyte / kMixRowB;          // 8: padding
+            const int n = kMLoadsPerBlk * tw + (r8 < 8 ? r8 : 7);
+            const int id = __builtin_amdgcn_ds_bpermute(4 * (r8 < 8 ? r8 : 7), myid);
+            int c = (pbyte - kMixRowB * r8) / 16 - ((n & 15) >> 2);
+            if (c < 0) c += 36;
+            const uint32_t src = r8 < 8 ? (uint32_t)id * kMixRowB + 16u * c : 0u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kvres, (lds_void_ptr)(dst + tw * kMixRegion + 1024 * j), 16, src,
+                                                     0, 0, 0);
         };
         auto gather = [&](int blk, uint8_t* dst) {
             const int myid = gather_ids(blk);
+            if constexpr (MIX) {
 #pragma unroll
-            for (int r8 = 0; r8 < kMLoadsPerBlk; ++r8) gather_row(myid, r8, dst);
+                for (int j = 0; j < kMixGathers; ++j) gather_mix(myid, j, dst);
+            } else {
+#pragma unroll
+                for (int r8 = 0; r8 < kMLoadsPerBlk; ++r8) gather_row(myid, r8, dst);
+            }
         };
+        // gather loads per block and wave: a step waits until only the newest block's are out
+        constexpr int kGathers = MIX ? kMixGathers : kMLoadsPerBlk;
         int aoff[4];
 #pragma unroll
         for (int b4 = 0; b4 < 4; ++b4) aoff[b4] = 16 * ((4 * b4 + g) ^ swz(n16));
@@ -640,11 +700,49 @@ mqa_sparse_ws(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
         // (the gather of a later block into `nxt` is issued row by row between the matrix
         // instructions: its address work and the memory pipeline's intake then overlap them)
         static_assert(kMC / 32 == 2 * kMLoadsPerBlk, "one gathered row every second step of the scores");
-        auto s_phase = [&](int blk, const uint8_t* st, int par, int gblk, uint8_t* nxt) __attribute__((always_inline)) {
+        auto s_phase = [&](int blk, const uint8_t* st, int par, int gblk, uint8_t* nxt,
+                           uint8_t* vdst) __attribute__((always_inline)) {
             const int gid = gather_ids(gblk);
             const uint32_t vg = vmask[blk] >> (4 * g);
-            constexpr int kSD = 8;
             f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+          if constexpr (MIX) {
+            // every operand byte of the block first: 7 fp8 pairs (chunk 4p + g) and the two bf16
+            // steps (chunk 28 + 4e + g), rows n16 and n16 + 16
+            uint4 rq[7][2], rb[2][2];
+#pragma unroll
+            for (int pp = 0; pp < 7; ++pp)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    rq[pp][h] = *reinterpret_cast<const uint4*>(st + mix_pos(n16 + 16 * h, 4 * pp + g));
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    rb[e][h] = *reinterpret_cast<const uint4*>(st + mix_pos(n16 + 16 * h, 28 + 4 * e + g));
+#pragma unroll
+            for (int s = 0; s < kMC / 32; ++s) {
+                bf16x8_t av[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    if (s < 14) {
+                        const uint4 r4 = rq[s >> 1][h];
+                        av[h] = (s & 1) ? fp8x8_to_bf16(r4.z, r4.w) : fp8x8_to_bf16(r4.x, r4.y);
+                    } else {
+                        av[h] = __builtin_bit_cast(bf16x8_t, rb[s - 14][h]);
+                    }
+                }
+                sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[0], qb[s], sacc[0], 0, 0, 0);
+                sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[1], qb[s], sacc[1], 0, 0, 0);
+                if ((s >> 2) == tw) {   // this wave's quarter of the channels, for the value waves
+                    const int ch = s < 14 ? 8 * (s >> 1) + 2 * g + (s & 1) : 4 * s + g;   // 16-byte chunk
+                    const int vo = n16 * kPitch + 256 * (ch >> 4) + 16 * ((ch & 15) ^ swz(n16));
+                    *reinterpret_cast<bf16x8_t*>(vdst + vo) = av[0];
+                    *reinterpret_cast<bf16x8_t*>(vdst + vo + 16 * kPitch) = av[1];
+                }
+                if (s % 3 == 0 && s / 3 < kMixGathers) gather_mix(gid, s / 3, nxt);   // steps 0, 3, 6, 9, 12
+            }
+          } else {
+            constexpr int kSD = 8;
             const uint8_t* arow = st + n16 * kPitch;
             auto lda = [&](int s, int h) {
                 return *reinterpret_cast<const bf16x8_t*>(arow + 16 * kPitch * h + 256 * (s >> 2) + aoff[s & 3]);
@@ -665,6 +763,7 @@ mqa_sparse_ws(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
                 }
                 if ((s & 1) == 0) gather_row(gid, s >> 1, nxt);
             }
+          }
             // online softmax for head 16*tw + n16 (values of lane: keys 16*hb + 4g + i)
             float p[8];
             float bmax = -INFINITY;
@@ -703,46 +802,61 @@ mqa_sparse_ws(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
             xpp[par][tw][lane] = pw;
             if (lane == 0) xflag[par][tw] = resc ? 1 : 0;
         };
+        // the buffer block i is gathered into (bf16: four in turn; MIX: the three raw ones)
+        auto gbuf = [&](int i) -> uint8_t* {
+            if constexpr (MIX) {
+                const int r = i % 3;
+                return r == 0 ? stage_c : r == 1 ? stage_d : stage_e;
+            } else {
+                const int r = i & 3;
+                return r == 0 ? stage_a : r == 1 ? stage_b : r == 2 ? stage_c : stage_d;
+            }
+        };
+        // MIX: the converted copy of block i (parity i % 2)
+        auto vbuf = [&](int i) -> uint8_t* { return (i & 1) ? stage_b : stage_a; };
         // blocks 0 and 1 in flight; block 0 staged before the first barrier
-        gather(0, stage_a);
-        gather(1, stage_b);
-        wait_vmcnt<kMLoadsPerBlk>();
+        gather(0, gbuf(0));
+        gather(1, gbuf(1));
+        wait_vmcnt<kGathers>();
         // step j < nblk: barrier j, gather block j+2 into the buffer block j-2 used (its
         // scores, then its values, are done by now), scores of block j, then wait until block
         // j+1 is staged; every step issues the same loads (no data-dependent branch inside)
-        auto step = [&](int j, const uint8_t* cur, uint8_t* nxt) __attribute__((always_inline)) {
+        auto step = [&](int j) __attribute__((always_inline)) {
             lds_barrier();
-            s_phase(j, cur, j & 1, j + 2, nxt);
-            wait_vmcnt<kMLoadsPerBlk>();
+            s_phase(j, gbuf(j), j & 1, j + 2, gbuf(j + 2), vbuf(j));
+            wait_vmcnt<kGathers>();
         };
         // The first 8 blocks (all of them in decode splits) run as nested straight-line steps:
         // where control flow merges (a loop back-edge, the join after an early exit) the
         // compiler no longer knows which buffer each in-flight gather writes, and would wait
         // for every gather (the one of block j+2 too) before the next block's first read.
+        // (the block numbers are constants here, so every buffer choice folds away)
         if (nblk > 0) {
-            step(0, stage_a, stage_c);
+            step(0);
             if (nblk > 1) {
-                step(1, stage_b, stage_d);
+                step(1);
                 if (nblk > 2) {
-                    step(2, stage_c, stage_a);
+                    step(2);
                     if (nblk > 3) {
-                        step(3, stage_d, stage_b);
+                        step(3);
                         if (nblk > 4) {
-                            step(4, stage_a, stage_c);
+                            step(4);
                             if (nblk > 5) {
-                                step(5, stage_b, stage_d);
+                                step(5);
                                 if (nblk > 6) {
-                                    step(6, stage_c, stage_a);
+                                    step(6);
                                     if (nblk > 7) {
-                                        step(7, stage_d, stage_b);
+                                        step(7);
+                                        // past 8 blocks: bf16 unrolled by the four buffers; MIX
+                                        // chooses its buffers at run time
                                         for (int j = 8; j < nblk; j += 4) {
-                                            step(j, stage_a, stage_c);
+                                            step(j);
                                             if (j + 1 >= nblk) break;
-                                            step(j + 1, stage_b, stage_d);
+                                            step(j + 1);
                                             if (j + 2 >= nblk) break;
-                                            step(j + 2, stage_c, stage_a);
+                                            step(j + 2);
                                             if (j + 3 >= nblk) break;
-                                            step(j + 3, stage_d, stage_b);
+                                            step(j + 3);
                                         }
                                     }
                                 }
@@ -827,8 +941,12 @@ mqa_sparse_ws(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
         // (not unrolled: with four copies of the step and their early exits the compiler
         // copies the accumulators between steps and runs out of registers)
         for (int j = 1; j <= nblk; ++j) {
-            const int sl = (j - 1) & 3;
-            step(j, sl == 0 ? stage_a : sl == 1 ? stage_b : sl == 2 ? stage_c : stage_d);
+            if constexpr (MIX) {
+                step(j, ((j - 1) & 1) ? stage_b : stage_a);
+            } else {
+                const int sl = (j - 1) & 3;
+                step(j, sl == 0 ? stage_a : sl == 1 ? stage_b : sl == 2 ? stage_c : stage_d);
+            }
         }
         __syncthreads();   // every block done, the (m, l) pairs published, no load in flight
         // normalised bf16 rows through LDS (heads 0-31 in A, 32-63 in B, swizzled as the
@@ -937,7 +1055,7 @@ int mqa_splits(int64_t rows, int H, int k) {
 }  // namespace
 
 size_t sparse_mqa_workspace(int64_t batch, int64_t T, int H, int c, int k, int t) {
-    if (t != DT_BF16 || c != kMC || H % kMHeadsWG != 0) return 0;
+    if ((t != DT_BF16 && t != DT_KV_FP8_BF16) || c != kMC || H % kMHeadsWG != 0) return 0;
     const int64_t rows = batch * T;
     const int ks = mqa_splits(rows, H, k);
     if (ks == 1) return 0;
@@ -947,6 +1065,35 @@ size_t sparse_mqa_workspace(int64_t batch, int64_t T, int H, int c, int k, int t
 int launch_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t batch, int64_t T, int64_t N, int H,
                       int c, int k, float scale, int t, void* out, void* ws, hipStream_t stream) {
     if (batch == 0 || T == 0) return 0;
+    if (t == DT_KV_FP8_BF16) {
+        // mixed-precision KV rows: the warp-specialised kernel only (decode shapes)
+        const int64_t rows = batch * T;
+        if (c != kMC || H % kMHeadsWG != 0 || N < 0 || N > 0xffffffffLL / (kMC + 64) || k > kMIdsLds ||
+            rows * (H / kMHeadsWG) > kMFillWGs)
+            return -2;
+        const int ks = mqa_splits(rows, H, k);
+        const int kps = ((k + ks - 1) / ks + kMBlk - 1) / kMBlk * kMBlk;
+        const int64_t units = ((rows + 7) / 8) * 8 * (H / kMHeadsWG) * ks;
+        uint16_t* part = nullptr;
+        float* part_ml = nullptr;
+        if (ks > 1) {
+            part = static_cast<uint16_t*>(ws);
+            part_ml = reinterpret_cast<float*>(part + rows * ks * H * (int64_t)kMC);
+        }
+        hipLaunchKernelGGL(mqa_sparse_ws<true>, dim3((unsigned)units), dim3(kWsWaves * kWave), 0, stream,
+                           static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(kv), idx, rows, T, N, H, k, ks,
+                           kps, scale * kLog2e, static_cast<uint16_t*>(out), part, part_ml);
+        if (ks > 1) {
+            const dim3 cgrid((unsigned)((rows + 7) / 8 * 8 * (H / kCombWaves))), cblock(kCombWaves * kWave);
+            if (ks <= 4)
+                hipLaunchKernelGGL(mqa_combine<4>, cgrid, cblock, 0, stream, part, part_ml, rows, H, ks,
+                                   static_cast<uint16_t*>(out));
+            else
+                hipLaunchKernelGGL(mqa_combine<8>, cgrid, cblock, 0, stream, part, part_ml, rows, H, ks,
+                                   static_cast<uint16_t*>(out));
+        }
+        return 0;
+    }
     if (t == DT_BF16 && c == kMC && H % kMHeadsWG == 0 && N > 0 && N <= kMMaxEntries) {
         const int64_t rows = batch * T;
         const int ks = mqa_splits(rows, H, k);
@@ -961,8 +1108,8 @@ int launch_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t
         }
         const float sl2 = scale * kLog2e;
         if (units <= kMFillWGs)   // at most one workgroup per CU: two waves per SIMD in two roles
-            hipLaunchKernelGGL(mqa_sparse_ws, dim3((unsigned)units), dim3(kWsWaves * kWave), 0, stream,
-                               static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx, rows, T, N, H,
+            hipLaunchKernelGGL(mqa_sparse_ws<false>, dim3((unsigned)units), dim3(kWsWaves * kWave), 0, stream,
+                               static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(kv), idx, rows, T, N, H,
                                k, ks, kps, sl2, static_cast<uint16_t*>(out), part, part_ml);
         else
             hipLaunchKernelGGL((mqa_sparse_mfma<false>), dim3((unsigned)units), dim3(kMWaves * kWave), 0, stream,

@@ -16,8 +16,8 @@ import math
 
 import torch
 
-from . import (csa_compress, csa_index_topk, csa_sparse_mqa, hca_compress, hca_dense_mqa, mqa_workspace_for,
-               workspace_for)
+from . import (CSA_KV_FP8_BF16, KVFp8Bf16, csa_compress, csa_index_topk, csa_sparse_mqa, hca_compress,
+               hca_dense_mqa, mqa_workspace_for, workspace_for)
 
 
 class CsaPrefill:
@@ -70,7 +70,7 @@ class CsaDecode:
         self.idx = torch.empty((batch, T, k), dtype=torch.int32, device=dev)
         self.sel = torch.empty((batch, T, k), dtype=torch.float32, device=dev)
         self.ws = workspace_for(batch, T, N, H_I, k, dev)
-        self.mqa_ws = mqa_workspace_for(q, k)
+        self.mqa_ws = mqa_workspace_for(q, k, CSA_KV_FP8_BF16 if isinstance(kv, KVFp8Bf16) else None)
         self.out = torch.empty_like(q)
 
     def select(self):

@@ -21,7 +21,7 @@ SRC = os.path.join(HERE, "csa_oracle.c")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(BUILD_DIR, "libcsa_oracle.so")
 
-F32, BF16, FP8, MXFP4 = 0, 1, 2, 3
+F32, BF16, FP8, MXFP4, KV_FP8_BF16 = 0, 1, 2, 3, 4
 KEEP_DOUBLE = -1
 
 _lib = None
@@ -53,6 +53,7 @@ def lib():
             "oracle_num_threads": ([], I),
             "oracle_decode": ([P, I, I64, P], I),
             "oracle_decode_mxfp4": ([P, I64, I, P], I),
+            "oracle_decode_kv_fp8_bf16": ([P, I64, I, P], I),
             "oracle_round": ([P, I, I64], I),
             "oracle_csa_compress": ([P, P, P, P, P, P, I64, I64, I, I, I, P], None),
             "oracle_hca_compress": ([P, P, P, I64, I64, I, I, I, P], None),
@@ -100,6 +101,19 @@ def decode_mxfp4(buf: np.ndarray, shape) -> np.ndarray:
     out = np.empty(shape, dtype=np.float64)
     if lib().oracle_decode_mxfp4(_p(buf), rows, c, _p(out)) != 0:
         raise ValueError("bad MXFP4 shape")
+    return out
+
+
+def decode_kv_fp8_bf16(buf: np.ndarray, c: int) -> np.ndarray:
+    """Mixed-precision KV rows (uint8 [..., c + 64]: c - 64 e4m3 bytes, then 64 bf16 values)
+    -> exact float64 [..., c]."""
+    buf = np.ascontiguousarray(buf, dtype=np.uint8)
+    if c < 64 or buf.shape[-1] != c + 64:
+        raise ValueError(f"rows of {buf.shape[-1]} bytes do not hold {c} mixed values")
+    rows = int(np.prod(buf.shape[:-1]))
+    out = np.empty(buf.shape[:-1] + (c,), dtype=np.float64)
+    if lib().oracle_decode_kv_fp8_bf16(_p(buf), rows, c, _p(out)) != 0:
+        raise ValueError("bad mixed KV shape")
     return out
 
 

@@ -103,6 +103,25 @@ int oracle_decode_mxfp4(const uint8_t* buf, int64_t rows, int c, double* dst) {
     return 0;
 }
 
+/* Mixed-precision KV rows ([N] §1.3 and [M] §2.3.4: the RoPE dimensions of a KV entry are
+ * kept in bf16, the others in fp8; [N] §1.3 and [M] §2.3.3 item 2: RoPE covers the last 64
+ * dimensions).  A row of c values is c - 64 OCP e4m3fn bytes (dimensions 0 .. c-65), then
+ * 64 bf16 values (dimensions c-64 .. c-1, little-endian): c + 64 bytes in all. */
+int oracle_decode_kv_fp8_bf16(const uint8_t* buf, int64_t rows, int c, double* dst) {
+    int64_t r;
+    int j;
+    if (c < 64) return -1;
+    for (r = 0; r < rows; ++r) {
+        const uint8_t* row = buf + r * (int64_t)(c + 64);
+        for (j = 0; j < c - 64; ++j) dst[r * c + j] = decode_e4m3(row[j]);
+        for (j = 0; j < 64; ++j) {
+            const uint8_t* p = row + (c - 64) + 2 * j;
+            dst[r * c + (c - 64) + j] = decode_bf16((uint16_t)(p[0] | (p[1] << 8)));
+        }
+    }
+    return 0;
+}
+
 /* Decode `count` stored values of type `dtype` into doubles (exact). */
 int oracle_decode(const void* src, int dtype, int64_t count, double* dst) {
     int64_t i;

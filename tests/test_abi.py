@@ -139,7 +139,19 @@ def test_mqa_rejects_bad_arguments(L):
     assert L.csa_sparse_mqa(A, A, A, 32, 1, 32768, 128, 512, 1024, 0.05, 1, A, None, 0, None) == WORKSPACE
     assert L.csa_sparse_mqa(A, A, A, 32, 1, 32768, 128, 512, 1024, 0.05, 1, A, A, need - 1, None) == WORKSPACE
     assert L.csa_sparse_mqa_workspace_size(1, 8192, 64, 512, 512, 1) == 0   # prefill: no split
+    # mixed fp8 / bf16 KV rows (t = 4): decode shapes only (c = 512, H % 64 == 0, at most 256
+    # (query, 64-head) units, k <= 1024); the split workspace is sized as for bf16
+    mix = 4
+    assert L.csa_sparse_mqa_workspace_size(32, 1, 128, 512, 1024, mix) == need
+    assert L.csa_sparse_mqa(A, A, A, 32, 1, 32768, 128, 512, 1024, 0.05, mix, A, None, 0, None) == WORKSPACE
+    for args in [(2, 1, 100, 64, 256, 64), (2, 1, 100, 96, 512, 64), (257, 1, 100, 64, 512, 64),
+                 (2, 1, 100, 64, 512, 2048), (1, 1, 100, 64, 512, 1025)]:
+        b_, t_, n_, h_, c_, k_ = args
+        assert L.csa_sparse_mqa(A, A, A, b_, t_, n_, h_, c_, k_, 0.05, mix, A, A, 1 << 30, None) == UNSUPPORTED
+    assert L.csa_sparse_mqa(A, A, A, 1, 1, 1 << 23, 64, 512, 64, 0.05, mix, A, A, 1 << 30, None) == UNSUPPORTED
+    assert L.csa_sparse_mqa(A, MIS, A, 1, 1, 100, 64, 512, 64, 0.05, mix, A, A, 1 << 30, None) == INVALID
     g = L.hca_dense_mqa
+    assert g(A, A, 1, 4, 0, 8, 64, 512, 128, 0.125, mix, A, None) == UNSUPPORTED
     assert g(A, A, 1, 4, 0, 8, 4, 64, 0, 0.125, 0, A, None) == INVALID
     assert g(A, A, 1, 4, -5, 8, 4, 64, 128, 0.125, 0, A, None) == INVALID
     assert g(A, MIS, 1, 4, 0, 8, 4, 64, 128, 0.125, 0, A, None) == INVALID

@@ -20,8 +20,15 @@ pytestmark = pytest.mark.gpu
 
 def upload(cfg, host):
     sh = shapes(cfg)
-    return {k: csa.MXFP4(torch.from_numpy(v).cuda(), sh[k][0]) if sh[k][1] == rng.MXFP4 else to_dev(v, sh[k][1])
-            for k, v in host.items()}
+
+    def one(k, v):
+        if sh[k][1] == rng.MXFP4:
+            return csa.MXFP4(torch.from_numpy(v).cuda(), sh[k][0])
+        if sh[k][1] == rng.KV_FP8_BF16:
+            return csa.KVFp8Bf16(torch.from_numpy(v).cuda(), sh[k][0][-1])
+        return to_dev(v, sh[k][1])
+
+    return {k: one(k, v) for k, v in host.items()}
 
 
 def indexer_operands(cfg, h, seqs):
@@ -105,6 +112,8 @@ def _decode_case(name, seqs):
     pipe.run()
     torch.cuda.synchronize()
     sub = {k: h[k][seqs] for k in ("kv", "q", "w")}
+    if cfg.kv_dt == rng.KV_FP8_BF16:
+        sub["kv"] = oracle.decode_kv_fp8_bf16(sub["kv"], cfg.c)
     sub["qI"], sub["kI"] = indexer_operands(cfg, h, seqs)
     sc = oracle.index_scores(sub["qI"], sub["w"], sub["kI"], cfg.m, q_pos0=cfg.q_pos0, qk_dtype=cfg.qk_dt)
     idx, sel = oracle.topk(sc, cfg.m, cfg.k, q_pos0=cfg.q_pos0)
@@ -122,6 +131,12 @@ def _decode_case(name, seqs):
 @pytest.mark.timeout(900)
 def test_cfg2_csa_decode_128k_sampled():
     _decode_case("cfg2_csa_decode_128k", np.array([0, 7, 19, 31]))
+
+
+@pytest.mark.timeout(900)
+def test_cfg2_csa_decode_128k_kvmixed_sampled():
+    """The 128K decode with its KV entries stored as 448 fp8 channels and 64 bf16 ones."""
+    _decode_case("cfg2_csa_decode_128k_kvmixed", np.array([0, 11, 31]))
 
 
 @pytest.mark.timeout(900)

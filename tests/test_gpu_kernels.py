@@ -282,6 +282,35 @@ def test_sparse_mqa_parity(case):
     out_tol(dt)(got, ref, "sparse_mqa")
 
 
+MIXED_KV_CASES = [  # batch, T, N, H, k  (c = 512; KV rows: 448 fp8 channels, 64 bf16)
+    (2, 1, 5000, 64, 1024),      # keys split over eight workgroups
+    (4, 2, 2000, 128, 333),      # k off the 32-key block, two 64-head groups
+    (32, 4, 1500, 128, 1024),    # 256 units, one key range each: 32 blocks per workgroup
+    (3, 1, 700, 64, 1024),       # fewer entries than k: pads
+    (1, 1, 0, 64, 40),           # no entries at all: zeros
+]
+
+
+@pytest.mark.parametrize("case", MIXED_KV_CASES, ids=lambda c: "b%d_T%d_N%d_H%d_k%d" % c)
+def test_sparse_mqa_mixed_kv_parity(case):
+    batch, T, N, H, k = case
+    c = 512
+    say(f"csa_sparse_mqa fp8/bf16 KV {case}")
+    sd = 1400 + N
+    q = draw(sd, 1, (batch, T, H, c), BF16)
+    kvm = rng.normal(sd, 2, (batch, N, c), rng.KV_FP8_BF16)
+    idx = _distinct_ids(np.random.RandomState(sd), batch, T, N, k) if N > 0 else np.full((batch, T, k), -1, np.int32)
+    idx[0, 0, :] = -1                       # a query with nothing selected -> zeros
+    if N > 0:
+        idx[-1, -1, 0] = N + 5              # an id past the entries is skipped
+    scale = 1.0 / np.sqrt(c)
+    ref = oracle.sparse_mqa(q, oracle.decode_kv_fp8_bf16(kvm, c), idx, scale, dtype=BF16)
+    kv_dev = csa.KVFp8Bf16(torch.from_numpy(kvm).cuda(), c)
+    got = from_dev(csa.csa_sparse_mqa(to_dev(q, BF16), kv_dev, torch.from_numpy(idx).cuda(), scale))
+    assert not got[0, 0].any()
+    out_tol(BF16)(got, ref, "sparse_mqa fp8/bf16 KV")
+
+
 DENSE_CASES = [  # batch, T, q_pos0, N, H, c, m', dtype
     (1, 40, 0, 9, 4, 64, 4, F32),
     (1, 64, 128 * 300 - 40, 300, 64, 512, 128, BF16),

@@ -45,6 +45,37 @@ def test_decode_e4m3_matches_torch_all_codes(orc):
 E2M1_SPEC = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]   # codes 0..7, the spec's FP4 E2M1 values
 
 
+def test_decode_kv_fp8_bf16_layout(orc):
+    """Mixed KV rows (the notes page §1.3: RoPE channels in bf16, the rest in fp8; RoPE on the
+    last 64 channels): c - 64 e4m3 bytes, then 64 little-endian bf16 values.  Values from the
+    formats' definitions: e4m3 0x38 = 1, 0xB8 = -1, 0x01 = 2^-9 (subnormal), 0x08 = 2^-6,
+    0x7E = 448; bf16 0x3F80 = 1, 0xC040 = -3, 0x0001 = 2^-133."""
+    c = 128
+    buf = np.zeros((2, c + 64), np.uint8)
+    buf[0, :5] = [0x38, 0xB8, 0x01, 0x08, 0x7E]
+    buf[1, c - 65] = 0x38                       # the last fp8 channel of row 1
+    bf = np.zeros((2, 64), np.uint16)
+    bf[0, 0], bf[0, 63], bf[1, 1] = 0x3F80, 0xC040, 0x0001
+    buf[:, c - 64:] = bf.astype("<u2").view(np.uint8).reshape(2, 128)
+    dec = orc.decode_kv_fp8_bf16(buf, c)
+    exp = np.zeros((2, c))
+    exp[0, :5] = [1.0, -1.0, 2.0 ** -9, 2.0 ** -6, 448.0]
+    exp[1, c - 65] = 1.0
+    exp[0, c - 64], exp[0, c - 1], exp[1, c - 63] = 1.0, -3.0, 2.0 ** -133
+    assert np.array_equal(dec, exp)
+
+
+def test_kv_fp8_bf16_generator_rounds_each_part_as_torch(orc):
+    """The generator's mixed rows, decoded by the oracle, equal torch's own roundings of the
+    same float32 draws: float8_e4m3fn for the first c - 64 channels, bfloat16 for the rest."""
+    x = rng.normal(7, 3, (6, 512), rng.F32)
+    dec = orc.decode_kv_fp8_bf16(rng.f32_to_kv_fp8_bf16(x), 512)
+    t = torch.from_numpy(x)
+    assert np.array_equal(dec[:, :448], t[:, :448].to(torch.float8_e4m3fn).double().numpy())
+    assert np.array_equal(dec[:, 448:], t[:, 448:].to(torch.bfloat16).double().numpy())
+    assert np.array_equal(rng.kv_fp8_bf16_to_f32(rng.f32_to_kv_fp8_bf16(x), 512), dec.astype(np.float32))
+
+
 def test_decode_mxfp4_elements_match_the_spec_table(orc):
     # one row of 32 values holding all 16 codes twice, scale 2^0: code 8 + j is -(code j)
     codes = np.concatenate([np.arange(16), np.arange(16)[::-1]]).astype(np.uint8)

@@ -17,7 +17,7 @@ import numpy as np
 
 from . import rng
 
-F32, BF16, FP8, MXFP4 = rng.F32, rng.BF16, rng.FP8, rng.MXFP4
+F32, BF16, FP8, MXFP4, KV_FP8_BF16 = rng.F32, rng.BF16, rng.FP8, rng.MXFP4, rng.KV_FP8_BF16
 
 # tensor ids, fixed forever (changing one changes every input)
 TID = {
@@ -44,6 +44,7 @@ class Config:
     H_I: int = 0         # indexer heads
     c_I: int = 0         # indexer head dim
     qk_dt: int = F32     # indexer q / key dtype
+    kv_dt: int = -1      # storage of the compressed KV entries given to decode (-1: dt)
     T: int = 0           # query tokens per sequence
     q_pos0: int = 0      # absolute position of query 0
     N: int = 0           # compressed entries per sequence
@@ -77,6 +78,11 @@ CONFIGS = {
     "cfg2_csa_decode_128k_mxfp4": Config("cfg2_csa_decode_128k_mxfp4", "csa_decode", batch=32, dt=BF16, c=512,
                                          H=128, k=1024, m=4, H_I=64, c_I=128, qk_dt=MXFP4, T=1,
                                          q_pos0=131072, N=32768, seed=1002),
+    # the decode at a 128K context with the KV entries in the mixed storage (the notes page's
+    # §1.3: RoPE channels in bf16, the others in fp8); same seed and draws as the bf16 decode
+    "cfg2_csa_decode_128k_kvmixed": Config("cfg2_csa_decode_128k_kvmixed", "csa_decode", batch=32, dt=BF16, c=512,
+                                           H=128, k=1024, m=4, H_I=64, c_I=128, qk_dt=FP8, T=1,
+                                           q_pos0=131072, N=32768, seed=1002, kv_dt=KV_FP8_BF16),
 }
 ORDER = list(CONFIGS)
 
@@ -96,7 +102,7 @@ def shapes(cfg: Config) -> dict:
         for nm in ("IBa", "IBb"):
             s[nm] = ((m, cI), F32, ("normal", 0.1))
     if cfg.kind == "csa_decode":
-        s["kv"] = ((B, cfg.N, c), cfg.dt, ("normal", 1.0))
+        s["kv"] = ((B, cfg.N, c), cfg.dt if cfg.kv_dt < 0 else cfg.kv_dt, ("normal", 1.0))
         s["kI"] = ((B, cfg.N, cfg.c_I), cfg.qk_dt, ("normal", 1.0))
     if cfg.kind in ("csa_prefill", "csa_decode"):
         s["q"] = ((B, cfg.T, cfg.H, c), cfg.dt, ("normal", 1.0))

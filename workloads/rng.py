@@ -1,7 +1,7 @@
 """Seeded, counter-based synthetic inputs shared by the tests, the smoke check and the benchmark.
 
 This module draws random numbers and stores them in the storage dtypes the kernels read
-(fp32, bf16, OCP fp8 e4m3fn, OCP MXFP4).  It holds none of the attention method's arithmetic: no
+(fp32, bf16, OCP fp8 e4m3fn, OCP MXFP4, and KV rows mixing fp8 and bf16).  It holds none of the attention method's arithmetic: no
 softmax, no pooling, no scoring.  Both the HIP path and the CPU oracle receive the very
 bytes produced here.
 
@@ -27,6 +27,10 @@ nearest E2M1 value, ties to the even code, saturating at +-6).
 MXFP4 storage of a tensor whose rows hold c values (c % 32 == 0): all rows' element bytes
 first, c/2 bytes per row with value 2i in the low nibble of byte i and 2i+1 in the high
 nibble, then all rows' scales, c/32 E8M0 bytes per row; one flat uint8 array.
+
+Mixed-precision KV storage (fp8 + bf16) of rows of c values: per row c - 64 e4m3fn bytes
+(values 0 .. c-65), then the last 64 values as bf16 (little-endian): c + 64 bytes a row,
+uint8 [..., c + 64].  Each part is rounded as its dtype alone.
 """
 from __future__ import annotations
 
@@ -40,8 +44,9 @@ _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
 
 # Storage dtype codes; the values match the C-ABI enum csa_dtype.
-F32, BF16, FP8, MXFP4 = 0, 1, 2, 3
-DTYPE_NAMES = {F32: "f32", BF16: "bf16", FP8: "fp8_e4m3", MXFP4: "mxfp4"}
+F32, BF16, FP8, MXFP4, KV_FP8_BF16 = 0, 1, 2, 3, 4
+DTYPE_NAMES = {F32: "f32", BF16: "bf16", FP8: "fp8_e4m3", MXFP4: "mxfp4", KV_FP8_BF16: "kv_fp8_bf16"}
+KV_ROPE = 64   # trailing values of a mixed KV row kept in bf16
 MX_BLOCK = 32
 NP_STORAGE = {F32: np.float32, BF16: np.uint16, FP8: np.uint8}
 
@@ -184,6 +189,29 @@ def mxfp4_rows(buf: np.ndarray, rows: int, c: int, r0: int, r1: int) -> np.ndarr
     return np.concatenate([buf[r0 * eb:r1 * eb], buf[rows * eb + r0 * sb:rows * eb + r1 * sb]])
 
 
+def f32_to_kv_fp8_bf16(x32: np.ndarray) -> np.ndarray:
+    """float32 [..., c] -> mixed KV storage uint8 [..., c + 64]."""
+    x32 = np.asarray(x32, dtype=np.float32)
+    c = x32.shape[-1]
+    assert c >= KV_ROPE
+    out = np.empty(x32.shape[:-1] + (c + KV_ROPE,), dtype=np.uint8)
+    out[..., : c - KV_ROPE] = f32_to_e4m3_bits(x32[..., : c - KV_ROPE])
+    bf = np.ascontiguousarray(f32_to_bf16_bits(x32[..., c - KV_ROPE:]).astype("<u2"))
+    out[..., c - KV_ROPE:] = bf.view(np.uint8).reshape(x32.shape[:-1] + (2 * KV_ROPE,))
+    return out
+
+
+def kv_fp8_bf16_to_f32(buf: np.ndarray, c: int) -> np.ndarray:
+    """Mixed KV storage uint8 [..., c + 64] -> float32 [..., c]."""
+    buf = np.asarray(buf, dtype=np.uint8)
+    assert buf.shape[-1] == c + KV_ROPE
+    out = np.empty(buf.shape[:-1] + (c,), dtype=np.float32)
+    out[..., : c - KV_ROPE] = e4m3_bits_to_f32(buf[..., : c - KV_ROPE])
+    bf = np.ascontiguousarray(buf[..., c - KV_ROPE:]).view("<u2")
+    out[..., c - KV_ROPE:] = bf16_bits_to_f32(bf)
+    return out
+
+
 def to_storage(x64: np.ndarray, dtype: int) -> np.ndarray:
     x32 = np.asarray(x64, dtype=np.float64).astype(np.float32)
     if dtype == F32:
@@ -233,6 +261,20 @@ def normal(seed: int, tid: int, shape, dtype: int = F32, std: float = 1.0) -> np
     (MXFP4: the flat storage of rows of shape[-1] values; the same draws as the other dtypes)."""
     if dtype == MXFP4:
         return f32_to_mxfp4(_fill(shape, F32, lambda s, c: std * _normal_chunk(seed, tid, s, c)))
+    if dtype == KV_FP8_BF16:   # uint8 [..., c + 64]; drawn and converted a block of rows at a time
+        c = int(shape[-1])
+        rows = int(np.prod(shape[:-1]))
+        out = np.empty((rows, c + KV_ROPE), dtype=np.uint8)
+        step = max(1, _CHUNK // c)
+
+        def work(r0):
+            r1 = min(rows, r0 + step)
+            x = (std * _normal_chunk(seed, tid, r0 * c, (r1 - r0) * c)).astype(np.float32)
+            out[r0:r1] = f32_to_kv_fp8_bf16(x.reshape(r1 - r0, c))
+
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(work, range(0, rows, step)))
+        return out.reshape(tuple(shape[:-1]) + (c + KV_ROPE,))
     return _fill(shape, dtype, lambda s, c: std * _normal_chunk(seed, tid, s, c))
 
 
