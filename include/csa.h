@@ -191,6 +191,22 @@ int csa_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t ba
 int hca_dense_mqa(const void* q, const void* kv, int64_t batch, int64_t T, int64_t q_pos0, int64_t N, int H,
                   int c, int m_prime, float scale, csa_dtype t, void* out, csa_stream_t stream);
 
+/*
+ * csa_sparse_mqa_sink / hca_dense_mqa_sink — the same attention with an attention sink ([N]
+ * §1.3 and [M] §2.3.3 item 4): head h has a learned logit sink[h] (natural-log units, like
+ * scale * q . kv) that joins the softmax denominator,
+ *     weight_s = exp(z_s) / (sum_r exp(z_r) + exp(sink[h])),
+ * so a head may give part of its attention to nothing.  A query with no entry still gets a
+ * zero output.  sink: device fp32 [H], 4-byte aligned, or NULL (the plain entry point's
+ * result).  Other arguments, dtypes and limits as csa_sparse_mqa / hca_dense_mqa.
+ */
+int csa_sparse_mqa_sink(const void* q, const void* kv, const int32_t* idx, int64_t batch, int64_t T, int64_t N,
+                        int H, int c, int k, float scale, const float* sink, csa_dtype t, void* out, void* workspace,
+                        size_t ws_bytes, csa_stream_t stream);
+int hca_dense_mqa_sink(const void* q, const void* kv, int64_t batch, int64_t T, int64_t q_pos0, int64_t N, int H,
+                       int c, int m_prime, float scale, const float* sink, csa_dtype t, void* out,
+                       csa_stream_t stream);
+
 /* Human-readable name of a csa_status value (static storage). */
 const char* csa_status_string(int status);
 

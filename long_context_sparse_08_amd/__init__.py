@@ -21,8 +21,8 @@ STATUS = {0: "CSA_OK", -1: "CSA_ERR_INVALID_ARG", -2: "CSA_ERR_UNSUPPORTED", -3:
           -4: "CSA_ERR_HIP"}
 
 ENTRY_POINTS = ("csa_compress", "hca_compress", "csa_index_topk_workspace_size", "csa_index_topk",
-                "csa_index_scores", "csa_topk_workspace_size", "csa_topk", "csa_sparse_mqa_workspace_size", "csa_sparse_mqa", "hca_dense_mqa",
-                "csa_status_string", "csa_version")
+                "csa_index_scores", "csa_topk_workspace_size", "csa_topk", "csa_sparse_mqa_workspace_size", "csa_sparse_mqa",
+                "hca_dense_mqa", "csa_sparse_mqa_sink", "hca_dense_mqa_sink", "csa_status_string", "csa_version")
 
 
 class CsaError(RuntimeError):
@@ -47,6 +47,8 @@ def _load():
         "csa_sparse_mqa_workspace_size": ([I64, I64, I, I, I, I], SZ),
         "csa_sparse_mqa": ([P, P, P, I64, I64, I64, I, I, I, F, I, P, P, SZ, P], I),
         "hca_dense_mqa": ([P, P, I64, I64, I64, I64, I, I, I, F, I, P, P], I),
+        "csa_sparse_mqa_sink": ([P, P, P, I64, I64, I64, I, I, I, F, P, I, P, P, SZ, P], I),
+        "hca_dense_mqa_sink": ([P, P, I64, I64, I64, I64, I, I, I, F, P, I, P, P], I),
         "csa_status_string": ([I], ctypes.c_char_p),
         "csa_version": ([], I),
     }
@@ -242,9 +244,16 @@ def mqa_workspace_for(q: torch.Tensor, k: int, dtype: int | None = None):
     return None if nbytes == 0 else torch.empty(nbytes, dtype=torch.uint8, device=q.device)
 
 
-def csa_sparse_mqa(q, kv, idx, scale: float, out=None, workspace=None):
+def _sink(sink, H, dev):
+    if sink is None:
+        return None
+    assert sink.dtype == torch.float32 and tuple(sink.shape) == (H,) and sink.device == dev and sink.is_contiguous()
+    return sink
+
+
+def csa_sparse_mqa(q, kv, idx, scale: float, out=None, workspace=None, sink=None):
     """q [batch, T, H, c], kv [batch, N, c] (or KVFp8Bf16 with bf16 q), idx [batch, T, k] int32
-    -> out [batch, T, H, c]."""
+    -> out [batch, T, H, c].  sink: optional fp32 [H] per-head sink logits (attention sink)."""
     mixed = isinstance(kv, KVFp8Bf16)
     kvt = kv.data if mixed else kv
     dev = _dev(q, kvt, idx, out, workspace)
@@ -263,18 +272,20 @@ def csa_sparse_mqa(q, kv, idx, scale: float, out=None, workspace=None):
     if workspace is None:
         workspace = mqa_workspace_for(q, k, dt)
     ws_bytes = 0 if workspace is None else workspace.numel()
-    _check("csa_sparse_mqa", lib.csa_sparse_mqa(_p(q), _p(kvt), _p(idx), batch, T, N, H, c, k, float(scale), dt,
-                                                _p(out), _p(workspace), ws_bytes, _stream(dev)))
+    sk = _sink(sink, H, dev)
+    _check("csa_sparse_mqa", lib.csa_sparse_mqa_sink(_p(q), _p(kvt), _p(idx), batch, T, N, H, c, k, float(scale), _p(sk),
+                                                     dt, _p(out), _p(workspace), ws_bytes, _stream(dev)))
     return out
 
 
-def hca_dense_mqa(q, kv, q_pos0: int, m_prime: int, scale: float, out=None):
+def hca_dense_mqa(q, kv, q_pos0: int, m_prime: int, scale: float, out=None, sink=None):
     dev = _dev(q, kv, out)
     batch, T, H, c = q.shape
     N = kv.shape[1]
     assert kv.shape == (batch, N, c) and kv.dtype == q.dtype
     if out is None:
         out = torch.empty_like(q)
-    _check("hca_dense_mqa", lib.hca_dense_mqa(_p(q), _p(kv), batch, T, q_pos0, N, H, c, m_prime, float(scale), _dt(q),
-                                              _p(out), _stream(dev)))
+    sk = _sink(sink, H, dev)
+    _check("hca_dense_mqa", lib.hca_dense_mqa_sink(_p(q), _p(kv), batch, T, q_pos0, N, H, c, m_prime, float(scale),
+                                                   _p(sk), _dt(q), _p(out), _stream(dev)))
     return out

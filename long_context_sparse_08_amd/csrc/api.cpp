@@ -199,6 +199,13 @@ size_t csa_sparse_mqa_workspace_size(int64_t batch, int64_t T, int H, int c, int
 
 int csa_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t batch, int64_t T, int64_t N, int H, int c,
                    int k, float scale, csa_dtype t, void* out, void* workspace, size_t ws_bytes, csa_stream_t stream) {
+    return csa_sparse_mqa_sink(q, kv, idx, batch, T, N, H, c, k, scale, nullptr, t, out, workspace, ws_bytes, stream);
+}
+
+int csa_sparse_mqa_sink(const void* q, const void* kv, const int32_t* idx, int64_t batch, int64_t T, int64_t N, int H,
+                        int c, int k, float scale, const float* sink, csa_dtype t, void* out, void* workspace,
+                        size_t ws_bytes, csa_stream_t stream) {
+    if (sink && (reinterpret_cast<uintptr_t>(sink) & 3u)) return CSA_ERR_INVALID_ARG;
     const bool mixed = t == CSA_KV_FP8_BF16;   // q and out are bf16 then
     int rc = check_mqa(q, kv, out, batch, T, N, H, c, scale, mixed ? CSA_BF16 : t);
     if (rc != CSA_OK) return rc;
@@ -210,18 +217,24 @@ int csa_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t ba
     if (!idx) return CSA_ERR_INVALID_ARG;
     const size_t need = csa_sparse_mqa_workspace_size(batch, T, H, c, k, t);
     if (need > 0 && (!workspace || ws_bytes < need || !aligned16(workspace))) return CSA_ERR_WORKSPACE;
-    return finish(csa::launch_sparse_mqa(q, kv, idx, batch, T, N, H, c, k, scale, t, out, workspace,
+    return finish(csa::launch_sparse_mqa(q, kv, idx, batch, T, N, H, c, k, scale, t, out, workspace, sink,
                                          static_cast<hipStream_t>(stream)));
 }
 
 int hca_dense_mqa(const void* q, const void* kv, int64_t batch, int64_t T, int64_t q_pos0, int64_t N, int H, int c,
                   int m_prime, float scale, csa_dtype t, void* out, csa_stream_t stream) {
+    return hca_dense_mqa_sink(q, kv, batch, T, q_pos0, N, H, c, m_prime, scale, nullptr, t, out, stream);
+}
+
+int hca_dense_mqa_sink(const void* q, const void* kv, int64_t batch, int64_t T, int64_t q_pos0, int64_t N, int H, int c,
+                       int m_prime, float scale, const float* sink, csa_dtype t, void* out, csa_stream_t stream) {
+    if (sink && (reinterpret_cast<uintptr_t>(sink) & 3u)) return CSA_ERR_INVALID_ARG;
     int rc = check_mqa(q, kv, out, batch, T, N, H, c, scale, t);
     if (rc != CSA_OK) return rc;
     if (m_prime < 1 || q_pos0 < 0) return CSA_ERR_INVALID_ARG;
     if (m_prime > CSA_MAX_RATIO) return CSA_ERR_UNSUPPORTED;
     if (batch == 0 || T == 0) return CSA_OK;
-    return finish(csa::launch_dense_mqa(q, kv, batch, T, q_pos0, N, H, c, m_prime, scale, t, out,
+    return finish(csa::launch_dense_mqa(q, kv, batch, T, q_pos0, N, H, c, m_prime, scale, t, out, sink,
                                         static_cast<hipStream_t>(stream)));
 }
 

@@ -52,12 +52,13 @@ int topk_zero_words(int64_t rows, int64_t nv_max);
 uint32_t* topk_zero_region(void* extra_ws, int64_t rows, int64_t N);
 
 // Device workspace bytes launch_sparse_mqa needs (0: none) for the key-range partials.
+// `sink` (both MQA launchers): per-head sink logits [H] in natural-log units, or nullptr.
 size_t sparse_mqa_workspace(int64_t batch, int64_t T, int H, int c, int k, int t);
 
 int launch_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t batch, int64_t T, int64_t N, int H,
-                      int c, int k, float scale, int t, void* out, void* ws, hipStream_t stream);
+                      int c, int k, float scale, int t, void* out, void* ws, const float* sink, hipStream_t stream);
 
 int launch_dense_mqa(const void* q, const void* kv, int64_t batch, int64_t T, int64_t q_pos0, int64_t N, int H, int c,
-                     int ratio, float scale, int t, void* out, hipStream_t stream);
+                     int ratio, float scale, int t, void* out, const float* sink, hipStream_t stream);
 
 }  // namespace csa

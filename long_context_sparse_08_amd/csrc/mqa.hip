@@ -21,10 +21,19 @@ namespace {
 constexpr int kGenWaves = 4;
 constexpr int kKeyBatch = 4;
 
+// Attention sink ([N] §1.3 and [M] §2.3.3 item 4: a learned per-head logit z' joins the
+// softmax denominator as exp(z')): its term against the reference maximum m (log2 units) of
+// a head's accumulated weights.  None without sink logits or before any entry was seen (the
+// output is zero then anyway).
+__device__ __forceinline__ float sink_term(const float* sink, int64_t head, float m) {
+    return (sink != nullptr && m != -INFINITY) ? exp2f(sink[head] * kLog2e - m) : 0.f;
+}
+
 template <int DT, int CPL, bool DENSE>
 __global__ void __launch_bounds__(kGenWaves * kWave)
 mqa_generic(const void* __restrict__ q, const void* __restrict__ kv, const int32_t* __restrict__ idx, int64_t T,
-            int64_t N, int H, int c, int k, float scale, int64_t q_pos0, int ratio, void* __restrict__ out) {
+            int64_t N, int H, int c, int k, float scale, int64_t q_pos0, int ratio, void* __restrict__ out,
+            const float* __restrict__ sink) {
     const int lane = threadIdx.x & (kWave - 1);
     const int h = blockIdx.y * kGenWaves + threadIdx.x / kWave;
     const int64_t row = blockIdx.x;  // b*T + t
@@ -83,7 +92,8 @@ mqa_generic(const void* __restrict__ q, const void* __restrict__ kv, const int32
             mx = nm;
         }
     }
-    const float rden = den > 0.f ? 1.f / den : 0.f;
+    const float dtot = den + sink_term(sink, h, mx);
+    const float rden = dtot > 0.f ? 1.f / dtot : 0.f;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
         const int d = lane + kWave * j;
@@ -93,7 +103,7 @@ mqa_generic(const void* __restrict__ q, const void* __restrict__ kv, const int32
 
 template <int DT, bool DENSE>
 int launch_generic(const void* q, const void* kv, const int32_t* idx, int64_t batch, int64_t T, int64_t N, int H, int c,
-                   int k, float scale, int64_t q_pos0, int ratio, void* out, hipStream_t stream) {
+                   int k, float scale, int64_t q_pos0, int ratio, void* out, const float* sink, hipStream_t stream) {
     const int64_t rows = batch * T;
     if (rows > 0x7fffffffLL) return -2;
     const int cpl = (c + kWave - 1) / kWave;
@@ -101,7 +111,7 @@ int launch_generic(const void* q, const void* kv, const int32_t* idx, int64_t ba
 #define CSA_LAUNCH_CPL(C)                                                                                          \
     if (cpl <= C) {                                                                                                \
         hipLaunchKernelGGL((mqa_generic<DT, C, DENSE>), grid, dim3(kGenWaves * kWave), 0, stream, q, kv, idx, T, N, H, \
-                           c, k, scale, q_pos0, ratio, out);                                                       \
+                           c, k, scale, q_pos0, ratio, out, sink);                                                 \
         return 0;                                                                                                  \
     }
     CSA_LAUNCH_CPL(1)
@@ -240,7 +250,7 @@ __global__ void __launch_bounds__(kMWaves * kWave, 2)   // two workgroups per CU
 mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
                 int64_t rows, int64_t T, int64_t N, int H, int k, int ks_count, int keys_per_split, float sl2,
                 int64_t q_pos0, int ratio, uint16_t* __restrict__ out, uint16_t* __restrict__ part,
-                float* __restrict__ part_ml) {
+                float* __restrict__ part_ml, const float* __restrict__ sink) {
     // one array per pipeline parity: the DMA into one and the reads of the other are then
     // provably disjoint, so no wait for the in-flight gather is forced before the current
     // block's LDS reads
@@ -488,7 +498,8 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     l_run = sum_xor32(sum_xor16(l_run));
     if (g == 0) {
         xm[tw][n16] = m_run;
-        xl[tw][n16] = l_run;
+        // a complete row's denominator takes the sink here; key-range partials leave it to the merge
+        xl[tw][n16] = l_run + (part == nullptr ? sink_term(sink, h0 + 16 * tw + n16, m_run) : 0.f);
     }
     __syncthreads();   // every wave is past its last block: the staging buffers are free
     // Normalised bf16 rows go through LDS (heads 0-31 in A, 32-63 in B, one row per head) so
@@ -578,7 +589,8 @@ template <bool MIX>
 __global__ void __launch_bounds__(kWsWaves * kWave, 1)
 mqa_sparse_ws(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kvb, const int32_t* __restrict__ idx,
               int64_t rows, int64_t T, int64_t N, int H, int k, int ks_count, int keys_per_split, float sl2,
-              uint16_t* __restrict__ out, uint16_t* __restrict__ part, float* __restrict__ part_ml) {
+              uint16_t* __restrict__ out, uint16_t* __restrict__ part, float* __restrict__ part_ml,
+              const float* __restrict__ sink) {
     constexpr int kPitch = kMPitch<true>, kBuf = kMBuf<true>;
     constexpr int kRawBuf = kMHT * kMixRegion;
     constexpr int kRowB = MIX ? kMixRowB : 2 * kMC;   // bytes of one KV row in memory
@@ -871,7 +883,8 @@ mqa_sparse_ws(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kvb, c
         l_run = sum_xor32(sum_xor16(l_run));
         if (g == 0) {
             xm[tw][n16] = m_run;
-            xl[tw][n16] = l_run;
+            // a complete row's denominator takes the sink here; key-range partials leave it to the merge
+            xl[tw][n16] = l_run + (part == nullptr ? sink_term(sink, h0 + 16 * tw + n16, m_run) : 0.f);
             if (part != nullptr) {
                 const int64_t prow = (row * ks_count + ks) * H + h0 + 16 * tw + n16;
                 part_ml[2 * prow] = m_run;
@@ -992,7 +1005,7 @@ constexpr int kCombWaves = 4;
 template <int CG>
 __global__ void __launch_bounds__(kCombWaves * kWave)
 mqa_combine(const uint16_t* __restrict__ part, const float* __restrict__ part_ml, int64_t rows, int H, int ks_count,
-            uint16_t* __restrict__ out) {
+            uint16_t* __restrict__ out, const float* __restrict__ sink) {
     constexpr int kCombGroup = CG;
     // XCD-aware order (as the attention kernel's): row r on XCD r % 8, whose L2 holds the
     // row's partials; H / kCombWaves workgroups per row (H % 64 == 0 on this path)
@@ -1036,6 +1049,7 @@ mqa_combine(const uint16_t* __restrict__ part, const float* __restrict__ part_ml
             }
         }
     }
+    L += sink_term(sink, head, M);
     const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] *= inv;
@@ -1063,7 +1077,7 @@ size_t sparse_mqa_workspace(int64_t batch, int64_t T, int H, int c, int k, int t
 }
 
 int launch_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t batch, int64_t T, int64_t N, int H,
-                      int c, int k, float scale, int t, void* out, void* ws, hipStream_t stream) {
+                      int c, int k, float scale, int t, void* out, void* ws, const float* sink, hipStream_t stream) {
     if (batch == 0 || T == 0) return 0;
     if (t == DT_KV_FP8_BF16) {
         // mixed-precision KV rows: the warp-specialised kernel only (decode shapes)
@@ -1082,15 +1096,15 @@ int launch_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t
         }
         hipLaunchKernelGGL(mqa_sparse_ws<true>, dim3((unsigned)units), dim3(kWsWaves * kWave), 0, stream,
                            static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(kv), idx, rows, T, N, H, k, ks,
-                           kps, scale * kLog2e, static_cast<uint16_t*>(out), part, part_ml);
+                           kps, scale * kLog2e, static_cast<uint16_t*>(out), part, part_ml, sink);
         if (ks > 1) {
             const dim3 cgrid((unsigned)((rows + 7) / 8 * 8 * (H / kCombWaves))), cblock(kCombWaves * kWave);
             if (ks <= 4)
                 hipLaunchKernelGGL(mqa_combine<4>, cgrid, cblock, 0, stream, part, part_ml, rows, H, ks,
-                                   static_cast<uint16_t*>(out));
+                                   static_cast<uint16_t*>(out), sink);
             else
                 hipLaunchKernelGGL(mqa_combine<8>, cgrid, cblock, 0, stream, part, part_ml, rows, H, ks,
-                                   static_cast<uint16_t*>(out));
+                                   static_cast<uint16_t*>(out), sink);
         }
         return 0;
     }
@@ -1110,29 +1124,29 @@ int launch_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t
         if (units <= kMFillWGs)   // at most one workgroup per CU: two waves per SIMD in two roles
             hipLaunchKernelGGL(mqa_sparse_ws<false>, dim3((unsigned)units), dim3(kWsWaves * kWave), 0, stream,
                                static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(kv), idx, rows, T, N, H,
-                               k, ks, kps, sl2, static_cast<uint16_t*>(out), part, part_ml);
+                               k, ks, kps, sl2, static_cast<uint16_t*>(out), part, part_ml, sink);
         else
             hipLaunchKernelGGL((mqa_sparse_mfma<false>), dim3((unsigned)units), dim3(kMWaves * kWave), 0, stream,
                                static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx, rows, T, N, H,
-                               k, ks, kps, sl2, (int64_t)0, 1, static_cast<uint16_t*>(out), part, part_ml);
+                               k, ks, kps, sl2, (int64_t)0, 1, static_cast<uint16_t*>(out), part, part_ml, sink);
         if (ks > 1) {
             const dim3 cgrid((unsigned)((rows + 7) / 8 * 8 * (H / kCombWaves))), cblock(kCombWaves * kWave);
             if (ks <= 4)
                 hipLaunchKernelGGL(mqa_combine<4>, cgrid, cblock, 0, stream, part, part_ml, rows, H, ks,
-                                   static_cast<uint16_t*>(out));
+                                   static_cast<uint16_t*>(out), sink);
             else
                 hipLaunchKernelGGL(mqa_combine<8>, cgrid, cblock, 0, stream, part, part_ml, rows, H, ks,
-                                   static_cast<uint16_t*>(out));
+                                   static_cast<uint16_t*>(out), sink);
         }
         return 0;
     }
-    if (t == DT_F32) return launch_generic<DT_F32, false>(q, kv, idx, batch, T, N, H, c, k, scale, 0, 1, out, stream);
-    if (t == DT_BF16) return launch_generic<DT_BF16, false>(q, kv, idx, batch, T, N, H, c, k, scale, 0, 1, out, stream);
+    if (t == DT_F32) return launch_generic<DT_F32, false>(q, kv, idx, batch, T, N, H, c, k, scale, 0, 1, out, sink, stream);
+    if (t == DT_BF16) return launch_generic<DT_BF16, false>(q, kv, idx, batch, T, N, H, c, k, scale, 0, 1, out, sink, stream);
     return -2;
 }
 
 int launch_dense_mqa(const void* q, const void* kv, int64_t batch, int64_t T, int64_t q_pos0, int64_t N, int H, int c,
-                     int ratio, float scale, int t, void* out, hipStream_t stream) {
+                     int ratio, float scale, int t, void* out, const float* sink, hipStream_t stream) {
     if (batch == 0 || T == 0) return 0;
     if (t == DT_BF16 && c == kMC && H % kMHeadsWG == 0 && N <= kMMaxEntries) {
         // one workgroup per (query, 64 heads) walks every visible entry: no key split, no
@@ -1142,13 +1156,14 @@ int launch_dense_mqa(const void* q, const void* kv, int64_t batch, int64_t T, in
         if (units > 0x7fffffffLL) return -2;
         hipLaunchKernelGGL((mqa_sparse_mfma<true>), dim3((unsigned)units), dim3(kMWaves * kWave), 0, stream,
                            static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), nullptr, rows, T, N, H, 0,
-                           1, 0x7fffffff, scale * kLog2e, q_pos0, ratio, static_cast<uint16_t*>(out), nullptr, nullptr);
+                           1, 0x7fffffff, scale * kLog2e, q_pos0, ratio, static_cast<uint16_t*>(out), nullptr, nullptr,
+                           sink);
         return 0;
     }
     if (t == DT_F32)
-        return launch_generic<DT_F32, true>(q, kv, nullptr, batch, T, N, H, c, 0, scale, q_pos0, ratio, out, stream);
+        return launch_generic<DT_F32, true>(q, kv, nullptr, batch, T, N, H, c, 0, scale, q_pos0, ratio, out, sink, stream);
     if (t == DT_BF16)
-        return launch_generic<DT_BF16, true>(q, kv, nullptr, batch, T, N, H, c, 0, scale, q_pos0, ratio, out, stream);
+        return launch_generic<DT_BF16, true>(q, kv, nullptr, batch, T, N, H, c, 0, scale, q_pos0, ratio, out, sink, stream);
     return -2;
 }
 

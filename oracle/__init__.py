@@ -59,8 +59,8 @@ def lib():
             "oracle_hca_compress": ([P, P, P, I64, I64, I, I, I, P], None),
             "oracle_index_scores": ([P, P, P, I64, I64, P, I64, I, I, I, P], None),
             "oracle_topk": ([P, I64, I64, P, I64, I, I, P, P], None),
-            "oracle_sparse_mqa": ([P, P, P, I64, I64, I64, I, I, I, D, P], None),
-            "oracle_hca_dense_mqa": ([P, P, I64, I64, P, I64, I, I, I, D, P], None),
+            "oracle_sparse_mqa": ([P, P, P, I64, I64, I64, I, I, I, D, P, P], None),
+            "oracle_hca_dense_mqa": ([P, P, I64, I64, P, I64, I, I, I, D, P, P], None),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -183,7 +183,16 @@ def topk(scores, m: int, k: int, q_pos0: int = 0, qpos=None):
     return idx, sel
 
 
-def sparse_mqa(q, kv, idx, scale: float, dtype: int = F32):
+def _sink(sink, H):
+    """Per-head sink logits as float64 [H] (None: no sink)."""
+    if sink is None:
+        return None
+    s = np.ascontiguousarray(sink, dtype=np.float64)
+    assert s.shape == (H,)
+    return s
+
+
+def sparse_mqa(q, kv, idx, scale: float, dtype: int = F32, sink=None):
     q, kv = _d(q, dtype), _d(kv, dtype)
     idx = np.ascontiguousarray(idx, dtype=np.int32)
     batch, T, H, c = q.shape
@@ -191,16 +200,20 @@ def sparse_mqa(q, kv, idx, scale: float, dtype: int = F32):
     k = idx.shape[2]
     assert kv.shape == (batch, N, c) and idx.shape == (batch, T, k)
     out = np.empty((batch, T, H, c), dtype=np.float64)
-    lib().oracle_sparse_mqa(_p(q), _p(kv), _p(idx), batch, T, N, H, c, k, float(scale), _p(out))
+    sk = _sink(sink, H)
+    lib().oracle_sparse_mqa(_p(q), _p(kv), _p(idx), batch, T, N, H, c, k, float(scale),
+                            None if sk is None else _p(sk), _p(out))
     return out
 
 
-def hca_dense_mqa(q, kv, m_prime: int, scale: float, q_pos0: int = 0, dtype: int = F32, qpos=None):
+def hca_dense_mqa(q, kv, m_prime: int, scale: float, q_pos0: int = 0, dtype: int = F32, qpos=None, sink=None):
     q, kv = _d(q, dtype), _d(kv, dtype)
     batch, T, H, c = q.shape
     N = kv.shape[1]
     assert kv.shape == (batch, N, c)
     qp = _qpos(T, q_pos0, qpos)
     out = np.empty((batch, T, H, c), dtype=np.float64)
-    lib().oracle_hca_dense_mqa(_p(q), _p(kv), batch, T, _p(qp), N, H, c, m_prime, float(scale), _p(out))
+    sk = _sink(sink, H)
+    lib().oracle_hca_dense_mqa(_p(q), _p(kv), batch, T, _p(qp), N, H, c, m_prime, float(scale),
+                               None if sk is None else _p(sk), _p(out))
     return out

@@ -334,8 +334,12 @@ void oracle_topk(const double* scores, int64_t batch, int64_t T, const int64_t* 
 
 /* One query head attending to the entries listed in `ids` (shared-KV MQA, R8):
  * l_s = scale * q . kv_s, p = softmax(l), o = sum_s p_s kv_s. */
+/* Softmax attention of one head over the entries `ids`.  With a sink logit z' ([N] §1.3 and
+ * [M] §2.3.3 item 4, attention sink: the softmax denominator gains exp(z'), so a head may give
+ * part of its weight to nothing) the weights are exp(z_s) / (sum_r exp(z_r) + exp(z')); `sink`
+ * NULL means no sink.  Nothing selected: a zero output either way. */
 static void attend(const double* q, const double* kv, const int64_t* ids, int64_t nsel, int c,
-                   double scale, double* logit, double* o) {
+                   double scale, const double* sink, double* logit, double* o) {
     int64_t r;
     int d;
     double mx = -INFINITY, den = 0.0;
@@ -347,11 +351,13 @@ static void attend(const double* q, const double* kv, const int64_t* ids, int64_
         logit[r] = scale * dot;
         if (logit[r] > mx) mx = logit[r];
     }
+    if (sink && *sink > mx) mx = *sink;
     for (r = 0; r < nsel; ++r) {
         double p = exp(logit[r] - mx);
         den += p;
         for (d = 0; d < c; ++d) o[d] += p * kv[ids[r] * c + d];
     }
+    if (sink) den += exp(*sink - mx);
     for (d = 0; d < c; ++d) o[d] /= den;
 }
 
@@ -363,7 +369,7 @@ static void attend(const double* q, const double* kv, const int64_t* ids, int64_
  * Layouts: q [batch, T, H, c]; kv [batch, N, c]; idx [batch, T, k]; out [batch, T, H, c].
  */
 void oracle_sparse_mqa(const double* q, const double* kv, const int32_t* idx, int64_t batch, int64_t T,
-                       int64_t N, int H, int c, int k, double scale, double* out) {
+                       int64_t N, int H, int c, int k, double scale, const double* sink, double* out) {
     int64_t bt;
 #pragma omp parallel for schedule(dynamic, 1)
     for (bt = 0; bt < batch * T; ++bt) {
@@ -376,8 +382,8 @@ void oracle_sparse_mqa(const double* q, const double* kv, const int32_t* idx, in
             if (s >= 0 && s < N) ids[nsel++] = s;
         }
         for (h = 0; h < H; ++h)
-            attend(q + (bt * H + h) * (int64_t)c, kv + b * N * c, ids, nsel, c, scale, logit,
-                   out + (bt * H + h) * (int64_t)c);
+            attend(q + (bt * H + h) * (int64_t)c, kv + b * N * c, ids, nsel, c, scale, sink ? sink + h : NULL,
+                   logit, out + (bt * H + h) * (int64_t)c);
         free(ids);
         free(logit);
     }
@@ -389,7 +395,7 @@ void oracle_sparse_mqa(const double* q, const double* kv, const int32_t* idx, in
  * Layouts: q [batch, T, H, c]; kv [batch, N, c]; qpos [T]; out [batch, T, H, c].
  */
 void oracle_hca_dense_mqa(const double* q, const double* kv, int64_t batch, int64_t T, const int64_t* qpos,
-                          int64_t N, int H, int c, int mp, double scale, double* out) {
+                          int64_t N, int H, int c, int mp, double scale, const double* sink, double* out) {
     int64_t bt;
 #pragma omp parallel for schedule(dynamic, 1)
     for (bt = 0; bt < batch * T; ++bt) {
@@ -400,8 +406,8 @@ void oracle_hca_dense_mqa(const double* q, const double* kv, int64_t batch, int6
         for (s = 0; s < N; ++s)
             if (visible(s, mp, qpos[t])) ids[nsel++] = s;
         for (h = 0; h < H; ++h)
-            attend(q + (bt * H + h) * (int64_t)c, kv + b * N * c, ids, nsel, c, scale, logit,
-                   out + (bt * H + h) * (int64_t)c);
+            attend(q + (bt * H + h) * (int64_t)c, kv + b * N * c, ids, nsel, c, scale, sink ? sink + h : NULL,
+                   logit, out + (bt * H + h) * (int64_t)c);
         free(ids);
         free(logit);
     }

@@ -150,6 +150,12 @@ def test_mqa_rejects_bad_arguments(L):
         assert L.csa_sparse_mqa(A, A, A, b_, t_, n_, h_, c_, k_, 0.05, mix, A, A, 1 << 30, None) == UNSUPPORTED
     assert L.csa_sparse_mqa(A, A, A, 1, 1, 1 << 23, 64, 512, 64, 0.05, mix, A, A, 1 << 30, None) == UNSUPPORTED
     assert L.csa_sparse_mqa(A, MIS, A, 1, 1, 100, 64, 512, 64, 0.05, mix, A, A, 1 << 30, None) == INVALID
+    # sink logits ([H] fp32): 4-byte aligned or NULL
+    MIS2 = 0x10002
+    assert L.csa_sparse_mqa_sink(A, A, A, 1, 4, 64, 4, 64, 8, 0.125, MIS2, 0, A, None, 0, None) == INVALID
+    assert L.hca_dense_mqa_sink(A, A, 1, 4, 0, 8, 4, 64, 128, 0.125, MIS2, 0, A, None) == INVALID
+    assert L.csa_sparse_mqa_sink(A, A, A, 0, 4, 64, 4, 64, 8, 0.125, A, 0, A, None, 0, None) == OK
+    assert L.hca_dense_mqa_sink(A, A, 1, 0, 0, 8, 4, 64, 128, 0.125, None, 0, A, None) == OK
     g = L.hca_dense_mqa
     assert g(A, A, 1, 4, 0, 8, 64, 512, 128, 0.125, mix, A, None) == UNSUPPORTED
     assert g(A, A, 1, 4, 0, 8, 4, 64, 0, 0.125, 0, A, None) == INVALID

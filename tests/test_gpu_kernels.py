@@ -332,6 +332,50 @@ def test_dense_mqa_parity(case):
     out_tol(dt)(got, ref, "dense_mqa")
 
 
+SINK_CASES = [  # kind, batch, T, N, H, k (sparse) or q_pos0 (dense), dtype — one per kernel path
+    ("sparse", 2, 5, 40, 4, 8, F32),            # generic kernel
+    ("sparse", 1, 300, 700, 64, 100, BF16),     # two-stage kernel, one key range (> 256 units)
+    ("sparse", 3, 1, 3000, 128, 1024, BF16),    # warp-specialised, key ranges merged
+    ("sparse", 2, 64, 900, 128, 256, BF16),     # warp-specialised, 256 units, one range
+    ("mixed", 2, 1, 5000, 64, 1024, BF16),      # mixed fp8/bf16 KV rows, ranges merged
+    ("dense", 1, 40, 9, 4, 0, F32),             # generic dense, early queries see nothing
+    ("dense", 1, 64, 300, 64, 128 * 300 - 40, BF16),   # two-stage dense kernel
+]
+
+
+@pytest.mark.parametrize("case", SINK_CASES, ids=lambda c: "%s_b%d_T%d_N%d_H%d_%d_%d" % c)
+def test_mqa_with_attention_sink(case):
+    """Per-head sink logits join the softmax denominator (the notes page §1.3): each kernel
+    path against the oracle with the same sinks (spread wide, so some heads keep little)."""
+    kind, batch, T, N, H, kp, dt = case
+    c = 64 if dt == F32 else 512
+    say(f"mqa with sink {case}")
+    sd = 1500 + N
+    q = draw(sd, 1, (batch, T, H, c), dt)
+    sink = (3.0 * np.random.RandomState(sd).randn(H)).astype(np.float32)
+    sink_dev = torch.from_numpy(sink).cuda()
+    scale = 1.0 / np.sqrt(c)
+    if kind == "dense":
+        kv = draw(sd, 2, (batch, N, c), dt)
+        mp = 128 if dt == BF16 else 4
+        ref = oracle.hca_dense_mqa(q, kv, mp, scale, q_pos0=kp, dtype=dt, sink=sink)
+        got = from_dev(csa.hca_dense_mqa(to_dev(q, dt), to_dev(kv, dt), kp, mp, scale, sink=sink_dev))
+    else:
+        idx = _distinct_ids(np.random.RandomState(sd), batch, T, N, kp)
+        idx[0, 0, :] = -1                   # nothing selected: still zeros
+        if kind == "mixed":
+            kvm = rng.normal(sd, 2, (batch, N, c), rng.KV_FP8_BF16)
+            ref = oracle.sparse_mqa(q, oracle.decode_kv_fp8_bf16(kvm, c), idx, scale, dtype=dt, sink=sink)
+            kv_dev = csa.KVFp8Bf16(torch.from_numpy(kvm).cuda(), c)
+        else:
+            kv = draw(sd, 2, (batch, N, c), dt)
+            ref = oracle.sparse_mqa(q, kv, idx, scale, dtype=dt, sink=sink)
+            kv_dev = to_dev(kv, dt)
+        got = from_dev(csa.csa_sparse_mqa(to_dev(q, dt), kv_dev, torch.from_numpy(idx).cuda(), scale, sink=sink_dev))
+        assert not got[0, 0].any()
+    out_tol(dt)(got, ref, f"{kind} mqa with sink")
+
+
 def test_repeat_runs_are_bitwise_identical():
     batch, T, N, H, c, k = 2, 3, 900, 64, 512, 256
     q, kv = draw(77, 1, (batch, T, H, c), BF16), draw(77, 2, (batch, N, c), BF16)

@@ -469,3 +469,40 @@ def test_sparse_mqa_over_all_visible_equals_dense_csa_mask(orc):
                                rtol=1e-12, atol=1e-14)
     np.testing.assert_allclose(orc.sparse_mqa(q, kv, idx, 0.4), _dense_attention(q, kv, m, 0.4, np.arange(T)),
                                rtol=1e-12, atol=1e-14)
+
+
+def test_attention_sink_closed_forms(orc):
+    """Attention sink (the notes page §1.3, the mlpod page §2.3.3 item 4): the softmax
+    denominator gains exp(z'_h).  One entry with logit l gives the weight 1 / (1 + exp(z' - l))
+    (logistic); a sink far below every logit changes nothing; a query with no entry stays 0;
+    heads keep their own sink."""
+    c = 4
+    q = np.zeros((1, 2, 2, c))
+    q[0, :, 0, 0] = 1.0                 # head 0 of both queries: logit = scale * kv[s, 0]
+    q[0, :, 1, 1] = 1.0                 # head 1: logit = scale * kv[s, 1]
+    kv = np.array([[[2.0, 1.0, -1.0, 0.5], [0.0, -3.0, 4.0, 1.0]]])
+    idx = np.array([[[0, -1], [-1, -1]]], np.int32)   # query 1 selects nothing
+    scale, sink = 0.5, np.array([0.3, -2.0])
+    out = orc.sparse_mqa(q, kv, idx, scale, sink=sink)
+    for h, logit in ((0, 1.0), (1, 0.5)):
+        wgt = 1.0 / (1.0 + np.exp(sink[h] - logit))
+        assert np.allclose(out[0, 0, h], wgt * kv[0, 0], rtol=1e-15, atol=0)
+    assert not out[0, 1].any()
+    far = orc.sparse_mqa(q, kv, np.array([[[0, 1], [1, 0]]], np.int32), scale, sink=np.array([-1e300, -1e300]))
+    assert np.array_equal(far, orc.sparse_mqa(q, kv, np.array([[[0, 1], [1, 0]]], np.int32), scale))
+
+
+def test_dense_mqa_with_sink_equals_sparse_over_the_visible_entries(orc):
+    r = np.random.RandomState(5)
+    T, N, H, c, mp, p0 = 6, 9, 3, 8, 4, 10
+    q, kv = r.randn(1, T, H, c), r.randn(1, N, c)
+    sink = r.randn(H)
+    dense = orc.hca_dense_mqa(q, kv, mp, 0.3, q_pos0=p0, sink=sink)
+    idx = np.full((1, T, N), -1, np.int32)
+    for t in range(T):
+        vis = [s for s in range(N) if mp * (s + 1) - 1 <= p0 + t]
+        idx[0, t, :len(vis)] = vis
+    assert np.allclose(dense, orc.sparse_mqa(q, kv, idx, 0.3, sink=sink), rtol=1e-13, atol=1e-15)
+    # and the sink lowers every weight: the output is the no-sink output times sum/(sum + e^z')
+    plain = orc.hca_dense_mqa(q, kv, mp, 0.3, q_pos0=p0)
+    assert np.all(np.abs(dense) <= np.abs(plain) + 1e-15)
