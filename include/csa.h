@@ -207,6 +207,21 @@ int hca_dense_mqa_sink(const void* q, const void* kv, int64_t batch, int64_t T, 
                        int c, int m_prime, float scale, const float* sink, csa_dtype t, void* out,
                        csa_stream_t stream);
 
+/*
+ * csa_rope — partial rotary position embedding ([N] §1.3 and [M] §2.3.3 item 2: RoPE on the
+ * last 64 channels of queries and KV entries; the core attention output gets the rotation of
+ * the negative query position, so it reflects the query-to-entry distance), in place:
+ *   x : [batch, T, H, c], dtype t (CSA_F32 or CSA_BF16); H = 1 for KV entries.
+ * Row (b, t) has position p = pos0 + t * pos_step.  Channel pair (c - d + 2i, c - d + 2i + 1),
+ * i < d/2, turns by the angle p * base^(-2i/d) (RoFormer's pairing), or by its negative when
+ * inverse != 0 (the output side):  (x0, x1) -> (x0 cos a - x1 sin a, x0 sin a + x1 cos a).
+ * Angles, sines and cosines in double, the products in double, rounded once to dtype t.
+ * Limits: d even, 2 <= d <= min(c, 128), c % 8 == 0, c <= CSA_MAX_WIDTH, 1 <= H <=
+ * CSA_MAX_HEADS, base > 1.
+ */
+int csa_rope(void* x, int64_t batch, int64_t T, int H, int c, int d, int64_t pos0, int64_t pos_step, float base,
+             int inverse, csa_dtype t, csa_stream_t stream);
+
 /* Human-readable name of a csa_status value (static storage). */
 const char* csa_status_string(int status);
 

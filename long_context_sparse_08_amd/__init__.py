@@ -22,7 +22,8 @@ STATUS = {0: "CSA_OK", -1: "CSA_ERR_INVALID_ARG", -2: "CSA_ERR_UNSUPPORTED", -3:
 
 ENTRY_POINTS = ("csa_compress", "hca_compress", "csa_index_topk_workspace_size", "csa_index_topk",
                 "csa_index_scores", "csa_topk_workspace_size", "csa_topk", "csa_sparse_mqa_workspace_size", "csa_sparse_mqa",
-                "hca_dense_mqa", "csa_sparse_mqa_sink", "hca_dense_mqa_sink", "csa_status_string", "csa_version")
+                "hca_dense_mqa", "csa_sparse_mqa_sink", "hca_dense_mqa_sink", "csa_rope", "csa_status_string",
+                "csa_version")
 
 
 class CsaError(RuntimeError):
@@ -48,6 +49,7 @@ def _load():
         "csa_sparse_mqa": ([P, P, P, I64, I64, I64, I, I, I, F, I, P, P, SZ, P], I),
         "hca_dense_mqa": ([P, P, I64, I64, I64, I64, I, I, I, F, I, P, P], I),
         "csa_sparse_mqa_sink": ([P, P, P, I64, I64, I64, I, I, I, F, P, I, P, P, SZ, P], I),
+        "csa_rope": ([P, I64, I64, I, I, I, I64, I64, F, I, I, P], I),
         "hca_dense_mqa_sink": ([P, P, I64, I64, I64, I64, I, I, I, F, P, I, P, P], I),
         "csa_status_string": ([I], ctypes.c_char_p),
         "csa_version": ([], I),
@@ -276,6 +278,20 @@ def csa_sparse_mqa(q, kv, idx, scale: float, out=None, workspace=None, sink=None
     _check("csa_sparse_mqa", lib.csa_sparse_mqa_sink(_p(q), _p(kvt), _p(idx), batch, T, N, H, c, k, float(scale), _p(sk),
                                                      dt, _p(out), _p(workspace), ws_bytes, _stream(dev)))
     return out
+
+
+def csa_rope(x, pos0: int, pos_step: int = 1, d: int = 64, base: float = 10000.0, inverse: bool = False):
+    """Partial RoPE in place on x [batch, T, H, c] (or [batch, T, c] KV rows): the last d
+    channels of row (b, t) turn by position pos0 + t * pos_step (inverse: its negative)."""
+    dev = _dev(x)
+    if x.dim() == 3:
+        batch, T, c = x.shape
+        H = 1
+    else:
+        batch, T, H, c = x.shape
+    _check("csa_rope", lib.csa_rope(_p(x), batch, T, H, c, d, pos0, pos_step, float(base), 1 if inverse else 0, _dt(x),
+                                    _stream(dev)))
+    return x
 
 
 def hca_dense_mqa(q, kv, q_pos0: int, m_prime: int, scale: float, out=None, sink=None):

@@ -221,6 +221,18 @@ int csa_sparse_mqa_sink(const void* q, const void* kv, const int32_t* idx, int64
                                          static_cast<hipStream_t>(stream)));
 }
 
+int csa_rope(void* x, int64_t batch, int64_t T, int H, int c, int d, int64_t pos0, int64_t pos_step, float base,
+             int inverse, csa_dtype t, csa_stream_t stream) {
+    if (batch < 0 || T < 0 || H < 1 || c < 1 || d < 2 || d % 2 != 0 || d > c) return CSA_ERR_INVALID_ARG;
+    if (!(base > 1.f) || !isfinite(base)) return CSA_ERR_INVALID_ARG;
+    if (!io_dtype(t)) return CSA_ERR_UNSUPPORTED;
+    if (!width_ok(c) || H > CSA_MAX_HEADS || d > 128) return CSA_ERR_UNSUPPORTED;
+    if (batch * T == 0) return CSA_OK;
+    if (!x || !aligned16(x)) return CSA_ERR_INVALID_ARG;
+    return finish(csa::launch_rope(x, batch, T, H, c, d, pos0, pos_step, base, inverse != 0, t,
+                                   static_cast<hipStream_t>(stream)));
+}
+
 int hca_dense_mqa(const void* q, const void* kv, int64_t batch, int64_t T, int64_t q_pos0, int64_t N, int H, int c,
                   int m_prime, float scale, csa_dtype t, void* out, csa_stream_t stream) {
     return hca_dense_mqa_sink(q, kv, batch, T, q_pos0, N, H, c, m_prime, scale, nullptr, t, out, stream);

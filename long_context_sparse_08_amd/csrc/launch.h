@@ -51,6 +51,11 @@ constexpr int64_t kTopkMaxGroups = 8192;
 int topk_zero_words(int64_t rows, int64_t nv_max);
 uint32_t* topk_zero_region(void* extra_ws, int64_t rows, int64_t N);
 
+// Partial RoPE, in place on x [batch, T, H, c]: the last d channels of row (b, t) turn by the
+// position pos0 + t * pos_step (inverse: by its negative).
+int launch_rope(void* x, int64_t batch, int64_t T, int H, int c, int d, int64_t pos0, int64_t pos_step, float base,
+                bool inverse, int t, hipStream_t stream);
+
 // Device workspace bytes launch_sparse_mqa needs (0: none) for the key-range partials.
 // `sink` (both MQA launchers): per-head sink logits [H] in natural-log units, or nullptr.
 size_t sparse_mqa_workspace(int64_t batch, int64_t T, int H, int c, int k, int t);

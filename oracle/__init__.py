@@ -54,6 +54,7 @@ def lib():
             "oracle_decode": ([P, I, I64, P], I),
             "oracle_decode_mxfp4": ([P, I64, I, P], I),
             "oracle_decode_kv_fp8_bf16": ([P, I64, I, P], I),
+            "oracle_rope": ([P, I64, I64, I, I, I, I64, I64, D, I], None),
             "oracle_round": ([P, I, I64], I),
             "oracle_csa_compress": ([P, P, P, P, P, P, I64, I64, I, I, I, P], None),
             "oracle_hca_compress": ([P, P, P, I64, I64, I, I, I, P], None),
@@ -114,6 +115,17 @@ def decode_kv_fp8_bf16(buf: np.ndarray, c: int) -> np.ndarray:
     out = np.empty(buf.shape[:-1] + (c,), dtype=np.float64)
     if lib().oracle_decode_kv_fp8_bf16(_p(buf), rows, c, _p(out)) != 0:
         raise ValueError("bad mixed KV shape")
+    return out
+
+
+def rope(x, pos0: int, pos_step: int = 1, d: int = 64, base: float = 10000.0, inverse: bool = False,
+         dtype: int = F32):
+    """Partial RoPE of x [batch, T, H, c] (or [batch, T, c]) -> float64, same shape."""
+    out = np.array(_d(x, dtype), dtype=np.float64, copy=True, order="C")
+    shp = out.shape
+    batch, T = shp[0], shp[1]
+    H, c = (1, shp[2]) if out.ndim == 3 else (shp[2], shp[3])
+    lib().oracle_rope(_p(out), batch, T, H, c, d, pos0, pos_step, float(base), 1 if inverse else 0)
     return out
 
 

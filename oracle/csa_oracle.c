@@ -122,6 +122,27 @@ int oracle_decode_kv_fp8_bf16(const uint8_t* buf, int64_t rows, int c, double* d
     return 0;
 }
 
+/* Partial RoPE ([N] §1.3 and [M] §2.3.3 item 2: the last d channels of q and KV rows; the
+ * attention output turns by the negative query position).  Rotation as defined by RoFormer
+ * (Su et al. 2021): channel pair (c-d+2i, c-d+2i+1) of the row at position p turns by
+ * p * base^(-2i/d); `inverse` negates the angle.  In place on x [batch, T, H, c]; row (b, t)
+ * sits at position pos0 + t * pos_step. */
+void oracle_rope(double* x, int64_t batch, int64_t T, int H, int c, int d, int64_t pos0, int64_t pos_step,
+                 double base, int inverse) {
+    int64_t r;
+    for (r = 0; r < batch * T * H; ++r) {
+        const double p = (double)(pos0 + ((r / H) % T) * pos_step);
+        int i;
+        for (i = 0; i < d / 2; ++i) {
+            double* v = x + r * c + (c - d) + 2 * i;
+            const double a = (inverse ? -p : p) * pow(base, -2.0 * i / d);
+            const double x0 = v[0], x1 = v[1];
+            v[0] = x0 * cos(a) - x1 * sin(a);
+            v[1] = x0 * sin(a) + x1 * cos(a);
+        }
+    }
+}
+
 /* Decode `count` stored values of type `dtype` into doubles (exact). */
 int oracle_decode(const void* src, int dtype, int64_t count, double* dst) {
     int64_t i;

@@ -156,6 +156,15 @@ def test_mqa_rejects_bad_arguments(L):
     assert L.hca_dense_mqa_sink(A, A, 1, 4, 0, 8, 4, 64, 128, 0.125, MIS2, 0, A, None) == INVALID
     assert L.csa_sparse_mqa_sink(A, A, A, 0, 4, 64, 4, 64, 8, 0.125, A, 0, A, None, 0, None) == OK
     assert L.hca_dense_mqa_sink(A, A, 1, 0, 0, 8, 4, 64, 128, 0.125, None, 0, A, None) == OK
+    # partial RoPE: d even, 2 <= d <= min(c, 128), base > 1, fp32 / bf16 rows
+    r = L.csa_rope
+    assert r(A, 1, 4, 64, 512, 63, 0, 1, 10000.0, 0, 1, None) == INVALID
+    assert r(A, 1, 4, 64, 512, 0, 0, 1, 10000.0, 0, 1, None) == INVALID
+    assert r(A, 1, 4, 64, 512, 64, 0, 1, 1.0, 0, 1, None) == INVALID
+    assert r(A, 1, 4, 64, 512, 256, 0, 1, 10000.0, 0, 1, None) == UNSUPPORTED
+    assert r(A, 1, 4, 64, 512, 64, 0, 1, 10000.0, 0, 2, None) == UNSUPPORTED
+    assert r(MIS, 1, 4, 64, 512, 64, 0, 1, 10000.0, 0, 1, None) == INVALID
+    assert r(None, 0, 4, 64, 512, 64, 0, 1, 10000.0, 0, 1, None) == OK
     g = L.hca_dense_mqa
     assert g(A, A, 1, 4, 0, 8, 64, 512, 128, 0.125, mix, A, None) == UNSUPPORTED
     assert g(A, A, 1, 4, 0, 8, 4, 64, 0, 0.125, 0, A, None) == INVALID

@@ -376,6 +376,37 @@ def test_mqa_with_attention_sink(case):
     out_tol(dt)(got, ref, f"{kind} mqa with sink")
 
 
+ROPE_CASES = [  # batch, T, H, c, d, pos0, pos_step, inverse, dtype
+    (2, 5, 64, 512, 64, 1048575 - 4, 1, False, BF16),   # queries at the end of a 1M context
+    (1, 300, 1, 512, 64, 3, 4, False, BF16),             # compressed KV rows (H = 1), stride m
+    (3, 7, 4, 64, 32, 0, 1, True, F32),                  # inverse (output side), position 0 first
+    (1, 2, 2, 16, 16, 123456, 1, False, F32),            # every channel rotated
+]
+
+
+@pytest.mark.parametrize("case", ROPE_CASES, ids=lambda c: "b%d_T%d_H%d_c%d_d%d_p%d_s%d_%s_%d" % c)
+def test_rope_parity(case):
+    batch, T, H, c, d, p0, ps, inv, dt = case
+    say(f"csa_rope {case}")
+    shape = (batch, T, c) if H == 1 else (batch, T, H, c)
+    x = draw(1600 + c + T, 1, shape, dt)
+    ref = oracle.rope(x, p0, ps, d=d, inverse=inv, dtype=dt)
+    if dt == BF16:
+        ref = oracle.round_to(ref, BF16)
+    xd = to_dev(x, dt)
+    got = from_dev(csa.csa_rope(xd, p0, ps, d=d, inverse=inv))
+    if dt == BF16:   # both round one double to bf16: equal up to a rare last-place tie
+        assert np.mean(got == ref) > 0.999
+        assert_abs_close(got, ref, 2.0 ** -4, "rope bf16")   # one bf16 step at |x| < 8
+    else:
+        assert_fp32_close(got, ref, "rope f32")
+    back = from_dev(csa.csa_rope(csa.csa_rope(to_dev(x, dt), p0, ps, d=d), p0, ps, d=d, inverse=True))
+    if dt == BF16:   # two roundings to bf16 (one step each at |x| < 8)
+        assert_abs_close(back, oracle.decode(x, dt), 2.0 ** -3, "rope round trip")
+    else:
+        assert_fp32_close(back, oracle.decode(x, dt), "rope round trip")
+
+
 def test_repeat_runs_are_bitwise_identical():
     batch, T, N, H, c, k = 2, 3, 900, 64, 512, 256
     q, kv = draw(77, 1, (batch, T, H, c), BF16), draw(77, 2, (batch, N, c), BF16)

@@ -506,3 +506,27 @@ def test_dense_mqa_with_sink_equals_sparse_over_the_visible_entries(orc):
     # and the sink lowers every weight: the output is the no-sink output times sum/(sum + e^z')
     plain = orc.hca_dense_mqa(q, kv, mp, 0.3, q_pos0=p0)
     assert np.all(np.abs(dense) <= np.abs(plain) + 1e-15)
+
+
+def test_rope_pairs_frequencies_and_relative_positions(orc):
+    """Partial RoPE (the notes page §1.3: the last 64 channels; rotation as in RoFormer):
+    unit vectors on pair 0 and pair 1 land on (cos, sin) of p and p * base^(-2/d); the leading
+    channels stay; position 0 is the identity; the inverse undoes it; and rotated dot products
+    depend only on the position difference (the property RoPE exists for)."""
+    c, d, base, p = 96, 64, 10000.0, 37
+    x = np.zeros((1, 1, c))
+    x[0, 0, c - d] = 1.0                        # pair 0, first channel
+    x[0, 0, c - d + 3] = 1.0                    # pair 1, second channel
+    x[0, 0, 5] = 2.5                            # outside the rotated part
+    y = orc.rope(x, p, d=d, base=base)
+    a1 = p * base ** (-2.0 / d)
+    assert np.allclose(y[0, 0, c - d:c - d + 4], [np.cos(p), np.sin(p), -np.sin(a1), np.cos(a1)], rtol=0, atol=1e-15)
+    assert y[0, 0, 5] == 2.5 and not y[0, 0, c - d + 4:].any()
+    r = np.random.RandomState(3)
+    v = r.randn(2, 3, 4, c)
+    assert np.array_equal(orc.rope(v, 0, pos_step=0), v)
+    assert np.allclose(orc.rope(orc.rope(v, 1000, 7), 1000, 7, inverse=True), v, rtol=0, atol=1e-12)
+    a, b = r.randn(1, 1, c), r.randn(1, 1, c)
+    lhs = (orc.rope(a, 5000)[..., c - d:] * orc.rope(b, 4321)[..., c - d:]).sum()
+    rhs = (orc.rope(a, 5000 - 4321)[..., c - d:] * b[..., c - d:]).sum()
+    assert abs(lhs - rhs) < 1e-9 * max(1.0, abs(rhs))
