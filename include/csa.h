@@ -222,6 +222,23 @@ int hca_dense_mqa_sink(const void* q, const void* kv, int64_t batch, int64_t T, 
 int csa_rope(void* x, int64_t batch, int64_t T, int H, int c, int d, int64_t pos0, int64_t pos_step, float base,
              int inverse, csa_dtype t, csa_stream_t stream);
 
+/*
+ * csa_sparse_mqa_swa — csa_sparse_mqa (with optional sink) plus the sliding-window branch ([N]
+ * §1.3 and [M] §2.3.3 item 3: next to the compressed attention, each query also attends to the
+ * most recent n_win uncompressed KV tokens, n_win = 128 on the pages): the query at absolute
+ * position p = q_pos0 + t attends, in one softmax, to its selected entries idx[t,:] and to the
+ * raw rows win_kv[j] whose position win_pos0 + j lies in [p - n_win + 1, p].
+ *   win_kv : [batch, W, c] raw KV rows of each sequence (bf16 / fp32 as q), rows at absolute
+ *            positions win_pos0 .. win_pos0 + W - 1 (a decode step passes its window state;
+ *            a prefill chunk its own raw KV).  May be NULL when n_win == 0 or W == 0.
+ *   workspace : at least csa_sparse_mqa_workspace_size(batch, T, H, c, k + n_win, t) bytes.
+ * Limits: as csa_sparse_mqa; 0 <= n_win <= 1024; N + W < 2^31; not with CSA_KV_FP8_BF16.
+ */
+int csa_sparse_mqa_swa(const void* q, const void* kv, const int32_t* idx, int64_t batch, int64_t T, int64_t N,
+                       int H, int c, int k, float scale, const float* sink, const void* win_kv, int64_t W,
+                       int64_t win_pos0, int64_t q_pos0, int n_win, csa_dtype t, void* out, void* workspace,
+                       size_t ws_bytes, csa_stream_t stream);
+
 /* Human-readable name of a csa_status value (static storage). */
 const char* csa_status_string(int status);
 

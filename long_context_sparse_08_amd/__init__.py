@@ -22,7 +22,7 @@ STATUS = {0: "CSA_OK", -1: "CSA_ERR_INVALID_ARG", -2: "CSA_ERR_UNSUPPORTED", -3:
 
 ENTRY_POINTS = ("csa_compress", "hca_compress", "csa_index_topk_workspace_size", "csa_index_topk",
                 "csa_index_scores", "csa_topk_workspace_size", "csa_topk", "csa_sparse_mqa_workspace_size", "csa_sparse_mqa",
-                "hca_dense_mqa", "csa_sparse_mqa_sink", "hca_dense_mqa_sink", "csa_rope", "csa_status_string",
+                "hca_dense_mqa", "csa_sparse_mqa_sink", "hca_dense_mqa_sink", "csa_sparse_mqa_swa", "csa_rope", "csa_status_string",
                 "csa_version")
 
 
@@ -50,6 +50,7 @@ def _load():
         "hca_dense_mqa": ([P, P, I64, I64, I64, I64, I, I, I, F, I, P, P], I),
         "csa_sparse_mqa_sink": ([P, P, P, I64, I64, I64, I, I, I, F, P, I, P, P, SZ, P], I),
         "csa_rope": ([P, I64, I64, I, I, I, I64, I64, F, I, I, P], I),
+        "csa_sparse_mqa_swa": ([P, P, P, I64, I64, I64, I, I, I, F, P, P, I64, I64, I64, I, I, P, P, SZ, P], I),
         "hca_dense_mqa_sink": ([P, P, I64, I64, I64, I64, I, I, I, F, P, I, P, P], I),
         "csa_status_string": ([I], ctypes.c_char_p),
         "csa_version": ([], I),
@@ -253,9 +254,10 @@ def _sink(sink, H, dev):
     return sink
 
 
-def csa_sparse_mqa(q, kv, idx, scale: float, out=None, workspace=None, sink=None):
+def csa_sparse_mqa(q, kv, idx, scale: float, out=None, workspace=None, sink=None, window=None):
     """q [batch, T, H, c], kv [batch, N, c] (or KVFp8Bf16 with bf16 q), idx [batch, T, k] int32
-    -> out [batch, T, H, c].  sink: optional fp32 [H] per-head sink logits (attention sink)."""
+    -> out [batch, T, H, c].  sink: optional fp32 [H] per-head sink logits (attention sink).
+    window: optional (win_kv [batch, W, c], win_pos0, q_pos0, n_win), the sliding-window branch."""
     mixed = isinstance(kv, KVFp8Bf16)
     kvt = kv.data if mixed else kv
     dev = _dev(q, kvt, idx, out, workspace)
@@ -271,12 +273,19 @@ def csa_sparse_mqa(q, kv, idx, scale: float, out=None, workspace=None, sink=None
     assert idx.dtype == torch.int32 and idx.shape == (batch, T, k)
     if out is None:
         out = torch.empty_like(q)
+    wkv, W, wp0, qp0, n_win = None, 0, 0, 0, 0
+    if window is not None:
+        wkv, wp0, qp0, n_win = window
+        assert wkv.dtype == q.dtype and wkv.shape[0] == batch and wkv.shape[2] == c
+        _dev(q, wkv)
+        W = wkv.shape[1]
     if workspace is None:
-        workspace = mqa_workspace_for(q, k, dt)
+        workspace = mqa_workspace_for(q, k + n_win, dt)
     ws_bytes = 0 if workspace is None else workspace.numel()
     sk = _sink(sink, H, dev)
-    _check("csa_sparse_mqa", lib.csa_sparse_mqa_sink(_p(q), _p(kvt), _p(idx), batch, T, N, H, c, k, float(scale), _p(sk),
-                                                     dt, _p(out), _p(workspace), ws_bytes, _stream(dev)))
+    _check("csa_sparse_mqa", lib.csa_sparse_mqa_swa(_p(q), _p(kvt), _p(idx), batch, T, N, H, c, k, float(scale), _p(sk),
+                                                    _p(wkv), W, wp0, qp0, n_win, dt, _p(out), _p(workspace), ws_bytes,
+                                                    _stream(dev)))
     return out
 
 

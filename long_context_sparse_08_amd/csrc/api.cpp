@@ -205,7 +205,19 @@ int csa_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t ba
 int csa_sparse_mqa_sink(const void* q, const void* kv, const int32_t* idx, int64_t batch, int64_t T, int64_t N, int H,
                         int c, int k, float scale, const float* sink, csa_dtype t, void* out, void* workspace,
                         size_t ws_bytes, csa_stream_t stream) {
+    return csa_sparse_mqa_swa(q, kv, idx, batch, T, N, H, c, k, scale, sink, nullptr, 0, 0, 0, 0, t, out, workspace,
+                              ws_bytes, stream);
+}
+
+int csa_sparse_mqa_swa(const void* q, const void* kv, const int32_t* idx, int64_t batch, int64_t T, int64_t N, int H,
+                       int c, int k, float scale, const float* sink, const void* win_kv, int64_t W, int64_t win_pos0,
+                       int64_t q_pos0, int n_win, csa_dtype t, void* out, void* workspace, size_t ws_bytes,
+                       csa_stream_t stream) {
     if (sink && (reinterpret_cast<uintptr_t>(sink) & 3u)) return CSA_ERR_INVALID_ARG;
+    if (n_win < 0 || W < 0 || win_pos0 < 0 || q_pos0 < 0) return CSA_ERR_INVALID_ARG;
+    if (n_win > 1024 || (n_win > 0 && t == CSA_KV_FP8_BF16)) return CSA_ERR_UNSUPPORTED;
+    if (n_win > 0 && W > 0 && (!win_kv || !aligned16(win_kv))) return CSA_ERR_INVALID_ARG;
+    if (N + W >= (int64_t(1) << 31)) return CSA_ERR_UNSUPPORTED;   // one 32-bit id space
     const bool mixed = t == CSA_KV_FP8_BF16;   // q and out are bf16 then
     int rc = check_mqa(q, kv, out, batch, T, N, H, c, scale, mixed ? CSA_BF16 : t);
     if (rc != CSA_OK) return rc;
@@ -215,9 +227,10 @@ int csa_sparse_mqa_sink(const void* q, const void* kv, const int32_t* idx, int64
         return CSA_ERR_UNSUPPORTED;
     if (batch == 0 || T == 0) return CSA_OK;
     if (!idx) return CSA_ERR_INVALID_ARG;
-    const size_t need = csa_sparse_mqa_workspace_size(batch, T, H, c, k, t);
+    const size_t need = csa_sparse_mqa_workspace_size(batch, T, H, c, k + n_win, t);
     if (need > 0 && (!workspace || ws_bytes < need || !aligned16(workspace))) return CSA_ERR_WORKSPACE;
-    return finish(csa::launch_sparse_mqa(q, kv, idx, batch, T, N, H, c, k, scale, t, out, workspace, sink,
+    const csa::SwaArgs swa{n_win > 0 ? win_kv : nullptr, n_win > 0 ? W : 0, win_pos0, q_pos0, n_win};
+    return finish(csa::launch_sparse_mqa(q, kv, idx, batch, T, N, H, c, k, scale, t, out, workspace, sink, swa,
                                          static_cast<hipStream_t>(stream)));
 }
 

@@ -56,12 +56,22 @@ uint32_t* topk_zero_region(void* extra_ws, int64_t rows, int64_t N);
 int launch_rope(void* x, int64_t batch, int64_t T, int H, int c, int d, int64_t pos0, int64_t pos_step, float base,
                 bool inverse, int t, hipStream_t stream);
 
+// Sliding-window branch of the sparse attention: raw (uncompressed) KV rows kv [batch, W, c]
+// at absolute positions win_pos0 + j; query t (position q_pos0 + t) also attends to the rows
+// whose position lies in [p - n_win + 1, p].  n_win = 0: no window.
+struct SwaArgs {
+    const void* kv;
+    int64_t W, win_pos0, q_pos0;
+    int n_win;
+};
+
 // Device workspace bytes launch_sparse_mqa needs (0: none) for the key-range partials.
 // `sink` (both MQA launchers): per-head sink logits [H] in natural-log units, or nullptr.
 size_t sparse_mqa_workspace(int64_t batch, int64_t T, int H, int c, int k, int t);
 
 int launch_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t batch, int64_t T, int64_t N, int H,
-                      int c, int k, float scale, int t, void* out, void* ws, const float* sink, hipStream_t stream);
+                      int c, int k, float scale, int t, void* out, void* ws, const float* sink, const SwaArgs& swa,
+                      hipStream_t stream);
 
 int launch_dense_mqa(const void* q, const void* kv, int64_t batch, int64_t T, int64_t q_pos0, int64_t N, int H, int c,
                      int ratio, float scale, int t, void* out, const float* sink, hipStream_t stream);

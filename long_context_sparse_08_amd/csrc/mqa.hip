@@ -29,11 +29,25 @@ __device__ __forceinline__ float sink_term(const float* sink, int64_t head, floa
     return (sink != nullptr && m != -INFINITY) ? exp2f(sink[head] * kLog2e - m) : 0.f;
 }
 
+// Key i of a row's list ([N] §1.3 and [M] §2.3.3 item 3: a sliding-window branch over the most
+// recent n_win uncompressed tokens joins the compressed entries): i < k is the selected entry
+// idx[row, i] (its id, or -1 if outside [0, N)); k <= i < k + n_win is the window token at
+// position p - n_win + 1 + (i - k), id N + its raw row, or -1 outside the given raw rows.
+__device__ __forceinline__ int list_key(const int32_t* __restrict__ idx, int64_t row, int k, int n_ent, int64_t p,
+                                        const SwaArgs& w, int i) {
+    if (i < k) {
+        const int s = idx[row * k + i];
+        return (uint32_t)s < (uint32_t)n_ent ? s : -1;
+    }
+    const int64_t pw = p - w.n_win + 1 + (i - k);
+    return (pw >= 0 && pw >= w.win_pos0 && pw < w.win_pos0 + w.W) ? n_ent + (int)(pw - w.win_pos0) : -1;
+}
+
 template <int DT, int CPL, bool DENSE>
 __global__ void __launch_bounds__(kGenWaves * kWave)
 mqa_generic(const void* __restrict__ q, const void* __restrict__ kv, const int32_t* __restrict__ idx, int64_t T,
             int64_t N, int H, int c, int k, float scale, int64_t q_pos0, int ratio, void* __restrict__ out,
-            const float* __restrict__ sink) {
+            const float* __restrict__ sink, SwaArgs swa) {
     const int lane = threadIdx.x & (kWave - 1);
     const int h = blockIdx.y * kGenWaves + threadIdx.x / kWave;
     const int64_t row = blockIdx.x;  // b*T + t
@@ -51,8 +65,7 @@ mqa_generic(const void* __restrict__ q, const void* __restrict__ kv, const int32
     }
     float mx = -INFINITY, den = 0.f;
 
-    const int64_t count = DENSE ? visible_entries(q_pos0 + t, ratio, N) : (int64_t)k;
-    const int32_t* ids = DENSE ? nullptr : idx + row * k;
+    const int64_t count = DENSE ? visible_entries(q_pos0 + t, ratio, N) : (int64_t)k + swa.n_win;
     const int64_t kvbase = b * N * c;
 
     for (int64_t r0 = 0; r0 < count; r0 += kKeyBatch) {
@@ -62,8 +75,8 @@ mqa_generic(const void* __restrict__ q, const void* __restrict__ kv, const int32
         for (int u = 0; u < kKeyBatch; ++u) {
             const int64_t r = r0 + u;
             int64_t s = -1;
-            if (r < count) s = DENSE ? r : (int64_t)ids[r];
-            ok[u] = s >= 0 && s < N;
+            if (r < count) s = DENSE ? r : (int64_t)list_key(idx, row, k, (int)N, swa.q_pos0 + t, swa, (int)r);
+            ok[u] = DENSE ? (s >= 0 && s < N) : s >= 0;
             sidx[u] = ok[u] ? s : 0;
         }
         float kvv[kKeyBatch][CPL], part[kKeyBatch];
@@ -73,7 +86,9 @@ mqa_generic(const void* __restrict__ q, const void* __restrict__ kv, const int32
 #pragma unroll
             for (int j = 0; j < CPL; ++j) {
                 const int d = lane + kWave * j;
-                kvv[u][j] = (ok[u] && d < c) ? load1<DT>(kv, kvbase + sidx[u] * c + d) : 0.f;
+                kvv[u][j] = !(ok[u] && d < c) ? 0.f
+                            : sidx[u] < N ? load1<DT>(kv, kvbase + sidx[u] * c + d)
+                                          : load1<DT>(swa.kv, (b * swa.W + sidx[u] - N) * c + d);
                 part[u] = fmaf(qv[j], kvv[u][j], part[u]);
             }
         }
@@ -103,7 +118,8 @@ mqa_generic(const void* __restrict__ q, const void* __restrict__ kv, const int32
 
 template <int DT, bool DENSE>
 int launch_generic(const void* q, const void* kv, const int32_t* idx, int64_t batch, int64_t T, int64_t N, int H, int c,
-                   int k, float scale, int64_t q_pos0, int ratio, void* out, const float* sink, hipStream_t stream) {
+                   int k, float scale, int64_t q_pos0, int ratio, void* out, const float* sink, const SwaArgs& swa,
+                   hipStream_t stream) {
     const int64_t rows = batch * T;
     if (rows > 0x7fffffffLL) return -2;
     const int cpl = (c + kWave - 1) / kWave;
@@ -111,7 +127,7 @@ int launch_generic(const void* q, const void* kv, const int32_t* idx, int64_t ba
 #define CSA_LAUNCH_CPL(C)                                                                                          \
     if (cpl <= C) {                                                                                                \
         hipLaunchKernelGGL((mqa_generic<DT, C, DENSE>), grid, dim3(kGenWaves * kWave), 0, stream, q, kv, idx, T, N, H, \
-                           c, k, scale, q_pos0, ratio, out, sink);                                                 \
+                           c, k, scale, q_pos0, ratio, out, sink, swa);                                            \
         return 0;                                                                                                  \
     }
     CSA_LAUNCH_CPL(1)
@@ -250,7 +266,7 @@ __global__ void __launch_bounds__(kMWaves * kWave, 2)   // two workgroups per CU
 mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
                 int64_t rows, int64_t T, int64_t N, int H, int k, int ks_count, int keys_per_split, float sl2,
                 int64_t q_pos0, int ratio, uint16_t* __restrict__ out, uint16_t* __restrict__ part,
-                float* __restrict__ part_ml, const float* __restrict__ sink) {
+                float* __restrict__ part_ml, const float* __restrict__ sink, SwaArgs swa) {
     // one array per pipeline parity: the DMA into one and the reads of the other are then
     // provably disjoint, so no wait for the in-flight gather is forced before the current
     // block's LDS reads
@@ -283,7 +299,7 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int hg = (int)(rem / ks_count), ks = (int)(rem % ks_count);
     if (row >= rows) return;
     const int64_t b = row / T;
-    const int64_t klen = DENSE ? visible_entries(q_pos0 + row % T, ratio, N) : (int64_t)k;
+    const int64_t klen = DENSE ? visible_entries(q_pos0 + row % T, ratio, N) : (int64_t)k + swa.n_win;
     const int key0 = ks * keys_per_split;
     const int nkeys = (int)max((int64_t)0, min(klen, (int64_t)key0 + keys_per_split) - key0);
     const int h0 = hg * kMHeadsWG;
@@ -303,7 +319,7 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
 #pragma unroll
         for (int u = 0; u < kIdsPerThread; ++u) {
             const int i = tid + u * kMWaves * kWave;
-            idv[u] = i < nkeys ? idx[row * k + key0 + i] : -1;
+            idv[u] = i < nkeys ? list_key(idx, row, k, n_ent, swa.q_pos0 + row % T, swa, key0 + i) : -1;
         }
     }
     // this wave's q (head tile tw) as the B operand of S^T: head n16, channels 32*s + 8*g .. +8
@@ -317,7 +333,7 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
 #pragma unroll
         for (int u = 0; u < kIdsPerThread; ++u) {
             const int i = tid + u * kMWaves * kWave;
-            const bool ok = i < nkeys && (uint32_t)idv[u] < (uint32_t)n_ent;
+            const bool ok = i < nkeys && idv[u] >= 0;
             if (i < nkeys) ids[i] = ok ? idv[u] : 0;
             const unsigned long long bits = __ballot(ok);
             if (lane == 0) {
@@ -348,6 +364,12 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     // this sequence's KV rows (N <= kMMaxEntries, checked at launch); loads past them read 0
     const __amdgpu_buffer_rsrc_t kvres = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(kvbytes), (short)0, (int)(uint32_t)(N * 2 * kMC), 0x00020000);
+    // the sequence's raw window rows (bf16, 1 KB each; none without a window)
+    const __amdgpu_buffer_rsrc_t winres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(swa.kv != nullptr ? static_cast<const void*>(static_cast<const uint8_t*>(swa.kv) +
+                                                                       b * swa.W * (int64_t)(2 * kMC))
+                                            : static_cast<const void*>(kvbytes)),
+        (short)0, swa.kv != nullptr ? (int)(uint32_t)(swa.W * 2 * kMC) : 0, 0x00020000);
     const uint32_t lane_off = 16u * lane;
     auto gather = [&](int blk, uint8_t* dst) {   // block `blk` of the range into `dst`
         // (the key ids one by one: at two workgroups per CU the kernel is at its register limit)
@@ -356,8 +378,9 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
             const int r = kMLoadsPerBlk * tw + r8;
             // one 1 KB row per instruction: the row is wave-uniform (scalar base, lane offset)
             const int sidx = __builtin_amdgcn_readfirstlane(key_id(blk * kMBlk + r));
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(kvres, (lds_void_ptr)(dst + r * kPitch), 16, lane_off,
-                                                     (uint32_t)sidx * (2 * kMC), 0, 0);
+            const bool wr = sidx >= n_ent;   // a window row (wave-uniform)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr ? winres : kvres, (lds_void_ptr)(dst + r * kPitch), 16,
+                                                     lane_off, (uint32_t)(wr ? sidx - n_ent : sidx) * (2 * kMC), 0, 0);
         }
     };
     auto compute = [&](int blk, const uint8_t* st) {
@@ -590,7 +613,7 @@ __global__ void __launch_bounds__(kWsWaves * kWave, 1)
 mqa_sparse_ws(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kvb, const int32_t* __restrict__ idx,
               int64_t rows, int64_t T, int64_t N, int H, int k, int ks_count, int keys_per_split, float sl2,
               uint16_t* __restrict__ out, uint16_t* __restrict__ part, float* __restrict__ part_ml,
-              const float* __restrict__ sink) {
+              const float* __restrict__ sink, SwaArgs swa) {
     constexpr int kPitch = kMPitch<true>, kBuf = kMBuf<true>;
     constexpr int kRawBuf = kMHT * kMixRegion;
     constexpr int kRowB = MIX ? kMixRowB : 2 * kMC;   // bytes of one KV row in memory
@@ -624,7 +647,7 @@ mqa_sparse_ws(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kvb, c
     if (row >= rows) return;
     const int64_t b = row / T;
     const int key0 = ks * keys_per_split;
-    const int nkeys = (int)max((int64_t)0, min((int64_t)k, (int64_t)key0 + keys_per_split) - key0);
+    const int nkeys = (int)max((int64_t)0, min((int64_t)k + swa.n_win, (int64_t)key0 + keys_per_split) - key0);
     const int h0 = hg * kMHeadsWG;
     const int n_ent = (int)N;
     auto key_id = [&](int i) -> int { return i < nkeys ? ids[i] : 0; };
@@ -635,12 +658,12 @@ mqa_sparse_ws(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kvb, c
 #pragma unroll
     for (int u = 0; u < kIdsPerThread; ++u) {
         const int i = tid + u * kWsWaves * kWave;
-        idv[u] = i < nkeys ? idx[row * k + key0 + i] : -1;
+        idv[u] = i < nkeys ? list_key(idx, row, k, n_ent, swa.q_pos0 + row % T, swa, key0 + i) : -1;
     }
 #pragma unroll
     for (int u = 0; u < kIdsPerThread; ++u) {
         const int i = tid + u * kWsWaves * kWave;
-        const bool ok = i < nkeys && (uint32_t)idv[u] < (uint32_t)n_ent;
+        const bool ok = i < nkeys && idv[u] >= 0;
         if (i < nkeys) ids[i] = ok ? idv[u] : 0;
         const unsigned long long bits = __ballot(ok);
         if (lane == 0) {
@@ -656,6 +679,12 @@ mqa_sparse_ws(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kvb, c
     // this sequence's KV rows (N * kRowB < 2^32, checked at launch); loads past them read 0
     const __amdgpu_buffer_rsrc_t kvres = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(kvbytes), (short)0, (int)(uint32_t)(N * kRowB), 0x00020000);
+    // the sequence's raw window rows (bf16, 1 KB each; none without a window)
+    const __amdgpu_buffer_rsrc_t winres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(swa.kv != nullptr ? static_cast<const void*>(static_cast<const uint8_t*>(swa.kv) +
+                                                                       b * swa.W * (int64_t)(2 * kMC))
+                                            : static_cast<const void*>(kvbytes)),
+        (short)0, swa.kv != nullptr ? (int)(uint32_t)(swa.W * 2 * kMC) : 0, 0x00020000);
 
     // Each role keeps its state inside its own branch (the barriers of the two branches pair
     // up one to one), so the score waves' q and the value waves' accumulators never share
@@ -678,8 +707,10 @@ mqa_sparse_ws(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kvb, c
         auto gather_row = [&](int myid, int r8, uint8_t* dst) {
             const int r = kMLoadsPerBlk * tw + r8;
             const int sidx = __builtin_amdgcn_readlane(myid, r8);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(kvres, (lds_void_ptr)(dst + r * kPitch), 16,
-                                                     16u * (lane ^ swz(r)), (uint32_t)sidx * kRowB, 0, 0);
+            const bool wr = sidx >= n_ent;   // a window row (wave-uniform)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr ? winres : kvres, (lds_void_ptr)(dst + r * kPitch), 16,
+                                                     16u * (lane ^ swz(r)), (uint32_t)(wr ? sidx - n_ent : sidx) * kRowB,
+                                                     0, 0);
         };
         // MIX: load j (0..4) of this wave's region of block blk; `myid` as from gather_ids
         auto gather_mix = [&](int myid, int j, uint8_t* dst) {
@@ -1077,9 +1108,12 @@ size_t sparse_mqa_workspace(int64_t batch, int64_t T, int H, int c, int k, int t
 }
 
 int launch_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t batch, int64_t T, int64_t N, int H,
-                      int c, int k, float scale, int t, void* out, void* ws, const float* sink, hipStream_t stream) {
+                      int c, int k, float scale, int t, void* out, void* ws, const float* sink, const SwaArgs& swa,
+                      hipStream_t stream) {
     if (batch == 0 || T == 0) return 0;
+    const int kt = k + swa.n_win;   // keys per row's list: the selected entries, then the window
     if (t == DT_KV_FP8_BF16) {
+        if (swa.n_win > 0) return -2;   // the window's raw rows are bf16: not on this path
         // mixed-precision KV rows: the warp-specialised kernel only (decode shapes)
         const int64_t rows = batch * T;
         if (c != kMC || H % kMHeadsWG != 0 || N < 0 || N > 0xffffffffLL / (kMC + 64) || k > kMIdsLds ||
@@ -1096,7 +1130,7 @@ int launch_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t
         }
         hipLaunchKernelGGL(mqa_sparse_ws<true>, dim3((unsigned)units), dim3(kWsWaves * kWave), 0, stream,
                            static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(kv), idx, rows, T, N, H, k, ks,
-                           kps, scale * kLog2e, static_cast<uint16_t*>(out), part, part_ml, sink);
+                           kps, scale * kLog2e, static_cast<uint16_t*>(out), part, part_ml, sink, swa);
         if (ks > 1) {
             const dim3 cgrid((unsigned)((rows + 7) / 8 * 8 * (H / kCombWaves))), cblock(kCombWaves * kWave);
             if (ks <= 4)
@@ -1108,10 +1142,10 @@ int launch_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t
         }
         return 0;
     }
-    if (t == DT_BF16 && c == kMC && H % kMHeadsWG == 0 && N > 0 && N <= kMMaxEntries) {
+    if (t == DT_BF16 && c == kMC && H % kMHeadsWG == 0 && N > 0 && N <= kMMaxEntries && swa.W <= kMMaxEntries) {
         const int64_t rows = batch * T;
-        const int ks = mqa_splits(rows, H, k);
-        const int kps = ((k + ks - 1) / ks + kMBlk - 1) / kMBlk * kMBlk;
+        const int ks = mqa_splits(rows, H, kt);
+        const int kps = ((kt + ks - 1) / ks + kMBlk - 1) / kMBlk * kMBlk;
         const int64_t units = ((rows + 7) / 8) * 8 * (H / kMHeadsWG) * ks;
         if (units > 0x7fffffffLL) return -2;
         uint16_t* part = nullptr;
@@ -1124,11 +1158,11 @@ int launch_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t
         if (units <= kMFillWGs)   // at most one workgroup per CU: two waves per SIMD in two roles
             hipLaunchKernelGGL(mqa_sparse_ws<false>, dim3((unsigned)units), dim3(kWsWaves * kWave), 0, stream,
                                static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(kv), idx, rows, T, N, H,
-                               k, ks, kps, sl2, static_cast<uint16_t*>(out), part, part_ml, sink);
+                               k, ks, kps, sl2, static_cast<uint16_t*>(out), part, part_ml, sink, swa);
         else
             hipLaunchKernelGGL((mqa_sparse_mfma<false>), dim3((unsigned)units), dim3(kMWaves * kWave), 0, stream,
                                static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx, rows, T, N, H,
-                               k, ks, kps, sl2, (int64_t)0, 1, static_cast<uint16_t*>(out), part, part_ml, sink);
+                               k, ks, kps, sl2, (int64_t)0, 1, static_cast<uint16_t*>(out), part, part_ml, sink, swa);
         if (ks > 1) {
             const dim3 cgrid((unsigned)((rows + 7) / 8 * 8 * (H / kCombWaves))), cblock(kCombWaves * kWave);
             if (ks <= 4)
@@ -1140,8 +1174,8 @@ int launch_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t
         }
         return 0;
     }
-    if (t == DT_F32) return launch_generic<DT_F32, false>(q, kv, idx, batch, T, N, H, c, k, scale, 0, 1, out, sink, stream);
-    if (t == DT_BF16) return launch_generic<DT_BF16, false>(q, kv, idx, batch, T, N, H, c, k, scale, 0, 1, out, sink, stream);
+    if (t == DT_F32) return launch_generic<DT_F32, false>(q, kv, idx, batch, T, N, H, c, k, scale, 0, 1, out, sink, swa, stream);
+    if (t == DT_BF16) return launch_generic<DT_BF16, false>(q, kv, idx, batch, T, N, H, c, k, scale, 0, 1, out, sink, swa, stream);
     return -2;
 }
 
@@ -1157,13 +1191,15 @@ int launch_dense_mqa(const void* q, const void* kv, int64_t batch, int64_t T, in
         hipLaunchKernelGGL((mqa_sparse_mfma<true>), dim3((unsigned)units), dim3(kMWaves * kWave), 0, stream,
                            static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), nullptr, rows, T, N, H, 0,
                            1, 0x7fffffff, scale * kLog2e, q_pos0, ratio, static_cast<uint16_t*>(out), nullptr, nullptr,
-                           sink);
+                           sink, SwaArgs{});
         return 0;
     }
     if (t == DT_F32)
-        return launch_generic<DT_F32, true>(q, kv, nullptr, batch, T, N, H, c, 0, scale, q_pos0, ratio, out, sink, stream);
+        return launch_generic<DT_F32, true>(q, kv, nullptr, batch, T, N, H, c, 0, scale, q_pos0, ratio, out, sink, SwaArgs{},
+                                                      stream);
     if (t == DT_BF16)
-        return launch_generic<DT_BF16, true>(q, kv, nullptr, batch, T, N, H, c, 0, scale, q_pos0, ratio, out, sink, stream);
+        return launch_generic<DT_BF16, true>(q, kv, nullptr, batch, T, N, H, c, 0, scale, q_pos0, ratio, out, sink, SwaArgs{},
+                                                      stream);
     return -2;
 }
 

@@ -204,8 +204,26 @@ def _sink(sink, H):
     return s
 
 
-def sparse_mqa(q, kv, idx, scale: float, dtype: int = F32, sink=None):
+def sparse_mqa(q, kv, idx, scale: float, dtype: int = F32, sink=None, window=None):
+    """window: (win_kv [batch, W, c], win_pos0, q_pos0, n_win) — the sliding-window branch (the
+    notes page §1.3): query t (position p = q_pos0 + t) also attends, in the same softmax, to
+    the raw rows at positions p - n_win + 1 .. p that win_kv holds.  Written as the plain
+    union: the raw rows are appended to the entries and their ids to the row's list."""
     q, kv = _d(q, dtype), _d(kv, dtype)
+    if window is not None:
+        wkv, wp0, qp0, n_win = window
+        wkv = _d(wkv, dtype)
+        batch, T = q.shape[0], q.shape[1]
+        N, W = kv.shape[1], wkv.shape[1]
+        idx = np.where((idx >= 0) & (idx < N), idx, -1).astype(np.int32)
+        wid = np.full((batch, T, n_win), -1, np.int32)
+        for t in range(T):
+            for j in range(n_win):
+                pw = qp0 + t - n_win + 1 + j
+                if pw >= 0 and wp0 <= pw < wp0 + W:
+                    wid[:, t, j] = N + (pw - wp0)
+        kv = np.concatenate([kv, wkv], axis=1)
+        idx = np.concatenate([idx, wid], axis=2)
     idx = np.ascontiguousarray(idx, dtype=np.int32)
     batch, T, H, c = q.shape
     N = kv.shape[1]

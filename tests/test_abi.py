@@ -156,6 +156,14 @@ def test_mqa_rejects_bad_arguments(L):
     assert L.hca_dense_mqa_sink(A, A, 1, 4, 0, 8, 4, 64, 128, 0.125, MIS2, 0, A, None) == INVALID
     assert L.csa_sparse_mqa_sink(A, A, A, 0, 4, 64, 4, 64, 8, 0.125, A, 0, A, None, 0, None) == OK
     assert L.hca_dense_mqa_sink(A, A, 1, 0, 0, 8, 4, 64, 128, 0.125, None, 0, A, None) == OK
+    # sliding window: n_win in [0, 1024], a raw-row buffer when there is a window, bf16 / fp32 KV
+    sw = L.csa_sparse_mqa_swa
+    assert sw(A, A, A, 1, 4, 64, 4, 64, 8, 0.125, None, A, 16, 0, 0, -1, 0, A, None, 0, None) == INVALID
+    assert sw(A, A, A, 1, 4, 64, 4, 64, 8, 0.125, None, A, 16, 0, 0, 2048, 0, A, None, 0, None) == UNSUPPORTED
+    assert sw(A, A, A, 1, 4, 64, 4, 64, 8, 0.125, None, None, 16, 0, 0, 8, 0, A, None, 0, None) == INVALID
+    assert sw(A, A, A, 1, 4, 64, 4, 64, 8, 0.125, None, MIS, 16, 0, 0, 8, 0, A, None, 0, None) == INVALID
+    assert sw(A, A, A, 1, 1, 100, 64, 512, 64, 0.05, None, A, 16, 0, 0, 8, mix, A, A, 1 << 30, None) == UNSUPPORTED
+    assert sw(A, A, A, 0, 4, 64, 4, 64, 8, 0.125, None, None, 0, 0, 0, 0, 0, A, None, 0, None) == OK
     # partial RoPE: d even, 2 <= d <= min(c, 128), base > 1, fp32 / bf16 rows
     r = L.csa_rope
     assert r(A, 1, 4, 64, 512, 63, 0, 1, 10000.0, 0, 1, None) == INVALID

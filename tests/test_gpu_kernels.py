@@ -407,6 +407,33 @@ def test_rope_parity(case):
         assert_fp32_close(back, oracle.decode(x, dt), "rope round trip")
 
 
+SWA_CASES = [  # batch, T, N, H, k, W, win_pos0, q_pos0, n_win, sink, dtype — one per kernel path
+    (2, 5, 40, 4, 8, 20, 0, 10, 6, False, F32),                     # generic kernel
+    (1, 300, 700, 64, 100, 300, 0, 0, 128, True, BF16),             # two-stage kernel: a prefill chunk
+    (3, 1, 3000, 128, 1024, 128, 131072 - 127, 131072, 128, True, BF16),   # decode: ranges merged
+    (2, 64, 900, 128, 256, 200, 60, 100, 128, False, BF16),         # warp-specialised, one range
+]
+
+
+@pytest.mark.parametrize("case", SWA_CASES, ids=lambda c: "b%d_T%d_N%d_H%d_k%d_W%d_w%d_p%d_n%d_%d_%d" % c)
+def test_sparse_mqa_sliding_window(case):
+    """Selected entries plus the raw rows of each query's last n_win positions in one softmax
+    (the notes page §1.3), against the oracle's plain union."""
+    batch, T, N, H, k, W, wp0, qp0, n_win, with_sink, dt = case
+    c = 64 if dt == F32 else 512
+    say(f"csa_sparse_mqa_swa {case}")
+    sd = 1700 + N
+    q, kv, wkv = draw(sd, 1, (batch, T, H, c), dt), draw(sd, 2, (batch, N, c), dt), draw(sd, 3, (batch, W, c), dt)
+    idx = _distinct_ids(np.random.RandomState(sd), batch, T, N, k)
+    sink = (2.0 * np.random.RandomState(sd).randn(H)).astype(np.float32) if with_sink else None
+    scale = 1.0 / np.sqrt(c)
+    ref = oracle.sparse_mqa(q, kv, idx, scale, dtype=dt, sink=sink, window=(wkv, wp0, qp0, n_win))
+    got = from_dev(csa.csa_sparse_mqa(to_dev(q, dt), to_dev(kv, dt), torch.from_numpy(idx).cuda(), scale,
+                                      sink=None if sink is None else torch.from_numpy(sink).cuda(),
+                                      window=(to_dev(wkv, dt), wp0, qp0, n_win)))
+    out_tol(dt)(got, ref, "sparse mqa + window")
+
+
 def test_repeat_runs_are_bitwise_identical():
     batch, T, N, H, c, k = 2, 3, 900, 64, 512, 256
     q, kv = draw(77, 1, (batch, T, H, c), BF16), draw(77, 2, (batch, N, c), BF16)

@@ -530,3 +530,31 @@ def test_rope_pairs_frequencies_and_relative_positions(orc):
     lhs = (orc.rope(a, 5000)[..., c - d:] * orc.rope(b, 4321)[..., c - d:]).sum()
     rhs = (orc.rope(a, 5000 - 4321)[..., c - d:] * b[..., c - d:]).sum()
     assert abs(lhs - rhs) < 1e-9 * max(1.0, abs(rhs))
+
+
+def test_sliding_window_branch(orc):
+    """Sliding-window branch (the notes page §1.3: each query also attends to the most recent
+    n_win uncompressed tokens): with nothing selected it is causal attention over the last n_win
+    raw rows (scipy softmax, written here independently); n_win = 0 changes nothing; a window
+    row and a selected entry share one softmax (the union equals attention over both rows)."""
+    r = np.random.RandomState(11)
+    B, T, H, c, W, n_win = 1, 6, 2, 8, 10, 4
+    q, wkv, kv = r.randn(B, T, H, c), r.randn(B, W, c), r.randn(B, 5, c)
+    idx = np.full((B, T, 3), -1, np.int32)
+    out = orc.sparse_mqa(q, kv, idx, 0.4, window=(wkv, 0, 2, n_win))
+    for t in range(T):
+        p = 2 + t
+        rows = [j for j in range(W) if p - n_win + 1 <= j <= p]
+        for h in range(H):
+            w = softmax(0.4 * wkv[0, rows] @ q[0, t, h])
+            assert np.allclose(out[0, t, h], w @ wkv[0, rows], rtol=1e-12, atol=1e-14)
+    sel = r.randint(0, 5, size=(B, T, 3)).astype(np.int32)
+    sel[..., 1] = -1
+    assert np.array_equal(orc.sparse_mqa(q, kv, sel, 0.4, window=(wkv, 0, 2, 0)), orc.sparse_mqa(q, kv, sel, 0.4))
+    one = np.zeros((B, T, 1), np.int32)          # entry 0 selected by every query
+    both = orc.sparse_mqa(q, kv, one, 0.4, window=(wkv, 3, 3, 1))   # plus the row at its own position
+    for t in range(T):
+        rows = np.stack([kv[0, 0], wkv[0, t]])
+        for h in range(H):
+            w = softmax(0.4 * rows @ q[0, t, h])
+            assert np.allclose(both[0, t, h], w @ rows, rtol=1e-12, atol=1e-14)
