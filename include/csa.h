@@ -239,6 +239,23 @@ int csa_sparse_mqa_swa(const void* q, const void* kv, const int32_t* idx, int64_
                        int64_t win_pos0, int64_t q_pos0, int n_win, csa_dtype t, void* out, void* workspace,
                        size_t ws_bytes, csa_stream_t stream);
 
+/*
+ * csa_compress_step — CSA compression as a decode step ([N] §1.1 step 1; [M] "state cache":
+ * the tokens of a block that is not complete yet, and the previous block's, stay uncompressed
+ * in a per-request state until the block fills): once block `block` (tokens m*block ..
+ * m*block + m - 1) is complete, computes compressed entry `block` exactly as csa_compress
+ * would for the whole sequence, and writes it to row `block` of the caller's cache.
+ *   Ca, Za, Cb, Zb : the state, [batch, 2m, c] each (the raw tokens of blocks block-1 and
+ *                    block, in token order); [batch, m, c] (block `block` only) when block == 0.
+ *   Ba, Bb         : [m, c] fp32 position biases.
+ *   cache          : [batch, cache_rows, c] dtype out_t; only row `block` of each sequence is
+ *                    written.  0 <= block < cache_rows.
+ * Dtypes and limits as csa_compress.
+ */
+int csa_compress_step(const void* Ca, const void* Cb, const void* Za, const void* Zb, const float* Ba,
+                      const float* Bb, int64_t batch, int64_t block, int m, int c, csa_dtype in_t, void* cache,
+                      int64_t cache_rows, csa_dtype out_t, csa_stream_t stream);
+
 /* Human-readable name of a csa_status value (static storage). */
 const char* csa_status_string(int status);
 

@@ -22,7 +22,7 @@ STATUS = {0: "CSA_OK", -1: "CSA_ERR_INVALID_ARG", -2: "CSA_ERR_UNSUPPORTED", -3:
 
 ENTRY_POINTS = ("csa_compress", "hca_compress", "csa_index_topk_workspace_size", "csa_index_topk",
                 "csa_index_scores", "csa_topk_workspace_size", "csa_topk", "csa_sparse_mqa_workspace_size", "csa_sparse_mqa",
-                "hca_dense_mqa", "csa_sparse_mqa_sink", "hca_dense_mqa_sink", "csa_sparse_mqa_swa", "csa_rope", "csa_status_string",
+                "hca_dense_mqa", "csa_sparse_mqa_sink", "hca_dense_mqa_sink", "csa_sparse_mqa_swa", "csa_rope", "csa_compress_step", "csa_status_string",
                 "csa_version")
 
 
@@ -50,6 +50,7 @@ def _load():
         "hca_dense_mqa": ([P, P, I64, I64, I64, I64, I, I, I, F, I, P, P], I),
         "csa_sparse_mqa_sink": ([P, P, P, I64, I64, I64, I, I, I, F, P, I, P, P, SZ, P], I),
         "csa_rope": ([P, I64, I64, I, I, I, I64, I64, F, I, I, P], I),
+        "csa_compress_step": ([P, P, P, P, P, P, I64, I64, I, I, I, P, I64, I, P], I),
         "csa_sparse_mqa_swa": ([P, P, P, I64, I64, I64, I, I, I, F, P, P, I64, I64, I64, I, I, P, P, SZ, P], I),
         "hca_dense_mqa_sink": ([P, P, I64, I64, I64, I64, I, I, I, F, P, I, P, P], I),
         "csa_status_string": ([I], ctypes.c_char_p),
@@ -287,6 +288,18 @@ def csa_sparse_mqa(q, kv, idx, scale: float, out=None, workspace=None, sink=None
                                                     _p(wkv), W, wp0, qp0, n_win, dt, _p(out), _p(workspace), ws_bytes,
                                                     _stream(dev)))
     return out
+
+
+def csa_compress_step(Ca, Cb, Za, Zb, Ba, Bb, block: int, cache):
+    """Decode-step CSA compression: the state streams [batch, 2m, c] (blocks block-1 and block;
+    [batch, m, c] when block == 0) -> row `block` of cache [batch, rows, c], in place."""
+    dev = _dev(Ca, Cb, Za, Zb, Ba, Bb, cache)
+    batch, ns, c = Ca.shape
+    m = Ba.shape[0]
+    assert ns == (2 * m if block > 0 else m) and cache.shape[0] == batch and cache.shape[2] == c
+    _check("csa_compress_step", lib.csa_compress_step(_p(Ca), _p(Cb), _p(Za), _p(Zb), _p(Ba), _p(Bb), batch, block, m, c,
+                                                      _dt(Ca), _p(cache), cache.shape[1], _dt(cache), _stream(dev)))
+    return cache
 
 
 def csa_rope(x, pos0: int, pos_step: int = 1, d: int = 64, base: float = 10000.0, inverse: bool = False):

@@ -87,6 +87,22 @@ int csa_compress(const void* Ca, const void* Cb, const void* Za, const void* Zb,
                                        static_cast<hipStream_t>(stream)));
 }
 
+int csa_compress_step(const void* Ca, const void* Cb, const void* Za, const void* Zb, const float* Ba,
+                      const float* Bb, int64_t batch, int64_t block, int m, int c, csa_dtype in_t, void* cache,
+                      int64_t cache_rows, csa_dtype out_t, csa_stream_t stream) {
+    if (batch < 0 || block < 0 || m < 1 || c < 1 || cache_rows <= block) return CSA_ERR_INVALID_ARG;
+    if (!io_dtype(in_t) || !io_dtype(out_t)) return CSA_ERR_UNSUPPORTED;
+    if (!width_ok(c) || m > CSA_MAX_RATIO) return CSA_ERR_UNSUPPORTED;
+    if (batch == 0) return CSA_OK;
+    if (!Ca || !Za || !Ba || !cache || (block > 0 && (!Cb || !Zb || !Bb))) return CSA_ERR_INVALID_ARG;
+    if (!aligned16(Ca) || !aligned16(Za) || !aligned16(Ba) || !aligned16(cache) ||
+        (block > 0 && (!aligned16(Cb) || !aligned16(Zb) || !aligned16(Bb))))
+        return CSA_ERR_INVALID_ARG;
+    return finish(csa::launch_compress_step(Ca, Za, Ba, block > 0 ? Cb : Ca, block > 0 ? Zb : Za, block > 0 ? Bb : Ba,
+                                            batch, block, m, c, in_t, cache, cache_rows, out_t,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 int hca_compress(const void* C, const void* Z, const float* B, int64_t batch, int64_t n, int m_prime, int c,
                  csa_dtype in_t, void* out, csa_dtype out_t, csa_stream_t stream) {
     if (batch < 0 || n < 0 || m_prime < 1 || c < 1) return CSA_ERR_INVALID_ARG;

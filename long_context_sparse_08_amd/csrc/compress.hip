@@ -32,6 +32,9 @@ struct CompressArgs {
     int64_t batch, n, N;
     int m, c;
     void* out;
+    // entries first .. N-1 of each sequence are computed; entry i of sequence b goes to output
+    // row b * out_ld + out_off + (i - first)
+    int64_t first, out_ld, out_off;
 };
 
 template <int DTI, int DTO>
@@ -41,7 +44,8 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a, int 
     const int row = tid / G, g = tid - row * G;
     const int e_local = row / split, part = row - e_local * split;
     const int64_t ent = (int64_t)blockIdx.x * epb + e_local;
-    const bool active = (g < G) && (row < epb * split) && (ent < a.batch * a.N);
+    const int64_t per_seq = a.N - a.first;
+    const bool active = (g < G) && (row < epb * split) && (ent < a.batch * per_seq);
     const bool overlap = a.Cb != nullptr;
 
     float mx[8], sum[8], acc[8];
@@ -50,8 +54,8 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a, int 
 
     int64_t b = 0, i = 0;
     if (active) {
-        b = ent / a.N;
-        i = ent - b * a.N;
+        b = ent / per_seq;
+        i = a.first + (ent - b * per_seq);
         const int m = a.m;
         const int W = overlap ? 2 * m : m;        // window positions u: [0,m) stream a, [m,2m) stream b
         const int per = (W + split - 1) / split;
@@ -128,7 +132,7 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a, int 
         float o[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = acc[e] / sum[e];
-        store8<DTO>(a.out, ent * a.c + 8 * g, o);
+        store8<DTO>(a.out, (b * a.out_ld + a.out_off + (i - a.first)) * a.c + 8 * g, o);
     }
 }
 
@@ -141,7 +145,7 @@ int launch(const CompressArgs& a, hipStream_t stream) {
     // split long windows across rows (>= 8 tokens per part) to keep more loads in flight
     while (split * 2 <= rows && W / (split * 2) >= 8) split *= 2;
     const int epb = rows / split;
-    const int64_t entries = a.batch * a.N;
+    const int64_t entries = a.batch * (a.N - a.first);
     const int64_t blocks = (entries + epb - 1) / epb;
     if (blocks > 0x7fffffffLL) return -2;
     hipLaunchKernelGGL((compress_kernel<DTI, DTO>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a, G, split,
@@ -149,17 +153,36 @@ int launch(const CompressArgs& a, hipStream_t stream) {
     return 0;
 }
 
+int launch_any(const CompressArgs& a, int in_t, int out_t, hipStream_t stream);
+
 }  // namespace
 
 int launch_compress(const void* Ca, const void* Za, const float* Ba, const void* Cb, const void* Zb, const float* Bb,
                     int64_t batch, int64_t n, int m, int c, int in_t, void* out, int out_t, hipStream_t stream) {
-    CompressArgs a{Ca, Za, Ba, Cb, Zb, Bb, batch, n, n / m, m, c, out};
+    CompressArgs a{Ca, Za, Ba, Cb, Zb, Bb, batch, n, n / m, m, c, out, 0, n / m, 0};
     if (a.N == 0 || batch == 0) return 0;
+    return launch_any(a, in_t, out_t, stream);
+}
+
+int launch_compress_step(const void* Ca, const void* Za, const float* Ba, const void* Cb, const void* Zb,
+                         const float* Bb, int64_t batch, int64_t block, int m, int c, int in_t, void* cache,
+                         int64_t cache_rows, int out_t, hipStream_t stream) {
+    // the state holds the raw tokens of blocks block-1 and block (only block 0 when block == 0):
+    // entry `block` is the last entry of that 2m- (or m-) token sequence
+    const int64_t ns = block > 0 ? 2 * (int64_t)m : m;
+    CompressArgs a{Ca, Za, Ba, Cb, Zb, Bb, batch, ns, ns / m, m, c, cache, ns / m - 1, cache_rows, block};
+    if (batch == 0) return 0;
+    return launch_any(a, in_t, out_t, stream);
+}
+
+namespace {
+int launch_any(const CompressArgs& a, int in_t, int out_t, hipStream_t stream) {
     if (in_t == DT_F32 && out_t == DT_F32) return launch<DT_F32, DT_F32>(a, stream);
     if (in_t == DT_F32 && out_t == DT_BF16) return launch<DT_F32, DT_BF16>(a, stream);
     if (in_t == DT_BF16 && out_t == DT_F32) return launch<DT_BF16, DT_F32>(a, stream);
     if (in_t == DT_BF16 && out_t == DT_BF16) return launch<DT_BF16, DT_BF16>(a, stream);
     return -2;
 }
+}  // namespace
 
 }  // namespace csa

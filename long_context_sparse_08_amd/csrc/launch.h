@@ -12,6 +12,13 @@ namespace csa {
 int launch_compress(const void* Ca, const void* Za, const float* Ba, const void* Cb, const void* Zb, const float* Bb,
                     int64_t batch, int64_t n, int m, int c, int in_t, void* out, int out_t, hipStream_t stream);
 
+// One decode step of CSA compression: the state holds the raw tokens of blocks block-1 and
+// block ([batch, 2m, c] each stream; [batch, m, c] when block == 0); writes entry `block` to
+// row `block` of the cache [batch, cache_rows, c].
+int launch_compress_step(const void* Ca, const void* Za, const float* Ba, const void* Cb, const void* Zb,
+                         const float* Bb, int64_t batch, int64_t block, int m, int c, int in_t, void* cache,
+                         int64_t cache_rows, int out_t, hipStream_t stream);
+
 // Indexer scores for every (query, entry) pair into `scores` ([batch*T, ld] fp32, ld >= N).
 // write_invisible: also write -inf for entries the query may not see (else they are skipped).
 // chunk_mm (optional, [batch*T, index_chunks(...)] pairs): min / max of each chunk of visible

@@ -74,6 +74,17 @@ def test_compress_rejects_bad_arguments(L):
     assert call(n=3, c=60) == UNSUPPORTED      # ...but sizes and dtypes are still checked
 
 
+def test_compress_step_rejects_bad_arguments(L):
+    f = L.csa_compress_step   # Ca, Cb, Za, Zb, Ba, Bb, batch, block, m, c, in_t, cache, rows, out_t, stream
+    assert f(A, A, A, A, A, A, 1, 5, 4, 64, 0, A, 5, 0, None) == INVALID      # block past the cache
+    assert f(A, None, A, A, A, A, 1, 2, 4, 64, 0, A, 8, 0, None) == INVALID   # no stream b past block 0
+    assert f(A, A, A, A, A, A, 1, -1, 4, 64, 0, A, 8, 0, None) == INVALID
+    assert f(A, A, A, A, A, A, 1, 2, 4, 60, 0, A, 8, 0, None) == UNSUPPORTED
+    assert f(A, A, A, A, A, A, 1, 2, 4, 64, 2, A, 8, 0, None) == UNSUPPORTED
+    assert f(A, A, MIS, A, A, A, 1, 2, 4, 64, 0, A, 8, 0, None) == INVALID
+    assert f(None, None, None, None, None, None, 0, 2, 4, 64, 0, None, 8, 0, None) == OK
+
+
 def test_hca_compress_rejects_bad_arguments(L):
     f = L.hca_compress
     assert f(None, A, A, 1, 256, 128, 64, 0, A, 0, None) == INVALID

@@ -434,6 +434,33 @@ def test_sparse_mqa_sliding_window(case):
     out_tol(dt)(got, ref, "sparse mqa + window")
 
 
+@pytest.mark.parametrize("dt", [F32, BF16])
+def test_compress_step_matches_whole_sequence(dt):
+    """Decode-step compression from a state of the last two blocks (the state cache of the
+    pages' serving section) writes exactly the entry csa_compress computes for the whole
+    sequence, and only that cache row; block 0 takes a one-block state."""
+    batch, m, c, nb = 2, 4, 512 if dt == BF16 else 64, 9
+    n = m * nb
+    say(f"csa_compress_step dt={dt}")
+    sd = 1800 + c
+    st = {k: draw(sd, i + 1, (batch, n, c), dt) for i, k in enumerate(("Ca", "Cb", "Za", "Zb"))}
+    Ba, Bb = draw(sd, 5, (m, c), F32, std=0.1), draw(sd, 6, (m, c), F32, std=0.1)
+    dev = {k: to_dev(v, dt) for k, v in st.items()}
+    Bad, Bbd = to_dev(Ba, F32), to_dev(Bb, F32)
+    full = csa.csa_compress(dev["Ca"], dev["Cb"], dev["Za"], dev["Zb"], Bad, Bbd, m,
+                            out=torch.empty((batch, nb, c), dtype=dev["Ca"].dtype, device="cuda"))
+    cache = torch.zeros((batch, nb + 3, c), dtype=dev["Ca"].dtype, device="cuda")
+    for blk in range(nb):
+        t0 = m * max(0, blk - 1)
+        sl = {k: v[:, t0:m * (blk + 1)].contiguous() for k, v in dev.items()}
+        csa.csa_compress_step(sl["Ca"], sl["Cb"], sl["Za"], sl["Zb"], Bad, Bbd, blk, cache)
+    assert torch.equal(cache[:, :nb], full)
+    assert not cache[:, nb:].any()
+    ref = oracle.csa_compress(st["Ca"], st["Cb"], st["Za"], st["Zb"], Ba, Bb, m, in_dtype=dt,
+                              out_dtype=dt)
+    out_tol(dt)(from_dev(cache[:, :nb]), ref, "compress step")
+
+
 def test_repeat_runs_are_bitwise_identical():
     batch, T, N, H, c, k = 2, 3, 900, 64, 512, 256
     q, kv = draw(77, 1, (batch, T, H, c), BF16), draw(77, 2, (batch, N, c), BF16)
