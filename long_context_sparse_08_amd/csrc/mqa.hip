@@ -261,7 +261,7 @@ constexpr int kMColBlkW = kMColW / 16;    // 16-column blocks per wave (8)
 constexpr int kMIdsLds = 1024;            // key ids staged per workgroup (longer ranges are split)
 constexpr int kMFillWGs = 256;            // workgroups a key split aims for
 
-template <bool DENSE>
+template <bool DENSE, bool WIN>   // WIN: the row lists hold window tokens (a second KV buffer)
 __global__ void __launch_bounds__(kMWaves * kWave, 2)   // two workgroups per CU
 mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
                 int64_t rows, int64_t T, int64_t N, int H, int k, int ks_count, int keys_per_split, float sl2,
@@ -378,7 +378,7 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
             const int r = kMLoadsPerBlk * tw + r8;
             // one 1 KB row per instruction: the row is wave-uniform (scalar base, lane offset)
             const int sidx = __builtin_amdgcn_readfirstlane(key_id(blk * kMBlk + r));
-            const bool wr = sidx >= n_ent;   // a window row (wave-uniform)
+            const bool wr = WIN && sidx >= n_ent;   // a window row (wave-uniform)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(wr ? winres : kvres, (lds_void_ptr)(dst + r * kPitch), 16,
                                                      lane_off, (uint32_t)(wr ? sidx - n_ent : sidx) * (2 * kMC), 0, 0);
         }
@@ -608,7 +608,7 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
     return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-template <bool MIX>
+template <bool MIX, bool WIN>   // WIN: the row lists hold window tokens (a second KV buffer)
 __global__ void __launch_bounds__(kWsWaves * kWave, 1)
 mqa_sparse_ws(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kvb, const int32_t* __restrict__ idx,
               int64_t rows, int64_t T, int64_t N, int H, int k, int ks_count, int keys_per_split, float sl2,
@@ -707,7 +707,7 @@ mqa_sparse_ws(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kvb, c
         auto gather_row = [&](int myid, int r8, uint8_t* dst) {
             const int r = kMLoadsPerBlk * tw + r8;
             const int sidx = __builtin_amdgcn_readlane(myid, r8);
-            const bool wr = sidx >= n_ent;   // a window row (wave-uniform)
+            const bool wr = WIN && sidx >= n_ent;   // a window row (wave-uniform)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(wr ? winres : kvres, (lds_void_ptr)(dst + r * kPitch), 16,
                                                      16u * (lane ^ swz(r)), (uint32_t)(wr ? sidx - n_ent : sidx) * kRowB,
                                                      0, 0);
@@ -1128,7 +1128,7 @@ int launch_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t
             part = static_cast<uint16_t*>(ws);
             part_ml = reinterpret_cast<float*>(part + rows * ks * H * (int64_t)kMC);
         }
-        hipLaunchKernelGGL(mqa_sparse_ws<true>, dim3((unsigned)units), dim3(kWsWaves * kWave), 0, stream,
+        hipLaunchKernelGGL((mqa_sparse_ws<true, false>), dim3((unsigned)units), dim3(kWsWaves * kWave), 0, stream,
                            static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(kv), idx, rows, T, N, H, k, ks,
                            kps, scale * kLog2e, static_cast<uint16_t*>(out), part, part_ml, sink, swa);
         if (ks > 1) {
@@ -1156,11 +1156,13 @@ int launch_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t
         }
         const float sl2 = scale * kLog2e;
         if (units <= kMFillWGs)   // at most one workgroup per CU: two waves per SIMD in two roles
-            hipLaunchKernelGGL(mqa_sparse_ws<false>, dim3((unsigned)units), dim3(kWsWaves * kWave), 0, stream,
+            hipLaunchKernelGGL((swa.n_win > 0 ? mqa_sparse_ws<false, true> : mqa_sparse_ws<false, false>),
+                               dim3((unsigned)units), dim3(kWsWaves * kWave), 0, stream,
                                static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(kv), idx, rows, T, N, H,
                                k, ks, kps, sl2, static_cast<uint16_t*>(out), part, part_ml, sink, swa);
         else
-            hipLaunchKernelGGL((mqa_sparse_mfma<false>), dim3((unsigned)units), dim3(kMWaves * kWave), 0, stream,
+            hipLaunchKernelGGL((swa.n_win > 0 ? mqa_sparse_mfma<false, true> : mqa_sparse_mfma<false, false>),
+                               dim3((unsigned)units), dim3(kMWaves * kWave), 0, stream,
                                static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx, rows, T, N, H,
                                k, ks, kps, sl2, (int64_t)0, 1, static_cast<uint16_t*>(out), part, part_ml, sink, swa);
         if (ks > 1) {
@@ -1188,7 +1190,7 @@ int launch_dense_mqa(const void* q, const void* kv, int64_t batch, int64_t T, in
         const int64_t rows = batch * T;
         const int64_t units = ((rows + 7) / 8) * 8 * (H / kMHeadsWG);
         if (units > 0x7fffffffLL) return -2;
-        hipLaunchKernelGGL((mqa_sparse_mfma<true>), dim3((unsigned)units), dim3(kMWaves * kWave), 0, stream,
+        hipLaunchKernelGGL((mqa_sparse_mfma<true, false>), dim3((unsigned)units), dim3(kMWaves * kWave), 0, stream,
                            static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), nullptr, rows, T, N, H, 0,
                            1, 0x7fffffff, scale * kLog2e, q_pos0, ratio, static_cast<uint16_t*>(out), nullptr, nullptr,
                            sink, SwaArgs{});
