@@ -64,7 +64,7 @@ def counter_mean(run_dir: str, counter: str, kernel_substr: str) -> tuple[float,
 
 def write_stats(a):
     rows = kernel_stats(a.csv)
-    lines = [f"# {a.title}", "", "Command (from the repository root, GPU box):", "", "```", a.command, "```", "",
+    lines = [f"# {a.title}", "", "Command (from the repository root, on an MI355X):", "", "```", a.command, "```", "",
              "| kernel | calls | average µs | total µs |", "|---|---:|---:|---:|"]
     for n, c, avg, tot in rows:
         lines.append(f"| `{n}` | {c} | {avg / 1e3:.2f} | {tot / 1e3:.1f} |")
@@ -94,7 +94,7 @@ def write_counters(a):
              f"| write | {w_k:.1f} | {w_scale:.4f} | {write_b:.4g} |",
              f"| copy calibration fetch / write | {f_c:.1f} / {w_c:.1f} | | {a.copy_bytes} |", "",
              f"Source `{a.source}` sha256[:16] = `{rec['source_sha']}` (bench.py reports this traffic only while",
-             "the file is unchanged).", "", "Commands (from the repository root, GPU box):", "", "```"]
+             "the file is unchanged).", "", "Commands (from the repository root, on an MI355X):", "", "```"]
     lines += list(a.commands) + ["```", "", MARK + json.dumps(rec) + " -->"]
     open(a.out, "w").write("\n".join(lines) + "\n")
 
