@@ -45,6 +45,11 @@ def stage_work(cfg):
     B, c, H = cfg.batch, cfg.c, cfg.H
     e = DT_BYTES[cfg.dt]
     st = {}
+    if cfg.kind == "csa_compress":
+        n = cfg.n
+        st["compress"] = dict(bytes=4 * B * n * c * e + B * (n // cfg.m) * c * e + 2 * cfg.m * c * 4, flops=0,
+                              bound="hbm")
+        return st
     if cfg.kind in ("csa_decode", "csa_prefill"):
         T, N, HI, cI, k = cfg.T, cfg.N, cfg.H_I, cfg.c_I, cfg.k
         eq = DT_BYTES[cfg.qk_dt]
@@ -122,6 +127,12 @@ def _cpu_sample(cfg, host):
         oracle.sparse_mqa(sub["q"], sub["kv"], idx, cfg.scale, dtype=cfg.dt)
         tokens = nseq * cfg.T
         sample = f"all {nseq} sequences x {cfg.T} token (index + top-k + MQA, float64)"
+    elif cfg.kind == "csa_compress":
+        nt = 1 << 16
+        oracle.csa_compress(*(host[k][:, :nt] for k in ("Ca", "Cb", "Za", "Zb")), host["Ba"], host["Bb"], cfg.m,
+                            in_dtype=cfg.dt, out_dtype=cfg.dt)
+        tokens = nt
+        sample = f"the first {nt} tokens of the sequence (CSA compression, float64)"
     elif cfg.kind == "csa_prefill":
         rows = np.arange(cfg.T - 64, cfg.T)
         dt = cfg.dt
@@ -174,7 +185,7 @@ def main():
     import torch
 
     import long_context_sparse_08_amd as csa
-    from long_context_sparse_08_amd.pipeline import CsaDecode, CsaPrefill, HcaChunk
+    from long_context_sparse_08_amd.pipeline import CsaCompress, CsaDecode, CsaPrefill, HcaChunk
     from workloads import CONFIGS, make_inputs, shapes
 
     cfg = CONFIGS[args.config]
@@ -200,6 +211,8 @@ def main():
         pipe = CsaDecode(dev, cfg.m, cfg.k, cfg.q_pos0)
     elif cfg.kind == "csa_prefill":
         pipe = CsaPrefill(dev, cfg.m, cfg.k, cfg.q_pos0)
+    elif cfg.kind == "csa_compress":
+        pipe = CsaCompress(dev, cfg.m)
     else:
         pipe = HcaChunk(dev, cfg.m_prime, cfg.q_pos0)
 
@@ -254,6 +267,8 @@ def main():
         # (decode launches have at most one workgroup per CU: the warp-specialised kernel)
         stages["attend"] = (pipe.attend, ["mqa_sparse_ws"] + (["mqa_combine"] if split else []),
                             None if split else "mqa")
+    elif cfg.kind == "csa_compress":
+        stages["compress"] = (pipe.run, ["compress_kernel"], "compress")
     elif cfg.kind == "csa_prefill":
         scores = torch.empty((cfg.batch, cfg.T, cfg.N), dtype=torch.float32, device="cuda")
         stages["compress_kv"] = (lambda: csa.csa_compress(i["Ca"], i["Cb"], i["Za"], i["Zb"], i["Ba"], i["Bb"], cfg.m,

@@ -87,6 +87,19 @@ class CsaDecode:
         return self.out
 
 
+class CsaCompress:
+    """CSA compression of whole sequences (the step of a prefill that builds the KV cache)."""
+
+    def __init__(self, inp: dict, m: int):
+        self.inp, self.m = inp, m
+        batch, n, c = inp["Ca"].shape
+        self.kv = torch.empty((batch, n // m, c), dtype=inp["Ca"].dtype, device=inp["Ca"].device)
+
+    def run(self):
+        i = self.inp
+        return csa_compress(i["Ca"], i["Cb"], i["Za"], i["Zb"], i["Ba"], i["Bb"], self.m, out=self.kv)
+
+
 class HcaChunk:
     def __init__(self, inp: dict, m_prime: int, q_pos0: int, scale: float | None = None):
         self.inp, self.mp, self.q_pos0 = inp, m_prime, q_pos0

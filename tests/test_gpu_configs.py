@@ -10,7 +10,7 @@ import torch
 
 import long_context_sparse_08_amd as csa
 import oracle
-from long_context_sparse_08_amd.pipeline import CsaDecode, CsaPrefill, HcaChunk
+from long_context_sparse_08_amd.pipeline import CsaCompress, CsaDecode, CsaPrefill, HcaChunk
 from tests._util import (BF16, F32, FP8, assert_abs_close, assert_fp32_close, check_topk_recall, from_dev, say,
                          to_dev)
 from workloads import CONFIGS, make_inputs, rng, shapes
@@ -179,3 +179,21 @@ def test_cfg3_hca_chunk_sampled():
     qpos = cfg.q_pos0 + rows
     out = oracle.hca_dense_mqa(h["q"][:, rows], kv, cfg.m_prime, cfg.scale, dtype=cfg.dt, qpos=qpos)
     assert_abs_close(from_dev(pipe.out)[:, rows], out, 2e-2, "O")
+
+
+@pytest.mark.timeout(900)
+def test_s1_csa_compress_1m_sampled():
+    """CSA compression of a whole 1M-token sequence (4 GiB of bf16 streams) on the GPU; the
+    oracle recomputes sampled entries from their own windows (an entry reads only its block
+    and the previous one), entry 0 and the last entry included."""
+    cfg = CONFIGS["s1_csa_compress_1m"]
+    say(f"config {cfg.name}: GPU full size, oracle on sampled entries")
+    h = make_inputs(cfg)
+    d = upload(cfg, h)
+    out = from_dev(CsaCompress(d, cfg.m).run())
+    m, N = cfg.m, cfg.n // cfg.m
+    for e in [0, 1, 777, N // 2, N - 2, N - 1]:
+        t0 = m * max(0, e - 1)
+        sl = [h[k][:, t0:m * (e + 1)] for k in ("Ca", "Cb", "Za", "Zb")]
+        ref = oracle.csa_compress(*sl, h["Ba"], h["Bb"], m, in_dtype=cfg.dt, out_dtype=cfg.dt)[:, -1]
+        assert_abs_close(out[:, e], ref, 2e-2, f"entry {e}")

@@ -78,6 +78,10 @@ CONFIGS = {
     "cfg2_csa_decode_128k_mxfp4": Config("cfg2_csa_decode_128k_mxfp4", "csa_decode", batch=32, dt=BF16, c=512,
                                          H=128, k=1024, m=4, H_I=64, c_I=128, qk_dt=MXFP4, T=1,
                                          q_pos0=131072, N=32768, seed=1002),
+    # CSA compression alone over a 1M-token sequence (4 GiB of bf16 streams): the compressor's
+    # bandwidth at full size; T counts the raw tokens compressed per step
+    "s1_csa_compress_1m": Config("s1_csa_compress_1m", "csa_compress", batch=1, dt=BF16, c=512, H=0, n=1 << 20, m=4,
+                                 T=1 << 20, seed=1005),
     # the decode at a 128K context with the KV entries in the mixed storage (the notes page's
     # §1.3: RoPE channels in bf16, the others in fp8); same seed and draws as the bf16 decode
     "cfg2_csa_decode_128k_kvmixed": Config("cfg2_csa_decode_128k_kvmixed", "csa_decode", batch=32, dt=BF16, c=512,
@@ -101,6 +105,11 @@ def shapes(cfg: Config) -> dict:
             s[nm] = ((B, n, cI), cfg.dt, ("normal", 1.0))
         for nm in ("IBa", "IBb"):
             s[nm] = ((m, cI), F32, ("normal", 0.1))
+    if cfg.kind == "csa_compress":
+        for nm in ("Ca", "Cb", "Za", "Zb"):
+            s[nm] = ((B, cfg.n, c), cfg.dt, ("normal", 1.0))
+        for nm in ("Ba", "Bb"):
+            s[nm] = ((cfg.m, c), F32, ("normal", 0.1))
     if cfg.kind == "csa_decode":
         s["kv"] = ((B, cfg.N, c), cfg.dt if cfg.kv_dt < 0 else cfg.kv_dt, ("normal", 1.0))
         s["kI"] = ((B, cfg.N, cfg.c_I), cfg.qk_dt, ("normal", 1.0))
