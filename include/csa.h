@@ -19,7 +19,8 @@
  *     the query.
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null stream).  The
  *     library never allocates device memory, never synchronises, and holds no mutable global
- *     state, so calls on different streams may overlap freely.
+ *     state other than the fixed scratch of csa_index_topk_noalloc, so calls on different
+ *     streams may overlap freely (calls of csa_index_topk_noalloc on one GPU excepted).
  *   - A tensor with zero elements may be passed as NULL (calls with an empty output return
  *     CSA_OK after the size and dtype checks and launch nothing).
  *   - Return value: CSA_OK or a negative csa_status.  All argument checks run on the host
@@ -61,7 +62,8 @@ typedef enum {
     CSA_ERR_INVALID_ARG = -1,  /* null pointer, negative or inconsistent size */
     CSA_ERR_UNSUPPORTED = -2,  /* valid but not implemented: dtype combination or shape limit */
     CSA_ERR_WORKSPACE = -3,    /* workspace pointer null or smaller than the required size */
-    CSA_ERR_HIP = -4           /* the HIP runtime reported an error at launch */
+    CSA_ERR_HIP = -4,          /* the HIP runtime reported an error at launch */
+    CSA_ERR_TOO_LARGE = -5     /* csa_index_topk_noalloc: the call needs more than its fixed scratch */
 } csa_status;
 
 /* A hipStream_t passed through the C ABI. */
@@ -133,6 +135,31 @@ size_t csa_index_topk_workspace_size(int64_t batch, int64_t T, int64_t N, int H_
 int csa_index_topk(const void* qI, const float* w, const void* kI, int64_t batch, int64_t T, int64_t q_pos0,
                    int64_t N, int H_I, int c_I, int m, int k, csa_dtype qk_t, int32_t* idx, float* sel_scores,
                    void* workspace, size_t ws_bytes, csa_stream_t stream);
+
+/*
+ * csa_index_topk_noalloc — csa_index_topk for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation, arguments and results, without a workspace argument.  Its scratch is a
+ * fixed array of CSA_NOALLOC_SCRATCH_BYTES in the library's device code, one copy per GPU,
+ * held from the first call on that GPU until the process ends; its address is looked up on
+ * the first call on each device (hipGetSymbolAddress, no allocation).  The call runs on the
+ * CURRENT device (hipSetDevice), which must be the device of `stream` and of every pointer.
+ * No call allocates, frees or synchronises.
+ * Every call on a GPU uses that GPU's one scratch array: calls that may overlap on one GPU
+ * (on different streams, or from several host threads) RACE and must be serialised by the
+ * caller, e.g. by issuing them on one stream.  Nothing is assumed about the array's contents
+ * on entry (it keeps the previous call's data).
+ * Returns CSA_ERR_TOO_LARGE when csa_index_topk_workspace_size(batch, T, N, H_I, k) exceeds
+ * CSA_NOALLOC_SCRATCH_BYTES (about 32 query rows of up to 224,000 entries, or 8 rows of up to
+ * 976,000: decode batches of 32 sequences at a 128K-token context and of 8 at a 1M-token
+ * context fit; the 8192 query rows of an 8K-token prefill do not),
+ * CSA_ERR_HIP when the device or the scratch address cannot be obtained; otherwise as
+ * csa_index_topk (argument checks first: an invalid call makes no HIP call at all).
+ */
+#define CSA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int csa_index_topk_noalloc(const void* qI, const float* w, const void* kI, int64_t batch, int64_t T, int64_t q_pos0,
+                           int64_t N, int H_I, int c_I, int m, int k, csa_dtype qk_t, int32_t* idx, float* sel_scores,
+                           csa_stream_t stream);
 
 /*
  * csa_index_scores — the indexer scores alone, as a dense [batch, T, N] float32 matrix

@@ -18,9 +18,11 @@ LIB_PATH = os.path.join(HERE, "_build", "libcsa.so")
 
 CSA_F32, CSA_BF16, CSA_FP8_E4M3, CSA_MXFP4, CSA_KV_FP8_BF16 = 0, 1, 2, 3, 4
 STATUS = {0: "CSA_OK", -1: "CSA_ERR_INVALID_ARG", -2: "CSA_ERR_UNSUPPORTED", -3: "CSA_ERR_WORKSPACE",
-          -4: "CSA_ERR_HIP"}
+          -4: "CSA_ERR_HIP", -5: "CSA_ERR_TOO_LARGE"}
+NOALLOC_SCRATCH_BYTES = 32 << 20   # CSA_NOALLOC_SCRATCH_BYTES
 
 ENTRY_POINTS = ("csa_compress", "hca_compress", "csa_index_topk_workspace_size", "csa_index_topk",
+                "csa_index_topk_noalloc",
                 "csa_index_scores", "csa_topk_workspace_size", "csa_topk", "csa_sparse_mqa_workspace_size", "csa_sparse_mqa",
                 "hca_dense_mqa", "csa_sparse_mqa_sink", "hca_dense_mqa_sink", "csa_sparse_mqa_swa", "csa_rope", "csa_compress_step", "csa_status_string",
                 "csa_version")
@@ -42,6 +44,7 @@ def _load():
         "hca_compress": ([P, P, P, I64, I64, I, I, I, P, I, P], I),
         "csa_index_topk_workspace_size": ([I64, I64, I64, I, I], SZ),
         "csa_index_topk": ([P, P, P, I64, I64, I64, I64, I, I, I, I, I, P, P, P, SZ, P], I),
+        "csa_index_topk_noalloc": ([P, P, P, I64, I64, I64, I64, I, I, I, I, I, P, P, P], I),
         "csa_index_scores": ([P, P, P, I64, I64, I64, I64, I, I, I, I, P, P], I),
         "csa_topk_workspace_size": ([I64, I64, I64, I], SZ),
         "csa_topk": ([P, I64, I64, I64, I64, I64, I, I, P, P, P, SZ, P], I),
@@ -139,6 +142,13 @@ def _dev(*ts):
     return dev
 
 
+def _check_out(t, shape, dtype, what):
+    """A caller-supplied buffer must have exactly the shape and dtype the call writes (the C
+    ABI sees only its address)."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{what}: expected {dtype} {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+
+
 def _stream(dev) -> int:
     return torch.cuda.current_stream(dev).cuda_stream
 
@@ -205,6 +215,30 @@ def csa_index_topk(qI, w, kI, q_pos0: int, m: int, k: int, idx=None, sel_scores=
     _check("csa_index_topk", lib.csa_index_topk(_p(qt), _p(w), _p(kt), batch, T, q_pos0, N, H_I, c_I, m, k, qk_dt,
                                                 _p(idx), _p(sel_scores), _p(workspace), workspace.numel(),
                                                 _stream(dev)))
+    return idx, sel_scores
+
+
+def csa_index_topk_noalloc(qI, w, kI, q_pos0: int, m: int, k: int, idx=None, sel_scores=None,
+                           want_scores: bool = True):
+    """csa_index_topk without a workspace: the library's fixed per-GPU scratch serves instead
+    (for callers that cannot allocate; calls on one GPU must not overlap).  Runs on the
+    tensors' device, which must be torch's current device."""
+    qt, kt, qs, ks, qk_dt = _qk(qI, kI)
+    dev = _dev(qt, w, kt, idx, sel_scores)
+    if dev.index != torch.cuda.current_device():
+        raise ValueError("csa_index_topk_noalloc runs on the current device: call torch.cuda.set_device first")
+    batch, T, H_I, c_I = qs
+    N = ks[1]
+    assert ks == (batch, N, c_I) and w.shape == (batch, T, H_I) and w.dtype == torch.float32
+    if idx is None:
+        idx = torch.empty((batch, T, k), dtype=torch.int32, device=dev)
+    if sel_scores is None and want_scores:
+        sel_scores = torch.empty((batch, T, k), dtype=torch.float32, device=dev)
+    _check_out(idx, (batch, T, k), torch.int32, "idx")
+    if sel_scores is not None:
+        _check_out(sel_scores, (batch, T, k), torch.float32, "sel_scores")
+    _check("csa_index_topk_noalloc", lib.csa_index_topk_noalloc(_p(qt), _p(w), _p(kt), batch, T, q_pos0, N, H_I, c_I,
+                                                                m, k, qk_dt, _p(idx), _p(sel_scores), _stream(dev)))
     return idx, sel_scores
 
 

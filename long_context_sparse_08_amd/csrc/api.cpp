@@ -3,8 +3,16 @@
 // Every check runs before the first HIP call, so an invalid call never touches the device.
 #include <math.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "../../include/csa.h"
 #include "launch.h"
+
+// Scratch of csa_index_topk_noalloc: one copy per GPU the library runs on, kept until the
+// process ends.  On the host this name is only a stand-in symbol, never a device address:
+// host code uses the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[CSA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -66,6 +74,8 @@ const char* csa_status_string(int status) {
         case CSA_ERR_UNSUPPORTED: return "CSA_ERR_UNSUPPORTED: dtype or shape outside the implemented limits";
         case CSA_ERR_WORKSPACE: return "CSA_ERR_WORKSPACE: workspace missing or too small";
         case CSA_ERR_HIP: return "CSA_ERR_HIP: the HIP runtime reported a launch error";
+        case CSA_ERR_TOO_LARGE:
+            return "CSA_ERR_TOO_LARGE: the call needs more scratch than the allocation-free entry point holds";
         default: return "unknown csa_status";
     }
 }
@@ -137,9 +147,10 @@ size_t csa_index_topk_workspace_size(int64_t batch, int64_t T, int64_t N, int H_
            group_region(rows, T, N, k) + kWsAlign;
 }
 
-int csa_index_topk(const void* qI, const float* w, const void* kI, int64_t batch, int64_t T, int64_t q_pos0, int64_t N,
-                   int H_I, int c_I, int m, int k, csa_dtype qk_t, int32_t* idx, float* sel_scores, void* workspace,
-                   size_t ws_bytes, csa_stream_t stream) {
+// The argument checks of csa_index_topk other than the workspace's.
+int check_index_topk(const void* qI, const float* w, const void* kI, int64_t batch, int64_t T, int64_t q_pos0,
+                     int64_t N, int H_I, int c_I, int m, int k, csa_dtype qk_t, const int32_t* idx,
+                     const float* sel_scores) {
     int rc = check_indexer(qI, w, kI, batch, T, q_pos0, N, H_I, c_I, m, qk_t);
     if (rc != CSA_OK) return rc;
     if (k < 1) return CSA_ERR_INVALID_ARG;
@@ -147,6 +158,14 @@ int csa_index_topk(const void* qI, const float* w, const void* kI, int64_t batch
     if (batch == 0 || T == 0) return CSA_OK;
     if (!idx) return CSA_ERR_INVALID_ARG;
     if (sel_scores && !aligned16(sel_scores)) return CSA_ERR_INVALID_ARG;
+    return CSA_OK;
+}
+
+int csa_index_topk(const void* qI, const float* w, const void* kI, int64_t batch, int64_t T, int64_t q_pos0, int64_t N,
+                   int H_I, int c_I, int m, int k, csa_dtype qk_t, int32_t* idx, float* sel_scores, void* workspace,
+                   size_t ws_bytes, csa_stream_t stream) {
+    int rc = check_index_topk(qI, w, kI, batch, T, q_pos0, N, H_I, c_I, m, k, qk_t, idx, sel_scores);
+    if (rc != CSA_OK || batch == 0 || T == 0) return rc;
     const size_t need = csa_index_topk_workspace_size(batch, T, N, H_I, k);
     if (!workspace || ws_bytes < need || !aligned16(workspace)) return CSA_ERR_WORKSPACE;
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -177,6 +196,49 @@ int csa_index_topk(const void* qI, const float* w, const void* kI, int64_t batch
     return finish(csa::launch_topk(scores, ld, batch, T, q_pos0, N, m, k, idx, sel_scores,
                                    n_chunk_mm > 0 ? chunk_mm : nullptr, n_chunk_mm, gmax, G, gld,
                                    zero_words > 0 ? extra : nullptr, st));
+}
+
+// ---- allocation-free variant: the workspace is this device's copy of `scratch`
+namespace {
+constexpr int kMaxDevices = 256;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's copy of `scratch`, looked up once per device.
+int scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return CSA_ERR_HIP;
+    }
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+                (void)hipGetLastError();
+                return CSA_ERR_HIP;
+            }
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return CSA_OK;
+}
+}  // namespace
+
+int csa_index_topk_noalloc(const void* qI, const float* w, const void* kI, int64_t batch, int64_t T, int64_t q_pos0,
+                           int64_t N, int H_I, int c_I, int m, int k, csa_dtype qk_t, int32_t* idx, float* sel_scores,
+                           csa_stream_t stream) {
+    int rc = check_index_topk(qI, w, kI, batch, T, q_pos0, N, H_I, c_I, m, k, qk_t, idx, sel_scores);
+    if (rc != CSA_OK || batch == 0 || T == 0) return rc;
+    if (csa_index_topk_workspace_size(batch, T, N, H_I, k) > CSA_NOALLOC_SCRATCH_BYTES) return CSA_ERR_TOO_LARGE;
+    void* ws = nullptr;
+    rc = scratch_address(&ws);
+    if (rc != CSA_OK) return rc;
+    return csa_index_topk(qI, w, kI, batch, T, q_pos0, N, H_I, c_I, m, k, qk_t, idx, sel_scores, ws,
+                          CSA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int csa_index_scores(const void* qI, const float* w, const void* kI, int64_t batch, int64_t T, int64_t q_pos0, int64_t N,

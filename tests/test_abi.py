@@ -10,7 +10,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "csa.h")
 
-OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+OK, INVALID, UNSUPPORTED, WORKSPACE, TOO_LARGE = 0, -1, -2, -3, -5
 A = 0x10000      # a 16-byte aligned fake address, never dereferenced
 MIS = 0x10004    # misaligned fake address
 
@@ -43,7 +43,8 @@ def test_library_exports_every_declared_symbol(L):
 
 def test_version_and_status_strings(L):
     assert L.csa_version() == 100
-    for s, tag in ((0, "CSA_OK"), (-1, "INVALID"), (-2, "UNSUPPORTED"), (-3, "WORKSPACE"), (-4, "HIP")):
+    for s, tag in ((0, "CSA_OK"), (-1, "INVALID"), (-2, "UNSUPPORTED"), (-3, "WORKSPACE"), (-4, "HIP"),
+                   (-5, "TOO_LARGE")):
         assert tag in L.csa_status_string(s).decode()
     assert "unknown" in L.csa_status_string(7).decode()
 
@@ -130,6 +131,32 @@ def test_index_topk_rejects_bad_arguments(L):
     assert call(ws=None) == WORKSPACE
     assert call(wsb=need - 1) == WORKSPACE
     assert call(batch=0, wsb=L.csa_index_topk_workspace_size(0, 8, 64, 2, 8)) == OK
+
+
+def test_index_topk_noalloc_checks_before_any_hip_call(L):
+    # the allocation-free variant runs the same argument checks, then refuses calls whose
+    # workspace would exceed its fixed scratch, all before its first HIP call (no call here
+    # reaches the device: each one fails a host-side check)
+    f = L.csa_index_topk_noalloc
+    good = dict(qI=A, w=A, kI=A, batch=1, T=8, q_pos0=0, N=64, H_I=2, c_I=32, m=4, k=8, t=0, idx=A, sel=A)
+
+    def call(**over):
+        a = dict(good, **over)
+        return f(a["qI"], a["w"], a["kI"], a["batch"], a["T"], a["q_pos0"], a["N"], a["H_I"], a["c_I"], a["m"],
+                 a["k"], a["t"], a["idx"], a["sel"], None)
+
+    assert call(qI=None) == INVALID
+    assert call(idx=None) == INVALID
+    assert call(sel=MIS) == INVALID
+    assert call(k=0) == INVALID
+    assert call(k=4096) == UNSUPPORTED
+    assert call(t=3) == UNSUPPORTED
+    assert call(batch=0) == OK
+    # an 8K-token prefill's score rows alone are 64 MiB
+    assert call(T=8192, N=2048, H_I=64, c_I=128, k=512) == TOO_LARGE
+    assert L.csa_index_topk_workspace_size(1, 8192, 2048, 64, 512) > (32 << 20)
+    assert L.csa_index_topk_workspace_size(32, 1, 32768, 64, 1024) <= (32 << 20)
+    assert L.csa_index_topk_workspace_size(8, 1, 262144, 64, 1024) <= (32 << 20)
 
 
 def test_mqa_rejects_bad_arguments(L):
