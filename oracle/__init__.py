@@ -130,7 +130,8 @@ def rope(x, pos0: int, pos_step: int = 1, d: int = 64, base: float = 10000.0, in
 
 
 def round_to(x: np.ndarray, dtype: int) -> np.ndarray:
-    """Round float64 values to the nearest value of storage type `dtype` (f32 or bf16)."""
+    """Round float64 values to the nearest value of storage type `dtype` (f32, bf16 or fp8 e4m3fn,
+    nearest-even, fp8 saturating at +-448)."""
     out = np.array(x, dtype=np.float64, copy=True, order="C")
     if lib().oracle_round(_p(out), dtype, out.size) != 0:
         raise ValueError(f"bad dtype {dtype}")
@@ -236,7 +237,22 @@ def sparse_mqa(q, kv, idx, scale: float, dtype: int = F32, sink=None, window=Non
     return out
 
 
-def hca_dense_mqa(q, kv, m_prime: int, scale: float, q_pos0: int = 0, dtype: int = F32, qpos=None, sink=None):
+def hca_dense_mqa(q, kv, m_prime: int, scale: float, q_pos0: int = 0, dtype: int = F32, qpos=None, sink=None,
+                  window=None):
+    """Dense causal MQA over the HCA entries each query may see (m'(s+1)-1 <= p).
+    window: (win_kv [batch, W, c], win_pos0, n_win) — the sliding-window branch, which the notes
+    page §1.3 gives to HCA as to CSA: written as the plain union, i.e. the query's visible
+    entries listed explicitly and handed, with the window, to the sparse oracle."""
+    if window is not None:
+        assert qpos is None
+        wkv, wp0, n_win = window
+        batch, T = q.shape[0], q.shape[1]
+        N = kv.shape[1]
+        idx = np.full((batch, T, max(N, 1)), -1, np.int32)
+        for t in range(T):
+            nv = min(N, (q_pos0 + t + 1) // m_prime)
+            idx[:, t, :nv] = np.arange(nv, dtype=np.int32)
+        return sparse_mqa(q, kv, idx, scale, dtype=dtype, sink=sink, window=(wkv, wp0, q_pos0, n_win))
     q, kv = _d(q, dtype), _d(kv, dtype)
     batch, T, H, c = q.shape
     N = kv.shape[1]

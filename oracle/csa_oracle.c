@@ -172,16 +172,30 @@ static double round_bf16(double x) {
     return nearbyint(x / q) * q;  /* default rounding mode: to nearest, ties to even */
 }
 
+/* Round a finite double to the nearest OCP e4m3fn value, ties to even, saturating at +-448:
+ * the grid's quantum at |x| is 2^(floor(log2|x|) - 3) for normal values (exponent >= -6) and
+ * 2^-9 for subnormals (R12: unit scale). */
+static double round_e4m3(double x) {
+    int e;
+    double a = fabs(x), q;
+    if (a == 0.0 || !isfinite(x)) return x;
+    if (a > 448.0) a = 448.0;
+    frexp(a, &e);                 /* a = f * 2^e, 0.5 <= f < 1: floor(log2 a) = e - 1 */
+    q = ldexp(1.0, ((e - 1 > -6) ? e - 1 : -6) - 3);
+    return copysign(nearbyint(a / q) * q, x);
+}
+
 static double round_to(double x, int dtype) {
     if (dtype == OR_F32) return (double)(float)x;
     if (dtype == OR_BF16) return round_bf16(x);
+    if (dtype == OR_FP8_E4M3) return round_e4m3(x);
     return x;                     /* -1: keep double */
 }
 
 /* Round `count` doubles in place to storage type `dtype` (values stay doubles). */
 int oracle_round(double* x, int dtype, int64_t count) {
     int64_t i;
-    if (dtype != OR_F32 && dtype != OR_BF16) return -1;
+    if (dtype != OR_F32 && dtype != OR_BF16 && dtype != OR_FP8_E4M3) return -1;
     for (i = 0; i < count; ++i) x[i] = round_to(x[i], dtype);
     return 0;
 }

@@ -30,6 +30,23 @@ def test_decode_bf16_matches_torch(orc):
     assert np.array_equal(got[ok], ref[ok]) and np.isnan(got[~ok]).all()
 
 
+def test_round_to_e4m3_matches_torch_and_saturates(orc):
+    """Rounding to fp8 e4m3fn (the storage of fp8 compressed indexer keys): every code's value,
+    every midpoint between neighbouring codes (ties go to the even code), random values and
+    subnormals round as torch's float8_e4m3fn cast does inside the format's range; beyond
+    +-448 the oracle saturates (448 is the largest finite e4m3fn value, +-464 the overflow
+    midpoint), checked by hand."""
+    vals = torch.arange(0, 127, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()   # +0 .. 448
+    mids = (vals[:-1] + vals[1:]) / 2
+    r = np.random.RandomState(5)
+    x = np.concatenate([vals, mids, r.uniform(-448, 448, 5000), r.uniform(-0.02, 0.02, 2000), r.randn(2000)])
+    x = np.concatenate([x, -x])
+    ref = torch.from_numpy(x).float().to(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(orc.round_to(x.astype(np.float32).astype(np.float64), 2), ref)
+    got = orc.round_to(np.array([448.0, 449.0, 463.9, 500.0, 1e6, -500.0, -1e9, 2.0 ** -10, 3 * 2.0 ** -11]), 2)
+    assert np.array_equal(got, [448.0, 448.0, 448.0, 448.0, 448.0, -448.0, -448.0, 0.0, 2.0 ** -9])
+
+
 def test_decode_e4m3_matches_torch_all_codes(orc):
     codes = np.arange(256, dtype=np.uint8)
     ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
@@ -558,3 +575,35 @@ def test_sliding_window_branch(orc):
         for h in range(H):
             w = softmax(0.4 * rows @ q[0, t, h])
             assert np.allclose(both[0, t, h], w @ rows, rtol=1e-12, atol=1e-14)
+
+
+def test_dense_mqa_with_window_equals_masked_attention_over_both(orc):
+    """HCA dense attention plus the sliding-window branch (the notes page §1.3 gives the window
+    to HCA too): brute force over the concatenation [HCA entries, raw rows] with an explicit
+    mask (entry s iff m'(s+1)-1 <= p; raw row j iff its position lies in [p - n_win + 1, p]) and
+    scipy's softmax, written here independently of the oracle.  Covers queries that see no
+    entry (window only), window rows whose tokens an entry also covers, and a sink."""
+    r = np.random.RandomState(21)
+    B, T, H, c, mp, N, W, n_win = 2, 7, 3, 8, 4, 6, 12, 5
+    q0, wp0 = 2, 1                     # queries at positions 2..8; raw rows at positions 1..12
+    q, kv, wkv = r.randn(B, T, H, c), r.randn(B, N, c), r.randn(B, W, c)
+    sink = r.randn(H)
+    for sk in (None, sink):
+        out = orc.hca_dense_mqa(q, kv, mp, 0.3, q_pos0=q0, sink=sk, window=(wkv, wp0, n_win))
+        for b in range(B):
+            for t in range(T):
+                p = q0 + t
+                rows = [kv[b, s] for s in range(N) if mp * (s + 1) - 1 <= p]
+                rows += [wkv[b, j] for j in range(W) if p - n_win + 1 <= wp0 + j <= p]
+                rows = np.stack(rows)
+                for h in range(H):
+                    z = 0.3 * rows @ q[b, t, h]
+                    if sk is None:
+                        wgt = softmax(z)
+                    else:
+                        e = np.exp(z - z.max())
+                        wgt = e / (e.sum() + np.exp(sk[h] - z.max()))
+                    assert np.allclose(out[b, t, h], wgt @ rows, rtol=1e-12, atol=1e-13)
+    # n_win = 0 is plain dense attention
+    assert np.allclose(orc.hca_dense_mqa(q, kv, mp, 0.3, q_pos0=q0, window=(wkv, wp0, 0)),
+                       orc.hca_dense_mqa(q, kv, mp, 0.3, q_pos0=q0), rtol=1e-13, atol=1e-14)
