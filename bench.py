@@ -4,9 +4,11 @@
 
 Default workload: CSA decode at a 131,072-token context (batch 32, 32,768 compressed entries
 per sequence, c = 512, 128 query heads, fp8 e4m3 indexer 64 x 128, top-k 1024).  One step =
-index + top-k + sparse MQA for one new token per sequence (that token opens an incomplete
-block, so no entry is compressed in the step).  The step is captured once in a HIP graph and
-replayed K times between two synchronisations; inputs are resident in HBM before timing.
+index + top-k + sparse MQA for one new token per sequence; every m-th step (m = 4) the new
+token completes a block, and that step first compresses the block's KV entry (bf16) and
+index-key entry (fp8) from the decode state into the caches.  A run of m consecutive steps is
+captured once in a HIP graph and replayed between two synchronisations (K is rounded up to a
+multiple of m); inputs are resident in HBM before timing.
 
 Prints one JSON line: whole-step throughput (query tokens/s), the roofline of the dominant
 kernel (timed with HIP events on the stream it runs on), and the CPU oracle's throughput on a
@@ -27,6 +29,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "CSA query tokens/s (compress+index+top-k+MQA) at 128K ctx; % of roofline"
+# the compressor-only workload counts raw tokens compressed, not query tokens
+METRIC_COMPRESS = "CSA raw tokens compressed/s (csa_compress over a 1M-token sequence); % of HBM roofline"
 HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
 MFMA_PEAK = {"bf16": 2.5e15, "fp8": 5.0e15}
 # MXFP4: a 4-bit value plus a 1-byte scale per 32; mixed KV rows: 448 fp8 + 64 bf16 per 512
@@ -50,6 +54,13 @@ def stage_work(cfg):
         st["compress"] = dict(bytes=4 * B * n * c * e + B * (n // cfg.m) * c * e + 2 * cfg.m * c * 4, flops=0,
                               bound="hbm")
         return st
+    if cfg.kind == "csa_decode":
+        # one decode-step compression (both caches, every sequence): the a-streams' current
+        # block and the b-streams' previous block (m tokens each), the biases, one entry out
+        m, cI = cfg.m, cfg.c_I
+        e_kI = DT_BYTES[cfg.qk_dt]
+        st["compress_step"] = dict(bytes=4 * B * m * (c + cI) * e + B * (c * e + cI * e_kI) + 2 * m * (c + cI) * 4,
+                                   flops=0, bound="hbm")
     if cfg.kind in ("csa_decode", "csa_prefill"):
         T, N, HI, cI, k = cfg.T, cfg.N, cfg.H_I, cfg.c_I, cfg.k
         eq = DT_BYTES[cfg.qk_dt]
@@ -92,6 +103,16 @@ def peak_for(cfg, stage, bound):
 
 
 # ---------------------------------------------------------------------------- CPU baseline
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, host, budget_s=10.0):
     """The oracle on a bounded sample of the workload, repeated until about budget_s seconds of
     CPU work have been timed."""
@@ -105,7 +126,7 @@ def cpu_baseline(cfg, host, budget_s=10.0):
     import oracle
 
     return {"value": tokens / elapsed, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{sample}; {reps} repetitions", "seconds": round(elapsed, 3)}
+            "sample": f"{sample}; {reps} repetitions", "seconds": round(elapsed, 3), "cpu_model": cpu_model()}
 
 
 def _cpu_sample(cfg, host):
@@ -125,8 +146,15 @@ def _cpu_sample(cfg, host):
         sc = oracle.index_scores(sub["qI"], sub["w"], sub["kI"], cfg.m, q_pos0=cfg.q_pos0, qk_dtype=cfg.qk_dt)
         idx, _ = oracle.topk(sc, cfg.m, cfg.k, q_pos0=cfg.q_pos0)
         oracle.sparse_mqa(sub["q"], sub["kv"], idx, cfg.scale, dtype=cfg.dt)
+        what = "index + top-k + MQA"
+        if "Ca" in host and "ICa" in host:   # one block's entries per sequence (every m steps)
+            oracle.csa_compress(host["Ca"], host["Cb"], host["Za"], host["Zb"], host["Ba"], host["Bb"], cfg.m,
+                                in_dtype=cfg.dt, out_dtype=cfg.dt)
+            oracle.csa_compress(host["ICa"], host["ICb"], host["IZa"], host["IZb"], host["IBa"], host["IBb"], cfg.m,
+                                in_dtype=cfg.dt, out_dtype=cfg.qk_dt)
+            what = "index + top-k + MQA, plus one step's compression of the KV and index-key entries"
         tokens = nseq * cfg.T
-        sample = f"all {nseq} sequences x {cfg.T} token (index + top-k + MQA, float64)"
+        sample = f"all {nseq} sequences x {cfg.T} token ({what}, float64)"
     elif cfg.kind == "csa_compress":
         nt = 1 << 16
         oracle.csa_compress(*(host[k][:, :nt] for k in ("Ca", "Cb", "Za", "Zb")), host["Ba"], host["Bb"], cfg.m,
@@ -216,40 +244,54 @@ def main():
     else:
         pipe = HcaChunk(dev, cfg.m_prime, cfg.q_pos0)
 
-    for _ in range(args.warmup):
-        pipe.run()
-    torch.cuda.synchronize()
+    # the timed unit: one step, or (decode with a state) a run of m steps whose last one
+    # compresses the entries of the block its token completes
+    with_compress = cfg.kind == "csa_decode" and pipe.can_compress()
+    unit_fn = pipe.run_steps if with_compress else pipe.run
+    per_unit = cfg.m if with_compress else 1
 
-    graph = None
-    if not args.no_graph:
+    def capture(fn):
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
-            pipe.run()
+            fn()
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            pipe.run()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
         for _ in range(3):
-            graph.replay()
+            g.replay()
         torch.cuda.synchronize()
+        return g
 
-    # ---- timed region: K whole steps
-    log(f"[bench] timing {args.steps} steps ({'graph' if graph else 'eager'})")
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    def timed(fn, units):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(units):
+            fn()
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end)
+
+    for _ in range(max(1, args.warmup // per_unit)):
+        unit_fn()
     torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
-        if graph is not None:
-            graph.replay()
-        else:
-            pipe.run()
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
+    graph = None if args.no_graph else capture(unit_fn)
+
+    # ---- timed region: K whole steps (K rounded up to whole units)
+    units = (args.steps + per_unit - 1) // per_unit
+    steps = units * per_unit
+    log(f"[bench] timing {steps} steps ({'graph' if graph else 'eager'})")
+    ms = timed(graph.replay if graph is not None else unit_fn, units) / steps
     tokens = cfg.batch * cfg.T
     value = tokens / (ms * 1e-3)
+    # the same steps without the compression, for comparison
+    ms_plain = None
+    if with_compress:
+        g1 = None if args.no_graph else capture(pipe.run)
+        ms_plain = timed(g1.replay if g1 is not None else pipe.run, steps) / steps
 
     # ---- per-stage time: back-to-back launches of each stage's library call, HIP events on the
     # stream the launches go to (torch's current stream).  Each stage is one of the step's own
@@ -265,8 +307,9 @@ def main():
                            ["index_scores_mfma"], "index")
         stages["select"] = (pipe.select, ["index_scores_mfma", "topk"], None)
         # (decode launches have at most one workgroup per CU: the warp-specialised kernel)
-        stages["attend"] = (pipe.attend, ["mqa_sparse_ws"] + (["mqa_combine"] if split else []),
-                            None if split else "mqa")
+        stages["attend"] = (pipe.attend, ["mqa_sparse_ws"] + (["mqa_combine"] if split else []), "mqa")
+        if with_compress:   # the two decode-step compressions (KV and index-key entries)
+            stages["compress_step"] = (pipe.compress, ["compress_kernel", "compress_kernel"], "compress_step")
     elif cfg.kind == "csa_compress":
         stages["compress"] = (pipe.run, ["compress_kernel"], "compress")
     elif cfg.kind == "csa_prefill":
@@ -284,17 +327,33 @@ def main():
         stages["attend"] = (pipe.attend, ["mqa_sparse_mfma"], "mqa")
     work = stage_work(cfg)
     stage_ms = {}
+    # stages whose kernels are too short to time by launches from Python (the host would be
+    # the limit): timed as a captured graph of back-to-back calls
+    graph_stages = {"compress_step"}
     for name, (fn, _, _) in stages.items():
         fn()
         torch.cuda.synchronize()
         n_rep = max(3, reps if cfg.kind != "hca_chunk" else min(reps, 20))
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(n_rep):
-            fn()
-        b.record()
-        torch.cuda.synchronize()
-        stage_ms[name] = a.elapsed_time(b) / n_rep
+        if name in graph_stages and not args.no_graph:
+            def many(fn=fn):
+                for _ in range(20):
+                    fn()
+            g = capture(many)
+            stage_ms[name] = timed(g.replay, max(1, n_rep // 20)) / (20 * max(1, n_rep // 20))
+            continue
+        stage_ms[name] = timed(fn, n_rep) / n_rep
+    # every stage's fraction of its own roofline (a stage of several kernels over its call
+    # time; top-k alone as select - index)
+    def frac(wk, t_ms):
+        wv = work[wk]
+        if wv["bound"] == "hbm":
+            return wv["bytes"] / (t_ms * 1e-3) / HBM_PEAK
+        return wv["flops"] / (t_ms * 1e-3) / peak_for(cfg, wk, "mfma")[0]
+
+    stage_frac = {n: round(frac(wk, stage_ms[n]), 4) for n, (_, _, wk) in stages.items() if wk is not None}
+    if "select" in stage_ms and "index" in stage_ms and stage_ms["select"] > stage_ms["index"]:
+        stage_ms["topk (select - index)"] = stage_ms["select"] - stage_ms["index"]
+        stage_frac["topk (select - index)"] = round(frac("topk", stage_ms["topk (select - index)"]), 4)
     # roofline of the dominant kernel: the longest stage that is a single kernel
     single = [n for n, (_, ks, wk) in stages.items() if len(ks) == 1 and wk is not None]
     dom = max(single, key=stage_ms.get)
@@ -317,14 +376,16 @@ def main():
     roof["ms_per_launch"] = round(stage_ms[dom], 5)
     roof["algorithmic_bytes"] = int(w["bytes"])
     roof["algorithmic_flops"] = int(w["flops"])
-    ideal = sum(max(v["bytes"] / HBM_PEAK, v["flops"] / peak_for(cfg, k, "mfma")[0]) for k, v in work.items())
+    # ideal step time: every stage at its roofline (the decode-step compression once every m steps)
+    ideal = sum(max(v["bytes"] / HBM_PEAK, v["flops"] / peak_for(cfg, k, "mfma")[0]) / (cfg.m if k == "compress_step" else 1)
+                for k, v in work.items() if k != "compress_step" or with_compress)
 
     result = {
-        "metric": METRIC,
+        "metric": METRIC_COMPRESS if cfg.kind == "csa_compress" else METRIC,
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
@@ -339,9 +400,14 @@ def main():
                    "graph": graph is not None},
         "roofline": roof,
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        "stage_roofline_frac": stage_frac,
         "stage_kernels": {k: v[1] for k, v in stages.items()},
         "step_roofline_frac": round(ideal / (ms * 1e-3), 4),
     }
+    if with_compress:
+        # the step above includes one compression every m steps; the same steps without it
+        result["ms_per_step_without_compress"] = round(ms_plain, 5)
+        result["compress_ms_per_step_amortised"] = round(ms - ms_plain, 5)
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(cfg, host)

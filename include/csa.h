@@ -85,8 +85,9 @@ typedef void* csa_stream_t;
  * window; its weights come from window 0 of stream a alone.
  *   Ca, Cb, Za, Zb : [batch, n, c], dtype in_t (CSA_F32 or CSA_BF16)
  *   Ba, Bb         : [m, c] float32 learned position biases
- *   out            : [batch, floor(n/m), c], dtype out_t (CSA_F32 or CSA_BF16; bf16 is
- *                    rounded to nearest even from the fp32 result)
+ *   out            : [batch, floor(n/m), c], dtype out_t (CSA_F32, CSA_BF16 or CSA_FP8_E4M3;
+ *                    bf16 and fp8 are rounded to nearest even from the fp32 result, fp8
+ *                    saturating at +-448: e.g. fp8 indexer keys)
  * Used for both the KV entries (width c) and the indexer keys (width c_I).
  * Limits: 1 <= m <= CSA_MAX_RATIO, c % 8 == 0, c <= CSA_MAX_WIDTH.  n < m is valid and
  * writes nothing.
@@ -282,6 +283,36 @@ int csa_sparse_mqa_swa(const void* q, const void* kv, const int32_t* idx, int64_
 int csa_compress_step(const void* Ca, const void* Cb, const void* Za, const void* Zb, const float* Ba,
                       const float* Bb, int64_t batch, int64_t block, int m, int c, csa_dtype in_t, void* cache,
                       int64_t cache_rows, csa_dtype out_t, csa_stream_t stream);
+
+/*
+ * hca_dense_mqa_swa — hca_dense_mqa (with optional sink) plus the sliding-window branch ([N]
+ * §1.3: the window of the most recent n_win uncompressed tokens is given to HCA as well as to
+ * CSA; [M] §2.3.3 item 3): the query at absolute position p = q_pos0 + t attends, in one
+ * softmax, to every HCA entry it may see (m'(s+1)-1 <= p) and to the raw rows win_kv[j] whose
+ * position win_pos0 + j lies in [p - n_win + 1, p].  A raw row whose tokens an entry also
+ * covers is still attended to as its own key (the two branches are a plain union).
+ *   win_kv : [batch, W, c] raw KV rows (dtype t), rows at absolute positions win_pos0 ..
+ *            win_pos0 + W - 1.  May be NULL when n_win == 0 or W == 0.
+ * Limits: as hca_dense_mqa; 0 <= n_win <= 1024; N + W < 2^31.
+ */
+int hca_dense_mqa_swa(const void* q, const void* kv, int64_t batch, int64_t T, int64_t q_pos0, int64_t N, int H,
+                      int c, int m_prime, float scale, const float* sink, const void* win_kv, int64_t W,
+                      int64_t win_pos0, int n_win, csa_dtype t, void* out, csa_stream_t stream);
+
+/*
+ * hca_compress_step — HCA compression as a decode step ([N] §1.2: m' = 128, no overlap; [M]
+ * "state cache": the raw tokens of a block that is not complete yet stay in a per-request
+ * state until the block fills): once block `block` (tokens m'*block .. m'*block + m' - 1) is
+ * complete, computes HCA entry `block` exactly as hca_compress would for the whole sequence and
+ * writes it to row `block` of the caller's cache.
+ *   C, Z  : the state, [batch, m', c] each: the raw tokens of block `block`, in token order
+ *   B     : [m', c] fp32 position biases
+ *   cache : [batch, cache_rows, c] dtype out_t; only row `block` of each sequence is written.
+ *           0 <= block < cache_rows.
+ * Dtypes and limits as hca_compress.
+ */
+int hca_compress_step(const void* C, const void* Z, const float* B, int64_t batch, int64_t block, int m_prime, int c,
+                      csa_dtype in_t, void* cache, int64_t cache_rows, csa_dtype out_t, csa_stream_t stream);
 
 /* Human-readable name of a csa_status value (static storage). */
 const char* csa_status_string(int status);

@@ -24,7 +24,7 @@ NOALLOC_SCRATCH_BYTES = 32 << 20   # CSA_NOALLOC_SCRATCH_BYTES
 ENTRY_POINTS = ("csa_compress", "hca_compress", "csa_index_topk_workspace_size", "csa_index_topk",
                 "csa_index_topk_noalloc",
                 "csa_index_scores", "csa_topk_workspace_size", "csa_topk", "csa_sparse_mqa_workspace_size", "csa_sparse_mqa",
-                "hca_dense_mqa", "csa_sparse_mqa_sink", "hca_dense_mqa_sink", "csa_sparse_mqa_swa", "csa_rope", "csa_compress_step", "csa_status_string",
+                "hca_dense_mqa", "csa_sparse_mqa_sink", "hca_dense_mqa_sink", "csa_sparse_mqa_swa", "csa_rope", "csa_compress_step", "hca_dense_mqa_swa", "hca_compress_step", "csa_status_string",
                 "csa_version")
 
 
@@ -56,6 +56,8 @@ def _load():
         "csa_compress_step": ([P, P, P, P, P, P, I64, I64, I, I, I, P, I64, I, P], I),
         "csa_sparse_mqa_swa": ([P, P, P, I64, I64, I64, I, I, I, F, P, P, I64, I64, I64, I, I, P, P, SZ, P], I),
         "hca_dense_mqa_sink": ([P, P, I64, I64, I64, I64, I, I, I, F, P, I, P, P], I),
+        "hca_dense_mqa_swa": ([P, P, I64, I64, I64, I64, I, I, I, F, P, P, I64, I64, I, I, P, P], I),
+        "hca_compress_step": ([P, P, P, I64, I64, I, I, I, P, I64, I, P], I),
         "csa_status_string": ([I], ctypes.c_char_p),
         "csa_version": ([], I),
     }
@@ -350,14 +352,36 @@ def csa_rope(x, pos0: int, pos_step: int = 1, d: int = 64, base: float = 10000.0
     return x
 
 
-def hca_dense_mqa(q, kv, q_pos0: int, m_prime: int, scale: float, out=None, sink=None):
+def hca_dense_mqa(q, kv, q_pos0: int, m_prime: int, scale: float, out=None, sink=None, window=None):
+    """q [batch, T, H, c], kv [batch, N, c] HCA entries -> out [batch, T, H, c] (dense causal MQA).
+    sink: optional fp32 [H]; window: optional (win_kv [batch, W, c], win_pos0, n_win), the
+    sliding-window branch over the raw rows at positions p - n_win + 1 .. p."""
     dev = _dev(q, kv, out)
     batch, T, H, c = q.shape
     N = kv.shape[1]
     assert kv.shape == (batch, N, c) and kv.dtype == q.dtype
     if out is None:
         out = torch.empty_like(q)
+    _check_out(out, (batch, T, H, c), q.dtype, "out")
+    wkv, W, wp0, n_win = None, 0, 0, 0
+    if window is not None:
+        wkv, wp0, n_win = window
+        assert wkv.dtype == q.dtype and wkv.shape[0] == batch and wkv.shape[2] == c
+        _dev(q, wkv)
+        W = wkv.shape[1]
     sk = _sink(sink, H, dev)
-    _check("hca_dense_mqa", lib.hca_dense_mqa_sink(_p(q), _p(kv), batch, T, q_pos0, N, H, c, m_prime, float(scale),
-                                                   _p(sk), _dt(q), _p(out), _stream(dev)))
+    _check("hca_dense_mqa", lib.hca_dense_mqa_swa(_p(q), _p(kv), batch, T, q_pos0, N, H, c, m_prime, float(scale),
+                                                  _p(sk), _p(wkv), W, wp0, n_win, _dt(q), _p(out), _stream(dev)))
     return out
+
+
+def hca_compress_step(C, Z, B, block: int, cache):
+    """Decode-step HCA compression: the state streams [batch, m', c] (the raw tokens of block
+    `block`) -> row `block` of cache [batch, rows, c], in place."""
+    dev = _dev(C, Z, B, cache)
+    batch, mp, c = C.shape
+    assert Z.shape == C.shape and Z.dtype == C.dtype and B.dtype == torch.float32 and tuple(B.shape) == (mp, c)
+    assert cache.dim() == 3 and cache.shape[0] == batch and cache.shape[2] == c
+    _check("hca_compress_step", lib.hca_compress_step(_p(C), _p(Z), _p(B), batch, block, mp, c, _dt(C), _p(cache),
+                                                      cache.shape[1], _dt(cache), _stream(dev)))
+    return cache

@@ -24,6 +24,9 @@ bool width_ok(int c) { return c > 0 && c % 8 == 0 && c <= CSA_MAX_WIDTH; }
 
 bool io_dtype(csa_dtype t) { return t == CSA_F32 || t == CSA_BF16; }
 
+// compressed entries may also be stored as fp8 (e.g. indexer keys)
+bool compress_out_dtype(csa_dtype t) { return io_dtype(t) || t == CSA_FP8_E4M3; }
+
 int finish(int rc) {
     if (rc == -2) return CSA_ERR_UNSUPPORTED;
     if (rc != 0) return CSA_ERR_INVALID_ARG;
@@ -86,7 +89,7 @@ int csa_compress(const void* Ca, const void* Cb, const void* Za, const void* Zb,
                  int64_t batch, int64_t n, int m, int c, csa_dtype in_t, void* out, csa_dtype out_t,
                  csa_stream_t stream) {
     if (batch < 0 || n < 0 || m < 1 || c < 1) return CSA_ERR_INVALID_ARG;
-    if (!io_dtype(in_t) || !io_dtype(out_t)) return CSA_ERR_UNSUPPORTED;
+    if (!io_dtype(in_t) || !compress_out_dtype(out_t)) return CSA_ERR_UNSUPPORTED;
     if (!width_ok(c) || m > CSA_MAX_RATIO) return CSA_ERR_UNSUPPORTED;
     if (batch == 0 || n / m == 0) return CSA_OK;   // empty output: pointers may be NULL
     if (!Ca || !Cb || !Za || !Zb || !Ba || !Bb || !out) return CSA_ERR_INVALID_ARG;
@@ -101,7 +104,7 @@ int csa_compress_step(const void* Ca, const void* Cb, const void* Za, const void
                       const float* Bb, int64_t batch, int64_t block, int m, int c, csa_dtype in_t, void* cache,
                       int64_t cache_rows, csa_dtype out_t, csa_stream_t stream) {
     if (batch < 0 || block < 0 || m < 1 || c < 1 || cache_rows <= block) return CSA_ERR_INVALID_ARG;
-    if (!io_dtype(in_t) || !io_dtype(out_t)) return CSA_ERR_UNSUPPORTED;
+    if (!io_dtype(in_t) || !compress_out_dtype(out_t)) return CSA_ERR_UNSUPPORTED;
     if (!width_ok(c) || m > CSA_MAX_RATIO) return CSA_ERR_UNSUPPORTED;
     if (batch == 0) return CSA_OK;
     if (!Ca || !Za || !Ba || !cache || (block > 0 && (!Cb || !Zb || !Bb))) return CSA_ERR_INVALID_ARG;
@@ -116,7 +119,7 @@ int csa_compress_step(const void* Ca, const void* Cb, const void* Za, const void
 int hca_compress(const void* C, const void* Z, const float* B, int64_t batch, int64_t n, int m_prime, int c,
                  csa_dtype in_t, void* out, csa_dtype out_t, csa_stream_t stream) {
     if (batch < 0 || n < 0 || m_prime < 1 || c < 1) return CSA_ERR_INVALID_ARG;
-    if (!io_dtype(in_t) || !io_dtype(out_t)) return CSA_ERR_UNSUPPORTED;
+    if (!io_dtype(in_t) || !compress_out_dtype(out_t)) return CSA_ERR_UNSUPPORTED;
     if (!width_ok(c) || m_prime > CSA_MAX_RATIO) return CSA_ERR_UNSUPPORTED;
     if (batch == 0 || n / m_prime == 0) return CSA_OK;   // empty output: pointers may be NULL
     if (!C || !Z || !B || !out) return CSA_ERR_INVALID_ARG;
@@ -183,7 +186,8 @@ int csa_index_topk(const void* qI, const float* w, const void* kI, int64_t batch
     // the decode-shaped indexer (n_chunks > 0) also writes group maxima when the selection can
     // use them; otherwise it clears the multi-workgroup selection's per-row counters if needed
     const int G = n_chunks > 0 && group_region(rows, T, N, k) > 0 ? csa::topk_group(nv_max, k) : 0;
-    const int64_t gld = G > 0 ? (nv_max + G - 1) / G : 0;   // <= kTopkMaxGroups
+    // (rows of group maxima start 16-byte aligned: a multiple of 4, <= kTopkMaxGroups)
+    const int64_t gld = G > 0 ? ((nv_max + G - 1) / G + 3) & ~int64_t(3) : 0;
     float* gmax = G > 0 ? reinterpret_cast<float*>(static_cast<char*>(extra) +
                                                    round_up(csa::topk_extra_workspace(rows, N, k)))
                         : nullptr;
@@ -331,14 +335,37 @@ int hca_dense_mqa(const void* q, const void* kv, int64_t batch, int64_t T, int64
 
 int hca_dense_mqa_sink(const void* q, const void* kv, int64_t batch, int64_t T, int64_t q_pos0, int64_t N, int H, int c,
                        int m_prime, float scale, const float* sink, csa_dtype t, void* out, csa_stream_t stream) {
+    return hca_dense_mqa_swa(q, kv, batch, T, q_pos0, N, H, c, m_prime, scale, sink, nullptr, 0, 0, 0, t, out, stream);
+}
+
+int hca_dense_mqa_swa(const void* q, const void* kv, int64_t batch, int64_t T, int64_t q_pos0, int64_t N, int H, int c,
+                      int m_prime, float scale, const float* sink, const void* win_kv, int64_t W, int64_t win_pos0,
+                      int n_win, csa_dtype t, void* out, csa_stream_t stream) {
     if (sink && (reinterpret_cast<uintptr_t>(sink) & 3u)) return CSA_ERR_INVALID_ARG;
+    if (n_win < 0 || W < 0 || win_pos0 < 0) return CSA_ERR_INVALID_ARG;
+    if (n_win > 1024) return CSA_ERR_UNSUPPORTED;
+    if (n_win > 0 && W > 0 && (!win_kv || !aligned16(win_kv))) return CSA_ERR_INVALID_ARG;
+    if (N + W >= (int64_t(1) << 31)) return CSA_ERR_UNSUPPORTED;   // one 32-bit id space
     int rc = check_mqa(q, kv, out, batch, T, N, H, c, scale, t);
     if (rc != CSA_OK) return rc;
     if (m_prime < 1 || q_pos0 < 0) return CSA_ERR_INVALID_ARG;
     if (m_prime > CSA_MAX_RATIO) return CSA_ERR_UNSUPPORTED;
     if (batch == 0 || T == 0) return CSA_OK;
-    return finish(csa::launch_dense_mqa(q, kv, batch, T, q_pos0, N, H, c, m_prime, scale, t, out, sink,
+    const csa::SwaArgs swa{n_win > 0 ? win_kv : nullptr, n_win > 0 ? W : 0, win_pos0, q_pos0, n_win};
+    return finish(csa::launch_dense_mqa(q, kv, batch, T, q_pos0, N, H, c, m_prime, scale, t, out, sink, swa,
                                         static_cast<hipStream_t>(stream)));
+}
+
+int hca_compress_step(const void* C, const void* Z, const float* B, int64_t batch, int64_t block, int m_prime, int c,
+                      csa_dtype in_t, void* cache, int64_t cache_rows, csa_dtype out_t, csa_stream_t stream) {
+    if (batch < 0 || block < 0 || m_prime < 1 || c < 1 || cache_rows <= block) return CSA_ERR_INVALID_ARG;
+    if (!io_dtype(in_t) || !compress_out_dtype(out_t)) return CSA_ERR_UNSUPPORTED;
+    if (!width_ok(c) || m_prime > CSA_MAX_RATIO) return CSA_ERR_UNSUPPORTED;
+    if (batch == 0) return CSA_OK;
+    if (!C || !Z || !B || !cache) return CSA_ERR_INVALID_ARG;
+    if (!aligned16(C) || !aligned16(Z) || !aligned16(B) || !aligned16(cache)) return CSA_ERR_INVALID_ARG;
+    return finish(csa::launch_hca_compress_step(C, Z, B, batch, block, m_prime, c, in_t, cache, cache_rows, out_t,
+                                                static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -175,12 +175,22 @@ int launch_compress_step(const void* Ca, const void* Za, const float* Ba, const 
     return launch_any(a, in_t, out_t, stream);
 }
 
+int launch_hca_compress_step(const void* C, const void* Z, const float* B, int64_t batch, int64_t block, int m_prime,
+                             int c, int in_t, void* cache, int64_t cache_rows, int out_t, hipStream_t stream) {
+    // the state is the m' raw tokens of block `block`: entry `block` is its only entry
+    CompressArgs a{C, Z, B, nullptr, nullptr, nullptr, batch, m_prime, 1, m_prime, c, cache, 0, cache_rows, block};
+    if (batch == 0) return 0;
+    return launch_any(a, in_t, out_t, stream);
+}
+
 namespace {
 int launch_any(const CompressArgs& a, int in_t, int out_t, hipStream_t stream) {
     if (in_t == DT_F32 && out_t == DT_F32) return launch<DT_F32, DT_F32>(a, stream);
     if (in_t == DT_F32 && out_t == DT_BF16) return launch<DT_F32, DT_BF16>(a, stream);
     if (in_t == DT_BF16 && out_t == DT_F32) return launch<DT_BF16, DT_F32>(a, stream);
     if (in_t == DT_BF16 && out_t == DT_BF16) return launch<DT_BF16, DT_BF16>(a, stream);
+    if (in_t == DT_F32 && out_t == DT_FP8) return launch<DT_F32, DT_FP8>(a, stream);
+    if (in_t == DT_BF16 && out_t == DT_FP8) return launch<DT_BF16, DT_FP8>(a, stream);
     return -2;
 }
 }  // namespace

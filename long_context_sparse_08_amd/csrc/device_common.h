@@ -35,6 +35,22 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
     return (b & 0x80u) ? -v : v;
 }
 
+// fp32 -> OCP e4m3fn byte: round to nearest, ties to even, saturating at +-448 (finite input).
+// The grid's quantum at |x| is 2^(floor(log2|x|) - 3) for normal values (exponent >= -6) and
+// 2^-9 below; dividing by it is exact, rintf rounds to nearest even.
+__device__ __forceinline__ uint32_t f32_to_e4m3_rne(float f) {
+    const uint32_t sign = (__float_as_uint(f) >> 24) & 0x80u;
+    const float a = fminf(fabsf(f), 448.f);
+    const int ea = (int)((__float_as_uint(a) >> 23) & 255u) - 127;
+    const float q = __uint_as_float((uint32_t)((ea > -6 ? ea : -6) - 3 + 127) << 23);
+    const float r = rintf(a / q) * q;
+    if (r == 0.f) return sign;
+    const uint32_t rb = __float_as_uint(r);
+    const int er = (int)((rb >> 23) & 255u) - 127;
+    if (er < -6) return sign | (uint32_t)(r * 512.f);   // subnormal: r = mant * 2^-9
+    return sign | ((uint32_t)(er + 7) << 3) | ((rb >> 20) & 7u);
+}
+
 // Order-preserving map fp32 -> uint32 (larger float -> larger key); -0 and +0 map together.
 __device__ __forceinline__ uint32_t order_key(float f) {
     uint32_t u = __float_as_uint(f);
@@ -77,13 +93,20 @@ __device__ __forceinline__ float load1(const void* __restrict__ base, int64_t i)
     else return e4m3_to_f32(static_cast<const uint8_t*>(base)[i]);
 }
 
-// Store 8 floats at element offset i (8-aligned) as DT (F32 or BF16).
+// Store 8 floats at element offset i (8-aligned) as DT (F32, BF16 or FP8).
 template <int DT>
 __device__ __forceinline__ void store8(void* __restrict__ base, int64_t i, const float (&v)[8]) {
     if constexpr (DT == DT_F32) {
         float4* p = reinterpret_cast<float4*>(static_cast<float*>(base) + i);
         p[0] = make_float4(v[0], v[1], v[2], v[3]);
         p[1] = make_float4(v[4], v[5], v[6], v[7]);
+    } else if constexpr (DT == DT_FP8) {
+        uint2 r;
+        r.x = f32_to_e4m3_rne(v[0]) | (f32_to_e4m3_rne(v[1]) << 8) | (f32_to_e4m3_rne(v[2]) << 16) |
+              (f32_to_e4m3_rne(v[3]) << 24);
+        r.y = f32_to_e4m3_rne(v[4]) | (f32_to_e4m3_rne(v[5]) << 8) | (f32_to_e4m3_rne(v[6]) << 16) |
+              (f32_to_e4m3_rne(v[7]) << 24);
+        *reinterpret_cast<uint2*>(static_cast<uint8_t*>(base) + i) = r;
     } else {
         uint4 r;
         r.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);

@@ -80,7 +80,15 @@ int launch_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t
                       int c, int k, float scale, int t, void* out, void* ws, const float* sink, const SwaArgs& swa,
                       hipStream_t stream);
 
+// Dense causal MQA over the visible entries (ratio r) and, with swa.n_win > 0, the query's
+// window rows (swa.q_pos0 must equal q_pos0).
 int launch_dense_mqa(const void* q, const void* kv, int64_t batch, int64_t T, int64_t q_pos0, int64_t N, int H, int c,
-                     int ratio, float scale, int t, void* out, const float* sink, hipStream_t stream);
+                     int ratio, float scale, int t, void* out, const float* sink, const SwaArgs& swa,
+                     hipStream_t stream);
+
+// HCA compression as a decode step: the state holds the raw tokens of block `block`
+// ([batch, m', c] per stream); writes entry `block` to row `block` of the cache.
+int launch_hca_compress_step(const void* C, const void* Z, const float* B, int64_t batch, int64_t block, int m_prime,
+                             int c, int in_t, void* cache, int64_t cache_rows, int out_t, hipStream_t stream);
 
 }  // namespace csa

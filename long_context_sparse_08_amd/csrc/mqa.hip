@@ -29,18 +29,24 @@ __device__ __forceinline__ float sink_term(const float* sink, int64_t head, floa
     return (sink != nullptr && m != -INFINITY) ? exp2f(sink[head] * kLog2e - m) : 0.f;
 }
 
-// Key i of a row's list ([N] §1.3 and [M] §2.3.3 item 3: a sliding-window branch over the most
-// recent n_win uncompressed tokens joins the compressed entries): i < k is the selected entry
-// idx[row, i] (its id, or -1 if outside [0, N)); k <= i < k + n_win is the window token at
-// position p - n_win + 1 + (i - k), id N + its raw row, or -1 outside the given raw rows.
+// Window slot j < n_win of the query at position p ([N] §1.3 and [M] §2.3.3 item 3: a
+// sliding-window branch over the most recent n_win uncompressed tokens joins the compressed
+// entries): the raw token at position p - n_win + 1 + j, id n_ent + its row in the window
+// buffer, or -1 when that position is before 0 or outside the given raw rows.
+__device__ __forceinline__ int window_key(int64_t p, const SwaArgs& w, int j, int n_ent) {
+    const int64_t pw = p - w.n_win + 1 + j;
+    return (pw >= 0 && pw >= w.win_pos0 && pw < w.win_pos0 + w.W) ? n_ent + (int)(pw - w.win_pos0) : -1;
+}
+
+// Key i of a sparse row's list: i < k is the selected entry idx[row, i] (its id, or -1 if
+// outside [0, N)); k <= i < k + n_win is window slot i - k.
 __device__ __forceinline__ int list_key(const int32_t* __restrict__ idx, int64_t row, int k, int n_ent, int64_t p,
                                         const SwaArgs& w, int i) {
     if (i < k) {
         const int s = idx[row * k + i];
         return (uint32_t)s < (uint32_t)n_ent ? s : -1;
     }
-    const int64_t pw = p - w.n_win + 1 + (i - k);
-    return (pw >= 0 && pw >= w.win_pos0 && pw < w.win_pos0 + w.W) ? n_ent + (int)(pw - w.win_pos0) : -1;
+    return window_key(p, w, i - k, n_ent);
 }
 
 template <int DT, int CPL, bool DENSE>
@@ -65,7 +71,9 @@ mqa_generic(const void* __restrict__ q, const void* __restrict__ kv, const int32
     }
     float mx = -INFINITY, den = 0.f;
 
-    const int64_t count = DENSE ? visible_entries(q_pos0 + t, ratio, N) : (int64_t)k + swa.n_win;
+    // dense: the visible entries 0 .. nvis-1, then the window slots (if any)
+    const int64_t nvis = DENSE ? visible_entries(q_pos0 + t, ratio, N) : 0;
+    const int64_t count = DENSE ? nvis + swa.n_win : (int64_t)k + swa.n_win;
     const int64_t kvbase = b * N * c;
 
     for (int64_t r0 = 0; r0 < count; r0 += kKeyBatch) {
@@ -75,8 +83,11 @@ mqa_generic(const void* __restrict__ q, const void* __restrict__ kv, const int32
         for (int u = 0; u < kKeyBatch; ++u) {
             const int64_t r = r0 + u;
             int64_t s = -1;
-            if (r < count) s = DENSE ? r : (int64_t)list_key(idx, row, k, (int)N, swa.q_pos0 + t, swa, (int)r);
-            ok[u] = DENSE ? (s >= 0 && s < N) : s >= 0;
+            if (r < count)
+                s = !DENSE ? (int64_t)list_key(idx, row, k, (int)N, swa.q_pos0 + t, swa, (int)r)
+                    : r < nvis ? r
+                               : (int64_t)window_key(q_pos0 + t, swa, (int)(r - nvis), (int)N);
+            ok[u] = s >= 0;
             sidx[u] = ok[u] ? s : 0;
         }
         float kvv[kKeyBatch][CPL], part[kKeyBatch];
@@ -299,17 +310,27 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int hg = (int)(rem / ks_count), ks = (int)(rem % ks_count);
     if (row >= rows) return;
     const int64_t b = row / T;
-    const int64_t klen = DENSE ? visible_entries(q_pos0 + row % T, ratio, N) : (int64_t)k + swa.n_win;
+    // dense: the visible entries 0 .. nvis-1, then (WIN) the window slots
+    const int64_t nvis = DENSE ? visible_entries(q_pos0 + row % T, ratio, N) : 0;
+    const int64_t klen = DENSE ? nvis + (WIN ? swa.n_win : 0) : (int64_t)k + swa.n_win;
     const int key0 = ks * keys_per_split;
     const int nkeys = (int)max((int64_t)0, min(klen, (int64_t)key0 + keys_per_split) - key0);
     const int h0 = hg * kMHeadsWG;
     const int n_ent = (int)N;   // entry ids are 32-bit (the C ABI rejects N >= 2^31)
+    // dense window slot j: its id (>= n_ent), or -1
+    auto dense_window = [&](int j) { return window_key(q_pos0 + row % T, swa, j, n_ent); };
     // entry gathered for slot i of this range: slots past the range and invalid ids load
     // entry 0, which the validity mask of the block keeps out of the softmax
     auto key_id = [&](int i) -> int {
         if (i >= nkeys) return 0;
-        if constexpr (DENSE) return key0 + i;
-        else return ids[i];
+        if constexpr (DENSE) {
+            const int j = key0 + i;
+            if (!WIN || j < nvis) return j;
+            const int w = dense_window(j - (int)nvis);
+            return w < 0 ? 0 : w;
+        } else {
+            return ids[i];
+        }
     };
 
     // key ids first, then q: q's loads overlap the id round trip and the first gather
@@ -386,7 +407,12 @@ mqa_sparse_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     auto compute = [&](int blk, const uint8_t* st) {
         // validity of the 32 keys of this block (bit r), shifted to this lane's key group
         uint32_t vg;
-        if constexpr (DENSE) {
+        if constexpr (DENSE && WIN) {
+            // bit r: slot blk*32 + r is a visible entry or a window row (a ballot of lanes 0-31)
+            const int i = blk * kMBlk + (lane & 31), j = key0 + i;
+            const bool ok = i < nkeys && (j < nvis || dense_window(j - (int)nvis) >= 0);
+            vg = (uint32_t)__ballot(ok) >> (4 * g);
+        } else if constexpr (DENSE) {
             const int nv = nkeys - blk * kMBlk;   // >= 1
             vg = (nv >= 32 ? ~0u : (1u << nv) - 1u) >> (4 * g);
         } else {
@@ -1182,26 +1208,28 @@ int launch_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t
 }
 
 int launch_dense_mqa(const void* q, const void* kv, int64_t batch, int64_t T, int64_t q_pos0, int64_t N, int H, int c,
-                     int ratio, float scale, int t, void* out, const float* sink, hipStream_t stream) {
+                     int ratio, float scale, int t, void* out, const float* sink, const SwaArgs& swa,
+                     hipStream_t stream) {
     if (batch == 0 || T == 0) return 0;
-    if (t == DT_BF16 && c == kMC && H % kMHeadsWG == 0 && N <= kMMaxEntries) {
-        // one workgroup per (query, 64 heads) walks every visible entry: no key split, no
-        // partials (used for query chunks, which supply rows * H / 64 >= 256 workgroups)
+    if (t == DT_BF16 && c == kMC && H % kMHeadsWG == 0 && N <= kMMaxEntries && swa.W <= kMMaxEntries) {
+        // one workgroup per (query, 64 heads) walks every visible entry (and its window rows):
+        // no key split, no partials (used for query chunks, which supply rows * H / 64 >= 256
+        // workgroups)
         const int64_t rows = batch * T;
         const int64_t units = ((rows + 7) / 8) * 8 * (H / kMHeadsWG);
         if (units > 0x7fffffffLL) return -2;
-        hipLaunchKernelGGL((mqa_sparse_mfma<true, false>), dim3((unsigned)units), dim3(kMWaves * kWave), 0, stream,
-                           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), nullptr, rows, T, N, H, 0,
-                           1, 0x7fffffff, scale * kLog2e, q_pos0, ratio, static_cast<uint16_t*>(out), nullptr, nullptr,
-                           sink, SwaArgs{});
+        hipLaunchKernelGGL((swa.n_win > 0 ? mqa_sparse_mfma<true, true> : mqa_sparse_mfma<true, false>),
+                           dim3((unsigned)units), dim3(kMWaves * kWave), 0, stream, static_cast<const uint16_t*>(q),
+                           static_cast<const uint16_t*>(kv), nullptr, rows, T, N, H, 0, 1, 0x7fffffff, scale * kLog2e,
+                           q_pos0, ratio, static_cast<uint16_t*>(out), nullptr, nullptr, sink, swa);
         return 0;
     }
     if (t == DT_F32)
-        return launch_generic<DT_F32, true>(q, kv, nullptr, batch, T, N, H, c, 0, scale, q_pos0, ratio, out, sink, SwaArgs{},
-                                                      stream);
+        return launch_generic<DT_F32, true>(q, kv, nullptr, batch, T, N, H, c, 0, scale, q_pos0, ratio, out, sink, swa,
+                                            stream);
     if (t == DT_BF16)
-        return launch_generic<DT_BF16, true>(q, kv, nullptr, batch, T, N, H, c, 0, scale, q_pos0, ratio, out, sink, SwaArgs{},
-                                                      stream);
+        return launch_generic<DT_BF16, true>(q, kv, nullptr, batch, T, N, H, c, 0, scale, q_pos0, ratio, out, sink, swa,
+                                             stream);
     return -2;
 }
 

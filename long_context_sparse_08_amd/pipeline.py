@@ -3,8 +3,9 @@ allocated once up front (so a step allocates nothing and can be timed or graph-c
 
     CsaPrefill  compress KV + compress index keys -> index/top-k -> sparse MQA
     CsaDecode   index/top-k over a pre-compressed context -> sparse MQA (one new token per
-                sequence; at position ctx_len the new token opens an incomplete block, so
-                no entry is compressed in this step)
+                sequence); every m-th step the new token completes a block, and that step
+                first compresses the block's KV entry and index-key entry from the state
+                (the raw streams of the last two blocks) into the caches
     HcaChunk    HCA compression of the whole context -> dense causal MQA for a query chunk
 
 Inputs are device tensors in their storage dtypes (bf16 as torch.bfloat16, fp8 e4m3fn as
@@ -16,8 +17,8 @@ import math
 
 import torch
 
-from . import (CSA_KV_FP8_BF16, KVFp8Bf16, csa_compress, csa_index_topk, csa_sparse_mqa, hca_compress,
-               hca_dense_mqa, mqa_workspace_for, workspace_for)
+from . import (CSA_KV_FP8_BF16, KVFp8Bf16, csa_compress, csa_compress_step, csa_index_topk, csa_sparse_mqa,
+               hca_compress, hca_dense_mqa, mqa_workspace_for, workspace_for)
 
 
 class CsaPrefill:
@@ -81,9 +82,32 @@ class CsaDecode:
     def attend(self):
         csa_sparse_mqa(self.inp["q"], self.inp["kv"], self.idx, self.scale, out=self.out, workspace=self.mqa_ws)
 
+    def can_compress(self) -> bool:
+        """The inputs hold a decode state for the KV and the index-key caches."""
+        return all(nm in self.inp for nm in ("Ca", "Cb", "Za", "Zb", "Ba", "Bb", "ICa", "ICb", "IZa", "IZb",
+                                             "IBa", "IBb"))
+
+    def compress(self):
+        """The entries of the block the newest token completes: the block is the last one of
+        the caches (entry N-1), computed from the state of its two blocks and written in place."""
+        i = self.inp
+        blk = i["kv"].shape[1] - 1
+        csa_compress_step(i["Ca"], i["Cb"], i["Za"], i["Zb"], i["Ba"], i["Bb"], blk, i["kv"])
+        csa_compress_step(i["ICa"], i["ICb"], i["IZa"], i["IZb"], i["IBa"], i["IBb"], blk, i["kI"])
+
     def run(self):
         self.select()
         self.attend()
+        return self.out
+
+    def run_steps(self):
+        """m decode steps: the last one's token completes a block, so that step compresses its
+        entries first (one compression every m steps)."""
+        for j in range(self.m):
+            if j == self.m - 1:
+                self.compress()
+            self.select()
+            self.attend()
         return self.out
 
 

@@ -154,6 +154,8 @@ DECODE_TOPK_CASES = [  # batch, T, q_pos0, N, k, levels, zero-key fraction
     (1, 1, 4 * 36000, 36000, 512, 1, 0.0),        # every score equal
     (3, 1, 4 * 5000, 5000, 1024, 4, 0.0),         # groups of one score
     (2, 2, 4 * 20000 - 5, 20000, 1024, 3, 0.0),   # register-staged rows, ragged tails
+    (4, 1, 4 * 9001 + 3, 9001, 1024, 5, 0.0),     # register-staged: a partial last float4 group
+    (2, 3, 4 * 32768 - 9, 32768, 2048, 4, 0.5),   # register-staged: half the keys zero, rows of three lengths
     (2, 1, 4 * 32768, 32768, 1024, 6, 0.0),       # the 128K decode shape: b2 ranked in one wave
     (1, 2, 4 * 30000, 30000, 1024, 3, 0.99),      # register-staged, heavy ties: select over the row
     (1, 3, 4 * 30000 - 6, 30000, 2048, 2, 0.0),   # register-staged, 100-170 members of b2
@@ -182,6 +184,36 @@ def test_topk_decode_shapes_bit_exact(case):
     ref_idx, ref_sel = oracle.topk(sc, m, k, q_pos0=p0)
     idx, sel = csa.csa_index_topk(to_dev(q8, FP8), to_dev(w, F32), to_dev(k8, FP8), p0, m, k)
     idx, sel = from_dev(idx), from_dev(sel)
+    assert np.array_equal(idx, ref_idx)
+    assert np.array_equal(sel, ref_sel.astype(np.float32).astype(np.float64))
+
+
+SELECT_ON_GPU_SCORES = [  # batch, T, q_pos0, N, k, dtype: continuous (non-integer) scores
+    (32, 1, 4 * 32768, 32768, 1024, FP8),       # the 128K decode shape
+    (4, 1, 4 * 9001 + 3, 9001, 1024, FP8),      # a ragged row tail (nv % 4 = 1)
+    (2, 3, 4 * 32768 - 9, 32768, 2048, FP8),    # rows of different lengths, maximum k
+    (3, 1, 4 * 20000, 20000, 512, BF16),
+    (2, 1, 4 * 100000, 100000, 1024, FP8),      # the indexer's group maxima
+]
+
+
+@pytest.mark.parametrize("case", SELECT_ON_GPU_SCORES, ids=lambda c: "b%d_T%d_p%d_N%d_k%d_%d" % c)
+def test_topk_bit_exact_on_the_gpu_scores(case):
+    """The selection of csa_index_topk equals the oracle's top-k rule applied to the very fp32
+    scores the GPU indexer produces (csa_index_scores runs the same indexer kernel), on
+    continuous scores: ids and selected scores bit for bit."""
+    batch, T, p0, N, k, dt = case
+    H, cI, m = 64, 128, 4
+    say(f"selection on GPU scores {case}")
+    sd = 1700 + N
+    qI, kI = draw(sd, 1, (batch, T, H, cI), dt), draw(sd, 2, (batch, N, cI), dt)
+    w = rng.uniform(sd, 3, (batch, T, H), F32)
+    q_d, w_d, k_d = to_dev(qI, dt), to_dev(w, F32), to_dev(kI, dt)
+    sc = from_dev(csa.csa_index_scores(q_d, w_d, k_d, p0, m))
+    ref_idx, ref_sel = oracle.topk(sc, m, k, q_pos0=p0)
+    idx, sel = csa.csa_index_topk(q_d, w_d, k_d, p0, m, k)
+    idx, sel = from_dev(idx), from_dev(sel)
+    say(f"  rows identical: {np.mean(np.all(idx == ref_idx, axis=-1)):.4f}")
     assert np.array_equal(idx, ref_idx)
     assert np.array_equal(sel, ref_sel.astype(np.float32).astype(np.float64))
 
@@ -434,6 +466,56 @@ def test_sparse_mqa_sliding_window(case):
     out_tol(dt)(got, ref, "sparse mqa + window")
 
 
+DENSE_SWA_CASES = [  # batch, T, q_pos0, N, H, m', W, win_pos0, n_win, sink, dtype
+    (2, 9, 1, 4, 4, 4, 14, 0, 5, False, F32),          # generic kernel: the first queries see no entry
+    (1, 70, 128 * 40 - 30, 40, 64, 128, 200, 128 * 40 - 160, 128, True, BF16),   # matrix cores
+    (1, 33, 128 * 9 - 5, 12, 128, 128, 40, 128 * 9 - 37, 128, False, BF16),     # window rows missing at the
+                                                                                  # buffer start; two head groups
+    (2, 8, 504, 4, 64, 128, 64, 470, 16, True, BF16),  # last query: every window row also in an entry
+]
+
+
+@pytest.mark.parametrize("case", DENSE_SWA_CASES, ids=lambda c: "b%d_T%d_p%d_N%d_H%d_m%d_W%d_w%d_n%d_%d_%d" % c)
+def test_dense_mqa_sliding_window(case):
+    """HCA dense attention plus the window branch (the notes page §1.3 gives HCA the window
+    too): every visible HCA entry and the raw rows of the query's last n_win positions in one
+    softmax, against the oracle's plain union; one case per kernel path."""
+    batch, T, p0, N, H, mp, W, wp0, n_win, with_sink, dt = case
+    c = 64 if dt == F32 else 512
+    say(f"hca_dense_mqa_swa {case}")
+    sd = 1900 + T
+    q, kv, wkv = draw(sd, 1, (batch, T, H, c), dt), draw(sd, 2, (batch, N, c), dt), draw(sd, 3, (batch, W, c), dt)
+    sink = (2.0 * np.random.RandomState(sd).randn(H)).astype(np.float32) if with_sink else None
+    scale = 1.0 / np.sqrt(c)
+    ref = oracle.hca_dense_mqa(q, kv, mp, scale, q_pos0=p0, dtype=dt, sink=sink, window=(wkv, wp0, n_win))
+    got = from_dev(csa.hca_dense_mqa(to_dev(q, dt), to_dev(kv, dt), p0, mp, scale,
+                                     sink=None if sink is None else torch.from_numpy(sink).cuda(),
+                                     window=(to_dev(wkv, dt), wp0, n_win)))
+    out_tol(dt)(got, ref, "dense mqa + window")
+
+
+@pytest.mark.parametrize("dt", [F32, BF16])
+def test_hca_compress_step_matches_whole_sequence(dt):
+    """Decode-step HCA compression (m' = 128) from the state of the current block writes exactly
+    the entry hca_compress computes for the whole sequence, and only that cache row."""
+    batch, mp, c, nb = 2, 128, 512 if dt == BF16 else 64, 5
+    n = mp * nb + 7
+    say(f"hca_compress_step dt={dt}")
+    sd = 1950 + c
+    C, Z = draw(sd, 1, (batch, n, c), dt), draw(sd, 2, (batch, n, c), dt)
+    B = draw(sd, 3, (mp, c), F32, std=0.1)
+    Cd, Zd, Bd = to_dev(C, dt), to_dev(Z, dt), to_dev(B, F32)
+    full = csa.hca_compress(Cd, Zd, Bd, mp)
+    cache = torch.zeros((batch, nb + 2, c), dtype=Cd.dtype, device="cuda")
+    for blk in (3, 0, 4, 1, 2):   # any order: each step reads only its own block
+        sl = slice(mp * blk, mp * (blk + 1))
+        csa.hca_compress_step(Cd[:, sl].contiguous(), Zd[:, sl].contiguous(), Bd, blk, cache)
+    assert torch.equal(cache[:, :nb], full)
+    assert not cache[:, nb:].any()
+    ref = oracle.hca_compress(C, Z, B, mp, in_dtype=dt, out_dtype=dt)
+    out_tol(dt)(from_dev(cache[:, :nb]), ref, "hca compress step")
+
+
 @pytest.mark.parametrize("dt", [F32, BF16])
 def test_compress_step_matches_whole_sequence(dt):
     """Decode-step compression from a state of the last two blocks (the state cache of the
@@ -459,6 +541,84 @@ def test_compress_step_matches_whole_sequence(dt):
     ref = oracle.csa_compress(st["Ca"], st["Cb"], st["Za"], st["Zb"], Ba, Bb, m, in_dtype=dt,
                               out_dtype=dt)
     out_tol(dt)(from_dev(cache[:, :nb]), ref, "compress step")
+
+
+@pytest.mark.parametrize("kind", ["csa", "csa_step", "hca", "hca_step"])
+def test_compress_fp8_output(kind):
+    """fp8 e4m3 outputs of the compressor (the storage of fp8 indexer keys): the bytes are exactly
+    the nearest-even, saturating e4m3 rounding of the same kernel's fp32 result (the oracle's
+    rounding applied to the GPU's fp32 output), and within one e4m3 step of the oracle's
+    rounded entries."""
+    batch, c = 3, 128
+    m = 4 if kind.startswith("csa") else 128
+    nb = 6
+    n = m * nb
+    say(f"compress with fp8 output: {kind}")
+    sd = 2000 + m
+    # values of up to ~700: some entries pass 448 and saturate; scores of unit scale
+    st = [draw(sd, i + 1, (batch, n, c), BF16, std=250.0 if i < 2 else 1.0) for i in range(4)]
+    Ba, Bb = draw(sd, 5, (m, c), F32, std=0.1), draw(sd, 6, (m, c), F32, std=0.1)
+    d = [to_dev(x, BF16) for x in st]
+    Bad, Bbd = to_dev(Ba, F32), to_dev(Bb, F32)
+    u8 = torch.uint8
+    if kind == "csa":
+        g32 = csa.csa_compress(*d, Bad, Bbd, m, out_dtype=torch.float32)
+        g8 = csa.csa_compress(*d, Bad, Bbd, m, out_dtype=u8)
+        ref = oracle.csa_compress(*st, Ba, Bb, m, in_dtype=BF16, out_dtype=FP8)
+    elif kind == "hca":
+        g32 = csa.hca_compress(d[0], d[2], Bad, m, out_dtype=torch.float32)
+        g8 = csa.hca_compress(d[0], d[2], Bad, m, out_dtype=u8)
+        ref = oracle.hca_compress(st[0], st[2], Ba, m, in_dtype=BF16, out_dtype=FP8)
+    else:
+        g32 = torch.zeros((batch, nb, c), dtype=torch.float32, device="cuda")
+        g8 = torch.zeros((batch, nb, c), dtype=u8, device="cuda")
+        for blk in range(nb):
+            if kind == "csa_step":
+                sl = slice(m * max(0, blk - 1), m * (blk + 1))
+                args = [x[:, sl].contiguous() for x in d] + [Bad, Bbd, blk]
+                csa.csa_compress_step(*args, g32)
+                csa.csa_compress_step(*args, g8)
+            else:
+                sl = slice(m * blk, m * (blk + 1))
+                csa.hca_compress_step(d[0][:, sl].contiguous(), d[2][:, sl].contiguous(), Bad, blk, g32)
+                csa.hca_compress_step(d[0][:, sl].contiguous(), d[2][:, sl].contiguous(), Bad, blk, g8)
+        ref = (oracle.csa_compress(*st, Ba, Bb, m, in_dtype=BF16, out_dtype=FP8) if kind == "csa_step"
+               else oracle.hca_compress(st[0], st[2], Ba, m, in_dtype=BF16, out_dtype=FP8))
+    torch.cuda.synchronize()
+    got = oracle.decode(from_dev(g8), FP8)
+    assert np.array_equal(got, oracle.round_to(from_dev(g32), FP8))
+    step = np.maximum(2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -6))) - 3), 2.0 ** -9)
+    assert np.all(np.abs(got - ref) <= step)
+    same = np.mean(got == ref)
+    say(f"  fp8 entries equal to the oracle's rounding: {same:.5f}; saturated: {np.mean(np.abs(got) == 448):.4f}")
+    assert same >= 0.99
+
+
+def test_decode_step_compression_through_the_pipeline():
+    """The decode step that completes a block (the pipeline's compress stage) writes the KV entry
+    (bf16) and the fp8 index-key entry of that block into the last cache rows: equal to the
+    oracle's compression of the state, rounded to the caches' dtypes."""
+    from long_context_sparse_08_amd.pipeline import CsaDecode
+    from workloads import CONFIGS, make_inputs, scaled, shapes
+    cfg = scaled(CONFIGS["cfg2_csa_decode_128k"], batch=3, N=2000, q_pos0=4 * 2000, k=256)
+    host = make_inputs(cfg)
+    sh = shapes(cfg)
+    dev = {k: to_dev(v, sh[k][1]) for k, v in host.items()}
+    pipe = CsaDecode(dev, cfg.m, cfg.k, cfg.q_pos0)
+    assert pipe.can_compress()
+    pipe.run_steps()
+    torch.cuda.synchronize()
+    kv_ref = oracle.csa_compress(host["Ca"], host["Cb"], host["Za"], host["Zb"], host["Ba"], host["Bb"], cfg.m,
+                                 in_dtype=BF16, out_dtype=BF16)
+    kI_ref = oracle.csa_compress(host["ICa"], host["ICb"], host["IZa"], host["IZb"], host["IBa"], host["IBb"],
+                                 cfg.m, in_dtype=BF16, out_dtype=FP8)
+    kv_got = from_dev(dev["kv"][:, -1])
+    kI_got = oracle.decode(from_dev(dev["kI"][:, -1]), FP8)
+    assert_abs_close(kv_got, kv_ref[:, -1], 2e-2, "decode-step KV entry")
+    step = np.maximum(2.0 ** (np.floor(np.log2(np.maximum(np.abs(kI_ref[:, -1]), 2.0 ** -6))) - 3), 2.0 ** -9)
+    assert np.all(np.abs(kI_got - kI_ref[:, -1]) <= step)
+    # the rows before the last are the context as given
+    assert np.array_equal(from_dev(dev["kv"][:, :-1]), oracle.decode(host["kv"][:, :-1], BF16))
 
 
 def test_repeat_runs_are_bitwise_identical():

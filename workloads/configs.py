@@ -113,6 +113,20 @@ def shapes(cfg: Config) -> dict:
     if cfg.kind == "csa_decode":
         s["kv"] = ((B, cfg.N, c), cfg.dt if cfg.kv_dt < 0 else cfg.kv_dt, ("normal", 1.0))
         s["kI"] = ((B, cfg.N, cfg.c_I), cfg.qk_dt, ("normal", 1.0))
+        # the decode state: raw streams of the last two blocks (2m tokens), from which the step
+        # whose token completes a block computes the new KV entry and index-key entry (caches
+        # in bf16 / fp8; no state for caches stored in other formats)
+        m2 = 2 * cfg.m
+        if cfg.kv_dt < 0:
+            for nm in ("Ca", "Cb", "Za", "Zb"):
+                s[nm] = ((B, m2, c), cfg.dt, ("normal", 1.0))
+            for nm in ("Ba", "Bb"):
+                s[nm] = ((cfg.m, c), F32, ("normal", 0.1))
+        if cfg.qk_dt in (F32, BF16, FP8):
+            for nm in ("ICa", "ICb", "IZa", "IZb"):
+                s[nm] = ((B, m2, cfg.c_I), cfg.dt, ("normal", 1.0))
+            for nm in ("IBa", "IBb"):
+                s[nm] = ((cfg.m, cfg.c_I), F32, ("normal", 0.1))
     if cfg.kind in ("csa_prefill", "csa_decode"):
         s["q"] = ((B, cfg.T, cfg.H, c), cfg.dt, ("normal", 1.0))
         s["qI"] = ((B, cfg.T, cfg.H_I, cfg.c_I), cfg.qk_dt, ("normal", 1.0))
