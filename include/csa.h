@@ -200,10 +200,11 @@ int csa_topk(const float* scores, int64_t ld, int64_t batch, int64_t T, int64_t 
  *               NULL when that size is 0), 16-byte aligned; holds per-key-range partial
  *               results when a query's keys are split over several workgroups.
  * Limits: c % 8 == 0, c <= CSA_MAX_WIDTH, 1 <= H <= CSA_MAX_HEADS, 1 <= k <= CSA_MAX_TOPK.
- * CSA_KV_FP8_BF16 is built for decode shapes only: c == 512, H % 64 == 0,
- * batch * T * H / 64 <= 256, k <= 1024; other shapes return CSA_ERR_UNSUPPORTED (as does
- * hca_dense_mqa for it).  The fp8 values are used exactly (converted to bf16 for the
- * products); logits, softmax and accumulation stay fp32.
+ * CSA_KV_FP8_BF16 (c >= 64): decode shapes (c == 512, H % 64 == 0, batch * T * H / 64 <=
+ * 256, k <= 1024, no window) run on the matrix cores; every other shape, the window branch
+ * and hca_dense_mqa take a vector-ALU kernel (any shape; the prefill and HCA matrix-core
+ * paths are compute-bound, where fp8 rows would save no time).  The fp8 values are used
+ * exactly; logits, softmax and accumulation stay fp32.
  */
 size_t csa_sparse_mqa_workspace_size(int64_t batch, int64_t T, int H, int c, int k, csa_dtype t);
 int csa_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t batch, int64_t T, int64_t N, int H,
@@ -213,7 +214,8 @@ int csa_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t ba
 /*
  * hca_dense_mqa — dense causal shared-KV MQA over every visible HCA entry ([M] §2.3.2; [N]
  * §1.2: no selection): for the query at position p, the entries s with m'(s+1)-1 <= p.
- *   q : [batch, T, H, c], kv : [batch, N, c], out : [batch, T, H, c], all dtype t.
+ *   q : [batch, T, H, c], kv : [batch, N, c], out : [batch, T, H, c], all dtype t (or
+ *   t = CSA_KV_FP8_BF16: kv in the mixed rows of csa_sparse_mqa, q and out bf16).
  * A query that sees no entry gets a zero output.  Limits as csa_sparse_mqa.
  */
 int hca_dense_mqa(const void* q, const void* kv, int64_t batch, int64_t T, int64_t q_pos0, int64_t N, int H,
@@ -256,11 +258,12 @@ int csa_rope(void* x, int64_t batch, int64_t T, int H, int c, int d, int64_t pos
  * most recent n_win uncompressed KV tokens, n_win = 128 on the pages): the query at absolute
  * position p = q_pos0 + t attends, in one softmax, to its selected entries idx[t,:] and to the
  * raw rows win_kv[j] whose position win_pos0 + j lies in [p - n_win + 1, p].
- *   win_kv : [batch, W, c] raw KV rows of each sequence (bf16 / fp32 as q), rows at absolute
- *            positions win_pos0 .. win_pos0 + W - 1 (a decode step passes its window state;
- *            a prefill chunk its own raw KV).  May be NULL when n_win == 0 or W == 0.
+ *   win_kv : [batch, W, c] raw KV rows of each sequence (bf16 / fp32 as q; bf16 with
+ *            CSA_KV_FP8_BF16 entries), rows at absolute positions win_pos0 .. win_pos0 + W - 1
+ *            (a decode step passes its window state; a prefill chunk its own raw KV).  May be
+ *            NULL when n_win == 0 or W == 0.
  *   workspace : at least csa_sparse_mqa_workspace_size(batch, T, H, c, k + n_win, t) bytes.
- * Limits: as csa_sparse_mqa; 0 <= n_win <= 1024; N + W < 2^31; not with CSA_KV_FP8_BF16.
+ * Limits: as csa_sparse_mqa; 0 <= n_win <= 1024; N + W < 2^31.
  */
 int csa_sparse_mqa_swa(const void* q, const void* kv, const int32_t* idx, int64_t batch, int64_t T, int64_t N,
                        int H, int c, int k, float scale, const float* sink, const void* win_kv, int64_t W,

@@ -310,6 +310,7 @@ def csa_sparse_mqa(q, kv, idx, scale: float, out=None, workspace=None, sink=None
     assert idx.dtype == torch.int32 and idx.shape == (batch, T, k)
     if out is None:
         out = torch.empty_like(q)
+    _check_out(out, (batch, T, H, c), q.dtype, "out")
     wkv, W, wp0, qp0, n_win = None, 0, 0, 0, 0
     if window is not None:
         wkv, wp0, qp0, n_win = window
@@ -356,10 +357,17 @@ def hca_dense_mqa(q, kv, q_pos0: int, m_prime: int, scale: float, out=None, sink
     """q [batch, T, H, c], kv [batch, N, c] HCA entries -> out [batch, T, H, c] (dense causal MQA).
     sink: optional fp32 [H]; window: optional (win_kv [batch, W, c], win_pos0, n_win), the
     sliding-window branch over the raw rows at positions p - n_win + 1 .. p."""
-    dev = _dev(q, kv, out)
+    mixed = isinstance(kv, KVFp8Bf16)
+    kvt = kv.data if mixed else kv
+    dev = _dev(q, kvt, out)
     batch, T, H, c = q.shape
     N = kv.shape[1]
-    assert kv.shape == (batch, N, c) and kv.dtype == q.dtype
+    if mixed:
+        assert q.dtype == torch.bfloat16 and kv.c == c and kvt.shape[0] == batch
+        dt = CSA_KV_FP8_BF16
+    else:
+        assert kv.shape == (batch, N, c) and kv.dtype == q.dtype
+        dt = _dt(q)
     if out is None:
         out = torch.empty_like(q)
     _check_out(out, (batch, T, H, c), q.dtype, "out")
@@ -370,8 +378,8 @@ def hca_dense_mqa(q, kv, q_pos0: int, m_prime: int, scale: float, out=None, sink
         _dev(q, wkv)
         W = wkv.shape[1]
     sk = _sink(sink, H, dev)
-    _check("hca_dense_mqa", lib.hca_dense_mqa_swa(_p(q), _p(kv), batch, T, q_pos0, N, H, c, m_prime, float(scale),
-                                                  _p(sk), _p(wkv), W, wp0, n_win, _dt(q), _p(out), _stream(dev)))
+    _check("hca_dense_mqa", lib.hca_dense_mqa_swa(_p(q), _p(kvt), batch, T, q_pos0, N, H, c, m_prime, float(scale),
+                                                  _p(sk), _p(wkv), W, wp0, n_win, dt, _p(out), _stream(dev)))
     return out
 
 

@@ -297,7 +297,7 @@ int csa_sparse_mqa_swa(const void* q, const void* kv, const int32_t* idx, int64_
                        csa_stream_t stream) {
     if (sink && (reinterpret_cast<uintptr_t>(sink) & 3u)) return CSA_ERR_INVALID_ARG;
     if (n_win < 0 || W < 0 || win_pos0 < 0 || q_pos0 < 0) return CSA_ERR_INVALID_ARG;
-    if (n_win > 1024 || (n_win > 0 && t == CSA_KV_FP8_BF16)) return CSA_ERR_UNSUPPORTED;
+    if (n_win > 1024) return CSA_ERR_UNSUPPORTED;
     if (n_win > 0 && W > 0 && (!win_kv || !aligned16(win_kv))) return CSA_ERR_INVALID_ARG;
     if (N + W >= (int64_t(1) << 31)) return CSA_ERR_UNSUPPORTED;   // one 32-bit id space
     const bool mixed = t == CSA_KV_FP8_BF16;   // q and out are bf16 then
@@ -305,8 +305,7 @@ int csa_sparse_mqa_swa(const void* q, const void* kv, const int32_t* idx, int64_
     if (rc != CSA_OK) return rc;
     if (k < 1) return CSA_ERR_INVALID_ARG;
     if (k > CSA_MAX_TOPK) return CSA_ERR_UNSUPPORTED;
-    if (mixed && (c != 512 || H % 64 != 0 || batch * T * (H / 64) > 256 || k > 1024 || N > 0xffffffffLL / (c + 64)))
-        return CSA_ERR_UNSUPPORTED;
+    if (mixed && c < 64) return CSA_ERR_UNSUPPORTED;   // the last 64 channels are the bf16 part
     if (batch == 0 || T == 0) return CSA_OK;
     if (!idx) return CSA_ERR_INVALID_ARG;
     const size_t need = csa_sparse_mqa_workspace_size(batch, T, H, c, k + n_win, t);
@@ -346,7 +345,9 @@ int hca_dense_mqa_swa(const void* q, const void* kv, int64_t batch, int64_t T, i
     if (n_win > 1024) return CSA_ERR_UNSUPPORTED;
     if (n_win > 0 && W > 0 && (!win_kv || !aligned16(win_kv))) return CSA_ERR_INVALID_ARG;
     if (N + W >= (int64_t(1) << 31)) return CSA_ERR_UNSUPPORTED;   // one 32-bit id space
-    int rc = check_mqa(q, kv, out, batch, T, N, H, c, scale, t);
+    const bool mixed = t == CSA_KV_FP8_BF16;   // q, out and window rows are bf16 then
+    if (mixed && c < 64) return CSA_ERR_UNSUPPORTED;
+    int rc = check_mqa(q, kv, out, batch, T, N, H, c, scale, mixed ? CSA_BF16 : t);
     if (rc != CSA_OK) return rc;
     if (m_prime < 1 || q_pos0 < 0) return CSA_ERR_INVALID_ARG;
     if (m_prime > CSA_MAX_RATIO) return CSA_ERR_UNSUPPORTED;

@@ -49,7 +49,20 @@ __device__ __forceinline__ int list_key(const int32_t* __restrict__ idx, int64_t
     return window_key(p, w, i - k, n_ent);
 }
 
-template <int DT, int CPL, bool DENSE>
+// Channel d of KV entry s of sequence b.  MIX: entries in the mixed storage (c - 64 e4m3 bytes,
+// then 64 bf16 values; c + 64 bytes per row), decoded exactly; else dtype DT like q.
+template <int DT, bool MIX>
+__device__ __forceinline__ float kv_elem(const void* __restrict__ kv, int64_t b, int64_t N, int c, int64_t s, int d) {
+    if constexpr (MIX) {
+        const uint8_t* row = static_cast<const uint8_t*>(kv) + (b * N + s) * (int64_t)(c + 64);
+        const int nf = c - 64;
+        return d < nf ? e4m3_to_f32(row[d]) : bf16_to_f32(reinterpret_cast<const uint16_t*>(row + nf)[d - nf]);
+    } else {
+        return load1<DT>(kv, (b * N + s) * c + d);
+    }
+}
+
+template <int DT, int CPL, bool DENSE, bool MIX = false>
 __global__ void __launch_bounds__(kGenWaves * kWave)
 mqa_generic(const void* __restrict__ q, const void* __restrict__ kv, const int32_t* __restrict__ idx, int64_t T,
             int64_t N, int H, int c, int k, float scale, int64_t q_pos0, int ratio, void* __restrict__ out,
@@ -74,7 +87,6 @@ mqa_generic(const void* __restrict__ q, const void* __restrict__ kv, const int32
     // dense: the visible entries 0 .. nvis-1, then the window slots (if any)
     const int64_t nvis = DENSE ? visible_entries(q_pos0 + t, ratio, N) : 0;
     const int64_t count = DENSE ? nvis + swa.n_win : (int64_t)k + swa.n_win;
-    const int64_t kvbase = b * N * c;
 
     for (int64_t r0 = 0; r0 < count; r0 += kKeyBatch) {
         int64_t sidx[kKeyBatch];
@@ -98,7 +110,7 @@ mqa_generic(const void* __restrict__ q, const void* __restrict__ kv, const int32
             for (int j = 0; j < CPL; ++j) {
                 const int d = lane + kWave * j;
                 kvv[u][j] = !(ok[u] && d < c) ? 0.f
-                            : sidx[u] < N ? load1<DT>(kv, kvbase + sidx[u] * c + d)
+                            : sidx[u] < N ? kv_elem<DT, MIX>(kv, b, N, c, sidx[u], d)
                                           : load1<DT>(swa.kv, (b * swa.W + sidx[u] - N) * c + d);
                 part[u] = fmaf(qv[j], kvv[u][j], part[u]);
             }
@@ -127,7 +139,7 @@ mqa_generic(const void* __restrict__ q, const void* __restrict__ kv, const int32
     }
 }
 
-template <int DT, bool DENSE>
+template <int DT, bool DENSE, bool MIX = false>
 int launch_generic(const void* q, const void* kv, const int32_t* idx, int64_t batch, int64_t T, int64_t N, int H, int c,
                    int k, float scale, int64_t q_pos0, int ratio, void* out, const float* sink, const SwaArgs& swa,
                    hipStream_t stream) {
@@ -137,7 +149,7 @@ int launch_generic(const void* q, const void* kv, const int32_t* idx, int64_t ba
     const dim3 grid((unsigned)rows, (unsigned)((H + kGenWaves - 1) / kGenWaves));
 #define CSA_LAUNCH_CPL(C)                                                                                          \
     if (cpl <= C) {                                                                                                \
-        hipLaunchKernelGGL((mqa_generic<DT, C, DENSE>), grid, dim3(kGenWaves * kWave), 0, stream, q, kv, idx, T, N, H, \
+        hipLaunchKernelGGL((mqa_generic<DT, C, DENSE, MIX>), grid, dim3(kGenWaves * kWave), 0, stream, q, kv, idx, T, N, H, \
                            c, k, scale, q_pos0, ratio, out, sink, swa);                                            \
         return 0;                                                                                                  \
     }
@@ -1139,12 +1151,13 @@ int launch_sparse_mqa(const void* q, const void* kv, const int32_t* idx, int64_t
     if (batch == 0 || T == 0) return 0;
     const int kt = k + swa.n_win;   // keys per row's list: the selected entries, then the window
     if (t == DT_KV_FP8_BF16) {
-        if (swa.n_win > 0) return -2;   // the window's raw rows are bf16: not on this path
-        // mixed-precision KV rows: the warp-specialised kernel only (decode shapes)
+        // mixed-precision KV rows: the warp-specialised kernel for decode shapes without a
+        // window, the generic kernel (bf16 q and window rows) for every other shape
         const int64_t rows = batch * T;
-        if (c != kMC || H % kMHeadsWG != 0 || N < 0 || N > 0xffffffffLL / (kMC + 64) || k > kMIdsLds ||
-            rows * (H / kMHeadsWG) > kMFillWGs)
-            return -2;
+        if (swa.n_win > 0 || c != kMC || H % kMHeadsWG != 0 || N < 1 || N > 0xffffffffLL / (kMC + 64) ||
+            k > kMIdsLds || rows * (H / kMHeadsWG) > kMFillWGs)
+            return launch_generic<DT_BF16, false, true>(q, kv, idx, batch, T, N, H, c, k, scale, 0, 1, out, sink, swa,
+                                                        stream);
         const int ks = mqa_splits(rows, H, k);
         const int kps = ((k + ks - 1) / ks + kMBlk - 1) / kMBlk * kMBlk;
         const int64_t units = ((rows + 7) / 8) * 8 * (H / kMHeadsWG) * ks;
@@ -1224,6 +1237,9 @@ int launch_dense_mqa(const void* q, const void* kv, int64_t batch, int64_t T, in
                            q_pos0, ratio, static_cast<uint16_t*>(out), nullptr, nullptr, sink, swa);
         return 0;
     }
+    if (t == DT_KV_FP8_BF16)   // mixed-precision entries (bf16 q, output and window rows)
+        return launch_generic<DT_BF16, true, true>(q, kv, nullptr, batch, T, N, H, c, 0, scale, q_pos0, ratio, out,
+                                                   sink, swa, stream);
     if (t == DT_F32)
         return launch_generic<DT_F32, true>(q, kv, nullptr, batch, T, N, H, c, 0, scale, q_pos0, ratio, out, sink, swa,
                                             stream);

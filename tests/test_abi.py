@@ -177,17 +177,16 @@ def test_mqa_rejects_bad_arguments(L):
     assert L.csa_sparse_mqa(A, A, A, 32, 1, 32768, 128, 512, 1024, 0.05, 1, A, None, 0, None) == WORKSPACE
     assert L.csa_sparse_mqa(A, A, A, 32, 1, 32768, 128, 512, 1024, 0.05, 1, A, A, need - 1, None) == WORKSPACE
     assert L.csa_sparse_mqa_workspace_size(1, 8192, 64, 512, 512, 1) == 0   # prefill: no split
-    # mixed fp8 / bf16 KV rows (t = 4): decode shapes only (c = 512, H % 64 == 0, at most 256
-    # (query, 64-head) units, k <= 1024); the split workspace is sized as for bf16
+    # mixed fp8 / bf16 KV rows (t = 4): any shape whose rows hold the 64 bf16 channels (c >= 64);
+    # the split workspace is sized as for bf16 (every call below fails a host-side check)
     mix = 4
     assert L.csa_sparse_mqa_workspace_size(32, 1, 128, 512, 1024, mix) == need
     assert L.csa_sparse_mqa(A, A, A, 32, 1, 32768, 128, 512, 1024, 0.05, mix, A, None, 0, None) == WORKSPACE
-    for args in [(2, 1, 100, 64, 256, 64), (2, 1, 100, 96, 512, 64), (257, 1, 100, 64, 512, 64),
-                 (2, 1, 100, 64, 512, 2048), (1, 1, 100, 64, 512, 1025)]:
-        b_, t_, n_, h_, c_, k_ = args
-        assert L.csa_sparse_mqa(A, A, A, b_, t_, n_, h_, c_, k_, 0.05, mix, A, A, 1 << 30, None) == UNSUPPORTED
-    assert L.csa_sparse_mqa(A, A, A, 1, 1, 1 << 23, 64, 512, 64, 0.05, mix, A, A, 1 << 30, None) == UNSUPPORTED
+    assert L.csa_sparse_mqa(A, A, A, 2, 1, 100, 64, 56, 64, 0.05, mix, A, A, 1 << 30, None) == UNSUPPORTED
+    assert L.csa_sparse_mqa(A, A, A, 2, 1, 100, 64, 512, 4096, 0.05, mix, A, A, 1 << 30, None) == UNSUPPORTED
     assert L.csa_sparse_mqa(A, MIS, A, 1, 1, 100, 64, 512, 64, 0.05, mix, A, A, 1 << 30, None) == INVALID
+    assert L.hca_dense_mqa_swa(A, A, 1, 4, 0, 8, 4, 56, 128, 0.1, None, None, 0, 0, 0, mix, A, None) == UNSUPPORTED
+    assert L.hca_dense_mqa_swa(A, MIS, 1, 4, 0, 8, 4, 512, 128, 0.1, None, None, 0, 0, 0, mix, A, None) == INVALID
     # sink logits ([H] fp32): 4-byte aligned or NULL
     MIS2 = 0x10002
     assert L.csa_sparse_mqa_sink(A, A, A, 1, 4, 64, 4, 64, 8, 0.125, MIS2, 0, A, None, 0, None) == INVALID
@@ -200,7 +199,23 @@ def test_mqa_rejects_bad_arguments(L):
     assert sw(A, A, A, 1, 4, 64, 4, 64, 8, 0.125, None, A, 16, 0, 0, 2048, 0, A, None, 0, None) == UNSUPPORTED
     assert sw(A, A, A, 1, 4, 64, 4, 64, 8, 0.125, None, None, 16, 0, 0, 8, 0, A, None, 0, None) == INVALID
     assert sw(A, A, A, 1, 4, 64, 4, 64, 8, 0.125, None, MIS, 16, 0, 0, 8, 0, A, None, 0, None) == INVALID
-    assert sw(A, A, A, 1, 1, 100, 64, 512, 64, 0.05, None, A, 16, 0, 0, 8, mix, A, A, 1 << 30, None) == UNSUPPORTED
+    assert sw(A, A, A, 1, 1, 100, 64, 48, 64, 0.05, None, A, 16, 0, 0, 8, mix, A, A, 1 << 30, None) == UNSUPPORTED
+    # the dense attention's window: the same argument rules
+    dw = L.hca_dense_mqa_swa   # q, kv, batch, T, q_pos0, N, H, c, m', scale, sink, win, W, wp0, n_win, t, out, st
+    assert dw(A, A, 1, 4, 0, 8, 4, 64, 128, 0.1, None, A, 16, 0, -1, 0, A, None) == INVALID
+    assert dw(A, A, 1, 4, 0, 8, 4, 64, 128, 0.1, None, A, 16, 0, 2048, 0, A, None) == UNSUPPORTED
+    assert dw(A, A, 1, 4, 0, 8, 4, 64, 128, 0.1, None, None, 16, 0, 8, 0, A, None) == INVALID
+    assert dw(A, A, 1, 4, 0, 8, 4, 64, 128, 0.1, None, MIS, 16, 0, 8, 0, A, None) == INVALID
+    assert dw(A, A, 1, 4, -1, 8, 4, 64, 128, 0.1, None, A, 16, 0, 8, 0, A, None) == INVALID
+    assert dw(A, A, 0, 4, 0, 8, 4, 64, 128, 0.1, None, None, 0, 0, 0, 0, A, None) == OK
+    # the HCA decode-step compression: block inside the cache, state pointers, dtypes
+    hs = L.hca_compress_step   # C, Z, B, batch, block, m', c, in_t, cache, rows, out_t, stream
+    assert hs(A, A, A, 1, 5, 128, 64, 0, A, 5, 0, None) == INVALID
+    assert hs(None, A, A, 1, 2, 128, 64, 0, A, 5, 0, None) == INVALID
+    assert hs(A, A, A, 1, 2, 128, 60, 0, A, 5, 0, None) == UNSUPPORTED
+    assert hs(A, A, A, 1, 2, 128, 64, 2, A, 5, 0, None) == UNSUPPORTED   # fp8 streams are no input
+    assert hs(A, MIS, A, 1, 2, 128, 64, 0, A, 5, 2, None) == INVALID
+    assert hs(None, None, None, 0, 2, 128, 64, 0, None, 5, 0, None) == OK
     assert sw(A, A, A, 0, 4, 64, 4, 64, 8, 0.125, None, None, 0, 0, 0, 0, 0, A, None, 0, None) == OK
     # partial RoPE: d even, 2 <= d <= min(c, 128), base > 1, fp32 / bf16 rows
     r = L.csa_rope
@@ -212,7 +227,7 @@ def test_mqa_rejects_bad_arguments(L):
     assert r(MIS, 1, 4, 64, 512, 64, 0, 1, 10000.0, 0, 1, None) == INVALID
     assert r(None, 0, 4, 64, 512, 64, 0, 1, 10000.0, 0, 1, None) == OK
     g = L.hca_dense_mqa
-    assert g(A, A, 1, 4, 0, 8, 64, 512, 128, 0.125, mix, A, None) == UNSUPPORTED
+    assert g(A, A, 1, 4, 0, 8, 64, 40, 128, 0.125, mix, A, None) == UNSUPPORTED   # mixed rows need c >= 64
     assert g(A, A, 1, 4, 0, 8, 4, 64, 0, 0.125, 0, A, None) == INVALID
     assert g(A, A, 1, 4, -5, 8, 4, 64, 128, 0.125, 0, A, None) == INVALID
     assert g(A, MIS, 1, 4, 0, 8, 4, 64, 128, 0.125, 0, A, None) == INVALID

@@ -320,6 +320,8 @@ MIXED_KV_CASES = [  # batch, T, N, H, k  (c = 512; KV rows: 448 fp8 channels, 64
     (32, 4, 1500, 128, 1024),    # 256 units, one key range each: 32 blocks per workgroup
     (3, 1, 700, 64, 1024),       # fewer entries than k: pads
     (1, 1, 0, 64, 40),           # no entries at all: zeros
+    (1, 40, 900, 64, 100),       # prefill-shaped rows: the vector-ALU kernel
+    (2, 2, 600, 48, 64),         # heads off the 64-head tiling: the vector-ALU kernel
 ]
 
 
@@ -514,6 +516,41 @@ def test_hca_compress_step_matches_whole_sequence(dt):
     assert not cache[:, nb:].any()
     ref = oracle.hca_compress(C, Z, B, mp, in_dtype=dt, out_dtype=dt)
     out_tol(dt)(from_dev(cache[:, :nb]), ref, "hca compress step")
+
+
+MIXED_OTHER_CASES = [  # kind, batch, T, q_pos0, N, H, k (or m'), W, win_pos0, n_win
+    ("sparse_window", 2, 1, 131072, 3000, 128, 1024, 128, 131072 - 127, 128),   # decode shape + window
+    ("sparse_window", 1, 30, 200, 400, 64, 64, 230, 0, 32),                     # prefill chunk + window
+    ("dense", 1, 20, 128 * 30 - 10, 30, 64, 128, 0, 0, 0),
+    ("dense_window", 2, 9, 128 * 6 - 4, 7, 64, 128, 40, 128 * 6 - 30, 16),
+]
+
+
+@pytest.mark.parametrize("case", MIXED_OTHER_CASES, ids=lambda c: "%s_b%d_T%d_p%d_N%d_H%d_k%d_W%d_w%d_n%d" % c)
+def test_mixed_kv_rows_on_every_attention(case):
+    """Mixed fp8/bf16 KV rows (the notes page §1.3: RoPE channels bf16, the rest fp8) with the
+    window branch and on HCA's dense attention, against the oracle on the decoded rows."""
+    kind, batch, T, p0, N, H, k, W, wp0, n_win = case
+    c = 512
+    say(f"mixed KV rows: {case}")
+    sd = 2100 + N
+    q = draw(sd, 1, (batch, T, H, c), BF16)
+    kvm = rng.normal(sd, 2, (batch, N, c), rng.KV_FP8_BF16)
+    kvd = oracle.decode_kv_fp8_bf16(kvm, c)
+    kv_dev = csa.KVFp8Bf16(torch.from_numpy(kvm).cuda(), c)
+    scale = 1.0 / np.sqrt(c)
+    wkv = draw(sd, 3, (batch, max(W, 1), c), BF16)[:, :W]
+    if kind == "sparse_window":
+        idx = _distinct_ids(np.random.RandomState(sd), batch, T, N, k)
+        ref = oracle.sparse_mqa(q, kvd, idx, scale, dtype=BF16, window=(wkv, wp0, p0, n_win))
+        got = csa.csa_sparse_mqa(to_dev(q, BF16), kv_dev, torch.from_numpy(idx).cuda(), scale,
+                                 window=(to_dev(np.ascontiguousarray(wkv), BF16), wp0, p0, n_win))
+    else:
+        win = (wkv, wp0, n_win) if kind == "dense_window" else None
+        ref = oracle.hca_dense_mqa(q, kvd, k, scale, q_pos0=p0, dtype=BF16, window=win)
+        got = csa.hca_dense_mqa(to_dev(q, BF16), kv_dev, p0, k, scale,
+                                window=None if win is None else (to_dev(np.ascontiguousarray(wkv), BF16), wp0, n_win))
+    out_tol(BF16)(from_dev(got), ref, f"{kind} on mixed rows")
 
 
 @pytest.mark.parametrize("dt", [F32, BF16])
