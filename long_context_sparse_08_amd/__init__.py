@@ -125,7 +125,7 @@ def _qk(qI, kI):
         if not (isinstance(qI, MXFP4) and isinstance(kI, MXFP4)):
             raise TypeError("qI and kI must both be MXFP4")
         return qI.data, kI.data, qI.shape, kI.shape, CSA_MXFP4
-    assert _dt(qI) == _dt(kI)
+    _need(_dt(qI) == _dt(kI), "qI and kI must have one dtype")
     return qI, kI, tuple(qI.shape), tuple(kI.shape), _dt(qI)
 
 
@@ -145,10 +145,17 @@ def _dev(*ts):
 
 
 def _check_out(t, shape, dtype, what):
-    """A caller-supplied buffer must have exactly the shape and dtype the call writes (the C
-    ABI sees only its address)."""
+    """A caller-supplied buffer must have exactly the shape and dtype the call reads or writes
+    (the C ABI sees only its address)."""
+    if t is None:
+        return
     if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
         raise ValueError(f"{what}: expected {dtype} {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+
+
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
 
 
 def _stream(dev) -> int:
@@ -164,27 +171,35 @@ def version() -> int:
 
 
 def csa_compress(Ca, Cb, Za, Zb, Ba, Bb, m: int, out=None, out_dtype=None):
-    """[batch, n, c] streams (f32/bf16), [m, c] fp32 biases -> [batch, n // m, c]."""
-    dev = _dev(Ca, Cb, Za, Zb, Ba, Bb, out)
+    """[batch, n, c] streams (f32/bf16), [m, c] fp32 biases -> [batch, n // m, c] (f32, bf16 or
+    fp8 e4m3 as uint8)."""
+    _need(Ca.dim() == 3, "streams are [batch, n, c]")
     batch, n, c = Ca.shape
-    for t in (Cb, Za, Zb):
-        assert t.shape == Ca.shape and t.dtype == Ca.dtype
-    assert Ba.dtype == torch.float32 and Bb.dtype == torch.float32
+    for nm, t in (("Cb", Cb), ("Za", Za), ("Zb", Zb)):
+        _check_out(t, Ca.shape, Ca.dtype, nm)
+    _check_out(Ba, (m, c), torch.float32, "Ba")
+    _check_out(Bb, (m, c), torch.float32, "Bb")
+    if out is not None:
+        _need(tuple(out.shape) == (batch, n // m, c), f"out: expected shape {(batch, n // m, c)}")
+    dev = _dev(Ca, Cb, Za, Zb, Ba, Bb, out)
     if out is None:
         out = torch.empty((batch, n // m, c), dtype=out_dtype or Ca.dtype, device=dev)
-    assert out.shape == (batch, n // m, c)
     _check("csa_compress", lib.csa_compress(_p(Ca), _p(Cb), _p(Za), _p(Zb), _p(Ba), _p(Bb), batch, n, m, c, _dt(Ca),
                                             _p(out), _dt(out), _stream(dev)))
     return out
 
 
 def hca_compress(C, Z, B, m_prime: int, out=None, out_dtype=None):
-    dev = _dev(C, Z, B, out)
+    """[batch, n, c] stream and scores, [m', c] fp32 biases -> [batch, n // m', c]."""
+    _need(C.dim() == 3, "streams are [batch, n, c]")
     batch, n, c = C.shape
-    assert Z.shape == C.shape and Z.dtype == C.dtype and B.dtype == torch.float32
+    _check_out(Z, C.shape, C.dtype, "Z")
+    _check_out(B, (m_prime, c), torch.float32, "B")
+    if out is not None:
+        _need(tuple(out.shape) == (batch, n // m_prime, c), f"out: expected shape {(batch, n // m_prime, c)}")
+    dev = _dev(C, Z, B, out)
     if out is None:
         out = torch.empty((batch, n // m_prime, c), dtype=out_dtype or C.dtype, device=dev)
-    assert out.shape == (batch, n // m_prime, c)
     _check("hca_compress", lib.hca_compress(_p(C), _p(Z), _p(B), batch, n, m_prime, c, _dt(C), _p(out), _dt(out),
                                             _stream(dev)))
     return out
@@ -204,10 +219,16 @@ def csa_index_topk(qI, w, kI, q_pos0: int, m: int, k: int, idx=None, sel_scores=
     """qI [batch, T, H_I, c_I], w [batch, T, H_I] fp32, kI [batch, N, c_I] -> (idx, sel_scores).
     qI and kI: tensors of one dtype (f32, bf16, e4m3 as uint8) or both MXFP4."""
     qt, kt, qs, ks, qk_dt = _qk(qI, kI)
-    dev = _dev(qt, w, kt, idx, sel_scores, workspace)
+    _need(len(qs) == 4 and len(ks) == 3, "qI is [batch, T, H_I, c_I], kI [batch, N, c_I]")
     batch, T, H_I, c_I = qs
     N = ks[1]
-    assert ks == (batch, N, c_I) and w.shape == (batch, T, H_I) and w.dtype == torch.float32
+    _need(ks == (batch, N, c_I), f"kI: expected shape {(batch, N, c_I)}")
+    _check_out(w, (batch, T, H_I), torch.float32, "w")
+    _check_out(idx, (batch, T, k), torch.int32, "idx")
+    _check_out(sel_scores, (batch, T, k), torch.float32, "sel_scores")
+    if workspace is not None:
+        _need(workspace.dtype == torch.uint8 and workspace.dim() == 1, "workspace is a flat uint8 tensor")
+    dev = _dev(qt, w, kt, idx, sel_scores, workspace)
     if idx is None:
         idx = torch.empty((batch, T, k), dtype=torch.int32, device=dev)
     if sel_scores is None and want_scores:
@@ -226,12 +247,16 @@ def csa_index_topk_noalloc(qI, w, kI, q_pos0: int, m: int, k: int, idx=None, sel
     (for callers that cannot allocate; calls on one GPU must not overlap).  Runs on the
     tensors' device, which must be torch's current device."""
     qt, kt, qs, ks, qk_dt = _qk(qI, kI)
+    _need(len(qs) == 4 and len(ks) == 3, "qI is [batch, T, H_I, c_I], kI [batch, N, c_I]")
+    batch, T, H_I, c_I = qs
+    N = ks[1]
+    _need(ks == (batch, N, c_I), f"kI: expected shape {(batch, N, c_I)}")
+    _check_out(w, (batch, T, H_I), torch.float32, "w")
+    _check_out(idx, (batch, T, k), torch.int32, "idx")
+    _check_out(sel_scores, (batch, T, k), torch.float32, "sel_scores")
     dev = _dev(qt, w, kt, idx, sel_scores)
     if dev.index != torch.cuda.current_device():
         raise ValueError("csa_index_topk_noalloc runs on the current device: call torch.cuda.set_device first")
-    batch, T, H_I, c_I = qs
-    N = ks[1]
-    assert ks == (batch, N, c_I) and w.shape == (batch, T, H_I) and w.dtype == torch.float32
     if idx is None:
         idx = torch.empty((batch, T, k), dtype=torch.int32, device=dev)
     if sel_scores is None and want_scores:
@@ -245,10 +270,15 @@ def csa_index_topk_noalloc(qI, w, kI, q_pos0: int, m: int, k: int, idx=None, sel
 
 
 def csa_index_scores(qI, w, kI, q_pos0: int, m: int, scores=None):
+    """The indexer scores alone: [batch, T, N] fp32, -inf where the entry is not visible."""
     qt, kt, qs, ks, qk_dt = _qk(qI, kI)
-    dev = _dev(qt, w, kt, scores)
+    _need(len(qs) == 4 and len(ks) == 3, "qI is [batch, T, H_I, c_I], kI [batch, N, c_I]")
     batch, T, H_I, c_I = qs
     N = ks[1]
+    _need(ks == (batch, N, c_I), f"kI: expected shape {(batch, N, c_I)}")
+    _check_out(w, (batch, T, H_I), torch.float32, "w")
+    _check_out(scores, (batch, T, N), torch.float32, "scores")
+    dev = _dev(qt, w, kt, scores)
     if scores is None:
         scores = torch.empty((batch, T, N), dtype=torch.float32, device=dev)
     _check("csa_index_scores", lib.csa_index_scores(_p(qt), _p(w), _p(kt), batch, T, q_pos0, N, H_I, c_I, m, qk_dt,
@@ -259,9 +289,12 @@ def csa_index_scores(qI, w, kI, q_pos0: int, m: int, scores=None):
 def csa_topk(scores, q_pos0: int, m: int, k: int, idx=None, sel_scores=None, workspace=None,
              want_scores: bool = True):
     """scores [batch, T, N] fp32 (N % 4 == 0 for 16-byte rows) -> (idx, sel_scores)."""
-    dev = _dev(scores, idx, sel_scores, workspace)
+    _need(scores.dim() == 3 and scores.dtype == torch.float32, "scores are [batch, T, N] fp32")
     batch, T, N = scores.shape
-    assert scores.dtype == torch.float32
+    _need(N % 4 == 0, "score rows must hold a multiple of 4 entries (16-byte rows)")
+    _check_out(idx, (batch, T, k), torch.int32, "idx")
+    _check_out(sel_scores, (batch, T, k), torch.float32, "sel_scores")
+    dev = _dev(scores, idx, sel_scores, workspace)
     if idx is None:
         idx = torch.empty((batch, T, k), dtype=torch.int32, device=dev)
     if sel_scores is None and want_scores:
@@ -287,7 +320,8 @@ def mqa_workspace_for(q: torch.Tensor, k: int, dtype: int | None = None):
 def _sink(sink, H, dev):
     if sink is None:
         return None
-    assert sink.dtype == torch.float32 and tuple(sink.shape) == (H,) and sink.device == dev and sink.is_contiguous()
+    _check_out(sink, (H,), torch.float32, "sink")
+    _need(sink.device == dev and sink.is_contiguous(), "sink: a contiguous tensor on the call's device")
     return sink
 
 
@@ -297,26 +331,28 @@ def csa_sparse_mqa(q, kv, idx, scale: float, out=None, workspace=None, sink=None
     window: optional (win_kv [batch, W, c], win_pos0, q_pos0, n_win), the sliding-window branch."""
     mixed = isinstance(kv, KVFp8Bf16)
     kvt = kv.data if mixed else kv
-    dev = _dev(q, kvt, idx, out, workspace)
+    _need(q.dim() == 4 and idx.dim() == 3, "q is [batch, T, H, c], idx [batch, T, k]")
     batch, T, H, c = q.shape
     N = kv.shape[1]
     k = idx.shape[2]
     if mixed:
-        assert q.dtype == torch.bfloat16 and kv.c == c and kvt.shape[0] == batch
+        _need(q.dtype == torch.bfloat16 and kv.c == c and kvt.shape[0] == batch, "mixed KV rows take bf16 q of width c")
         dt = CSA_KV_FP8_BF16
     else:
-        assert kv.shape == (batch, N, c) and kv.dtype == q.dtype
+        _check_out(kv, (batch, N, c), q.dtype, "kv")
         dt = _dt(q)
-    assert idx.dtype == torch.int32 and idx.shape == (batch, T, k)
-    if out is None:
-        out = torch.empty_like(q)
+    _check_out(idx, (batch, T, k), torch.int32, "idx")
     _check_out(out, (batch, T, H, c), q.dtype, "out")
     wkv, W, wp0, qp0, n_win = None, 0, 0, 0, 0
     if window is not None:
         wkv, wp0, qp0, n_win = window
-        assert wkv.dtype == q.dtype and wkv.shape[0] == batch and wkv.shape[2] == c
-        _dev(q, wkv)
+        _need(wkv.dim() == 3, "win_kv is [batch, W, c]")
+        _check_out(wkv, (batch, wkv.shape[1], c), q.dtype, "win_kv")
         W = wkv.shape[1]
+    _check_out(sink, (H,), torch.float32, "sink")
+    dev = _dev(q, kvt, idx, out, workspace, wkv)
+    if out is None:
+        out = torch.empty_like(q)
     if workspace is None:
         workspace = mqa_workspace_for(q, k + n_win, dt)
     ws_bytes = 0 if workspace is None else workspace.numel()
@@ -330,10 +366,16 @@ def csa_sparse_mqa(q, kv, idx, scale: float, out=None, workspace=None, sink=None
 def csa_compress_step(Ca, Cb, Za, Zb, Ba, Bb, block: int, cache):
     """Decode-step CSA compression: the state streams [batch, 2m, c] (blocks block-1 and block;
     [batch, m, c] when block == 0) -> row `block` of cache [batch, rows, c], in place."""
-    dev = _dev(Ca, Cb, Za, Zb, Ba, Bb, cache)
+    _need(Ca.dim() == 3 and Ba.dim() == 2 and cache.dim() == 3, "state [batch, rows, c], biases [m, c], cache 3-d")
     batch, ns, c = Ca.shape
     m = Ba.shape[0]
-    assert ns == (2 * m if block > 0 else m) and cache.shape[0] == batch and cache.shape[2] == c
+    _need(ns == (2 * m if block > 0 else m), f"state: {2 * m if block > 0 else m} tokens per sequence")
+    for nm, t in (("Cb", Cb), ("Za", Za), ("Zb", Zb)):
+        _check_out(t, Ca.shape, Ca.dtype, nm)
+    _check_out(Ba, (m, c), torch.float32, "Ba")
+    _check_out(Bb, (m, c), torch.float32, "Bb")
+    _need(cache.shape[0] == batch and cache.shape[2] == c and 0 <= block < cache.shape[1], "cache: row `block` of [batch, rows, c]")
+    dev = _dev(Ca, Cb, Za, Zb, Ba, Bb, cache)
     _check("csa_compress_step", lib.csa_compress_step(_p(Ca), _p(Cb), _p(Za), _p(Zb), _p(Ba), _p(Bb), batch, block, m, c,
                                                       _dt(Ca), _p(cache), cache.shape[1], _dt(cache), _stream(dev)))
     return cache
@@ -359,24 +401,26 @@ def hca_dense_mqa(q, kv, q_pos0: int, m_prime: int, scale: float, out=None, sink
     sliding-window branch over the raw rows at positions p - n_win + 1 .. p."""
     mixed = isinstance(kv, KVFp8Bf16)
     kvt = kv.data if mixed else kv
-    dev = _dev(q, kvt, out)
+    _need(q.dim() == 4, "q is [batch, T, H, c]")
     batch, T, H, c = q.shape
     N = kv.shape[1]
     if mixed:
-        assert q.dtype == torch.bfloat16 and kv.c == c and kvt.shape[0] == batch
+        _need(q.dtype == torch.bfloat16 and kv.c == c and kvt.shape[0] == batch, "mixed KV rows take bf16 q of width c")
         dt = CSA_KV_FP8_BF16
     else:
-        assert kv.shape == (batch, N, c) and kv.dtype == q.dtype
+        _check_out(kv, (batch, N, c), q.dtype, "kv")
         dt = _dt(q)
-    if out is None:
-        out = torch.empty_like(q)
     _check_out(out, (batch, T, H, c), q.dtype, "out")
     wkv, W, wp0, n_win = None, 0, 0, 0
     if window is not None:
         wkv, wp0, n_win = window
-        assert wkv.dtype == q.dtype and wkv.shape[0] == batch and wkv.shape[2] == c
-        _dev(q, wkv)
+        _need(wkv.dim() == 3, "win_kv is [batch, W, c]")
+        _check_out(wkv, (batch, wkv.shape[1], c), q.dtype, "win_kv")
         W = wkv.shape[1]
+    _check_out(sink, (H,), torch.float32, "sink")
+    dev = _dev(q, kvt, out, wkv)
+    if out is None:
+        out = torch.empty_like(q)
     sk = _sink(sink, H, dev)
     _check("hca_dense_mqa", lib.hca_dense_mqa_swa(_p(q), _p(kvt), batch, T, q_pos0, N, H, c, m_prime, float(scale),
                                                   _p(sk), _p(wkv), W, wp0, n_win, dt, _p(out), _stream(dev)))
@@ -386,10 +430,12 @@ def hca_dense_mqa(q, kv, q_pos0: int, m_prime: int, scale: float, out=None, sink
 def hca_compress_step(C, Z, B, block: int, cache):
     """Decode-step HCA compression: the state streams [batch, m', c] (the raw tokens of block
     `block`) -> row `block` of cache [batch, rows, c], in place."""
-    dev = _dev(C, Z, B, cache)
+    _need(C.dim() == 3 and cache.dim() == 3, "state [batch, m', c], cache [batch, rows, c]")
     batch, mp, c = C.shape
-    assert Z.shape == C.shape and Z.dtype == C.dtype and B.dtype == torch.float32 and tuple(B.shape) == (mp, c)
-    assert cache.dim() == 3 and cache.shape[0] == batch and cache.shape[2] == c
+    _check_out(Z, C.shape, C.dtype, "Z")
+    _check_out(B, (mp, c), torch.float32, "B")
+    _need(cache.shape[0] == batch and cache.shape[2] == c and 0 <= block < cache.shape[1], "cache: row `block` of [batch, rows, c]")
+    dev = _dev(C, Z, B, cache)
     _check("hca_compress_step", lib.hca_compress_step(_p(C), _p(Z), _p(B), batch, block, mp, c, _dt(C), _p(cache),
                                                       cache.shape[1], _dt(cache), _stream(dev)))
     return cache

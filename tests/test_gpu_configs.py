@@ -4,6 +4,8 @@ objects (and therefore the same kernel launches) the benchmark times.
 cfg0 runs the oracle on everything.  The large configs run the GPU at full size and the
 oracle on sampled query rows / sequences (every stage of the oracle chain starts from the
 generator's bytes: the oracle compresses, scores, selects and attends on its own)."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -152,9 +154,18 @@ def test_cfg2_csa_decode_128k_mxfp4_sampled():
     sc8 = oracle.index_scores(h8["qI"][seqs], h8["w"][seqs], h8["kI"][seqs], f8.m, q_pos0=f8.q_pos0, qk_dtype=FP8)
     idx8, _ = oracle.topk(sc8, f8.m, f8.k, q_pos0=f8.q_pos0)
     a, b = gidx.reshape(-1, cfg.k), idx8.reshape(-1, f8.k)
-    recall = np.mean([len(set(a[r]) & set(b[r])) / f8.k for r in range(a.shape[0])])
-    say(f"  MXFP4 selection keeps {recall:.4f} of the fp8 selection")
-    assert recall > 0.5
+    per_seq = np.array([len(set(a[r]) & set(b[r])) / f8.k for r in range(a.shape[0])])
+    say(f"  MXFP4 selection keeps {per_seq.mean():.4f} of the fp8 selection (per sequence {per_seq})")
+    # the oracle's value for these sequences (tests/golden/mxfp4_recall.py over all 32 of them):
+    # the GPU's MXFP4 selection may differ from the oracle's only at near-ties of the cut
+    golden = {}
+    for line in open(os.path.join(os.path.dirname(__file__), "golden", "mxfp4_recall_cfg2.txt")):
+        if line and not line.startswith("#"):
+            key, *vals = line.split()
+            golden[key] = [float(v) for v in vals]
+    stored = np.array(golden["per_sequence"])[seqs]
+    say(f"  stored oracle recall for them: {stored}")
+    assert np.all(np.abs(per_seq - stored) <= 0.01)
 
 
 @pytest.mark.timeout(900)
@@ -175,7 +186,12 @@ def test_cfg3_hca_chunk_sampled():
     assert_abs_close(gkv, kv, 2e-2, "HCA KV (bf16)")
     say(f"  KV equal to oracle rounding: {np.mean(gkv == kv):.5f}")
     assert np.mean(gkv == kv) >= 0.999
-    rows = np.array([0, 1, 126, 127, 128, 2047, 2048, 4094, 4095])
+    # the chunk's ends, rows on both sides of every 512th visibility step (a query whose position
+    # completes an entry sees one more), and 40 rows drawn at random: 72 rows
+    edges = [r for b in range(127, cfg.T, 512) for r in (b - 1, b, b + 1) if 0 <= r < cfg.T]
+    rnd = np.random.RandomState(33).choice(cfg.T, 40, replace=False)
+    rows = np.unique(np.concatenate([[0, 1, 2047, 2048, 4094, 4095], edges, rnd]))
+    assert len(rows) >= 64
     qpos = cfg.q_pos0 + rows
     out = oracle.hca_dense_mqa(h["q"][:, rows], kv, cfg.m_prime, cfg.scale, dtype=cfg.dt, qpos=qpos)
     assert_abs_close(from_dev(pipe.out)[:, rows], out, 2e-2, "O")

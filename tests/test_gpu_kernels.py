@@ -218,6 +218,38 @@ def test_topk_bit_exact_on_the_gpu_scores(case):
     assert np.array_equal(sel, ref_sel.astype(np.float32).astype(np.float64))
 
 
+CSA_TOPK_CASES = [  # batch, T, q_pos0, N, k, integer-valued scores (ties)
+    (1, 6, 4 * 3000 - 9, 3000, 512, True),          # short rows: small workgroups
+    (2, 2, 4 * 20000 - 3, 20000, 1024, False),      # register-staged rows
+    (1, 5, 4 * 10000 - 17, 10000, 2048, True),      # rows staged in LDS (fewer than 8k entries)
+    (1, 5, 4 * 100000 - 17, 100000, 1024, False),   # rows past LDS staging, read from memory
+    (1, 4, 4 * 100000 - 9, 100000, 2048, True),     # the same with heavy ties
+    (1, 4, 4 * 300000 - 9, 300000, 1024, False),    # rows past 262144 entries: one-row kernel
+    (1, 2, 4 * 300000, 300000, 512, True),
+]
+
+
+@pytest.mark.parametrize("case", CSA_TOPK_CASES, ids=lambda c: "b%d_T%d_p%d_N%d_k%d_int%d" % c)
+def test_csa_topk_on_caller_scores(case):
+    """csa_topk (the selection alone, through the C ABI) on fp32 score rows the caller supplies,
+    bit-exact against the oracle's rule (score desc, index asc; ids ascending, -1 padded).
+    Rows of several lengths per call (consecutive query positions) reach every one-workgroup
+    selection kernel, including rows longer than 32768 and 262144 visible entries."""
+    batch, T, p0, N, k, integer = case
+    m = 4
+    say(f"csa_topk {case}")
+    r = np.random.RandomState(2300 + N + k)
+    if integer:
+        sc = r.randint(0, 40, size=(batch, T, N)).astype(np.float32)
+    else:
+        sc = r.standard_normal((batch, T, N)).astype(np.float32) * 30 + 100
+    ref_idx, ref_sel = oracle.topk(sc.astype(np.float64), m, k, q_pos0=p0)
+    idx, sel = csa.csa_topk(torch.from_numpy(sc).cuda(), p0, m, k)
+    idx, sel = from_dev(idx), from_dev(sel)
+    assert np.array_equal(idx, ref_idx)
+    assert np.array_equal(sel, ref_sel.astype(np.float32).astype(np.float64))
+
+
 # ------------------------------------------------------------------------------ MXFP4 indexer
 def _mxfp4_exact(r, rows, c):
     """MXFP4 storage (element bytes of every row, then the scales) of random E2M1 codes with
