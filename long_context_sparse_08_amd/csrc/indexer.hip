@@ -372,6 +372,7 @@ index_scores_prefill(const void* __restrict__ qI, const float* __restrict__ w, c
     constexpr int kLoadWaves = 32 / kRowsPerLoad;       // waves that stage a block (8 / 4)
     static_assert(kLoadWaves <= kPfWaves, "staging waves");
     __shared__ __attribute__((aligned(16))) uint8_t stg[2][32 * kPitch];
+    __shared__ __attribute__((aligned(16))) uint8_t qst[kPfWaves][H * kRowB];
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 5, n = lane & 31;
@@ -394,18 +395,43 @@ index_scores_prefill(const void* __restrict__ qI, const float* __restrict__ w, c
     const int64_t blk0 = (int64_t)chunk * cb;
     const int64_t blk1 = min(blk0 + cb, nblk_all);
     float* out = scores + row * ld;
-    if (write_invisible && tok)
-        for (int64_t s = max(nv, blk0 * 32) + lane; s < min(blk1 * 32, N); s += kWave) out[s] = -INFINITY;
     const int64_t bend = min(blk1, (nv_last + 31) / 32);
     const int nb = bend > blk0 ? (int)(bend - blk0) : 0;   // the same for the whole workgroup
-    if (nb == 0) return;
+    auto invisible = [&]() {   // -inf where the entry is not visible to this wave's query
+        if (write_invisible && tok)
+            for (int64_t s = max(nv, blk0 * 32) + lane; s < min(blk1 * 32, N); s += kWave) out[s] = -INFINITY;
+    };
+    if (nb == 0) {
+        invisible();
+        return;
+    }
 
-    // this wave's q (A operands) and the w of the heads its accumulator rows hold
+    // this wave's q (H rows of kRowB bytes) goes through the wave's own LDS region: loaded with
+    // wave-wide 16-byte loads that each cover 1 KB of consecutive bytes, then read back in the
+    // MFMA operand order (after the first barrier).  Loading the operand order straight from
+    // global memory makes each wave-wide load touch 64 cache lines, which the CU's address unit
+    // takes one line at a time.  16-byte chunk c of row r sits at chunk position c ^ s(r), so
+    // that the 16 lanes of a read phase (rows n .. n+15, one chunk) hit distinct banks.
+    auto qpos = [](int r, int c) {
+        return r * kRowB + ((c ^ (kRowB == 256 ? (r & 15) : ((r >> 1) & 7))) << 4);
+    };
+    {
+        constexpr int kQLoads = H * kRowB / 1024;
+        const uint8_t* qb = static_cast<const uint8_t*>(qI) + row * (int64_t)H * kRowB;
+        uint4 qv[kQLoads];
+#pragma unroll
+        for (int r = 0; r < kQLoads; ++r) qv[r] = *reinterpret_cast<const uint4*>(qb + 1024 * r + 16 * lane);
+#pragma unroll
+        for (int r = 0; r < kQLoads; ++r) {
+            const int o = 1024 * r + 16 * lane;
+            *reinterpret_cast<uint4*>(&qst[wid][qpos(o / kRowB, (o % kRowB) >> 4)]) = qv[r];
+        }
+    }
+    // the w of the heads this wave's accumulator rows hold
     typename O::Frag qa[MB];
     float wv[MB][16];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-        load_half_row<DT>(qI, row * H + 32 * mb + n, g, qa[mb], batch * T * H);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
             const float4 w4 = *reinterpret_cast<const float4*>(w + row * H + 32 * mb + 8 * q4 + 4 * g);
@@ -460,7 +486,16 @@ index_scores_prefill(const void* __restrict__ qI, const float* __restrict__ w, c
         rc = gload(2);
         *reinterpret_cast<uint4*>(&stg[0][srow * kPitch + scol]) = ra;
     }
+    // the -inf stores go out after the loads: vector memory operations complete in order, so
+    // stores issued first would hold up the first block's staging
+    invisible();
     __syncthreads();
+    // q operands: entry row 32 mb + n, channel half g (chunks g * kLoads .. g * kLoads + kLoads - 1)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < O::kLoads; ++j)
+            qa[mb].v[j] = *reinterpret_cast<const uint4*>(&qst[wid][qpos(32 * mb + n, g * O::kLoads + j)]);
     f32x16 acc0, acc1;
     float part = 0.f;   // 64 heads: block i's tile-0 sum, carried into step i+1
     // x: the accumulator step i writes first; y: the one holding the previous tile
