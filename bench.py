@@ -361,7 +361,7 @@ def main():
     w = work[wkey]
     peak, unit = peak_for(cfg, wkey, w["bound"])
     t_s = stage_ms[dom] * 1e-3
-    from long_context_sparse_08_amd.profiling import traffic_for
+    from long_context_sparse_08_amd.profiling import traffic_for, utilization_for
     tr = traffic_for(kernel, cfg.name)
     if w["bound"] == "hbm":
         achieved = w["bytes"] / t_s
@@ -372,6 +372,11 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved / 1e12, 1), "peak": peak / 1e12, "unit": unit,
                 "frac": round(achieved / peak, 4)}
     roof["traffic"] = None if tr is None else tr["traffic_bytes"]
+    # the matrix cores' busy time from committed hardware counters (rocprofv3 MfmaUtil), for a
+    # kernel bound by them; null when there is no summary for this kernel's current source
+    util = utilization_for(kernel, cfg.name)
+    if w["bound"] == "mfma":
+        roof["mfma_util_pct"] = None if util is None or "MfmaUtil" not in util else util["MfmaUtil"]
     roof["kernel"] = kernel
     roof["ms_per_launch"] = round(stage_ms[dom], 5)
     roof["algorithmic_bytes"] = int(w["bytes"])
@@ -404,6 +409,15 @@ def main():
         "stage_kernels": {k: v[1] for k, v in stages.items()},
         "step_roofline_frac": round(ideal / (ms * 1e-3), 4),
     }
+    # hardware counters of the stages' kernels from committed summaries (MfmaUtil etc.)
+    hw = {}
+    for n, (_, ks, wk) in stages.items():
+        if len(ks) == 1:
+            u = utilization_for(ks[0], cfg.name)
+            if u is not None:
+                hw[n] = u
+    if hw:
+        result["stage_counters"] = hw
     if with_compress:
         # the step above includes one compression every m steps; the same steps without it
         result["ms_per_step_without_compress"] = round(ms_plain, 5)

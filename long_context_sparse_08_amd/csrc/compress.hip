@@ -9,9 +9,13 @@
 //
 // Design (HBM-bound, ~1 flop per byte): each thread owns 8 consecutive channels (one
 // 16-byte bf16 load or two fp32 float4 loads per token and stream), so a wave reads whole
-// rows coalesced.  The softmax is computed online over chunks of 4 tokens (one rescale per
-// chunk, so ~1.25 exp per element).  Long HCA windows are split across the rows of a block
-// and merged through LDS so that enough loads are in flight per CU.
+// rows coalesced.  The softmax is computed online over chunks of CH tokens (one rescale per
+// chunk).  The loads in flight per CU set the speed, so registers (occupancy) matter more than
+// the rescale count: CSA windows (2m = 8 tokens at m = 4) take CH = 2 (94 registers, five waves
+// per SIMD: 0.89 ms for a 1M-token sequence, against 0.92 ms with CH = 4 at 128 registers, 1.23
+// ms with CH = 8 and 0.99 ms with CH = 1); the long HCA windows CH = 4 (~1.25 exp per element),
+// split across the rows of a block and merged through LDS so that enough loads are in flight
+// per CU.
 #include "device_common.h"
 #include "launch.h"
 
@@ -20,7 +24,6 @@ namespace csa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kChunk = 4;
 
 struct CompressArgs {
     const void* Ca;
@@ -37,7 +40,7 @@ struct CompressArgs {
     int64_t first, out_ld, out_off;
 };
 
-template <int DTI, int DTO>
+template <int DTI, int DTO, int CH>
 __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a, int G, int split, int epb) {
     __shared__ float sm[3][kThreads][8];
     const int tid = threadIdx.x;
@@ -62,10 +65,10 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a, int 
         const int u0 = part * per;
         const int u1 = min(W, u0 + per);
         const int64_t seq = b * a.n;
-        for (int u = u0; u < u1; u += kChunk) {
-            float z[kChunk][8], cv[kChunk][8];
+        for (int u = u0; u < u1; u += CH) {
+            float z[CH][8], cv[CH][8];
 #pragma unroll
-            for (int q = 0; q < kChunk; ++q) {
+            for (int q = 0; q < CH; ++q) {
                 const int uu = u + q;
                 const bool is_a = uu < m;
                 const bool ok = uu < u1 && (is_a || i > 0);
@@ -89,13 +92,13 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a, int 
             for (int e = 0; e < 8; ++e) {
                 float cm = z[0][e];
 #pragma unroll
-                for (int q = 1; q < kChunk; ++q) cm = fmaxf(cm, z[q][e]);
+                for (int q = 1; q < CH; ++q) cm = fmaxf(cm, z[q][e]);
                 const float nm = fmaxf(mx[e], cm);
                 if (nm == -INFINITY) continue;
                 const float r = exp2f(mx[e] - nm);
                 float s = sum[e] * r, ac = acc[e] * r;
 #pragma unroll
-                for (int q = 0; q < kChunk; ++q) {
+                for (int q = 0; q < CH; ++q) {
                     const float p = exp2f(z[q][e] - nm);
                     s += p;
                     ac = fmaf(p, cv[q][e], ac);
@@ -148,8 +151,12 @@ int launch(const CompressArgs& a, hipStream_t stream) {
     const int64_t entries = a.batch * (a.N - a.first);
     const int64_t blocks = (entries + epb - 1) / epb;
     if (blocks > 0x7fffffffLL) return -2;
-    hipLaunchKernelGGL((compress_kernel<DTI, DTO>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a, G, split,
-                       epb);
+    if (split == 1 && W <= 8)   // short (CSA) windows
+        hipLaunchKernelGGL((compress_kernel<DTI, DTO, 2>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a, G,
+                           split, epb);
+    else
+        hipLaunchKernelGGL((compress_kernel<DTI, DTO, 4>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a, G,
+                           split, epb);
     return 0;
 }
 

@@ -6,6 +6,13 @@
         --fetch <dir> --write <dir> --copy-fetch <dir> --copy-write <dir> --copy-bytes <B>
         --commands "<cmd1>" "<cmd2>" ... --out profiles/<name>.md
 
+    python -m long_context_sparse_08_amd.profiling utilization --kernel <substring> --source <csrc file>
+        --workload <name> --runs <dir> [<dir> ...] --commands "<cmd1>" ... --out profiles/<name>.md
+
+`utilization` records derived hardware counters of one kernel (rocprofv3's MfmaUtil, LdsUtil,
+LDSBankConflict, ...: the mean over its dispatches of each counter found in the --pmc runs),
+with the same source hash; `utilization_for` returns them while the source is unchanged.
+
 `counters` turns two --pmc runs of a workload (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch)
 into HBM bytes per launch of one kernel, each counter scaled by what it reads for a plain
 device-to-device copy of known size (the copy kernel runs in its own two --pmc runs).  The
@@ -43,6 +50,25 @@ def kernel_stats(path: str):
         rows.append((_short(r["Name"]), int(r["Calls"]), float(r["AverageNs"]), float(r["TotalDurationNs"])))
     rows.sort(key=lambda x: -x[3])
     return rows
+
+
+UTIL_MARK = "<!-- util-json: "
+
+
+def counter_means(run_dir: str, kernel_substr: str) -> dict:
+    """{counter: (mean over dispatches, dispatches)} of every counter in the --pmc run for
+    kernels whose name contains kernel_substr (each dispatch's instances summed)."""
+    per = {}
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            name = r.get("Kernel_Name", r.get("Kernel-Name", ""))
+            if kernel_substr not in name:
+                continue
+            c = r.get("Counter_Name", r.get("Counter-Name"))
+            d = r.get("Dispatch_Id", r.get("Dispatch-Id"))
+            per.setdefault(c, {})
+            per[c][d] = per[c].get(d, 0.0) + float(r.get("Counter_Value", r.get("Counter-Value", 0)))
+    return {c: (sum(v.values()) / len(v), len(v)) for c, v in per.items()}
 
 
 def counter_mean(run_dir: str, counter: str, kernel_substr: str) -> tuple[float, int]:
@@ -99,6 +125,48 @@ def write_counters(a):
     open(a.out, "w").write("\n".join(lines) + "\n")
 
 
+def write_utilization(a):
+    vals = {}
+    for d in a.runs:
+        for c, (mean, n) in counter_means(d, a.kernel).items():
+            vals[c] = (mean, n)
+    if not vals:
+        raise SystemExit(f"no counters for kernels matching {a.kernel!r} under {a.runs}")
+    rec = {"kernel": a.kernel, "source": a.source, "source_sha": source_hash(os.path.join(ROOT, a.source)),
+           "workload": a.workload, "counters": {c: round(m, 4) for c, (m, _) in sorted(vals.items())},
+           "dispatches": {c: n for c, (_, n) in sorted(vals.items())}}
+    lines = [f"# Hardware counters of `{a.kernel}` — {a.workload}", "",
+             "Derived counters from rocprofv3 --pmc runs of the workload (mean over the kernel's dispatches).",
+             "MfmaUtil: percent of the time the matrix cores are busy; LdsUtil: percent of LDS",
+             "bandwidth used; LDSBankConflict: percent of LDS cycles lost to bank conflicts.", "",
+             "| counter | mean | dispatches |", "|---|---:|---:|"]
+    for c, (m, n) in sorted(vals.items()):
+        lines.append(f"| {c} | {m:.2f} | {n} |")
+    lines += ["", f"Source `{a.source}` sha256[:16] = `{rec['source_sha']}` (bench.py reports these only while",
+              "the file is unchanged).", "", "Commands (from the repository root, on an MI355X):", "", "```"]
+    lines += list(a.commands) + ["```", "", UTIL_MARK + json.dumps(rec) + " -->"]
+    open(a.out, "w").write("\n".join(lines) + "\n")
+
+
+def _records(mark: str, profiles_dir: str):
+    for f in sorted(glob.glob(os.path.join(profiles_dir, "*.md"))):
+        for line in open(f, encoding="utf-8"):
+            if line.startswith(mark):
+                yield json.loads(line[len(mark):].rsplit(" -->", 1)[0])
+
+
+def utilization_for(kernel: str, workload: str, profiles_dir: str = os.path.join(ROOT, "profiles")):
+    """The counters of a committed utilization summary of `kernel` on `workload`, or None when
+    there is none or the kernel's source has changed since they were taken."""
+    for rec in _records(UTIL_MARK, profiles_dir):
+        if rec.get("kernel") != kernel or rec.get("workload") != workload:
+            continue
+        src = os.path.join(ROOT, rec["source"])
+        if os.path.exists(src) and source_hash(src) == rec["source_sha"]:
+            return rec["counters"]
+    return None
+
+
 def traffic_for(kernel: str, workload: str, profiles_dir: str = os.path.join(ROOT, "profiles")):
     """HBM bytes per launch of `kernel` on `workload` from a committed counter summary, or None
     when there is none or the kernel's source has changed since the counters were taken."""
@@ -135,8 +203,15 @@ def main():
     c.add_argument("--copy-bytes", type=int, required=True)
     c.add_argument("--commands", nargs="+", required=True)
     c.add_argument("--out", required=True)
+    u = sub.add_parser("utilization")
+    u.add_argument("--kernel", required=True)
+    u.add_argument("--source", required=True)
+    u.add_argument("--workload", required=True)
+    u.add_argument("--runs", nargs="+", required=True)
+    u.add_argument("--commands", nargs="+", required=True)
+    u.add_argument("--out", required=True)
     a = ap.parse_args()
-    (write_stats if a.cmd == "stats" else write_counters)(a)
+    {"stats": write_stats, "counters": write_counters, "utilization": write_utilization}[a.cmd](a)
 
 
 if __name__ == "__main__":
