@@ -287,11 +287,12 @@ def main():
     ms = timed(graph.replay if graph is not None else unit_fn, units) / steps
     tokens = cfg.batch * cfg.T
     value = tokens / (ms * 1e-3)
-    # the same steps without the compression, for comparison
+    # the same m-step units without the compression, for comparison
     ms_plain = None
     if with_compress:
-        g1 = None if args.no_graph else capture(pipe.run)
-        ms_plain = timed(g1.replay if g1 is not None else pipe.run, steps) / steps
+        plain = lambda: pipe.run_steps(compress=False)
+        g1 = None if args.no_graph else capture(plain)
+        ms_plain = timed(g1.replay if g1 is not None else plain, units) / steps
 
     # ---- per-stage time: back-to-back launches of each stage's library call, HIP events on the
     # stream the launches go to (torch's current stream).  Each stage is one of the step's own

@@ -100,11 +100,12 @@ class CsaDecode:
         self.attend()
         return self.out
 
-    def run_steps(self):
+    def run_steps(self, compress: bool = True):
         """m decode steps: the last one's token completes a block, so that step compresses its
-        entries first (one compression every m steps)."""
+        entries first (one compression every m steps; compress=False leaves it out, to time the
+        same steps without it)."""
         for j in range(self.m):
-            if j == self.m - 1:
+            if compress and j == self.m - 1:
                 self.compress()
             self.select()
             self.attend()
