@@ -195,6 +195,8 @@ def main():
     ap.add_argument("--stage-reps", type=int, default=0, help="launches per stage for kernel timing (0: = steps)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run device-to-device copies of BYTES (HBM counter calibration) and exit")
+    ap.add_argument("--rope", action="store_true",
+                    help="only time csa_rope (the last 64 channels) on a copy of the workload's q and exit")
     args = ap.parse_args()
     if args.copy_calibration:
         import torch
@@ -218,6 +220,28 @@ def main():
 
     cfg = CONFIGS[args.config]
     torch.cuda.set_device(0)
+    if args.rope:
+        # partial RoPE in place on a copy of q (bf16 [batch, T, H, c]); HBM-bound: each rotated
+        # channel is read and written once
+        q = torch.randn((cfg.batch, cfg.T, cfg.H, cfg.c), device="cuda").to(torch.bfloat16)
+        d = 64
+        fn = lambda: csa.csa_rope(q, cfg.q_pos0, 1, d)
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        reps = max(args.steps, 10)
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(reps):
+            fn()
+        end.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / reps
+        byt = 2 * cfg.batch * cfg.T * cfg.H * d * 2
+        print(json.dumps({"rope": {"workload": cfg.name, "rows": cfg.batch * cfg.T, "heads": cfg.H, "d": d,
+                                   "ms_per_call": round(ms, 5), "bytes": byt,
+                                   "hbm_frac": round(byt / (ms * 1e-3) / HBM_PEAK, 4)}}), flush=True)
+        return
     log(f"[bench] generating inputs for {cfg.name}")
     host = make_inputs(cfg)
     sh = shapes(cfg)

@@ -170,7 +170,7 @@ def test_cfg2_csa_decode_128k_mxfp4_sampled():
 
 @pytest.mark.timeout(900)
 def test_cfg4_csa_decode_1m_sampled():
-    _decode_case("cfg4_csa_decode_1m", np.array([0, 5]))
+    _decode_case("cfg4_csa_decode_1m", np.array([0, 3, 5, 7]))
 
 
 @pytest.mark.timeout(900)
