@@ -328,6 +328,11 @@ MQA_CASES = [  # batch, T, N, H, c, k, dtype
     (1, 3, 40, 48, 512, 16, BF16),         # head count off the 64-head tiling (generic kernel)
     (1, 2, 300, 256, 512, 64, BF16),       # maximum heads: four 64-head groups on matrix cores
     (1, 1, 50, 256, 1024, 8, F32),         # maximum heads and width (generic kernel)
+    # more than 256 (row, 64-head) units: the prefill kernel (two 4-wave workgroups per CU)
+    (1, 300, 700, 64, 512, 100, BF16),     # k off the 32-key block, rows of four blocks
+    (2, 150, 900, 128, 512, 160, BF16),    # two sequences, two head groups per row
+    (1, 290, 500, 64, 512, 1024, BF16),    # the largest k it takes, fewer entries than k: pads
+    (1, 600, 300, 256, 512, 40, BF16),     # four head groups, rows of two blocks
 ]
 
 
@@ -344,6 +349,60 @@ def test_sparse_mqa_parity(case):
     got = from_dev(csa.csa_sparse_mqa(to_dev(q, dt), to_dev(kv, dt), torch.from_numpy(idx).cuda(), scale))
     assert not got[0, 0].any()
     out_tol(dt)(got, ref, "sparse_mqa")
+
+
+def test_sparse_mqa_rows_walk_patterns():
+    """Prefill-shaped rows of very different lengths: a row's blocks run up to its last valid
+    id (trailing all-invalid blocks are skipped), rows with none are zeros, a row whose only id
+    sits in its last slot starts its softmax there, and ids past N are skipped."""
+    batch, T, N, H, c, k = 1, 700, 400, 64, 512, 96
+    say(f"csa_sparse_mqa walk patterns {(batch, T, N, H, c, k)}")
+    sd = 1777
+    q, kv = draw(sd, 1, (batch, T, H, c), BF16), draw(sd, 2, (batch, N, c), BF16)
+    r = np.random.RandomState(sd)
+    idx = np.full((batch, T, k), -1, np.int32)
+    for t in range(T):
+        sel = r.choice(N, size=k, replace=False).astype(np.int32)
+        kind = t % 6
+        if kind == 0:
+            continue                              # nothing selected: zeros
+        if kind == 1:
+            idx[0, t, :5] = sel[:5]               # valid ids in the first block only
+        elif kind == 2:
+            idx[0, t, k - 1] = sel[0]             # a single id in the last slot
+        elif kind == 3:
+            idx[0, t] = sel                       # full
+        elif kind == 4:
+            idx[0, t] = sel
+            idx[0, t, ::3] = N + r.randint(0, 1000, size=len(idx[0, t, ::3]))   # ids past N: skipped
+        else:
+            idx[0, t, 32:64] = sel[:32]           # only the middle block
+    scale = 1.0 / np.sqrt(c)
+    ref = oracle.sparse_mqa(q, kv, idx, scale, dtype=BF16)
+    got = from_dev(csa.csa_sparse_mqa(to_dev(q, BF16), to_dev(kv, BF16), torch.from_numpy(idx).cuda(), scale))
+    assert not got[0, ::6].any()
+    out_tol(BF16)(got, ref, "sparse_mqa walk patterns")
+
+
+def test_sparse_mqa_rows_large_grid():
+    """A launch of 16500 (row, 64-head) workgroups, many rounds of the chip: sampled rows
+    against the oracle (q drawn on the device from a seeded generator)."""
+    batch, T, N, H, c, k = 1, 16500, 64, 64, 512, 8
+    say(f"csa_sparse_mqa large grid {(batch, T, N, H, c, k)}")
+    sd = 1888
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(sd)
+    q_dev = torch.randn((batch, T, H, c), device="cuda", generator=gen).to(torch.bfloat16)
+    kv = draw(sd, 2, (batch, N, c), BF16)
+    r = np.random.RandomState(sd)
+    idx = np.stack([r.choice(N, size=k, replace=False) for _ in range(T)]).astype(np.int32)[None]
+    idx[0, 7, :] = -1
+    scale = 1.0 / np.sqrt(c)
+    got = csa.csa_sparse_mqa(q_dev, to_dev(kv, BF16), torch.from_numpy(idx).cuda(), scale)
+    rows = np.unique(np.concatenate([np.arange(0, 10), np.arange(T - 10, T), r.choice(T, 40, replace=False)]))
+    q_s = from_dev(q_dev[:, rows])
+    ref = oracle.sparse_mqa(q_s.astype(np.float32), rng.bf16_bits_to_f32(kv), idx[:, rows], scale, dtype=F32)
+    out_tol(BF16)(from_dev(got[:, rows]), ref, "sparse_mqa large grid (sampled rows)")
 
 
 MIXED_KV_CASES = [  # batch, T, N, H, k  (c = 512; KV rows: 448 fp8 channels, 64 bf16)
