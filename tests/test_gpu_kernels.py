@@ -749,6 +749,43 @@ def test_decode_step_compression_through_the_pipeline():
     assert np.array_equal(from_dev(dev["kv"][:, :-1]), oracle.decode(host["kv"][:, :-1], BF16))
 
 
+def test_decode_steps_graph_replay():
+    """The m decode steps of the pipeline (the last one compresses the new KV and index-key
+    entries first): the attention sees the new entry (its output equals an attention over the
+    updated cache), and the steps captured in a graph and replayed, with eager work between the
+    replays, give the eager result bit for bit."""
+    from long_context_sparse_08_amd.pipeline import CsaDecode
+    from workloads import CONFIGS, make_inputs, scaled, shapes
+    cfg = scaled(CONFIGS["cfg2_csa_decode_128k"], batch=3, N=2000, q_pos0=4 * 2000, k=256)
+    host = make_inputs(cfg)
+    sh = shapes(cfg)
+    dev = {k: to_dev(v, sh[k][1]) for k, v in host.items()}
+    pipe = CsaDecode(dev, cfg.m, cfg.k, cfg.q_pos0)
+    pipe.run_steps()
+    torch.cuda.synchronize()
+    ref = pipe.out.clone()
+    again = csa.csa_sparse_mqa(dev["q"], dev["kv"], pipe.idx, pipe.scale)
+    torch.cuda.synchronize()
+    say(f"  new entry selected in {int((pipe.idx == cfg.N - 1).sum())} of {pipe.idx.numel()} slots")
+    assert torch.equal(again, ref)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        pipe.run_steps()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pipe.run_steps()
+    for rep in range(3):
+        pipe.out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        junk = torch.randn(1 << 20, device="cuda").sum().item()   # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(pipe.out, ref), (rep, junk)
+
+
 def test_repeat_runs_are_bitwise_identical():
     batch, T, N, H, c, k = 2, 3, 900, 64, 512, 256
     q, kv = draw(77, 1, (batch, T, H, c), BF16), draw(77, 2, (batch, N, c), BF16)
