@@ -1221,12 +1221,24 @@ topk_groups(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
         }
         __syncthreads();
         const int bstar = sh.bstar;
-        // the selected groups (every lane of a wave runs the same trip count)
-        for (int64_t j0 = 0; j0 < ng; j0 += kGThreads) {
-            const int64_t j = j0 + tid;
-            const bool take = j < ng && bin_of_n<kGBins>(gv[j], flo, inv) >= bstar;
-            const uint32_t p = wave_append(take, &sh.ngroups);
-            if (take) sh.b[p] = (uint32_t)j;
+        // the selected groups in index order: thread t takes groups kPer*t .. kPer*t + kPer-1,
+        // one block scan of the per-thread counts places them (no atomics on one counter)
+        {
+            uint32_t tk = 0u, cnt = 0u;
+#pragma unroll
+            for (int u = 0; u < kPer; ++u) {
+                const int64_t j = (int64_t)kPer * tid + u;
+                if (j < ng && bin_of_n<kGBins>(gv[j], flo, inv) >= bstar) {
+                    tk |= 1u << u;
+                    ++cnt;
+                }
+            }
+            uint32_t total;
+            uint32_t p = block_excl_scan<kGWaves>(cnt, sh.scan, &total);
+#pragma unroll
+            for (int u = 0; u < kPer; ++u)
+                if ((tk >> u) & 1u) sh.b[p++] = (uint32_t)(kPer * tid + u);
+            if (tid == 0) sh.ngroups = total;
         }
         __syncthreads();
         const int64_t nsel = sh.ngroups;
@@ -1262,11 +1274,14 @@ topk_groups(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
         if (G >= 4) {
             const int lq = __builtin_ctz((unsigned)G) - 2;   // 16-byte pieces per group: 1 << lq
             const int64_t nq = nsel << lq;
-            for (int64_t q0 = 0; q0 < nq; q0 += 8 * kGThreads) {
-                float xs[32];
-                int64_t e0[8];
+            // kCPer pieces per thread, every load of a round in flight together: the ~k selected
+            // groups of a k = 1024 selection take one round (8 pieces per thread took two)
+            constexpr int kCPer = 12, kCHalf = kCPer / 2;
+            for (int64_t q0 = 0; q0 < nq; q0 += kCPer * kGThreads) {
+                float xs[4 * kCPer];
+                int64_t e0[kCPer];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
+                for (int u = 0; u < kCPer; ++u) {
                     const int64_t q = q0 + tid + (int64_t)u * kGThreads;
                     e0[u] = q < nq ? ((int64_t)sh.b[q >> lq] << (lq + 2)) + ((q & ((1 << lq) - 1)) << 2) : -1;
                     if (e0[u] >= nv) e0[u] = -1;   // wholly past the row (a piece that starts below
@@ -1277,13 +1292,20 @@ topk_groups(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
                     xs[4 * u + 2] = x4.z;
                     xs[4 * u + 3] = x4.w;
                 }
-                uint32_t mask = 0u;
+                // appended in two halves (a thread's takes of a half fit one 32-bit mask)
 #pragma unroll
-                for (int u = 0; u < 8; ++u)
+                for (int hf = 0; hf < 2; ++hf) {
+                    uint32_t mask = 0u;
 #pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        if (e0[u] >= 0 && in_b(e0[u] + c, xs[4 * u + c])) mask |= 1u << (4 * u + c);
-                append(mask, e0, xs, std::integral_constant<int, 32>{}, std::integral_constant<int, 4>{});
+                    for (int u = 0; u < kCHalf; ++u)
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            const int uu = kCHalf * hf + u;
+                            if (e0[uu] >= 0 && in_b(e0[uu] + c, xs[4 * uu + c])) mask |= 1u << (4 * u + c);
+                        }
+                    append(mask, e0 + kCHalf * hf, xs + 4 * kCHalf * hf, std::integral_constant<int, 4 * kCHalf>{},
+                           std::integral_constant<int, 4>{});
+                }
             }
         } else {
             const int lg = __builtin_ctz((unsigned)G);
