@@ -191,7 +191,8 @@ int csa_index_topk(const void* qI, const float* w, const void* kI, int64_t batch
     float* gmax = G > 0 ? reinterpret_cast<float*>(static_cast<char*>(extra) +
                                                    round_up(csa::topk_extra_workspace(rows, N, k)))
                         : nullptr;
-    const int zero_words = n_chunks > 0 && G == 0 ? csa::topk_zero_words(rows, nv_max) : 0;
+    // (the per-row counters of the multi-workgroup selections: with or without group maxima)
+    const int zero_words = n_chunks > 0 ? csa::topk_zero_words(rows, nv_max) : 0;
     uint32_t* zero = zero_words > 0 ? csa::topk_zero_region(extra, rows, N) : nullptr;
     int n_chunk_mm = 0;
     rc = csa::launch_index_scores(qI, w, kI, batch, T, q_pos0, N, H_I, c_I, m, qk_t, scores, ld, false, chunk_mm,

@@ -1147,17 +1147,30 @@ __device__ __forceinline__ uint32_t first_bits(uint32_t w, uint32_t n) {
     return r;
 }
 
+// MODE 0: the whole row in one workgroup, as above.  Long rows of a few queries spread the
+// candidate step over the chip in two launches:
+// MODE 1 (grid rows x P): workgroup (row, p) finds b* as in step 1 (every workgroup of a row
+//   from the same maxima: the same b*) and appends the candidates of groups p*kSliceGroups ..
+//   (p+1)*kSliceGroups - 1 to the row's list (value, index) in global memory, one atomic per
+//   wave on the row's counter (cleared by the indexer at the start of the call);
+// MODE 2 (grid rows): steps 3-4 from that list (more than kGCap candidates: over the whole row).
+constexpr int kSliceGroups = 256;
+
+template <int MODE>
 __global__ void __launch_bounds__(kGThreads)
 topk_groups(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_pos0, int64_t N, int m, int k,
-            const float* __restrict__ gmax, int64_t gld, int G, int32_t* __restrict__ idx, float* __restrict__ sel) {
+            const float* __restrict__ gmax, int64_t gld, int G, int32_t* __restrict__ idx, float* __restrict__ sel,
+            int P, uint32_t* __restrict__ ccount, int ccount_ld, float* __restrict__ cval, int32_t* __restrict__ cidx) {
     __shared__ GroupShared sh;
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform: scalar registers
-    const int64_t row = blockIdx.x;
+    const int64_t row = MODE == 1 ? blockIdx.x / P : blockIdx.x;
+    const int slice = MODE == 1 ? (int)(blockIdx.x % P) : 0;
     const int64_t nv = visible_entries(q_pos0 + row % T, m, N);
     const float* sc = scores + row * ld;
     int32_t* oi = idx + row * k;
     float* os = sel ? sel + row * k : nullptr;
+    if (MODE == 1 && nv <= k) return;
     if (nv <= k) {
         for (int r = tid; r < k; r += kGThreads) {
             oi[r] = r < nv ? r : -1;
@@ -1168,9 +1181,32 @@ topk_groups(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
     // (the launcher sends rows of at most kGMaxRow entries and at most kGMaxGroups groups)
     const int64_t ng = (nv + G - 1) / G;
     bool full = ng <= k;
+    if (MODE == 1 && full) return;
     uint32_t kstar = 0u, need_eq = 0u;
     int64_t ncand = 0;
-    if (!full) {
+    if (MODE == 2 && !full) {
+        // the candidates the slices appended: keys and indices into LDS, their range
+        ncand = ccount[row * ccount_ld];
+        if (ncand > kGCap || ncand < k) {
+            full = true;   // heavy ties at b* (the second cannot happen)
+        } else {
+            uint32_t lo = ~0u, hi = 0u;
+            for (int64_t i2 = tid; i2 < ncand; i2 += kGThreads) {
+                const uint32_t key = order_key(cval[row * kMCap + i2]);
+                sh.ckey[i2] = key;
+                sh.cidx[i2] = cidx[row * kMCap + i2];
+                lo = min(lo, key);
+                hi = max(hi, key);
+            }
+            block_minmax(lo, hi, sh);   // (its barrier also publishes the candidates)
+            kstar = radix_kth<kGThreads>(
+                [&](auto f) {
+                    for (int64_t i2 = tid; i2 < ncand; i2 += kGThreads) f(sh.ckey[i2]);
+                },
+                (uint32_t)k, lo, hi, sh.hist, sh.ctl, &need_eq);
+        }
+    }
+    if (MODE != 2 && !full) {
         // group maxima into LDS (all loads in flight together) and their range
         const float* gm = gmax + row * gld;
         float* gv = reinterpret_cast<float*>(sh.a);
@@ -1221,6 +1257,56 @@ topk_groups(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
         }
         __syncthreads();
         const int bstar = sh.bstar;
+        auto in_b = [&](int64_t e, float x) { return e < nv && bin_of_n<kGBins>(x, flo, inv) >= bstar; };
+        if constexpr (MODE == 1) {
+            // this slice's groups whose maximum is in a bin >= b*: their entries in bins >= b*
+            // (G >= 4: 16-byte pieces, 1 << lq per group, kSP per thread, all loads in flight
+            // together); placed by one block scan and one atomic per workgroup on the row's count
+            constexpr int kSP = kSliceGroups * (kGMaxG / 4) / kGThreads;
+            const int lq = __builtin_ctz((unsigned)G) - 2;
+            const int64_t j0 = (int64_t)slice * kSliceGroups, j1 = min(ng, j0 + kSliceGroups);
+            const int npieces = j1 > j0 ? (int)((j1 - j0) << lq) : 0;
+            int64_t e0[kSP];
+            float xs[4 * kSP];
+#pragma unroll
+            for (int u = 0; u < kSP; ++u) {
+                const int q = tid + u * kGThreads;
+                const int64_t j = j0 + (q >> lq);
+                e0[u] = (q < npieces && bin_of_n<kGBins>(gv[j], flo, inv) >= bstar)
+                            ? (j << (lq + 2)) + ((int64_t)(q & ((1 << lq) - 1)) << 2) : -1;
+                if (e0[u] >= nv) e0[u] = -1;   // wholly past the row (see step 2 of MODE 0)
+                const float4 x4 = e0[u] >= 0 ? *reinterpret_cast<const float4*>(sc + e0[u]) : make_float4(0.f, 0.f, 0.f, 0.f);
+                xs[4 * u] = x4.x;
+                xs[4 * u + 1] = x4.y;
+                xs[4 * u + 2] = x4.z;
+                xs[4 * u + 3] = x4.w;
+            }
+            uint32_t mask = 0u;
+#pragma unroll
+            for (int u = 0; u < kSP; ++u)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    if (e0[u] >= 0 && in_b(e0[u] + c, xs[4 * u + c])) mask |= 1u << (4 * u + c);
+            uint32_t total;
+            const uint32_t pre = block_excl_scan<kGWaves>((uint32_t)__popc(mask), sh.scan, &total);
+            if (total == 0u) return;
+            if (tid == 0) sh.ngroups = atomicAdd(&ccount[row * ccount_ld], total);
+            __syncthreads();
+            uint32_t at = sh.ngroups + pre;
+#pragma unroll
+            for (int u = 0; u < kSP; ++u)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    if ((mask >> (4 * u + c)) & 1u) {
+                        if (at < (uint32_t)kMCap) {
+                            cval[row * kMCap + at] = xs[4 * u + c];
+                            cidx[row * kMCap + at] = (int32_t)(e0[u] + c);
+                        }
+                        ++at;
+                    }
+                }
+            return;
+        }
         // the selected groups in index order: thread t takes groups kPer*t .. kPer*t + kPer-1,
         // one block scan of the per-thread counts places them (no atomics on one counter)
         {
@@ -1270,7 +1356,6 @@ topk_groups(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
                 }
             }
         };
-        auto in_b = [&](int64_t e, float x) { return e < nv && bin_of_n<kGBins>(x, flo, inv) >= bstar; };
         if (G >= 4) {
             const int lq = __builtin_ctz((unsigned)G) - 2;   // 16-byte pieces per group: 1 << lq
             const int64_t nq = nsel << lq;
@@ -1385,31 +1470,62 @@ topk_groups(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
     }
     __syncthreads();
 
-    // ordered extraction: each thread owns a run of words; the ties ahead of its run decide
-    // how many of its own ties it keeps
-    const int64_t per = (nwords + kGThreads - 1) / kGThreads;
-    const int64_t w0 = (int64_t)tid * per, w1 = min(nwords, w0 + per);
-    uint32_t ceq = 0;
-    for (int64_t w = w0; w < w1; ++w) ceq += __popc(sh.a[w]);
-    uint32_t total;
-    uint32_t taken = block_excl_scan<kGWaves>(ceq, sh.scan, &total);
-    uint32_t cnt = 0;
-    for (int64_t w = w0; w < w1; ++w) {
-        uint32_t eqw = sh.a[w];
+    // ordered extraction.  Wave v owns words [v*R, v*R + R) (R a multiple of 64) and lane l of
+    // its round j takes word v*R + 64*j + l, so that every LDS access of a round is one
+    // contiguous run (threads that own runs of consecutive words hit the same banks 16 times
+    // over: 4.5 us of scans at a 1M context).  A word's prefix in index order is the earlier
+    // waves' total, the wave's earlier rounds' totals and the earlier lanes' counts in its round.
+    constexpr int kXR = kGMaxRow / 32 / kGThreads;   // rounds at most
+    const int64_t R = ((nwords + kGWaves - 1) / kGWaves + kWave - 1) / kWave * kWave;
+    const int nr = (int)(R / kWave);
+    auto word_at = [&](int j) { return (int64_t)wid * R + (int64_t)kWave * j + lane; };
+    // pre[j]: the sum of c over the words before word_at(j) (c is 0 past the row)
+    auto prefix = [&](const uint32_t (&c)[kXR], uint32_t (&pre)[kXR]) {
+        uint32_t run = 0u;
+#pragma unroll
+        for (int j = 0; j < kXR; ++j) {
+            if (j < nr) {
+                const uint32_t inc = wave_incl_scan(c[j]);
+                pre[j] = run + inc - c[j];
+                run += __builtin_amdgcn_readlane(inc, kWave - 1);
+            }
+        }
+        uint32_t total;
+        const uint32_t wb = block_excl_scan<kGWaves>(lane == 0 ? run : 0u, sh.scan, &total);
+        const uint32_t base = __builtin_amdgcn_readlane(wb, 0);
+#pragma unroll
+        for (int j = 0; j < kXR; ++j) pre[j] += base;
+    };
+    uint32_t eq[kXR], kw[kXR], cnt[kXR], pre[kXR];
+#pragma unroll
+    for (int j = 0; j < kXR; ++j) {
+        const int64_t w = word_at(j);
+        const bool in = j < nr && w < nwords;
+        eq[j] = in ? sh.a[w] : 0u;
+        kw[j] = in ? sh.b[w] : 0u;
+        cnt[j] = __popc(eq[j]);
+    }
+    prefix(cnt, pre);   // the ties before each word decide how many of its own it keeps
+#pragma unroll
+    for (int j = 0; j < kXR; ++j) {
+        const uint32_t taken = pre[j];
+        uint32_t eqw = eq[j];
         if (taken >= need_eq) eqw = 0u;
         else if (taken + __popc(eqw) > need_eq) eqw = first_bits(eqw, need_eq - taken);
-        taken += __popc(sh.a[w]);
-        const uint32_t kw = sh.b[w] | eqw;
-        sh.b[w] = kw;   // this thread's words only
-        cnt += __popc(kw);
+        kw[j] |= eqw;
+        cnt[j] = __popc(kw[j]);
     }
-    uint32_t pos = block_excl_scan<kGWaves>(cnt, sh.scan, &total);
+    prefix(cnt, pre);   // kept entries before each word
     if (!full) {
         // every kept entry is a candidate: its slot is the kept count before its word plus
         // the kept bits below it in the word; its score comes back from its key
-        for (int64_t w = w0; w < w1; ++w) {
-            sh.a[w] = pos;
-            pos += __popc(sh.b[w]);
+#pragma unroll
+        for (int j = 0; j < kXR; ++j) {
+            const int64_t w = word_at(j);
+            if (j < nr && w < nwords) {
+                sh.b[w] = kw[j];
+                sh.a[w] = pre[j];
+            }
         }
         __syncthreads();
         for (int64_t i2 = tid; i2 < ncand; i2 += kGThreads) {
@@ -1423,8 +1539,10 @@ topk_groups(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
         }
         return;
     }
-    for (int64_t w = w0; w < w1; ++w) {
-        uint32_t word = sh.b[w];
+#pragma unroll
+    for (int j = 0; j < kXR; ++j) {
+        uint32_t word = kw[j], pos = pre[j];
+        const int64_t w = word_at(j);
         while (word) {
             const int bit = __ffs(word) - 1;
             word &= word - 1;
@@ -1892,8 +2010,21 @@ int launch_topk(const float* scores, int64_t ld, int64_t batch, int64_t T, int64
     int64_t nv_max = (q_pos0 + T) / m;
     if (nv_max > N) nv_max = N;
     if (gmax != nullptr && G > 0) {   // the indexer wrote the group maxima (G = topk_group)
-        hipLaunchKernelGGL(topk_groups, dim3((unsigned)rows), dim3(kGThreads), 0, stream, scores, ld, T, q_pos0, N, m,
-                           k, gmax, gld, G, idx, sel);
+        if (extra_ws != nullptr && G >= 4 && multi_rows(rows, nv_max)) {
+            // few long rows: the candidates of each row found by (row, group slice) workgroups
+            // over the chip, then one workgroup per row selects from them (the indexer cleared
+            // the rows' candidate counters)
+            MultiWs L;
+            multi_bytes(rows, N, &L, extra_ws);
+            const int P = (int)(((nv_max + G - 1) / G + kSliceGroups - 1) / kSliceGroups);
+            hipLaunchKernelGGL(topk_groups<1>, dim3((unsigned)(rows * P)), dim3(kGThreads), 0, stream, scores, ld, T,
+                               q_pos0, N, m, k, gmax, gld, G, idx, sel, P, L.zero + kBins, kZeroWords, L.cval, L.cidx);
+            hipLaunchKernelGGL(topk_groups<2>, dim3((unsigned)rows), dim3(kGThreads), 0, stream, scores, ld, T, q_pos0,
+                               N, m, k, gmax, gld, G, idx, sel, P, L.zero + kBins, kZeroWords, L.cval, L.cidx);
+            return 0;
+        }
+        hipLaunchKernelGGL(topk_groups<0>, dim3((unsigned)rows), dim3(kGThreads), 0, stream, scores, ld, T, q_pos0, N,
+                           m, k, gmax, gld, G, idx, sel, 1, nullptr, 0, nullptr, nullptr);
         return 0;
     }
     if (chunk_mm != nullptr && extra_ws != nullptr && multi_rows(rows, nv_max)) {

@@ -162,6 +162,7 @@ DECODE_TOPK_CASES = [  # batch, T, q_pos0, N, k, levels, zero-key fraction
     (1, 1, 4 * 32768, 32768, 1024, 1, 0.0),       # register-staged, every score equal
     (1, 3, 4 * 100000 - 3, 100000, 2048, 6, 0.0),
     (1, 1, 4 * 262144, 262144, 1024, 8, 0.0),     # the longest row the group maxima serve
+    (3, 1, 4 * 200000 - 7, 200000, 2048, 5, 0.0), # group slices over the chip: several rows, maximum k
     (1, 1, 4 * 300000, 300000, 1024, 8, 0.0),     # longer: the multi-workgroup selection
 ]
 
@@ -170,7 +171,8 @@ DECODE_TOPK_CASES = [  # batch, T, q_pos0, N, k, levels, zero-key fraction
 def test_topk_decode_shapes_bit_exact(case):
     # decode-shaped calls (fp8 indexer, T < 4): rows of up to 32768 entries (at least 8k) take
     # the register-staged selection, other rows that fit LDS the one-workgroup bitmap
-    # selection, longer ones up to 262144 entries the indexer's group maxima, longer still
+    # selection, longer ones up to 262144 entries the indexer's group maxima (few such rows:
+    # candidates found by group-slice workgroups over the chip, then one per row), longer still
     # per-chunk ranges and several workgroups per row; integer-valued fp8 inputs keep every
     # score exact
     batch, T, p0, N, k, levels, zfrac = case
