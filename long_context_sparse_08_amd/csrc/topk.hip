@@ -1160,12 +1160,17 @@ template <int MODE>
 __global__ void __launch_bounds__(kGThreads)
 topk_groups(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_pos0, int64_t N, int m, int k,
             const float* __restrict__ gmax, int64_t gld, int G, int32_t* __restrict__ idx, float* __restrict__ sel,
-            int P, uint32_t* __restrict__ ccount, int ccount_ld, float* __restrict__ cval, int32_t* __restrict__ cidx) {
+            int64_t rows, int P, uint32_t* __restrict__ ccount, int ccount_ld, float* __restrict__ cval,
+            int32_t* __restrict__ cidx) {
     __shared__ GroupShared sh;
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform: scalar registers
-    const int64_t row = MODE == 1 ? blockIdx.x / P : blockIdx.x;
-    const int slice = MODE == 1 ? (int)(blockIdx.x % P) : 0;
+    // MODE 1: the slices of row r run on XCD r % 8 (workgroups are dealt round-robin over the
+    // 8 XCDs), where the indexer wrote the row's scores and maxima and where the selecting
+    // workgroup of the row runs: their loads and the candidates they write stay in that L2
+    const int64_t row = MODE == 1 ? (int64_t)(blockIdx.x / 8 / P) * 8 + blockIdx.x % 8 : (int64_t)blockIdx.x;
+    const int slice = MODE == 1 ? (int)(blockIdx.x / 8 % P) : 0;
+    if (MODE == 1 && row >= rows) return;   // (rows padded to whole XCD rounds)
     const int64_t nv = visible_entries(q_pos0 + row % T, m, N);
     const float* sc = scores + row * ld;
     int32_t* oi = idx + row * k;
@@ -2017,14 +2022,15 @@ int launch_topk(const float* scores, int64_t ld, int64_t batch, int64_t T, int64
             MultiWs L;
             multi_bytes(rows, N, &L, extra_ws);
             const int P = (int)(((nv_max + G - 1) / G + kSliceGroups - 1) / kSliceGroups);
-            hipLaunchKernelGGL(topk_groups<1>, dim3((unsigned)(rows * P)), dim3(kGThreads), 0, stream, scores, ld, T,
-                               q_pos0, N, m, k, gmax, gld, G, idx, sel, P, L.zero + kBins, kZeroWords, L.cval, L.cidx);
+            hipLaunchKernelGGL(topk_groups<1>, dim3((unsigned)((rows + 7) / 8 * 8 * P)), dim3(kGThreads), 0, stream, scores, ld, T,
+                               q_pos0, N, m, k, gmax, gld, G, idx, sel, rows, P, L.zero + kBins, kZeroWords, L.cval,
+                               L.cidx);
             hipLaunchKernelGGL(topk_groups<2>, dim3((unsigned)rows), dim3(kGThreads), 0, stream, scores, ld, T, q_pos0,
-                               N, m, k, gmax, gld, G, idx, sel, P, L.zero + kBins, kZeroWords, L.cval, L.cidx);
+                               N, m, k, gmax, gld, G, idx, sel, rows, P, L.zero + kBins, kZeroWords, L.cval, L.cidx);
             return 0;
         }
         hipLaunchKernelGGL(topk_groups<0>, dim3((unsigned)rows), dim3(kGThreads), 0, stream, scores, ld, T, q_pos0, N,
-                           m, k, gmax, gld, G, idx, sel, 1, nullptr, 0, nullptr, nullptr);
+                           m, k, gmax, gld, G, idx, sel, rows, 1, nullptr, 0, nullptr, nullptr);
         return 0;
     }
     if (chunk_mm != nullptr && extra_ws != nullptr && multi_rows(rows, nv_max)) {
