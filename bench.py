@@ -31,6 +31,22 @@ sys.path.insert(0, ROOT)
 METRIC = "CSA query tokens/s (compress+index+top-k+MQA) at 128K ctx; % of roofline"
 # the compressor-only workload counts raw tokens compressed, not query tokens
 METRIC_COMPRESS = "CSA raw tokens compressed/s (csa_compress over a 1M-token sequence); % of HBM roofline"
+
+
+def metric_for(cfg) -> str:
+    """The metric string of a workload: the headline one for 128K-context decode, else a label
+    that names what that workload's tokens/s counts."""
+    if cfg.kind == "csa_compress":
+        return METRIC_COMPRESS
+    if cfg.kind == "csa_decode":
+        ctx = cfg.q_pos0   # tokens before the query
+        if ctx == 1 << 17:
+            return METRIC
+        return METRIC.replace("at 128K ctx", "at %s ctx" % ("1M" if ctx == 1 << 20 else str(ctx)))
+    if cfg.kind == "csa_prefill":
+        return "CSA prefill query tokens/s (compress+index+top-k+MQA) over a %d-token chunk; %% of roofline" % cfg.T
+    return ("HCA query tokens/s (compress+dense MQA) for a %d-query chunk ending at position %d; %% of roofline"
+            % (cfg.T, cfg.q_pos0 + cfg.T))
 HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
 MFMA_PEAK = {"bf16": 2.5e15, "fp8": 5.0e15}
 # MXFP4: a 4-bit value plus a 1-byte scale per 32; mixed KV rows: 448 fp8 + 64 bf16 per 512
@@ -411,7 +427,7 @@ def main():
                 for k, v in work.items() if k != "compress_step" or with_compress)
 
     result = {
-        "metric": METRIC_COMPRESS if cfg.kind == "csa_compress" else METRIC,
+        "metric": metric_for(cfg),
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
