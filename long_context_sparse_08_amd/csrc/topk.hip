@@ -1978,6 +1978,177 @@ topk_regs(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_pos
     }
 }
 
+// Short rows (prefill: at most 2048 visible entries), one wave per row and four rows per
+// workgroup, with no workgroup barrier: the wave holds its row in registers (entry 64 i + lane
+// in value i of the lane, 32 per lane, loaded coalesced), finds the row's range with two wave
+// reductions, counts a 256-bin histogram LINEAR in value in its own LDS, and takes the bin b*
+// that holds the k-th largest value (bins are monotone in value, so every entry of a higher
+// bin is kept and none of a lower one).  The order keys of b*'s members go to a list in the
+// wave's LDS; the exact k-th key K* among them and the number of entries equal to it to take
+// come from an 8-bit radix select over that list (four passes over the same histogram).  The
+// output goes out in index order with one ballot per 64 entries: entry e is kept iff its bin
+// is above b*, or it is in b* with key > K*, or key == K* and it is among the first need_eq
+// such entries.  (The rows are short and many: the kernel is bound by instruction issue, so
+// each value's bin is kept in a register and key work is skipped wherever no lane of the wave
+// holds a member of b*.)
+constexpr int kWvRow = 2048;                 // longest row served
+constexpr int kWvPer = kWvRow / kWave;       // values per lane (32)
+constexpr int kWvRows = 4;                   // rows (waves) per workgroup
+constexpr int kWvBins = 256;
+
+// the wave's LDS operations so far are complete, and the compiler moves none across this point
+// (a wave's histogram and list are only ever touched by that wave)
+__device__ __forceinline__ void wave_lds_sync() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+}
+
+// one wave: the bin of `hist` (kWvBins counts) that holds the need-th largest counted value,
+// searched from the top, and how many of its members that leaves to take (need >= 1, and the
+// counts sum to at least need)
+__device__ __forceinline__ void wave_top_bin(const uint32_t* hist, uint32_t need, int* bin, uint32_t* left) {
+    const int lane = threadIdx.x & (kWave - 1);
+    // lane l: bins 255 - 4l (x.w) down to 252 - 4l (x.x)
+    const uint4 x = *reinterpret_cast<const uint4*>(hist + kWvBins - 4 - 4 * lane);
+    const uint32_t sum = x.x + x.y + x.z + x.w;
+    const uint32_t inc = wave_incl_scan(sum);
+    const unsigned long long hit = __ballot(inc - sum < need && inc >= need);   // exactly one lane
+    const int L = __builtin_ctzll(hit);
+    uint32_t cum = inc - sum;
+    int b;
+    if (cum + x.w >= need) {
+        b = kWvBins - 1 - 4 * lane;
+    } else if ((cum += x.w) + x.z >= need) {
+        b = kWvBins - 2 - 4 * lane;
+    } else if ((cum += x.z) + x.y >= need) {
+        b = kWvBins - 3 - 4 * lane;
+    } else {
+        cum += x.y;
+        b = kWvBins - 4 - 4 * lane;
+    }
+    *bin = __builtin_amdgcn_readlane(b, L);
+    *left = need - __builtin_amdgcn_readlane(cum, L);
+}
+
+struct WaveTopkShared {
+    uint32_t hist[kWvRows][kWvBins];
+    uint32_t mem[kWvRows][kWvRow];   // order keys of b*'s members
+};
+
+__global__ void __launch_bounds__(kWvRows * kWave)
+topk_wave(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_pos0, int64_t N, int m, int k,
+          int64_t rows, int32_t* __restrict__ idx, float* __restrict__ sel) {
+    __shared__ __attribute__((aligned(16))) WaveTopkShared sh;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t row = (int64_t)blockIdx.x * kWvRows + wid;
+    if (row >= rows) return;   // a whole wave; the kernel has no workgroup barrier
+    uint32_t* hist = sh.hist[wid];
+    uint32_t* mem = sh.mem[wid];
+    const int64_t nv = visible_entries(q_pos0 + row % T, m, N);
+    const float* sc = scores + row * ld;
+    int32_t* oi = idx + row * k;
+    float* os = sel ? sel + row * k : nullptr;
+    if (nv <= k) {
+        for (int r = lane; r < k; r += kWave) {
+            oi[r] = r < nv ? r : -1;
+            if (os) os[r] = r < nv ? sc[r] : -INFINITY;
+        }
+        return;
+    }
+    // (the launcher sends rows of at most kWvRow visible entries)
+    const int nvi = (int)nv;
+    // the row's visible entries; loads past them read 0
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(sc), (short)0,
+                                                                        (int)(4 * nvi), 0x00020000);
+    float v[kWvPer];
+#pragma unroll
+    for (int i = 0; i < kWvPer; ++i)
+        v[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4u * lane, 4u * kWave * i, 0));
+    // value i of this lane is an entry iff i < nmine
+    const int nmine = (nvi - lane + kWave - 1) / kWave;
+
+    // range (entries only) and linear bins (inv = 0: one bin, the radix select does all the work)
+    float lo = v[0], hi = v[0];   // entry `lane`; lanes past a row of fewer than 64 take entry 0's
+    if (lane >= nvi) lo = hi = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v[0])));
+#pragma unroll
+    for (int i = 1; i < kWvPer; ++i)
+        if (i < nmine) {
+            lo = fminf(lo, v[i]);
+            hi = fmaxf(hi, v[i]);
+        }
+    lo = wave_ext<false>(lo);
+    hi = wave_ext<true>(hi);
+    float inv = (float)kWvBins / (hi - lo);
+    if (!(hi > lo) || !isfinite(inv)) inv = 0.f;
+    *reinterpret_cast<uint4*>(hist + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
+    int bn[kWvPer];   // bin of value i (-1: not an entry)
+#pragma unroll
+    for (int i = 0; i < kWvPer; ++i) {
+        bn[i] = i < nmine ? bin_of_n<kWvBins>(v[i], lo, inv) : -1;
+        if (i < nmine) atomicAdd(&hist[bn[i]], 1u);
+    }
+    int bstar;
+    uint32_t need;   // members of b* to take (1 .. its count)
+    wave_lds_sync();
+    wave_top_bin(hist, (uint32_t)k, &bstar, &need);
+
+    // b*'s members' keys to the list
+    const unsigned long long below = (1ull << lane) - 1ull;   // lanes before this one
+    uint32_t nmem = 0u;
+#pragma unroll
+    for (int i = 0; i < kWvPer; ++i) {
+        const bool mb = bn[i] == bstar;
+        const unsigned long long mm = __ballot(mb);
+        if (mm != 0ull) {   // wave-uniform
+            if (mb) mem[nmem + (uint32_t)__popcll(mm & below)] = order_key(v[i]);
+            nmem += (uint32_t)__popcll(mm);
+        }
+    }
+
+    // K* among the members: 8 bits of the key per pass, from the top
+    uint32_t prefix = 0u;
+#pragma unroll 1
+    for (int p = 0; p < 4; ++p) {
+        const int shift = 24 - 8 * p;
+        const uint32_t hmask = p == 0 ? 0u : ~0u << (shift + 8);
+        wave_lds_sync();
+        *reinterpret_cast<uint4*>(hist + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
+        for (uint32_t j = lane; j < nmem; j += kWave) {
+            const uint32_t key = mem[j];
+            if ((key & hmask) == prefix) atomicAdd(&hist[(key >> shift) & (kWvBins - 1)], 1u);
+        }
+        int d;
+        wave_lds_sync();
+        wave_top_bin(hist, need, &d, &need);
+        prefix |= (uint32_t)d << shift;
+    }
+    const uint32_t kstar = prefix, need_eq = need;   // take the first need_eq entries with key K*
+
+    // ordered output
+    uint32_t base = 0u, eq_seen = 0u;
+#pragma unroll
+    for (int i = 0; i < kWvPer; ++i) {
+        bool take = bn[i] > bstar;
+        const bool mb = bn[i] == bstar;
+        if (__ballot(mb) != 0ull) {   // wave-uniform: some lane holds a member of b*
+            const uint32_t key = order_key(v[i]);
+            const bool eq = mb && key == kstar;
+            const unsigned long long em = __ballot(eq);
+            take = take || (mb && key > kstar) || (eq && eq_seen + (uint32_t)__popcll(em & below) < need_eq);
+            eq_seen += (uint32_t)__popcll(em);
+        }
+        const unsigned long long tm = __ballot(take);
+        if (take) {
+            const uint32_t slot = base + (uint32_t)__popcll(tm & below);
+            oi[slot] = kWave * i + lane;
+            if (os) os[slot] = v[i];
+        }
+        base += (uint32_t)__popcll(tm);
+    }
+}
+
 // Group size for the group-bounded selection (0: not used): a power of two up to kGMaxG with
 // at most kGMaxGroups groups in the longest row, and preferably at least 4k of them.
 // Rows that fit the LDS staging of the one-workgroup bitmap selection are faster there.
@@ -2053,6 +2224,11 @@ int launch_topk(const float* scores, int64_t ld, int64_t batch, int64_t T, int64
     if (nv_min > N) nv_min = N;
     if (rows < 256 && nv_max > kShortRow && nv_max <= kRRow && nv_min >= 8 * (int64_t)k) {
         hipLaunchKernelGGL(topk_regs, grid, dim3(kRThreads), 0, stream, scores, ld, T, q_pos0, N, m, k, idx, sel);
+        return 0;
+    }
+    if (nv_max <= kWvRow) {   // prefill rows of up to 2048 entries: one wave per row
+        hipLaunchKernelGGL(topk_wave, dim3((unsigned)((rows + kWvRows - 1) / kWvRows)), dim3(kWvRows * kWave), 0,
+                           stream, scores, ld, T, q_pos0, N, m, k, rows, idx, sel);
         return 0;
     }
     if (nv_max <= kShortRow)   // short rows (prefill): small workgroups, several rows per CU

@@ -220,7 +220,15 @@ def test_topk_bit_exact_on_the_gpu_scores(case):
     assert np.array_equal(sel, ref_sel.astype(np.float32).astype(np.float64))
 
 
-CSA_TOPK_CASES = [  # batch, T, q_pos0, N, k, integer-valued scores (ties)
+CSA_TOPK_CASES = [  # batch, T, q_pos0, N, k, scores: 0 continuous, 1 integer (ties), 2 all equal, 3 signed with +-0
+    # rows of up to 2048 entries: one wave per row
+    (1, 8, 4 * 2048 - 20, 2048, 512, 0),            # rows of 2043 .. 2048 entries (ragged last lane group)
+    (2, 6, 4 * 1500 - 11, 1500, 512, 1),            # ~40-way ties at the cut, two sequences
+    (1, 3, 4 * 1000, 1000, 100, 2),                 # every score equal: the first k ids
+    (3, 5, 4 * 700 - 9, 700, 300, 3),               # negative and positive scores, +0 and -0 equal
+    (1, 5, 4 * 900 - 3, 900, 1, 0),                 # k = 1
+    (1, 4, 4 * 700, 700, 699, 1),                   # all but one entry kept
+    (2, 700, 0, 600, 64, 0),                        # early rows with fewer than k entries, 1400 rows
     (1, 6, 4 * 3000 - 9, 3000, 512, True),          # short rows: small workgroups
     (2, 2, 4 * 20000 - 3, 20000, 1024, False),      # register-staged rows
     (1, 5, 4 * 10000 - 17, 10000, 2048, True),      # rows staged in LDS (fewer than 8k entries)
@@ -231,18 +239,25 @@ CSA_TOPK_CASES = [  # batch, T, q_pos0, N, k, integer-valued scores (ties)
 ]
 
 
-@pytest.mark.parametrize("case", CSA_TOPK_CASES, ids=lambda c: "b%d_T%d_p%d_N%d_k%d_int%d" % c)
+@pytest.mark.parametrize("case", CSA_TOPK_CASES, ids=lambda c: "b%d_T%d_p%d_N%d_k%d_s%d" % c)
 def test_csa_topk_on_caller_scores(case):
     """csa_topk (the selection alone, through the C ABI) on fp32 score rows the caller supplies,
     bit-exact against the oracle's rule (score desc, index asc; ids ascending, -1 padded).
     Rows of several lengths per call (consecutive query positions) reach every one-workgroup
     selection kernel, including rows longer than 32768 and 262144 visible entries."""
-    batch, T, p0, N, k, integer = case
+    batch, T, p0, N, k, kind = case
     m = 4
     say(f"csa_topk {case}")
     r = np.random.RandomState(2300 + N + k)
-    if integer:
+    if kind == 1:
         sc = r.randint(0, 40, size=(batch, T, N)).astype(np.float32)
+    elif kind == 2:
+        sc = np.full((batch, T, N), 1.5, np.float32)
+    elif kind == 3:
+        sc = r.standard_normal((batch, T, N)).astype(np.float32)
+        u = r.random_sample((batch, T, N))
+        sc[u < 0.1] = 0.0
+        sc[u < 0.05] = -0.0
     else:
         sc = r.standard_normal((batch, T, N)).astype(np.float32) * 30 + 100
     ref_idx, ref_sel = oracle.topk(sc.astype(np.float64), m, k, q_pos0=p0)
