@@ -1032,6 +1032,7 @@ struct GroupShared {
     uint32_t red_lo[kGWaves], red_hi[kGWaves];
     uint32_t ctl[3];   // radix select state
     uint32_t ngroups, ncand;
+    uint32_t neq;      // entries with key == K* (all of them are taken when need_eq equals it)
 };
 static_assert(kGMaxRow / 32 >= kGMaxGroups, "group keys share the tie bitmap");
 
@@ -1190,18 +1191,32 @@ topk_groups(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
     uint32_t kstar = 0u, need_eq = 0u;
     int64_t ncand = 0;
     if (MODE == 2 && !full) {
-        // the candidates the slices appended: keys and indices into LDS, their range
+        // the candidates the slices appended: keys and indices into LDS, their range.  The
+        // list's first kGCap slots are loaded together with its length (one memory round trip
+        // instead of two; slots past the length hold stale values and are dropped)
+        constexpr int kCPer = kGCap / kGThreads;
+        float cv[kCPer];
+        int32_t ci[kCPer];
+#pragma unroll
+        for (int u = 0; u < kCPer; ++u) {
+            cv[u] = cval[row * kMCap + tid + u * kGThreads];
+            ci[u] = cidx[row * kMCap + tid + u * kGThreads];
+        }
         ncand = ccount[row * ccount_ld];
         if (ncand > kGCap || ncand < k) {
             full = true;   // heavy ties at b* (the second cannot happen)
         } else {
             uint32_t lo = ~0u, hi = 0u;
-            for (int64_t i2 = tid; i2 < ncand; i2 += kGThreads) {
-                const uint32_t key = order_key(cval[row * kMCap + i2]);
-                sh.ckey[i2] = key;
-                sh.cidx[i2] = cidx[row * kMCap + i2];
-                lo = min(lo, key);
-                hi = max(hi, key);
+#pragma unroll
+            for (int u = 0; u < kCPer; ++u) {
+                const int i2 = tid + u * kGThreads;
+                if (i2 < ncand) {
+                    const uint32_t key = order_key(cv[u]);
+                    sh.ckey[i2] = key;
+                    sh.cidx[i2] = ci[u];
+                    lo = min(lo, key);
+                    hi = max(hi, key);
+                }
             }
             block_minmax(lo, hi, sh);   // (its barrier also publishes the candidates)
             kstar = radix_kth<kGThreads>(
@@ -1447,14 +1462,21 @@ topk_groups(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
         sh.a[w] = 0u;
         sh.b[w] = 0u;
     }
+    if (tid == 0) sh.neq = 0u;
     __syncthreads();
     if (!full) {
+        uint32_t neq = 0u;
         for (int64_t i = tid; i < ncand; i += kGThreads) {
             const uint32_t key = sh.ckey[i];
             const int32_t e = sh.cidx[i];
-            if (key > kstar) atomicOr(&sh.b[e >> 5], 1u << (e & 31));
-            else if (key == kstar) atomicOr(&sh.a[e >> 5], 1u << (e & 31));
+            if (key > kstar) {
+                atomicOr(&sh.b[e >> 5], 1u << (e & 31));
+            } else if (key == kstar) {
+                atomicOr(&sh.a[e >> 5], 1u << (e & 31));
+                ++neq;
+            }
         }
+        if (neq != 0u) atomicAdd(&sh.neq, neq);
     } else {
         // one ballot per 64 entries gives two words of each bitmap
         for (int64_t b0 = (int64_t)wid * kWave; b0 < nv; b0 += kGThreads) {
@@ -1464,6 +1486,7 @@ topk_groups(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
             const unsigned long long gt = __ballot(ok && key > kstar);
             const unsigned long long eq = __ballot(ok && key == kstar);
             if (lane == 0) {
+                if (eq != 0ull) atomicAdd(&sh.neq, (uint32_t)__popcll(eq));
                 sh.b[b0 >> 5] = (uint32_t)gt;
                 sh.a[b0 >> 5] = (uint32_t)eq;
                 if ((b0 >> 5) + 1 < nwords) {
@@ -1510,15 +1533,23 @@ topk_groups(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
         kw[j] = in ? sh.b[w] : 0u;
         cnt[j] = __popc(eq[j]);
     }
-    prefix(cnt, pre);   // the ties before each word decide how many of its own it keeps
+    if (sh.neq == need_eq) {   // every entry equal to K* is taken (block-uniform)
 #pragma unroll
-    for (int j = 0; j < kXR; ++j) {
-        const uint32_t taken = pre[j];
-        uint32_t eqw = eq[j];
-        if (taken >= need_eq) eqw = 0u;
-        else if (taken + __popc(eqw) > need_eq) eqw = first_bits(eqw, need_eq - taken);
-        kw[j] |= eqw;
-        cnt[j] = __popc(kw[j]);
+        for (int j = 0; j < kXR; ++j) {
+            kw[j] |= eq[j];
+            cnt[j] = __popc(kw[j]);
+        }
+    } else {
+        prefix(cnt, pre);   // the ties before each word decide how many of its own it keeps
+#pragma unroll
+        for (int j = 0; j < kXR; ++j) {
+            const uint32_t taken = pre[j];
+            uint32_t eqw = eq[j];
+            if (taken >= need_eq) eqw = 0u;
+            else if (taken + __popc(eqw) > need_eq) eqw = first_bits(eqw, need_eq - taken);
+            kw[j] |= eqw;
+            cnt[j] = __popc(kw[j]);
+        }
     }
     prefix(cnt, pre);   // kept entries before each word
     if (!full) {
