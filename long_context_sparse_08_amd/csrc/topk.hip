@@ -1019,6 +1019,8 @@ constexpr int kGMaxG = 32;           // groups never cross the indexer's 32-entr
 
 constexpr int kGBins = 2048;         // linear bins over the group maxima
 
+constexpr int kGMaxSlices = 32;      // group slices of the longest row (two-launch select)
+
 struct GroupShared {
     uint32_t a[kGMaxRow / 32];   // group maxima (fp32 bits), then the tie bitmap, then word offsets
     uint32_t b[kGMaxRow / 32];   // indices of the selected groups, then the kept bitmap
@@ -1033,6 +1035,9 @@ struct GroupShared {
     uint32_t ctl[3];   // radix select state
     uint32_t ngroups, ncand;
     uint32_t neq;      // entries with key == K* (all of them are taken when need_eq equals it)
+    // two-launch select: slice p's chunk of the candidate list (start, count) and the
+    // candidates of the slices before it
+    uint32_t rbase[kGMaxSlices], rcnt[kGMaxSlices], rpre[kGMaxSlices];
 };
 static_assert(kGMaxRow / 32 >= kGMaxGroups, "group keys share the tie bitmap");
 
@@ -1152,10 +1157,14 @@ __device__ __forceinline__ uint32_t first_bits(uint32_t w, uint32_t n) {
 // candidate step over the chip in two launches:
 // MODE 1 (grid rows x P): workgroup (row, p) finds b* as in step 1 (every workgroup of a row
 //   from the same maxima: the same b*) and appends the candidates of groups p*kSliceGroups ..
-//   (p+1)*kSliceGroups - 1 to the row's list (value, index) in global memory, one atomic per
-//   wave on the row's counter (cleared by the indexer at the start of the call);
-// MODE 2 (grid rows): steps 3-4 from that list (more than kGCap candidates: over the whole row).
+//   (p+1)*kSliceGroups - 1 to the row's list (value, index) in global memory as one chunk in
+//   index order, its place taken by one atomic per workgroup on the row's counter (cleared by
+//   the indexer at the start of the call), and records the chunk (start, count);
+// MODE 2 (grid rows): the exact cut over that list (radix select), then the chunks copied in
+//   slice order, which is index order, and the output placed by one block scan (more than
+//   kGCap candidates: steps 3-4 over the whole row).
 constexpr int kSliceGroups = 256;
+static_assert(kGMaxGroups / kSliceGroups <= kGMaxSlices, "a record per slice");
 
 template <int MODE>
 __global__ void __launch_bounds__(kGThreads)
@@ -1202,6 +1211,9 @@ topk_groups(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
             cv[u] = cval[row * kMCap + tid + u * kGThreads];
             ci[u] = cidx[row * kMCap + tid + u * kGThreads];
         }
+        // slice `tid`'s chunk record (zero for a slice without candidates)
+        const uint32_t rb = tid < P ? ccount[row * ccount_ld + 1 + 2 * tid] : 0u;
+        const uint32_t rc = tid < P ? ccount[row * ccount_ld + 2 + 2 * tid] : 0u;
         ncand = ccount[row * ccount_ld];
         if (ncand > kGCap || ncand < k) {
             full = true;   // heavy ties at b* (the second cannot happen)
@@ -1218,12 +1230,72 @@ topk_groups(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
                     hi = max(hi, key);
                 }
             }
-            block_minmax(lo, hi, sh);   // (its barrier also publishes the candidates)
+            if (wid == 0) {   // the chunks' places in index order (P <= 64: one wave)
+                const uint32_t c = lane < P ? rc : 0u;
+                const uint32_t inc = wave_incl_scan(c);
+                if (lane < P) {
+                    sh.rbase[lane] = rb;
+                    sh.rcnt[lane] = c;
+                    sh.rpre[lane] = inc - c;
+                }
+            }
+            block_minmax(lo, hi, sh);   // (its barrier also publishes the candidates and chunks)
             kstar = radix_kth<kGThreads>(
                 [&](auto f) {
                     for (int64_t i2 = tid; i2 < ncand; i2 += kGThreads) f(sh.ckey[i2]);
                 },
                 (uint32_t)k, lo, hi, sh.hist, sh.ctl, &need_eq);
+            // The candidates in index order: each slice appended its own in index order, and
+            // slices follow each other in the row, so chunk p goes to slots rpre[p] .. of a / b
+            // (threads 32p .. 32p + 31 copy chunk p).  No row bitmap is needed then.
+            {
+                const int p = tid >> 5, j = tid & 31;
+                if (p < P) {
+                    const uint32_t s0 = sh.rbase[p], d0 = sh.rpre[p], n = sh.rcnt[p];
+                    for (uint32_t u = (uint32_t)j; u < n; u += 32u) {
+                        sh.a[d0 + u] = sh.ckey[s0 + u];
+                        sh.b[d0 + u] = (uint32_t)sh.cidx[s0 + u];
+                    }
+                }
+            }
+            __syncthreads();
+            // Ordered output: thread t holds candidates 4t .. 4t+3 (index order); one block scan
+            // of (ties << 16 | greater) counts gives the kept entries before it: every entry
+            // with key > K*, and of the ties (key == K*) the first need_eq in index order.
+            constexpr int kOPer = kGCap / kGThreads;
+            uint32_t gt = 0u, eqm = 0u;
+#pragma unroll
+            for (int u = 0; u < kOPer; ++u) {
+                const int64_t i = (int64_t)kOPer * tid + u;
+                if (i < ncand) {
+                    const uint32_t key = sh.a[i];
+                    gt |= (key > kstar ? 1u : 0u) << u;
+                    eqm |= (key == kstar ? 1u : 0u) << u;
+                }
+            }
+            uint32_t tot;
+            const uint32_t pre =
+                block_excl_scan<kGWaves>(((uint32_t)__popc(eqm) << 16) | (uint32_t)__popc(gt), sh.scan, &tot);
+            const uint32_t tb = pre >> 16, gb = pre & 0xffffu;
+            uint32_t takeq = 0u;
+            if (tb < need_eq) {
+                const uint32_t room = need_eq - tb;
+                takeq = (uint32_t)__popc(eqm) <= room ? eqm : first_bits(eqm, room);
+            }
+            const uint32_t keep = gt | takeq;
+            uint32_t slot = gb + min(tb, need_eq);
+#pragma unroll
+            for (int u = 0; u < kOPer; ++u) {
+                if ((keep >> u) & 1u) {
+                    const int64_t i = (int64_t)kOPer * tid + u;
+                    if (slot < (uint32_t)k) {
+                        oi[slot] = (int32_t)sh.b[i];
+                        if (os) os[slot] = key_value(sh.a[i]);
+                    }
+                    ++slot;
+                }
+            }
+            return;
         }
     }
     if (MODE != 2 && !full) {
@@ -1280,8 +1352,9 @@ topk_groups(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
         auto in_b = [&](int64_t e, float x) { return e < nv && bin_of_n<kGBins>(x, flo, inv) >= bstar; };
         if constexpr (MODE == 1) {
             // this slice's groups whose maximum is in a bin >= b*: their entries in bins >= b*
-            // (G >= 4: 16-byte pieces, 1 << lq per group, kSP per thread, all loads in flight
-            // together); placed by one block scan and one atomic per workgroup on the row's count
+            // (G >= 4: 16-byte pieces, 1 << lq per group, kSP consecutive ones per thread, all
+            // loads in flight together); placed by one block scan (so the slice's chunk of the
+            // list is in index order) and one atomic per workgroup on the row's count
             constexpr int kSP = kSliceGroups * (kGMaxG / 4) / kGThreads;
             const int lq = __builtin_ctz((unsigned)G) - 2;
             const int64_t j0 = (int64_t)slice * kSliceGroups, j1 = min(ng, j0 + kSliceGroups);
@@ -1290,7 +1363,7 @@ topk_groups(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
             float xs[4 * kSP];
 #pragma unroll
             for (int u = 0; u < kSP; ++u) {
-                const int q = tid + u * kGThreads;
+                const int q = kSP * tid + u;
                 const int64_t j = j0 + (q >> lq);
                 e0[u] = (q < npieces && bin_of_n<kGBins>(gv[j], flo, inv) >= bstar)
                             ? (j << (lq + 2)) + ((int64_t)(q & ((1 << lq) - 1)) << 2) : -1;
@@ -1310,7 +1383,13 @@ topk_groups(const float* __restrict__ scores, int64_t ld, int64_t T, int64_t q_p
             uint32_t total;
             const uint32_t pre = block_excl_scan<kGWaves>((uint32_t)__popc(mask), sh.scan, &total);
             if (total == 0u) return;
-            if (tid == 0) sh.ngroups = atomicAdd(&ccount[row * ccount_ld], total);
+            if (tid == 0) {
+                const uint32_t at0 = atomicAdd(&ccount[row * ccount_ld], total);
+                sh.ngroups = at0;
+                // this slice's chunk of the list (its candidates in index order): start, count
+                ccount[row * ccount_ld + 1 + 2 * slice] = at0;
+                ccount[row * ccount_ld + 2 + 2 * slice] = total;
+            }
             __syncthreads();
             uint32_t at = sh.ngroups + pre;
 #pragma unroll
@@ -2224,11 +2303,12 @@ int launch_topk(const float* scores, int64_t ld, int64_t batch, int64_t T, int64
             MultiWs L;
             multi_bytes(rows, N, &L, extra_ws);
             const int P = (int)(((nv_max + G - 1) / G + kSliceGroups - 1) / kSliceGroups);
+            // (each row's zeroed region: word 0 the list length, words 1 + 2p, 2 + 2p slice p's chunk)
+            static_assert(1 + 2 * kGMaxSlices <= kZeroWords, "the chunk records fit the row's zeroed words");
             hipLaunchKernelGGL(topk_groups<1>, dim3((unsigned)((rows + 7) / 8 * 8 * P)), dim3(kGThreads), 0, stream, scores, ld, T,
-                               q_pos0, N, m, k, gmax, gld, G, idx, sel, rows, P, L.zero + kBins, kZeroWords, L.cval,
-                               L.cidx);
+                               q_pos0, N, m, k, gmax, gld, G, idx, sel, rows, P, L.zero, kZeroWords, L.cval, L.cidx);
             hipLaunchKernelGGL(topk_groups<2>, dim3((unsigned)rows), dim3(kGThreads), 0, stream, scores, ld, T, q_pos0,
-                               N, m, k, gmax, gld, G, idx, sel, rows, P, L.zero + kBins, kZeroWords, L.cval, L.cidx);
+                               N, m, k, gmax, gld, G, idx, sel, rows, P, L.zero, kZeroWords, L.cval, L.cidx);
             return 0;
         }
         hipLaunchKernelGGL(topk_groups<0>, dim3((unsigned)rows), dim3(kGThreads), 0, stream, scores, ld, T, q_pos0, N,
