@@ -349,8 +349,8 @@ def main():
         stages["select"] = (pipe.select, ["index_scores_mfma", "topk"], None)
         # (decode launches have at most one workgroup per CU: the warp-specialised kernel)
         stages["attend"] = (pipe.attend, ["mqa_sparse_ws"] + (["mqa_combine"] if split else []), "mqa")
-        if with_compress:   # the two decode-step compressions (KV and index-key entries)
-            stages["compress_step"] = (pipe.compress, ["compress_kernel", "compress_kernel"], "compress_step")
+        if with_compress:   # the decode-step compression of the KV and index-key entries (one launch)
+            stages["compress_step"] = (pipe.compress, ["compress_pair_kernel"], "compress_step")
     elif cfg.kind == "csa_compress":
         stages["compress"] = (pipe.run, ["compress_kernel"], "compress")
     elif cfg.kind == "csa_prefill":

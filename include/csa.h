@@ -317,6 +317,29 @@ int hca_dense_mqa_swa(const void* q, const void* kv, int64_t batch, int64_t T, i
 int hca_compress_step(const void* C, const void* Z, const float* B, int64_t batch, int64_t block, int m_prime, int c,
                       csa_dtype in_t, void* cache, int64_t cache_rows, csa_dtype out_t, csa_stream_t stream);
 
+/*
+ * csa_compress_step_kv_index — the decode-step compression of one CSA layer ([N] §1.1 step 1:
+ * the KV entries and the indexer's keys are compressed from the same tokens by the same
+ * overlapped softmax pooling, each stream with its own weights; [M] "state cache"): once block
+ * `block` is complete, its KV entry and its index-key entry, each exactly as csa_compress_step
+ * computes it (the same bits), written to row `block` of the two caches.  One kernel launch
+ * when m == 4 (the pages' CSA ratio), else two.
+ *   Ca, Cb, Za, Zb, Ba, Bb     : the KV state [batch, 2m, c] ([batch, m, c] when block == 0) and
+ *                                [m, c] fp32 biases, as csa_compress_step
+ *   kv_cache                   : [batch, kv_rows, c] dtype kv_t
+ *   ICa, ICb, IZa, IZb, IBa, IBb : the index-key state [batch, 2m, c_I] (or [batch, m, c_I]) and
+ *                                [m, c_I] fp32 biases
+ *   ki_cache                   : [batch, ki_rows, c_I] dtype ki_t
+ *   in_t                       : dtype of both states (CSA_F32 or CSA_BF16)
+ * Limits: as csa_compress_step for each stream; block < kv_rows and block < ki_rows.  Errors
+ * are reported before anything is launched.
+ */
+int csa_compress_step_kv_index(const void* Ca, const void* Cb, const void* Za, const void* Zb, const float* Ba,
+                               const float* Bb, int c, void* kv_cache, int64_t kv_rows, csa_dtype kv_t,
+                               const void* ICa, const void* ICb, const void* IZa, const void* IZb, const float* IBa,
+                               const float* IBb, int c_I, void* ki_cache, int64_t ki_rows, csa_dtype ki_t,
+                               int64_t batch, int64_t block, int m, csa_dtype in_t, csa_stream_t stream);
+
 /* Human-readable name of a csa_status value (static storage). */
 const char* csa_status_string(int status);
 

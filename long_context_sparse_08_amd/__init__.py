@@ -24,7 +24,7 @@ NOALLOC_SCRATCH_BYTES = 32 << 20   # CSA_NOALLOC_SCRATCH_BYTES
 ENTRY_POINTS = ("csa_compress", "hca_compress", "csa_index_topk_workspace_size", "csa_index_topk",
                 "csa_index_topk_noalloc",
                 "csa_index_scores", "csa_topk_workspace_size", "csa_topk", "csa_sparse_mqa_workspace_size", "csa_sparse_mqa",
-                "hca_dense_mqa", "csa_sparse_mqa_sink", "hca_dense_mqa_sink", "csa_sparse_mqa_swa", "csa_rope", "csa_compress_step", "hca_dense_mqa_swa", "hca_compress_step", "csa_status_string",
+                "hca_dense_mqa", "csa_sparse_mqa_sink", "hca_dense_mqa_sink", "csa_sparse_mqa_swa", "csa_rope", "csa_compress_step", "hca_dense_mqa_swa", "hca_compress_step", "csa_compress_step_kv_index", "csa_status_string",
                 "csa_version")
 
 
@@ -58,6 +58,8 @@ def _load():
         "hca_dense_mqa_sink": ([P, P, I64, I64, I64, I64, I, I, I, F, P, I, P, P], I),
         "hca_dense_mqa_swa": ([P, P, I64, I64, I64, I64, I, I, I, F, P, P, I64, I64, I, I, P, P], I),
         "hca_compress_step": ([P, P, P, I64, I64, I, I, I, P, I64, I, P], I),
+        "csa_compress_step_kv_index": ([P, P, P, P, P, P, I, P, I64, I, P, P, P, P, P, P, I, P, I64, I, I64, I64, I, I, P],
+                                       I),
         "csa_status_string": ([I], ctypes.c_char_p),
         "csa_version": ([], I),
     }
@@ -366,19 +368,45 @@ def csa_sparse_mqa(q, kv, idx, scale: float, out=None, workspace=None, sink=None
 def csa_compress_step(Ca, Cb, Za, Zb, Ba, Bb, block: int, cache):
     """Decode-step CSA compression: the state streams [batch, 2m, c] (blocks block-1 and block;
     [batch, m, c] when block == 0) -> row `block` of cache [batch, rows, c], in place."""
-    _need(Ca.dim() == 3 and Ba.dim() == 2 and cache.dim() == 3, "state [batch, rows, c], biases [m, c], cache 3-d")
-    batch, ns, c = Ca.shape
-    m = Ba.shape[0]
-    _need(ns == (2 * m if block > 0 else m), f"state: {2 * m if block > 0 else m} tokens per sequence")
-    for nm, t in (("Cb", Cb), ("Za", Za), ("Zb", Zb)):
-        _check_out(t, Ca.shape, Ca.dtype, nm)
-    _check_out(Ba, (m, c), torch.float32, "Ba")
-    _check_out(Bb, (m, c), torch.float32, "Bb")
-    _need(cache.shape[0] == batch and cache.shape[2] == c and 0 <= block < cache.shape[1], "cache: row `block` of [batch, rows, c]")
+    batch, m, c = _step_state(Ca, Cb, Za, Zb, Ba, Bb, block, cache, "KV")
     dev = _dev(Ca, Cb, Za, Zb, Ba, Bb, cache)
     _check("csa_compress_step", lib.csa_compress_step(_p(Ca), _p(Cb), _p(Za), _p(Zb), _p(Ba), _p(Bb), batch, block, m, c,
                                                       _dt(Ca), _p(cache), cache.shape[1], _dt(cache), _stream(dev)))
     return cache
+
+
+def _step_state(Ca, Cb, Za, Zb, Ba, Bb, block: int, cache, what: str):
+    # the checks of csa_compress_step for one state and its cache; returns (batch, m, c)
+    _need(Ca.dim() == 3 and Ba.dim() == 2 and cache.dim() == 3,
+          f"{what}: state [batch, rows, c], biases [m, c], cache 3-d")
+    batch, ns, c = Ca.shape
+    m = Ba.shape[0]
+    _need(ns == (2 * m if block > 0 else m), f"{what} state: {2 * m if block > 0 else m} tokens per sequence")
+    for nm, t in (("Cb", Cb), ("Za", Za), ("Zb", Zb)):
+        _check_out(t, Ca.shape, Ca.dtype, f"{what} {nm}")
+    _check_out(Ba, (m, c), torch.float32, f"{what} Ba")
+    _check_out(Bb, (m, c), torch.float32, f"{what} Bb")
+    _need(cache.shape[0] == batch and cache.shape[2] == c and 0 <= block < cache.shape[1],
+          f"{what} cache: row `block` of [batch, rows, c]")
+    return batch, m, c
+
+
+def csa_compress_step_kv_index(kv_state, kv_cache, ki_state, ki_cache, block: int):
+    """The decode-step compression of one CSA layer: kv_state = (Ca, Cb, Za, Zb, Ba, Bb) and
+    ki_state = (ICa, ICb, IZa, IZb, IBa, IBb), each as csa_compress_step takes it, -> row `block`
+    of kv_cache and of ki_cache, in place (one launch at m = 4; the same bits as two
+    csa_compress_step calls)."""
+    _need(len(kv_state) == 6 and len(ki_state) == 6, "states are (Ca, Cb, Za, Zb, Ba, Bb)")
+    batch, m, c = _step_state(*kv_state, block, kv_cache, "KV")
+    bi, mi, ci = _step_state(*ki_state, block, ki_cache, "index-key")
+    _need(bi == batch and mi == m, "both states: the same batch and m")
+    _need(ki_state[0].dtype == kv_state[0].dtype, "both states: the same dtype")
+    dev = _dev(*kv_state, kv_cache, *ki_state, ki_cache)
+    _check("csa_compress_step_kv_index",
+           lib.csa_compress_step_kv_index(*[_p(t) for t in kv_state], c, _p(kv_cache), kv_cache.shape[1], _dt(kv_cache),
+                                          *[_p(t) for t in ki_state], ci, _p(ki_cache), ki_cache.shape[1],
+                                          _dt(ki_cache), batch, block, m, _dt(kv_state[0]), _stream(dev)))
+    return kv_cache, ki_cache
 
 
 def csa_rope(x, pos0: int, pos_step: int = 1, d: int = 64, base: float = 10000.0, inverse: bool = False):

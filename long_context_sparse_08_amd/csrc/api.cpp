@@ -100,9 +100,11 @@ int csa_compress(const void* Ca, const void* Cb, const void* Za, const void* Zb,
                                        static_cast<hipStream_t>(stream)));
 }
 
-int csa_compress_step(const void* Ca, const void* Cb, const void* Za, const void* Zb, const float* Ba,
-                      const float* Bb, int64_t batch, int64_t block, int m, int c, csa_dtype in_t, void* cache,
-                      int64_t cache_rows, csa_dtype out_t, csa_stream_t stream) {
+namespace {
+// the checks of csa_compress_step for one stream (CSA_OK: valid)
+int step_stream_status(const void* Ca, const void* Cb, const void* Za, const void* Zb, const float* Ba,
+                       const float* Bb, int64_t batch, int64_t block, int m, int c, csa_dtype in_t, const void* cache,
+                       int64_t cache_rows, csa_dtype out_t) {
     if (batch < 0 || block < 0 || m < 1 || c < 1 || cache_rows <= block) return CSA_ERR_INVALID_ARG;
     if (!io_dtype(in_t) || !compress_out_dtype(out_t)) return CSA_ERR_UNSUPPORTED;
     if (!width_ok(c) || m > CSA_MAX_RATIO) return CSA_ERR_UNSUPPORTED;
@@ -111,9 +113,36 @@ int csa_compress_step(const void* Ca, const void* Cb, const void* Za, const void
     if (!aligned16(Ca) || !aligned16(Za) || !aligned16(Ba) || !aligned16(cache) ||
         (block > 0 && (!aligned16(Cb) || !aligned16(Zb) || !aligned16(Bb))))
         return CSA_ERR_INVALID_ARG;
+    return CSA_OK;
+}
+}  // namespace
+
+int csa_compress_step(const void* Ca, const void* Cb, const void* Za, const void* Zb, const float* Ba,
+                      const float* Bb, int64_t batch, int64_t block, int m, int c, csa_dtype in_t, void* cache,
+                      int64_t cache_rows, csa_dtype out_t, csa_stream_t stream) {
+    const int rc = step_stream_status(Ca, Cb, Za, Zb, Ba, Bb, batch, block, m, c, in_t, cache, cache_rows, out_t);
+    if (rc != CSA_OK || batch == 0) return rc;
     return finish(csa::launch_compress_step(Ca, Za, Ba, block > 0 ? Cb : Ca, block > 0 ? Zb : Za, block > 0 ? Bb : Ba,
                                             batch, block, m, c, in_t, cache, cache_rows, out_t,
                                             static_cast<hipStream_t>(stream)));
+}
+
+int csa_compress_step_kv_index(const void* Ca, const void* Cb, const void* Za, const void* Zb, const float* Ba,
+                               const float* Bb, int c, void* kv_cache, int64_t kv_rows, csa_dtype kv_t,
+                               const void* ICa, const void* ICb, const void* IZa, const void* IZb, const float* IBa,
+                               const float* IBb, int c_I, void* ki_cache, int64_t ki_rows, csa_dtype ki_t,
+                               int64_t batch, int64_t block, int m, csa_dtype in_t, csa_stream_t stream) {
+    int rc = step_stream_status(Ca, Cb, Za, Zb, Ba, Bb, batch, block, m, c, in_t, kv_cache, kv_rows, kv_t);
+    if (rc != CSA_OK) return rc;
+    rc = step_stream_status(ICa, ICb, IZa, IZb, IBa, IBb, batch, block, m, c_I, in_t, ki_cache, ki_rows, ki_t);
+    if (rc != CSA_OK) return rc;
+    if (batch == 0) return CSA_OK;
+    // (block 0: the one-block state stands in for the missing previous block, which is masked)
+    const csa::StepStreams kv{Ca, Za, Ba, block > 0 ? Cb : Ca, block > 0 ? Zb : Za, block > 0 ? Bb : Ba,
+                              c, kv_cache, kv_rows, kv_t};
+    const csa::StepStreams ki{ICa, IZa, IBa, block > 0 ? ICb : ICa, block > 0 ? IZb : IZa, block > 0 ? IBb : IBa,
+                              c_I, ki_cache, ki_rows, ki_t};
+    return finish(csa::launch_compress_step_pair(kv, ki, batch, block, m, in_t, static_cast<hipStream_t>(stream)));
 }
 
 int hca_compress(const void* C, const void* Z, const float* B, int64_t batch, int64_t n, int m_prime, int c,

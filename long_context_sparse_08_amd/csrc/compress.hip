@@ -50,13 +50,15 @@ struct CompressArgs {
 // runs from registers: the same arithmetic in the same order as PRE == 0, so the results are
 // identical bit for bit.  For launches of a few entries (a decode step), where nothing hides a
 // memory round trip per position (32 entries: 5.1 us against 6.2 without the preload).
+// The entries of workgroup `wg` (epb per workgroup, split threads-rows per entry); sm is the
+// workgroup's merge area (used when split > 1).
 template <int DTI, int DTO, int CH, int PRE>
-__global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a, int G, int split, int epb) {
-    __shared__ float sm[3][kThreads][8];
+__device__ __forceinline__ void compress_entries(const CompressArgs& a, int G, int split, int epb, int64_t wg,
+                                                 float (&sm)[3][kThreads][8]) {
     const int tid = threadIdx.x;
     const int row = tid / G, g = tid - row * G;
     const int e_local = row / split, part = row - e_local * split;
-    const int64_t ent = (int64_t)blockIdx.x * epb + e_local;
+    const int64_t ent = wg * epb + e_local;
     const int64_t per_seq = a.N - a.first;
     const bool active = (g < G) && (row < epb * split) && (ent < a.batch * per_seq);
     const bool overlap = a.Cb != nullptr;
@@ -197,6 +199,23 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a, int 
     }
 }
 
+template <int DTI, int DTO, int CH, int PRE>
+__global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a, int G, int split, int epb) {
+    __shared__ float sm[3][kThreads][8];
+    compress_entries<DTI, DTO, CH, PRE>(a, G, split, epb, blockIdx.x, sm);
+}
+
+// Two decode-step compressions of m = 4 in one launch (a CSA layer's KV entry and index-key
+// entry): workgroups 0 .. wgs0-1 compute a0's entries, the rest a1's, each as the one-wave
+// decode-step launch of compress_kernel would (the same arithmetic, so the same bits).
+template <int DTI, int DTO0, int DTO1>
+__global__ void __launch_bounds__(kThreads) compress_pair_kernel(CompressArgs a0, int G0, int epw0, int64_t wgs0,
+                                                                 CompressArgs a1, int G1, int epw1) {
+    __shared__ float sm[3][kThreads][8];
+    if ((int64_t)blockIdx.x < wgs0) compress_entries<DTI, DTO0, 2, 8>(a0, G0, 1, epw0, blockIdx.x, sm);
+    else compress_entries<DTI, DTO1, 2, 8>(a1, G1, 1, epw1, blockIdx.x - wgs0, sm);
+}
+
 template <int DTI, int DTO>
 int launch(const CompressArgs& a, hipStream_t stream) {
     const int G = a.c / 8;                     // threads per entry row
@@ -209,10 +228,14 @@ int launch(const CompressArgs& a, hipStream_t stream) {
     const int64_t entries = a.batch * (a.N - a.first);
     const int64_t blocks = (entries + epb - 1) / epb;
     if (blocks > 0x7fffffffLL) return -2;
-    if (split == 1 && a.Cb != nullptr && a.m == 4 && entries < 2048)   // a few CSA entries (a decode step)
-        hipLaunchKernelGGL((compress_kernel<DTI, DTO, 2, 8>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a,
-                           G, split, epb);
-    else if (split == 1 && W <= 8)   // short (CSA) windows
+    if (split == 1 && a.Cb != nullptr && a.m == 4 && entries < 2048) {
+        // a few CSA entries (a decode step): one-wave workgroups (whole entries each) spread the
+        // loads over as many CUs as possible (32 entries of c = 512: 32 CUs instead of 8)
+        const int nt = (G + kWave - 1) / kWave * kWave;
+        const int epw = nt / G;
+        hipLaunchKernelGGL((compress_kernel<DTI, DTO, 2, 8>), dim3((unsigned)((entries + epw - 1) / epw)), dim3(nt), 0,
+                           stream, a, G, 1, epw);
+    } else if (split == 1 && W <= 8)   // short (CSA) windows
         hipLaunchKernelGGL((compress_kernel<DTI, DTO, 2, 0>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a,
                            G, split, epb);
     else
@@ -222,6 +245,44 @@ int launch(const CompressArgs& a, hipStream_t stream) {
 }
 
 int launch_any(const CompressArgs& a, int in_t, int out_t, hipStream_t stream);
+
+// the arguments of a decode step: the state holds the raw tokens of blocks block-1 and block
+// (only block 0 when block == 0), so entry `block` is the last entry of that 2m- (or m-) token
+// sequence
+CompressArgs step_args(const void* Ca, const void* Za, const float* Ba, const void* Cb, const void* Zb,
+                       const float* Bb, int64_t batch, int64_t block, int m, int c, void* cache, int64_t cache_rows) {
+    const int64_t ns = block > 0 ? 2 * (int64_t)m : m;
+    return CompressArgs{Ca, Za, Ba, Cb, Zb, Bb, batch, ns, ns / m, m, c, cache, ns / m - 1, cache_rows, block};
+}
+
+template <int DTI, int DTO0, int DTO1>
+int launch_pair(const CompressArgs& a0, const CompressArgs& a1, hipStream_t stream) {
+    const int G0 = a0.c / 8, G1 = a1.c / 8;
+    const int nt = max((G0 + kWave - 1) / kWave, (G1 + kWave - 1) / kWave) * kWave;   // <= kThreads
+    const int epw0 = nt / G0, epw1 = nt / G1;
+    const int64_t w0 = (a0.batch * (a0.N - a0.first) + epw0 - 1) / epw0;
+    const int64_t w1 = (a1.batch * (a1.N - a1.first) + epw1 - 1) / epw1;
+    if (w0 + w1 > 0x7fffffffLL) return -2;
+    hipLaunchKernelGGL((compress_pair_kernel<DTI, DTO0, DTO1>), dim3((unsigned)(w0 + w1)), dim3(nt), 0, stream, a0, G0,
+                       epw0, w0, a1, G1, epw1);
+    return 0;
+}
+
+template <int DTI, int DTO0>
+int launch_pair_out1(const CompressArgs& a0, const CompressArgs& a1, int out1, hipStream_t stream) {
+    if (out1 == DT_F32) return launch_pair<DTI, DTO0, DT_F32>(a0, a1, stream);
+    if (out1 == DT_BF16) return launch_pair<DTI, DTO0, DT_BF16>(a0, a1, stream);
+    if (out1 == DT_FP8) return launch_pair<DTI, DTO0, DT_FP8>(a0, a1, stream);
+    return -2;
+}
+
+template <int DTI>
+int launch_pair_out0(const CompressArgs& a0, const CompressArgs& a1, int out0, int out1, hipStream_t stream) {
+    if (out0 == DT_F32) return launch_pair_out1<DTI, DT_F32>(a0, a1, out1, stream);
+    if (out0 == DT_BF16) return launch_pair_out1<DTI, DT_BF16>(a0, a1, out1, stream);
+    if (out0 == DT_FP8) return launch_pair_out1<DTI, DT_FP8>(a0, a1, out1, stream);
+    return -2;
+}
 
 }  // namespace
 
@@ -235,12 +296,24 @@ int launch_compress(const void* Ca, const void* Za, const float* Ba, const void*
 int launch_compress_step(const void* Ca, const void* Za, const float* Ba, const void* Cb, const void* Zb,
                          const float* Bb, int64_t batch, int64_t block, int m, int c, int in_t, void* cache,
                          int64_t cache_rows, int out_t, hipStream_t stream) {
-    // the state holds the raw tokens of blocks block-1 and block (only block 0 when block == 0):
-    // entry `block` is the last entry of that 2m- (or m-) token sequence
-    const int64_t ns = block > 0 ? 2 * (int64_t)m : m;
-    CompressArgs a{Ca, Za, Ba, Cb, Zb, Bb, batch, ns, ns / m, m, c, cache, ns / m - 1, cache_rows, block};
     if (batch == 0) return 0;
-    return launch_any(a, in_t, out_t, stream);
+    return launch_any(step_args(Ca, Za, Ba, Cb, Zb, Bb, batch, block, m, c, cache, cache_rows), in_t, out_t, stream);
+}
+
+int launch_compress_step_pair(const StepStreams& s0, const StepStreams& s1, int64_t batch, int64_t block, int m,
+                              int in_t, hipStream_t stream) {
+    if (batch == 0) return 0;
+    const CompressArgs a0 = step_args(s0.Ca, s0.Za, s0.Ba, s0.Cb, s0.Zb, s0.Bb, batch, block, m, s0.c, s0.cache,
+                                      s0.cache_rows);
+    const CompressArgs a1 = step_args(s1.Ca, s1.Za, s1.Ba, s1.Cb, s1.Zb, s1.Bb, batch, block, m, s1.c, s1.cache,
+                                      s1.cache_rows);
+    if (m != 4) {   // (the one-launch kernel is the m = 4 window kernel)
+        const int r = launch_any(a0, in_t, s0.out_t, stream);
+        return r != 0 ? r : launch_any(a1, in_t, s1.out_t, stream);
+    }
+    if (in_t == DT_F32) return launch_pair_out0<DT_F32>(a0, a1, s0.out_t, s1.out_t, stream);
+    if (in_t == DT_BF16) return launch_pair_out0<DT_BF16>(a0, a1, s0.out_t, s1.out_t, stream);
+    return -2;
 }
 
 int launch_hca_compress_step(const void* C, const void* Z, const float* B, int64_t batch, int64_t block, int m_prime,

@@ -19,6 +19,26 @@ int launch_compress_step(const void* Ca, const void* Za, const float* Ba, const 
                          const float* Bb, int64_t batch, int64_t block, int m, int c, int in_t, void* cache,
                          int64_t cache_rows, int out_t, hipStream_t stream);
 
+// The state and cache of one decode-step compression (as launch_compress_step takes them).
+struct StepStreams {
+    const void* Ca;
+    const void* Za;
+    const float* Ba;
+    const void* Cb;
+    const void* Zb;
+    const float* Bb;
+    int c;
+    void* cache;
+    int64_t cache_rows;
+    int out_t;
+};
+
+// Two decode-step compressions with the same batch, block, m and input dtype (a CSA layer's KV
+// entry and index-key entry): one launch when m == 4, else two launch_compress_step launches.
+// The results are those of the two separate calls, bit for bit.
+int launch_compress_step_pair(const StepStreams& s0, const StepStreams& s1, int64_t batch, int64_t block, int m,
+                              int in_t, hipStream_t stream);
+
 // Indexer scores for every (query, entry) pair into `scores` ([batch*T, ld] fp32, ld >= N).
 // write_invisible: also write -inf for entries the query may not see (else they are skipped).
 // chunk_mm (optional, [batch*T, index_chunks(...)] pairs): min / max of each chunk of visible

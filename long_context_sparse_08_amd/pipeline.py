@@ -17,7 +17,7 @@ import math
 
 import torch
 
-from . import (CSA_KV_FP8_BF16, KVFp8Bf16, csa_compress, csa_compress_step, csa_index_topk, csa_sparse_mqa,
+from . import (CSA_KV_FP8_BF16, KVFp8Bf16, csa_compress, csa_compress_step_kv_index, csa_index_topk, csa_sparse_mqa,
                hca_compress, hca_dense_mqa, mqa_workspace_for, workspace_for)
 
 
@@ -92,8 +92,8 @@ class CsaDecode:
         the caches (entry N-1), computed from the state of its two blocks and written in place."""
         i = self.inp
         blk = i["kv"].shape[1] - 1
-        csa_compress_step(i["Ca"], i["Cb"], i["Za"], i["Zb"], i["Ba"], i["Bb"], blk, i["kv"])
-        csa_compress_step(i["ICa"], i["ICb"], i["IZa"], i["IZb"], i["IBa"], i["IBb"], blk, i["kI"])
+        csa_compress_step_kv_index([i[k] for k in ("Ca", "Cb", "Za", "Zb", "Ba", "Bb")], i["kv"],
+                                   [i[k] for k in ("ICa", "ICb", "IZa", "IZb", "IBa", "IBb")], i["kI"], blk)
 
     def run(self):
         self.select()

@@ -86,6 +86,31 @@ def test_compress_step_rejects_bad_arguments(L):
     assert f(None, None, None, None, None, None, 0, 2, 4, 64, 0, None, 8, 0, None) == OK
 
 
+def test_compress_step_kv_index_rejects_bad_arguments(L):
+    f = L.csa_compress_step_kv_index
+    good = dict(kv=(A,) * 6, c=512, kv_cache=A, kv_rows=8, kv_t=1, ki=(A,) * 6, c_I=128, ki_cache=A, ki_rows=8,
+                ki_t=2, batch=1, block=2, m=4, in_t=1)
+
+    def call(**over):
+        a = dict(good, **over)
+        return f(*a["kv"], a["c"], a["kv_cache"], a["kv_rows"], a["kv_t"], *a["ki"], a["c_I"], a["ki_cache"],
+                 a["ki_rows"], a["ki_t"], a["batch"], a["block"], a["m"], a["in_t"], None)
+
+    assert call(kv_rows=2) == INVALID                       # block past the KV cache
+    assert call(ki_rows=2) == INVALID                       # ... past the index-key cache
+    assert call(ki=(A, None, A, A, A, A)) == INVALID        # no index-key stream b past block 0
+    assert call(kv=(A, A, A, A, MIS, A)) == INVALID
+    assert call(ki_cache=None) == INVALID
+    assert call(c_I=60) == UNSUPPORTED
+    assert call(c=2048) == UNSUPPORTED
+    assert call(in_t=2) == UNSUPPORTED                      # fp8 states are not a compress input
+    assert call(ki_t=5) == UNSUPPORTED
+    assert call(m=0) == INVALID
+    assert call(block=-1) == INVALID
+    assert call(batch=0, kv=(None,) * 6, ki=(None,) * 6, kv_cache=None, ki_cache=None) == OK
+    assert call(batch=0, c_I=60) == UNSUPPORTED             # sizes and dtypes are checked first
+
+
 def test_hca_compress_rejects_bad_arguments(L):
     f = L.hca_compress
     assert f(None, A, A, 1, 256, 128, 64, 0, A, 0, None) == INVALID

@@ -31,6 +31,24 @@ def test_compress_arguments():
         csa.hca_compress_step(z(1, 8, 16), z(1, 8, 16), z(4, 16), 0, z(1, 2, 16))
 
 
+def test_layer_step_compression_arguments():
+    S = z(1, 8, 16)
+    st = (S, S, S, S, z(4, 16), z(4, 16))
+    with pytest.raises(ValueError, match="index-key Zb"):
+        csa.csa_compress_step_kv_index(st, z(1, 9, 16), (S, S, S, z(1, 4, 16), z(4, 16), z(4, 16)), z(1, 9, 16), 3)
+    with pytest.raises(ValueError, match="KV cache"):
+        csa.csa_compress_step_kv_index(st, z(1, 3, 16), st, z(1, 9, 16), 3)
+    with pytest.raises(ValueError, match="same batch"):
+        S2 = z(2, 8, 16)
+        csa.csa_compress_step_kv_index(st, z(1, 9, 16), (S2, S2, S2, S2, z(4, 16), z(4, 16)), z(2, 9, 16), 3)
+    with pytest.raises(ValueError, match="same dtype"):
+        Sb = z(1, 8, 16, dtype=bf16)
+        csa.csa_compress_step_kv_index(st, z(1, 9, 16), (Sb, Sb, Sb, Sb, z(4, 16), z(4, 16)),
+                                       z(1, 9, 16, dtype=bf16), 3)
+    with pytest.raises(ValueError, match="states are"):
+        csa.csa_compress_step_kv_index(st[:5], z(1, 9, 16), st, z(1, 9, 16), 3)
+
+
 def test_indexer_and_selection_arguments():
     qI, kI, w = z(2, 1, 4, 32, dtype=u8), z(2, 100, 32, dtype=u8), z(2, 1, 4)
     with pytest.raises(ValueError, match="w"):

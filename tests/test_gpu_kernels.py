@@ -688,6 +688,51 @@ def test_compress_step_matches_whole_sequence(dt):
     out_tol(dt)(from_dev(cache[:, :nb]), ref, "compress step")
 
 
+@pytest.mark.parametrize("case", [(BF16, 4, 512, 128, FP8, 5), (F32, 4, 64, 32, F32, 3), (F32, 2, 64, 24, BF16, 2)],
+                         ids=["bf16_kv512_ki128fp8_b5", "f32_kv64_ki32_b3", "f32_m2_two_launches"])
+def test_compress_step_kv_index_matches_two_steps(case):
+    """One CSA layer's decode-step compression in one call (the KV entry and the index-key entry
+    of the block, one launch at m = 4): every block of a sequence, block 0's one-block state
+    included, gives exactly the bytes of two csa_compress_step calls, and only row `block` of
+    each cache is written; the entries are the oracle's within the output dtype's tolerance."""
+    in_dt, m, c, cI, ki_dt, batch = case
+    nb = 7
+    n = m * nb
+    say(f"csa_compress_step_kv_index in={in_dt} m={m} c={c} c_I={cI} ki={ki_dt} batch={batch}")
+    sd = 2100 + c + cI + m
+    kv_st = [draw(sd, i + 1, (batch, n, c), in_dt) for i in range(4)]
+    ki_st = [draw(sd, i + 11, (batch, n, cI), in_dt) for i in range(4)]
+    kvB = [draw(sd, 5, (m, c), F32, std=0.1), draw(sd, 6, (m, c), F32, std=0.1)]
+    kiB = [draw(sd, 15, (m, cI), F32, std=0.1), draw(sd, 16, (m, cI), F32, std=0.1)]
+    kv_d, ki_d = [to_dev(x, in_dt) for x in kv_st], [to_dev(x, in_dt) for x in ki_st]
+    kvB_d, kiB_d = [to_dev(x, F32) for x in kvB], [to_dev(x, F32) for x in kiB]
+    kv_t = kv_d[0].dtype
+    ki_t = torch.uint8 if ki_dt == FP8 else (torch.bfloat16 if ki_dt == BF16 else torch.float32)
+    kv_pair = torch.zeros((batch, nb + 2, c), dtype=kv_t, device="cuda")
+    ki_pair = torch.zeros((batch, nb + 2, cI), dtype=ki_t, device="cuda")
+    kv_two, ki_two = torch.zeros_like(kv_pair), torch.zeros_like(ki_pair)
+    for blk in range(nb):
+        sl = slice(m * max(0, blk - 1), m * (blk + 1))
+        kv_s = [x[:, sl].contiguous() for x in kv_d] + kvB_d
+        ki_s = [x[:, sl].contiguous() for x in ki_d] + kiB_d
+        csa.csa_compress_step_kv_index(kv_s, kv_pair, ki_s, ki_pair, blk)
+        csa.csa_compress_step(*kv_s, blk, kv_two)
+        csa.csa_compress_step(*ki_s, blk, ki_two)
+    torch.cuda.synchronize()
+    assert torch.equal(kv_pair, kv_two)
+    assert torch.equal(ki_pair, ki_two)
+    assert not kv_pair[:, nb:].any() and not ki_pair[:, nb:].any()
+    kv_ref = oracle.csa_compress(*kv_st, *kvB, m, in_dtype=in_dt, out_dtype=in_dt)
+    out_tol(in_dt)(from_dev(kv_pair[:, :nb]), kv_ref, "KV entries")
+    ki_ref = oracle.csa_compress(*ki_st, *kiB, m, in_dtype=in_dt, out_dtype=ki_dt)
+    ki_got = oracle.decode(from_dev(ki_pair[:, :nb]), ki_dt) if ki_dt == FP8 else from_dev(ki_pair[:, :nb])
+    if ki_dt == FP8:
+        step = np.maximum(2.0 ** (np.floor(np.log2(np.maximum(np.abs(ki_ref), 2.0 ** -6))) - 3), 2.0 ** -9)
+        assert np.all(np.abs(ki_got - ki_ref) <= step)
+    else:
+        out_tol(ki_dt)(ki_got, ki_ref, "index-key entries")
+
+
 @pytest.mark.parametrize("kind", ["csa", "csa_step", "hca", "hca_step"])
 def test_compress_fp8_output(kind):
     """fp8 e4m3 outputs of the compressor (the storage of fp8 indexer keys): the bytes are exactly
