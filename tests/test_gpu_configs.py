@@ -136,6 +136,48 @@ def test_cfg2_csa_decode_128k_sampled():
 
 
 @pytest.mark.timeout(900)
+def test_cfg2_decode_steps_with_compression_full_size():
+    """The unit the 128K decode benchmark times, at full size: m decode steps, the last of which
+    first compresses the block its token completes (the KV entry in bf16 and the index-key entry
+    in fp8, one launch) into the last cache rows.  Every sequence's two new entries against the
+    oracle's compression of the decode state; top-k and O of sampled sequences against the
+    oracle run on the caches with those oracle entries in place."""
+    cfg = CONFIGS["cfg2_csa_decode_128k"]
+    h = make_inputs(cfg)
+    dev = upload(cfg, h)
+    pipe = CsaDecode(dev, cfg.m, cfg.k, cfg.q_pos0)
+    assert pipe.can_compress()
+    say(f"config {cfg.name}: {cfg.m} decode steps with the block compression, full size")
+    pipe.run_steps()
+    torch.cuda.synchronize()
+    kv_new = oracle.csa_compress(h["Ca"], h["Cb"], h["Za"], h["Zb"], h["Ba"], h["Bb"], cfg.m, in_dtype=BF16,
+                                 out_dtype=BF16)[:, -1]
+    kI_new = oracle.csa_compress(h["ICa"], h["ICb"], h["IZa"], h["IZb"], h["IBa"], h["IBb"], cfg.m, in_dtype=BF16,
+                                 out_dtype=FP8)[:, -1]
+    assert_abs_close(from_dev(dev["kv"][:, -1]), kv_new, 2e-2, "new KV entries")
+    got_kI = oracle.decode(from_dev(dev["kI"][:, -1]), FP8)
+    step = np.maximum(2.0 ** (np.floor(np.log2(np.maximum(np.abs(kI_new), 2.0 ** -6))) - 3), 2.0 ** -9)
+    assert np.all(np.abs(got_kI - kI_new) <= step)
+    say(f"  new index-key entries equal to the oracle's rounding: {np.mean(got_kI == kI_new):.5f}")
+    # the oracle's selection for every sequence; its attention for sequence 0 and for the
+    # sequences whose oracle selection takes the new entry (up to four)
+    kI = oracle.decode(h["kI"], FP8)
+    kI[:, -1] = kI_new
+    sc = oracle.index_scores(oracle.decode(h["qI"], FP8), h["w"], kI, cfg.m, q_pos0=cfg.q_pos0, qk_dtype=FP8)
+    idx, _ = oracle.topk(sc, cfg.m, cfg.k, q_pos0=cfg.q_pos0)
+    gidx = from_dev(pipe.idx)
+    check_topk_recall(gidx.reshape(-1, cfg.k), idx.reshape(-1, cfg.k), sc.reshape(-1, sc.shape[-1]), cfg.k,
+                      what="top-k after the compressing step")
+    takes_new = np.flatnonzero((idx == cfg.N - 1).any(axis=(1, 2)))
+    say(f"  the oracle selects the new entry for {len(takes_new)} of {cfg.batch} sequences")
+    seqs = np.unique(np.concatenate([[0], takes_new[:4]]))
+    kv = oracle.decode(h["kv"][seqs], BF16)
+    kv[:, -1] = kv_new[seqs]
+    out = oracle.sparse_mqa(h["q"][seqs], kv, idx[seqs], cfg.scale, dtype=cfg.dt)
+    assert_abs_close(from_dev(pipe.out)[seqs], out, 2e-2, f"O after the compressing step, sequences {list(seqs)}")
+
+
+@pytest.mark.timeout(900)
 def test_cfg2_csa_decode_128k_kvmixed_sampled():
     """The 128K decode with its KV entries stored as 448 fp8 channels and 64 bf16 ones."""
     _decode_case("cfg2_csa_decode_128k_kvmixed", np.array([0, 11, 31]))
