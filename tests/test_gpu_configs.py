@@ -94,7 +94,7 @@ def test_cfg1_csa_prefill_sampled():
     pipe.run()
     torch.cuda.synchronize()
     rows = np.unique(np.concatenate([np.arange(0, 8), [2047, 2048, 2051, 4095], np.arange(8192 - 6, 8192),
-                                     np.random.RandomState(1).choice(8192, 24, replace=False)]))
+                                     np.random.RandomState(1).choice(8192, 200, replace=False)]))
     kv, kI, sc, idx, sel, out = oracle_csa_front(cfg, h, rows)
     gkv, gkI = from_dev(pipe.kv), from_dev(pipe.kI)
     assert_abs_close(gkv, kv, 2e-2, "KV (bf16)")
