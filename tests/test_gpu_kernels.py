@@ -688,8 +688,10 @@ def test_compress_step_matches_whole_sequence(dt):
     out_tol(dt)(from_dev(cache[:, :nb]), ref, "compress step")
 
 
-@pytest.mark.parametrize("case", [(BF16, 4, 512, 128, FP8, 5), (F32, 4, 64, 32, F32, 3), (F32, 2, 64, 24, BF16, 2)],
-                         ids=["bf16_kv512_ki128fp8_b5", "f32_kv64_ki32_b3", "f32_m2_two_launches"])
+@pytest.mark.parametrize("case", [(BF16, 4, 512, 128, FP8, 5), (F32, 4, 64, 32, F32, 3), (F32, 2, 64, 24, BF16, 2),
+                                  (BF16, 4, 1024, 8, BF16, 67)],
+                         ids=["bf16_kv512_ki128fp8_b5", "f32_kv64_ki32_b3", "f32_m2_two_launches",
+                              "bf16_kv1024_ki8_b67"])
 def test_compress_step_kv_index_matches_two_steps(case):
     """One CSA layer's decode-step compression in one call (the KV entry and the index-key entry
     of the block, one launch at m = 4): every block of a sequence, block 0's one-block state
