@@ -33,6 +33,21 @@ METRIC = "CSA query tokens/s (compress+index+top-k+MQA) at 128K ctx; % of roofli
 METRIC_COMPRESS = "CSA raw tokens compressed/s (csa_compress over a 1M-token sequence); % of HBM roofline"
 
 
+def mxfp4_recall_record():
+    """Mean / min / max per-sequence recall of the fp8 top-k by the MXFP4 top-k (both the
+    oracle's, on the 128K decode draws), from tests/golden/mxfp4_recall_cfg2.txt; None if absent."""
+    path = os.path.join(ROOT, "tests", "golden", "mxfp4_recall_cfg2.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        parts = line.split()
+        if len(parts) == 2 and parts[0] in ("recall_mean", "recall_min", "recall_max"):
+            rec[parts[0][len("recall_"):]] = float(parts[1])
+    rec["source"] = "tests/golden/mxfp4_recall_cfg2.txt"
+    return rec
+
+
 def metric_for(cfg) -> str:
     """The metric string of a workload: the headline one for 128K-context decode, else a label
     that names what that workload's tokens/s counts."""
@@ -459,6 +474,12 @@ def main():
                 hw[n] = u
     if hw:
         result["stage_counters"] = hw
+    if cfg.qk_dt == 3:
+        # selection quality of the MXFP4 indexer: the committed record of how much of the fp8
+        # oracle selection the MXFP4 oracle selection keeps on these draws (oracle-only figures)
+        rec = mxfp4_recall_record()
+        if rec is not None:
+            result["mxfp4_recall_vs_fp8"] = rec
     if with_compress:
         # the step above includes one compression every m steps; the same steps without it
         result["ms_per_step_without_compress"] = round(ms_plain, 5)
